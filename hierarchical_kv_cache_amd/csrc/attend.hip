@@ -1,0 +1,653 @@
+// Sparse and dense split-K decode attention with the (a, Z) merge.
+//
+// [ZHA] "전제와 한계" (premises and limits): each query attends exactly over the
+// sink token 0, every key of its selected leaves, and the open chunk.
+// [ATT] "같은 계산을 메모리 IO 를 줄여서 한다: FlashAttention 계열": online softmax
+// (running max m, sum l, unnormalised output o, rescaled by e^{m_old - m_new})
+// and Flash-Decoding (split the cache along its length, merge the splits).
+// [ASM] "방법론": two attention states merge as a = (Z_A a_A + Z_B a_B)/(Z_A + Z_B).
+//
+// Work decomposition (one GPU): a "group" is one (sequence, KV head); its leaf
+// list is cut into tiles of 64 keys and tiles into work items of 16 tiles; one
+// extra item per group holds the sink and the open chunk.  A persistent grid
+// walks all items of all groups; the 4 waves of a workgroup take alternate
+// tiles of an item and merge their states before writing one partial per query
+// head.  A group's K/V tile is read once for all G query heads of the group;
+// heads that did not select a leaf see its keys masked to -inf.
+//
+// Scores are kept in log2 units: q is pre-multiplied by scale * log2(e).
+#include "zha_internal.hpp"
+
+namespace zha {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+
+constexpr int kWavesPerWg = 4;
+constexpr int kMaxGroups = 2048;
+constexpr int kAttendGrid = 1024;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct AttendParams {
+  const float* q;             // [BHq][d]
+  const void* K;              // [BH][T_cap][d]
+  const void* V;
+  const int64_t* T;           // [B]
+  const int32_t* leaf_ids;    // [BH][leaf_cap] or null (dense)
+  const uint32_t* leaf_mask;  // [BH][leaf_cap] or null (dense)
+  const int32_t* leaf_count;  // [BH] or null (dense)
+  int32_t leaf_cap;
+  float* part;                // [BHq][split_cap][d + 2]
+  int32_t* status;
+  int32_t B, H_kv, G, C;
+  int64_t T_cap;
+  int32_t split_cap;
+  float qscale;               // scale * log2(e)
+};
+
+// Per-group geometry shared by the partial and merge kernels.
+struct GroupInfo {
+  int64_t T;
+  int32_t n1;      // complete leaves
+  int32_t U;       // leaf-list entries (dense: n1)
+  int32_t tiles;   // 64-key tiles over the list
+  int32_t items;   // work items incl. the tail item
+};
+
+__device__ inline GroupInfo group_info(const AttendParams& P, int gi) {
+  GroupInfo g;
+  const int b = gi / P.H_kv;
+  int64_t T = P.T[b];
+  if (T < 0) T = 0;
+  if (T > P.T_cap) T = P.T_cap;
+  g.T = T;
+  g.n1 = (int32_t)(T / P.C);
+  if (P.leaf_ids == nullptr) {
+    g.U = g.n1;
+  } else {
+    int32_t u = P.leaf_count[gi];
+    if (u < 0) u = 0;
+    if (u > P.leaf_cap) u = P.leaf_cap;
+    g.U = u;
+  }
+  g.tiles = (int32_t)(((int64_t)g.U * P.C + kTileKeys - 1) / kTileKeys);
+  g.items = (g.tiles + kTilesPerItem - 1) / kTilesPerItem + 1;
+  return g;
+}
+
+// Token and head mask of key slot `slot` (0..63) of tile `tile` of a group;
+// tile == -1 is the tail tile (slot 0: sink, slots 1..: open chunk).  Slots that
+// hold no key get token 0 (always inside the allocation) and mask 0.
+struct Slot { int32_t tok; uint32_t mask; };
+
+__device__ inline Slot slot_of(const AttendParams& P, int gi, const GroupInfo& g,
+                               int tile, int slot, uint32_t full, uint32_t sinkmask) {
+  Slot s{0, 0u};
+  if (tile < 0) {
+    if (slot == 0) {
+      s.mask = sinkmask;
+    } else {
+      const int64_t t = (int64_t)g.n1 * P.C + (slot - 1);
+      if (t < g.T) { s.tok = (int32_t)t; s.mask = full; }
+    }
+    return s;
+  }
+  const int64_t e = (int64_t)tile * kTileKeys + slot;
+  const int64_t entry = e / P.C;
+  if (entry < g.U) {
+    const int kk = (int)(e - entry * P.C);
+    if (P.leaf_ids == nullptr) {
+      s.tok = (int32_t)(entry * P.C + kk);
+      s.mask = full;
+    } else {
+      const int64_t off = (int64_t)gi * P.leaf_cap + entry;
+      const int32_t leaf = P.leaf_ids[off];
+      if (leaf >= 0 && leaf < g.n1) {
+        s.tok = leaf * P.C + kk;
+        s.mask = P.leaf_mask[off] & full;
+      }
+    }
+  }
+  return s;
+}
+
+// Sink mask of a group: heads that did not select leaf 0 take token 0 from the
+// tail tile.  Dense attention and T < C never need it.
+__device__ inline uint32_t sink_mask(const AttendParams& P, int gi, const GroupInfo& g,
+                                     uint32_t full) {
+  if (P.leaf_ids == nullptr || g.n1 == 0) return 0u;
+  uint32_t m0 = 0u;
+  if (g.U > 0 && P.leaf_ids[(int64_t)gi * P.leaf_cap] == 0)
+    m0 = P.leaf_mask[(int64_t)gi * P.leaf_cap];
+  return full & ~m0;
+}
+
+// LDS of the partial kernels.
+template <int D>
+struct AttendSmem {
+  int32_t item_prefix[kMaxGroups + 1];
+  int32_t scan[16];
+  float p[kWavesPerWg][kTileKeys][16];          // softmax numerators per slot, head
+  float alpha[kWavesPerWg][16];                 // rescale factors per head
+  float state[kWavesPerWg][16][D + 2];          // (m, l, o[D]) per wave and head
+  float qf[16][D];                              // fp32 path: scaled queries
+};
+
+// Work items of every group, prefix-summed into LDS; returns the total.
+template <int D>
+__device__ inline int plan_items(const AttendParams& P, AttendSmem<D>& sm) {
+  const int BH = P.B * P.H_kv;
+  const int per = (BH + blockDim.x - 1) / blockDim.x;
+  const int g0 = threadIdx.x * per;
+  int mine = 0;
+  for (int k = 0; k < per; ++k)
+    if (g0 + k < BH) mine += group_info(P, g0 + k).items;
+  int total = 0;
+  int acc = block_exclusive_scan<int>(mine, sm.scan, &total);
+  for (int k = 0; k < per; ++k)
+    if (g0 + k < BH) {
+      sm.item_prefix[g0 + k] = acc;
+      acc += group_info(P, g0 + k).items;
+    }
+  if (threadIdx.x == 0) sm.item_prefix[BH] = total;
+  __syncthreads();
+  return total;
+}
+
+__device__ inline int find_group(const int32_t* prefix, int BH, int item) {
+  int lo = 0, hi = BH;  // prefix[lo] <= item < prefix[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= item) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// WG-level merge of the per-wave states into one partial per query head.
+template <int D>
+__device__ inline void write_partial(const AttendParams& P, AttendSmem<D>& sm, int gi,
+                                     int item) {
+  const int G = P.G;
+  for (int idx = threadIdx.x; idx < G * (D + 2); idx += blockDim.x) {
+    const int g = idx / (D + 2), c = idx % (D + 2);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWavesPerWg; ++w) M = fmaxf(M, sm.state[w][g][0]);
+    float v;
+    if (c == 0) {
+      v = M;
+    } else {
+      v = 0.0f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kWavesPerWg; ++w) {
+          const float mw = sm.state[w][g][0];
+          if (mw != -INFINITY) v += sm.state[w][g][c] * exp2f(mw - M);
+        }
+      }
+    }
+    const int64_t head = (int64_t)gi * G + g;
+    P.part[(head * P.split_cap + item) * (D + 2) + c] = v;
+  }
+}
+
+// Online-softmax state of one wave for the bf16 path.  Scores arrive in MFMA
+// output layout: lane holds heads 4*(lane/16)+i (i < 4) for slot lane%16 of each
+// 16-slot column block.
+struct WaveSoftmax {
+  float m[4], l[4];
+};
+
+// ---------------------------------------------------------------- bf16 path
+//
+// QK^T on MFMA 16x16x32 bf16: rows = query heads of the group (padded to 16),
+// columns = 16 keys, contraction over d in steps of 32.  The fp32 query (times
+// scale*log2e) is split into three bf16 parts hi + mid + lo, whose sum carries
+// the fp32 value to ~2^-24 relative; the three products accumulate in fp32.
+// Lane l supplies row/column l%16 and the 8 consecutive dims s*32 + (l/16)*8 of
+// contraction step s for both operands, so each lane's K load is 16 contiguous
+// bytes.  P V runs on VALU: lane owns 8 consecutive dims of a few key rows.
+
+template <int D, int GP>
+__global__ void __launch_bounds__(256)
+attend_partial_bf16(AttendParams P) {
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(GP == 4 || GP == 8 || GP == 16, "padded heads");
+  constexpr int KSTEPS = D / 32;              // MFMA K steps
+  constexpr int LPR = D / 8;                  // lanes per V row (16 B each)
+  constexpr int RPI = kWave / LPR;            // V rows per load instruction
+  constexpr int VLOADS = kTileKeys / RPI;     // V loads per lane per tile
+  __shared__ AttendSmem<D> sm;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int BH = P.B * P.H_kv;
+  const int total = plan_items<D>(P, sm);
+  const uint32_t full = (P.G >= 32) ? 0xffffffffu : ((1u << P.G) - 1u);
+  const int hrow = (lane >> 4) * 4;           // first head row this lane holds
+
+  const uint16_t* Kb = (const uint16_t*)P.K;
+  const uint16_t* Vb = (const uint16_t*)P.V;
+
+  int cur_group = -1;
+  bf16x8_t a_hi[KSTEPS], a_mid[KSTEPS], a_lo[KSTEPS];
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int gi = find_group(sm.item_prefix, BH, item);
+    const int li = item - sm.item_prefix[gi];
+    const GroupInfo g = group_info(P, gi);
+
+    if (gi != cur_group) {
+      cur_group = gi;
+      const int row = lane & 15;          // head within the group
+      const int kg = lane >> 4;           // contraction group of 8 dims
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        bf16x8_t hi, mid, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float x = 0.0f;
+          if (row < P.G)
+            x = P.q[((int64_t)gi * P.G + row) * D + s * 32 + kg * 8 + j] * P.qscale;
+          const uint16_t h16 = f32_to_bf16_rne(x);
+          const float r1 = x - __uint_as_float((uint32_t)h16 << 16);
+          const uint16_t m16 = f32_to_bf16_rne(r1);
+          const float r2 = r1 - __uint_as_float((uint32_t)m16 << 16);
+          const uint16_t l16 = f32_to_bf16_rne(r2);
+          hi[j] = __builtin_bit_cast(__bf16, h16);
+          mid[j] = __builtin_bit_cast(__bf16, m16);
+          lo[j] = __builtin_bit_cast(__bf16, l16);
+        }
+        a_hi[s] = hi; a_mid[s] = mid; a_lo[s] = lo;
+      }
+    }
+
+    const bool tail = (li == g.items - 1);
+    const uint32_t smask = tail ? sink_mask(P, gi, g, full) : 0u;
+    // tiles of this wave: tail item -> wave 0 takes the single tail tile (-1)
+    int tile, t_end, t_step;
+    if (tail) { tile = (wave == 0) ? -1 : 0; t_end = 0; t_step = 1; }
+    else {
+      tile = li * kTilesPerItem + wave;
+      t_end = min(g.tiles, (li + 1) * kTilesPerItem);
+      t_step = kWavesPerWg;
+    }
+
+    WaveSoftmax st;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { st.m[i] = -INFINITY; st.l[i] = 0.0f; }
+    float o[GP][8];
+#pragma unroll
+    for (int hh = 0; hh < GP; ++hh)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[hh][j] = 0.0f;
+
+    const int64_t kv_base = (int64_t)gi * P.T_cap;
+    for (; tile < t_end; tile += t_step) {
+      const Slot my = slot_of(P, gi, g, tile, lane, full, smask);
+      const int my_valid = my.mask != 0u ? 1 : 0;
+
+      // K rows of the four 16-slot column blocks
+      u32x4_t kraw[4][KSTEPS];
+      uint32_t kmask[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int slot = t * 16 + (lane & 15);
+        const int tok = __shfl(my.tok, slot, 64);
+        kmask[t] = (uint32_t)__shfl((int)my.mask, slot, 64);
+        const uint16_t* row = Kb + (kv_base + tok) * D + (lane >> 4) * 8;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+          kraw[t][s] = *(const u32x4_t*)(row + s * 32);
+      }
+      // V rows: slot = RPI * i + lane / LPR, dims (lane % LPR) * 8 .. + 8
+      u32x4_t vraw[VLOADS];
+#pragma unroll
+      for (int i = 0; i < VLOADS; ++i) {
+        const int slot = RPI * i + lane / LPR;
+        const int tok = __shfl(my.tok, slot, 64);
+        const int ok = __shfl(my_valid, slot, 64);
+        const u32x4_t v = *(const u32x4_t*)(Vb + (kv_base + tok) * D + (lane % LPR) * 8);
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        vraw[i] = ok ? v : z;
+      }
+
+      // scores (log2 units): acc[t][i] = head hrow+i, slot t*16 + lane%16
+      f32x4_t acc[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kraw[t][s]);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[s], kb, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_mid[s], kb, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[s], kb, c, 0, 0, 0);
+        }
+        acc[t] = c;
+      }
+
+      // mask, per-head max over the 64 slots, online-softmax update
+      float alpha[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int head = hrow + i;
+        float v = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bool ok = (kmask[t] >> head) & 1u;
+          const float sc = ok ? acc[t][i] : -INFINITY;
+          acc[t][i] = sc;
+          v = fmaxf(v, sc);
+        }
+        v = fmaxf(v, swz_xor<1>(v));
+        v = fmaxf(v, swz_xor<2>(v));
+        v = fmaxf(v, swz_xor<4>(v));
+        v = fmaxf(v, swz_xor<8>(v));
+        const float mnew = fmaxf(st.m[i], v);
+        alpha[i] = (mnew == -INFINITY) ? 1.0f : exp2f(st.m[i] - mnew);
+        float ls = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float pv = (acc[t][i] == -INFINITY) ? 0.0f : exp2f(acc[t][i] - mnew);
+          acc[t][i] = pv;
+          ls += pv;
+        }
+        st.l[i] = st.l[i] * alpha[i] + ls;
+        st.m[i] = mnew;
+      }
+      // hand probabilities and rescale factors to the PV layout through LDS
+      if (hrow < GP) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          *(f32x4_t*)&sm.p[wave][t * 16 + (lane & 15)][hrow] = acc[t];
+        if ((lane & 15) == 0) {
+          const f32x4_t av = {alpha[0], alpha[1], alpha[2], alpha[3]};
+          *(f32x4_t*)&sm.alpha[wave][hrow] = av;
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int q4 = 0; q4 < GP / 4; ++q4) {
+        const f32x4_t av = *(const f32x4_t*)&sm.alpha[wave][q4 * 4];
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[q4 * 4 + hh][j] *= av[hh];
+      }
+#pragma unroll
+      for (int i = 0; i < VLOADS; ++i) {
+        const int slot = RPI * i + lane / LPR;
+        float vf[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vf[2 * j] = bf16_lo(vraw[i][j]);
+          vf[2 * j + 1] = bf16_hi(vraw[i][j]);
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < GP / 4; ++q4) {
+          const f32x4_t pv = *(const f32x4_t*)&sm.p[wave][slot][q4 * 4];
+#pragma unroll
+          for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[q4 * 4 + hh][j] += pv[hh] * vf[j];
+        }
+      }
+      wave_lds_sync();
+    }
+
+    // wave totals: l over the 16 columns, o over the V row groups
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = st.l[i];
+      v += swz_xor<1>(v);
+      v += swz_xor<2>(v);
+      v += swz_xor<4>(v);
+      v += swz_xor<8>(v);
+      st.l[i] = v;
+    }
+#pragma unroll
+    for (int hh = 0; hh < GP; ++hh)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float v = o[hh][j];
+        if (LPR <= 8) v += swz_xor<8>(v);
+        v += swz_xor<16>(v);
+        v += shfl_xor32(v);
+        o[hh][j] = v;
+      }
+    if ((lane & 15) == 0 && hrow < GP) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sm.state[wave][hrow + i][0] = st.m[i];
+        sm.state[wave][hrow + i][1] = st.l[i];
+      }
+    }
+    if (lane < LPR) {
+#pragma unroll
+      for (int hh = 0; hh < GP; ++hh)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sm.state[wave][hh][2 + lane * 8 + j] = o[hh][j];
+    }
+    __syncthreads();
+    write_partial<D>(P, sm, gi, li);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- fp32 path
+//
+// fp32 K/V (exact-precision runs): VALU only.  Lane = key slot for the scores
+// (q broadcast from LDS); lane = dims for P V.
+
+template <int D, int GP>
+__global__ void __launch_bounds__(256)
+attend_partial_f32(AttendParams P) {
+  constexpr int DPL = D / kWave;            // dims per lane in P V
+  __shared__ AttendSmem<D> sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int BH = P.B * P.H_kv;
+  const int total = plan_items<D>(P, sm);
+  const uint32_t full = (P.G >= 32) ? 0xffffffffu : ((1u << P.G) - 1u);
+  const float* Kf = (const float*)P.K;
+  const float* Vf = (const float*)P.V;
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int gi = find_group(sm.item_prefix, BH, item);
+    const int li = item - sm.item_prefix[gi];
+    const GroupInfo g = group_info(P, gi);
+    for (int idx = threadIdx.x; idx < 16 * D; idx += blockDim.x) {
+      const int hh = idx / D, c = idx % D;
+      sm.qf[hh][c] = (hh < P.G) ? P.q[((int64_t)gi * P.G + hh) * D + c] * P.qscale : 0.0f;
+    }
+    __syncthreads();
+
+    const bool tail = (li == g.items - 1);
+    const uint32_t smask = tail ? sink_mask(P, gi, g, full) : 0u;
+    int tile, t_end, t_step;
+    if (tail) { tile = (wave == 0) ? -1 : 0; t_end = 0; t_step = 1; }
+    else {
+      tile = li * kTilesPerItem + wave;
+      t_end = min(g.tiles, (li + 1) * kTilesPerItem);
+      t_step = kWavesPerWg;
+    }
+    float m[GP], l[GP], o[GP][DPL];
+#pragma unroll
+    for (int hh = 0; hh < GP; ++hh) {
+      m[hh] = -INFINITY; l[hh] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) o[hh][j] = 0.0f;
+    }
+    const int64_t kv_base = (int64_t)gi * P.T_cap;
+    for (; tile < t_end; tile += t_step) {
+      const Slot my = slot_of(P, gi, g, tile, lane, full, smask);
+      const float* krow = Kf + (kv_base + my.tok) * D;
+      float sc[GP];
+#pragma unroll
+      for (int hh = 0; hh < GP; ++hh) sc[hh] = 0.0f;
+      for (int c = 0; c < D; c += 4) {
+        const f32x4_t k4 = *(const f32x4_t*)(krow + c);
+#pragma unroll
+        for (int hh = 0; hh < GP; ++hh) {
+          const f32x4_t q4 = *(const f32x4_t*)&sm.qf[hh][c];
+          sc[hh] += q4[0] * k4[0];
+          sc[hh] += q4[1] * k4[1];
+          sc[hh] += q4[2] * k4[2];
+          sc[hh] += q4[3] * k4[3];
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < GP; ++hh) {
+        const bool ok = (my.mask >> hh) & 1u;
+        const float s = ok ? sc[hh] : -INFINITY;
+        const float mnew = fmaxf(m[hh], wave_max(s));
+        const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m[hh] - mnew);
+        const float pv = ok ? exp2f(s - mnew) : 0.0f;
+        l[hh] = l[hh] * alpha + pv;
+        m[hh] = mnew;
+        sm.p[wave][lane][hh] = pv;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) o[hh][j] *= alpha;
+      }
+      wave_lds_sync();
+      for (int slot = 0; slot < kTileKeys; ++slot) {
+        const int tok = __shfl(my.tok, slot, 64);
+        const int ok = __shfl(my.mask != 0u ? 1 : 0, slot, 64);
+        if (!ok) continue;  // wave-uniform
+        const float* vrow = Vf + (kv_base + tok) * D;
+        float v[DPL];
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) v[j] = vrow[lane + j * kWave];
+#pragma unroll
+        for (int hh = 0; hh < GP; ++hh) {
+          const float pv = sm.p[wave][slot][hh];
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) o[hh][j] += pv * v[j];
+        }
+      }
+      wave_lds_sync();
+    }
+#pragma unroll
+    for (int hh = 0; hh < GP; ++hh) {
+      const float lt = wave_sum(l[hh]);
+      if (lane == 0) { sm.state[wave][hh][0] = m[hh]; sm.state[wave][hh][1] = lt; }
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) sm.state[wave][hh][2 + lane + j * kWave] = o[hh][j];
+    }
+    __syncthreads();
+    write_partial<D>(P, sm, gi, li);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- merge
+//
+// [ASM] "방법론": lse = log sum_s Z_s, out = sum_s (Z_s / Z) a_s, evaluated as a
+// two-pass log-domain merge in a fixed order (max first, then weighted sums).
+template <int D>
+__global__ void __launch_bounds__(D)
+attend_merge(AttendParams P, float* out, float* lse) {
+  __shared__ float red[16];
+  const int head = blockIdx.x;              // b * Hq + j
+  const int gi = head / P.G;
+  const GroupInfo g = group_info(P, gi);
+  const int n = min(g.items, P.split_cap);
+  const float* base = P.part + (int64_t)head * P.split_cap * (D + 2);
+  float M = -INFINITY;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, base[(int64_t)i * (D + 2)]);
+  M = block_reduce_max<float>(M, red);
+  const int c = threadIdx.x;
+  float L = 0.0f, Ov = 0.0f;
+  if (M != -INFINITY) {
+    for (int i = 0; i < n; ++i) {
+      const float* pi = base + (int64_t)i * (D + 2);
+      const float mi = pi[0];
+      if (mi == -INFINITY) continue;
+      const float w = exp2f(mi - M);
+      L += pi[1] * w;
+      Ov += pi[2 + c] * w;
+    }
+  }
+  out[(int64_t)head * D + c] = (L > 0.0f) ? Ov / L : 0.0f;
+  if (c == 0) lse[head] = (L > 0.0f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------- host
+
+template <int D, int GP>
+static void launch_partial(const AttendParams& P, int kv_dtype, int grid, hipStream_t s) {
+  if (kv_dtype == ZHA_BF16)
+    hipLaunchKernelGGL((attend_partial_bf16<D, GP>), dim3(grid), dim3(256), 0, s, P);
+  else
+    hipLaunchKernelGGL((attend_partial_f32<D, GP>), dim3(grid), dim3(256), 0, s, P);
+}
+
+template <int D>
+static void launch_partial_g(const AttendParams& P, int kv_dtype, int grid, hipStream_t s) {
+  if (P.G <= 4) launch_partial<D, 4>(P, kv_dtype, grid, s);
+  else if (P.G <= 8) launch_partial<D, 8>(P, kv_dtype, grid, s);
+  else launch_partial<D, 16>(P, kv_dtype, grid, s);
+}
+
+static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
+                          const int32_t* leaf_ids, const uint32_t* leaf_mask,
+                          const int32_t* leaf_count, float* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream, bool dense) {
+  int32_t rc = zha_check_cfg(cfg);
+  if (rc != ZHA_OK) return rc;
+  if (cfg->G > 16) return ZHA_EUNSUPPORTED;
+  if ((int64_t)cfg->B * cfg->H_kv > kMaxGroups) return ZHA_EUNSUPPORTED;
+  if (q == nullptr || kv == nullptr || kv->K == nullptr || kv->V == nullptr ||
+      kv->T == nullptr || out == nullptr || lse == nullptr)
+    return ZHA_EINVAL;
+  if (!dense && (leaf_ids == nullptr || leaf_mask == nullptr || leaf_count == nullptr ||
+                 cfg->leaf_cap < 1))
+    return ZHA_EINVAL;
+  rc = zha_check_ws(cfg, dense ? ZHA_OP_DENSE : ZHA_OP_ATTEND, ws, ws_bytes);
+  if (rc != ZHA_OK) return rc;
+  const WsLayout w = ws_layout(*cfg);
+  AttendParams P;
+  P.q = q; P.K = kv->K; P.V = kv->V; P.T = kv->T;
+  P.leaf_ids = dense ? nullptr : leaf_ids;
+  P.leaf_mask = dense ? nullptr : leaf_mask;
+  P.leaf_count = dense ? nullptr : leaf_count;
+  P.leaf_cap = cfg->leaf_cap;
+  P.part = (float*)((char*)ws + w.attend_off);
+  P.status = (int32_t*)ws;
+  P.B = cfg->B; P.H_kv = cfg->H_kv; P.G = cfg->G; P.C = cfg->C;
+  P.T_cap = cfg->T_cap;
+  P.split_cap = w.split_cap;
+  P.qscale = cfg->scale * kLog2e;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t max_items = (int64_t)cfg->B * cfg->H_kv * w.split_cap;
+  const int grid = (int)(max_items < kAttendGrid ? max_items : kAttendGrid);
+  const int BHq = cfg->B * cfg->H_kv * cfg->G;
+  if (cfg->d == 64) {
+    launch_partial_g<64>(P, cfg->kv_dtype, grid, s);
+    hipLaunchKernelGGL((attend_merge<64>), dim3(BHq), dim3(64), 0, s, P, out, lse);
+  } else {
+    launch_partial_g<128>(P, cfg->kv_dtype, grid, s);
+    hipLaunchKernelGGL((attend_merge<128>), dim3(BHq), dim3(128), 0, s, P, out, lse);
+  }
+  return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
+}
+
+}  // namespace zha
+
+extern "C" int32_t zha_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
+                              const int32_t* leaf_ids, const uint32_t* leaf_mask,
+                              const int32_t* leaf_count, float* out, float* lse,
+                              void* ws, size_t ws_bytes, void* stream) {
+  return zha::run_attend(cfg, q, kv, leaf_ids, leaf_mask, leaf_count, out, lse, ws,
+                         ws_bytes, stream, false);
+}
+
+extern "C" int32_t dense_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
+                                float* out, float* lse, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return zha::run_attend(cfg, q, kv, nullptr, nullptr, nullptr, out, lse, ws, ws_bytes,
+                         stream, true);
+}

@@ -1,0 +1,212 @@
+// Internal helpers shared by the libzha translation units (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/zha.h"
+
+namespace zha {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- workspace layout
+//
+// One workspace serves every operation; regions are disjoint so a route and the
+// attend that consumes its leaf list may share one buffer.
+//   [0, 256)            header: int32 status word (sticky first error)
+//   route region        per level l (1..L): union ids/masks, counts, scores, sel,
+//                       per-head kept counts; plus cut staging
+//   attend region       split partials [B*Hq][split_cap][d+2] fp32
+struct WsLayout {
+  size_t route_off = 0, route_bytes = 0;
+  size_t attend_off = 0, attend_bytes = 0;
+  size_t total = 0;
+  // per-level route arrays (offsets from the workspace base); index l-1
+  size_t uids[ZHA_MAX_L], umask[ZHA_MAX_L], ucount[ZHA_MAX_L];
+  size_t scores[ZHA_MAX_L], sel[ZHA_MAX_L], kept[ZHA_MAX_L];
+  int64_t cap[ZHA_MAX_L];
+  size_t stage = 0;        // cut staging: [B*Hq][stage_cap] (u32 key, f32 w)
+  int64_t stage_cap = 0;
+  int32_t split_cap = 0;   // partial slots per query head
+};
+
+constexpr int kTileKeys = 64;       // keys per attend tile
+constexpr int kTilesPerItem = 16;   // tiles per split (work item)
+constexpr int kPartPad = 2;         // (m, l) ahead of the d outputs
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Node capacity of level l (1-based) for a cache of T_cap tokens.
+inline int64_t level_cap(const zha_cfg& c, int l) {
+  int64_t span = 1;
+  for (int i = 0; i < l; ++i) span *= c.C;
+  int64_t n = c.T_cap / span;
+  return n < 1 ? 1 : n;
+}
+
+// Work items (splits) per query head: tiles of the largest leaf list, plus the
+// tail item holding the open chunk and the sink.
+inline int32_t split_capacity(const zha_cfg& c) {
+  int64_t leaves = c.leaf_cap;
+  int64_t dense_leaves = c.T_cap / c.C;
+  if (dense_leaves > leaves) leaves = dense_leaves;
+  int64_t tiles = ceil_div(leaves * c.C, kTileKeys);
+  return (int32_t)(ceil_div(tiles, kTilesPerItem) + 1);
+}
+
+inline WsLayout ws_layout(const zha_cfg& c) {
+  WsLayout w;
+  const int64_t BH = (int64_t)c.B * c.H_kv, BHq = BH * c.G;
+  size_t off = 256;
+  w.route_off = off;
+  for (int l = 1; l <= c.L; ++l) {
+    int64_t cap = level_cap(c, l);
+    w.cap[l - 1] = cap;
+    w.uids[l - 1] = off;   off = align_up(off + (size_t)BH * cap * 4, 256);
+    w.umask[l - 1] = off;  off = align_up(off + (size_t)BH * cap * 4, 256);
+    w.ucount[l - 1] = off; off = align_up(off + (size_t)BH * 4, 256);
+    w.scores[l - 1] = off; off = align_up(off + (size_t)BHq * cap * 4, 256);
+    w.sel[l - 1] = off;    off = align_up(off + (size_t)BHq * cap, 256);
+    w.kept[l - 1] = off;   off = align_up(off + (size_t)BHq * 4, 256);
+  }
+  // Cut staging for lists too long for LDS: as long as the largest level.
+  int64_t scap = 0;
+  for (int l = 1; l <= c.L; ++l) scap = w.cap[l - 1] > scap ? w.cap[l - 1] : scap;
+  int64_t lcap = c.leaf_cap > 0 ? c.leaf_cap : 1;
+  if (lcap > scap) scap = lcap;
+  w.stage_cap = scap;
+  w.stage = off; off = align_up(off + (size_t)BHq * scap * 8, 256);
+  w.route_bytes = off - w.route_off;
+  w.attend_off = off;
+  w.split_cap = split_capacity(c);
+  off = align_up(off + (size_t)BHq * w.split_cap * (c.d + kPartPad) * 4, 256);
+  w.attend_bytes = off - w.attend_off;
+  w.total = off;
+  return w;
+}
+
+// ---------------------------------------------------------------- device helpers
+
+__device__ inline void set_status(int32_t* status, int32_t code) {
+  atomicCAS(status, 0, code);
+}
+
+// bf16 (raw 16 bits) to fp32: exact.
+__device__ inline float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ inline float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ inline uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t r = 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)((u + r) >> 16);
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key).
+__device__ inline uint32_t order_key(float x) {
+  if (x == 0.0f) x = 0.0f;  // fold -0 into +0
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Lane-exchange within 32-lane halves, xor pattern (ds_swizzle bitmask mode).
+template <int XOR>
+__device__ inline float swz_xor(float v) {
+  static_assert(XOR > 0 && XOR < 32, "xor within 32 lanes");
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (XOR << 10) | 0x1f));
+}
+
+__device__ inline float shfl_xor32(float v) {
+  // lanes l and l ^ 32 (crosses the 32-lane halves)
+  return __shfl_xor(v, 32, 64);
+}
+
+__device__ inline float wave_max(float v) {
+  v = fmaxf(v, swz_xor<1>(v));
+  v = fmaxf(v, swz_xor<2>(v));
+  v = fmaxf(v, swz_xor<4>(v));
+  v = fmaxf(v, swz_xor<8>(v));
+  v = fmaxf(v, swz_xor<16>(v));
+  v = fmaxf(v, shfl_xor32(v));
+  return v;
+}
+
+__device__ inline float wave_sum(float v) {
+  v += swz_xor<1>(v);
+  v += swz_xor<2>(v);
+  v += swz_xor<4>(v);
+  v += swz_xor<8>(v);
+  v += swz_xor<16>(v);
+  v += shfl_xor32(v);
+  return v;
+}
+
+// Exclusive prefix sum of one value per thread over the whole workgroup
+// (blockDim.x a multiple of 64, at most 1024).  `scratch` holds 16 T in LDS.
+// Returns the exclusive prefix; *total receives the block sum.  Deterministic.
+template <typename T>
+__device__ inline T block_exclusive_scan(T v, T* scratch, T* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  T x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    T y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  T before = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const T t = scratch[w];
+    if (w < wave) before += t;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+template <typename T>
+__device__ inline T block_reduce_max(T v, T* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    T y = __shfl_xor(v, off, 64);
+    v = v > y ? v : y;
+  }
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  T m = scratch[0];
+  for (int w = 1; w < nw; ++w) m = m > scratch[w] ? m : scratch[w];
+  __syncthreads();
+  return m;
+}
+
+template <typename T>
+__device__ inline T block_reduce_sum(T v, T* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  T s = 0;
+  for (int w = 0; w < nw; ++w) s += scratch[w];
+  __syncthreads();
+  return s;
+}
+
+// Order LDS traffic of one wave against itself (no cross-wave synchronisation).
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace zha
+
+// Host-side helpers implemented in api.hip.
+int32_t zha_check_cfg(const zha_cfg* cfg);
+int32_t zha_check_ws(const zha_cfg* cfg, int32_t op, const void* ws, size_t ws_bytes);
