@@ -25,8 +25,22 @@ def rel_err(o, ref) -> float:
     return float(np.max(np.abs(o - ref)) / den)
 
 
-def lists_from_sets(sets_per_head, B, H_kv, G, cap):
+def union_cap(sets_per_head, B, H_kv, G):
+    """Largest per-group union size of per-head sets (at least 1)."""
+    m = 1
+    for b in range(B):
+        for h in range(H_kv):
+            u = set()
+            for g in range(G):
+                u.update(int(x) for x in sets_per_head[b][h * G + g])
+            m = max(m, len(u))
+    return m
+
+
+def lists_from_sets(sets_per_head, B, H_kv, G, cap=None):
     """Per-head leaf sets -> (ids, mask, count) union lists [B][H_kv][cap]."""
+    if cap is None:
+        cap = union_cap(sets_per_head, B, H_kv, G)
     ids = torch.zeros(B, H_kv, cap, dtype=torch.int32)
     mask = torch.zeros(B, H_kv, cap, dtype=torch.int32)
     count = torch.zeros(B, H_kv, dtype=torch.int32)

@@ -1,0 +1,125 @@
+"""GPU parity of the tree builders (zha_build_level, zha_append) against the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.gpu_util import f64
+
+pytestmark = pytest.mark.gpu
+zha = pytest.importorskip("hierarchical_kv_cache_amd.zha")
+DEV = "cuda"
+
+# fp32 accumulation bounds of the builder relative to the data scale; each level
+# adds one weighted mean of the level below
+KHAT_TOL = {l: 1e-5 * 2 ** (l - 1) * 1.5 for l in range(1, 9)}
+BHAT_TOL = {l: 2e-5 * 2 ** (l - 1) * 1.25 for l in range(1, 9)}
+
+
+def _workload(name, **kw):
+    return synth.WORKLOADS[name].with_(**kw)
+
+
+def _build_gpu(wl, T, T_cap=None):
+    T_cap = T_cap or T
+    K, V = synth.make_cache(wl.with_(N=T, open_len=0, steps=0), DEV, T_cap)
+    qref = synth.make_qref(wl, DEV)
+    cfg = zha.Config(B=wl.B, H_kv=wl.H_kv, G=wl.G, d=wl.d, C=wl.C, L=wl.L, R=wl.R,
+                     T_cap=T_cap, kv_dtype=zha.F32 if wl.kv_dtype == "f32" else zha.BF16,
+                     rope=wl.rope, rope_base=wl.rope_base)
+    tree = zha.Tree(cfg, DEV)
+    ws = zha.new_workspace(cfg)
+    Tt = torch.full((wl.B,), T, dtype=torch.int64, device=DEV)
+    zha.build(cfg, K, V, Tt, qref, tree, ws)
+    torch.cuda.synchronize()
+    return cfg, K, V, qref, tree, ws, Tt
+
+
+def _compare_tree(cfg, K, qref, tree, T, rope_base, b=0, h=0):
+    ref = O.build_tree(f64(K[b, h, :T]), f64(qref[h]), T, cfg.C, cfg.L, cfg.scale, rope_base)
+    assert tree.n_built[:, b].tolist() == [T // cfg.C ** l for l in range(1, cfg.L + 1)]
+    worst = {}
+    for level in range(1, cfg.L + 1):
+        n = T // cfg.C ** level
+        if n == 0:
+            continue
+        kg = f64(tree.khat[level - 1][b, h, :n])
+        bg = f64(tree.bhat[level - 1][b, h, :n])
+        kr, br = ref[level - 1]["khat"], ref[level - 1]["bhat"]
+        scale_k = np.max(np.abs(kr))
+        ek = np.max(np.abs(kg - kr)) / scale_k
+        eb = np.max(np.abs(bg - br) / np.maximum(1.0, np.abs(br)))
+        worst[level] = (ek, eb)
+        assert ek <= KHAT_TOL[level], (level, ek)
+        assert eb <= BHAT_TOL[level], (level, eb)
+    return worst
+
+
+def test_build_tiny_fp32_nope():
+    wl = _workload("tiny")
+    cfg, K, V, qref, tree, ws, Tt = _build_gpu(wl, 4096)
+    _compare_tree(cfg, K, qref, tree, 4096, None)
+
+
+@pytest.mark.parametrize("C,L,T,G", [(16, 3, 10000, 4), (64, 2, 9000 + 17, 4), (4, 4, 1500, 8)])
+def test_build_bf16_nope_levels(C, L, T, G):
+    wl = _workload("gqa128k", H_kv=2, G=G, C=C, L=L, n_clusters=64)
+    cfg, K, V, qref, tree, ws, Tt = _build_gpu(wl, T)
+    for h in range(2):
+        _compare_tree(cfg, K, qref, tree, T, None, h=h)
+
+
+def test_build_rope_parent_correction():
+    """RoPE: reference queries rotated to each node's first key position; parents
+    rescore children at their own rotated query (the correction term)."""
+    wl = _workload("rope_batch", B=2, H_kv=1, G=2, C=32, L=3, n_clusters=64)
+    T = 32 ** 3 * 2 + 100
+    cfg, K, V, qref, tree, ws, Tt = _build_gpu(wl, T)
+    for b in range(2):
+        _compare_tree(cfg, K, qref, tree, T, wl.rope_base, b=b)
+
+
+def test_append_cascade_equals_prefill_build():
+    """Growing T one token at a time with zha_append yields exactly the tree a
+    prefill build of the final length gives (the append cadence)."""
+    wl = _workload("gqa128k", H_kv=2, G=4, C=8, L=3, n_clusters=16)
+    T0, T1 = 8 ** 3 - 37, 8 ** 3 * 2 + 70
+    K, V = synth.make_cache(wl.with_(N=T1, open_len=0, steps=0), DEV, T1 + 8)
+    qref = synth.make_qref(wl, DEV)
+    cfg = zha.Config(B=1, H_kv=2, G=4, d=128, C=8, L=3, R=16, T_cap=T1 + 8)
+    tree = zha.Tree(cfg, DEV)
+    ws = zha.new_workspace(cfg)
+    T = torch.tensor([T0], dtype=torch.int64, device=DEV)
+    zha.build(cfg, K, V, T, qref, tree, ws)
+    for t in range(T0 + 1, T1 + 1):
+        T.fill_(t)
+        zha.append(cfg, K, V, T, qref, tree, ws, max_new_tokens=1)
+    # one multi-token append as well (max_new_tokens bounds only the grid)
+    tree2 = zha.Tree(cfg, DEV)
+    T.fill_(T0)
+    zha.build(cfg, K, V, T, qref, tree2, ws)
+    T.fill_(T1)
+    zha.append(cfg, K, V, T, qref, tree2, ws, max_new_tokens=3)
+    ref = zha.Tree(cfg, DEV)
+    zha.build(cfg, K, V, T, qref, ref, ws)
+    torch.cuda.synchronize()
+    for level in range(1, 4):
+        n = T1 // 8 ** level
+        assert torch.equal(tree.khat[level - 1][:, :, :n], ref.khat[level - 1][:, :, :n])
+        assert torch.equal(tree.bhat[level - 1][:, :, :n], ref.bhat[level - 1][:, :, :n])
+        assert torch.equal(tree2.khat[level - 1][:, :, :n], ref.khat[level - 1][:, :, :n])
+    assert tree.n_built[:, 0].tolist() == [T1 // 8, T1 // 64, T1 // 512]
+    assert zha.ws_status(ws) == 0
+
+
+def test_build_is_deterministic():
+    wl = _workload("gqa128k", H_kv=1, G=4, C=64, L=2, n_clusters=8)
+    cfg, K, V, qref, tree, ws, Tt = _build_gpu(wl, 8192)
+    tree2 = zha.Tree(cfg, DEV)
+    zha.build(cfg, K, V, Tt, qref, tree2, ws)
+    torch.cuda.synchronize()
+    for a, b in zip(tree.khat + tree.bhat, tree2.khat + tree2.bhat):
+        assert torch.equal(a, b)

@@ -1,0 +1,214 @@
+"""GPU parity of the router (zha_route_level, zha_route) against the oracle.
+
+The GPU and the oracle route over the same fp32 tree (built by the oracle and
+rounded to fp32), so any difference is the router's own.  Levels are compared
+one at a time; after an allowed mismatch (near-tie or near-threshold, see
+route_check) the oracle continues from the GPU's selection.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.gpu_util import f64, lists_from_sets, sets_from_lists
+from tests.route_check import classify
+
+pytestmark = pytest.mark.gpu
+zha = pytest.importorskip("hierarchical_kv_cache_amd.zha")
+DEV = "cuda"
+SCORE_TOL = 2e-5  # |s_gpu - s_ref| / max(1, |s_ref|): fp32 dot of d terms + fp32 plane
+
+
+def oracle_tree32(wl, T, K):
+    """Oracle trees of every (b, h), rounded to fp32: list[b][h] of levels."""
+    qref = f64(synth.make_qref(wl, "cpu"))
+    trees = []
+    for b in range(wl.B):
+        row = []
+        for h in range(wl.H_kv):
+            t = O.build_tree(f64(K[b, h, :T]), qref[h], T, wl.C, wl.L, wl.scale,
+                             wl.rope_base if wl.rope else None)
+            row.append([{"khat": O.fp32(lv["khat"]), "bhat": O.fp32(lv["bhat"])} for lv in t])
+        trees.append(row)
+    return trees
+
+
+def upload(cfg, trees, T):
+    tree = zha.Tree(cfg, DEV)
+    for b in range(cfg.B):
+        for h in range(cfg.H_kv):
+            for level in range(1, cfg.L + 1):
+                n = T // cfg.C ** level
+                if n:
+                    tree.khat[level - 1][b, h, :n] = torch.tensor(trees[b][h][level - 1]["khat"], dtype=torch.float32)
+                    tree.bhat[level - 1][b, h, :n] = torch.tensor(trees[b][h][level - 1]["bhat"], dtype=torch.float32)
+    for level in range(1, cfg.L + 1):
+        tree.n_built[level - 1, :] = T // cfg.C ** level
+    return tree
+
+
+def level_sync_compare(cfg, tree_gpu, trees_host, q, T, p, ws, report):
+    """Route level by level on the GPU (zha_route_level) and check each level
+    against the oracle; returns GPU leaf sets per (b, query head)."""
+    qh = f64(q)
+    G, C, L = cfg.G, cfg.C, cfg.L
+    over = [[{} for _ in range(cfg.Hq)] for _ in range(cfg.B)]
+    leaves = [[None] * cfg.Hq for _ in range(cfg.B)]
+    for level in range(L, 0, -1):
+        cuts, cands = [], []
+        for b in range(cfg.B):
+            cb, kb = [], []
+            for j in range(cfg.Hq):
+                rt = O.route(qh[b, j], trees_host[b][j // G], T, C, L, p, cfg.scale,
+                             level_override=over[b][j])
+                lr = rt.level(level)
+                cb.append(lr.cut)
+                kb.append(lr.cand)
+            cuts.append(cb)
+            cands.append(kb)
+        ids, mask, count = lists_from_sets(cands, cfg.B, cfg.H_kv, G)
+        cap = ids.shape[-1]
+        scores = torch.full((cfg.B, cfg.Hq, cap), float("nan"), device=DEV)
+        sel = torch.zeros(cfg.B, cfg.Hq, cap, dtype=torch.uint8, device=DEV)
+        zha.route_level(cfg, level, q, tree_gpu, p, ids.to(DEV), mask.to(DEV), count.to(DEV),
+                        scores, sel, ws)
+        torch.cuda.synchronize()
+        sc, sl = scores.cpu().numpy(), sel.cpu().numpy()
+        idn, cnt = ids.numpy(), count.numpy()
+        for b in range(cfg.B):
+            for j in range(cfg.Hq):
+                h = j // G
+                n = int(cnt[b, h])
+                cut = cuts[b][j]
+                pos = {int(x): k for k, x in enumerate(idn[b, h, :n])}
+                # scores of this head's candidates
+                for k, cid in enumerate(cut.ids):
+                    s_g = sc[b, j, pos[int(cid)]]
+                    assert abs(s_g - cut.scores[k]) <= SCORE_TOL * max(1.0, abs(cut.scores[k])), \
+                        (level, b, j, int(cid), s_g, cut.scores[k])
+                # the GPU keeps only this head's candidates
+                gsel = [int(idn[b, h, u]) for u in range(n) if sl[b, j, u]]
+                cand_set = set(int(x) for x in cut.ids)
+                assert set(gsel) <= cand_set
+                ok, note = classify(cut, gsel)
+                assert ok, (level, b, j, note)
+                if note:
+                    report.append((level, b, j, note))
+                over[b][j][level] = np.array(sorted(gsel), dtype=np.int64)
+                if level == 1:
+                    leaves[b][j] = np.array(sorted(gsel), dtype=np.int64)
+    return leaves
+
+
+def _setup(wl, T, step=0):
+    K, V = synth.make_cache(wl.with_(N=T, open_len=0, steps=0), "cpu", T)
+    cfg = zha.Config(B=wl.B, H_kv=wl.H_kv, G=wl.G, d=wl.d, C=wl.C, L=wl.L, R=wl.R, T_cap=T,
+                     kv_dtype=zha.F32 if wl.kv_dtype == "f32" else zha.BF16,
+                     rope=wl.rope, rope_base=wl.rope_base)
+    trees = oracle_tree32(wl, T, K)
+    return cfg, K, V, trees
+
+
+CASES = {
+    "tiny": (synth.WORKLOADS["tiny"], 4096),
+    "tiny_iid": (synth.WORKLOADS["tiny"].with_(placement="iid"), 4096),
+    "gqa_c16": (synth.WORKLOADS["gqa128k"].with_(H_kv=2, C=16, L=3, n_clusters=256), 20000 + 7),
+    "deep": (synth.WORKLOADS["deep"].with_(H_kv=1, C=4, L=5, N=4 ** 5 * 3 + 50), 4 ** 5 * 3 + 50),
+    "rope": (synth.WORKLOADS["rope_batch"].with_(B=2, H_kv=1, G=4, C=16, L=3, n_clusters=64),
+             16 ** 3 * 2 + 40),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+@pytest.mark.parametrize("p", [0.5, 0.9])
+def test_route_level_parity_and_zha_route_composition(case, p):
+    wl, T = CASES[case]
+    cfg, K, V, trees = _setup(wl, T)
+    tree = upload(cfg, trees, T)
+    ws = zha.new_workspace(cfg)
+    Tt = torch.full((cfg.B,), T, dtype=torch.int64, device=DEV)
+    report = []
+    for step in range(3):
+        q = synth.make_query(wl, step, T, "cpu").to(DEV)
+        leaves = level_sync_compare(cfg, tree, trees, q, T, p, ws, report)
+        lst = zha.LeafList(cfg, DEV)
+        zha.route(cfg, q, tree, Tt, p, lst.ids, lst.mask, lst.count, ws)
+        torch.cuda.synchronize()
+        full = sets_from_lists(lst.ids, lst.mask, lst.count, cfg.G)
+        for b in range(cfg.B):
+            for j in range(cfg.Hq):
+                np.testing.assert_array_equal(full[b][j], leaves[b][j])
+        assert zha.ws_status(ws) == 0
+    for r in report:
+        print("allowed:", case, p, r)
+
+
+def test_p_one_selects_every_leaf_and_matches_dense():
+    wl, T = CASES["gqa_c16"]
+    cfg, K, V, trees = _setup(wl, T)
+    tree = upload(cfg, trees, T)
+    ws = zha.new_workspace(cfg)
+    Tt = torch.full((cfg.B,), T, dtype=torch.int64, device=DEV)
+    q = synth.make_query(wl, 0, T, "cpu").to(DEV)
+    lst = zha.LeafList(cfg, DEV)
+    zha.route(cfg, q, tree, Tt, 1.0, lst.ids, lst.mask, lst.count, ws)
+    torch.cuda.synchronize()
+    n1 = T // cfg.C
+    assert lst.count.cpu().tolist() == [[n1] * cfg.H_kv] * cfg.B
+    assert torch.equal(lst.ids[0, 0, :n1].cpu(), torch.arange(n1, dtype=torch.int32))
+    full = (1 << cfg.G) - 1
+    assert bool(torch.all(lst.mask[:, :, :n1] == full))
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    out, lse = torch.empty(cfg.B, cfg.Hq, cfg.d, device=DEV), torch.empty(cfg.B, cfg.Hq, device=DEV)
+    out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+    zha.attend(cfg, q, Kd, Vd, Tt, lst.ids, lst.mask, lst.count, out, lse, ws)
+    zha.dense_attend(cfg, q, Kd, Vd, Tt, out2, lse2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_ties_go_to_lower_id_on_gpu():
+    """Leaves 3 and 9 hold identical keys: equal scores; with one kept, it is 3."""
+    C, d, T = 16, 64, 16 * 16
+    g = torch.Generator().manual_seed(0)
+    K = torch.randn(1, 1, T, d, generator=g)
+    K[0, 0, 3 * C:4 * C] = 4.0 + 0.01 * torch.randn(C, d, generator=g)
+    K[0, 0, 9 * C:10 * C] = K[0, 0, 3 * C:4 * C]
+    V = torch.randn(1, 1, T, d, generator=g)
+    cfg = zha.Config(B=1, H_kv=1, G=1, d=d, C=C, L=1, R=4, T_cap=T, kv_dtype=zha.F32)
+    qref = (torch.randn(1, 4, d, generator=g) / 8).to(DEV)
+    tree = zha.Tree(cfg, DEV)
+    ws = zha.new_workspace(cfg)
+    Tt = torch.tensor([T], dtype=torch.int64, device=DEV)
+    zha.build(cfg, K.to(DEV), V.to(DEV), Tt, qref, tree, ws)
+    q = torch.ones(1, 1, d, device=DEV)
+    lst = zha.LeafList(cfg, DEV)
+    for p, expect in ((0.3, [3]), (0.6, [3, 9])):
+        zha.route(cfg, q, tree, Tt, p, lst.ids, lst.mask, lst.count, ws)
+        torch.cuda.synchronize()
+        n = int(lst.count[0, 0])
+        assert lst.ids[0, 0, :n].cpu().tolist() == expect
+    assert torch.equal(tree.khat[0][0, 0, 3], tree.khat[0][0, 0, 9])
+
+
+def test_stale_tree_is_reported():
+    wl, T = CASES["tiny"]
+    cfg, K, V, trees = _setup(wl, T)
+    tree = upload(cfg, trees, T)
+    ws = zha.new_workspace(cfg)
+    Tt = torch.full((1,), T + cfg.C, dtype=torch.int64, device=DEV)  # grew without append
+    cfg2 = zha.Config(**{**cfg.__dict__, "T_cap": T + cfg.C, "leaf_cap": None})
+    tree2 = zha.Tree(cfg2, DEV)
+    for level in range(cfg.L):
+        n = tree.khat[level].shape[2]
+        tree2.khat[level][:, :, :n] = tree.khat[level]
+        tree2.bhat[level][:, :, :n] = tree.bhat[level]
+        tree2.n_built[level] = tree.n_built[level]
+    ws2 = zha.new_workspace(cfg2)
+    lst = zha.LeafList(cfg2, DEV)
+    q = synth.make_query(wl, 0, T, "cpu").to(DEV)
+    zha.route(cfg2, q, tree2, Tt, 0.9, lst.ids, lst.mask, lst.count, ws2)
+    assert zha.ws_status(ws2) == zha.ESTALE
