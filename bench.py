@@ -1,0 +1,337 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of tree-summarised (ZHA) attention on one MI355X.
+
+A step is one pass of the hot path for every query head of the batch: the
+caller advances T (the new token's key/value are already in the cache), the tree
+grows when a chunk completes (zha_append, every C steps), the queries are routed
+down the tree (zha_route) and attend over the routed keys (zha_attend).  Inputs
+are synthetic and resident in HBM before timing starts.  The same steps are then
+timed with the dense split-K baseline (dense_attend) over every key.
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "routed decode-attn µs/step at 1M ctx; effective KV GB/s vs HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="long1m", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--p", type=float, default=None, help="top-p (default: the workload's)")
+    ap.add_argument("--p-sweep", default="0.75", help="extra p values timed (comma list, '' for none)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
+    ap.add_argument("--no-stats", action="store_true", help="skip the byte-accounting replay")
+    return ap.parse_args()
+
+
+class Run:
+    """Device state of one workload: cache, queries, tree, buffers."""
+
+    def __init__(self, wl, steps_total, dev="cuda"):
+        from hierarchical_kv_cache_amd import zha
+        self.zha = zha
+        self.wl = wl
+        self.T_cap = wl.T0 + steps_total + wl.C
+        t0 = time.time()
+        self.K, self.V = synth.make_cache(wl.with_(steps=steps_total + wl.C), dev, self.T_cap)
+        self.qref = synth.make_qref(wl, dev)
+        self.Q = torch.stack([synth.make_query(wl, s, wl.T0 + s, dev) for s in range(steps_total)])
+        torch.cuda.synchronize()
+        log(f"[bench] synthetic cache {wl.name}: {time.time() - t0:.1f}s")
+        self.cfg = zha.Config(B=wl.B, H_kv=wl.H_kv, G=wl.G, d=wl.d, C=wl.C, L=wl.L, R=wl.R,
+                              T_cap=self.T_cap,
+                              kv_dtype=zha.F32 if wl.kv_dtype == "f32" else zha.BF16,
+                              rope=wl.rope, rope_base=wl.rope_base)
+        self.dec = zha.Decoder(self.cfg, self.qref, dev)
+        self.T = torch.full((wl.B,), wl.T0, dtype=torch.int64, device=dev)
+
+    def prefill(self):
+        self.T.fill_(self.wl.T0)
+        self.dec.tree.n_built.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        self.dec.prefill(self.K, self.V, self.T)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def routed_steps(self, s0, s1, p, ev=None, counts=None):
+        """Steps s0..s1-1.  ev: list collecting (route, attend, append) event pairs."""
+        C = self.wl.C
+        for s in range(s0, s1):
+            t = self.wl.T0 + s
+            self.T.fill_(t)
+            q = self.Q[s]
+            if t % C == 0:
+                if ev is not None:
+                    a0 = torch.cuda.Event(enable_timing=True)
+                    a0.record()
+                self.dec.append(self.K, self.V, self.T, 1)
+                if ev is not None:
+                    a1 = torch.cuda.Event(enable_timing=True)
+                    a1.record()
+                    ev["append"].append((a0, a1))
+            if ev is not None:
+                r0 = torch.cuda.Event(enable_timing=True)
+                r0.record()
+            self.zha.route(self.cfg, q, self.dec.tree, self.T, p, self.dec.leaves.ids,
+                           self.dec.leaves.mask, self.dec.leaves.count, self.dec.ws)
+            if ev is not None:
+                r1 = torch.cuda.Event(enable_timing=True)
+                r1.record()
+            self.zha.attend(self.cfg, q, self.K, self.V, self.T, self.dec.leaves.ids,
+                            self.dec.leaves.mask, self.dec.leaves.count, self.dec.out,
+                            self.dec.lse, self.dec.ws)
+            if ev is not None:
+                r2 = torch.cuda.Event(enable_timing=True)
+                r2.record()
+                ev["route"].append((r0, r1))
+                ev["attend"].append((r1, r2))
+            if counts is not None:
+                L = self.wl.L
+                uc = torch.empty(L, self.wl.B, self.wl.H_kv, dtype=torch.int32, device="cuda")
+                kc = torch.empty(L, self.wl.B, self.wl.Hq, dtype=torch.int32, device="cuda")
+                self.zha.route_counts(self.cfg, self.dec.ws, uc, kc)
+                first = self.dec.leaves.ids[:, :, 0].clone()
+                counts.append((t, uc, kc, self.dec.leaves.count.clone(), first))
+
+    def dense_steps(self, s0, s1, ev=None):
+        for s in range(s0, s1):
+            self.T.fill_(self.wl.T0 + s)
+            if ev is not None:
+                d0 = torch.cuda.Event(enable_timing=True)
+                d0.record()
+            self.zha.dense_attend(self.cfg, self.Q[s], self.K, self.V, self.T, self.dec.out,
+                                  self.dec.lse, self.dec.ws)
+            if ev is not None:
+                d1 = torch.cuda.Event(enable_timing=True)
+                d1.record()
+                ev.append((d0, d1))
+
+
+def timed(fn):
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def bytes_of_step(wl, rec):
+    """Algorithmic bytes of one routed step from its route counts: unique summary
+    bytes scored per level, unique K/V bytes of the attended key set, q and out."""
+    t, uc, kc, lc, first = rec
+    uc, lc, first = uc.cpu(), lc.cpu(), first.cpu()
+    node_bytes = wl.R * (wl.d + 1) * 4
+    kv_row = 2 * wl.d * (2 if wl.kv_dtype == "bf16" else 4)
+    n1 = t // wl.C
+    route_b = int(uc.sum()) * node_bytes
+    keys = 0
+    for b in range(wl.B):
+        for h in range(wl.H_kv):
+            u = int(lc[b, h])
+            sink = 1 if (n1 > 0 and (u == 0 or int(first[b, h]) != 0)) else 0
+            keys += u * wl.C + (t - n1 * wl.C) + sink
+    qo = wl.B * wl.Hq * (wl.d * 4 + (wl.d + 1) * 4)
+    return route_b, keys * kv_row + qo, keys
+
+
+def cpu_baseline(run, p, s):
+    """The oracle timed on a bounded sample: one KV head of sequence 0 (its G query
+    heads) for one decode step, with the oracle's own tree; scaled to a full step."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    import oracle as O
+    wl = run.wl
+    t = wl.T0 + s
+    K = run.K[0, 0, :t].to("cpu").to(torch.float64).numpy()
+    V = run.V[0, 0, :t].to("cpu").to(torch.float64).numpy()
+    qref = run.qref[0].to("cpu").to(torch.float64).numpy()
+    q = run.Q[s, 0, :wl.G].to("cpu").to(torch.float64).numpy()
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        tree = O.build_tree(K, qref, t, wl.C, wl.L, wl.scale, wl.rope_base if wl.rope else None)
+        build_s = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for g in range(wl.G):
+            rt = O.route(q[g], tree, t, wl.C, wl.L, p, wl.scale)
+            keys = O.routed_keys(rt.leaves, t, wl.C)
+            O.attend_keys(q[g], K, V, keys, wl.scale)
+        step_s = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for g in range(wl.G):
+            O.attention(q[g], K, V, wl.scale)
+        dense_s = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    groups = wl.B * wl.H_kv
+    return {
+        "value": step_s * groups * 1e6, "unit": "us/step", "cores": 1, "kind": "oracle",
+        "sample": f"KV head 0 of sequence 0 ({wl.G} query heads), one decode step at T={t}, "
+                  f"numpy float64 single-threaded; x{groups} KV-head groups for a full step",
+        "dense_us_per_step": dense_s * groups * 1e6,
+        "tree_build_s_one_head": build_s,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design note, not part of this build", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    wl = synth.WORKLOADS[args.workload]
+    p = args.p if args.p is not None else wl.p
+    W, K = args.warmup, args.steps
+    run = Run(wl, W + K)
+    zha = run.zha
+
+    build_ms = run.prefill()
+    log(f"[bench] prefill tree build: {build_ms:.2f} ms")
+
+    # ---- routed: warmup, then exactly K timed steps
+    run.routed_steps(0, W, p)
+    ev = {"route": [], "attend": [], "append": []}
+    total_ms = timed(lambda: run.routed_steps(W, W + K, p, ev))
+    st = zha.ws_status(run.dec.ws)
+    if st != 0:
+        raise RuntimeError(f"device status {zha.status_str(st)}")
+    route_ms = [a.elapsed_time(b) for a, b in ev["route"]]
+    attend_ms = [a.elapsed_time(b) for a, b in ev["attend"]]
+    append_ms = [a.elapsed_time(b) for a, b in ev["append"]]
+    us_step = total_ms * 1000.0 / K
+    log(f"[bench] routed p={p}: {us_step:.1f} us/step (route {1000*sum(route_ms)/K:.1f}, "
+        f"attend {1000*sum(attend_ms)/K:.1f}, appends {len(append_ms)})")
+
+    extra = {}
+    # ---- p sweep (same steps, warm)
+    for ps in [float(x) for x in args.p_sweep.split(",") if x.strip()]:
+        if ps == p:
+            continue
+        run.prefill()
+        run.routed_steps(0, W, ps)
+        ms = timed(lambda: run.routed_steps(W, W + K, ps))
+        extra[f"p{ps}"] = {"us_per_step": ms * 1000.0 / K}
+        log(f"[bench] routed p={ps}: {ms * 1000.0 / K:.1f} us/step")
+
+    # ---- dense baseline over the same steps
+    dense = None
+    if not args.no_dense:
+        run.dense_steps(0, W)
+        dev = []
+        ms = timed(lambda: run.dense_steps(W, W + K, dev))
+        dk = [a.elapsed_time(b) for a, b in dev]
+        dense_bytes = 0
+        for s in range(W, W + K):
+            dense_bytes += wl.B * wl.H_kv * (wl.T0 + s) * 2 * wl.d * 2
+        dense = {"us_per_step": ms * 1000.0 / K,
+                 "effective_GBps": dense_bytes / K / (sum(dk) / K * 1e-3) / 1e9,
+                 "kernel_us": 1000 * sum(dk) / K}
+        dense["hbm_frac"] = dense["effective_GBps"] / HBM_PEAK_GBPS
+        log(f"[bench] dense: {dense['us_per_step']:.1f} us/step, {dense['effective_GBps']:.0f} GB/s")
+
+    # ---- replay for byte accounting (deterministic: identical routing)
+    route_bytes = attend_bytes = keys_total = 0
+    sel_frac = None
+    if not args.no_stats:
+        run.prefill()
+        run.routed_steps(0, W, p)
+        recs = []
+        run.routed_steps(W, W + K, p, counts=recs)
+        torch.cuda.synchronize()
+        kept = torch.zeros(wl.L)
+        for rec in recs:
+            rb, ab, keys = bytes_of_step(wl, rec)
+            route_bytes += rb
+            attend_bytes += ab
+            keys_total += keys
+            kept += rec[2].cpu().to(torch.float64).sum(dim=(1, 2))
+        sel_frac = keys_total / sum(wl.B * wl.H_kv * (wl.T0 + s) for s in range(W, W + K))
+        extra["kept_per_head_per_level"] = [float(x) / (K * wl.B * wl.Hq) for x in kept]
+
+    att_s = sum(attend_ms) * 1e-3
+    rte_s = sum(route_ms) * 1e-3
+    att_gbps = attend_bytes / att_s / 1e9 if att_s > 0 and attend_bytes else None
+    rte_gbps = route_bytes / rte_s / 1e9 if rte_s > 0 and route_bytes else None
+    step_gbps = (attend_bytes + route_bytes) / (total_ms * 1e-3) / 1e9 if attend_bytes else None
+    dominant = "attend" if sum(attend_ms) >= sum(route_ms) else "route"
+    ach = att_gbps if dominant == "attend" else rte_gbps
+    roofline = {
+        "bound": "hbm",
+        "kernel": "zha_attend (split-K partial + merge)" if dominant == "attend" else "zha_route (all levels)",
+        "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": (ach / HBM_PEAK_GBPS) if ach else None,
+        "traffic": None,
+        "avg_launch_us": 1000 * (sum(attend_ms) if dominant == "attend" else sum(route_ms)) / K,
+        "algorithmic_bytes_per_launch": (attend_bytes if dominant == "attend" else route_bytes) / K,
+    }
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] oracle CPU baseline (bounded sample) ...")
+        cpu = cpu_baseline(run, p, W)
+        log(f"[bench] oracle: {cpu['value']:.0f} us/step (sample)")
+
+    out = {
+        "metric": METRIC, "value": us_step, "unit": "us/step", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": total_ms / K, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H_kv": wl.H_kv, "G": wl.G, "d": wl.d,
+                   "T0": wl.T0, "C": wl.C, "L": wl.L, "R": wl.R, "p": p, "kv_dtype": wl.kv_dtype,
+                   "clusters": wl.n_clusters, "cluster_law": wl.freq},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "route_us": 1000 * sum(route_ms) / K,
+        "attend_us": 1000 * sum(attend_ms) / K,
+        "append_us_each": (1000 * sum(append_ms) / len(append_ms)) if append_ms else None,
+        "appends_in_timed_steps": len(append_ms),
+        "prefill_build_ms": build_ms,
+        "effective_GBps_step": step_gbps,
+        "route_GBps": rte_gbps,
+        "attend_GBps": att_gbps,
+        "selected_key_frac": sel_frac,
+        "dense": dense,
+        "speedup_vs_dense": (dense["us_per_step"] / us_step) if dense else None,
+        **extra,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

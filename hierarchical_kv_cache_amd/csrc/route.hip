@@ -528,3 +528,23 @@ extern "C" int32_t zha_route_level(const zha_cfg* cfg, int32_t level, const floa
   hipLaunchKernelGGL(cut_topp, dim3(cfg->B * cfg->H_kv * cfg->G), dim3(kCutThreads), 0, s, P);
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
 }
+
+extern "C" int32_t zha_route_counts(const zha_cfg* cfg, const void* ws, int32_t* union_count,
+                                    int32_t* kept_count, void* stream) {
+  using namespace zha;
+  int32_t rc = zha_check_cfg(cfg);
+  if (rc != ZHA_OK) return rc;
+  if (ws == nullptr || union_count == nullptr || kept_count == nullptr) return ZHA_EINVAL;
+  const WsLayout w = ws_layout(*cfg);
+  hipStream_t s = (hipStream_t)stream;
+  const size_t BH = (size_t)cfg->B * cfg->H_kv, BHq = BH * cfg->G;
+  for (int l = 1; l <= cfg->L; ++l) {
+    if (hipMemcpyAsync(union_count + (l - 1) * BH, (const char*)ws + w.ucount[l - 1],
+                       BH * sizeof(int32_t), hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return ZHA_EHIP;
+    if (hipMemcpyAsync(kept_count + (l - 1) * BHq, (const char*)ws + w.kept[l - 1],
+                       BHq * sizeof(int32_t), hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return ZHA_EHIP;
+  }
+  return ZHA_OK;
+}

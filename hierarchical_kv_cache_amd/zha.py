@@ -24,7 +24,8 @@ F32, BF16 = 0, 1
 OP_BUILD, OP_ROUTE, OP_ATTEND, OP_DENSE, OP_ALL = range(5)
 
 EXPORTS = ["zha_workspace_bytes", "zha_status_str", "zha_build_level", "zha_append",
-           "zha_route", "zha_route_level", "zha_attend", "dense_attend", "zha_ws_status"]
+           "zha_route", "zha_route_level", "zha_attend", "dense_attend", "zha_route_counts",
+           "zha_ws_status"]
 
 
 class ZhaError(RuntimeError):
@@ -66,6 +67,7 @@ def _load() -> ctypes.CDLL:
         "zha_route_level": (i32, [cfgp, i32, P, treep, f32, P, P, P, i32, P, P, P, sz, P]),
         "zha_attend": (i32, [cfgp, P, kvp, P, P, P, P, P, P, sz, P]),
         "dense_attend": (i32, [cfgp, P, kvp, P, P, P, sz, P]),
+        "zha_route_counts": (i32, [cfgp, P, P, P, P]),
         "zha_ws_status": (i32, [P, P, ctypes.POINTER(i32)]),
     }
     for name, (res, args) in sig.items():
@@ -219,6 +221,13 @@ def dense_attend(cfg: Config, q, K, V, T, out, lse, ws, stream=None):
     _check(_lib.dense_attend(ctypes.byref(cfg.c()), _ptr(q), ctypes.byref(_kv(K, V, T)),
                              _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)),
            "dense_attend")
+
+
+def route_counts(cfg: Config, ws, union_count, kept_count, stream=None):
+    """Per-level candidate-union sizes [L][B][H_kv] and kept counts [L][B][Hq] of
+    the last route on ``ws`` (int32 device tensors, filled asynchronously)."""
+    _check(_lib.zha_route_counts(ctypes.byref(cfg.c()), _ptr(ws), _ptr(union_count),
+                                 _ptr(kept_count), _stream(stream)), "zha_route_counts")
 
 
 def ws_status(ws, stream=None) -> int:

@@ -55,7 +55,7 @@ extern "C" {
 #endif
 
 #define ZHA_MAX_L 8      /* deepest tree supported */
-#define ZHA_MAX_G 32     /* query heads per KV head (leaf_mask is 32 bits) */
+#define ZHA_MAX_G 16     /* query heads per KV head (leaf_mask bits used) */
 
 enum zha_status {
   ZHA_OK = 0,
@@ -79,7 +79,7 @@ typedef struct zha_cfg {
   int32_t B, H_kv, G, d;
   int32_t C;             /* chunk size: keys per leaf and children per node */
   int32_t L;             /* tree levels, 1..ZHA_MAX_L */
-  int32_t R;             /* reference queries per tree, 1..32 */
+  int32_t R;             /* reference queries per tree, 1..16 */
   float scale;           /* score scale, normally 1/sqrt(d) ([ATT] SDPA equation) */
   int32_t rope;          /* 0: NoPE; 1: reference queries rotated (rotate-half) */
   float rope_base;       /* RoPE base when rope = 1, e.g. 1e6 */
@@ -192,6 +192,16 @@ int32_t zha_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
  */
 int32_t dense_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
                      float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * zha_route_counts -- diagnostics of the most recent zha_route that used ``ws``:
+ * copies, on ``stream``, the per-level size of every group's candidate union
+ * list into union_count [L][B][H_kv] and every query head's kept count into
+ * kept_count [L][B][Hq] (int32, device; level l at index l-1).  Used to count the
+ * summary bytes a step actually scored.
+ */
+int32_t zha_route_counts(const zha_cfg* cfg, const void* ws, int32_t* union_count,
+                         int32_t* kept_count, void* stream);
 
 /*
  * zha_ws_status -- synchronise ``stream``, copy the workspace status word into

@@ -1,0 +1,91 @@
+"""The C ABI library loads, exports every function include/zha.h declares, and
+rejects bad arguments on the host before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zha.h")
+
+zha = pytest.importorskip("hierarchical_kv_cache_amd.zha")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert "zha_route" in names and "dense_attend" in names and len(names) >= 10
+    lib = ctypes.CDLL(zha.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(zha.EXPORTS) == names
+
+
+def test_status_strings_and_workspace_sizes():
+    for code in range(7):
+        assert zha.status_str(code).startswith("ZHA")
+    small = zha.Config(B=1, H_kv=1, G=1, d=64, C=16, L=2, R=4, T_cap=4096)
+    big = zha.Config(B=1, H_kv=8, G=4, d=128, C=64, L=3, R=16, T_cap=(1 << 20) + 128)
+    assert 0 < zha.workspace_bytes(small) < zha.workspace_bytes(big)
+    for op in range(5):
+        assert zha.workspace_bytes(big, op) > 0
+    assert zha.workspace_bytes(big, zha.OP_ROUTE) <= zha.workspace_bytes(big, zha.OP_ALL)
+
+
+@pytest.mark.parametrize("bad", [dict(d=96), dict(C=3), dict(C=128), dict(L=9), dict(R=17),
+                                 dict(G=0), dict(B=0), dict(kv_dtype=7)])
+def test_unsupported_geometry_is_rejected(bad):
+    kw = dict(B=1, H_kv=1, G=1, d=64, C=16, L=2, R=4, T_cap=4096)
+    kw.update(bad)
+    with pytest.raises(zha.ZhaError):
+        zha.workspace_bytes(zha.Config(**kw))
+
+
+def _route(cfg, p=0.9, ws_bytes=None, q=1, leaf=1):
+    fake = ctypes.c_void_p(0x1000)
+    tree = zha._Tree()
+    for i in range(cfg.L):
+        tree.khat[i] = 0x2000
+        tree.bhat[i] = 0x3000
+        tree.n_cap[i] = cfg.level_cap(i + 1)
+    tree.n_built = 0x4000
+    need = ws_bytes if ws_bytes is not None else zha.workspace_bytes(cfg, zha.OP_ROUTE)
+    return zha._lib.zha_route(ctypes.byref(cfg.c()), fake if q else None, ctypes.byref(tree),
+                              fake, ctypes.c_float(p), fake if leaf else None, fake, fake,
+                              ctypes.c_void_p(0x100000), need,
+                              None)
+
+
+def test_bad_arguments_return_codes_without_launching():
+    cfg = zha.Config(B=1, H_kv=2, G=4, d=128, C=64, L=3, R=16, T_cap=1 << 16)
+    assert _route(cfg, p=0.0) == zha.EINVAL
+    assert _route(cfg, p=1.5) == zha.EINVAL
+    assert _route(cfg, p=float("nan")) == zha.EINVAL
+    assert _route(cfg, q=0) == zha.EINVAL
+    assert _route(cfg, leaf=0) == zha.EINVAL
+    assert _route(cfg, ws_bytes=100) == zha.EWORKSPACE
+    small_leaf = zha.Config(B=1, H_kv=2, G=4, d=128, C=64, L=3, R=16, T_cap=1 << 16, leaf_cap=10)
+    assert _route(small_leaf) == zha.EINVAL
+    g17 = zha.Config(B=1, H_kv=1, G=17, d=128, C=64, L=3, R=16, T_cap=1 << 16)
+    assert _route(g17, ws_bytes=1 << 30) == zha.EUNSUPPORTED
+    out = zha._lib.dense_attend(ctypes.byref(cfg.c()), None, None, None, None, None, 0, None)
+    assert out == zha.EINVAL
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    pkg = tmp_path / "hierarchical_kv_cache_amd"
+    shutil.copytree(os.path.join(ROOT, "hierarchical_kv_cache_amd"), pkg,
+                    ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__"))
+    code = "import hierarchical_kv_cache_amd as h; h.Config"
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True)
+    assert r.returncode != 0 and "ImportError" in r.stderr and "not built" in r.stderr
