@@ -545,34 +545,51 @@ attend_partial_f32(AttendParams P) {
 
 // ---------------------------------------------------------------- merge
 //
-// [ASM] "방법론": lse = log sum_s Z_s, out = sum_s (Z_s / Z) a_s, evaluated as a
-// two-pass log-domain merge in a fixed order (max first, then weighted sums).
+// [ASM] "방법론": lse = log sum_s Z_s, out = sum_s (Z_s / Z) a_s, evaluated in the
+// log domain in two passes: the maximum of the partial maxima, then the rescaled
+// sums.  Wave w of the workgroup takes partials w, w+4, ... (lanes over dims, the
+// loads of successive partials are independent); the four wave sums are added in
+// a fixed order, so the result is deterministic.
 template <int D>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(256)
 attend_merge(AttendParams P, float* out, float* lse) {
+  constexpr int DPL = D / kWave;
   __shared__ float red[16];
+  __shared__ float acc_o[kWavesPerWg][D];
+  __shared__ float acc_l[kWavesPerWg];
   const int head = blockIdx.x;              // b * Hq + j
   const int gi = head / P.G;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const GroupInfo g = group_info(P, gi);
   const int n = min(g.items, P.split_cap);
   const float* base = P.part + (int64_t)head * P.split_cap * (D + 2);
   float M = -INFINITY;
   for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, base[(int64_t)i * (D + 2)]);
   M = block_reduce_max<float>(M, red);
-  const int c = threadIdx.x;
-  float L = 0.0f, Ov = 0.0f;
+  float l = 0.0f, o[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) o[j] = 0.0f;
   if (M != -INFINITY) {
-    for (int i = 0; i < n; ++i) {
+#pragma unroll 4
+    for (int i = wave; i < n; i += kWavesPerWg) {
       const float* pi = base + (int64_t)i * (D + 2);
-      const float mi = pi[0];
-      if (mi == -INFINITY) continue;
-      const float w = exp2f(mi - M);
-      L += pi[1] * w;
-      Ov += pi[2 + c] * w;
+      const float w = exp2f(pi[0] - M);       // 0 for an empty partial (m = -inf)
+      l += pi[1] * w;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) o[j] += pi[2 + lane + j * kWave] * w;
     }
   }
-  out[(int64_t)head * D + c] = (L > 0.0f) ? Ov / L : 0.0f;
-  if (c == 0) lse[head] = (L > 0.0f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) acc_o[wave][lane + j * kWave] = o[j];
+  if (lane == 0) acc_l[wave] = l;
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float L = 0.0f, Ov = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWavesPerWg; ++w) { L += acc_l[w]; Ov += acc_o[w][c]; }
+    out[(int64_t)head * D + c] = (L > 0.0f) ? Ov / L : 0.0f;
+    if (c == 0) lse[head] = (L > 0.0f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+  }
 }
 
 // ---------------------------------------------------------------- host
@@ -627,10 +644,10 @@ static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
   const int BHq = cfg->B * cfg->H_kv * cfg->G;
   if (cfg->d == 64) {
     launch_partial_g<64>(P, cfg->kv_dtype, grid, s);
-    hipLaunchKernelGGL((attend_merge<64>), dim3(BHq), dim3(64), 0, s, P, out, lse);
+    hipLaunchKernelGGL((attend_merge<64>), dim3(BHq), dim3(256), 0, s, P, out, lse);
   } else {
     launch_partial_g<128>(P, cfg->kv_dtype, grid, s);
-    hipLaunchKernelGGL((attend_merge<128>), dim3(BHq), dim3(128), 0, s, P, out, lse);
+    hipLaunchKernelGGL((attend_merge<128>), dim3(BHq), dim3(256), 0, s, P, out, lse);
   }
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
 }

@@ -149,7 +149,7 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
 // ---------------------------------------------------------------- top-p cut (A4)
 
 constexpr int kCutThreads = 1024;
-constexpr int kCutLds = 8192;          // entries staged in LDS; longer lists use the workspace
+constexpr int kCutLds = 16384;         // entries staged in LDS; longer lists use the workspace
 constexpr double kFix = 1099511627776.0;  // 2^40
 
 __device__ inline uint64_t fixmass(float w) { return (uint64_t)((double)w * kFix); }
@@ -221,12 +221,30 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < 256; i += kCutThreads) { sm.cnt[i] = 0u; sm.mass[i] = 0ull; }
     __syncthreads();
-    for (int u = tid; u < U; u += kCutThreads) {
-      const uint32_t k = skey[u];
-      if (k != 0u && (k & pmask) == prefix) {
-        const uint32_t bkt = (k >> shift) & 255u;
+    // Scores cluster, so most lanes of a wave often hit one bucket: such waves
+    // add one aggregated (count, mass) instead of 64 conflicting LDS atomics.
+    const int lane = tid & 63;
+    for (int base = 0; base < U; base += kCutThreads) {
+      const int u = base + tid;
+      const uint32_t k = (u < U) ? skey[u] : 0u;
+      const bool in = k != 0u && (k & pmask) == prefix;
+      const uint64_t act = __ballot(in);
+      if (act == 0ull) continue;                       // wave-uniform
+      const uint32_t bkt = in ? (k >> shift) & 255u : 0u;
+      const unsigned long long ms = in ? (unsigned long long)fixmass(sw[u]) : 0ull;
+      const int leader = __ffsll((long long)act) - 1;
+      const uint32_t lb = __shfl(bkt, leader, 64);
+      if (__ballot(in && bkt != lb) == 0ull) {
+        unsigned long long tot = ms;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+        if (lane == leader) {
+          atomicAdd(&sm.cnt[lb], (uint32_t)__popcll(act));
+          atomicAdd(&sm.mass[lb], tot);
+        }
+      } else if (in) {
         atomicAdd(&sm.cnt[bkt], 1u);
-        atomicAdd(&sm.mass[bkt], (unsigned long long)fixmass(sw[u]));
+        atomicAdd(&sm.mass[bkt], ms);
       }
     }
     __syncthreads();
@@ -296,20 +314,36 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
 }
 
 // ---------------------------------------------------------------- expansion (A5)
+//
+// One workgroup per group.  The union list is walked in tiles of 1024 entries
+// (thread t takes entry tile*1024 + t, so the selection bytes load coalesced);
+// an entry is kept when any head kept it, its mask being the OR of the heads'
+// bits; a block scan per tile gives its position in list order.  Kept parents
+// are staged, then their children are written with consecutive threads on
+// consecutive outputs, followed by the parentless nodes of the next level.  The
+// final level writes the kept leaves themselves.  The top list (every level-L
+// node) is built the same way with no parents; that launch also checks that the
+// tree matches T.
 
 struct ExpandParams {
   const int64_t* T;
+  const int64_t* n_built;        // [L][B] (top launch only)
   const int32_t* uids; const uint32_t* umask; const int32_t* ucount; int64_t ucap;
-  const uint8_t* sel;           // [BHq][ucap]
+  const uint8_t* sel;            // [BHq][ucap]
   int32_t* nids; uint32_t* nmask; int32_t* ncount; int64_t ncap;   // next list
+  int32_t* xstage;               // [BH][xcap][2]
+  int64_t xcap;
   int32_t* status;
-  int32_t B, H_kv, G, C, level;  // level of the input list; 0 = build the top list
-  int32_t final_;                // 1: write the leaf list (no children)
+  int32_t B, H_kv, G, C, L;
+  int32_t level;                 // level of the input list; 0 = build the top list
+  int32_t final_;                // 1: write the kept leaves (no children)
   int64_t span_next;             // C^(level-1): tokens per node of the next level
   int64_t T_cap;
 };
 
-__global__ void __launch_bounds__(1024) expand_level(ExpandParams P) {
+constexpr int kExpandThreads = 1024;
+
+__global__ void __launch_bounds__(kExpandThreads) expand_level(ExpandParams P) {
   __shared__ int32_t red[16];
   const int gi = blockIdx.x;
   const int b = gi / P.H_kv;
@@ -318,66 +352,64 @@ __global__ void __launch_bounds__(1024) expand_level(ExpandParams P) {
   if (T < 0) T = 0;
   if (T > P.T_cap) T = P.T_cap;
   const uint32_t full = (P.G >= 32) ? 0xffffffffu : ((1u << P.G) - 1u);
-  const int64_t n_next = T / P.span_next;                       // nodes at the next level
+  if (P.level == 0 && tid == 0 && (gi % P.H_kv) == 0) {
+    int64_t span = 1;
+    for (int l = 1; l <= P.L; ++l) {
+      span *= P.C;
+      if (P.n_built[(int64_t)(l - 1) * P.B + b] != T / span) set_status(P.status, ZHA_ESTALE);
+    }
+  }
+  const int64_t n_next = T / P.span_next;                     // nodes at the next level
   const int64_t n_here = (P.level == 0) ? 0 : T / (P.span_next * P.C);
   const int U = (P.level == 0) ? 0 : clamp_count(P.ucount[gi], P.ucap);
-  const int per = (U + blockDim.x - 1) / blockDim.x;
-  const int u0 = tid * per, u1 = min(U, u0 + per);
-  int mine = 0;
-  for (int u = u0; u < u1; ++u) {
-    uint32_t m = 0u;
-    for (int g = 0; g < P.G; ++g)
-      m |= (P.sel[((int64_t)gi * P.G + g) * P.ucap + u] ? 1u : 0u) << g;
-    mine += m ? 1 : 0;
-  }
+  int32_t* st = P.xstage + (int64_t)gi * P.xcap * 2;
+  int32_t* ids = P.nids + (int64_t)gi * P.ncap;
+  uint32_t* msk = P.nmask + (int64_t)gi * P.ncap;
+
+  // kept entries in list order
   int nsel = 0;
-  int pos = block_exclusive_scan<int>(mine, red, &nsel);
-  const int per_entry = P.final_ ? 1 : P.C;
+  for (int base = 0; base < U; base += kExpandThreads) {
+    const int u = base + tid;
+    uint32_t m = 0u;
+    if (u < U)
+      for (int g = 0; g < P.G; ++g)
+        m |= (P.sel[((int64_t)gi * P.G + g) * P.ucap + u] ? 1u : 0u) << g;
+    int tot = 0;
+    const int pos = nsel + block_exclusive_scan<int>(m ? 1 : 0, red, &tot);
+    if (m) {
+      const int32_t id = P.uids[(int64_t)gi * P.ucap + u];
+      if (P.final_) {
+        if (pos < P.ncap) { ids[pos] = id; msk[pos] = m; }
+      } else {
+        st[2 * pos] = id;
+        st[2 * pos + 1] = (int32_t)m;
+      }
+    }
+    nsel += tot;
+  }
   int64_t n_orph = P.final_ ? 0 : (n_next - (int64_t)P.C * n_here);
   if (n_orph < 0) n_orph = 0;
-  int64_t count = (int64_t)nsel * per_entry + n_orph;
+  int64_t count = P.final_ ? nsel : (int64_t)nsel * P.C + n_orph;
   if (count > P.ncap) {
     if (tid == 0) set_status(P.status, ZHA_ECAPACITY);
     count = P.ncap;
   }
-  int32_t* ids = P.nids + (int64_t)gi * P.ncap;
-  uint32_t* msk = P.nmask + (int64_t)gi * P.ncap;
-  for (int u = u0; u < u1; ++u) {
-    uint32_t m = 0u;
-    for (int g = 0; g < P.G; ++g)
-      m |= (P.sel[((int64_t)gi * P.G + g) * P.ucap + u] ? 1u : 0u) << g;
-    if (!m) continue;
-    const int32_t id = P.uids[(int64_t)gi * P.ucap + u];
-    for (int c = 0; c < per_entry; ++c) {
-      const int64_t o = (int64_t)pos * per_entry + c;
-      if (o < count) {
-        ids[o] = P.final_ ? id : id * P.C + c;
-        msk[o] = m;
-      }
+  if (!P.final_) {
+    __syncthreads();   // staged parents visible to the whole block
+    const int64_t nch = (int64_t)nsel * P.C;
+    const int cshift = __ffs(P.C) - 1;   // C is a power of two
+    for (int64_t o = tid; o < nch && o < count; o += kExpandThreads) {
+      const int64_t pi = o >> cshift;
+      ids[o] = st[2 * pi] * P.C + (int32_t)(o & (P.C - 1));
+      msk[o] = (uint32_t)st[2 * pi + 1];
     }
-    ++pos;
-  }
-  const int64_t first_orph = (int64_t)P.C * n_here;
-  for (int64_t i = tid; i < n_orph; i += blockDim.x) {
-    const int64_t o = (int64_t)nsel * per_entry + i;
-    if (o < count) { ids[o] = (int32_t)(first_orph + i); msk[o] = full; }
+    const int64_t first_orph = (int64_t)P.C * n_here;
+    for (int64_t i = tid; i < n_orph; i += kExpandThreads) {
+      const int64_t o = nch + i;
+      if (o < count) { ids[o] = (int32_t)(first_orph + i); msk[o] = full; }
+    }
   }
   if (tid == 0) P.ncount[gi] = (int32_t)count;
-}
-
-// Stale-tree check: every level must hold T / C^l built nodes.
-__global__ void check_tree(const int64_t* T, const int64_t* n_built, int B, int C, int L,
-                           int64_t T_cap, int32_t* status) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
-  int64_t t = T[b];
-  if (t < 0) t = 0;
-  if (t > T_cap) t = T_cap;
-  int64_t span = 1;
-  for (int l = 1; l <= L; ++l) {
-    span *= C;
-    if (n_built[(int64_t)(l - 1) * B + b] != t / span) set_status(status, ZHA_ESTALE);
-  }
 }
 
 // ---------------------------------------------------------------- host
@@ -453,16 +485,15 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
   hipStream_t s = (hipStream_t)stream;
   char* base = (char*)ws;
   const int BH = cfg->B * cfg->H_kv, BHq = BH * cfg->G, L = cfg->L;
-  hipLaunchKernelGGL(check_tree, dim3((cfg->B + 63) / 64), dim3(64), 0, s, T,
-                     tree->n_built, cfg->B, cfg->C, L, cfg->T_cap, (int32_t*)ws);
   int64_t span[ZHA_MAX_L + 1];
   span[0] = 1;
   for (int l = 1; l <= L; ++l) span[l] = span[l - 1] * cfg->C;
 
   // top list: every level-L node, every head
   ExpandParams E;
-  E.T = T; E.status = (int32_t*)ws;
-  E.B = cfg->B; E.H_kv = cfg->H_kv; E.G = cfg->G; E.C = cfg->C; E.T_cap = cfg->T_cap;
+  E.T = T; E.status = (int32_t*)ws; E.n_built = tree->n_built;
+  E.B = cfg->B; E.H_kv = cfg->H_kv; E.G = cfg->G; E.C = cfg->C; E.L = L; E.T_cap = cfg->T_cap;
+  E.xstage = (int32_t*)(base + w.xstage); E.xcap = w.stage_cap;
   E.level = 0; E.final_ = 0;
   E.uids = nullptr; E.umask = nullptr; E.ucount = nullptr; E.ucap = 1; E.sel = nullptr;
   E.nids = (int32_t*)(base + w.uids[L - 1]);
@@ -470,7 +501,7 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
   E.ncount = (int32_t*)(base + w.ucount[L - 1]);
   E.ncap = w.cap[L - 1];
   E.span_next = span[L];
-  hipLaunchKernelGGL(expand_level, dim3(BH), dim3(1024), 0, s, E);
+  hipLaunchKernelGGL(expand_level, dim3(BH), dim3(kExpandThreads), 0, s, E);
 
   for (int l = L; l >= 1; --l) {
     LevelParams P = level_params(cfg, q, tree, l, p, ws, w);
@@ -498,7 +529,7 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
       E.nids = leaf_ids; E.nmask = leaf_mask; E.ncount = leaf_count;
       E.ncap = cfg->leaf_cap;
     }
-    hipLaunchKernelGGL(expand_level, dim3(BH), dim3(1024), 0, s, E);
+    hipLaunchKernelGGL(expand_level, dim3(BH), dim3(kExpandThreads), 0, s, E);
   }
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
 }

@@ -29,6 +29,7 @@ struct WsLayout {
   int64_t cap[ZHA_MAX_L];
   size_t stage = 0;        // cut staging: [B*Hq][stage_cap] (u32 key, f32 w)
   int64_t stage_cap = 0;
+  size_t xstage = 0;       // expansion staging: [B*H_kv][stage_cap] (i32 id, u32 mask)
   int32_t split_cap = 0;   // partial slots per query head
 };
 
@@ -79,6 +80,7 @@ inline WsLayout ws_layout(const zha_cfg& c) {
   if (lcap > scap) scap = lcap;
   w.stage_cap = scap;
   w.stage = off; off = align_up(off + (size_t)BHq * scap * 8, 256);
+  w.xstage = off; off = align_up(off + (size_t)BH * scap * 8, 256);
   w.route_bytes = off - w.route_off;
   w.attend_off = off;
   w.split_cap = split_capacity(c);
