@@ -23,6 +23,7 @@ namespace zha {
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWavesPerWg = 4;
 constexpr int kMaxGroups = 2048;
@@ -166,15 +167,16 @@ __device__ inline int find_group(const int32_t* prefix, int BH, int item) {
 }
 
 // WG-level merge of the per-wave states into one partial per query head.
-template <int D>
-__device__ inline void write_partial(const AttendParams& P, AttendSmem<D>& sm, int gi,
-                                     int item) {
+template <int D, int NH>
+__device__ inline void write_partial_state(const AttendParams& P,
+                                           const float (*state)[NH][D + 2], int gi,
+                                           int item) {
   const int G = P.G;
   for (int idx = threadIdx.x; idx < G * (D + 2); idx += blockDim.x) {
     const int g = idx / (D + 2), c = idx % (D + 2);
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWavesPerWg; ++w) M = fmaxf(M, sm.state[w][g][0]);
+    for (int w = 0; w < kWavesPerWg; ++w) M = fmaxf(M, state[w][g][0]);
     float v;
     if (c == 0) {
       v = M;
@@ -183,14 +185,20 @@ __device__ inline void write_partial(const AttendParams& P, AttendSmem<D>& sm, i
       if (M != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < kWavesPerWg; ++w) {
-          const float mw = sm.state[w][g][0];
-          if (mw != -INFINITY) v += sm.state[w][g][c] * exp2f(mw - M);
+          const float mw = state[w][g][0];
+          if (mw != -INFINITY) v += state[w][g][c] * exp2f(mw - M);
         }
       }
     }
     const int64_t head = (int64_t)gi * G + g;
     P.part[(head * P.split_cap + item) * (D + 2) + c] = v;
   }
+}
+
+template <int D>
+__device__ inline void write_partial(const AttendParams& P, AttendSmem<D>& sm, int gi,
+                                     int item) {
+  write_partial_state<D, 16>(P, sm.state, gi, item);
 }
 
 // Online-softmax state of one wave for the bf16 path.  Scores arrive in MFMA
@@ -202,37 +210,248 @@ struct WaveSoftmax {
 
 // ---------------------------------------------------------------- bf16 path
 //
-// QK^T on MFMA 16x16x32 bf16: rows = query heads of the group (padded to 16),
+// QK^T on MFMA 16x16x32 bf16: rows = the group's query heads (padded to 16),
 // columns = 16 keys, contraction over d in steps of 32.  The fp32 query (times
-// scale*log2e) is split into three bf16 parts hi + mid + lo, whose sum carries
-// the fp32 value to ~2^-24 relative; the three products accumulate in fp32.
-// Lane l supplies row/column l%16 and the 8 consecutive dims s*32 + (l/16)*8 of
-// contraction step s for both operands, so each lane's K load is 16 contiguous
-// bytes.  P V runs on VALU: lane owns 8 consecutive dims of a few key rows.
+// scale*log2e) is split into two bf16 parts hi + lo, whose sum carries it to
+// ~2^-17 relative (score error ~1e-4 at d = 128, far inside what bf16 keys
+// allow); both products accumulate in fp32.  Lane l supplies row/column l%16
+// and the 8 consecutive dims s*32 + (l/16)*8 of step s for both operands, so
+// each lane's K load is 16 contiguous bytes.  P V runs on VALU: lane owns 8
+// consecutive dims of a few key rows; V rows load 16 bytes per lane, coalesced.
+//
+// Each wave walks 16-key chunks of an item (chunks w, w+4, ...).  When every
+// chunk is 16 consecutive cache rows under one head mask (dense, or leaves of
+// C >= 16 keys) the chunk's address and mask are wave-uniform and the next
+// chunk's K/V loads are issued before the current chunk is computed (two
+// register buffers).  Otherwise (the tail item with the sink and the open chunk,
+// or C < 16) each key's row is looked up per lane.  The item's leaf entries are
+// staged in LDS once.  The running max is raised lazily: only when a chunk's max
+// exceeds it by more than kLazy (log2 units) are o and l rescaled, so
+// probabilities stay below 2^kLazy.
+
+constexpr float kLazy = 8.0f;
+constexpr int kItemKeys = kTilesPerItem * kTileKeys;   // 1024
 
 template <int D, int GP>
+struct AttendSmemB {
+  int32_t item_prefix[kMaxGroups + 1];
+  int32_t scan[16];
+  int32_t lid[kItemKeys / 2 + 2];               // leaf ids of the item (C >= 2)
+  uint32_t lmask[kItemKeys / 2 + 2];
+  float p[kWavesPerWg][16][GP];                 // probabilities per key, head
+  float alpha[kWavesPerWg][16];
+  float state[kWavesPerWg][GP][D + 2];
+};
+
+// Where the keys of one work item come from.
+struct ItemView {
+  int tail;           // 1: the sink + open-chunk item
+  int64_t kbase;      // first list key of the item
+  int nkeys;          // keys in the item
+  int64_t first;      // first leaf entry staged in LDS
+  int cshift;         // log2 C
+  uint32_t smask;     // sink mask (tail item)
+};
+
+template <typename SM>
+__device__ inline Slot item_slot(const AttendParams& P, const SM& sm, const GroupInfo& g,
+                                 const ItemView& it, int e, uint32_t full) {
+  Slot s{0, 0u};
+  if (e >= it.nkeys) return s;
+  if (it.tail) {
+    if (e == 0) { s.mask = it.smask; }
+    else {
+      const int64_t t = (int64_t)g.n1 * P.C + (e - 1);
+      if (t < g.T) { s.tok = (int32_t)t; s.mask = full; }
+    }
+    return s;
+  }
+  const int64_t gk = it.kbase + e;
+  if (P.leaf_ids == nullptr) {
+    s.tok = (int32_t)gk;
+    s.mask = full;
+    return s;
+  }
+  const int loc = (int)((gk >> it.cshift) - it.first);
+  s.tok = sm.lid[loc] * P.C + (int32_t)(gk & (P.C - 1));
+  s.mask = sm.lmask[loc];
+  return s;
+}
+
+template <int D>
+struct ChunkBuf {
+  u32x4_t k[D / 32];
+  u32x4_t v[16 / (kWave / (D / 8))];
+  uint32_t kmask;     // head mask of this lane's K column key
+  uint32_t vok;       // bit i: V row i holds an attended key
+};
+
+// General chunk load: rows looked up per lane.
+template <int D, typename SM>
+__device__ inline void load_chunk_any(const AttendParams& P, const SM& sm, const GroupInfo& g,
+                                      const ItemView& it, int chunk, uint32_t full,
+                                      int64_t kv_base, int lane, ChunkBuf<D>& buf) {
+  constexpr int KSTEPS = D / 32, LPR = D / 8, RPI = kWave / LPR, VL = 16 / RPI;
+  const uint16_t* Kb = (const uint16_t*)P.K;
+  const uint16_t* Vb = (const uint16_t*)P.V;
+  const Slot ks = item_slot(P, sm, g, it, chunk * 16 + (lane & 15), full);
+  buf.kmask = ks.mask;
+  const uint16_t* krow = Kb + (kv_base + ks.tok) * D + (lane >> 4) * 8;
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) buf.k[s] = *(const u32x4_t*)(krow + s * 32);
+  buf.vok = 0u;
+#pragma unroll
+  for (int i = 0; i < VL; ++i) {
+    const Slot vs = item_slot(P, sm, g, it, chunk * 16 + RPI * i + lane / LPR, full);
+    buf.v[i] = *(const u32x4_t*)(Vb + (kv_base + vs.tok) * D + (lane % LPR) * 8);
+    buf.vok |= (vs.mask ? 1u : 0u) << i;
+  }
+}
+
+// Contiguous chunk load: rows row0 .. row0+nv-1 of the group under one head mask
+// (row0, nv, hm wave-uniform).  Lanes past nv re-read row row0 and are masked.
+template <int D>
+__device__ inline void load_chunk_rows(const uint16_t* klane, const uint16_t* vlane, int lane,
+                                       int64_t row0, int nv, uint32_t hm, ChunkBuf<D>& buf) {
+  constexpr int KSTEPS = D / 32, LPR = D / 8, RPI = kWave / LPR, VL = 16 / RPI;
+  const int kr = lane & 15;
+  const int kof = kr < nv ? kr : 0;
+  const uint16_t* kp = klane + (row0 + kof) * D;
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) buf.k[s] = *(const u32x4_t*)(kp + s * 32);
+  buf.vok = 0u;
+#pragma unroll
+  for (int i = 0; i < VL; ++i) {
+    const int vr = RPI * i + lane / LPR;
+    const int vof = vr < nv ? vr : 0;
+    buf.v[i] = *(const u32x4_t*)(vlane + (row0 + vof) * D);
+    buf.vok |= (vr < nv && hm != 0u ? 1u : 0u) << i;
+  }
+  buf.kmask = kr < nv ? hm : 0u;
+}
+
+template <int D, int GP>
+__device__ inline void compute_chunk(AttendSmemB<D, GP>& sm, const ChunkBuf<D>& buf,
+                                     const bf16x8_t* a_hi, const bf16x8_t* a_lo,
+                                     int lane, int wave,
+                                     float* m_run, float* l_run, float (*o)[8]) {
+  constexpr int KSTEPS = D / 32, LPR = D / 8, RPI = kWave / LPR, VL = 16 / RPI;
+  const int hrow = (lane >> 4) * 4;
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, buf.k[s]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[s], kb, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[s], kb, acc, 0, 0, 0);
+  }
+  // acc[i]: head hrow+i, key lane%16
+  float cm[4];
+  bool need = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool ok = (buf.kmask >> (hrow + i)) & 1u;
+    const float sc = ok ? acc[i] : -INFINITY;
+    acc[i] = sc;
+    float v = sc;
+    v = fmaxf(v, swz_xor<1>(v));
+    v = fmaxf(v, swz_xor<2>(v));
+    v = fmaxf(v, swz_xor<4>(v));
+    v = fmaxf(v, swz_xor<8>(v));
+    cm[i] = v;
+    need = need || (v > m_run[i] + kLazy);
+  }
+  if (__ballot(need) != 0ull) {           // wave-uniform: raise some running maxima
+    float al[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mnew = (cm[i] > m_run[i] + kLazy) ? cm[i] : m_run[i];
+      al[i] = (mnew == -INFINITY) ? 1.0f : exp2f(m_run[i] - mnew);
+      l_run[i] *= al[i];
+      m_run[i] = mnew;
+    }
+    if ((lane & 15) == 0 && hrow < GP) {
+      const f32x4_t av = {al[0], al[1], al[2], al[3]};
+      *(f32x4_t*)&sm.alpha[wave][hrow] = av;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int q4 = 0; q4 < GP / 4; ++q4) {
+      const f32x4_t av = *(const f32x4_t*)&sm.alpha[wave][q4 * 4];
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[q4 * 4 + hh][j] *= av[hh];
+    }
+  }
+  f32x4_t pv4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float pv = (acc[i] == -INFINITY) ? 0.0f : exp2f(acc[i] - m_run[i]);
+    pv4[i] = pv;
+    l_run[i] += pv;
+  }
+  if (hrow < GP) *(f32x4_t*)&sm.p[wave][lane & 15][hrow] = pv4;
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < VL; ++i) {
+    const int key = RPI * i + lane / LPR;
+    float vf[8];
+    const bool ok = (buf.vok >> i) & 1u;   // rows of keys nobody attends may hold anything
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = ok ? buf.v[i][j] : 0u;
+      vf[2 * j] = bf16_lo(w);
+      vf[2 * j + 1] = bf16_hi(w);
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < GP / 4; ++q4) {
+      const f32x4_t pp = *(const f32x4_t*)&sm.p[wave][key][q4 * 4];
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[q4 * 4 + hh][j] += pp[hh] * vf[j];
+    }
+  }
+  wave_lds_sync();
+}
+
+template <int D, int GP, bool CONTIG>
 __global__ void __launch_bounds__(256)
 attend_partial_bf16(AttendParams P) {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(GP == 4 || GP == 8 || GP == 16, "padded heads");
-  constexpr int KSTEPS = D / 32;              // MFMA K steps
-  constexpr int LPR = D / 8;                  // lanes per V row (16 B each)
-  constexpr int RPI = kWave / LPR;            // V rows per load instruction
-  constexpr int VLOADS = kTileKeys / RPI;     // V loads per lane per tile
-  __shared__ AttendSmem<D> sm;
+  constexpr int KSTEPS = D / 32;
+  constexpr int LPR = D / 8;
+  constexpr int RPI = kWave / LPR;
+  __shared__ AttendSmemB<D, GP> sm;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int BH = P.B * P.H_kv;
-  const int total = plan_items<D>(P, sm);
   const uint32_t full = (P.G >= 32) ? 0xffffffffu : ((1u << P.G) - 1u);
-  const int hrow = (lane >> 4) * 4;           // first head row this lane holds
+  const int hrow = (lane >> 4) * 4;
+  const int cshift = __ffs(P.C) - 1;
 
-  const uint16_t* Kb = (const uint16_t*)P.K;
-  const uint16_t* Vb = (const uint16_t*)P.V;
+  // work items of every group, prefix-summed into LDS
+  int total;
+  {
+    const int per = (BH + blockDim.x - 1) / blockDim.x;
+    const int g0 = threadIdx.x * per;
+    int mine = 0;
+    for (int k = 0; k < per; ++k)
+      if (g0 + k < BH) mine += group_info(P, g0 + k).items;
+    int acc = block_exclusive_scan<int>(mine, sm.scan, &total);
+    for (int k = 0; k < per; ++k)
+      if (g0 + k < BH) {
+        sm.item_prefix[g0 + k] = acc;
+        acc += group_info(P, g0 + k).items;
+      }
+    if (threadIdx.x == 0) sm.item_prefix[BH] = total;
+    __syncthreads();
+  }
 
   int cur_group = -1;
-  bf16x8_t a_hi[KSTEPS], a_mid[KSTEPS], a_lo[KSTEPS];
+  bf16x8_t a_hi[KSTEPS], a_lo[KSTEPS];
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int gi = find_group(sm.item_prefix, BH, item);
@@ -241,11 +460,11 @@ attend_partial_bf16(AttendParams P) {
 
     if (gi != cur_group) {
       cur_group = gi;
-      const int row = lane & 15;          // head within the group
-      const int kg = lane >> 4;           // contraction group of 8 dims
+      const int row = lane & 15;
+      const int kg = lane >> 4;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        bf16x8_t hi, mid, lo;
+        bf16x8_t hi, lo;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           float x = 0.0f;
@@ -253,31 +472,46 @@ attend_partial_bf16(AttendParams P) {
             x = P.q[((int64_t)gi * P.G + row) * D + s * 32 + kg * 8 + j] * P.qscale;
           const uint16_t h16 = f32_to_bf16_rne(x);
           const float r1 = x - __uint_as_float((uint32_t)h16 << 16);
-          const uint16_t m16 = f32_to_bf16_rne(r1);
-          const float r2 = r1 - __uint_as_float((uint32_t)m16 << 16);
-          const uint16_t l16 = f32_to_bf16_rne(r2);
+          const uint16_t l16 = f32_to_bf16_rne(r1);
           hi[j] = __builtin_bit_cast(__bf16, h16);
-          mid[j] = __builtin_bit_cast(__bf16, m16);
           lo[j] = __builtin_bit_cast(__bf16, l16);
         }
-        a_hi[s] = hi; a_mid[s] = mid; a_lo[s] = lo;
+        a_hi[s] = hi; a_lo[s] = lo;
       }
     }
 
-    const bool tail = (li == g.items - 1);
-    const uint32_t smask = tail ? sink_mask(P, gi, g, full) : 0u;
-    // tiles of this wave: tail item -> wave 0 takes the single tail tile (-1)
-    int tile, t_end, t_step;
-    if (tail) { tile = (wave == 0) ? -1 : 0; t_end = 0; t_step = 1; }
-    else {
-      tile = li * kTilesPerItem + wave;
-      t_end = min(g.tiles, (li + 1) * kTilesPerItem);
-      t_step = kWavesPerWg;
+    ItemView it;
+    it.tail = (li == g.items - 1) ? 1 : 0;
+    it.cshift = cshift;
+    it.smask = 0u;
+    it.first = 0;
+    if (it.tail) {
+      it.kbase = 0;
+      it.nkeys = kTileKeys;
+      it.smask = sink_mask(P, gi, g, full);
+    } else {
+      it.kbase = (int64_t)li * kItemKeys;
+      const int64_t left = (int64_t)g.U * P.C - it.kbase;
+      it.nkeys = (int)(left < kItemKeys ? left : kItemKeys);
+      if (P.leaf_ids != nullptr) {
+        it.first = it.kbase >> cshift;
+        const int64_t last = (it.kbase + it.nkeys - 1) >> cshift;
+        const int cnt = (int)(last - it.first + 1);
+        for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
+          const int64_t off = (int64_t)gi * P.leaf_cap + it.first + i;
+          int32_t leaf = P.leaf_ids[off];
+          uint32_t m = P.leaf_mask[off] & full;
+          if (leaf < 0 || leaf >= g.n1) { leaf = 0; m = 0u; }
+          sm.lid[i] = leaf;
+          sm.lmask[i] = m;
+        }
+      }
     }
+    __syncthreads();
 
-    WaveSoftmax st;
+    float m_run[4], l_run[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { st.m[i] = -INFINITY; st.l[i] = 0.0f; }
+    for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.0f; }
     float o[GP][8];
 #pragma unroll
     for (int hh = 0; hh < GP; ++hh)
@@ -285,128 +519,67 @@ attend_partial_bf16(AttendParams P) {
       for (int j = 0; j < 8; ++j) o[hh][j] = 0.0f;
 
     const int64_t kv_base = (int64_t)gi * P.T_cap;
-    for (; tile < t_end; tile += t_step) {
-      const Slot my = slot_of(P, gi, g, tile, lane, full, smask);
-      const int my_valid = my.mask != 0u ? 1 : 0;
-
-      // K rows of the four 16-slot column blocks
-      u32x4_t kraw[4][KSTEPS];
-      uint32_t kmask[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int slot = t * 16 + (lane & 15);
-        const int tok = __shfl(my.tok, slot, 64);
-        kmask[t] = (uint32_t)__shfl((int)my.mask, slot, 64);
-        const uint16_t* row = Kb + (kv_base + tok) * D + (lane >> 4) * 8;
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-          kraw[t][s] = *(const u32x4_t*)(row + s * 32);
-      }
-      // V rows: slot = RPI * i + lane / LPR, dims (lane % LPR) * 8 .. + 8
-      u32x4_t vraw[VLOADS];
-#pragma unroll
-      for (int i = 0; i < VLOADS; ++i) {
-        const int slot = RPI * i + lane / LPR;
-        const int tok = __shfl(my.tok, slot, 64);
-        const int ok = __shfl(my_valid, slot, 64);
-        const u32x4_t v = *(const u32x4_t*)(Vb + (kv_base + tok) * D + (lane % LPR) * 8);
-        const u32x4_t z = {0u, 0u, 0u, 0u};
-        vraw[i] = ok ? v : z;
-      }
-
-      // scores (log2 units): acc[t][i] = head hrow+i, slot t*16 + lane%16
-      f32x4_t acc[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kraw[t][s]);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[s], kb, c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_mid[s], kb, c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[s], kb, c, 0, 0, 0);
+    if constexpr (CONTIG) {
+      // Chunks of consecutive rows.  Regular item: 16-key chunks of the list.
+      // Tail item: chunk 0 is the sink row, then the open chunk in 16-row pieces.
+      const int64_t open0 = (int64_t)g.n1 * P.C;
+      const int open_len = (int)(g.T - open0);
+      const int nchunks = it.tail ? 1 + (open_len + 15) / 16 : (it.nkeys + 15) / 16;
+      const uint16_t* klane = (const uint16_t*)P.K + kv_base * D + (lane >> 4) * 8;
+      const uint16_t* vlane = (const uint16_t*)P.V + kv_base * D + (lane % LPR) * 8;
+      auto chunk_src = [&](int c, int64_t& row0, int& nv, uint32_t& hm) {
+        if (it.tail) {
+          if (c == 0) { row0 = 0; nv = 1; hm = it.smask; }
+          else {
+            row0 = open0 + 16 * (c - 1);
+            nv = min(16, (int)(g.T - row0));
+            hm = full;
+          }
+        } else {
+          const int64_t gk = it.kbase + (int64_t)c * 16;
+          nv = min(16, it.nkeys - 16 * c);   // partial only when C < 16 (dense)
+          if (P.leaf_ids == nullptr) { row0 = gk; hm = full; }
+          else {
+            const int loc = (int)((gk >> cshift) - it.first);
+            row0 = (int64_t)sm.lid[loc] * P.C + (gk & (P.C - 1));
+            hm = sm.lmask[loc];
+          }
         }
-        acc[t] = c;
-      }
-
-      // mask, per-head max over the 64 slots, online-softmax update
-      float alpha[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int head = hrow + i;
-        float v = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bool ok = (kmask[t] >> head) & 1u;
-          const float sc = ok ? acc[t][i] : -INFINITY;
-          acc[t][i] = sc;
-          v = fmaxf(v, sc);
+        row0 = __builtin_amdgcn_readfirstlane((int)row0);
+        hm = __builtin_amdgcn_readfirstlane(hm);
+      };
+      // rotating buffer: chunk c+4's loads are in flight while chunk c computes
+      ChunkBuf<D> cur, nxt;
+      int64_t r0; int nv; uint32_t hm;
+      int c = wave;
+      if (c < nchunks) { chunk_src(c, r0, nv, hm); load_chunk_rows<D>(klane, vlane, lane, r0, nv, hm, cur); }
+      for (; c < nchunks; c += kWavesPerWg) {
+        const bool more = c + kWavesPerWg < nchunks;
+        if (more) {
+          chunk_src(c + kWavesPerWg, r0, nv, hm);
+          load_chunk_rows<D>(klane, vlane, lane, r0, nv, hm, nxt);
         }
-        v = fmaxf(v, swz_xor<1>(v));
-        v = fmaxf(v, swz_xor<2>(v));
-        v = fmaxf(v, swz_xor<4>(v));
-        v = fmaxf(v, swz_xor<8>(v));
-        const float mnew = fmaxf(st.m[i], v);
-        alpha[i] = (mnew == -INFINITY) ? 1.0f : exp2f(st.m[i] - mnew);
-        float ls = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float pv = (acc[t][i] == -INFINITY) ? 0.0f : exp2f(acc[t][i] - mnew);
-          acc[t][i] = pv;
-          ls += pv;
-        }
-        st.l[i] = st.l[i] * alpha[i] + ls;
-        st.m[i] = mnew;
+        compute_chunk<D, GP>(sm, cur, a_hi, a_lo, lane, wave, m_run, l_run, o);
+        if (more) cur = nxt;
       }
-      // hand probabilities and rescale factors to the PV layout through LDS
-      if (hrow < GP) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          *(f32x4_t*)&sm.p[wave][t * 16 + (lane & 15)][hrow] = acc[t];
-        if ((lane & 15) == 0) {
-          const f32x4_t av = {alpha[0], alpha[1], alpha[2], alpha[3]};
-          *(f32x4_t*)&sm.alpha[wave][hrow] = av;
-        }
+    } else {
+      const int nchunks = (it.nkeys + 15) / 16;
+      for (int k = wave; k < nchunks; k += kWavesPerWg) {
+        ChunkBuf<D> A;
+        load_chunk_any<D>(P, sm, g, it, k, full, kv_base, lane, A);
+        compute_chunk<D, GP>(sm, A, a_hi, a_lo, lane, wave, m_run, l_run, o);
       }
-      wave_lds_sync();
-#pragma unroll
-      for (int q4 = 0; q4 < GP / 4; ++q4) {
-        const f32x4_t av = *(const f32x4_t*)&sm.alpha[wave][q4 * 4];
-#pragma unroll
-        for (int hh = 0; hh < 4; ++hh)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) o[q4 * 4 + hh][j] *= av[hh];
-      }
-#pragma unroll
-      for (int i = 0; i < VLOADS; ++i) {
-        const int slot = RPI * i + lane / LPR;
-        float vf[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vf[2 * j] = bf16_lo(vraw[i][j]);
-          vf[2 * j + 1] = bf16_hi(vraw[i][j]);
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < GP / 4; ++q4) {
-          const f32x4_t pv = *(const f32x4_t*)&sm.p[wave][slot][q4 * 4];
-#pragma unroll
-          for (int hh = 0; hh < 4; ++hh)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o[q4 * 4 + hh][j] += pv[hh] * vf[j];
-        }
-      }
-      wave_lds_sync();
     }
 
-    // wave totals: l over the 16 columns, o over the V row groups
+    // wave totals: l over the 16 key columns, o over the V row groups
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = st.l[i];
+      float v = l_run[i];
       v += swz_xor<1>(v);
       v += swz_xor<2>(v);
       v += swz_xor<4>(v);
       v += swz_xor<8>(v);
-      st.l[i] = v;
+      l_run[i] = v;
     }
 #pragma unroll
     for (int hh = 0; hh < GP; ++hh)
@@ -421,8 +594,8 @@ attend_partial_bf16(AttendParams P) {
     if ((lane & 15) == 0 && hrow < GP) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sm.state[wave][hrow + i][0] = st.m[i];
-        sm.state[wave][hrow + i][1] = st.l[i];
+        sm.state[wave][hrow + i][0] = m_run[i];
+        sm.state[wave][hrow + i][1] = l_run[i];
       }
     }
     if (lane < LPR) {
@@ -432,7 +605,7 @@ attend_partial_bf16(AttendParams P) {
         for (int j = 0; j < 8; ++j) sm.state[wave][hh][2 + lane * 8 + j] = o[hh][j];
     }
     __syncthreads();
-    write_partial<D>(P, sm, gi, li);
+    write_partial_state<D, GP>(P, sm.state, gi, li);
     __syncthreads();
   }
 }
@@ -550,13 +723,16 @@ attend_partial_f32(AttendParams P) {
 // sums.  Wave w of the workgroup takes partials w, w+4, ... (lanes over dims, the
 // loads of successive partials are independent); the four wave sums are added in
 // a fixed order, so the result is deterministic.
+constexpr int kMergeWaves = 16;
+
 template <int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kMergeWaves * 64)
 attend_merge(AttendParams P, float* out, float* lse) {
   constexpr int DPL = D / kWave;
-  __shared__ float red[16];
-  __shared__ float acc_o[kWavesPerWg][D];
-  __shared__ float acc_l[kWavesPerWg];
+  constexpr int U = 8;                       // partials in flight per wave
+  __shared__ float red[kMergeWaves];
+  __shared__ float acc_o[kMergeWaves][D];
+  __shared__ float acc_l[kMergeWaves];
   const int head = blockIdx.x;              // b * Hq + j
   const int gi = head / P.G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -565,18 +741,29 @@ attend_merge(AttendParams P, float* out, float* lse) {
   const float* base = P.part + (int64_t)head * P.split_cap * (D + 2);
   float M = -INFINITY;
   for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, base[(int64_t)i * (D + 2)]);
-  M = block_reduce_max<float>(M, red);
+  M = block_max_f<kMergeWaves>(M, red);
   float l = 0.0f, o[DPL];
 #pragma unroll
   for (int j = 0; j < DPL; ++j) o[j] = 0.0f;
   if (M != -INFINITY) {
-#pragma unroll 4
-    for (int i = wave; i < n; i += kWavesPerWg) {
-      const float* pi = base + (int64_t)i * (D + 2);
-      const float w = exp2f(pi[0] - M);       // 0 for an empty partial (m = -inf)
-      l += pi[1] * w;
+    for (int i0 = wave; i0 < n; i0 += kMergeWaves * U) {
+      float mi[U], li[U], oi[U][DPL];
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) o[j] += pi[2 + lane + j * kWave] * w;
+      for (int k = 0; k < U; ++k) {
+        const int i = i0 + k * kMergeWaves;
+        const float* pi = base + (int64_t)(i < n ? i : 0) * (D + 2);
+        mi[k] = (i < n) ? pi[0] : -INFINITY;
+        li[k] = pi[1];
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) oi[k][j] = pi[2 + lane + j * kWave];
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const float w = exp2f(mi[k] - M);      // 0 for an empty or absent partial
+        l += (w != 0.0f) ? li[k] * w : 0.0f;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) o[j] += (w != 0.0f) ? oi[k][j] * w : 0.0f;
+      }
     }
   }
 #pragma unroll
@@ -586,7 +773,7 @@ attend_merge(AttendParams P, float* out, float* lse) {
   for (int c = threadIdx.x; c < D; c += blockDim.x) {
     float L = 0.0f, Ov = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWavesPerWg; ++w) { L += acc_l[w]; Ov += acc_o[w][c]; }
+    for (int w = 0; w < kMergeWaves; ++w) { L += acc_l[w]; Ov += acc_o[w][c]; }
     out[(int64_t)head * D + c] = (L > 0.0f) ? Ov / L : 0.0f;
     if (c == 0) lse[head] = (L > 0.0f) ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
@@ -596,10 +783,15 @@ attend_merge(AttendParams P, float* out, float* lse) {
 
 template <int D, int GP>
 static void launch_partial(const AttendParams& P, int kv_dtype, int grid, hipStream_t s) {
-  if (kv_dtype == ZHA_BF16)
-    hipLaunchKernelGGL((attend_partial_bf16<D, GP>), dim3(grid), dim3(256), 0, s, P);
-  else
+  const bool contig = (P.leaf_ids == nullptr) || (P.C >= 16);
+  if (kv_dtype == ZHA_BF16) {
+    if (contig)
+      hipLaunchKernelGGL((attend_partial_bf16<D, GP, true>), dim3(grid), dim3(256), 0, s, P);
+    else
+      hipLaunchKernelGGL((attend_partial_bf16<D, GP, false>), dim3(grid), dim3(256), 0, s, P);
+  } else {
     hipLaunchKernelGGL((attend_partial_f32<D, GP>), dim3(grid), dim3(256), 0, s, P);
+  }
 }
 
 template <int D>
@@ -644,10 +836,10 @@ static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
   const int BHq = cfg->B * cfg->H_kv * cfg->G;
   if (cfg->d == 64) {
     launch_partial_g<64>(P, cfg->kv_dtype, grid, s);
-    hipLaunchKernelGGL((attend_merge<64>), dim3(BHq), dim3(256), 0, s, P, out, lse);
+    hipLaunchKernelGGL((attend_merge<64>), dim3(BHq), dim3(kMergeWaves * 64), 0, s, P, out, lse);
   } else {
     launch_partial_g<128>(P, cfg->kv_dtype, grid, s);
-    hipLaunchKernelGGL((attend_merge<128>), dim3(BHq), dim3(256), 0, s, P, out, lse);
+    hipLaunchKernelGGL((attend_merge<128>), dim3(BHq), dim3(kMergeWaves * 64), 0, s, P, out, lse);
   }
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
 }

@@ -13,12 +13,16 @@
 // candidates; the next level's union list is expanded from the OR of the heads'
 // selections.  Everything stays on the device between levels.
 //
-// The top-p cut needs only the threshold, not a full sort: an MSD radix pass
-// over the order-preserving 32-bit image of the fp32 scores histograms count and
-// mass per 8-bit digit and keeps the digit where the running mass (from the top)
-// first reaches p * W; four passes fix the threshold score, ties at it are taken
-// in ascending id order.  Masses are w = exp(s - max s) in fp32, accumulated as
-// 64-bit fixed point (w * 2^40) with integer atomics, so the cut is deterministic.
+// The top-p cut needs only the threshold, not a full sort.  Candidates are
+// histogrammed (count and mass) over 2048 buckets of relative score
+// floor((max s - s) * 64), which is monotone in the score, so every bucket holds
+// a contiguous stretch of the descending order; a block scan finds the bucket
+// where the running mass first reaches p * W, and only that bucket is sorted
+// exactly by (score desc, id asc) to place the cut.  A bucket too large to sort
+// (near-equal scores) falls back to an MSD radix select over the order-preserving
+// 32-bit image of the scores, four 8-bit digits, ties taken by ascending id.
+// Masses are w = exp(s - max s) in fp32, accumulated as 64-bit fixed point
+// (w * 2^40) with integer atomics, so the cut is deterministic.
 #include "zha_internal.hpp"
 
 #include <float.h>
@@ -37,6 +41,7 @@ struct LevelParams {
   float* scores;               // [BHq][ucap]
   uint8_t* sel;                // [BHq][ucap]
   int32_t* kept;               // [BHq]
+  uint32_t* selor;             // [BH][ucap] OR of kept bits, or null
   uint32_t* stage;             // [BHq][stage_cap][2] (key, w bits) for long lists
   int64_t stage_cap;
   int32_t* status;
@@ -100,6 +105,7 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
 
   const int nwaves = gridDim.x * (blockDim.x >> 6);
   for (int u = blockIdx.x * (blockDim.x >> 6) + wave; u < U; u += nwaves) {
+    if (P.selor != nullptr && lane == 0) P.selor[(int64_t)gi * P.ucap + u] = 0u;
     const int node = P.uids[(int64_t)gi * P.ucap + u];
     if (node < 0 || node >= P.ncap) {   // not a node of this tree: never selected
       if (lane < P.G) P.scores[((int64_t)gi * P.G + lane) * P.ucap + u] = -INFINITY;
@@ -150,23 +156,53 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
 
 constexpr int kCutThreads = 1024;
 constexpr int kCutLds = 16384;         // entries staged in LDS; longer lists use the workspace
-constexpr double kFix = 1099511627776.0;  // 2^40
 
-__device__ inline uint64_t fixmass(float w) { return (uint64_t)((double)w * kFix); }
+// w * 2^40 truncated to an integer, for 0 <= w <= 1, from the fp32 bits: the
+// 24-bit mantissa shifted by (exponent + 17).  Equal to (uint64)((double)w * 2^40).
+__device__ inline uint64_t fixmass(float w) {
+  const uint32_t b = __float_as_uint(w);
+  const int sh = (int)(b >> 23) - 127 + 17;
+  if (b == 0u || sh <= -24) return 0ull;
+  const uint64_t m = (uint64_t)((b & 0x7fffffu) | 0x800000u);
+  return sh >= 0 ? (m << sh) : (m >> (-sh));
+}
+
+// Estimated mass exp(s - max) on the hardware exp2.
+__device__ inline float mass_of(float s, float mx) {
+  return __builtin_amdgcn_exp2f((s - mx) * 1.4426950408889634f);
+}
 
 __device__ inline float sanitize(float s) { return isfinite(s) ? s : -FLT_MAX; }
+
+constexpr int kRelBuckets = 2048;
+constexpr float kRelScale = 64.0f;     // buckets per unit of score
+constexpr int kSortMax = 1024;         // largest crossing bucket sorted exactly
 
 struct CutSmem {
   uint32_t key[kCutLds];
   float w[kCutLds];
-  uint32_t cnt[256];
-  unsigned long long mass[256];
+  union {
+    struct { uint32_t cnt[kRelBuckets]; unsigned long long mass[kRelBuckets]; } rel;
+    struct { uint32_t cnt[256]; unsigned long long mass[256]; } rad;
+    unsigned long long sortbuf[kSortMax];
+  } u;
   float redf[16];
   unsigned long long redu[16];
   int32_t redi[16];
   uint32_t bucket;
+  int32_t first;
+  int32_t count;
   unsigned long long above;
 };
+
+__device__ inline float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ inline int rel_bucket(float s, float mx) {
+  const float r = (mx - s) * kRelScale;
+  return r >= (float)(kRelBuckets - 1) ? kRelBuckets - 1 : (int)r;
+}
 
 __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
   __shared__ CutSmem sm;
@@ -182,33 +218,204 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
   uint32_t* skey = lds ? sm.key : P.stage + (int64_t)head * P.stage_cap * 2;
   float* sw = lds ? sm.w : (float*)(P.stage + (int64_t)head * P.stage_cap * 2 + P.stage_cap);
 
-  // max score and candidate count of this head
-  float mx = -FLT_MAX;
+  uint32_t* selor = P.selor ? P.selor + (int64_t)gi * P.ucap : nullptr;
+  // Lists that fit keep this thread's scores (entries j*1024 + tid) in registers
+  // across every pass; all loads are issued before any is used.
+  constexpr int PER = kCutLds / kCutThreads;
+  float sv[PER];
+  float mx = -INFINITY;
   int ncand = 0;
-  for (int u = tid; u < U; u += kCutThreads)
-    if (mk[u] & bit) { mx = fmaxf(mx, sanitize(sc[u])); ++ncand; }
-  mx = block_reduce_max<float>(mx, sm.redf);
-  ncand = block_reduce_sum<int>(ncand, sm.redi);
+  if (lds) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int u = j * kCutThreads + tid;
+      const int uu = u < U ? u : 0;         // in bounds: loads never wait on each other
+      const uint32_t m = mk[uu];
+      const float sj = sc[uu];
+      sv[j] = (u < U && (m & bit)) ? sanitize(sj) : -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (sv[j] != -INFINITY) { mx = fmaxf(mx, sv[j]); ++ncand; }
+  } else {
+    for (int u = tid; u < U; u += kCutThreads)
+      if (mk[u] & bit) { mx = fmaxf(mx, sanitize(sc[u])); ++ncand; }
+  }
+  constexpr int NW = kCutThreads / kWave;
+  mx = block_max_f<NW>(mx, sm.redf);
+  ncand = (int)block_sum<NW, uint32_t>((uint32_t)ncand, (uint32_t*)sm.redi);
 
   if (ncand == 0 || P.p >= 1.0f) {
-    for (int u = tid; u < U; u += kCutThreads) out[u] = (P.p >= 1.0f && (mk[u] & bit)) ? 1 : 0;
+    for (int u = tid; u < U; u += kCutThreads) {
+      const bool s1 = P.p >= 1.0f && (mk[u] & bit);
+      out[u] = s1 ? 1 : 0;
+      if (s1 && selor) atomicOr(&selor[u], bit);
+    }
     if (tid == 0) P.kept[head] = (P.p >= 1.0f) ? ncand : 0;
     return;
   }
 
-  // stage (key, w); non-candidates get w = 0 and key 0 (never above the threshold)
-  unsigned long long wsum = 0;
-  for (int u = tid; u < U; u += kCutThreads) {
-    uint32_t k = 0u;
-    float w = 0.0f;
-    if (mk[u] & bit) {
-      const float s = sanitize(sc[u]);
-      k = order_key(s);
-      w = expf(s - mx);
-      wsum += fixmass(w);
+  if (lds) {
+    // ---- histogram of mass over relative-score buckets; W is its total
+    for (int i = tid; i < kRelBuckets; i += kCutThreads) { sm.u.rel.cnt[i] = 0u; sm.u.rel.mass[i] = 0ull; }
+    if (tid == 0) { sm.first = kRelBuckets; sm.count = 0; }
+    __syncthreads();
+    unsigned long long wsum = 0ull;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (sv[j] != -INFINITY) {
+        const uint64_t fx = fixmass(mass_of(sv[j], mx));
+        const int b = rel_bucket(sv[j], mx);
+        wsum += fx;
+        atomicAdd(&sm.u.rel.cnt[b], 1u);
+        atomicAdd(&sm.u.rel.mass[b], (unsigned long long)fx);
+      }
     }
-    skey[u] = k;
-    sw[u] = w;
+    const unsigned long long W = block_sum<NW, unsigned long long>(wsum, sm.redu);
+    const double target = (double)P.p * (double)W;
+    // bucket b holds the scores just below those of buckets < b: running mass in
+    // increasing b; thread t owns buckets 2t and 2t+1
+    {
+      const unsigned long long m0 = sm.u.rel.mass[2 * tid], m1 = sm.u.rel.mass[2 * tid + 1];
+      unsigned long long tot;
+      const unsigned long long pre = block_excl_scan<NW, unsigned long long>(m0 + m1, sm.redu, &tot);
+      // exactly one bucket has its running mass cross p * W
+      const bool c0 = (double)pre < target && (double)(pre + m0) >= target;
+      const bool c1 = (double)(pre + m0) < target && (double)(pre + m0 + m1) >= target;
+      if (c0) { sm.first = 2 * tid; sm.above = pre; }
+      if (c1) { sm.first = 2 * tid + 1; sm.above = pre + m0; }
+      __syncthreads();
+    }
+    const int bstar = sm.first;
+    const unsigned long long above_b = sm.above;
+    const int cstar = (bstar < kRelBuckets) ? (int)sm.u.rel.cnt[bstar] : kSortMax + 1;
+    __syncthreads();
+    if (cstar <= kSortMax) {
+      // gather the crossing bucket as (key << 32 | ~u); sort descending: score
+      // descending, then id ascending
+      int n2 = 1;
+      while (n2 < cstar) n2 <<= 1;
+      for (int i = tid; i < n2; i += kCutThreads) sm.u.sortbuf[i] = 0ull;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if (sv[j] != -INFINITY && rel_bucket(sv[j], mx) == bstar) {
+          const int u = j * kCutThreads + tid;
+          const int slot = atomicAdd(&sm.count, 1);
+          sm.u.sortbuf[slot] = ((unsigned long long)order_key(sv[j]) << 32) | (uint32_t)(~(uint32_t)u);
+        }
+      }
+      __syncthreads();
+      const int lane = tid & 63;
+      if (n2 <= kWave) {
+        // one wave sorts and scans; the others wait at the next barrier
+        if (tid < kWave) {
+          for (int k2 = 2; k2 <= n2; k2 <<= 1) {
+            for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
+              const int ij = lane ^ jj;
+              unsigned long long a = 0ull, b = 0ull;
+              if (lane < n2 && ij > lane) { a = sm.u.sortbuf[lane]; b = sm.u.sortbuf[ij]; }
+              wave_lds_sync();
+              if (lane < n2 && ij > lane) {
+                const bool desc = (lane & k2) == 0;
+                if (desc ? (a < b) : (a > b)) { sm.u.sortbuf[lane] = b; sm.u.sortbuf[ij] = a; }
+              }
+              wave_lds_sync();
+            }
+          }
+          unsigned long long mi = 0ull;
+          const unsigned long long e = (lane < n2) ? sm.u.sortbuf[lane] : 0ull;
+          if ((uint32_t)(e >> 32) != 0u) mi = fixmass(mass_of(key_score((uint32_t)(e >> 32)), mx));
+          const unsigned long long inc = wave_incl_scan<unsigned long long>(mi);
+          const uint64_t reach = __ballot(mi != 0ull && (double)(above_b + inc) >= target);
+          int ic = reach ? (__ffsll((long long)reach) - 1) : cstar - 1;
+          if (ic > cstar - 1) ic = cstar - 1;
+          if (lane == 0) sm.count = ic;
+        }
+      } else {
+        for (int k2 = 2; k2 <= n2; k2 <<= 1) {
+          for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
+            for (int i = tid; i < n2; i += kCutThreads) {
+              const int ij = i ^ jj;
+              if (ij > i) {
+                const unsigned long long a = sm.u.sortbuf[i], b = sm.u.sortbuf[ij];
+                const bool desc = (i & k2) == 0;
+                if (desc ? (a < b) : (a > b)) { sm.u.sortbuf[i] = b; sm.u.sortbuf[ij] = a; }
+              }
+            }
+            __syncthreads();
+          }
+        }
+        // running mass in sorted order; the cut is the first element reaching p * W
+        unsigned long long mi = 0ull;
+        if (tid < n2) {
+          const unsigned long long e = sm.u.sortbuf[tid];
+          const uint32_t k = (uint32_t)(e >> 32);
+          if (k != 0u) mi = fixmass(mass_of(key_score(k), mx));
+        }
+        unsigned long long tot2;
+        const unsigned long long pre2 = block_excl_scan<NW, unsigned long long>(mi, sm.redu, &tot2);
+        if (tid == 0) sm.count = kSortMax;
+        __syncthreads();
+        if (tid < n2 && mi != 0ull && (double)(above_b + pre2 + mi) >= target) atomicMin(&sm.count, tid);
+        __syncthreads();
+        if (tid == 0 && sm.count > cstar - 1) sm.count = cstar - 1;
+      }
+      __syncthreads();
+      const int ic = sm.count;
+      const unsigned long long ce = sm.u.sortbuf[ic];
+      const uint32_t kap = (uint32_t)(ce >> 32);
+      const int ukap = (int)(~(uint32_t)ce);
+      uint32_t kept = 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int u = j * kCutThreads + tid;
+        if (u < U) {
+          uint8_t sel = 0;
+          if (sv[j] != -INFINITY) {
+            const uint32_t k = order_key(sv[j]);
+            sel = (k > kap || (k == kap && u <= ukap)) ? 1 : 0;
+          }
+          out[u] = sel;
+          kept += sel;
+          if (sel && selor) atomicOr(&selor[u], bit);
+        }
+      }
+      kept = block_sum<NW, uint32_t>(kept, (uint32_t*)sm.redi);
+      if (tid == 0) P.kept[head] = (int32_t)kept;
+      return;
+    }
+    __syncthreads();
+  }
+
+  // ---- general path: stage (key, w); non-candidates get key 0 and w 0
+  unsigned long long wsum = 0;
+  if (lds) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int u = j * kCutThreads + tid;
+      uint32_t k = 0u;
+      float w = 0.0f;
+      if (sv[j] != -INFINITY) {
+        k = order_key(sv[j]);
+        w = mass_of(sv[j], mx);
+        wsum += fixmass(w);
+      }
+      if (u < U) { skey[u] = k; sw[u] = w; }
+    }
+  } else {
+    for (int u = tid; u < U; u += kCutThreads) {
+      uint32_t k = 0u;
+      float w = 0.0f;
+      if (mk[u] & bit) {
+        const float sc1 = sanitize(sc[u]);
+        k = order_key(sc1);
+        w = mass_of(sc1, mx);
+        wsum += fixmass(w);
+      }
+      skey[u] = k;
+      sw[u] = w;
+    }
   }
   const unsigned long long W = block_reduce_sum<unsigned long long>(wsum, sm.redu);
   const double target = (double)P.p * (double)W;
@@ -219,7 +426,7 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
   uint32_t tie_count = 0u;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kCutThreads) { sm.cnt[i] = 0u; sm.mass[i] = 0ull; }
+    for (int i = tid; i < 256; i += kCutThreads) { sm.u.rad.cnt[i] = 0u; sm.u.rad.mass[i] = 0ull; }
     __syncthreads();
     // Scores cluster, so most lanes of a wave often hit one bucket: such waves
     // add one aggregated (count, mass) instead of 64 conflicting LDS atomics.
@@ -239,12 +446,12 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
         if (lane == leader) {
-          atomicAdd(&sm.cnt[lb], (uint32_t)__popcll(act));
-          atomicAdd(&sm.mass[lb], tot);
+          atomicAdd(&sm.u.rad.cnt[lb], (uint32_t)__popcll(act));
+          atomicAdd(&sm.u.rad.mass[lb], tot);
         }
       } else if (in) {
-        atomicAdd(&sm.cnt[bkt], 1u);
-        atomicAdd(&sm.mass[bkt], ms);
+        atomicAdd(&sm.u.rad.cnt[bkt], 1u);
+        atomicAdd(&sm.u.rad.mass[bkt], ms);
       }
     }
     __syncthreads();
@@ -252,7 +459,7 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
       // lane owns buckets 4*lane .. 4*lane+3; suffix sums from the top bucket down
       unsigned long long own = 0ull;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) own += sm.mass[4 * tid + i];
+      for (int i = 0; i < 4; ++i) own += sm.u.rad.mass[4 * tid + i];
       unsigned long long suf = own;   // sum over lanes >= tid
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -266,8 +473,8 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
         unsigned long long run = above + (suf - own);  // mass of buckets above this lane's
         int bk = 4 * tid + 3;
         for (; bk > 4 * tid; --bk) {
-          if ((double)(run + sm.mass[bk]) >= target) break;
-          run += sm.mass[bk];
+          if ((double)(run + sm.u.rad.mass[bk]) >= target) break;
+          run += sm.u.rad.mass[bk];
         }
         sm.bucket = (uint32_t)bk;
         sm.above = run;
@@ -278,7 +485,7 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
     above = sm.above;
     prefix |= bk << shift;
     pmask |= 255u << shift;
-    tie_count = sm.cnt[bk];
+    tie_count = sm.u.rad.cnt[bk];
     __syncthreads();
   }
   // ties at the threshold key: all share one mass; take the first k by position
@@ -308,6 +515,7 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
     else if (k == kappa) { s = (rank < k_ties) ? 1 : 0; ++rank; }
     out[u] = s;
     kept += s;
+    if (s && selor) atomicOr(&selor[u], bit);
   }
   kept = block_reduce_sum<int>(kept, sm.redi);
   if (tid == 0) P.kept[head] = kept;
@@ -329,7 +537,7 @@ struct ExpandParams {
   const int64_t* T;
   const int64_t* n_built;        // [L][B] (top launch only)
   const int32_t* uids; const uint32_t* umask; const int32_t* ucount; int64_t ucap;
-  const uint8_t* sel;            // [BHq][ucap]
+  const uint32_t* selor;         // [BH][ucap] OR of the heads' kept bits
   int32_t* nids; uint32_t* nmask; int32_t* ncount; int64_t ncap;   // next list
   int32_t* xstage;               // [BH][xcap][2]
   int64_t xcap;
@@ -343,8 +551,13 @@ struct ExpandParams {
 
 constexpr int kExpandThreads = 1024;
 
+constexpr int kExpandLds = 8192;   // kept parents staged in LDS; more use the workspace
+
 __global__ void __launch_bounds__(kExpandThreads) expand_level(ExpandParams P) {
-  __shared__ int32_t red[16];
+  constexpr int NW = kExpandThreads / kWave;
+  __shared__ int32_t red[NW];
+  __shared__ int32_t spid[kExpandLds];
+  __shared__ uint32_t spm[kExpandLds];
   const int gi = blockIdx.x;
   const int b = gi / P.H_kv;
   const int tid = threadIdx.x;
@@ -362,30 +575,75 @@ __global__ void __launch_bounds__(kExpandThreads) expand_level(ExpandParams P) {
   const int64_t n_next = T / P.span_next;                     // nodes at the next level
   const int64_t n_here = (P.level == 0) ? 0 : T / (P.span_next * P.C);
   const int U = (P.level == 0) ? 0 : clamp_count(P.ucount[gi], P.ucap);
-  int32_t* st = P.xstage + (int64_t)gi * P.xcap * 2;
   int32_t* ids = P.nids + (int64_t)gi * P.ncap;
   uint32_t* msk = P.nmask + (int64_t)gi * P.ncap;
+  const uint32_t* so = P.selor ? P.selor + (int64_t)gi * P.ucap : nullptr;
+  const int32_t* uid = P.uids ? P.uids + (int64_t)gi * P.ucap : nullptr;
 
-  // kept entries in list order
-  int nsel = 0;
-  for (int base = 0; base < U; base += kExpandThreads) {
-    const int u = base + tid;
-    uint32_t m = 0u;
-    if (u < U)
-      for (int g = 0; g < P.G; ++g)
-        m |= (P.sel[((int64_t)gi * P.G + g) * P.ucap + u] ? 1u : 0u) << g;
-    int tot = 0;
-    const int pos = nsel + block_exclusive_scan<int>(m ? 1 : 0, red, &tot);
-    if (m) {
-      const int32_t id = P.uids[(int64_t)gi * P.ucap + u];
-      if (P.final_) {
-        if (pos < P.ncap) { ids[pos] = id; msk[pos] = m; }
-      } else {
-        st[2 * pos] = id;
-        st[2 * pos + 1] = (int32_t)m;
-      }
+  // Wave w owns the contiguous entries [w*R, (w+1)*R), read 64 at a time with
+  // consecutive lanes on consecutive entries.  Kept entries are counted with
+  // ballots; one prefix over the wave counts gives each wave's first output
+  // position; a second ballot pass places every kept entry in list order.
+  const int lane = tid & 63, wave = tid >> 6;
+  const int R = (((U + NW - 1) / NW) + 63) & ~63;
+  const int nj = R / 64;
+  const int w0 = wave * R;
+  constexpr int kReg = 16;
+  uint32_t mv[kReg];
+  int32_t iv[kReg];
+  int cnt = 0;
+  if (nj <= kReg) {
+#pragma unroll
+    for (int j = 0; j < kReg; ++j) {
+      const int u = w0 + j * 64 + lane;
+      const bool in = j < nj && u < U;
+      mv[j] = in ? so[u] : 0u;
+      iv[j] = in ? uid[u] : 0;
     }
-    nsel += tot;
+#pragma unroll
+    for (int j = 0; j < kReg; ++j) cnt += __popcll(__ballot(mv[j] != 0u));
+  } else {
+    for (int j = 0; j < nj; ++j) {
+      const int u = w0 + j * 64 + lane;
+      cnt += __popcll(__ballot(u < U && so[u] != 0u));
+    }
+  }
+  if (lane == 0) red[wave] = cnt;
+  __syncthreads();
+  int pos = 0, nsel = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int c = red[w];
+    pos += (w < wave) ? c : 0;
+    nsel += c;
+  }
+  const bool lds = nsel <= kExpandLds;
+  int32_t* st = P.xstage + (int64_t)gi * P.xcap * 2;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes below this one
+  auto emit = [&](int p, int32_t id, uint32_t m) {
+    if (P.final_) {
+      if (p < P.ncap) { ids[p] = id; msk[p] = m; }
+    } else if (lds) {
+      spid[p] = id; spm[p] = m;
+    } else {
+      st[2 * p] = id; st[2 * p + 1] = (int32_t)m;
+    }
+  };
+  if (nj <= kReg) {
+#pragma unroll
+    for (int j = 0; j < kReg; ++j) {
+      const uint64_t bal = __ballot(mv[j] != 0u);
+      if (mv[j]) emit(pos + __popcll(bal & lt), iv[j], mv[j]);
+      pos += __popcll(bal);
+    }
+  } else {
+    for (int j = 0; j < nj; ++j) {
+      const int u = w0 + j * 64 + lane;
+      const uint32_t m = (u < U) ? so[u] : 0u;
+      const uint64_t bal = __ballot(m != 0u);
+      if (m) emit(pos + __popcll(bal & lt), uid[u], m);
+      pos += __popcll(bal);
+    }
   }
   int64_t n_orph = P.final_ ? 0 : (n_next - (int64_t)P.C * n_here);
   if (n_orph < 0) n_orph = 0;
@@ -400,8 +658,10 @@ __global__ void __launch_bounds__(kExpandThreads) expand_level(ExpandParams P) {
     const int cshift = __ffs(P.C) - 1;   // C is a power of two
     for (int64_t o = tid; o < nch && o < count; o += kExpandThreads) {
       const int64_t pi = o >> cshift;
-      ids[o] = st[2 * pi] * P.C + (int32_t)(o & (P.C - 1));
-      msk[o] = (uint32_t)st[2 * pi + 1];
+      const int32_t pid = lds ? spid[pi] : st[2 * pi];
+      const uint32_t pm = lds ? spm[pi] : (uint32_t)st[2 * pi + 1];
+      ids[o] = pid * P.C + (int32_t)(o & (P.C - 1));
+      msk[o] = pm;
     }
     const int64_t first_orph = (int64_t)P.C * n_here;
     for (int64_t i = tid; i < n_orph; i += kExpandThreads) {
@@ -495,7 +755,7 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
   E.B = cfg->B; E.H_kv = cfg->H_kv; E.G = cfg->G; E.C = cfg->C; E.L = L; E.T_cap = cfg->T_cap;
   E.xstage = (int32_t*)(base + w.xstage); E.xcap = w.stage_cap;
   E.level = 0; E.final_ = 0;
-  E.uids = nullptr; E.umask = nullptr; E.ucount = nullptr; E.ucap = 1; E.sel = nullptr;
+  E.uids = nullptr; E.umask = nullptr; E.ucount = nullptr; E.ucap = 1; E.selor = nullptr;
   E.nids = (int32_t*)(base + w.uids[L - 1]);
   E.nmask = (uint32_t*)(base + w.umask[L - 1]);
   E.ncount = (int32_t*)(base + w.ucount[L - 1]);
@@ -512,11 +772,12 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
     P.scores = (float*)(base + w.scores[l - 1]);
     P.sel = (uint8_t*)(base + w.sel[l - 1]);
     P.kept = (int32_t*)(base + w.kept[l - 1]);
+    P.selor = (uint32_t*)(base + w.selor[l - 1]);
     launch_score(P, P.ucap, s);
     hipLaunchKernelGGL(cut_topp, dim3(BHq), dim3(kCutThreads), 0, s, P);
     E.level = l;
     E.uids = P.uids; E.umask = P.umask; E.ucount = P.ucount; E.ucap = P.ucap;
-    E.sel = P.sel;
+    E.selor = P.selor;
     E.span_next = span[l - 1];
     if (l > 1) {
       E.final_ = 0;
@@ -555,6 +816,7 @@ extern "C" int32_t zha_route_level(const zha_cfg* cfg, int32_t level, const floa
   P.uids = cand_ids; P.umask = cand_mask; P.ucount = cand_count; P.ucap = cand_cap;
   P.scores = scores; P.sel = sel;
   P.kept = (int32_t*)((char*)ws + w.kept[level - 1]);
+  P.selor = nullptr;
   launch_score(P, cand_cap, s);
   hipLaunchKernelGGL(cut_topp, dim3(cfg->B * cfg->H_kv * cfg->G), dim3(kCutThreads), 0, s, P);
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;

@@ -26,6 +26,7 @@ struct WsLayout {
   // per-level route arrays (offsets from the workspace base); index l-1
   size_t uids[ZHA_MAX_L], umask[ZHA_MAX_L], ucount[ZHA_MAX_L];
   size_t scores[ZHA_MAX_L], sel[ZHA_MAX_L], kept[ZHA_MAX_L];
+  size_t selor[ZHA_MAX_L];  // per union entry: OR of the heads' kept bits
   int64_t cap[ZHA_MAX_L];
   size_t stage = 0;        // cut staging: [B*Hq][stage_cap] (u32 key, f32 w)
   int64_t stage_cap = 0;
@@ -72,6 +73,7 @@ inline WsLayout ws_layout(const zha_cfg& c) {
     w.scores[l - 1] = off; off = align_up(off + (size_t)BHq * cap * 4, 256);
     w.sel[l - 1] = off;    off = align_up(off + (size_t)BHq * cap, 256);
     w.kept[l - 1] = off;   off = align_up(off + (size_t)BHq * 4, 256);
+    w.selor[l - 1] = off;  off = align_up(off + (size_t)BH * cap * 4, 256);
   }
   // Cut staging for lists too long for LDS: as long as the largest level.
   int64_t scap = 0;
@@ -198,6 +200,126 @@ __device__ inline T block_reduce_sum(T v, T* scratch) {
   for (int w = 0; w < nw; ++w) s += scratch[w];
   __syncthreads();
   return s;
+}
+
+// ---- fast collectives: DPP row operations + readlane, compile-time wave count
+//
+// Within each row of 16 lanes, quad_perm (lane^1, lane^2), row_half_mirror and
+// row_mirror pair every lane with partners that differ in each of the low four
+// lane bits, so four steps leave the row total in every lane of the row; the
+// four row totals are combined through readlane.  Scans use row_shr:1,2,4,8
+// (Hillis-Steele within a row) and add the totals of earlier rows.  64-bit
+// values move as two 32-bit halves.
+
+template <int CTRL>
+__device__ inline uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ inline float dppf(float v) { return __uint_as_float(dpp32<CTRL>(__float_as_uint(v))); }
+template <int CTRL>
+__device__ inline uint64_t dpp64(uint64_t v) {
+  return ((uint64_t)dpp32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp32<CTRL>((uint32_t)v);
+}
+__device__ inline uint32_t rl32(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+__device__ inline uint64_t rl64(uint64_t v, int lane) {
+  return ((uint64_t)rl32((uint32_t)(v >> 32), lane) << 32) | rl32((uint32_t)v, lane);
+}
+__device__ inline float rlf(float v, int lane) { return __uint_as_float(rl32(__float_as_uint(v), lane)); }
+
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ inline float wave_max_fast(float v) {
+  v = fmaxf(v, dppf<kDppXor1>(v));
+  v = fmaxf(v, dppf<kDppXor2>(v));
+  v = fmaxf(v, dppf<kDppHalfMirror>(v));
+  v = fmaxf(v, dppf<kDppMirror>(v));
+  return fmaxf(fmaxf(rlf(v, 0), rlf(v, 16)), fmaxf(rlf(v, 32), rlf(v, 48)));
+}
+__device__ inline uint32_t wave_sum_u32(uint32_t v) {
+  v += dpp32<kDppXor1>(v);
+  v += dpp32<kDppXor2>(v);
+  v += dpp32<kDppHalfMirror>(v);
+  v += dpp32<kDppMirror>(v);
+  return (rl32(v, 0) + rl32(v, 16)) + (rl32(v, 32) + rl32(v, 48));
+}
+__device__ inline uint64_t wave_sum_u64(uint64_t v) {
+  v += dpp64<kDppXor1>(v);
+  v += dpp64<kDppXor2>(v);
+  v += dpp64<kDppHalfMirror>(v);
+  v += dpp64<kDppMirror>(v);
+  return (rl64(v, 0) + rl64(v, 16)) + (rl64(v, 32) + rl64(v, 48));
+}
+// Inclusive prefix sum over the 64 lanes.
+template <typename T>
+__device__ inline T wave_incl_scan(T x) {
+  if constexpr (sizeof(T) == 8) {
+    uint64_t v = (uint64_t)x;
+    v += dpp64<0x111>(v);
+    v += dpp64<0x112>(v);
+    v += dpp64<0x114>(v);
+    v += dpp64<0x118>(v);
+    const uint64_t r0 = rl64(v, 15), r1 = rl64(v, 31), r2 = rl64(v, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    v += (row >= 1 ? r0 : 0ull) + (row >= 2 ? r1 : 0ull) + (row >= 3 ? r2 : 0ull);
+    return (T)v;
+  } else {
+    uint32_t v = (uint32_t)x;
+    v += dpp32<0x111>(v);
+    v += dpp32<0x112>(v);
+    v += dpp32<0x114>(v);
+    v += dpp32<0x118>(v);
+    const uint32_t r0 = rl32(v, 15), r1 = rl32(v, 31), r2 = rl32(v, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    v += (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+    return (T)v;
+  }
+}
+
+// Block-wide collectives over NW waves (blockDim.x == 64 * NW).  `scratch`
+// holds NW values in LDS.  Every thread returns the block result.
+template <int NW>
+__device__ inline float block_max_f(float v, float* scratch) {
+  v = wave_max_fast(v);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = scratch[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) m = fmaxf(m, scratch[w]);
+  __syncthreads();
+  return m;
+}
+template <int NW, typename T>
+__device__ inline T block_sum(T v, T* scratch) {
+  T t;
+  if constexpr (sizeof(T) == 8) t = (T)wave_sum_u64((uint64_t)v);
+  else t = (T)wave_sum_u32((uint32_t)v);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = t;
+  __syncthreads();
+  T s = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += scratch[w];
+  __syncthreads();
+  return s;
+}
+template <int NW, typename T>
+__device__ inline T block_excl_scan(T v, T* scratch, T* total) {
+  const T inc = wave_incl_scan<T>(v);
+  if ((threadIdx.x & 63) == 63) scratch[threadIdx.x >> 6] = inc;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  T before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const T t = scratch[w];
+    before += (w < wave) ? t : (T)0;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + inc - v;
 }
 
 // Order LDS traffic of one wave against itself (no cross-wave synchronisation).

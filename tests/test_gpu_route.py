@@ -212,3 +212,31 @@ def test_stale_tree_is_reported():
     q = synth.make_query(wl, 0, T, "cpu").to(DEV)
     zha.route(cfg2, q, tree2, Tt, 0.9, lst.ids, lst.mask, lst.count, ws2)
     assert zha.ws_status(ws2) == zha.ESTALE
+
+
+@pytest.mark.parametrize("p", [0.5, 0.9, 0.3])
+def test_all_equal_scores_take_lowest_ids(p):
+    """2048 identical leaves: every score ties, so the cut keeps ceil(p n) leaves
+    with the lowest ids (the same count the oracle's rule gives for uniform
+    masses).  More than 1024 ties at the threshold exercises the radix path."""
+    C, d, n = 16, 64, 2048
+    T = C * n
+    g = torch.Generator().manual_seed(1)
+    chunk = torch.randn(C, d, generator=g)
+    K = chunk.repeat(n, 1).reshape(1, 1, T, d)
+    V = torch.randn(1, 1, T, d, generator=g)
+    cfg = zha.Config(B=1, H_kv=1, G=1, d=d, C=C, L=1, R=2, T_cap=T, kv_dtype=zha.F32)
+    qref = (torch.randn(1, 2, d, generator=g) / 8).to(DEV)
+    tree = zha.Tree(cfg, DEV)
+    ws = zha.new_workspace(cfg)
+    Tt = torch.tensor([T], dtype=torch.int64, device=DEV)
+    zha.build(cfg, K.to(DEV), V.to(DEV), Tt, qref, tree, ws)
+    q = torch.randn(1, 1, d, generator=g).to(DEV)
+    lst = zha.LeafList(cfg, DEV)
+    zha.route(cfg, q, tree, Tt, p, lst.ids, lst.mask, lst.count, ws)
+    torch.cuda.synchronize()
+    m = math.ceil(float(np.float32(p)) * n - 1e-9)
+    cut = O.topp_cut(np.arange(n), np.zeros(n), p)
+    assert cut.m == m
+    assert int(lst.count[0, 0]) == m
+    assert lst.ids[0, 0, :m].cpu().tolist() == list(range(m))
