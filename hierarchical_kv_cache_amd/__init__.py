@@ -2,7 +2,7 @@
 
 The compute path is libzha.so (HIP kernels behind a C ABI, include/zha.h);
 ``hierarchical_kv_cache_amd.zha`` is its ctypes binding.  Names are resolved on
-first use so that ``python -m hierarchical_kv_cache_amd.build`` can rebuild the
+first use so that ``python -m hierarchical_kv_cache_amd.buildlib`` can rebuild the
 library; using any of them without a built library raises ImportError.
 """
 _API = ("Config", "Decoder", "LeafList", "Tree", "ZhaError", "append", "attend", "build",

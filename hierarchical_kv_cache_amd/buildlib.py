@@ -1,6 +1,6 @@
 """Compile libzha (HIP, gfx950) in place: hierarchical_kv_cache_amd/libzha.so.
 
-Run as ``python -m hierarchical_kv_cache_amd.build``; needs hipcc, no GPU.
+Run as ``python -m hierarchical_kv_cache_amd.buildlib``; needs hipcc, no GPU.
 """
 from __future__ import annotations
 

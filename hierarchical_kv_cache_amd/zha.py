@@ -53,7 +53,7 @@ class _Tree(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m hierarchical_kv_cache_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m hierarchical_kv_cache_amd.buildlib`")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     i32, f32, i64, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_int64, ctypes.c_size_t
