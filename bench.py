@@ -90,7 +90,7 @@ def stored_traffic(workload, p):
 
 
 class Run:
-    """Device state of one workload: cache, queries, tree, buffers."""
+    """Device state of one workload: cache, queries, per-step lengths, tree, buffers."""
 
     def __init__(self, wl, steps_total, dev="cuda"):
         from hierarchical_kv_cache_amd import zha
@@ -101,6 +101,9 @@ class Run:
         self.K, self.V = synth.make_cache(wl.with_(steps=steps_total + wl.C), dev, self.T_cap)
         self.qref = synth.make_qref(wl, dev)
         self.Q = torch.stack([synth.make_query(wl, s, wl.T0 + s, dev) for s in range(steps_total)])
+        # length of every sequence at step s (the token of step s is already cached)
+        self.Ts = (wl.T0 + torch.arange(steps_total, dtype=torch.int64, device=dev)).unsqueeze(1) \
+            .repeat(1, wl.B).contiguous()
         torch.cuda.synchronize()
         log(f"[bench] synthetic cache {wl.name}: {time.time() - t0:.1f}s")
         self.cfg = zha.Config(B=wl.B, H_kv=wl.H_kv, G=wl.G, d=wl.d, C=wl.C, L=wl.L, R=wl.R,
@@ -108,30 +111,29 @@ class Run:
                               kv_dtype=zha.F32 if wl.kv_dtype == "f32" else zha.BF16,
                               rope=wl.rope, rope_base=wl.rope_base)
         self.dec = zha.Decoder(self.cfg, self.qref, dev)
-        self.T = torch.full((wl.B,), wl.T0, dtype=torch.int64, device=dev)
 
     def prefill(self):
-        self.T.fill_(self.wl.T0)
         self.dec.tree.n_built.zero_()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        self.dec.prefill(self.K, self.V, self.T)
+        self.dec.prefill(self.K, self.V, self.Ts[0])
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
-    def routed_steps(self, s0, s1, p, ev=None, counts=None):
-        """Steps s0..s1-1.  ev: list collecting (route, attend, append) event pairs."""
-        C = self.wl.C
+    def routed_steps(self, s0, s1, p, ev=None, counts=None, keep=None):
+        """Steps s0..s1-1.  ev: dict collecting (route, attend, append) event pairs;
+        keep: one LeafList per step, to hold each step's routed list."""
+        zha, dec, C = self.zha, self.dec, self.wl.C
         for s in range(s0, s1):
-            t = self.wl.T0 + s
-            self.T.fill_(t)
+            T = self.Ts[s]
             q = self.Q[s]
-            if t % C == 0:
+            lst = keep[s - s0] if keep is not None else dec.leaves
+            if (self.wl.T0 + s) % C == 0:
                 if ev is not None:
                     a0 = torch.cuda.Event(enable_timing=True)
                     a0.record()
-                self.dec.append(self.K, self.V, self.T, 1)
+                dec.append(self.K, self.V, T, 1)
                 if ev is not None:
                     a1 = torch.cuda.Event(enable_timing=True)
                     a1.record()
@@ -139,14 +141,12 @@ class Run:
             if ev is not None:
                 r0 = torch.cuda.Event(enable_timing=True)
                 r0.record()
-            self.zha.route(self.cfg, q, self.dec.tree, self.T, p, self.dec.leaves.ids,
-                           self.dec.leaves.mask, self.dec.leaves.count, self.dec.ws)
+            zha.route(self.cfg, q, dec.tree, T, p, lst.ids, lst.mask, lst.count, dec.ws)
             if ev is not None:
                 r1 = torch.cuda.Event(enable_timing=True)
                 r1.record()
-            self.zha.attend(self.cfg, q, self.K, self.V, self.T, self.dec.leaves.ids,
-                            self.dec.leaves.mask, self.dec.leaves.count, self.dec.out,
-                            self.dec.lse, self.dec.ws)
+            zha.attend(self.cfg, q, self.K, self.V, T, lst.ids, lst.mask, lst.count,
+                       dec.out, dec.lse, dec.ws)
             if ev is not None:
                 r2 = torch.cuda.Event(enable_timing=True)
                 r2.record()
@@ -156,17 +156,24 @@ class Run:
                 L = self.wl.L
                 uc = torch.empty(L, self.wl.B, self.wl.H_kv, dtype=torch.int32, device="cuda")
                 kc = torch.empty(L, self.wl.B, self.wl.Hq, dtype=torch.int32, device="cuda")
-                self.zha.route_counts(self.cfg, self.dec.ws, uc, kc)
-                first = self.dec.leaves.ids[:, :, 0].clone()
-                counts.append((t, uc, kc, self.dec.leaves.count.clone(), first))
+                zha.route_counts(self.cfg, dec.ws, uc, kc)
+                first = lst.ids[:, :, 0].clone()
+                counts.append((self.wl.T0 + s, uc, kc, lst.count.clone(), first))
+
+    def attend_replay(self, s0, keep):
+        """zha_attend of steps s0.. over their kept leaf lists, back to back."""
+        zha, dec = self.zha, self.dec
+        for i, lst in enumerate(keep):
+            s = s0 + i
+            zha.attend(self.cfg, self.Q[s], self.K, self.V, self.Ts[s], lst.ids, lst.mask,
+                       lst.count, dec.out, dec.lse, dec.ws)
 
     def dense_steps(self, s0, s1, ev=None):
         for s in range(s0, s1):
-            self.T.fill_(self.wl.T0 + s)
             if ev is not None:
                 d0 = torch.cuda.Event(enable_timing=True)
                 d0.record()
-            self.zha.dense_attend(self.cfg, self.Q[s], self.K, self.V, self.T, self.dec.out,
+            self.zha.dense_attend(self.cfg, self.Q[s], self.K, self.V, self.Ts[s], self.dec.out,
                                   self.dec.lse, self.dec.ws)
             if ev is not None:
                 d1 = torch.cuda.Event(enable_timing=True)
@@ -269,19 +276,34 @@ def main():
     build_ms = run.prefill()
     log(f"[bench] prefill tree build: {build_ms:.2f} ms")
 
-    # ---- routed: warmup, then exactly K timed steps
+    # ---- routed: warmup, then exactly K timed steps, nothing else in the queue
     run.routed_steps(0, W, p)
-    ev = {"route": [], "attend": [], "append": []}
-    total_ms = timed(lambda: run.routed_steps(W, W + K, p, ev))
+    total_ms = timed(lambda: run.routed_steps(W, W + K, p))
     st = zha.ws_status(run.dec.ws)
     if st != 0:
         raise RuntimeError(f"device status {zha.status_str(st)}")
-    route_ms = [a.elapsed_time(b) for a, b in ev["route"]]
-    attend_ms = [a.elapsed_time(b) for a, b in ev["attend"]]
-    append_ms = [a.elapsed_time(b) for a, b in ev["append"]]
     us_step = total_ms * 1000.0 / K
-    log(f"[bench] routed p={p}: {us_step:.1f} us/step (route {1000*sum(route_ms)/K:.1f}, "
-        f"attend {1000*sum(attend_ms)/K:.1f}, appends {len(append_ms)})")
+    log(f"[bench] routed p={p}: {us_step:.1f} us/step")
+
+    # ---- the same steps again, for the breakdown: events around each call (each
+    # event is a queue marker, so route_us + attend_us slightly exceed a step),
+    # every step's leaf list kept, and the route diagnostics for byte accounting
+    run.prefill()
+    run.routed_steps(0, W, p)
+    ev = {"route": [], "attend": [], "append": []}
+    keep = [zha.LeafList(run.cfg) for _ in range(K)]
+    recs = [] if not args.no_stats else None
+    run.routed_steps(W, W + K, p, ev, counts=recs, keep=keep)
+    torch.cuda.synchronize()
+    route_ms = [a.elapsed_time(b) for a, b in ev["route"]]
+    append_ms = [a.elapsed_time(b) for a, b in ev["append"]]
+    # the K attends replayed back to back over their own lists: the attend time
+    run.attend_replay(W, keep)
+    attend_ms_total = timed(lambda: run.attend_replay(W, keep))
+    attend_us = attend_ms_total * 1000.0 / K
+    route_us = 1000 * sum(route_ms) / K
+    log(f"[bench]   route {route_us:.1f} us (per-call events), attend {attend_us:.1f} us "
+        f"(replayed), appends {len(append_ms)}")
 
     extra = {}
     # ---- p sweep (same steps, warm)
@@ -298,27 +320,19 @@ def main():
     dense = None
     if not args.no_dense:
         run.dense_steps(0, W)
-        dev = []
-        ms = timed(lambda: run.dense_steps(W, W + K, dev))
-        dk = [a.elapsed_time(b) for a, b in dev]
+        ms = timed(lambda: run.dense_steps(W, W + K))
         dense_bytes = 0
         for s in range(W, W + K):
-            dense_bytes += wl.B * wl.H_kv * (wl.T0 + s) * 2 * wl.d * 2
+            dense_bytes += wl.B * wl.H_kv * (wl.T0 + s) * 2 * wl.d * (2 if wl.kv_dtype == "bf16" else 4)
         dense = {"us_per_step": ms * 1000.0 / K,
-                 "effective_GBps": dense_bytes / K / (sum(dk) / K * 1e-3) / 1e9,
-                 "kernel_us": 1000 * sum(dk) / K}
+                 "effective_GBps": dense_bytes / K / (ms / K * 1e-3) / 1e9}
         dense["hbm_frac"] = dense["effective_GBps"] / HBM_PEAK_GBPS
         log(f"[bench] dense: {dense['us_per_step']:.1f} us/step, {dense['effective_GBps']:.0f} GB/s")
 
-    # ---- replay for byte accounting (deterministic: identical routing)
+    # ---- byte accounting from the breakdown pass's route diagnostics
     route_bytes = attend_bytes = keys_total = 0
     sel_frac = None
-    if not args.no_stats:
-        run.prefill()
-        run.routed_steps(0, W, p)
-        recs = []
-        run.routed_steps(W, W + K, p, counts=recs)
-        torch.cuda.synchronize()
+    if recs is not None:
         kept = torch.zeros(wl.L)
         for rec in recs:
             rb, ab, keys = bytes_of_step(wl, rec)
@@ -329,12 +343,12 @@ def main():
         sel_frac = keys_total / sum(wl.B * wl.H_kv * (wl.T0 + s) for s in range(W, W + K))
         extra["kept_per_head_per_level"] = [float(x) / (K * wl.B * wl.Hq) for x in kept]
 
-    att_s = sum(attend_ms) * 1e-3
+    att_s = attend_ms_total * 1e-3
     rte_s = sum(route_ms) * 1e-3
     att_gbps = attend_bytes / att_s / 1e9 if att_s > 0 and attend_bytes else None
     rte_gbps = route_bytes / rte_s / 1e9 if rte_s > 0 and route_bytes else None
     step_gbps = (attend_bytes + route_bytes) / (total_ms * 1e-3) / 1e9 if attend_bytes else None
-    dominant = "attend" if sum(attend_ms) >= sum(route_ms) else "route"
+    dominant = "attend" if attend_us >= route_us else "route"
     ach = att_gbps if dominant == "attend" else rte_gbps
     roofline = {
         "bound": "hbm",
@@ -342,7 +356,7 @@ def main():
         "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": (ach / HBM_PEAK_GBPS) if ach else None,
         "traffic": stored_traffic(wl.name, p) if dominant == "attend" else None,
-        "avg_launch_us": 1000 * (sum(attend_ms) if dominant == "attend" else sum(route_ms)) / K,
+        "avg_launch_us": attend_us if dominant == "attend" else route_us,
         "algorithmic_bytes_per_launch": (attend_bytes if dominant == "attend" else route_bytes) / K,
     }
 
@@ -361,8 +375,8 @@ def main():
                    "clusters": wl.n_clusters, "cluster_law": wl.freq},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "route_us": 1000 * sum(route_ms) / K,
-        "attend_us": 1000 * sum(attend_ms) / K,
+        "route_us": route_us,
+        "attend_us": attend_us,
         "append_us_each": (1000 * sum(append_ms) / len(append_ms)) if append_ms else None,
         "appends_in_timed_steps": len(append_ms),
         "prefill_build_ms": build_ms,

@@ -15,7 +15,8 @@
 // head.  A group's K/V tile is read once for all G query heads of the group;
 // heads that did not select a leaf see its keys masked to -inf.
 //
-// Scores are kept in log2 units: q is pre-multiplied by scale * log2(e).
+// Scores are kept in log2 units: q is pre-multiplied by scale * log2(e).  K/V
+// rows are read once per step and carry the non-temporal hint.
 #include "zha_internal.hpp"
 
 namespace zha {
@@ -27,7 +28,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWavesPerWg = 4;
 constexpr int kMaxGroups = 2048;
-constexpr int kAttendGrid = 1024;
+constexpr int kAttendGrid = 512;      // two workgroups per CU: measured faster than four
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -298,12 +299,12 @@ __device__ inline void load_chunk_any(const AttendParams& P, const SM& sm, const
   buf.kmask = ks.mask;
   const uint16_t* krow = Kb + (kv_base + ks.tok) * D + (lane >> 4) * 8;
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) buf.k[s] = *(const u32x4_t*)(krow + s * 32);
+  for (int s = 0; s < KSTEPS; ++s) buf.k[s] = __builtin_nontemporal_load((const u32x4_t*)(krow + s * 32));
   buf.vok = 0u;
 #pragma unroll
   for (int i = 0; i < VL; ++i) {
     const Slot vs = item_slot(P, sm, g, it, chunk * 16 + RPI * i + lane / LPR, full);
-    buf.v[i] = *(const u32x4_t*)(Vb + (kv_base + vs.tok) * D + (lane % LPR) * 8);
+    buf.v[i] = __builtin_nontemporal_load((const u32x4_t*)(Vb + (kv_base + vs.tok) * D + (lane % LPR) * 8));
     buf.vok |= (vs.mask ? 1u : 0u) << i;
   }
 }
@@ -318,13 +319,13 @@ __device__ inline void load_chunk_rows(const uint16_t* klane, const uint16_t* vl
   const int kof = kr < nv ? kr : 0;
   const uint16_t* kp = klane + (row0 + kof) * D;
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) buf.k[s] = *(const u32x4_t*)(kp + s * 32);
+  for (int s = 0; s < KSTEPS; ++s) buf.k[s] = __builtin_nontemporal_load((const u32x4_t*)(kp + s * 32));
   buf.vok = 0u;
 #pragma unroll
   for (int i = 0; i < VL; ++i) {
     const int vr = RPI * i + lane / LPR;
     const int vof = vr < nv ? vr : 0;
-    buf.v[i] = *(const u32x4_t*)(vlane + (row0 + vof) * D);
+    buf.v[i] = __builtin_nontemporal_load((const u32x4_t*)(vlane + (row0 + vof) * D));
     buf.vok |= (vr < nv && hm != 0u ? 1u : 0u) << i;
   }
   buf.kmask = kr < nv ? hm : 0u;

@@ -58,7 +58,9 @@ __device__ inline int clamp_count(int32_t u, int64_t cap) {
 // ---------------------------------------------------------------- scoring (A3)
 //
 // One wave scores one node: the node's R x d summary (8 KiB at R=16, d=128) is
-// read as 1 KiB contiguous rows per load instruction.  Lane l holds rows
+// read as 1 KiB contiguous rows per load instruction, with the non-temporal hint
+// (summaries are streamed once per step; keeping them out of the caches measured
+// ~10% faster).  Lane l holds rows
 // r = RPI*s + l/LPR (s < NS) at dims (l%LPR)*4..+4 and the group's G query heads
 // at the same dims.  The NS x GP partial dots are summed over the LPR lanes of a
 // row by a transposing butterfly (each round halves the values a lane keeps),
@@ -82,73 +84,94 @@ __device__ inline void tr_round(float* a, int lane) {
   }
 }
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// The group's G queries at this lane's dims (t = lane % (D/4)), zero-padded to GP.
 template <int D, int GP>
-__global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
+__device__ inline void load_group_queries(const LevelParams& P, int gi, int lane,
+                                          float (&qv)[GP][4]) {
+  const int t = lane % (D / 4);
+#pragma unroll
+  for (int g = 0; g < GP; ++g)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      qv[g][j] = (g < P.G) ? P.q[((int64_t)gi * P.G + g) * D + t * 4 + j] : 0.0f;
+}
+
+// One wave scores list entry u (tree node `node`) of group gi for all G heads.
+template <int D, int GP>
+__device__ inline void score_node(const LevelParams& P, int gi, int node, int u,
+                                  const float (&qv)[GP][4], int lane) {
   constexpr int LPR = D / 4;           // lanes per summary row
   constexpr int RPI = kWave / LPR;     // rows per load instruction
   constexpr int NS = 16 / RPI;         // load instructions per node (R padded to 16)
   constexpr int V0 = NS * GP;          // partial dots per lane
   constexpr int J = GP / 4;            // full dots per lane after the butterfly
   static_assert(V0 / LPR == J, "butterfly shape");
+  const int t = lane % LPR;
+  if (P.selor != nullptr && lane == 0) P.selor[(int64_t)gi * P.ucap + u] = 0u;
+  if (node < 0 || node >= P.ncap) {   // not a node of this tree: never selected
+    if (lane < P.G) P.scores[((int64_t)gi * P.G + lane) * P.ucap + u] = -INFINITY;
+    if (lane == 0) set_status(P.status, ZHA_EINVAL);
+    return;
+  }
+  const float* base = P.khat + ((int64_t)gi * P.ncap + node) * P.R * D;
+  // after the butterfly this lane holds row r = RPI*(t/4) + lane/LPR
+  const int r_out = RPI * (t / 4) + lane / LPR;
+  const float bh = (r_out < P.R) ? P.bhat[((int64_t)gi * P.ncap + node) * P.R + r_out] : 0.0f;
+  float a[V0];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int r = RPI * s + lane / LPR;
+    f32x4_t k4 = {0.f, 0.f, 0.f, 0.f};
+    if (r < P.R) k4 = __builtin_nontemporal_load((const f32x4_t*)(base + r * D + t * 4));
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+      a[s * GP + g] = qv[g][0] * k4[0] + qv[g][1] * k4[1] + qv[g][2] * k4[2] + qv[g][3] * k4[3];
+  }
+  // butterfly over the LPR lanes of a row: deltas LPR/2 .. 1
+  if constexpr (LPR == 32) tr_round<V0, 16>(a, lane);
+  if constexpr (LPR >= 16) tr_round<V0 * 16 / LPR, 8>(a, lane);
+  tr_round<V0 * 8 / LPR, 4>(a, lane);
+  tr_round<V0 * 4 / LPR, 2>(a, lane);
+  tr_round<V0 * 2 / LPR, 1>(a, lane);
+  // lane now holds dot(s = t/4, g = (t%4)*J + j) for row r_out
+  float sc[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    float v = (r_out < P.R) ? fmaf(a[j], P.scale, bh) : -INFINITY;
+    v = fmaxf(v, xor_lane<4>(v));
+    v = fmaxf(v, xor_lane<8>(v));
+    v = fmaxf(v, xor_lane<16>(v));
+    v = fmaxf(v, xor_lane<32>(v));
+    sc[j] = v;
+  }
+  if (lane < 4) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int g = lane * J + j;
+      if (g < P.G) P.scores[((int64_t)gi * P.G + g) * P.ucap + u] = sc[j];
+    }
+  }
+}
+
+template <int D, int GP>
+__global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
   const int gi = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int U = clamp_count(P.ucount[gi], P.ucap);
-  const int t = lane % LPR;
-
-  // the group's queries at this lane's dims
   float qv[GP][4];
-#pragma unroll
-  for (int g = 0; g < GP; ++g)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      qv[g][j] = (g < P.G) ? P.q[((int64_t)gi * P.G + g) * D + t * 4 + j] : 0.0f;
-
+  load_group_queries<D, GP>(P, gi, lane, qv);
   const int nwaves = gridDim.x * (blockDim.x >> 6);
-  for (int u = blockIdx.x * (blockDim.x >> 6) + wave; u < U; u += nwaves) {
-    if (P.selor != nullptr && lane == 0) P.selor[(int64_t)gi * P.ucap + u] = 0u;
-    const int node = P.uids[(int64_t)gi * P.ucap + u];
-    if (node < 0 || node >= P.ncap) {   // not a node of this tree: never selected
-      if (lane < P.G) P.scores[((int64_t)gi * P.G + lane) * P.ucap + u] = -INFINITY;
-      if (lane == 0) set_status(P.status, ZHA_EINVAL);
-      continue;
-    }
-    const float* base = P.khat + ((int64_t)gi * P.ncap + node) * P.R * D;
-    float a[V0];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int r = RPI * s + lane / LPR;
-      float4 k4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (r < P.R) k4 = *(const float4*)(base + r * D + t * 4);
-#pragma unroll
-      for (int g = 0; g < GP; ++g)
-        a[s * GP + g] = qv[g][0] * k4.x + qv[g][1] * k4.y + qv[g][2] * k4.z + qv[g][3] * k4.w;
-    }
-    // butterfly over the LPR lanes of a row: deltas LPR/2 .. 1
-    if constexpr (LPR == 32) tr_round<V0, 16>(a, lane);
-    if constexpr (LPR >= 16) tr_round<V0 * 16 / LPR, 8>(a, lane);
-    tr_round<V0 * 8 / LPR, 4>(a, lane);
-    tr_round<V0 * 4 / LPR, 2>(a, lane);
-    tr_round<V0 * 2 / LPR, 1>(a, lane);
-    // lane now holds dot(s = t/4, g = (t%4)*J + j) for row r = RPI*(t/4) + lane/LPR
-    const int r = RPI * (t / 4) + lane / LPR;
-    const float bh = (r < P.R) ? P.bhat[((int64_t)gi * P.ncap + node) * P.R + r] : 0.0f;
-    float sc[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      float v = (r < P.R) ? fmaf(a[j], P.scale, bh) : -INFINITY;
-      v = fmaxf(v, xor_lane<4>(v));
-      v = fmaxf(v, xor_lane<8>(v));
-      v = fmaxf(v, xor_lane<16>(v));
-      v = fmaxf(v, xor_lane<32>(v));
-      sc[j] = v;
-    }
-    if (lane < 4) {
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int g = lane * J + j;
-        if (g < P.G) P.scores[((int64_t)gi * P.G + g) * P.ucap + u] = sc[j];
-      }
-    }
+  const int32_t* ul = P.uids + (int64_t)gi * P.ucap;
+  // the next node id is fetched one iteration ahead, so a wave's summary loads
+  // never wait behind the id load that addresses them
+  int u = blockIdx.x * (blockDim.x >> 6) + wave;
+  int node_next = (u < U) ? ul[u] : 0;
+  for (; u < U; u += nwaves) {
+    const int node = node_next;
+    if (u + nwaves < U) node_next = ul[u + nwaves];
+    score_node<D, GP>(P, gi, node, u, qv, lane);
   }
 }
 
@@ -156,6 +179,7 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
 
 constexpr int kCutThreads = 1024;
 constexpr int kCutLds = 16384;         // entries staged in LDS; longer lists use the workspace
+constexpr int kCutReg = 24;            // entries per thread held in registers (24576 per list)
 
 // w * 2^40 truncated to an integer, for 0 <= w <= 1, from the fp32 bits: the
 // 24-bit mantissa shifted by (exponent + 17).  Equal to (uint64)((double)w * 2^40).
@@ -221,11 +245,12 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
   uint32_t* selor = P.selor ? P.selor + (int64_t)gi * P.ucap : nullptr;
   // Lists that fit keep this thread's scores (entries j*1024 + tid) in registers
   // across every pass; all loads are issued before any is used.
-  constexpr int PER = kCutLds / kCutThreads;
+  constexpr int PER = kCutReg;
+  const bool reg = U <= PER * kCutThreads;
   float sv[PER];
   float mx = -INFINITY;
   int ncand = 0;
-  if (lds) {
+  if (reg) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int u = j * kCutThreads + tid;
@@ -255,7 +280,7 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
     return;
   }
 
-  if (lds) {
+  if (reg) {
     // ---- histogram of mass over relative-score buckets; W is its total
     for (int i = tid; i < kRelBuckets; i += kCutThreads) { sm.u.rel.cnt[i] = 0u; sm.u.rel.mass[i] = 0ull; }
     if (tid == 0) { sm.first = kRelBuckets; sm.count = 0; }
@@ -390,7 +415,7 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
 
   // ---- general path: stage (key, w); non-candidates get key 0 and w 0
   unsigned long long wsum = 0;
-  if (lds) {
+  if (reg) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int u = j * kCutThreads + tid;
@@ -495,10 +520,14 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
     if (skey[u] == kappa) s_wk = fixmass(sw[u]);   // identical for every tie
   __syncthreads();
   const unsigned long long wk = s_wk;
+  // the fewest ties k whose running mass above + k wk reaches p W, decided by the
+  // same integer-to-double comparison as the sorted path
   double need = (target - (double)above) / (double)(wk == 0ull ? 1ull : wk);
   long long k_ties = (long long)ceil(need);
   if (k_ties < 1) k_ties = 1;
   if (k_ties > (long long)tie_count) k_ties = tie_count;
+  while (k_ties > 1 && (double)(above + (unsigned long long)(k_ties - 1) * wk) >= target) --k_ties;
+  while (k_ties < (long long)tie_count && (double)(above + (unsigned long long)k_ties * wk) < target) ++k_ties;
 
   // selection in list order; ties ranked by position with a block scan
   const int per = (U + kCutThreads - 1) / kCutThreads;
@@ -523,15 +552,13 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
 
 // ---------------------------------------------------------------- expansion (A5)
 //
-// One workgroup per group.  The union list is walked in tiles of 1024 entries
-// (thread t takes entry tile*1024 + t, so the selection bytes load coalesced);
-// an entry is kept when any head kept it, its mask being the OR of the heads'
-// bits; a block scan per tile gives its position in list order.  Kept parents
-// are staged, then their children are written with consecutive threads on
-// consecutive outputs, followed by the parentless nodes of the next level.  The
-// final level writes the kept leaves themselves.  The top list (every level-L
-// node) is built the same way with no parents; that launch also checks that the
-// tree matches T.
+// One workgroup per group.  An entry of the union list is kept when any head
+// kept it, its mask being the OR of the heads' bits (selor); kept entries are
+// compacted in list order.  Kept parents are staged, then their children are
+// written with consecutive threads on consecutive outputs, followed by the
+// parentless nodes of the next level.  The final level writes the kept leaves
+// themselves.  The top list (every level-L node) is built the same way with no
+// parents; that launch also checks that the tree matches T.
 
 struct ExpandParams {
   const int64_t* T;
@@ -581,9 +608,10 @@ __global__ void __launch_bounds__(kExpandThreads) expand_level(ExpandParams P) {
   const int32_t* uid = P.uids ? P.uids + (int64_t)gi * P.ucap : nullptr;
 
   // Wave w owns the contiguous entries [w*R, (w+1)*R), read 64 at a time with
-  // consecutive lanes on consecutive entries.  Kept entries are counted with
-  // ballots; one prefix over the wave counts gives each wave's first output
-  // position; a second ballot pass places every kept entry in list order.
+  // consecutive lanes on consecutive entries, kReg loads in flight per batch.
+  // Kept entries are counted with ballots; one prefix over the wave counts gives
+  // each wave's first output position; a second ballot pass places every kept
+  // entry in list order (reusing the registers when one batch covers the range).
   const int lane = tid & 63, wave = tid >> 6;
   const int R = (((U + NW - 1) / NW) + 63) & ~63;
   const int nj = R / 64;
@@ -591,22 +619,23 @@ __global__ void __launch_bounds__(kExpandThreads) expand_level(ExpandParams P) {
   constexpr int kReg = 16;
   uint32_t mv[kReg];
   int32_t iv[kReg];
-  int cnt = 0;
-  if (nj <= kReg) {
+  auto load_batch = [&](int jb) {
 #pragma unroll
     for (int j = 0; j < kReg; ++j) {
-      const int u = w0 + j * 64 + lane;
-      const bool in = j < nj && u < U;
-      mv[j] = in ? so[u] : 0u;
-      iv[j] = in ? uid[u] : 0;
+      const int u = w0 + (jb + j) * 64 + lane;
+      const bool in = jb + j < nj && u < U;
+      const int uu = in ? u : 0;
+      const uint32_t m = so ? so[uu] : 0u;
+      const int32_t id = uid ? uid[uu] : 0;
+      mv[j] = in ? m : 0u;
+      iv[j] = in ? id : 0;
     }
+  };
+  int cnt = 0;
+  for (int jb = 0; jb < nj; jb += kReg) {
+    load_batch(jb);
 #pragma unroll
     for (int j = 0; j < kReg; ++j) cnt += __popcll(__ballot(mv[j] != 0u));
-  } else {
-    for (int j = 0; j < nj; ++j) {
-      const int u = w0 + j * 64 + lane;
-      cnt += __popcll(__ballot(u < U && so[u] != 0u));
-    }
   }
   if (lane == 0) red[wave] = cnt;
   __syncthreads();
@@ -629,19 +658,12 @@ __global__ void __launch_bounds__(kExpandThreads) expand_level(ExpandParams P) {
       st[2 * p] = id; st[2 * p + 1] = (int32_t)m;
     }
   };
-  if (nj <= kReg) {
+  for (int jb = 0; jb < nj; jb += kReg) {
+    if (nj > kReg) load_batch(jb);
 #pragma unroll
     for (int j = 0; j < kReg; ++j) {
       const uint64_t bal = __ballot(mv[j] != 0u);
       if (mv[j]) emit(pos + __popcll(bal & lt), iv[j], mv[j]);
-      pos += __popcll(bal);
-    }
-  } else {
-    for (int j = 0; j < nj; ++j) {
-      const int u = w0 + j * 64 + lane;
-      const uint32_t m = (u < U) ? so[u] : 0u;
-      const uint64_t bal = __ballot(m != 0u);
-      if (m) emit(pos + __popcll(bal & lt), uid[u], m);
       pos += __popcll(bal);
     }
   }
@@ -672,6 +694,237 @@ __global__ void __launch_bounds__(kExpandThreads) expand_level(ExpandParams P) {
   if (tid == 0) P.ncount[gi] = (int32_t)count;
 }
 
+// ---------------------------------------------------------------- small levels
+//
+// A level whose list holds at most kSmallCap nodes per group is cut and expanded
+// by one workgroup per group (route_small).  Each wave cuts one head: its
+// candidates, keyed (score desc, id asc), are sorted in registers by a bitonic
+// network; the masses exp(s - max) in that order, as the same 2^40 fixed point
+// the large-list cut uses, give the running sums, and the cut is the first entry
+// whose running mass reaches p W -- the same integers and the same comparisons
+// as cut_topp, so both paths keep the same nodes.  The heads' kept bits are ORed
+// in LDS and expanded exactly as expand_level does.  A level of at most kTinyCap
+// nodes is also scored by that workgroup (one launch for the whole level);
+// otherwise score_nodes runs first.  The top level's list (every level-L node,
+// every head) is implicit.  Nothing is handed between workgroups inside a launch.
+
+constexpr int kSmallCap = 256;
+constexpr int kTinyCap = 16;
+constexpr int kSmallThreads = 256;
+
+struct SmallParams {
+  int32_t top;                   // 1: the list is every level-L node (ids implicit)
+  const int64_t* T;
+  const int64_t* n_built;        // [L][B] (top launch: stale-tree check)
+  int32_t* ucount_out;           // top launch: the level's list size, for diagnostics
+  int32_t* nids; uint32_t* nmask; int32_t* ncount; int64_t ncap;   // next list
+  int32_t final_;                // 1: write the kept leaves (no children)
+  int32_t C, L;
+  int64_t span_next;             // C^(level-1)
+  int64_t T_cap;
+};
+
+__device__ inline uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Bitonic sort, descending, of the 64*NR values v[r] of lane l (entry r*64 + l).
+template <int NR>
+__device__ inline void wave_sort_desc(uint64_t (&v)[NR], int lane) {
+  constexpr int N = 64 * NR;
+#pragma unroll
+  for (int k2 = 2; k2 <= N; k2 <<= 1) {
+#pragma unroll
+    for (int j = k2 >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+        const int jr = j >> 6;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          if ((r & jr) == 0) {
+            const int r2 = r | jr;
+            const bool desc = ((r * 64) & k2) == 0;
+            const uint64_t a = v[r], b = v[r2];
+            const bool sw = desc ? (a < b) : (a > b);
+            v[r] = sw ? b : a;
+            v[r2] = sw ? a : b;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const uint64_t a = v[r];
+          const uint64_t b = shfl_xor_u64(a, j);
+          const bool lower = (lane & j) == 0;
+          const bool desc = ((r * 64 + lane) & k2) == 0;
+          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+          v[r] = (lower == desc) ? hi : lo;   // the lower entry of a descending pair keeps the larger
+        }
+      }
+    }
+  }
+}
+
+// Top-p cut of one head over a list of U <= 64*NR entries, by one wave; ORs the
+// head's bit into or_bits[u] of every kept entry and returns the kept count.
+template <int NR>
+__device__ inline int cut_head_wave(const float* sc, const uint32_t* cand_mask, uint32_t bit,
+                                    int U, float p, uint32_t* or_bits, int lane) {
+  uint64_t v[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int u = r * 64 + lane;
+    uint64_t e = 0ull;
+    if (u < U && (cand_mask[u] & bit))
+      e = ((uint64_t)order_key(sanitize(sc[u])) << 32) | (uint32_t)(~(uint32_t)u);
+    v[r] = e;
+  }
+  wave_sort_desc<NR>(v, lane);
+  const uint64_t first = rl64(v[0], 0);
+  if (first == 0ull) return 0;                       // no candidates
+  const float mx = key_score((uint32_t)(first >> 32));
+  uint64_t ms[NR];
+  uint32_t nc = 0;
+  uint64_t part = 0ull;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    ms[r] = (v[r] != 0ull) ? fixmass(mass_of(key_score((uint32_t)(v[r] >> 32)), mx)) : 0ull;
+    part += ms[r];
+    nc += __popcll(__ballot(v[r] != 0ull));
+  }
+  int ic;
+  if (p >= 1.0f) {
+    ic = (int)nc - 1;
+  } else {
+    const uint64_t W = wave_sum_u64(part);
+    const double target = (double)p * (double)W;
+    ic = -1;
+    uint64_t carry = 0ull;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint64_t inc = wave_incl_scan<uint64_t>(ms[r]) + carry;
+      const uint64_t reach = __ballot(ms[r] != 0ull && (double)inc >= target);
+      if (ic < 0 && reach != 0ull) ic = r * 64 + __ffsll((long long)reach) - 1;
+      carry = rl64(inc, 63);
+    }
+    if (ic < 0 || ic > (int)nc - 1) ic = (int)nc - 1;
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    if (v[r] != 0ull && r * 64 + lane <= ic) atomicOr(&or_bits[~(uint32_t)v[r]], bit);
+  }
+  return ic + 1;
+}
+
+template <int D, int GP, bool SCORE>
+__global__ void __launch_bounds__(kSmallThreads) route_small(LevelParams P, SmallParams S) {
+  constexpr int NW = kSmallThreads / kWave;
+  __shared__ uint32_t s_cm[kSmallCap];    // candidate masks
+  __shared__ int32_t s_id[kSmallCap];     // node ids
+  __shared__ uint32_t s_or[kSmallCap];    // OR of the heads' kept bits
+  __shared__ int32_t s_pid[kSmallCap];    // kept nodes in list order
+  __shared__ uint32_t s_pm[kSmallCap];
+  __shared__ int32_t s_red[NW];
+  const int gi = blockIdx.x;
+  const int b = gi / P.H_kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int64_t T = S.T[b];
+  if (T < 0) T = 0;
+  if (T > S.T_cap) T = S.T_cap;
+  const uint32_t full = (P.G >= 32) ? 0xffffffffu : ((1u << P.G) - 1u);
+  const int64_t n_here = T / (S.span_next * S.C);      // nodes at this level
+  int U;
+  if (S.top) U = (int)(n_here < P.ucap ? n_here : P.ucap);
+  else U = clamp_count(P.ucount[gi], P.ucap);
+  if (U > kSmallCap) U = kSmallCap;
+  const int32_t* ul = S.top ? nullptr : P.uids + (int64_t)gi * P.ucap;
+
+  if constexpr (SCORE) {
+    float qv[GP][4];
+    load_group_queries<D, GP>(P, gi, lane, qv);
+    for (int u = wave; u < U; u += NW) score_node<D, GP>(P, gi, S.top ? u : ul[u], u, qv, lane);
+    __syncthreads();   // the scores are read back by other waves of this workgroup
+  }
+
+  for (int u = tid; u < kSmallCap; u += kSmallThreads) {
+    s_or[u] = 0u;
+    if (u < U) {
+      s_id[u] = S.top ? u : ul[u];
+      s_cm[u] = S.top ? full : P.umask[(int64_t)gi * P.ucap + u];
+    }
+  }
+  __syncthreads();
+  // ---- cut: wave w takes heads w, w + NW, ...
+  for (int g = wave; g < P.G; g += NW) {
+    const int64_t head = (int64_t)gi * P.G + g;
+    const float* sc = P.scores + head * P.ucap;
+    int kept;
+    if (U <= 64) kept = cut_head_wave<1>(sc, s_cm, 1u << g, U, P.p, s_or, lane);
+    else if (U <= 128) kept = cut_head_wave<2>(sc, s_cm, 1u << g, U, P.p, s_or, lane);
+    else kept = cut_head_wave<4>(sc, s_cm, 1u << g, U, P.p, s_or, lane);
+    if (lane == 0) P.kept[head] = kept;
+  }
+  __syncthreads();
+  // ---- expand: kept entries in list order
+  const uint32_t m = (tid < U) ? s_or[tid] : 0u;
+  const uint64_t bal = __ballot(m != 0u);
+  if (lane == 0) s_red[wave] = __popcll(bal);
+  __syncthreads();
+  int pos = 0, nsel = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    pos += (w < wave) ? s_red[w] : 0;
+    nsel += s_red[w];
+  }
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  pos += __popcll(bal & lt);
+  if (m != 0u) { s_pid[pos] = s_id[tid]; s_pm[pos] = m; }
+  __syncthreads();
+  int32_t* ids = S.nids + (int64_t)gi * S.ncap;
+  uint32_t* msk = S.nmask + (int64_t)gi * S.ncap;
+  int64_t count;
+  if (S.final_) {
+    count = nsel;
+    for (int i = tid; i < nsel && i < S.ncap; i += kSmallThreads) { ids[i] = s_pid[i]; msk[i] = s_pm[i]; }
+  } else {
+    const int64_t n_next = T / S.span_next;
+    int64_t n_orph = n_next - (int64_t)S.C * n_here;
+    if (n_orph < 0) n_orph = 0;
+    const int64_t nch = (int64_t)nsel * S.C;
+    count = nch + n_orph;
+    const int64_t lim = count < S.ncap ? count : S.ncap;
+    const int cshift = __ffs(S.C) - 1;   // C is a power of two
+    for (int64_t o = tid; o < lim; o += kSmallThreads) {
+      if (o < nch) {
+        const int64_t pi = o >> cshift;
+        ids[o] = s_pid[pi] * S.C + (int32_t)(o & (S.C - 1));
+        msk[o] = s_pm[pi];
+      } else {
+        ids[o] = (int32_t)(S.C * n_here + (o - nch));
+        msk[o] = full;
+      }
+    }
+  }
+  if (count > S.ncap) {
+    if (tid == 0) set_status(P.status, ZHA_ECAPACITY);
+    count = S.ncap;
+  }
+  if (tid == 0) {
+    S.ncount[gi] = (int32_t)count;
+    if (S.top) {
+      S.ucount_out[gi] = U;
+      if ((gi % P.H_kv) == 0) {
+        int64_t span = 1;
+        for (int l = 1; l <= S.L; ++l) {
+          span *= S.C;
+          if (S.n_built[(int64_t)(l - 1) * P.B + b] != T / span) set_status(P.status, ZHA_ESTALE);
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- host
 
 static void launch_score(const LevelParams& P, int64_t ucap, hipStream_t s) {
@@ -691,6 +944,21 @@ static void launch_score(const LevelParams& P, int64_t ucap, hipStream_t s) {
     if (GP == 4) hipLaunchKernelGGL((score_nodes<64, 4>), grid, dim3(256), 0, s, P);
     else if (GP == 8) hipLaunchKernelGGL((score_nodes<64, 8>), grid, dim3(256), 0, s, P);
     else hipLaunchKernelGGL((score_nodes<64, 16>), grid, dim3(256), 0, s, P);
+  }
+}
+
+template <bool SCORE>
+static void launch_small_t(const LevelParams& P, const SmallParams& S, hipStream_t s) {
+  const dim3 grid((unsigned)(P.B * P.H_kv));
+  const int GP = P.G <= 4 ? 4 : (P.G <= 8 ? 8 : 16);
+  if (P.d == 128) {
+    if (GP == 4) hipLaunchKernelGGL((route_small<128, 4, SCORE>), grid, dim3(kSmallThreads), 0, s, P, S);
+    else if (GP == 8) hipLaunchKernelGGL((route_small<128, 8, SCORE>), grid, dim3(kSmallThreads), 0, s, P, S);
+    else hipLaunchKernelGGL((route_small<128, 16, SCORE>), grid, dim3(kSmallThreads), 0, s, P, S);
+  } else {
+    if (GP == 4) hipLaunchKernelGGL((route_small<64, 4, SCORE>), grid, dim3(kSmallThreads), 0, s, P, S);
+    else if (GP == 8) hipLaunchKernelGGL((route_small<64, 8, SCORE>), grid, dim3(kSmallThreads), 0, s, P, S);
+    else hipLaunchKernelGGL((route_small<64, 16, SCORE>), grid, dim3(kSmallThreads), 0, s, P, S);
   }
 }
 
@@ -749,19 +1017,27 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
   span[0] = 1;
   for (int l = 1; l <= L; ++l) span[l] = span[l - 1] * cfg->C;
 
-  // top list: every level-L node, every head
+  // Levels whose lists hold at most kSmallCap nodes run fused (score, cut and
+  // expand in one launch); longer ones run score_nodes, cut_topp, expand_level.
+  auto small = [&](int l) { return w.cap[l - 1] <= kSmallCap; };
+  auto tiny = [&](int l) { return w.cap[l - 1] <= kTinyCap; };
+  // an implicit top list needs the level scored in the same launch
+  const bool top_implicit = tiny(L);
   ExpandParams E;
   E.T = T; E.status = (int32_t*)ws; E.n_built = tree->n_built;
   E.B = cfg->B; E.H_kv = cfg->H_kv; E.G = cfg->G; E.C = cfg->C; E.L = L; E.T_cap = cfg->T_cap;
   E.xstage = (int32_t*)(base + w.xstage); E.xcap = w.stage_cap;
-  E.level = 0; E.final_ = 0;
-  E.uids = nullptr; E.umask = nullptr; E.ucount = nullptr; E.ucap = 1; E.selor = nullptr;
-  E.nids = (int32_t*)(base + w.uids[L - 1]);
-  E.nmask = (uint32_t*)(base + w.umask[L - 1]);
-  E.ncount = (int32_t*)(base + w.ucount[L - 1]);
-  E.ncap = w.cap[L - 1];
-  E.span_next = span[L];
-  hipLaunchKernelGGL(expand_level, dim3(BH), dim3(kExpandThreads), 0, s, E);
+  if (!top_implicit) {
+    // top list: every level-L node, every head
+    E.level = 0; E.final_ = 0;
+    E.uids = nullptr; E.umask = nullptr; E.ucount = nullptr; E.ucap = 1; E.selor = nullptr;
+    E.nids = (int32_t*)(base + w.uids[L - 1]);
+    E.nmask = (uint32_t*)(base + w.umask[L - 1]);
+    E.ncount = (int32_t*)(base + w.ucount[L - 1]);
+    E.ncap = w.cap[L - 1];
+    E.span_next = span[L];
+    hipLaunchKernelGGL(expand_level, dim3(BH), dim3(kExpandThreads), 0, s, E);
+  }
 
   for (int l = L; l >= 1; --l) {
     LevelParams P = level_params(cfg, q, tree, l, p, ws, w);
@@ -772,6 +1048,34 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
     P.scores = (float*)(base + w.scores[l - 1]);
     P.sel = (uint8_t*)(base + w.sel[l - 1]);
     P.kept = (int32_t*)(base + w.kept[l - 1]);
+    int32_t* nids; uint32_t* nmask; int32_t* ncount; int64_t ncap;
+    if (l > 1) {
+      nids = (int32_t*)(base + w.uids[l - 2]);
+      nmask = (uint32_t*)(base + w.umask[l - 2]);
+      ncount = (int32_t*)(base + w.ucount[l - 2]);
+      ncap = w.cap[l - 2];
+    } else {
+      nids = leaf_ids; nmask = leaf_mask; ncount = leaf_count; ncap = cfg->leaf_cap;
+    }
+    if (small(l)) {
+      P.selor = nullptr;
+      SmallParams S;
+      S.top = (l == L && top_implicit) ? 1 : 0;
+      S.T = T; S.n_built = tree->n_built;
+      S.ucount_out = (int32_t*)(base + w.ucount[l - 1]);
+      S.nids = nids; S.nmask = nmask; S.ncount = ncount; S.ncap = ncap;
+      S.final_ = (l == 1) ? 1 : 0;
+      S.C = cfg->C; S.L = L;
+      S.span_next = span[l - 1];
+      S.T_cap = cfg->T_cap;
+      if (tiny(l)) {
+        launch_small_t<true>(P, S, s);
+      } else {
+        launch_score(P, P.ucap, s);
+        launch_small_t<false>(P, S, s);
+      }
+      continue;
+    }
     P.selor = (uint32_t*)(base + w.selor[l - 1]);
     launch_score(P, P.ucap, s);
     hipLaunchKernelGGL(cut_topp, dim3(BHq), dim3(kCutThreads), 0, s, P);
@@ -779,17 +1083,8 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
     E.uids = P.uids; E.umask = P.umask; E.ucount = P.ucount; E.ucap = P.ucap;
     E.selor = P.selor;
     E.span_next = span[l - 1];
-    if (l > 1) {
-      E.final_ = 0;
-      E.nids = (int32_t*)(base + w.uids[l - 2]);
-      E.nmask = (uint32_t*)(base + w.umask[l - 2]);
-      E.ncount = (int32_t*)(base + w.ucount[l - 2]);
-      E.ncap = w.cap[l - 2];
-    } else {
-      E.final_ = 1;
-      E.nids = leaf_ids; E.nmask = leaf_mask; E.ncount = leaf_count;
-      E.ncap = cfg->leaf_cap;
-    }
+    E.final_ = (l == 1) ? 1 : 0;
+    E.nids = nids; E.nmask = nmask; E.ncount = ncount; E.ncap = ncap;
     hipLaunchKernelGGL(expand_level, dim3(BH), dim3(kExpandThreads), 0, s, E);
   }
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;

@@ -119,6 +119,11 @@ CASES = {
     "deep": (synth.WORKLOADS["deep"].with_(H_kv=1, C=4, L=5, N=4 ** 5 * 3 + 50), 4 ** 5 * 3 + 50),
     "rope": (synth.WORKLOADS["rope_batch"].with_(B=2, H_kv=1, G=4, C=16, L=3, n_clusters=64),
              16 ** 3 * 2 + 40),
+    # one level of 20000 / 30000 leaves: candidate pools beyond 16384 entries (the
+    # cut's LDS staging) and beyond 24576 (its register capacity), and final
+    # expansions longer than one register batch per wave
+    "wide20k": (synth.WORKLOADS["tiny"].with_(G=2, C=2, L=1, R=2, n_clusters=64), 40000),
+    "wide30k": (synth.WORKLOADS["tiny"].with_(G=2, C=2, L=1, R=2, n_clusters=64), 60000 + 1),
 }
 
 
