@@ -331,8 +331,8 @@ __device__ inline void load_chunk_rows(const uint16_t* klane, const uint16_t* vl
   buf.kmask = kr < nv ? hm : 0u;
 }
 
-template <int D, int GP>
-__device__ inline void compute_chunk(AttendSmemB<D, GP>& sm, const ChunkBuf<D>& buf,
+template <int D, int GP, typename SM>
+__device__ inline void compute_chunk(SM& sm, const ChunkBuf<D>& buf,
                                      const bf16x8_t* a_hi, const bf16x8_t* a_lo,
                                      int lane, int wave,
                                      float* m_run, float* l_run, float (*o)[8]) {
@@ -611,6 +611,324 @@ attend_partial_bf16(AttendParams P) {
   }
 }
 
+// ------------------------------------------------ bf16 path, pipelined over items
+//
+// The contiguous-chunk kernel (dense, or leaves of C >= 16 keys).  Everything an
+// item needs besides its K/V rows is fetched while the previous item is being
+// computed, so a workgroup always has K/V loads in flight:
+//   * per-group geometry (list length, leaf count, open-chunk length, sink mask)
+//     is read once per workgroup into LDS;
+//   * the next item's leaf entries and, when its group changes, its queries are
+//     loaded into registers during the current item's chunk loop and moved to
+//     LDS after it;
+//   * each wave issues the K/V loads of its first chunk of the next item before
+//     the current item's per-wave states are merged and written.
+// Items are assigned round-robin (item = blockIdx.x + k * gridDim.x).
+
+template <int D, int GP>
+struct PipeSmem {
+  int32_t item_prefix[kMaxGroups + 1];
+  int32_t g_U[kMaxGroups];           // leaf-list entries (dense: complete leaves)
+  int32_t g_n1[kMaxGroups];          // complete leaves
+  int32_t g_open[kMaxGroups];        // open-chunk length T - C n1
+  uint32_t g_smask[kMaxGroups];      // heads that take the sink from the tail item
+  int32_t scan[16];
+  int32_t lid[kItemKeys / 16 + 2];   // leaf entries of the current item (C >= 16)
+  uint32_t lmask[kItemKeys / 16 + 2];
+  float qs[GP * D];                  // the current group's queries, times scale*log2(e)
+  float p[kWavesPerWg][16][GP];
+  float alpha[kWavesPerWg][16];
+  float state[kWavesPerWg][GP][D + 2];
+};
+
+struct PipeItem {
+  int gi, li;
+  int tail;          // the sink + open-chunk item
+  int64_t kbase;     // first list key (regular items)
+  int nkeys;         // list keys in the item (regular items)
+  int64_t first;     // first leaf entry of the item
+  int nent;          // leaf entries touched
+  int nchunks;
+};
+
+template <int D, int GP>
+__device__ inline PipeItem pipe_item(const AttendParams& P, const PipeSmem<D, GP>& sm, int BH,
+                                     int item, int cshift) {
+  PipeItem it;
+  it.gi = find_group(sm.item_prefix, BH, item);
+  it.li = item - sm.item_prefix[it.gi];
+  const int items = sm.item_prefix[it.gi + 1] - sm.item_prefix[it.gi];
+  it.tail = (it.li == items - 1) ? 1 : 0;
+  it.kbase = 0; it.nkeys = 0; it.first = 0; it.nent = 0;
+  if (it.tail) {
+    it.nchunks = 1 + (sm.g_open[it.gi] + 15) / 16;
+  } else {
+    it.kbase = (int64_t)it.li * kItemKeys;
+    const int64_t left = ((int64_t)sm.g_U[it.gi] << cshift) - it.kbase;
+    it.nkeys = (int)(left < kItemKeys ? left : kItemKeys);
+    it.nchunks = (it.nkeys + 15) / 16;
+    if (P.leaf_ids != nullptr) {
+      it.first = it.kbase >> cshift;
+      it.nent = (int)(((it.kbase + it.nkeys - 1) >> cshift) - it.first + 1);
+    }
+  }
+  return it;
+}
+
+// Rows of chunk c of an item: row0 .. row0+nv-1 of the group under head mask hm.
+// ent_id / ent_mask: the leaf entry covering the chunk (sparse regular items).
+template <int D, int GP>
+__device__ inline void pipe_chunk_rows(const AttendParams& P, const PipeSmem<D, GP>& sm,
+                                       const PipeItem& it, int c, int cshift, uint32_t full,
+                                       int32_t ent_id, uint32_t ent_mask,
+                                       int64_t& row0, int& nv, uint32_t& hm) {
+  if (it.tail) {
+    if (c == 0) { row0 = 0; nv = 1; hm = sm.g_smask[it.gi]; }
+    else {
+      const int off = 16 * (c - 1);
+      row0 = ((int64_t)sm.g_n1[it.gi] << cshift) + off;
+      nv = min(16, sm.g_open[it.gi] - off);
+      hm = full;
+    }
+  } else {
+    const int64_t gk = it.kbase + (int64_t)c * 16;
+    nv = min(16, it.nkeys - 16 * c);     // partial only when C < 16 (dense)
+    if (P.leaf_ids == nullptr) { row0 = gk; hm = full; }
+    else { row0 = (int64_t)ent_id * P.C + (gk & (P.C - 1)); hm = ent_mask; }
+  }
+  row0 = __builtin_amdgcn_readfirstlane((int)row0);
+  nv = __builtin_amdgcn_readfirstlane(nv);
+  hm = __builtin_amdgcn_readfirstlane(hm);
+}
+
+template <int D, int GP>
+__global__ void __launch_bounds__(256)
+attend_partial_bf16_pipe(AttendParams P) {
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(GP == 4 || GP == 8 || GP == 16, "padded heads");
+  constexpr int KSTEPS = D / 32;
+  constexpr int LPR = D / 8;
+  constexpr int QPT = (GP * D + 255) / 256;    // query floats per thread when staging
+  __shared__ PipeSmem<D, GP> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int BH = P.B * P.H_kv;
+  const uint32_t full = (P.G >= 32) ? 0xffffffffu : ((1u << P.G) - 1u);
+  const int hrow = (lane >> 4) * 4;
+  const int cshift = __ffs(P.C) - 1;
+
+  // ---- per-group geometry and the item prefix, once per workgroup
+  int total;
+  {
+    const int per = (BH + blockDim.x - 1) / blockDim.x;
+    const int g0 = tid * per;
+    int mine = 0;
+    for (int k = 0; k < per; ++k) {
+      const int gi = g0 + k;
+      if (gi < BH) {
+        const GroupInfo g = group_info(P, gi);
+        mine += g.items;
+        sm.g_U[gi] = g.U;
+        sm.g_n1[gi] = g.n1;
+        sm.g_open[gi] = (int)(g.T - (int64_t)g.n1 * P.C);
+        sm.g_smask[gi] = sink_mask(P, gi, g, full);
+      }
+    }
+    int acc = block_exclusive_scan<int>(mine, sm.scan, &total);
+    for (int k = 0; k < per; ++k)
+      if (g0 + k < BH) {
+        sm.item_prefix[g0 + k] = acc;
+        acc += sm.g_U[g0 + k] >= 0 ? (int)((((int64_t)sm.g_U[g0 + k] << cshift) + kTileKeys - 1) / kTileKeys + kTilesPerItem - 1) / kTilesPerItem + 1 : 1;
+      }
+    if (tid == 0) sm.item_prefix[BH] = total;
+    __syncthreads();
+  }
+  int item = blockIdx.x;
+  if (item >= total) return;
+
+  // ---- the first item: staged synchronously
+  PipeItem it = pipe_item<D, GP>(P, sm, BH, item, cshift);
+  if (!it.tail && P.leaf_ids != nullptr && tid < it.nent) {
+    const int64_t off = (int64_t)it.gi * P.leaf_cap + it.first + tid;
+    int32_t leaf = P.leaf_ids[off];
+    uint32_t m = P.leaf_mask[off] & full;
+    if (leaf < 0 || leaf >= sm.g_n1[it.gi]) { leaf = 0; m = 0u; }
+    sm.lid[tid] = leaf;
+    sm.lmask[tid] = m;
+  }
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int idx = tid + 256 * k;
+    if (idx < GP * D)
+      sm.qs[idx] = (idx < P.G * D) ? P.q[(int64_t)it.gi * P.G * D + idx] * P.qscale : 0.0f;
+  }
+  __syncthreads();
+
+  bf16x8_t a_hi[KSTEPS], a_lo[KSTEPS];
+  auto convert_q = [&]() {
+    const int row = lane & 15;
+    const int kg = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      bf16x8_t hi, lo;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = (row < GP) ? sm.qs[row * D + s * 32 + kg * 8 + j] : 0.0f;
+        const uint16_t h16 = f32_to_bf16_rne(x);
+        const float r1 = x - __uint_as_float((uint32_t)h16 << 16);
+        const uint16_t l16 = f32_to_bf16_rne(r1);
+        hi[j] = __builtin_bit_cast(__bf16, h16);
+        lo[j] = __builtin_bit_cast(__bf16, l16);
+      }
+      a_hi[s] = hi; a_lo[s] = lo;
+    }
+  };
+  convert_q();
+
+  ChunkBuf<D> cur, nxt;
+  {
+    int64_t r0; int nv; uint32_t hm;
+    if (wave < it.nchunks) {
+      int32_t eid = 0; uint32_t em = 0u;
+      if (!it.tail && P.leaf_ids != nullptr) {
+        const int loc = (int)(((it.kbase + 16 * wave) >> cshift) - it.first);
+        eid = sm.lid[loc]; em = sm.lmask[loc];
+      }
+      pipe_chunk_rows<D, GP>(P, sm, it, wave, cshift, full, eid, em, r0, nv, hm);
+      const int64_t kv_base = (int64_t)it.gi * P.T_cap;
+      load_chunk_rows<D>((const uint16_t*)P.K + kv_base * D + (lane >> 4) * 8,
+                         (const uint16_t*)P.V + kv_base * D + (lane % LPR) * 8, lane, r0, nv, hm, cur);
+    }
+  }
+
+  for (;;) {
+    // ---- prefetch what the next item needs besides K/V
+    const int next = item + gridDim.x;
+    const bool has_next = next < total;
+    PipeItem nx = it;
+    if (has_next) nx = pipe_item<D, GP>(P, sm, BH, next, cshift);
+    const bool new_q = has_next && nx.gi != it.gi;
+    int32_t pf_id = 0;
+    uint32_t pf_m = 0u;
+    if (has_next && !nx.tail && P.leaf_ids != nullptr && tid < nx.nent) {
+      const int64_t off = (int64_t)nx.gi * P.leaf_cap + nx.first + tid;
+      pf_id = P.leaf_ids[off];
+      pf_m = P.leaf_mask[off];
+    }
+    float pf_q[QPT];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int idx = tid + 256 * k;
+      pf_q[k] = (new_q && idx < P.G * D) ? P.q[(int64_t)nx.gi * P.G * D + idx] : 0.0f;
+    }
+    // this wave's first chunk of the next item: its leaf entry
+    int32_t nf_id = 0;
+    uint32_t nf_m = 0u;
+    if (has_next && !nx.tail && P.leaf_ids != nullptr && wave < nx.nchunks) {
+      const int64_t e = (nx.kbase + 16 * wave) >> cshift;
+      const int64_t off = (int64_t)nx.gi * P.leaf_cap + e;
+      nf_id = P.leaf_ids[off];
+      nf_m = P.leaf_mask[off] & full;
+      if (nf_id < 0 || nf_id >= sm.g_n1[nx.gi]) { nf_id = 0; nf_m = 0u; }
+    }
+
+    // ---- the current item's chunks: chunk c+4's loads in flight while c computes
+    float m_run[4], l_run[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.0f; }
+    float o[GP][8];
+#pragma unroll
+    for (int hh = 0; hh < GP; ++hh)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[hh][j] = 0.0f;
+    {
+      const int64_t kv_base = (int64_t)it.gi * P.T_cap;
+      const uint16_t* klane = (const uint16_t*)P.K + kv_base * D + (lane >> 4) * 8;
+      const uint16_t* vlane = (const uint16_t*)P.V + kv_base * D + (lane % LPR) * 8;
+      for (int c = wave; c < it.nchunks; c += kWavesPerWg) {
+        const bool more = c + kWavesPerWg < it.nchunks;
+        if (more) {
+          int32_t eid = 0; uint32_t em = 0u;
+          if (!it.tail && P.leaf_ids != nullptr) {
+            const int loc = (int)(((it.kbase + 16 * (c + kWavesPerWg)) >> cshift) - it.first);
+            eid = sm.lid[loc]; em = sm.lmask[loc];
+          }
+          int64_t r0; int nv; uint32_t hm;
+          pipe_chunk_rows<D, GP>(P, sm, it, c + kWavesPerWg, cshift, full, eid, em, r0, nv, hm);
+          load_chunk_rows<D>(klane, vlane, lane, r0, nv, hm, nxt);
+        }
+        compute_chunk<D, GP>(sm, cur, a_hi, a_lo, lane, wave, m_run, l_run, o);
+        if (more) cur = nxt;
+      }
+    }
+
+    // ---- issue the next item's first chunk before merging this one
+    if (has_next && wave < nx.nchunks) {
+      int64_t r0; int nv; uint32_t hm;
+      pipe_chunk_rows<D, GP>(P, sm, nx, wave, cshift, full, nf_id, nf_m, r0, nv, hm);
+      const int64_t kv_base = (int64_t)nx.gi * P.T_cap;
+      load_chunk_rows<D>((const uint16_t*)P.K + kv_base * D + (lane >> 4) * 8,
+                         (const uint16_t*)P.V + kv_base * D + (lane % LPR) * 8, lane, r0, nv, hm, cur);
+    }
+
+    // ---- wave totals: l over the 16 key columns, o over the V row groups
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = l_run[i];
+      v += swz_xor<1>(v);
+      v += swz_xor<2>(v);
+      v += swz_xor<4>(v);
+      v += swz_xor<8>(v);
+      l_run[i] = v;
+    }
+#pragma unroll
+    for (int hh = 0; hh < GP; ++hh)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float v = o[hh][j];
+        if (LPR <= 8) v += swz_xor<8>(v);
+        v += swz_xor<16>(v);
+        v += shfl_xor32(v);
+        o[hh][j] = v;
+      }
+    if ((lane & 15) == 0 && hrow < GP) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sm.state[wave][hrow + i][0] = m_run[i];
+        sm.state[wave][hrow + i][1] = l_run[i];
+      }
+    }
+    if (lane < LPR) {
+#pragma unroll
+      for (int hh = 0; hh < GP; ++hh)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sm.state[wave][hh][2 + lane * 8 + j] = o[hh][j];
+    }
+    __syncthreads();
+    write_partial_state<D, GP>(P, sm.state, it.gi, it.li);
+    if (!has_next) break;
+    // ---- the next item's entries and queries into LDS
+    if (!nx.tail && P.leaf_ids != nullptr && tid < nx.nent) {
+      if (pf_id < 0 || pf_id >= sm.g_n1[nx.gi]) { pf_id = 0; pf_m = 0u; }
+      sm.lid[tid] = pf_id;
+      sm.lmask[tid] = pf_m & full;
+    }
+    if (new_q) {
+#pragma unroll
+      for (int k = 0; k < QPT; ++k) {
+        const int idx = tid + 256 * k;
+        if (idx < GP * D) sm.qs[idx] = pf_q[k] * P.qscale;
+      }
+    }
+    __syncthreads();
+    if (new_q) convert_q();
+    item = next;
+    it = nx;
+  }
+}
+
 // ---------------------------------------------------------------- fp32 path
 //
 // fp32 K/V (exact-precision runs): VALU only.  Lane = key slot for the scores
@@ -787,7 +1105,7 @@ static void launch_partial(const AttendParams& P, int kv_dtype, int grid, hipStr
   const bool contig = (P.leaf_ids == nullptr) || (P.C >= 16);
   if (kv_dtype == ZHA_BF16) {
     if (contig)
-      hipLaunchKernelGGL((attend_partial_bf16<D, GP, true>), dim3(grid), dim3(256), 0, s, P);
+      hipLaunchKernelGGL((attend_partial_bf16_pipe<D, GP>), dim3(grid), dim3(256), 0, s, P);
     else
       hipLaunchKernelGGL((attend_partial_bf16<D, GP, false>), dim3(grid), dim3(256), 0, s, P);
   } else {
