@@ -26,6 +26,7 @@
 #include "zha_internal.hpp"
 
 #include <float.h>
+#include <type_traits>
 
 namespace zha {
 
@@ -198,6 +199,48 @@ __device__ inline float mass_of(float s, float mx) {
 
 __device__ inline float sanitize(float s) { return isfinite(s) ? s : -FLT_MAX; }
 
+__device__ inline uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Bitonic sort, descending, of the 64*NR values v[r] of lane l (entry r*64 + l).
+template <int NR>
+__device__ inline void wave_sort_desc(uint64_t (&v)[NR], int lane) {
+  constexpr int N = 64 * NR;
+#pragma unroll
+  for (int k2 = 2; k2 <= N; k2 <<= 1) {
+#pragma unroll
+    for (int j = k2 >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+        const int jr = j >> 6;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          if ((r & jr) == 0) {
+            const int r2 = r | jr;
+            const bool desc = ((r * 64) & k2) == 0;
+            const uint64_t a = v[r], b = v[r2];
+            const bool sw = desc ? (a < b) : (a > b);
+            v[r] = sw ? b : a;
+            v[r2] = sw ? a : b;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const uint64_t a = v[r];
+          const uint64_t b = shfl_xor_u64(a, j);
+          const bool lower = (lane & j) == 0;
+          const bool desc = ((r * 64 + lane) & k2) == 0;
+          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+          v[r] = (lower == desc) ? hi : lo;   // the lower entry of a descending pair keeps the larger
+        }
+      }
+    }
+  }
+}
+
 constexpr int kRelBuckets = 2048;
 constexpr float kRelScale = 64.0f;     // buckets per unit of score
 constexpr int kSortMax = 1024;         // largest crossing bucket sorted exactly
@@ -332,30 +375,47 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
       }
       __syncthreads();
       const int lane = tid & 63;
-      if (n2 <= kWave) {
-        // one wave sorts and scans; the others wait at the next barrier
+      if (n2 <= 4 * kWave) {
+        // one wave sorts in registers and scans; the others wait at the next barrier
         if (tid < kWave) {
-          for (int k2 = 2; k2 <= n2; k2 <<= 1) {
-            for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
-              const int ij = lane ^ jj;
-              unsigned long long a = 0ull, b = 0ull;
-              if (lane < n2 && ij > lane) { a = sm.u.sortbuf[lane]; b = sm.u.sortbuf[ij]; }
-              wave_lds_sync();
-              if (lane < n2 && ij > lane) {
-                const bool desc = (lane & k2) == 0;
-                if (desc ? (a < b) : (a > b)) { sm.u.sortbuf[lane] = b; sm.u.sortbuf[ij] = a; }
-              }
-              wave_lds_sync();
+          auto finish = [&](auto& v, auto nr_tag) {
+            constexpr int NR = decltype(nr_tag)::value;
+            wave_sort_desc<NR>(v, lane);
+            int ic = -1;
+            unsigned long long carry = 0ull;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+              const uint64_t e = v[r];
+              unsigned long long mi = 0ull;
+              if ((uint32_t)(e >> 32) != 0u) mi = fixmass(mass_of(key_score((uint32_t)(e >> 32)), mx));
+              const unsigned long long inc = wave_incl_scan<unsigned long long>(mi) + carry;
+              const uint64_t reach = __ballot(mi != 0ull && (double)(above_b + inc) >= target);
+              if (ic < 0 && reach != 0ull) ic = r * 64 + __ffsll((long long)reach) - 1;
+              carry = rl64(inc, 63);
             }
+            if (ic < 0 || ic > cstar - 1) ic = cstar - 1;
+            // the cut entry, in sorted position ic, back to LDS for every wave
+            const int r_ic = ic >> 6, l_ic = ic & 63;
+            uint64_t ce = 0ull;
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+              if (r == r_ic) ce = rl64(v[r], l_ic);
+            if (lane == 0) { sm.count = 0; sm.u.sortbuf[0] = ce; }
+          };
+          if (n2 <= kWave) {
+            uint64_t v[1] = {lane < n2 ? (uint64_t)sm.u.sortbuf[lane] : 0ull};
+            finish(v, std::integral_constant<int, 1>());
+          } else if (n2 <= 2 * kWave) {
+            uint64_t v[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) v[r] = (r * 64 + lane < n2) ? (uint64_t)sm.u.sortbuf[r * 64 + lane] : 0ull;
+            finish(v, std::integral_constant<int, 2>());
+          } else {
+            uint64_t v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = (r * 64 + lane < n2) ? (uint64_t)sm.u.sortbuf[r * 64 + lane] : 0ull;
+            finish(v, std::integral_constant<int, 4>());
           }
-          unsigned long long mi = 0ull;
-          const unsigned long long e = (lane < n2) ? sm.u.sortbuf[lane] : 0ull;
-          if ((uint32_t)(e >> 32) != 0u) mi = fixmass(mass_of(key_score((uint32_t)(e >> 32)), mx));
-          const unsigned long long inc = wave_incl_scan<unsigned long long>(mi);
-          const uint64_t reach = __ballot(mi != 0ull && (double)(above_b + inc) >= target);
-          int ic = reach ? (__ffsll((long long)reach) - 1) : cstar - 1;
-          if (ic > cstar - 1) ic = cstar - 1;
-          if (lane == 0) sm.count = ic;
         }
       } else {
         for (int k2 = 2; k2 <= n2; k2 <<= 1) {
@@ -723,48 +783,6 @@ struct SmallParams {
   int64_t span_next;             // C^(level-1)
   int64_t T_cap;
 };
-
-__device__ inline uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Bitonic sort, descending, of the 64*NR values v[r] of lane l (entry r*64 + l).
-template <int NR>
-__device__ inline void wave_sort_desc(uint64_t (&v)[NR], int lane) {
-  constexpr int N = 64 * NR;
-#pragma unroll
-  for (int k2 = 2; k2 <= N; k2 <<= 1) {
-#pragma unroll
-    for (int j = k2 >> 1; j > 0; j >>= 1) {
-      if (j >= 64) {
-        const int jr = j >> 6;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          if ((r & jr) == 0) {
-            const int r2 = r | jr;
-            const bool desc = ((r * 64) & k2) == 0;
-            const uint64_t a = v[r], b = v[r2];
-            const bool sw = desc ? (a < b) : (a > b);
-            v[r] = sw ? b : a;
-            v[r2] = sw ? a : b;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const uint64_t a = v[r];
-          const uint64_t b = shfl_xor_u64(a, j);
-          const bool lower = (lane & j) == 0;
-          const bool desc = ((r * 64 + lane) & k2) == 0;
-          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-          v[r] = (lower == desc) ? hi : lo;   // the lower entry of a descending pair keeps the larger
-        }
-      }
-    }
-  }
-}
 
 // Top-p cut of one head over a list of U <= 64*NR entries, by one wave; ORs the
 // head's bit into or_bits[u] of every kept entry and returns the kept count.

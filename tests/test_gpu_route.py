@@ -245,3 +245,54 @@ def test_all_equal_scores_take_lowest_ids(p):
     assert cut.m == m
     assert int(lst.count[0, 0]) == m
     assert lst.ids[0, 0, :m].cpu().tolist() == list(range(m))
+
+
+@pytest.mark.parametrize("n_band", [40, 120, 200, 600])
+@pytest.mark.parametrize("p", [0.5, 0.9])
+def test_cut_crossing_bucket_sizes(n_band, p):
+    """Scores set exactly through the summaries (k_hat = 0, so a node's score is
+    its best b_hat): n_band nodes are spread over one 1/64-wide score interval
+    around the mass cut, so the bucket the cut falls in holds about n_band
+    entries (one wave sorts up to 256 of them in registers, more take the block
+    sort).  The rest sit far above (kept) or below (dropped)."""
+    rng = np.random.default_rng(7 + n_band)
+    n_hi, n_lo = 5, 3000
+    n = n_hi + n_band + n_lo
+    C, d, R = 16, 64, 2
+    T = n * C
+    s = np.empty(n)
+    s[:n_hi] = 3.0 + rng.uniform(0, 1, n_hi)
+    # the band holds three times the mass of the nodes above it, so the cut
+    # (1/3 of the way in at p = 0.5, 87% at p = 0.9) falls inside it
+    b0 = math.log(3.0 * np.exp(s[:n_hi]).sum() / n_band)
+    s[n_hi:n_hi + n_band] = b0 + rng.uniform(0, 1.0 / 64, n_band)
+    s[n_hi + n_band:] = b0 - 14.0 + rng.uniform(0, 1, n_lo)
+    s = np.float32(s)
+    perm = rng.permutation(n)
+    s = s[perm]
+    cfg = zha.Config(B=1, H_kv=1, G=1, d=d, C=C, L=1, R=R, T_cap=T, kv_dtype=zha.F32)
+    khat = np.zeros((n, R, d), np.float32)
+    bhat = np.stack([s, s - np.float32(1.0)], axis=1).astype(np.float32)
+    trees = [[[{"khat": khat, "bhat": bhat}]]]
+    tree = upload(cfg, trees, T)
+    ws = zha.new_workspace(cfg)
+    q = torch.zeros(1, 1, d, device=DEV)
+    ids = torch.arange(n, dtype=torch.int32).reshape(1, 1, n)
+    mask = torch.ones(1, 1, n, dtype=torch.int32)
+    count = torch.tensor([[n]], dtype=torch.int32)
+    scores = torch.empty(1, 1, n, device=DEV)
+    sel = torch.zeros(1, 1, n, dtype=torch.uint8, device=DEV)
+    zha.route_level(cfg, 1, q, tree, p, ids.to(DEV), mask.to(DEV), count.to(DEV), scores, sel, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(scores[0, 0].cpu(), torch.tensor(s)), "scores are the b_hat values"
+    cut = O.topp_cut(np.arange(n), s.astype(np.float64), p)
+    gsel = np.nonzero(sel[0, 0].cpu().numpy())[0]
+    np.testing.assert_array_equal(np.sort(gsel), np.sort(cut.selected))
+    # and the whole route (fused paths) keeps the same leaves
+    lst = zha.LeafList(cfg, DEV)
+    Tt = torch.tensor([T], dtype=torch.int64, device=DEV)
+    zha.route(cfg, q, tree, Tt, p, lst.ids, lst.mask, lst.count, ws)
+    torch.cuda.synchronize()
+    m = int(lst.count[0, 0])
+    np.testing.assert_array_equal(lst.ids[0, 0, :m].cpu().numpy(), np.sort(cut.selected))
+    assert zha.ws_status(ws) == 0
