@@ -10,8 +10,12 @@
 // is a candidate of at least one of its G query heads, ascending, with a G-bit
 // mask of the heads it is a candidate for.  Scoring reads each listed node's
 // summary once and scores it for all G heads; each head then cuts its own
-// candidates; the next level's union list is expanded from the OR of the heads'
-// selections.  Everything stays on the device between levels.
+// candidates; the kept entries of all heads (a node kept by any head, with the
+// OR of their bits) are compacted into the level's kept list.  The next level's
+// union list is never written out: entry u is child u % C of kept node u / C, or,
+// past the children, a parentless node; the top level's list is every level-L
+// node.  (An explicit list can be given instead, for zha_route_level.)
+// Everything stays on the device between levels.
 //
 // The top-p cut needs only the threshold, not a full sort.  Candidates are
 // histogrammed (count and mass) over 2048 buckets of relative score
@@ -30,25 +34,119 @@
 
 namespace zha {
 
+// The candidate union list of one level, per group: explicit arrays, or implicit
+// from the kept list of the level above (null kept list: every node, the top).
+struct ListRef {
+  const int32_t* ids;          // explicit: [BH][cap] ids, ascending (null: implicit)
+  const uint32_t* mask;        // explicit: [BH][cap] head masks
+  const int32_t* count;        // explicit: [BH]
+  int64_t cap;
+  const int32_t* pids;         // implicit: [BH][pcap] kept ids of the level above (null: top)
+  const uint32_t* pmask;       // implicit: their OR'd head masks
+  const int32_t* pcount;       // implicit: [BH]
+  int64_t pcap;
+  const int64_t* T;            // [B]
+  int64_t T_cap;
+  int64_t span;                // C^level: tokens per node of this level
+  int32_t C, cshift, H_kv;
+  uint32_t full;               // every head's bit
+};
+
+struct ListGeo {
+  int U;          // entries
+  int np;         // implicit: kept parents (children are entries [0, np*C))
+  int64_t orph0;  // implicit: id of the first parentless node
+};
+
+__device__ inline ListGeo list_geo(const ListRef& L, int gi, int64_t ucap) {
+  ListGeo g{0, 0, 0};
+  if (L.ids != nullptr) {
+    int32_t u = L.count[gi];
+    g.U = u < 0 ? 0 : (u > L.cap ? (int)L.cap : u);
+  } else {
+    int64_t T = L.T[gi / L.H_kv];
+    if (T < 0) T = 0;
+    if (T > L.T_cap) T = L.T_cap;
+    const int64_t n_here = T / L.span;
+    int64_t U;
+    if (L.pids != nullptr) {
+      int32_t np = L.pcount[gi];
+      np = np < 0 ? 0 : (np > L.pcap ? (int)L.pcap : np);
+      g.np = np;
+      g.orph0 = (T / (L.span * L.C)) * L.C;
+      const int64_t orph = n_here - g.orph0;
+      U = (int64_t)np * L.C + (orph > 0 ? orph : 0);
+    } else {
+      U = n_here;
+    }
+    g.U = (int)(U < ucap ? U : ucap);
+  }
+  return g;
+}
+
+// Node id and head mask of entry u (< U) of group gi's list.
+__device__ inline void list_entry(const ListRef& L, const ListGeo& g, int gi, int u,
+                                  int32_t& id, uint32_t& mask) {
+  if (L.ids != nullptr) {
+    id = L.ids[(int64_t)gi * L.cap + u];
+    mask = L.mask[(int64_t)gi * L.cap + u];
+  } else if (u < g.np * L.C) {
+    const int64_t pi = (int64_t)gi * L.pcap + (u >> L.cshift);
+    id = L.pids[pi] * L.C + (u & (L.C - 1));
+    mask = L.pmask[pi];
+  } else {
+    id = (int32_t)(g.orph0 + (u - (int64_t)g.np * L.C));
+    mask = L.full;
+  }
+}
+
+// Node id of entry u, with the kept parents' ids staged in LDS (spid) when given.
+__device__ inline int32_t list_id(const ListRef& L, const ListGeo& g, int gi, int u,
+                                  const int32_t* spid) {
+  if (L.ids != nullptr) return L.ids[(int64_t)gi * L.cap + u];
+  if (u < g.np * L.C) {
+    const int pi = u >> L.cshift;
+    const int32_t pid = spid ? spid[pi] : L.pids[(int64_t)gi * L.pcap + pi];
+    return pid * L.C + (u & (L.C - 1));
+  }
+  return (int32_t)(g.orph0 + (u - (int64_t)g.np * L.C));
+}
+
 struct LevelParams {
   const float* q;              // [BHq][d]
   const float* khat;           // [BH][ncap][R][d]
   const float* bhat;           // [BH][ncap][R]
   int64_t ncap;
-  const int32_t* uids;         // [BH][ucap] candidate union list, ascending
-  const uint32_t* umask;       // [BH][ucap] head masks
-  const int32_t* ucount;       // [BH]
+  ListRef list;                // this level's candidate union list
+  int32_t* ucount_out;         // [BH] list length (diagnostics), or null
   int64_t ucap;
   float* scores;               // [BHq][ucap]
   uint8_t* sel;                // [BHq][ucap]
   int32_t* kept;               // [BHq]
-  uint32_t* selor;             // [BH][ucap] OR of kept bits, or null
+  uint64_t* selbits;           // [BHq][nwcap] kept bits per head, 64 entries a word, or null
+  int64_t nwcap;
   uint32_t* stage;             // [BHq][stage_cap][2] (key, w bits) for long lists
   int64_t stage_cap;
   int32_t* status;
   int32_t B, H_kv, G, d, R;
   float scale, p;
+  const int64_t* n_built;      // [L][B]: checked against T by the first launch of a route
+  int32_t check_stale, L;
 };
+
+// The first launch of a route checks that every level was built for the current T.
+__device__ inline void stale_check(const LevelParams& P, int gi) {
+  if (!P.check_stale || (gi % P.H_kv) != 0) return;
+  const int b = gi / P.H_kv;
+  int64_t T = P.list.T[b];
+  if (T < 0) T = 0;
+  if (T > P.list.T_cap) T = P.list.T_cap;
+  int64_t span = 1;
+  for (int l = 1; l <= P.L; ++l) {
+    span *= P.list.C;
+    if (P.n_built[(int64_t)(l - 1) * P.B + b] != T / span) set_status(P.status, ZHA_ESTALE);
+  }
+}
 
 __device__ inline int clamp_count(int32_t u, int64_t cap) {
   if (u < 0) return 0;
@@ -110,7 +208,6 @@ __device__ inline void score_node(const LevelParams& P, int gi, int node, int u,
   constexpr int J = GP / 4;            // full dots per lane after the butterfly
   static_assert(V0 / LPR == J, "butterfly shape");
   const int t = lane % LPR;
-  if (P.selor != nullptr && lane == 0) P.selor[(int64_t)gi * P.ucap + u] = 0u;
   if (node < 0 || node >= P.ncap) {   // not a node of this tree: never selected
     if (lane < P.G) P.scores[((int64_t)gi * P.G + lane) * P.ucap + u] = -INFINITY;
     if (lane == 0) set_status(P.status, ZHA_EINVAL);
@@ -158,20 +255,30 @@ __device__ inline void score_node(const LevelParams& P, int gi, int node, int u,
 
 template <int D, int GP>
 __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
+  constexpr int kPidLds = 4096;
+  __shared__ int32_t s_pid[kPidLds];   // the group's kept parents (implicit lists)
   const int gi = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int U = clamp_count(P.ucount[gi], P.ucap);
+  if (blockIdx.x == 0 && threadIdx.x == 0) stale_check(P, gi);
+  const ListGeo geo = list_geo(P.list, gi, P.ucap);
+  const int U = geo.U;
+  const bool staged = P.list.ids == nullptr && P.list.pids != nullptr && geo.np <= kPidLds;
+  if (staged) {
+    for (int i = threadIdx.x; i < geo.np; i += blockDim.x)
+      s_pid[i] = P.list.pids[(int64_t)gi * P.list.pcap + i];
+  }
   float qv[GP][4];
   load_group_queries<D, GP>(P, gi, lane, qv);
+  __syncthreads();
+  const int32_t* spid = staged ? s_pid : nullptr;
   const int nwaves = gridDim.x * (blockDim.x >> 6);
-  const int32_t* ul = P.uids + (int64_t)gi * P.ucap;
   // the next node id is fetched one iteration ahead, so a wave's summary loads
   // never wait behind the id load that addresses them
   int u = blockIdx.x * (blockDim.x >> 6) + wave;
-  int node_next = (u < U) ? ul[u] : 0;
+  int32_t node_next = (u < U) ? list_id(P.list, geo, gi, u, spid) : 0;
   for (; u < U; u += nwaves) {
     const int node = node_next;
-    if (u + nwaves < U) node_next = ul[u + nwaves];
+    if (u + nwaves < U) node_next = list_id(P.list, geo, gi, u + nwaves, spid);
     score_node<D, GP>(P, gi, node, u, qv, lane);
   }
 }
@@ -199,57 +306,173 @@ __device__ inline float mass_of(float s, float mx) {
 
 __device__ inline float sanitize(float s) { return isfinite(s) ? s : -FLT_MAX; }
 
-__device__ inline uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
+// The value of lane (lane ^ J), J < 64: DPP row operations for J <= 8 (quad
+// permutes; row shifts by 4 selected per lane; row rotate by 8), a swizzle for
+// J = 16 and a permute across the 32-lane halves for J = 32.
+template <int J>
+__device__ inline uint32_t xor_partner32(uint32_t v, int lane) {
+  if constexpr (J == 1) return dpp32<0xB1>(v);
+  else if constexpr (J == 2) return dpp32<0x4E>(v);
+  else if constexpr (J == 4) {
+    const uint32_t up = dpp32<0x104>(v);    // row_shl:4: the value of lane + 4
+    const uint32_t dn = dpp32<0x114>(v);    // row_shr:4: the value of lane - 4
+    return (lane & 4) ? dn : up;
+  } else if constexpr (J == 8) return dpp32<0x128>(v);   // row_ror:8
+  else if constexpr (J == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (16 << 10) | 0x1f);
+  else return (uint32_t)__shfl_xor((int)v, 32, 64);
+}
+template <int J>
+__device__ inline uint64_t xor_partner64(uint64_t v, int lane) {
+  return ((uint64_t)xor_partner32<J>((uint32_t)(v >> 32), lane) << 32) |
+         xor_partner32<J>((uint32_t)v, lane);
+}
+
+template <int NR, int K2, int J>
+__device__ inline void bitonic_stage(uint64_t (&v)[NR], int lane) {
+  if constexpr (J >= 64) {
+    constexpr int jr = J >> 6;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      if ((r & jr) == 0) {
+        const int r2 = r | jr;
+        const bool desc = ((r * 64) & K2) == 0;
+        const uint64_t a = v[r], b = v[r2];
+        const bool sw = desc ? (a < b) : (a > b);
+        v[r] = sw ? b : a;
+        v[r2] = sw ? a : b;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint64_t a = v[r];
+      const uint64_t b = xor_partner64<J>(a, lane);
+      const bool lower = (lane & J) == 0;
+      const bool desc = ((r * 64 + lane) & K2) == 0;
+      const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+      v[r] = (lower == desc) ? hi : lo;   // the lower entry of a descending pair keeps the larger
+    }
+  }
+  if constexpr (J > 1) bitonic_stage<NR, K2, J / 2>(v, lane);
+}
+
+template <int NR, int K2>
+__device__ inline void bitonic_merge_all(uint64_t (&v)[NR], int lane) {
+  bitonic_stage<NR, K2, K2 / 2>(v, lane);
+  if constexpr (K2 < 64 * NR) bitonic_merge_all<NR, K2 * 2>(v, lane);
 }
 
 // Bitonic sort, descending, of the 64*NR values v[r] of lane l (entry r*64 + l).
 template <int NR>
 __device__ inline void wave_sort_desc(uint64_t (&v)[NR], int lane) {
-  constexpr int N = 64 * NR;
-#pragma unroll
-  for (int k2 = 2; k2 <= N; k2 <<= 1) {
-#pragma unroll
-    for (int j = k2 >> 1; j > 0; j >>= 1) {
-      if (j >= 64) {
-        const int jr = j >> 6;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          if ((r & jr) == 0) {
-            const int r2 = r | jr;
-            const bool desc = ((r * 64) & k2) == 0;
-            const uint64_t a = v[r], b = v[r2];
-            const bool sw = desc ? (a < b) : (a > b);
-            v[r] = sw ? b : a;
-            v[r2] = sw ? a : b;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const uint64_t a = v[r];
-          const uint64_t b = shfl_xor_u64(a, j);
-          const bool lower = (lane & j) == 0;
-          const bool desc = ((r * 64 + lane) & k2) == 0;
-          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-          v[r] = (lower == desc) ? hi : lo;   // the lower entry of a descending pair keeps the larger
-        }
-      }
-    }
-  }
+  bitonic_merge_all<NR, 2>(v, lane);
 }
 
 constexpr int kRelBuckets = 2048;
 constexpr float kRelScale = 64.0f;     // buckets per unit of score
 constexpr int kSortMax = 1024;         // largest crossing bucket sorted exactly
+static_assert(kSortMax == kCutThreads, "the crossing-bucket buffer is cleared one entry per thread");
+
+// ---------------------------------------------------------------- compaction (A5)
+//
+// One workgroup per group, after the cut.  An entry of the level's union list is
+// kept when any head kept it, its mask being the OR of the heads' bits, read from the heads'
+// bitmaps (one 64-bit word per 64 entries); kept entries are written in list
+// order (ascending ids) as the level's kept list -- the leaf list at level 1,
+// otherwise the parents of the next level's implicit list.
+
+struct CompactParams {
+  ListRef list;                  // this level's union list
+  int64_t ucap;
+  const uint64_t* selbits;       // [BHq][nwcap]
+  int64_t nwcap;
+  int32_t G;
+  int32_t* kids; uint32_t* kmask; int32_t* kcount; int64_t kcap;   // kept list out
+  int32_t* status;
+};
+
+constexpr int kCompactThreads = 1024;
+constexpr int kCompactWords = 8192;   // bitmap words staged in LDS per pass
+constexpr int kCompactPids = 4096;    // kept parents staged in LDS (implicit lists)
+
+// Compacts group gi's union list (blockDim.x == kCompactThreads); the LDS
+// scratch is kCompactWords words, kCompactThreads row offsets, kCompactPids
+// parent ids and NW scan slots.
+__device__ inline void compact_group(const CompactParams& P, int gi, uint64_t* words,
+                                     int32_t* rowoff, int32_t* s_pid, int32_t* scan) {
+  constexpr int NW = kCompactThreads / kWave;
+  constexpr int kPidLds = kCompactPids;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const ListGeo geo = list_geo(P.list, gi, P.ucap);
+  const int U = geo.U;
+  const int nrow = (U + 63) >> 6;
+  int32_t* ids = P.kids + (int64_t)gi * P.kcap;
+  uint32_t* msk = P.kmask + (int64_t)gi * P.kcap;
+  const uint64_t* hb = P.selbits + (int64_t)gi * P.G * P.nwcap;
+  const bool staged = P.list.ids == nullptr && P.list.pids != nullptr && geo.np <= kPidLds;
+  if (staged)
+    for (int i = tid; i < geo.np; i += kCompactThreads) s_pid[i] = P.list.pids[(int64_t)gi * P.list.pcap + i];
+  const int32_t* spid = staged ? s_pid : nullptr;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes below this one
+
+  // Rows of 64 entries, up to RP a pass.  Thread t loads row t's word of every
+  // head (into LDS) and counts the row's kept entries; a block scan gives each
+  // row's first output position; then wave w places the entries of rows w,
+  // w + 16, ..., lane l taking entry l, its mask the OR of the heads' bits.
+  const int RP = min(kCompactThreads, kCompactWords / P.G);
+  int base = 0;   // kept entries placed by earlier passes
+  for (int c0 = 0; c0 < nrow; c0 += RP) {
+    const int nr = min(RP, nrow - c0);
+    int cnt = 0;
+    if (tid < nr) {
+      const int r = c0 + tid;
+      const int valid = min(64, U - r * 64);
+      const uint64_t vmask = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
+      uint64_t any = 0ull;
+      for (int g = 0; g < P.G; ++g) {
+        const uint64_t w = hb[(int64_t)g * P.nwcap + r] & vmask;
+        words[g * RP + tid] = w;
+        any |= w;
+      }
+      cnt = __popcll(any);
+    }
+    int tot;
+    const int off = block_excl_scan<NW, int>(cnt, scan, &tot);
+    rowoff[tid] = base + off;
+    __syncthreads();
+    for (int i0 = wave; i0 < nr; i0 += 4 * NW) {
+      uint32_t m[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k * NW;
+        uint32_t mk = 0u;
+        if (i < nr)
+          for (int g = 0; g < P.G; ++g) mk |= (uint32_t)((words[g * RP + i] >> lane) & 1ull) << g;
+        m[k] = mk;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k * NW;
+        const uint64_t bal = __ballot(m[k] != 0u);   // m[k] == 0 past the pass's rows
+        if (m[k] != 0u) {
+          const int p = rowoff[i] + __popcll(bal & lt);
+          if (p < P.kcap) { ids[p] = list_id(P.list, geo, gi, (c0 + i) * 64 + lane, spid); msk[p] = m[k]; }
+        }
+      }
+    }
+    base += tot;
+    __syncthreads();   // words and rowoff are reused by the next pass
+  }
+  if (tid == 0) {
+    if (base > P.kcap) set_status(P.status, ZHA_ECAPACITY);
+    P.kcount[gi] = base > P.kcap ? (int32_t)P.kcap : base;
+  }
+}
 
 struct CutSmem {
-  uint32_t key[kCutLds];
-  float w[kCutLds];
+  struct { uint32_t key[kCutLds]; float w[kCutLds]; } st;   // general-path staging
   union {
-    struct { uint32_t cnt[kRelBuckets]; unsigned long long mass[kRelBuckets]; } rel;
+    unsigned long long relmass[kRelBuckets];
     struct { uint32_t cnt[256]; unsigned long long mass[256]; } rad;
     unsigned long long sortbuf[kSortMax];
   } u;
@@ -258,8 +481,11 @@ struct CutSmem {
   int32_t redi[16];
   uint32_t bucket;
   int32_t first;
-  int32_t count;
+  int32_t count;       // crossing-bucket entries gathered
+  int32_t nabove;      // candidates in buckets above the crossing one
+  int32_t ic;          // sorted position of the cut entry within the crossing bucket
   unsigned long long above;
+  unsigned long long cut_entry;
 };
 
 __device__ inline float key_score(uint32_t k) {
@@ -271,72 +497,84 @@ __device__ inline int rel_bucket(float s, float mx) {
   return r >= (float)(kRelBuckets - 1) ? kRelBuckets - 1 : (int)r;
 }
 
-__global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
-  __shared__ CutSmem sm;
+// One workgroup cuts one query head.  The head's kept entries are written as a
+// bitmap (bit u % 64 of word u / 64; a wave's 64 consecutive entries are one
+// ballot) and, when sel is given, as bytes.
+__device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
+  constexpr int NW = kCutThreads / kWave;
   const int head = blockIdx.x;
   const int gi = head / P.G, g = head % P.G;
-  const int tid = threadIdx.x;
-  const int U = clamp_count(P.ucount[gi], P.ucap);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const ListGeo geo = list_geo(P.list, gi, P.ucap);
+  const int U = geo.U;
+  if (g == 0 && tid == 0 && P.ucount_out != nullptr) P.ucount_out[gi] = U;
   const float* sc = P.scores + (int64_t)head * P.ucap;
-  const uint32_t* mk = P.umask + (int64_t)gi * P.ucap;
-  uint8_t* out = P.sel + (int64_t)head * P.ucap;
+  auto cmask = [&](int u) -> uint32_t {
+    int32_t id; uint32_t m;
+    list_entry(P.list, geo, gi, u, id, m);
+    return m;
+  };
+  uint8_t* out = P.sel ? P.sel + (int64_t)head * P.ucap : nullptr;
+  uint64_t* bits = P.selbits ? P.selbits + (int64_t)head * P.nwcap : nullptr;
+  const int nrow = (U + 63) >> 6;
   const uint32_t bit = 1u << g;
   const bool lds = U <= kCutLds;
-  uint32_t* skey = lds ? sm.key : P.stage + (int64_t)head * P.stage_cap * 2;
-  float* sw = lds ? sm.w : (float*)(P.stage + (int64_t)head * P.stage_cap * 2 + P.stage_cap);
+  uint32_t* skey = lds ? sm.st.key : P.stage + (int64_t)head * P.stage_cap * 2;
+  float* sw = lds ? sm.st.w : (float*)(P.stage + (int64_t)head * P.stage_cap * 2 + P.stage_cap);
+  if (tid == 0) { sm.nabove = 0; sm.count = 0; sm.first = kRelBuckets; }
 
-  uint32_t* selor = P.selor ? P.selor + (int64_t)gi * P.ucap : nullptr;
   // Lists that fit keep this thread's scores (entries j*1024 + tid) in registers
   // across every pass; all loads are issued before any is used.
   constexpr int PER = kCutReg;
   const bool reg = U <= PER * kCutThreads;
   float sv[PER];
   float mx = -INFINITY;
-  int ncand = 0;
   if (reg) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int u = j * kCutThreads + tid;
       const int uu = u < U ? u : 0;         // in bounds: loads never wait on each other
-      const uint32_t m = mk[uu];
+      const uint32_t m = cmask(uu);
       const float sj = sc[uu];
       sv[j] = (u < U && (m & bit)) ? sanitize(sj) : -INFINITY;
     }
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (sv[j] != -INFINITY) { mx = fmaxf(mx, sv[j]); ++ncand; }
+    for (int j = 0; j < PER; ++j) mx = fmaxf(mx, sv[j]);
   } else {
     for (int u = tid; u < U; u += kCutThreads)
-      if (mk[u] & bit) { mx = fmaxf(mx, sanitize(sc[u])); ++ncand; }
+      if (cmask(u) & bit) mx = fmaxf(mx, sanitize(sc[u]));
   }
-  constexpr int NW = kCutThreads / kWave;
-  mx = block_max_f<NW>(mx, sm.redf);
-  ncand = (int)block_sum<NW, uint32_t>((uint32_t)ncand, (uint32_t*)sm.redi);
+  mx = block_max_f<NW>(mx, sm.redf);     // -inf: the head has no candidates
 
-  if (ncand == 0 || P.p >= 1.0f) {
-    for (int u = tid; u < U; u += kCutThreads) {
-      const bool s1 = P.p >= 1.0f && (mk[u] & bit);
-      out[u] = s1 ? 1 : 0;
-      if (s1 && selor) atomicOr(&selor[u], bit);
+  if (mx == -INFINITY || P.p >= 1.0f) {
+    // p >= 1 keeps every candidate; no candidates keeps nothing
+    int kept = 0;
+    for (int j0 = 0; j0 < U; j0 += kCutThreads) {
+      const int u = j0 + tid;
+      const bool s1 = P.p >= 1.0f && u < U && (cmask(u) & bit);
+      const uint64_t b = __ballot(s1);
+      if (out && u < U) out[u] = s1 ? 1 : 0;
+      const int row = (j0 >> 6) + wave;
+      if (bits && lane == 0 && row < nrow) bits[row] = b;
+      kept += __popcll(b);
     }
-    if (tid == 0) P.kept[head] = (P.p >= 1.0f) ? ncand : 0;
+    if (lane == 0) atomicAdd(&sm.nabove, kept);
+    __syncthreads();
+    if (tid == 0) P.kept[head] = sm.nabove;
     return;
   }
 
   if (reg) {
     // ---- histogram of mass over relative-score buckets; W is its total
-    for (int i = tid; i < kRelBuckets; i += kCutThreads) { sm.u.rel.cnt[i] = 0u; sm.u.rel.mass[i] = 0ull; }
-    if (tid == 0) { sm.first = kRelBuckets; sm.count = 0; }
+    for (int i = tid; i < kRelBuckets; i += kCutThreads) sm.u.relmass[i] = 0ull;
     __syncthreads();
     unsigned long long wsum = 0ull;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       if (sv[j] != -INFINITY) {
         const uint64_t fx = fixmass(mass_of(sv[j], mx));
-        const int b = rel_bucket(sv[j], mx);
         wsum += fx;
-        atomicAdd(&sm.u.rel.cnt[b], 1u);
-        atomicAdd(&sm.u.rel.mass[b], (unsigned long long)fx);
+        atomicAdd(&sm.u.relmass[rel_bucket(sv[j], mx)], (unsigned long long)fx);
       }
     }
     const unsigned long long W = block_sum<NW, unsigned long long>(wsum, sm.redu);
@@ -344,7 +582,7 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
     // bucket b holds the scores just below those of buckets < b: running mass in
     // increasing b; thread t owns buckets 2t and 2t+1
     {
-      const unsigned long long m0 = sm.u.rel.mass[2 * tid], m1 = sm.u.rel.mass[2 * tid + 1];
+      const unsigned long long m0 = sm.u.relmass[2 * tid], m1 = sm.u.relmass[2 * tid + 1];
       unsigned long long tot;
       const unsigned long long pre = block_excl_scan<NW, unsigned long long>(m0 + m1, sm.redu, &tot);
       // exactly one bucket has its running mass cross p * W
@@ -356,25 +594,32 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
     }
     const int bstar = sm.first;
     const unsigned long long above_b = sm.above;
-    const int cstar = (bstar < kRelBuckets) ? (int)sm.u.rel.cnt[bstar] : kSortMax + 1;
+    // ---- gather the crossing bucket as (key << 32 | ~u), sorted below by score
+    // descending then id ascending; count the candidates above it
+    sm.u.sortbuf[tid] = 0ull;               // kSortMax == kCutThreads
     __syncthreads();
-    if (cstar <= kSortMax) {
-      // gather the crossing bucket as (key << 32 | ~u); sort descending: score
-      // descending, then id ascending
-      int n2 = 1;
-      while (n2 < cstar) n2 <<= 1;
-      for (int i = tid; i < n2; i += kCutThreads) sm.u.sortbuf[i] = 0ull;
-      __syncthreads();
+    int nab = 0;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if (sv[j] != -INFINITY && rel_bucket(sv[j], mx) == bstar) {
+    for (int j = 0; j < PER; ++j) {
+      if (sv[j] != -INFINITY) {
+        const int b = rel_bucket(sv[j], mx);
+        if (b < bstar) {
+          ++nab;
+        } else if (b == bstar) {
           const int u = j * kCutThreads + tid;
           const int slot = atomicAdd(&sm.count, 1);
-          sm.u.sortbuf[slot] = ((unsigned long long)order_key(sv[j]) << 32) | (uint32_t)(~(uint32_t)u);
+          if (slot < kSortMax)
+            sm.u.sortbuf[slot] = ((unsigned long long)order_key(sv[j]) << 32) | (uint32_t)(~(uint32_t)u);
         }
       }
-      __syncthreads();
-      const int lane = tid & 63;
+    }
+    nab = (int)wave_sum_u32((uint32_t)nab);
+    if (lane == 0) atomicAdd(&sm.nabove, nab);
+    __syncthreads();
+    const int cstar = (bstar < kRelBuckets) ? sm.count : kSortMax + 1;
+    if (cstar <= kSortMax) {
+      int n2 = 1;
+      while (n2 < cstar) n2 <<= 1;
       if (n2 <= 4 * kWave) {
         // one wave sorts in registers and scans; the others wait at the next barrier
         if (tid < kWave) {
@@ -394,26 +639,25 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
               carry = rl64(inc, 63);
             }
             if (ic < 0 || ic > cstar - 1) ic = cstar - 1;
-            // the cut entry, in sorted position ic, back to LDS for every wave
             const int r_ic = ic >> 6, l_ic = ic & 63;
             uint64_t ce = 0ull;
 #pragma unroll
             for (int r = 0; r < NR; ++r)
               if (r == r_ic) ce = rl64(v[r], l_ic);
-            if (lane == 0) { sm.count = 0; sm.u.sortbuf[0] = ce; }
+            if (lane == 0) { sm.ic = ic; sm.cut_entry = ce; }
           };
           if (n2 <= kWave) {
-            uint64_t v[1] = {lane < n2 ? (uint64_t)sm.u.sortbuf[lane] : 0ull};
+            uint64_t v[1] = {(uint64_t)sm.u.sortbuf[lane]};
             finish(v, std::integral_constant<int, 1>());
           } else if (n2 <= 2 * kWave) {
             uint64_t v[2];
 #pragma unroll
-            for (int r = 0; r < 2; ++r) v[r] = (r * 64 + lane < n2) ? (uint64_t)sm.u.sortbuf[r * 64 + lane] : 0ull;
+            for (int r = 0; r < 2; ++r) v[r] = (uint64_t)sm.u.sortbuf[r * 64 + lane];
             finish(v, std::integral_constant<int, 2>());
           } else {
             uint64_t v[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = (r * 64 + lane < n2) ? (uint64_t)sm.u.sortbuf[r * 64 + lane] : 0ull;
+            for (int r = 0; r < 4; ++r) v[r] = (uint64_t)sm.u.sortbuf[r * 64 + lane];
             finish(v, std::integral_constant<int, 4>());
           }
         }
@@ -440,34 +684,33 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
         }
         unsigned long long tot2;
         const unsigned long long pre2 = block_excl_scan<NW, unsigned long long>(mi, sm.redu, &tot2);
-        if (tid == 0) sm.count = kSortMax;
+        if (tid == 0) sm.ic = kSortMax;
         __syncthreads();
-        if (tid < n2 && mi != 0ull && (double)(above_b + pre2 + mi) >= target) atomicMin(&sm.count, tid);
+        if (tid < n2 && mi != 0ull && (double)(above_b + pre2 + mi) >= target) atomicMin(&sm.ic, tid);
         __syncthreads();
-        if (tid == 0 && sm.count > cstar - 1) sm.count = cstar - 1;
+        if (tid == 0) {
+          if (sm.ic > cstar - 1) sm.ic = cstar - 1;
+          sm.cut_entry = sm.u.sortbuf[sm.ic];
+        }
       }
       __syncthreads();
-      const int ic = sm.count;
-      const unsigned long long ce = sm.u.sortbuf[ic];
+      const unsigned long long ce = sm.cut_entry;
       const uint32_t kap = (uint32_t)(ce >> 32);
       const int ukap = (int)(~(uint32_t)ce);
-      uint32_t kept = 0;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int u = j * kCutThreads + tid;
-        if (u < U) {
-          uint8_t sel = 0;
-          if (sv[j] != -INFINITY) {
-            const uint32_t k = order_key(sv[j]);
-            sel = (k > kap || (k == kap && u <= ukap)) ? 1 : 0;
-          }
-          out[u] = sel;
-          kept += sel;
-          if (sel && selor) atomicOr(&selor[u], bit);
+        bool s1 = false;
+        if (sv[j] != -INFINITY) {
+          const uint32_t k = order_key(sv[j]);
+          s1 = k > kap || (k == kap && u <= ukap);
         }
+        if (out && u < U) out[u] = s1 ? 1 : 0;
+        const uint64_t b = __ballot(s1);
+        const int row = j * NW + wave;
+        if (bits && lane == 0 && row < nrow) bits[row] = b;
       }
-      kept = block_sum<NW, uint32_t>(kept, (uint32_t*)sm.redi);
-      if (tid == 0) P.kept[head] = (int32_t)kept;
+      if (tid == 0) P.kept[head] = sm.nabove + sm.ic + 1;
       return;
     }
     __syncthreads();
@@ -492,7 +735,7 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
     for (int u = tid; u < U; u += kCutThreads) {
       uint32_t k = 0u;
       float w = 0.0f;
-      if (mk[u] & bit) {
+      if (cmask(u) & bit) {
         const float sc1 = sanitize(sc[u]);
         k = order_key(sc1);
         w = mass_of(sc1, mx);
@@ -502,6 +745,8 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
       sw[u] = w;
     }
   }
+  if (bits)
+    for (int r = tid; r < nrow; r += kCutThreads) bits[r] = 0ull;
   const unsigned long long W = block_reduce_sum<unsigned long long>(wsum, sm.redu);
   const double target = (double)P.p * (double)W;
 
@@ -515,7 +760,6 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
     __syncthreads();
     // Scores cluster, so most lanes of a wave often hit one bucket: such waves
     // add one aggregated (count, mass) instead of 64 conflicting LDS atomics.
-    const int lane = tid & 63;
     for (int base = 0; base < U; base += kCutThreads) {
       const int u = base + tid;
       const uint32_t k = (u < U) ? skey[u] : 0u;
@@ -599,189 +843,52 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
   int kept = 0;
   for (int u = u0; u < u1; ++u) {
     const uint32_t k = skey[u];
-    uint8_t s = 0;
-    if (k > kappa) s = 1;
-    else if (k == kappa) { s = (rank < k_ties) ? 1 : 0; ++rank; }
-    out[u] = s;
-    kept += s;
-    if (s && selor) atomicOr(&selor[u], bit);
+    uint8_t s1 = 0;
+    if (k > kappa) s1 = 1;
+    else if (k == kappa) { s1 = (rank < k_ties) ? 1 : 0; ++rank; }
+    if (out) out[u] = s1;
+    kept += s1;
+    if (s1 && bits) atomicOr((unsigned long long*)&bits[u >> 6], 1ull << (u & 63));
   }
   kept = block_reduce_sum<int>(kept, sm.redi);
   if (tid == 0) P.kept[head] = kept;
 }
 
-// ---------------------------------------------------------------- expansion (A5)
-//
-// One workgroup per group.  An entry of the union list is kept when any head
-// kept it, its mask being the OR of the heads' bits (selor); kept entries are
-// compacted in list order.  Kept parents are staged, then their children are
-// written with consecutive threads on consecutive outputs, followed by the
-// parentless nodes of the next level.  The final level writes the kept leaves
-// themselves.  The top list (every level-L node) is built the same way with no
-// parents; that launch also checks that the tree matches T.
+__global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
+  __shared__ CutSmem sm;
+  cut_head(P, sm);
+}
 
-struct ExpandParams {
-  const int64_t* T;
-  const int64_t* n_built;        // [L][B] (top launch only)
-  const int32_t* uids; const uint32_t* umask; const int32_t* ucount; int64_t ucap;
-  const uint32_t* selor;         // [BH][ucap] OR of the heads' kept bits
-  int32_t* nids; uint32_t* nmask; int32_t* ncount; int64_t ncap;   // next list
-  int32_t* xstage;               // [BH][xcap][2]
-  int64_t xcap;
-  int32_t* status;
-  int32_t B, H_kv, G, C, L;
-  int32_t level;                 // level of the input list; 0 = build the top list
-  int32_t final_;                // 1: write the kept leaves (no children)
-  int64_t span_next;             // C^(level-1): tokens per node of the next level
-  int64_t T_cap;
-};
-
-constexpr int kExpandThreads = 1024;
-
-constexpr int kExpandLds = 8192;   // kept parents staged in LDS; more use the workspace
-
-__global__ void __launch_bounds__(kExpandThreads) expand_level(ExpandParams P) {
-  constexpr int NW = kExpandThreads / kWave;
-  __shared__ int32_t red[NW];
-  __shared__ int32_t spid[kExpandLds];
-  __shared__ uint32_t spm[kExpandLds];
-  const int gi = blockIdx.x;
-  const int b = gi / P.H_kv;
-  const int tid = threadIdx.x;
-  int64_t T = P.T[b];
-  if (T < 0) T = 0;
-  if (T > P.T_cap) T = P.T_cap;
-  const uint32_t full = (P.G >= 32) ? 0xffffffffu : ((1u << P.G) - 1u);
-  if (P.level == 0 && tid == 0 && (gi % P.H_kv) == 0) {
-    int64_t span = 1;
-    for (int l = 1; l <= P.L; ++l) {
-      span *= P.C;
-      if (P.n_built[(int64_t)(l - 1) * P.B + b] != T / span) set_status(P.status, ZHA_ESTALE);
-    }
-  }
-  const int64_t n_next = T / P.span_next;                     // nodes at the next level
-  const int64_t n_here = (P.level == 0) ? 0 : T / (P.span_next * P.C);
-  const int U = (P.level == 0) ? 0 : clamp_count(P.ucount[gi], P.ucap);
-  int32_t* ids = P.nids + (int64_t)gi * P.ncap;
-  uint32_t* msk = P.nmask + (int64_t)gi * P.ncap;
-  const uint32_t* so = P.selor ? P.selor + (int64_t)gi * P.ucap : nullptr;
-  const int32_t* uid = P.uids ? P.uids + (int64_t)gi * P.ucap : nullptr;
-
-  // Wave w owns the contiguous entries [w*R, (w+1)*R), read 64 at a time with
-  // consecutive lanes on consecutive entries, kReg loads in flight per batch.
-  // Kept entries are counted with ballots; one prefix over the wave counts gives
-  // each wave's first output position; a second ballot pass places every kept
-  // entry in list order (reusing the registers when one batch covers the range).
-  const int lane = tid & 63, wave = tid >> 6;
-  const int R = (((U + NW - 1) / NW) + 63) & ~63;
-  const int nj = R / 64;
-  const int w0 = wave * R;
-  constexpr int kReg = 16;
-  uint32_t mv[kReg];
-  int32_t iv[kReg];
-  auto load_batch = [&](int jb) {
-#pragma unroll
-    for (int j = 0; j < kReg; ++j) {
-      const int u = w0 + (jb + j) * 64 + lane;
-      const bool in = jb + j < nj && u < U;
-      const int uu = in ? u : 0;
-      const uint32_t m = so ? so[uu] : 0u;
-      const int32_t id = uid ? uid[uu] : 0;
-      mv[j] = in ? m : 0u;
-      iv[j] = in ? id : 0;
-    }
-  };
-  int cnt = 0;
-  for (int jb = 0; jb < nj; jb += kReg) {
-    load_batch(jb);
-#pragma unroll
-    for (int j = 0; j < kReg; ++j) cnt += __popcll(__ballot(mv[j] != 0u));
-  }
-  if (lane == 0) red[wave] = cnt;
-  __syncthreads();
-  int pos = 0, nsel = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int c = red[w];
-    pos += (w < wave) ? c : 0;
-    nsel += c;
-  }
-  const bool lds = nsel <= kExpandLds;
-  int32_t* st = P.xstage + (int64_t)gi * P.xcap * 2;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes below this one
-  auto emit = [&](int p, int32_t id, uint32_t m) {
-    if (P.final_) {
-      if (p < P.ncap) { ids[p] = id; msk[p] = m; }
-    } else if (lds) {
-      spid[p] = id; spm[p] = m;
-    } else {
-      st[2 * p] = id; st[2 * p + 1] = (int32_t)m;
-    }
-  };
-  for (int jb = 0; jb < nj; jb += kReg) {
-    if (nj > kReg) load_batch(jb);
-#pragma unroll
-    for (int j = 0; j < kReg; ++j) {
-      const uint64_t bal = __ballot(mv[j] != 0u);
-      if (mv[j]) emit(pos + __popcll(bal & lt), iv[j], mv[j]);
-      pos += __popcll(bal);
-    }
-  }
-  int64_t n_orph = P.final_ ? 0 : (n_next - (int64_t)P.C * n_here);
-  if (n_orph < 0) n_orph = 0;
-  int64_t count = P.final_ ? nsel : (int64_t)nsel * P.C + n_orph;
-  if (count > P.ncap) {
-    if (tid == 0) set_status(P.status, ZHA_ECAPACITY);
-    count = P.ncap;
-  }
-  if (!P.final_) {
-    __syncthreads();   // staged parents visible to the whole block
-    const int64_t nch = (int64_t)nsel * P.C;
-    const int cshift = __ffs(P.C) - 1;   // C is a power of two
-    for (int64_t o = tid; o < nch && o < count; o += kExpandThreads) {
-      const int64_t pi = o >> cshift;
-      const int32_t pid = lds ? spid[pi] : st[2 * pi];
-      const uint32_t pm = lds ? spm[pi] : (uint32_t)st[2 * pi + 1];
-      ids[o] = pid * P.C + (int32_t)(o & (P.C - 1));
-      msk[o] = pm;
-    }
-    const int64_t first_orph = (int64_t)P.C * n_here;
-    for (int64_t i = tid; i < n_orph; i += kExpandThreads) {
-      const int64_t o = nch + i;
-      if (o < count) { ids[o] = (int32_t)(first_orph + i); msk[o] = full; }
-    }
-  }
-  if (tid == 0) P.ncount[gi] = (int32_t)count;
+// One workgroup per group.
+__global__ void __launch_bounds__(kCompactThreads) compact_level(CompactParams P) {
+  constexpr int NW = kCompactThreads / kWave;
+  __shared__ uint64_t words[kCompactWords];
+  __shared__ int32_t rowoff[kCompactThreads];
+  __shared__ int32_t pid[kCompactPids];
+  __shared__ int32_t scan[NW];
+  compact_group(P, blockIdx.x, words, rowoff, pid, scan);
 }
 
 // ---------------------------------------------------------------- small levels
 //
-// A level whose list holds at most kSmallCap nodes per group is cut and expanded
+// A level whose list holds at most kSmallCap nodes per group is cut and compacted
 // by one workgroup per group (route_small).  Each wave cuts one head: its
 // candidates, keyed (score desc, id asc), are sorted in registers by a bitonic
 // network; the masses exp(s - max) in that order, as the same 2^40 fixed point
 // the large-list cut uses, give the running sums, and the cut is the first entry
 // whose running mass reaches p W -- the same integers and the same comparisons
 // as cut_topp, so both paths keep the same nodes.  The heads' kept bits are ORed
-// in LDS and expanded exactly as expand_level does.  A level of at most kTinyCap
-// nodes is also scored by that workgroup (one launch for the whole level);
-// otherwise score_nodes runs first.  The top level's list (every level-L node,
-// every head) is implicit.  Nothing is handed between workgroups inside a launch.
+// in LDS and the kept entries written in list order, as compact_level does.  A
+// level of at most kTinyCap nodes is also scored by that workgroup (one launch
+// for the whole level); otherwise score_nodes runs first.  Nothing is handed
+// between workgroups inside a launch.
 
 constexpr int kSmallCap = 256;
 constexpr int kTinyCap = 16;
 constexpr int kSmallThreads = 256;
 
 struct SmallParams {
-  int32_t top;                   // 1: the list is every level-L node (ids implicit)
-  const int64_t* T;
-  const int64_t* n_built;        // [L][B] (top launch: stale-tree check)
-  int32_t* ucount_out;           // top launch: the level's list size, for diagnostics
-  int32_t* nids; uint32_t* nmask; int32_t* ncount; int64_t ncap;   // next list
-  int32_t final_;                // 1: write the kept leaves (no children)
-  int32_t C, L;
-  int64_t span_next;             // C^(level-1)
-  int64_t T_cap;
+  int32_t* kids; uint32_t* kmask; int32_t* kcount; int64_t kcap;   // kept list out
 };
 
 // Top-p cut of one head over a list of U <= 64*NR entries, by one wave; ORs the
@@ -841,38 +948,30 @@ __global__ void __launch_bounds__(kSmallThreads) route_small(LevelParams P, Smal
   __shared__ uint32_t s_cm[kSmallCap];    // candidate masks
   __shared__ int32_t s_id[kSmallCap];     // node ids
   __shared__ uint32_t s_or[kSmallCap];    // OR of the heads' kept bits
-  __shared__ int32_t s_pid[kSmallCap];    // kept nodes in list order
-  __shared__ uint32_t s_pm[kSmallCap];
   __shared__ int32_t s_red[NW];
   const int gi = blockIdx.x;
-  const int b = gi / P.H_kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int64_t T = S.T[b];
-  if (T < 0) T = 0;
-  if (T > S.T_cap) T = S.T_cap;
-  const uint32_t full = (P.G >= 32) ? 0xffffffffu : ((1u << P.G) - 1u);
-  const int64_t n_here = T / (S.span_next * S.C);      // nodes at this level
-  int U;
-  if (S.top) U = (int)(n_here < P.ucap ? n_here : P.ucap);
-  else U = clamp_count(P.ucount[gi], P.ucap);
-  if (U > kSmallCap) U = kSmallCap;
-  const int32_t* ul = S.top ? nullptr : P.uids + (int64_t)gi * P.ucap;
+  if (tid == 0) stale_check(P, gi);
+  const ListGeo geo = list_geo(P.list, gi, P.ucap);
+  const int U = geo.U < kSmallCap ? geo.U : kSmallCap;
+  for (int u = tid; u < kSmallCap; u += kSmallThreads) {
+    s_or[u] = 0u;
+    if (u < U) {
+      int32_t id; uint32_t m;
+      list_entry(P.list, geo, gi, u, id, m);
+      s_id[u] = id;
+      s_cm[u] = m;
+    }
+  }
+  __syncthreads();
 
   if constexpr (SCORE) {
     float qv[GP][4];
     load_group_queries<D, GP>(P, gi, lane, qv);
-    for (int u = wave; u < U; u += NW) score_node<D, GP>(P, gi, S.top ? u : ul[u], u, qv, lane);
+    for (int u = wave; u < U; u += NW) score_node<D, GP>(P, gi, s_id[u], u, qv, lane);
     __syncthreads();   // the scores are read back by other waves of this workgroup
   }
 
-  for (int u = tid; u < kSmallCap; u += kSmallThreads) {
-    s_or[u] = 0u;
-    if (u < U) {
-      s_id[u] = S.top ? u : ul[u];
-      s_cm[u] = S.top ? full : P.umask[(int64_t)gi * P.ucap + u];
-    }
-  }
-  __syncthreads();
   // ---- cut: wave w takes heads w, w + NW, ...
   for (int g = wave; g < P.G; g += NW) {
     const int64_t head = (int64_t)gi * P.G + g;
@@ -884,7 +983,7 @@ __global__ void __launch_bounds__(kSmallThreads) route_small(LevelParams P, Smal
     if (lane == 0) P.kept[head] = kept;
   }
   __syncthreads();
-  // ---- expand: kept entries in list order
+  // ---- kept entries in list order
   const uint32_t m = (tid < U) ? s_or[tid] : 0u;
   const uint64_t bal = __ballot(m != 0u);
   if (lane == 0) s_red[wave] = __popcll(bal);
@@ -897,49 +996,14 @@ __global__ void __launch_bounds__(kSmallThreads) route_small(LevelParams P, Smal
   }
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   pos += __popcll(bal & lt);
-  if (m != 0u) { s_pid[pos] = s_id[tid]; s_pm[pos] = m; }
-  __syncthreads();
-  int32_t* ids = S.nids + (int64_t)gi * S.ncap;
-  uint32_t* msk = S.nmask + (int64_t)gi * S.ncap;
-  int64_t count;
-  if (S.final_) {
-    count = nsel;
-    for (int i = tid; i < nsel && i < S.ncap; i += kSmallThreads) { ids[i] = s_pid[i]; msk[i] = s_pm[i]; }
-  } else {
-    const int64_t n_next = T / S.span_next;
-    int64_t n_orph = n_next - (int64_t)S.C * n_here;
-    if (n_orph < 0) n_orph = 0;
-    const int64_t nch = (int64_t)nsel * S.C;
-    count = nch + n_orph;
-    const int64_t lim = count < S.ncap ? count : S.ncap;
-    const int cshift = __ffs(S.C) - 1;   // C is a power of two
-    for (int64_t o = tid; o < lim; o += kSmallThreads) {
-      if (o < nch) {
-        const int64_t pi = o >> cshift;
-        ids[o] = s_pid[pi] * S.C + (int32_t)(o & (S.C - 1));
-        msk[o] = s_pm[pi];
-      } else {
-        ids[o] = (int32_t)(S.C * n_here + (o - nch));
-        msk[o] = full;
-      }
-    }
-  }
-  if (count > S.ncap) {
-    if (tid == 0) set_status(P.status, ZHA_ECAPACITY);
-    count = S.ncap;
+  if (m != 0u && pos < S.kcap) {
+    S.kids[(int64_t)gi * S.kcap + pos] = s_id[tid];
+    S.kmask[(int64_t)gi * S.kcap + pos] = m;
   }
   if (tid == 0) {
-    S.ncount[gi] = (int32_t)count;
-    if (S.top) {
-      S.ucount_out[gi] = U;
-      if ((gi % P.H_kv) == 0) {
-        int64_t span = 1;
-        for (int l = 1; l <= S.L; ++l) {
-          span *= S.C;
-          if (S.n_built[(int64_t)(l - 1) * P.B + b] != T / span) set_status(P.status, ZHA_ESTALE);
-        }
-      }
-    }
+    if (nsel > S.kcap) set_status(P.status, ZHA_ECAPACITY);
+    S.kcount[gi] = nsel > S.kcap ? (int32_t)S.kcap : nsel;
+    if (P.ucount_out != nullptr) P.ucount_out[gi] = U;
   }
 }
 
@@ -1009,6 +1073,24 @@ static LevelParams level_params(const zha_cfg* cfg, const float* q, const zha_tr
   P.status = (int32_t*)ws;
   P.B = cfg->B; P.H_kv = cfg->H_kv; P.G = cfg->G; P.d = cfg->d; P.R = cfg->R;
   P.scale = cfg->scale; P.p = p;
+  P.ucount_out = nullptr;
+  P.sel = nullptr;
+  P.selbits = nullptr;
+  P.nwcap = 0;
+  P.n_built = tree->n_built;
+  P.check_stale = 0;
+  P.L = cfg->L;
+  ListRef& L = P.list;
+  L.ids = nullptr; L.mask = nullptr; L.count = nullptr; L.cap = 0;
+  L.pids = nullptr; L.pmask = nullptr; L.pcount = nullptr; L.pcap = 0;
+  L.T = nullptr; L.T_cap = cfg->T_cap;
+  int64_t span = 1;
+  for (int i = 0; i < level; ++i) span *= cfg->C;
+  L.span = span;
+  L.C = cfg->C;
+  L.cshift = __builtin_ctz((unsigned)cfg->C);
+  L.H_kv = cfg->H_kv;
+  L.full = (cfg->G >= 32) ? 0xffffffffu : ((1u << cfg->G) - 1u);
   return P;
 }
 
@@ -1031,79 +1113,55 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
   hipStream_t s = (hipStream_t)stream;
   char* base = (char*)ws;
   const int BH = cfg->B * cfg->H_kv, BHq = BH * cfg->G, L = cfg->L;
-  int64_t span[ZHA_MAX_L + 1];
-  span[0] = 1;
-  for (int l = 1; l <= L; ++l) span[l] = span[l - 1] * cfg->C;
 
-  // Levels whose lists hold at most kSmallCap nodes run fused (score, cut and
-  // expand in one launch); longer ones run score_nodes, cut_topp, expand_level.
-  auto small = [&](int l) { return w.cap[l - 1] <= kSmallCap; };
-  auto tiny = [&](int l) { return w.cap[l - 1] <= kTinyCap; };
-  // an implicit top list needs the level scored in the same launch
-  const bool top_implicit = tiny(L);
-  ExpandParams E;
-  E.T = T; E.status = (int32_t*)ws; E.n_built = tree->n_built;
-  E.B = cfg->B; E.H_kv = cfg->H_kv; E.G = cfg->G; E.C = cfg->C; E.L = L; E.T_cap = cfg->T_cap;
-  E.xstage = (int32_t*)(base + w.xstage); E.xcap = w.stage_cap;
-  if (!top_implicit) {
-    // top list: every level-L node, every head
-    E.level = 0; E.final_ = 0;
-    E.uids = nullptr; E.umask = nullptr; E.ucount = nullptr; E.ucap = 1; E.selor = nullptr;
-    E.nids = (int32_t*)(base + w.uids[L - 1]);
-    E.nmask = (uint32_t*)(base + w.umask[L - 1]);
-    E.ncount = (int32_t*)(base + w.ucount[L - 1]);
-    E.ncap = w.cap[L - 1];
-    E.span_next = span[L];
-    hipLaunchKernelGGL(expand_level, dim3(BH), dim3(kExpandThreads), 0, s, E);
-  }
-
+  // Levels whose lists hold at most kSmallCap nodes are cut and compacted by
+  // route_small (scored in the same launch when at most kTinyCap); longer ones
+  // run score_nodes, cut_topp and compact_level.
   for (int l = L; l >= 1; --l) {
     LevelParams P = level_params(cfg, q, tree, l, p, ws, w);
-    P.uids = (const int32_t*)(base + w.uids[l - 1]);
-    P.umask = (const uint32_t*)(base + w.umask[l - 1]);
-    P.ucount = (const int32_t*)(base + w.ucount[l - 1]);
-    P.ucap = w.cap[l - 1];
-    P.scores = (float*)(base + w.scores[l - 1]);
-    P.sel = (uint8_t*)(base + w.sel[l - 1]);
-    P.kept = (int32_t*)(base + w.kept[l - 1]);
-    int32_t* nids; uint32_t* nmask; int32_t* ncount; int64_t ncap;
-    if (l > 1) {
-      nids = (int32_t*)(base + w.uids[l - 2]);
-      nmask = (uint32_t*)(base + w.umask[l - 2]);
-      ncount = (int32_t*)(base + w.ucount[l - 2]);
-      ncap = w.cap[l - 2];
-    } else {
-      nids = leaf_ids; nmask = leaf_mask; ncount = leaf_count; ncap = cfg->leaf_cap;
+    P.list.T = T;
+    if (l < L) {   // children of the kept nodes of level l+1, then the parentless nodes
+      P.list.pids = (const int32_t*)(base + w.kids[l]);
+      P.list.pmask = (const uint32_t*)(base + w.kmask[l]);
+      P.list.pcount = (const int32_t*)(base + w.kcount[l]);
+      P.list.pcap = w.cap[l];
     }
-    if (small(l)) {
-      P.selor = nullptr;
+    P.ucap = w.cap[l - 1];
+    P.ucount_out = (int32_t*)(base + w.ucount[l - 1]);
+    P.scores = (float*)(base + w.scores[l - 1]);
+    P.kept = (int32_t*)(base + w.kept[l - 1]);
+    P.check_stale = (l == L) ? 1 : 0;
+    int32_t* kids; uint32_t* kmask; int32_t* kcount; int64_t kcap;
+    if (l > 1) {
+      kids = (int32_t*)(base + w.kids[l - 1]);
+      kmask = (uint32_t*)(base + w.kmask[l - 1]);
+      kcount = (int32_t*)(base + w.kcount[l - 1]);
+      kcap = w.cap[l - 1];
+    } else {
+      kids = leaf_ids; kmask = leaf_mask; kcount = leaf_count; kcap = cfg->leaf_cap;
+    }
+    if (w.cap[l - 1] <= kSmallCap) {
       SmallParams S;
-      S.top = (l == L && top_implicit) ? 1 : 0;
-      S.T = T; S.n_built = tree->n_built;
-      S.ucount_out = (int32_t*)(base + w.ucount[l - 1]);
-      S.nids = nids; S.nmask = nmask; S.ncount = ncount; S.ncap = ncap;
-      S.final_ = (l == 1) ? 1 : 0;
-      S.C = cfg->C; S.L = L;
-      S.span_next = span[l - 1];
-      S.T_cap = cfg->T_cap;
-      if (tiny(l)) {
+      S.kids = kids; S.kmask = kmask; S.kcount = kcount; S.kcap = kcap;
+      if (w.cap[l - 1] <= kTinyCap) {
         launch_small_t<true>(P, S, s);
       } else {
         launch_score(P, P.ucap, s);
+        P.check_stale = 0;
         launch_small_t<false>(P, S, s);
       }
       continue;
     }
-    P.selor = (uint32_t*)(base + w.selor[l - 1]);
+    P.selbits = (uint64_t*)(base + w.selbits[l - 1]);
+    P.nwcap = w.nwcap[l - 1];
     launch_score(P, P.ucap, s);
+    P.check_stale = 0;
+    CompactParams X;
+    X.list = P.list; X.ucap = P.ucap; X.selbits = P.selbits; X.nwcap = P.nwcap; X.G = cfg->G;
+    X.kids = kids; X.kmask = kmask; X.kcount = kcount; X.kcap = kcap;
+    X.status = (int32_t*)ws;
     hipLaunchKernelGGL(cut_topp, dim3(BHq), dim3(kCutThreads), 0, s, P);
-    E.level = l;
-    E.uids = P.uids; E.umask = P.umask; E.ucount = P.ucount; E.ucap = P.ucap;
-    E.selor = P.selor;
-    E.span_next = span[l - 1];
-    E.final_ = (l == 1) ? 1 : 0;
-    E.nids = nids; E.nmask = nmask; E.ncount = ncount; E.ncap = ncap;
-    hipLaunchKernelGGL(expand_level, dim3(BH), dim3(kExpandThreads), 0, s, E);
+    hipLaunchKernelGGL(compact_level, dim3(BH), dim3(kCompactThreads), 0, s, X);
   }
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
 }
@@ -1126,10 +1184,11 @@ extern "C" int32_t zha_route_level(const zha_cfg* cfg, int32_t level, const floa
   if ((int64_t)cand_cap > w.stage_cap) return ZHA_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   LevelParams P = level_params(cfg, q, tree, level, p, ws, w);
-  P.uids = cand_ids; P.umask = cand_mask; P.ucount = cand_count; P.ucap = cand_cap;
+  P.list.ids = cand_ids; P.list.mask = cand_mask; P.list.count = cand_count;
+  P.list.cap = cand_cap;
+  P.ucap = cand_cap;
   P.scores = scores; P.sel = sel;
   P.kept = (int32_t*)((char*)ws + w.kept[level - 1]);
-  P.selor = nullptr;
   launch_score(P, cand_cap, s);
   hipLaunchKernelGGL(cut_topp, dim3(cfg->B * cfg->H_kv * cfg->G), dim3(kCutThreads), 0, s, P);
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;

@@ -24,13 +24,14 @@ struct WsLayout {
   size_t attend_off = 0, attend_bytes = 0;
   size_t total = 0;
   // per-level route arrays (offsets from the workspace base); index l-1
-  size_t uids[ZHA_MAX_L], umask[ZHA_MAX_L], ucount[ZHA_MAX_L];
+  size_t kids[ZHA_MAX_L], kmask[ZHA_MAX_L], kcount[ZHA_MAX_L];  // kept list per level
+  size_t ucount[ZHA_MAX_L];  // candidate list length per level and group (diagnostics)
   size_t scores[ZHA_MAX_L], sel[ZHA_MAX_L], kept[ZHA_MAX_L];
-  size_t selor[ZHA_MAX_L];  // per union entry: OR of the heads' kept bits
+  size_t selbits[ZHA_MAX_L];  // per head: kept bits of the union list, 64 entries a word
+  int64_t nwcap[ZHA_MAX_L];
   int64_t cap[ZHA_MAX_L];
   size_t stage = 0;        // cut staging: [B*Hq][stage_cap] (u32 key, f32 w)
   int64_t stage_cap = 0;
-  size_t xstage = 0;       // expansion staging: [B*H_kv][stage_cap] (i32 id, u32 mask)
   int32_t split_cap = 0;   // partial slots per query head
 };
 
@@ -67,13 +68,15 @@ inline WsLayout ws_layout(const zha_cfg& c) {
   for (int l = 1; l <= c.L; ++l) {
     int64_t cap = level_cap(c, l);
     w.cap[l - 1] = cap;
-    w.uids[l - 1] = off;   off = align_up(off + (size_t)BH * cap * 4, 256);
-    w.umask[l - 1] = off;  off = align_up(off + (size_t)BH * cap * 4, 256);
+    w.kids[l - 1] = off;   off = align_up(off + (size_t)BH * cap * 4, 256);
+    w.kmask[l - 1] = off;  off = align_up(off + (size_t)BH * cap * 4, 256);
+    w.kcount[l - 1] = off; off = align_up(off + (size_t)BH * 4, 256);
     w.ucount[l - 1] = off; off = align_up(off + (size_t)BH * 4, 256);
     w.scores[l - 1] = off; off = align_up(off + (size_t)BHq * cap * 4, 256);
     w.sel[l - 1] = off;    off = align_up(off + (size_t)BHq * cap, 256);
     w.kept[l - 1] = off;   off = align_up(off + (size_t)BHq * 4, 256);
-    w.selor[l - 1] = off;  off = align_up(off + (size_t)BH * cap * 4, 256);
+    w.nwcap[l - 1] = (cap + 63) / 64;
+    w.selbits[l - 1] = off; off = align_up(off + (size_t)BHq * w.nwcap[l - 1] * 8, 256);
   }
   // Cut staging for lists too long for LDS: as long as the largest level.
   int64_t scap = 0;
@@ -82,7 +85,6 @@ inline WsLayout ws_layout(const zha_cfg& c) {
   if (lcap > scap) scap = lcap;
   w.stage_cap = scap;
   w.stage = off; off = align_up(off + (size_t)BHq * scap * 8, 256);
-  w.xstage = off; off = align_up(off + (size_t)BH * scap * 8, 256);
   w.route_bytes = off - w.route_off;
   w.attend_off = off;
   w.split_cap = split_capacity(c);

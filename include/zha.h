@@ -103,7 +103,11 @@ typedef struct zha_tree {
   int64_t* n_built;           /* [L][B] int64 nodes built per level and sequence */
 } zha_tree;
 
-/* Bytes of workspace the given operation needs for this geometry. */
+/*
+ * Bytes of workspace the given operation needs for this geometry.  A workspace
+ * must be zero-filled before its first use (it holds the status word).  Calls
+ * that share a workspace must not overlap (use one stream per workspace).
+ */
 size_t zha_workspace_bytes(const zha_cfg* cfg, int32_t op);
 
 /* Human-readable name of a status code (static string). */
