@@ -871,25 +871,16 @@ __global__ void __launch_bounds__(kCompactThreads) compact_level(CompactParams P
 
 // ---------------------------------------------------------------- small levels
 //
-// A level whose list holds at most kSmallCap nodes per group is cut and compacted
-// by one workgroup per group (route_small).  Each wave cuts one head: its
+// A list of at most kSmallCap entries is cut by one wave per head: its
 // candidates, keyed (score desc, id asc), are sorted in registers by a bitonic
 // network; the masses exp(s - max) in that order, as the same 2^40 fixed point
-// the large-list cut uses, give the running sums, and the cut is the first entry
-// whose running mass reaches p W -- the same integers and the same comparisons
-// as cut_topp, so both paths keep the same nodes.  The heads' kept bits are ORed
-// in LDS and the kept entries written in list order, as compact_level does.  A
-// level of at most kTinyCap nodes is also scored by that workgroup (one launch
-// for the whole level); otherwise score_nodes runs first.  Nothing is handed
-// between workgroups inside a launch.
+// cut_topp uses, give the running sums, and the cut is the first entry whose
+// running mass reaches p W -- the same integers and the same comparisons as
+// cut_topp, so both paths keep the same nodes.  The heads' kept bits are ORed in
+// LDS and the kept entries compacted in list order.
 
 constexpr int kSmallCap = 256;
-constexpr int kTinyCap = 16;
 constexpr int kSmallThreads = 256;
-
-struct SmallParams {
-  int32_t* kids; uint32_t* kmask; int32_t* kcount; int64_t kcap;   // kept list out
-};
 
 // Top-p cut of one head over a list of U <= 64*NR entries, by one wave; ORs the
 // head's bit into or_bits[u] of every kept entry and returns the kept count.
@@ -942,68 +933,149 @@ __device__ inline int cut_head_wave(const float* sc, const uint32_t* cand_mask, 
   return ic + 1;
 }
 
-template <int D, int GP, bool SCORE>
-__global__ void __launch_bounds__(kSmallThreads) route_small(LevelParams P, SmallParams S) {
+// The small top levels: every node of every level in the run is scored by one
+// launch (score_upper; these levels hold at most kSmallCap nodes each, a few MB
+// of summaries per group), then one workgroup per group (cut_upper) walks the
+// levels top-down -- cut each head, compact the kept nodes in LDS, take their
+// children plus the parentless nodes as the next level's list, gathering that
+// list's scores by node id -- and writes the lowest level's kept list.  Scoring
+// nodes whose parent was not kept reads summaries the route never uses, but the
+// scores of the nodes it does use are the same numbers, so the selection is
+// unchanged.
+
+struct UpperLevel {
+  const float* khat;           // [BH][ncap][R][d]
+  const float* bhat;           // [BH][ncap][R]
+  int64_t ncap;
+  float* scores;               // [BHq][cap], by node id
+  int64_t cap;
+  int64_t span;                // C^level
+  int32_t* kept;               // [BHq] kept per head (diagnostics)
+  int32_t* ucount;             // [BH] candidates per group (diagnostics)
+};
+
+struct UpperParams {
+  UpperLevel lv[ZHA_MAX_L];    // lv[0]: level L, lv[k]: level L-k
+  int32_t nlev;
+  LevelParams base;            // q, geometry, p, status, stale check
+  int32_t* kids; uint32_t* kmask; int32_t* kcount; int64_t kcap;   // lowest level's kept list
+};
+
+__device__ inline LevelParams upper_level_params(const UpperParams& U, int k) {
+  LevelParams P = U.base;
+  P.khat = U.lv[k].khat;
+  P.bhat = U.lv[k].bhat;
+  P.ncap = U.lv[k].ncap;
+  P.scores = U.lv[k].scores;
+  P.ucap = U.lv[k].cap;
+  return P;
+}
+
+__device__ inline int64_t upper_nodes(const UpperParams& U, int k, int64_t T) {
+  const int64_t n = T / U.lv[k].span;
+  return n < U.lv[k].cap ? n : U.lv[k].cap;
+}
+
+template <int D, int GP>
+__global__ void __launch_bounds__(256) score_upper(UpperParams U) {
+  constexpr int NW = 256 / kWave;
+  const int gi = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t T = U.base.list.T[gi / U.base.H_kv];
+  if (T < 0) T = 0;
+  if (T > U.base.list.T_cap) T = U.base.list.T_cap;
+  int total = 0;
+  for (int k = 0; k < U.nlev; ++k) total += (int)upper_nodes(U, k, T);
+  float qv[GP][4];
+  load_group_queries<D, GP>(U.base, gi, lane, qv);
+  for (int t = blockIdx.x * NW + wave; t < total; t += gridDim.x * NW) {
+    int k = 0, node = t;
+    while (node >= (int)upper_nodes(U, k, T)) { node -= (int)upper_nodes(U, k, T); ++k; }
+    score_node<D, GP>(upper_level_params(U, k), gi, node, node, qv, lane);
+  }
+}
+
+template <int GP>
+__global__ void __launch_bounds__(kSmallThreads) cut_upper(UpperParams U) {
   constexpr int NW = kSmallThreads / kWave;
-  __shared__ uint32_t s_cm[kSmallCap];    // candidate masks
-  __shared__ int32_t s_id[kSmallCap];     // node ids
-  __shared__ uint32_t s_or[kSmallCap];    // OR of the heads' kept bits
+  __shared__ int32_t s_id[kSmallCap];     // this level's list: node ids
+  __shared__ uint32_t s_cm[kSmallCap];    //   head masks
+  __shared__ float s_sc[GP][kSmallCap];   //   scores per head
+  __shared__ uint32_t s_or[kSmallCap];    //   OR of the heads' kept bits
+  __shared__ int32_t s_kid[kSmallCap];    // kept list of the level above / this level
+  __shared__ uint32_t s_km[kSmallCap];
   __shared__ int32_t s_red[NW];
+  const LevelParams& B = U.base;
   const int gi = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) stale_check(P, gi);
-  const ListGeo geo = list_geo(P.list, gi, P.ucap);
-  const int U = geo.U < kSmallCap ? geo.U : kSmallCap;
-  for (int u = tid; u < kSmallCap; u += kSmallThreads) {
-    s_or[u] = 0u;
-    if (u < U) {
-      int32_t id; uint32_t m;
-      list_entry(P.list, geo, gi, u, id, m);
-      s_id[u] = id;
-      s_cm[u] = m;
+  if (tid == 0) stale_check(B, gi);
+  int64_t T = B.list.T[gi / B.H_kv];
+  if (T < 0) T = 0;
+  if (T > B.list.T_cap) T = B.list.T_cap;
+  const int C = B.list.C, cshift = B.list.cshift;
+  const uint32_t full = B.list.full;
+  int np = 0;   // kept nodes of the level above
+  for (int k = 0; k < U.nlev; ++k) {
+    const UpperLevel& lv = U.lv[k];
+    const int64_t n_here = upper_nodes(U, k, T);
+    int cnt;
+    int64_t orph0 = 0;
+    if (k == 0) {
+      cnt = (int)n_here;
+    } else {
+      orph0 = (T / (lv.span * C)) * C;
+      const int64_t orph = n_here - orph0;
+      cnt = np * C + (int)(orph > 0 ? orph : 0);
     }
-  }
-  __syncthreads();
-
-  if constexpr (SCORE) {
-    float qv[GP][4];
-    load_group_queries<D, GP>(P, gi, lane, qv);
-    for (int u = wave; u < U; u += NW) score_node<D, GP>(P, gi, s_id[u], u, qv, lane);
-    __syncthreads();   // the scores are read back by other waves of this workgroup
-  }
-
-  // ---- cut: wave w takes heads w, w + NW, ...
-  for (int g = wave; g < P.G; g += NW) {
-    const int64_t head = (int64_t)gi * P.G + g;
-    const float* sc = P.scores + head * P.ucap;
-    int kept;
-    if (U <= 64) kept = cut_head_wave<1>(sc, s_cm, 1u << g, U, P.p, s_or, lane);
-    else if (U <= 128) kept = cut_head_wave<2>(sc, s_cm, 1u << g, U, P.p, s_or, lane);
-    else kept = cut_head_wave<4>(sc, s_cm, 1u << g, U, P.p, s_or, lane);
-    if (lane == 0) P.kept[head] = kept;
-  }
-  __syncthreads();
-  // ---- kept entries in list order
-  const uint32_t m = (tid < U) ? s_or[tid] : 0u;
-  const uint64_t bal = __ballot(m != 0u);
-  if (lane == 0) s_red[wave] = __popcll(bal);
-  __syncthreads();
-  int pos = 0, nsel = 0;
+    if (cnt > kSmallCap) cnt = kSmallCap;
+    for (int u = tid; u < kSmallCap; u += kSmallThreads) {
+      s_or[u] = 0u;
+      if (u < cnt) {
+        int32_t id;
+        uint32_t m;
+        if (k == 0) { id = u; m = full; }
+        else if (u < np * C) { id = s_kid[u >> cshift] * C + (u & (C - 1)); m = s_km[u >> cshift]; }
+        else { id = (int32_t)(orph0 + (u - np * C)); m = full; }
+        s_id[u] = id;
+        s_cm[u] = m;
+        for (int g = 0; g < B.G; ++g) s_sc[g][u] = lv.scores[((int64_t)gi * B.G + g) * lv.cap + id];
+      }
+    }
+    __syncthreads();
+    for (int g = wave; g < B.G; g += NW) {
+      int kept;
+      if (cnt <= 64) kept = cut_head_wave<1>(s_sc[g], s_cm, 1u << g, cnt, B.p, s_or, lane);
+      else if (cnt <= 128) kept = cut_head_wave<2>(s_sc[g], s_cm, 1u << g, cnt, B.p, s_or, lane);
+      else kept = cut_head_wave<4>(s_sc[g], s_cm, 1u << g, cnt, B.p, s_or, lane);
+      if (lane == 0) lv.kept[(int64_t)gi * B.G + g] = kept;
+    }
+    __syncthreads();
+    // kept entries in list order become the kept list of this level
+    const uint32_t m = (tid < cnt) ? s_or[tid] : 0u;
+    const uint64_t bal = __ballot(m != 0u);
+    if (lane == 0) s_red[wave] = __popcll(bal);
+    __syncthreads();
+    int pos = 0, nsel = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    pos += (w < wave) ? s_red[w] : 0;
-    nsel += s_red[w];
+    for (int w = 0; w < NW; ++w) {
+      pos += (w < wave) ? s_red[w] : 0;
+      nsel += s_red[w];
+    }
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    pos += __popcll(bal & lt);
+    if (m != 0u) { s_kid[pos] = s_id[tid]; s_km[pos] = m; }
+    if (tid == 0) lv.ucount[gi] = cnt;
+    np = nsel;
+    __syncthreads();
   }
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  pos += __popcll(bal & lt);
-  if (m != 0u && pos < S.kcap) {
-    S.kids[(int64_t)gi * S.kcap + pos] = s_id[tid];
-    S.kmask[(int64_t)gi * S.kcap + pos] = m;
+  const int nout = np < U.kcap ? np : (int)U.kcap;
+  for (int i = tid; i < nout; i += kSmallThreads) {
+    U.kids[(int64_t)gi * U.kcap + i] = s_kid[i];
+    U.kmask[(int64_t)gi * U.kcap + i] = s_km[i];
   }
   if (tid == 0) {
-    if (nsel > S.kcap) set_status(P.status, ZHA_ECAPACITY);
-    S.kcount[gi] = nsel > S.kcap ? (int32_t)S.kcap : nsel;
-    if (P.ucount_out != nullptr) P.ucount_out[gi] = U;
+    if (np > U.kcap) set_status(B.status, ZHA_ECAPACITY);
+    U.kcount[gi] = nout;
   }
 }
 
@@ -1029,19 +1101,26 @@ static void launch_score(const LevelParams& P, int64_t ucap, hipStream_t s) {
   }
 }
 
-template <bool SCORE>
-static void launch_small_t(const LevelParams& P, const SmallParams& S, hipStream_t s) {
-  const dim3 grid((unsigned)(P.B * P.H_kv));
-  const int GP = P.G <= 4 ? 4 : (P.G <= 8 ? 8 : 16);
-  if (P.d == 128) {
-    if (GP == 4) hipLaunchKernelGGL((route_small<128, 4, SCORE>), grid, dim3(kSmallThreads), 0, s, P, S);
-    else if (GP == 8) hipLaunchKernelGGL((route_small<128, 8, SCORE>), grid, dim3(kSmallThreads), 0, s, P, S);
-    else hipLaunchKernelGGL((route_small<128, 16, SCORE>), grid, dim3(kSmallThreads), 0, s, P, S);
+static void launch_upper(const UpperParams& U, hipStream_t s) {
+  const int BH = U.base.B * U.base.H_kv;
+  int64_t nodes = 0;
+  for (int k = 0; k < U.nlev; ++k) nodes += U.lv[k].cap;
+  int64_t gx = ceil_div(nodes, 4);   // one node per wave
+  if (gx < 1) gx = 1;
+  const dim3 grid((unsigned)gx, (unsigned)BH);
+  const int GP = U.base.G <= 4 ? 4 : (U.base.G <= 8 ? 8 : 16);
+  if (U.base.d == 128) {
+    if (GP == 4) hipLaunchKernelGGL((score_upper<128, 4>), grid, dim3(256), 0, s, U);
+    else if (GP == 8) hipLaunchKernelGGL((score_upper<128, 8>), grid, dim3(256), 0, s, U);
+    else hipLaunchKernelGGL((score_upper<128, 16>), grid, dim3(256), 0, s, U);
   } else {
-    if (GP == 4) hipLaunchKernelGGL((route_small<64, 4, SCORE>), grid, dim3(kSmallThreads), 0, s, P, S);
-    else if (GP == 8) hipLaunchKernelGGL((route_small<64, 8, SCORE>), grid, dim3(kSmallThreads), 0, s, P, S);
-    else hipLaunchKernelGGL((route_small<64, 16, SCORE>), grid, dim3(kSmallThreads), 0, s, P, S);
+    if (GP == 4) hipLaunchKernelGGL((score_upper<64, 4>), grid, dim3(256), 0, s, U);
+    else if (GP == 8) hipLaunchKernelGGL((score_upper<64, 8>), grid, dim3(256), 0, s, U);
+    else hipLaunchKernelGGL((score_upper<64, 16>), grid, dim3(256), 0, s, U);
   }
+  if (GP == 4) hipLaunchKernelGGL((cut_upper<4>), dim3(BH), dim3(kSmallThreads), 0, s, U);
+  else if (GP == 8) hipLaunchKernelGGL((cut_upper<8>), dim3(BH), dim3(kSmallThreads), 0, s, U);
+  else hipLaunchKernelGGL((cut_upper<16>), dim3(BH), dim3(kSmallThreads), 0, s, U);
 }
 
 static int32_t check_route_common(const zha_cfg* cfg, const float* q, const zha_tree* tree,
@@ -1114,10 +1193,46 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
   char* base = (char*)ws;
   const int BH = cfg->B * cfg->H_kv, BHq = BH * cfg->G, L = cfg->L;
 
-  // Levels whose lists hold at most kSmallCap nodes are cut and compacted by
-  // route_small (scored in the same launch when at most kTinyCap); longer ones
-  // run score_nodes, cut_topp and compact_level.
-  for (int l = L; l >= 1; --l) {
+  auto kept_list = [&](int l, int32_t*& kids, uint32_t*& kmask, int32_t*& kcount, int64_t& kcap) {
+    if (l > 1) {
+      kids = (int32_t*)(base + w.kids[l - 1]);
+      kmask = (uint32_t*)(base + w.kmask[l - 1]);
+      kcount = (int32_t*)(base + w.kcount[l - 1]);
+      kcap = w.cap[l - 1];
+    } else {
+      kids = leaf_ids; kmask = leaf_mask; kcount = leaf_count; kcap = cfg->leaf_cap;
+    }
+  };
+  // The run of small levels from the top (at most kSmallCap nodes each) is scored
+  // in one launch and cut in another; each lower level runs score_nodes,
+  // cut_topp and compact_level on the list implied by the level above.
+  int lo = L + 1;
+  if (w.cap[L - 1] <= kSmallCap) {
+    lo = L;
+    while (lo > 1 && w.cap[lo - 2] <= kSmallCap) --lo;
+    UpperParams U;
+    U.base = level_params(cfg, q, tree, L, p, ws, w);
+    U.base.list.T = T;
+    U.base.check_stale = 1;
+    U.nlev = L - lo + 1;
+    for (int k = 0; k < U.nlev; ++k) {
+      const int l = L - k;
+      UpperLevel& v = U.lv[k];
+      v.khat = tree->khat[l - 1];
+      v.bhat = tree->bhat[l - 1];
+      v.ncap = tree->n_cap[l - 1];
+      v.scores = (float*)(base + w.scores[l - 1]);
+      v.cap = w.cap[l - 1];
+      int64_t span = 1;
+      for (int i = 0; i < l; ++i) span *= cfg->C;
+      v.span = span;
+      v.kept = (int32_t*)(base + w.kept[l - 1]);
+      v.ucount = (int32_t*)(base + w.ucount[l - 1]);
+    }
+    kept_list(lo, U.kids, U.kmask, U.kcount, U.kcap);
+    launch_upper(U, s);
+  }
+  for (int l = lo - 1; l >= 1; --l) {
     LevelParams P = level_params(cfg, q, tree, l, p, ws, w);
     P.list.T = T;
     if (l < L) {   // children of the kept nodes of level l+1, then the parentless nodes
@@ -1131,35 +1246,14 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
     P.scores = (float*)(base + w.scores[l - 1]);
     P.kept = (int32_t*)(base + w.kept[l - 1]);
     P.check_stale = (l == L) ? 1 : 0;
-    int32_t* kids; uint32_t* kmask; int32_t* kcount; int64_t kcap;
-    if (l > 1) {
-      kids = (int32_t*)(base + w.kids[l - 1]);
-      kmask = (uint32_t*)(base + w.kmask[l - 1]);
-      kcount = (int32_t*)(base + w.kcount[l - 1]);
-      kcap = w.cap[l - 1];
-    } else {
-      kids = leaf_ids; kmask = leaf_mask; kcount = leaf_count; kcap = cfg->leaf_cap;
-    }
-    if (w.cap[l - 1] <= kSmallCap) {
-      SmallParams S;
-      S.kids = kids; S.kmask = kmask; S.kcount = kcount; S.kcap = kcap;
-      if (w.cap[l - 1] <= kTinyCap) {
-        launch_small_t<true>(P, S, s);
-      } else {
-        launch_score(P, P.ucap, s);
-        P.check_stale = 0;
-        launch_small_t<false>(P, S, s);
-      }
-      continue;
-    }
     P.selbits = (uint64_t*)(base + w.selbits[l - 1]);
     P.nwcap = w.nwcap[l - 1];
-    launch_score(P, P.ucap, s);
-    P.check_stale = 0;
     CompactParams X;
     X.list = P.list; X.ucap = P.ucap; X.selbits = P.selbits; X.nwcap = P.nwcap; X.G = cfg->G;
-    X.kids = kids; X.kmask = kmask; X.kcount = kcount; X.kcap = kcap;
+    kept_list(l, X.kids, X.kmask, X.kcount, X.kcap);
     X.status = (int32_t*)ws;
+    launch_score(P, P.ucap, s);
+    P.check_stale = 0;
     hipLaunchKernelGGL(cut_topp, dim3(BHq), dim3(kCutThreads), 0, s, P);
     hipLaunchKernelGGL(compact_level, dim3(BH), dim3(kCompactThreads), 0, s, X);
   }
