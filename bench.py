@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
     ap.add_argument("--no-stats", action="store_true", help="skip the byte-accounting replay")
+    ap.add_argument("--n-sweep", default="17,18,19",
+                    help="log2 context lengths also timed routed vs dense (comma list, '' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (known bytes) for counter calibration")
     return ap.parse_args()
@@ -329,6 +331,30 @@ def main():
         dense["hbm_frac"] = dense["effective_GBps"] / HBM_PEAK_GBPS
         log(f"[bench] dense: {dense['us_per_step']:.1f} us/step, {dense['effective_GBps']:.0f} GB/s")
 
+    # ---- quality of the routed steps against dense attention (untimed): the
+    # dense softmax mass the routed key set holds is exp(lse_routed - lse_dense)
+    if not args.no_dense:
+        recall, oerr = [], []
+        o_r = torch.empty_like(run.dec.out)
+        l_r = torch.empty_like(run.dec.lse)
+        for i, lst in enumerate(keep):
+            s = W + i
+            zha.attend(run.cfg, run.Q[s], run.K, run.V, run.Ts[s], lst.ids, lst.mask, lst.count,
+                       o_r, l_r, run.dec.ws)
+            zha.dense_attend(run.cfg, run.Q[s], run.K, run.V, run.Ts[s], run.dec.out,
+                             run.dec.lse, run.dec.ws)
+            recall.append(torch.exp(l_r - run.dec.lse).flatten())
+            num = (o_r - run.dec.out).abs().amax(dim=-1)
+            oerr.append((num / run.dec.out.abs().amax(dim=-1).clamp_min(1e-30)).flatten())
+        recall = torch.cat(recall).double().cpu()
+        oerr = torch.cat(oerr).double().cpu()
+        extra["quality_vs_dense"] = {
+            "mass_recall_mean": float(recall.mean()), "mass_recall_min": float(recall.min()),
+            "out_rel_err_mean": float(oerr.mean()), "out_rel_err_max": float(oerr.max()),
+            "note": "per query head and step: recall = dense softmax mass of the routed key set"}
+        log(f"[bench] dense-mass recall of the routed sets: mean {float(recall.mean()):.4f}, "
+            f"min {float(recall.min()):.4f}")
+
     # ---- byte accounting from the breakdown pass's route diagnostics
     route_bytes = attend_bytes = keys_total = 0
     sel_frac = None
@@ -359,6 +385,34 @@ def main():
         "avg_launch_us": attend_us if dominant == "attend" else route_us,
         "algorithmic_bytes_per_launch": (attend_bytes if dominant == "attend" else route_bytes) / K,
     }
+
+    # ---- context-length sweep at the same geometry: routed vs dense
+    sweep = {}
+    for e in [int(x) for x in args.n_sweep.split(",") if x.strip()]:
+        if (1 << e) == wl.N:
+            continue
+        del keep
+        keep = None
+        torch.cuda.empty_cache()
+        wls = wl.with_(N=1 << e)
+        Ws, Ks = 4, 16
+        rs = Run(wls, Ws + Ks)
+        rs.prefill()
+        rs.routed_steps(0, Ws, p)
+        ms_r = timed(lambda: rs.routed_steps(Ws, Ws + Ks, p))
+        rs.dense_steps(0, Ws)
+        ms_d = timed(lambda: rs.dense_steps(Ws, Ws + Ks))
+        sweep[str(wls.T0)] = {"routed_us_per_step": ms_r * 1000.0 / Ks,
+                              "dense_us_per_step": ms_d * 1000.0 / Ks,
+                              "speedup_vs_dense": ms_d / ms_r}
+        log(f"[bench] T={wls.T0}: routed {ms_r * 1000 / Ks:.1f} us/step, dense {ms_d * 1000 / Ks:.1f}")
+        del rs
+        torch.cuda.empty_cache()
+    if sweep:
+        sweep[str(wl.T0)] = {"routed_us_per_step": us_step,
+                             "dense_us_per_step": dense["us_per_step"] if dense else None,
+                             "speedup_vs_dense": (dense["us_per_step"] / us_step) if dense else None}
+        extra["context_sweep"] = sweep
 
     cpu = None
     if not args.no_cpu:
