@@ -952,6 +952,7 @@ struct UpperLevel {
   int64_t span;                // C^level
   int32_t* kept;               // [BHq] kept per head (diagnostics)
   int32_t* ucount;             // [BH] candidates per group (diagnostics)
+  float p;                     // this level's top-p
 };
 
 struct UpperParams {
@@ -1044,9 +1045,9 @@ __global__ void __launch_bounds__(kSmallThreads) cut_upper(UpperParams U) {
     __syncthreads();
     for (int g = wave; g < B.G; g += NW) {
       int kept;
-      if (cnt <= 64) kept = cut_head_wave<1>(s_sc[g], s_cm, 1u << g, cnt, B.p, s_or, lane);
-      else if (cnt <= 128) kept = cut_head_wave<2>(s_sc[g], s_cm, 1u << g, cnt, B.p, s_or, lane);
-      else kept = cut_head_wave<4>(s_sc[g], s_cm, 1u << g, cnt, B.p, s_or, lane);
+      if (cnt <= 64) kept = cut_head_wave<1>(s_sc[g], s_cm, 1u << g, cnt, lv.p, s_or, lane);
+      else if (cnt <= 128) kept = cut_head_wave<2>(s_sc[g], s_cm, 1u << g, cnt, lv.p, s_or, lane);
+      else kept = cut_head_wave<4>(s_sc[g], s_cm, 1u << g, cnt, lv.p, s_or, lane);
       if (lane == 0) lv.kept[(int64_t)gi * B.G + g] = kept;
     }
     __syncthreads();
@@ -1124,13 +1125,14 @@ static void launch_upper(const UpperParams& U, hipStream_t s) {
 }
 
 static int32_t check_route_common(const zha_cfg* cfg, const float* q, const zha_tree* tree,
-                                  float p) {
+                                  const float* p, int np) {
   int32_t rc = zha_check_cfg(cfg);
   if (rc != ZHA_OK) return rc;
   if (cfg->G > 16) return ZHA_EUNSUPPORTED;
   if ((int64_t)cfg->B * cfg->H_kv > 65535) return ZHA_EUNSUPPORTED;
-  if (q == nullptr || tree == nullptr) return ZHA_EINVAL;
-  if (!(p > 0.0f) || !(p <= 1.0f)) return ZHA_EINVAL;
+  if (q == nullptr || tree == nullptr || p == nullptr) return ZHA_EINVAL;
+  for (int i = 0; i < np; ++i)
+    if (!(p[i] > 0.0f) || !(p[i] <= 1.0f)) return ZHA_EINVAL;
   int64_t span = 1;
   for (int l = 1; l <= cfg->L; ++l) {
     span *= cfg->C;
@@ -1173,14 +1175,11 @@ static LevelParams level_params(const zha_cfg* cfg, const float* q, const zha_tr
   return P;
 }
 
-}  // namespace zha
-
-extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree* tree,
-                             const int64_t* T, float p, int32_t* leaf_ids,
-                             uint32_t* leaf_mask, int32_t* leaf_count, void* ws,
-                             size_t ws_bytes, void* stream) {
-  using namespace zha;
-  int32_t rc = check_route_common(cfg, q, tree, p);
+static int32_t route_impl(const zha_cfg* cfg, const float* q, const zha_tree* tree,
+                          const int64_t* T, const float* pl, int32_t* leaf_ids,
+                          uint32_t* leaf_mask, int32_t* leaf_count, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int32_t rc = check_route_common(cfg, q, tree, pl, cfg->L);
   if (rc != ZHA_OK) return rc;
   if (T == nullptr || tree->n_built == nullptr || leaf_ids == nullptr ||
       leaf_mask == nullptr || leaf_count == nullptr)
@@ -1211,7 +1210,7 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
     lo = L;
     while (lo > 1 && w.cap[lo - 2] <= kSmallCap) --lo;
     UpperParams U;
-    U.base = level_params(cfg, q, tree, L, p, ws, w);
+    U.base = level_params(cfg, q, tree, L, pl[L - 1], ws, w);
     U.base.list.T = T;
     U.base.check_stale = 1;
     U.nlev = L - lo + 1;
@@ -1228,12 +1227,13 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
       v.span = span;
       v.kept = (int32_t*)(base + w.kept[l - 1]);
       v.ucount = (int32_t*)(base + w.ucount[l - 1]);
+      v.p = pl[l - 1];
     }
     kept_list(lo, U.kids, U.kmask, U.kcount, U.kcap);
     launch_upper(U, s);
   }
   for (int l = lo - 1; l >= 1; --l) {
-    LevelParams P = level_params(cfg, q, tree, l, p, ws, w);
+    LevelParams P = level_params(cfg, q, tree, l, pl[l - 1], ws, w);
     P.list.T = T;
     if (l < L) {   // children of the kept nodes of level l+1, then the parentless nodes
       P.list.pids = (const int32_t*)(base + w.kids[l]);
@@ -1260,13 +1260,35 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
 }
 
+}  // namespace zha
+
+extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree* tree,
+                             const int64_t* T, float p, int32_t* leaf_ids,
+                             uint32_t* leaf_mask, int32_t* leaf_count, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (cfg == nullptr) return ZHA_EINVAL;
+  float pl[ZHA_MAX_L];
+  const int L = (cfg->L >= 1 && cfg->L <= ZHA_MAX_L) ? cfg->L : 1;
+  for (int i = 0; i < L; ++i) pl[i] = p;
+  return zha::route_impl(cfg, q, tree, T, pl, leaf_ids, leaf_mask, leaf_count, ws, ws_bytes,
+                         stream);
+}
+
+extern "C" int32_t zha_route_sched(const zha_cfg* cfg, const float* q, const zha_tree* tree,
+                                   const int64_t* T, const float* p_levels, int32_t* leaf_ids,
+                                   uint32_t* leaf_mask, int32_t* leaf_count, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return zha::route_impl(cfg, q, tree, T, p_levels, leaf_ids, leaf_mask, leaf_count, ws,
+                         ws_bytes, stream);
+}
+
 extern "C" int32_t zha_route_level(const zha_cfg* cfg, int32_t level, const float* q,
                                    const zha_tree* tree, float p, const int32_t* cand_ids,
                                    const uint32_t* cand_mask, const int32_t* cand_count,
                                    int32_t cand_cap, float* scores, uint8_t* sel,
                                    void* ws, size_t ws_bytes, void* stream) {
   using namespace zha;
-  int32_t rc = check_route_common(cfg, q, tree, p);
+  int32_t rc = check_route_common(cfg, q, tree, &p, 1);
   if (rc != ZHA_OK) return rc;
   if (level < 1 || level > cfg->L) return ZHA_EINVAL;
   if (cand_ids == nullptr || cand_mask == nullptr || cand_count == nullptr ||

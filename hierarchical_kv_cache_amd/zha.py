@@ -24,8 +24,8 @@ F32, BF16 = 0, 1
 OP_BUILD, OP_ROUTE, OP_ATTEND, OP_DENSE, OP_ALL = range(5)
 
 EXPORTS = ["zha_workspace_bytes", "zha_status_str", "zha_build_level", "zha_append",
-           "zha_route", "zha_route_level", "zha_attend", "dense_attend", "zha_route_counts",
-           "zha_ws_status"]
+           "zha_route", "zha_route_sched", "zha_route_level", "zha_attend", "dense_attend",
+           "zha_route_counts", "zha_ws_status"]
 
 
 class ZhaError(RuntimeError):
@@ -64,6 +64,7 @@ def _load() -> ctypes.CDLL:
         "zha_build_level": (i32, [cfgp, i32, kvp, P, treep, P, sz, P]),
         "zha_append": (i32, [cfgp, kvp, P, treep, i64, P, sz, P]),
         "zha_route": (i32, [cfgp, P, treep, P, f32, P, P, P, P, sz, P]),
+        "zha_route_sched": (i32, [cfgp, P, treep, P, ctypes.POINTER(f32), P, P, P, P, sz, P]),
         "zha_route_level": (i32, [cfgp, i32, P, treep, f32, P, P, P, i32, P, P, P, sz, P]),
         "zha_attend": (i32, [cfgp, P, kvp, P, P, P, P, P, P, sz, P]),
         "dense_attend": (i32, [cfgp, P, kvp, P, P, P, sz, P]),
@@ -195,11 +196,41 @@ def append(cfg: Config, K, V, T, qref, tree: Tree, ws, max_new_tokens: int = 1, 
                            _stream(stream)), "zha_append")
 
 
-def route(cfg: Config, q, tree: Tree, T, p: float, leaf_ids, leaf_mask, leaf_count, ws,
+def route(cfg: Config, q, tree: Tree, T, p, leaf_ids, leaf_mask, leaf_count, ws,
           stream=None):
+    """p: one top-p for every level, or a sequence of cfg.L values (entry l-1 for
+    level l), which calls zha_route_sched."""
+    if isinstance(p, (list, tuple)):
+        if len(p) != cfg.L:
+            raise ValueError(f"a depth schedule needs {cfg.L} values, got {len(p)}")
+        arr = (ctypes.c_float * cfg.L)(*[float(x) for x in p])
+        _check(_lib.zha_route_sched(ctypes.byref(cfg.c()), _ptr(q), ctypes.byref(tree.c()),
+                                    _ptr(T), arr, _ptr(leaf_ids), _ptr(leaf_mask),
+                                    _ptr(leaf_count), _ptr(ws), ws.numel(), _stream(stream)),
+               "zha_route_sched")
+        return
     _check(_lib.zha_route(ctypes.byref(cfg.c()), _ptr(q), ctypes.byref(tree.c()), _ptr(T),
                           float(p), _ptr(leaf_ids), _ptr(leaf_mask), _ptr(leaf_count),
                           _ptr(ws), ws.numel(), _stream(stream)), "zha_route")
+
+
+def p_schedule(kind: str, p: float, L: int, gamma: float = 1.0):
+    """Per-level top-p whose product is p (entry l-1 for level l).
+
+    "uniform": p at every level (the product is then p^L).
+    "root": p^(1/L) at every level.
+    "power": p^(w_l) with w_l proportional to l^-gamma and summing to one, so the
+    lowest levels, which hold the most candidates, cut hardest.
+    """
+    if kind == "uniform":
+        return [float(p)] * L
+    if kind == "root":
+        return [float(p) ** (1.0 / L)] * L
+    if kind == "power":
+        w = [float(l) ** (-gamma) for l in range(1, L + 1)]
+        tot = sum(w)
+        return [float(p) ** (x / tot) for x in w]
+    raise ValueError(f"unknown schedule {kind!r}")
 
 
 def route_level(cfg: Config, level: int, q, tree: Tree, p: float, cand_ids, cand_mask,

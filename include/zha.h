@@ -162,6 +162,17 @@ int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree* tree,
                   void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * zha_route_sched -- zha_route with one top-p per level (host array p_levels,
+ * entry l-1 for level l, each in (0, 1]): a depth schedule of the per-level cut,
+ * the open question of scaling p with depth raised in [ZHA] "전제와 한계".
+ * zha_route(p) equals zha_route_sched with every entry p.
+ */
+int32_t zha_route_sched(const zha_cfg* cfg, const float* q, const zha_tree* tree,
+                        const int64_t* T, const float* p_levels,
+                        int32_t* leaf_ids, uint32_t* leaf_mask, int32_t* leaf_count,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
  * zha_route_level -- one level of zha_route on a given candidate list, for tests
  * and custom schedules.  cand_ids/cand_mask/cand_count use the leaf-list layout
  * with capacity cand_cap ([B][H_kv][cand_cap]; ids ascending, bit g = candidate of

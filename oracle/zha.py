@@ -302,7 +302,7 @@ class Route:
         raise KeyError(l)
 
 
-def route(q, tree, T: int, C: int, L: int, p: float, scale: float,
+def route(q, tree, T: int, C: int, L: int, p, scale: float,
           level_override=None) -> Route:
     """Route one query down a tree ([ZHA] "전제와 한계").
 
@@ -310,6 +310,9 @@ def route(q, tree, T: int, C: int, L: int, p: float, scale: float,
     scored (max over planes), cut by top-p, and the next level's candidates are
     the children of the selected nodes plus that level's parentless nodes
     (n >= C * n_{l+1}).  An empty pool selects nothing.
+    ``p`` is one top-p for every level, or a sequence of L values (entry l-1 for
+    level l): a depth schedule, the open question of scaling p with depth that
+    the same section raises.
     ``level_override`` (optional dict level -> selected ids) replaces the cut of
     that level, so a comparison can continue from another implementation's
     allowed choice.
@@ -321,7 +324,7 @@ def route(q, tree, T: int, C: int, L: int, p: float, scale: float,
     for level in range(L, 0, -1):
         lv = tree[level - 1]
         scores = np.array([node_score(q, lv["khat"][n], lv["bhat"][n], scale) for n in cand])
-        cut = topp_cut(cand, scores, p)
+        cut = topp_cut(cand, scores, p[level - 1] if np.ndim(p) else p)
         if level_override is not None and level in level_override:
             cut.selected = np.sort(np.asarray(level_override[level], np.int64))
             cut.m = cut.selected.size

@@ -1,6 +1,7 @@
 """The C ABI library loads, exports every function include/zha.h declares, and
 rejects bad arguments on the host before launching anything (no GPU needed)."""
 import ctypes
+import math
 import os
 import re
 import shutil
@@ -80,6 +81,22 @@ def test_bad_arguments_return_codes_without_launching():
     assert _route(g17, ws_bytes=1 << 30) == zha.EUNSUPPORTED
     out = zha._lib.dense_attend(ctypes.byref(cfg.c()), None, None, None, None, None, 0, None)
     assert out == zha.EINVAL
+    fake = ctypes.c_void_p(0x1000)
+    tree = zha._Tree()
+    for i in range(cfg.L):
+        tree.khat[i] = 0x2000
+        tree.bhat[i] = 0x3000
+        tree.n_cap[i] = cfg.level_cap(i + 1)
+    tree.n_built = 0x4000
+    need = zha.workspace_bytes(cfg, zha.OP_ROUTE)
+    for bad in ([0.9, 1.5, 0.9], [0.9, 0.0, 0.9], [float("nan"), 0.9, 0.9]):
+        arr = (ctypes.c_float * 3)(*bad)
+        rc = zha._lib.zha_route_sched(ctypes.byref(cfg.c()), fake, ctypes.byref(tree), fake, arr,
+                                      fake, fake, fake, ctypes.c_void_p(0x100000), need, None)
+        assert rc == zha.EINVAL, bad
+    rc = zha._lib.zha_route_sched(ctypes.byref(cfg.c()), fake, ctypes.byref(tree), fake, None,
+                                  fake, fake, fake, ctypes.c_void_p(0x100000), need, None)
+    assert rc == zha.EINVAL
 
 
 def test_missing_library_fails_loudly(tmp_path):
@@ -89,3 +106,14 @@ def test_missing_library_fails_loudly(tmp_path):
     code = "import hierarchical_kv_cache_amd as h; h.Config"
     r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True)
     assert r.returncode != 0 and "ImportError" in r.stderr and "not built" in r.stderr
+
+
+def test_p_schedules_multiply_to_p():
+    for L in (1, 3, 6):
+        for kind in ("root", "power"):
+            pl = zha.p_schedule(kind, 0.8, L, gamma=1.5)
+            assert len(pl) == L and all(0 < x <= 1 for x in pl)
+            assert abs(math.prod(pl) - 0.8) < 1e-12
+        assert zha.p_schedule("uniform", 0.8, L) == [0.8] * L
+    pw = zha.p_schedule("power", 0.8, 4, gamma=1.0)
+    assert pw == sorted(pw)   # the leaf level cuts hardest

@@ -73,7 +73,8 @@ def level_sync_compare(cfg, tree_gpu, trees_host, q, T, p, ws, report):
         cap = ids.shape[-1]
         scores = torch.full((cfg.B, cfg.Hq, cap), float("nan"), device=DEV)
         sel = torch.zeros(cfg.B, cfg.Hq, cap, dtype=torch.uint8, device=DEV)
-        zha.route_level(cfg, level, q, tree_gpu, p, ids.to(DEV), mask.to(DEV), count.to(DEV),
+        p_here = p[level - 1] if isinstance(p, (list, tuple)) else p
+        zha.route_level(cfg, level, q, tree_gpu, p_here, ids.to(DEV), mask.to(DEV), count.to(DEV),
                         scores, sel, ws)
         torch.cuda.synchronize()
         sc, sl = scores.cpu().numpy(), sel.cpu().numpy()
@@ -296,3 +297,33 @@ def test_cut_crossing_bucket_sizes(n_band, p):
     m = int(lst.count[0, 0])
     np.testing.assert_array_equal(lst.ids[0, 0, :m].cpu().numpy(), np.sort(cut.selected))
     assert zha.ws_status(ws) == 0
+
+
+@pytest.mark.parametrize("case", ["gqa_c16", "deep", "tiny"])
+@pytest.mark.parametrize("kind", ["root", "power", "mixed"])
+def test_depth_scheduled_p(case, kind):
+    """zha_route_sched: one top-p per level, level by level against the oracle,
+    and end to end equal to the level-by-level composition."""
+    wl, T = CASES[case]
+    cfg, K, V, trees = _setup(wl, T)
+    tree = upload(cfg, trees, T)
+    ws = zha.new_workspace(cfg)
+    Tt = torch.full((cfg.B,), T, dtype=torch.int64, device=DEV)
+    if kind == "mixed":
+        pl = [0.6 if l % 2 else 0.97 for l in range(1, cfg.L + 1)]
+    else:
+        pl = zha.p_schedule(kind, 0.8, cfg.L, gamma=1.5)
+    report = []
+    for step in range(2):
+        q = synth.make_query(wl, step, T, "cpu").to(DEV)
+        leaves = level_sync_compare(cfg, tree, trees, q, T, pl, ws, report)
+        lst = zha.LeafList(cfg, DEV)
+        zha.route(cfg, q, tree, Tt, pl, lst.ids, lst.mask, lst.count, ws)
+        torch.cuda.synchronize()
+        full = sets_from_lists(lst.ids, lst.mask, lst.count, cfg.G)
+        for b in range(cfg.B):
+            for j in range(cfg.Hq):
+                np.testing.assert_array_equal(full[b][j], leaves[b][j])
+        assert zha.ws_status(ws) == 0
+    for r in report:
+        print("allowed:", case, kind, r)

@@ -391,3 +391,29 @@ def test_rope_relative_and_generator_agrees():
     got = synth.rope_rotate(x, pos, base).numpy()
     for i in range(3):
         np.testing.assert_allclose(got[i], O.rope(x[i].numpy(), int(pos[i]), base), atol=1e-12)
+
+
+def test_depth_schedule_indexing_reduces_to_flat_route():
+    """With p = 1 at every level above the leaves, the level-wise route keeps every
+    upper node, so its leaves are the flat top-p over all leaves (L = 1) at the
+    leaf level's p; a schedule entry applied to the wrong level breaks this."""
+    rng = np.random.default_rng(5)
+    C, d, R, T = 8, 16, 3, 8 ** 3 * 2 + 5
+    K = rng.standard_normal((T, d))
+    K[: T // 2] += 1.5 * rng.standard_normal(d)
+    qref = rng.standard_normal((R, d)) / np.sqrt(d)
+    scale = 1 / np.sqrt(d)
+    t3 = O.build_tree(K, qref, T, C, 3, scale)
+    t1 = O.build_tree(K, qref, T, C, 1, scale)
+    for s in range(4):
+        q = rng.standard_normal(d) * 2
+        for p in (0.5, 0.8):
+            deep = O.route(q, t3, T, C, 3, [p, 1.0, 1.0], scale)
+            flat = O.route(q, t1, T, C, 1, p, scale)
+            np.testing.assert_array_equal(deep.leaves, flat.leaves)
+            wrong = O.route(q, t3, T, C, 3, [1.0, 1.0, p], scale)
+            assert wrong.leaves.size >= deep.leaves.size
+        # a uniform schedule is the scalar route
+        a = O.route(q, t3, T, C, 3, [0.7, 0.7, 0.7], scale)
+        b = O.route(q, t3, T, C, 3, 0.7, scale)
+        np.testing.assert_array_equal(a.leaves, b.leaves)
