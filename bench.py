@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
     ap.add_argument("--no-stats", action="store_true", help="skip the byte-accounting replay")
+    ap.add_argument("--schedules", default="",
+                    help="depth schedules of p also measured (comma list of uniform,root,power)")
+    ap.add_argument("--gamma", type=float, default=1.5, help="exponent of the power schedule")
     ap.add_argument("--n-sweep", default="17,18,19",
                     help="log2 context lengths also timed routed vs dense (comma list, '' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -210,6 +213,48 @@ def bytes_of_step(wl, rec):
             keys += u * wl.C + (t - n1 * wl.C) + sink
     qo = wl.B * wl.Hq * (wl.d * 4 + (wl.d + 1) * 4)
     return route_b, keys * kv_row + qo, keys
+
+
+def schedule_report(run, W, K, pl):
+    """One depth schedule on the run's workload: step time, summary nodes scored
+    and nodes kept per level, K/V bytes attended, dense-mass recall."""
+    zha, wl = run.zha, run.wl
+    run.prefill()
+    run.routed_steps(0, W, pl)
+    ms = timed(lambda: run.routed_steps(W, W + K, pl))
+    run.prefill()
+    run.routed_steps(0, W, pl)
+    recs, keep = [], [zha.LeafList(run.cfg) for _ in range(K)]
+    run.routed_steps(W, W + K, pl, counts=recs, keep=keep)
+    torch.cuda.synchronize()
+    scored = torch.zeros(wl.L, dtype=torch.float64)
+    kept = torch.zeros(wl.L, dtype=torch.float64)
+    rb = ab = 0
+    for rec in recs:
+        r, a, _ = bytes_of_step(wl, rec)
+        rb += r
+        ab += a
+        scored += rec[1].cpu().to(torch.float64).sum(dim=(1, 2))
+        kept += rec[2].cpu().to(torch.float64).sum(dim=(1, 2))
+    recall = []
+    o_r, l_r = torch.empty_like(run.dec.out), torch.empty_like(run.dec.lse)
+    for i, lst in enumerate(keep):
+        s = W + i
+        zha.attend(run.cfg, run.Q[s], run.K, run.V, run.Ts[s], lst.ids, lst.mask, lst.count,
+                   o_r, l_r, run.dec.ws)
+        zha.dense_attend(run.cfg, run.Q[s], run.K, run.V, run.Ts[s], run.dec.out, run.dec.lse,
+                         run.dec.ws)
+        recall.append(torch.exp(l_r - run.dec.lse).flatten())
+    recall = torch.cat(recall).double().cpu()
+    return {
+        "p_levels": [float(x) for x in (pl if isinstance(pl, (list, tuple)) else [pl] * wl.L)],
+        "us_per_step": ms * 1000.0 / K,
+        "nodes_scored_per_group_per_level": [float(x) / (K * wl.B * wl.H_kv) for x in scored],
+        "nodes_kept_per_head_per_level": [float(x) / (K * wl.B * wl.Hq) for x in kept],
+        "summary_MB_per_step": rb / K / 1e6, "kv_MB_per_step": ab / K / 1e6,
+        "mass_recall_mean": float(recall.mean()), "mass_recall_min": float(recall.min()),
+        "note": "levels listed from 1 (leaves) to L",
+    }
 
 
 def cpu_baseline(run, p, s):
@@ -385,6 +430,19 @@ def main():
         "avg_launch_us": attend_us if dominant == "attend" else route_us,
         "algorithmic_bytes_per_launch": (attend_bytes if dominant == "attend" else route_bytes) / K,
     }
+
+    # ---- depth schedules of p (same product p = the headline p for root/power)
+    kinds = [x.strip() for x in args.schedules.split(",") if x.strip()]
+    if kinds:
+        sched = {}
+        for kind in kinds:
+            pl = zha.p_schedule(kind, p, wl.L, gamma=args.gamma)
+            sched[kind] = schedule_report(run, W, K, pl)
+            r = sched[kind]
+            log(f"[bench] schedule {kind}: {r['us_per_step']:.1f} us/step, summaries "
+                f"{r['summary_MB_per_step']:.1f} MB, K/V {r['kv_MB_per_step']:.1f} MB, "
+                f"recall {r['mass_recall_mean']:.3f}")
+        extra["depth_schedules"] = sched
 
     # ---- context-length sweep at the same geometry: routed vs dense
     sweep = {}
