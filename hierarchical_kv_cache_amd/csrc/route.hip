@@ -130,6 +130,7 @@ struct LevelParams {
   int32_t* status;
   int32_t B, H_kv, G, d, R;
   float scale, p;
+  int32_t topk;                // > 0: keep this many nodes per head instead of top-p
   const int64_t* n_built;      // [L][B]: checked against T by the first launch of a route
   int32_t check_stale, L;
 };
@@ -305,6 +306,23 @@ __device__ inline float mass_of(float s, float mx) {
 }
 
 __device__ inline float sanitize(float s) { return isfinite(s) ? s : -FLT_MAX; }
+
+// The weight a candidate carries into the cut: its estimated mass exp(s - max)
+// for top-p, or 1 for a fixed budget of topk nodes (the cut then falls on the
+// topk-th node in order).
+__device__ inline float cut_mass(float s, float mx, int topk) {
+  return topk > 0 ? 1.0f : mass_of(s, mx);
+}
+
+// The running weight at which the cut falls: p W for top-p; for a budget of topk
+// nodes, topk unit weights (2^40 each), or every candidate when fewer.
+__device__ inline double cut_target(float p, int topk, unsigned long long W) {
+  if (topk > 0) {
+    const double k = (double)topk * 1099511627776.0;
+    return k < (double)W ? k : (double)W;
+  }
+  return (double)p * (double)W;
+}
 
 // The value of lane (lane ^ J), J < 64: DPP row operations for J <= 8 (quad
 // permutes; row shifts by 4 selected per lane; row rotate by 8), a swizzle for
@@ -546,12 +564,12 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
   }
   mx = block_max_f<NW>(mx, sm.redf);     // -inf: the head has no candidates
 
-  if (mx == -INFINITY || P.p >= 1.0f) {
+  if (mx == -INFINITY || (P.topk == 0 && P.p >= 1.0f)) {
     // p >= 1 keeps every candidate; no candidates keeps nothing
     int kept = 0;
     for (int j0 = 0; j0 < U; j0 += kCutThreads) {
       const int u = j0 + tid;
-      const bool s1 = P.p >= 1.0f && u < U && (cmask(u) & bit);
+      const bool s1 = mx != -INFINITY && u < U && (cmask(u) & bit);
       const uint64_t b = __ballot(s1);
       if (out && u < U) out[u] = s1 ? 1 : 0;
       const int row = (j0 >> 6) + wave;
@@ -572,13 +590,13 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       if (sv[j] != -INFINITY) {
-        const uint64_t fx = fixmass(mass_of(sv[j], mx));
+        const uint64_t fx = fixmass(cut_mass(sv[j], mx, P.topk));
         wsum += fx;
         atomicAdd(&sm.u.relmass[rel_bucket(sv[j], mx)], (unsigned long long)fx);
       }
     }
     const unsigned long long W = block_sum<NW, unsigned long long>(wsum, sm.redu);
-    const double target = (double)P.p * (double)W;
+    const double target = cut_target(P.p, P.topk, W);
     // bucket b holds the scores just below those of buckets < b: running mass in
     // increasing b; thread t owns buckets 2t and 2t+1
     {
@@ -632,7 +650,7 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
             for (int r = 0; r < NR; ++r) {
               const uint64_t e = v[r];
               unsigned long long mi = 0ull;
-              if ((uint32_t)(e >> 32) != 0u) mi = fixmass(mass_of(key_score((uint32_t)(e >> 32)), mx));
+              if ((uint32_t)(e >> 32) != 0u) mi = fixmass(cut_mass(key_score((uint32_t)(e >> 32)), mx, P.topk));
               const unsigned long long inc = wave_incl_scan<unsigned long long>(mi) + carry;
               const uint64_t reach = __ballot(mi != 0ull && (double)(above_b + inc) >= target);
               if (ic < 0 && reach != 0ull) ic = r * 64 + __ffsll((long long)reach) - 1;
@@ -680,7 +698,7 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
         if (tid < n2) {
           const unsigned long long e = sm.u.sortbuf[tid];
           const uint32_t k = (uint32_t)(e >> 32);
-          if (k != 0u) mi = fixmass(mass_of(key_score(k), mx));
+          if (k != 0u) mi = fixmass(cut_mass(key_score(k), mx, P.topk));
         }
         unsigned long long tot2;
         const unsigned long long pre2 = block_excl_scan<NW, unsigned long long>(mi, sm.redu, &tot2);
@@ -726,7 +744,7 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
       float w = 0.0f;
       if (sv[j] != -INFINITY) {
         k = order_key(sv[j]);
-        w = mass_of(sv[j], mx);
+        w = cut_mass(sv[j], mx, P.topk);
         wsum += fixmass(w);
       }
       if (u < U) { skey[u] = k; sw[u] = w; }
@@ -738,7 +756,7 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
       if (cmask(u) & bit) {
         const float sc1 = sanitize(sc[u]);
         k = order_key(sc1);
-        w = mass_of(sc1, mx);
+        w = cut_mass(sc1, mx, P.topk);
         wsum += fixmass(w);
       }
       skey[u] = k;
@@ -748,7 +766,7 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
   if (bits)
     for (int r = tid; r < nrow; r += kCutThreads) bits[r] = 0ull;
   const unsigned long long W = block_reduce_sum<unsigned long long>(wsum, sm.redu);
-  const double target = (double)P.p * (double)W;
+  const double target = cut_target(P.p, P.topk, W);
 
   // MSD radix select of the threshold key over four 8-bit digits
   uint32_t prefix = 0u, pmask = 0u;
@@ -886,7 +904,7 @@ constexpr int kSmallThreads = 256;
 // head's bit into or_bits[u] of every kept entry and returns the kept count.
 template <int NR>
 __device__ inline int cut_head_wave(const float* sc, const uint32_t* cand_mask, uint32_t bit,
-                                    int U, float p, uint32_t* or_bits, int lane) {
+                                    int U, float p, int topk, uint32_t* or_bits, int lane) {
   uint64_t v[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
@@ -905,16 +923,16 @@ __device__ inline int cut_head_wave(const float* sc, const uint32_t* cand_mask, 
   uint64_t part = 0ull;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    ms[r] = (v[r] != 0ull) ? fixmass(mass_of(key_score((uint32_t)(v[r] >> 32)), mx)) : 0ull;
+    ms[r] = (v[r] != 0ull) ? fixmass(cut_mass(key_score((uint32_t)(v[r] >> 32)), mx, topk)) : 0ull;
     part += ms[r];
     nc += __popcll(__ballot(v[r] != 0ull));
   }
   int ic;
-  if (p >= 1.0f) {
+  if (topk == 0 && p >= 1.0f) {
     ic = (int)nc - 1;
   } else {
     const uint64_t W = wave_sum_u64(part);
-    const double target = (double)p * (double)W;
+    const double target = cut_target(p, topk, W);
     ic = -1;
     uint64_t carry = 0ull;
 #pragma unroll
@@ -953,6 +971,7 @@ struct UpperLevel {
   int32_t* kept;               // [BHq] kept per head (diagnostics)
   int32_t* ucount;             // [BH] candidates per group (diagnostics)
   float p;                     // this level's top-p
+  int32_t topk;                // > 0: this level's node budget instead
 };
 
 struct UpperParams {
@@ -1045,9 +1064,9 @@ __global__ void __launch_bounds__(kSmallThreads) cut_upper(UpperParams U) {
     __syncthreads();
     for (int g = wave; g < B.G; g += NW) {
       int kept;
-      if (cnt <= 64) kept = cut_head_wave<1>(s_sc[g], s_cm, 1u << g, cnt, lv.p, s_or, lane);
-      else if (cnt <= 128) kept = cut_head_wave<2>(s_sc[g], s_cm, 1u << g, cnt, lv.p, s_or, lane);
-      else kept = cut_head_wave<4>(s_sc[g], s_cm, 1u << g, cnt, lv.p, s_or, lane);
+      if (cnt <= 64) kept = cut_head_wave<1>(s_sc[g], s_cm, 1u << g, cnt, lv.p, lv.topk, s_or, lane);
+      else if (cnt <= 128) kept = cut_head_wave<2>(s_sc[g], s_cm, 1u << g, cnt, lv.p, lv.topk, s_or, lane);
+      else kept = cut_head_wave<4>(s_sc[g], s_cm, 1u << g, cnt, lv.p, lv.topk, s_or, lane);
       if (lane == 0) lv.kept[(int64_t)gi * B.G + g] = kept;
     }
     __syncthreads();
@@ -1154,6 +1173,7 @@ static LevelParams level_params(const zha_cfg* cfg, const float* q, const zha_tr
   P.status = (int32_t*)ws;
   P.B = cfg->B; P.H_kv = cfg->H_kv; P.G = cfg->G; P.d = cfg->d; P.R = cfg->R;
   P.scale = cfg->scale; P.p = p;
+  P.topk = 0;
   P.ucount_out = nullptr;
   P.sel = nullptr;
   P.selbits = nullptr;
@@ -1176,7 +1196,7 @@ static LevelParams level_params(const zha_cfg* cfg, const float* q, const zha_tr
 }
 
 static int32_t route_impl(const zha_cfg* cfg, const float* q, const zha_tree* tree,
-                          const int64_t* T, const float* pl, int32_t* leaf_ids,
+                          const int64_t* T, const float* pl, const int32_t* kl, int32_t* leaf_ids,
                           uint32_t* leaf_mask, int32_t* leaf_count, void* ws,
                           size_t ws_bytes, void* stream) {
   int32_t rc = check_route_common(cfg, q, tree, pl, cfg->L);
@@ -1228,12 +1248,14 @@ static int32_t route_impl(const zha_cfg* cfg, const float* q, const zha_tree* tr
       v.kept = (int32_t*)(base + w.kept[l - 1]);
       v.ucount = (int32_t*)(base + w.ucount[l - 1]);
       v.p = pl[l - 1];
+      v.topk = kl ? kl[l - 1] : 0;
     }
     kept_list(lo, U.kids, U.kmask, U.kcount, U.kcap);
     launch_upper(U, s);
   }
   for (int l = lo - 1; l >= 1; --l) {
     LevelParams P = level_params(cfg, q, tree, l, pl[l - 1], ws, w);
+    P.topk = kl ? kl[l - 1] : 0;
     P.list.T = T;
     if (l < L) {   // children of the kept nodes of level l+1, then the parentless nodes
       P.list.pids = (const int32_t*)(base + w.kids[l]);
@@ -1270,15 +1292,30 @@ extern "C" int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree*
   float pl[ZHA_MAX_L];
   const int L = (cfg->L >= 1 && cfg->L <= ZHA_MAX_L) ? cfg->L : 1;
   for (int i = 0; i < L; ++i) pl[i] = p;
-  return zha::route_impl(cfg, q, tree, T, pl, leaf_ids, leaf_mask, leaf_count, ws, ws_bytes,
-                         stream);
+  return zha::route_impl(cfg, q, tree, T, pl, nullptr, leaf_ids, leaf_mask, leaf_count, ws,
+                         ws_bytes, stream);
 }
 
 extern "C" int32_t zha_route_sched(const zha_cfg* cfg, const float* q, const zha_tree* tree,
                                    const int64_t* T, const float* p_levels, int32_t* leaf_ids,
                                    uint32_t* leaf_mask, int32_t* leaf_count, void* ws,
                                    size_t ws_bytes, void* stream) {
-  return zha::route_impl(cfg, q, tree, T, p_levels, leaf_ids, leaf_mask, leaf_count, ws,
+  return zha::route_impl(cfg, q, tree, T, p_levels, nullptr, leaf_ids, leaf_mask, leaf_count,
+                         ws, ws_bytes, stream);
+}
+
+extern "C" int32_t zha_route_topk(const zha_cfg* cfg, const float* q, const zha_tree* tree,
+                                  const int64_t* T, const int32_t* k_levels, int32_t* leaf_ids,
+                                  uint32_t* leaf_mask, int32_t* leaf_count, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  if (cfg == nullptr || k_levels == nullptr) return ZHA_EINVAL;
+  const int L = (cfg->L >= 1 && cfg->L <= ZHA_MAX_L) ? cfg->L : 1;
+  float pl[ZHA_MAX_L];
+  for (int i = 0; i < L; ++i) {
+    if (k_levels[i] < 1) return ZHA_EINVAL;
+    pl[i] = 1.0f;
+  }
+  return zha::route_impl(cfg, q, tree, T, pl, k_levels, leaf_ids, leaf_mask, leaf_count, ws,
                          ws_bytes, stream);
 }
 

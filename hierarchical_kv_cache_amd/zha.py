@@ -24,7 +24,7 @@ F32, BF16 = 0, 1
 OP_BUILD, OP_ROUTE, OP_ATTEND, OP_DENSE, OP_ALL = range(5)
 
 EXPORTS = ["zha_workspace_bytes", "zha_status_str", "zha_build_level", "zha_append",
-           "zha_route", "zha_route_sched", "zha_route_level", "zha_attend", "dense_attend",
+           "zha_route", "zha_route_sched", "zha_route_topk", "zha_route_level", "zha_attend", "dense_attend",
            "zha_route_counts", "zha_ws_status"]
 
 
@@ -65,6 +65,7 @@ def _load() -> ctypes.CDLL:
         "zha_append": (i32, [cfgp, kvp, P, treep, i64, P, sz, P]),
         "zha_route": (i32, [cfgp, P, treep, P, f32, P, P, P, P, sz, P]),
         "zha_route_sched": (i32, [cfgp, P, treep, P, ctypes.POINTER(f32), P, P, P, P, sz, P]),
+        "zha_route_topk": (i32, [cfgp, P, treep, P, ctypes.POINTER(i32), P, P, P, P, sz, P]),
         "zha_route_level": (i32, [cfgp, i32, P, treep, f32, P, P, P, i32, P, P, P, sz, P]),
         "zha_attend": (i32, [cfgp, P, kvp, P, P, P, P, P, P, sz, P]),
         "dense_attend": (i32, [cfgp, P, kvp, P, P, P, sz, P]),
@@ -212,6 +213,18 @@ def route(cfg: Config, q, tree: Tree, T, p, leaf_ids, leaf_mask, leaf_count, ws,
     _check(_lib.zha_route(ctypes.byref(cfg.c()), _ptr(q), ctypes.byref(tree.c()), _ptr(T),
                           float(p), _ptr(leaf_ids), _ptr(leaf_mask), _ptr(leaf_count),
                           _ptr(ws), ws.numel(), _stream(stream)), "zha_route")
+
+
+def route_topk(cfg: Config, q, tree: Tree, T, k, leaf_ids, leaf_mask, leaf_count, ws,
+               stream=None):
+    """Fixed node budget per level: k is one count for every level or cfg.L counts."""
+    ks = list(k) if isinstance(k, (list, tuple)) else [int(k)] * cfg.L
+    if len(ks) != cfg.L:
+        raise ValueError(f"a budget per level needs {cfg.L} values, got {len(ks)}")
+    arr = (ctypes.c_int32 * cfg.L)(*[int(x) for x in ks])
+    _check(_lib.zha_route_topk(ctypes.byref(cfg.c()), _ptr(q), ctypes.byref(tree.c()), _ptr(T),
+                               arr, _ptr(leaf_ids), _ptr(leaf_mask), _ptr(leaf_count), _ptr(ws),
+                               ws.numel(), _stream(stream)), "zha_route_topk")
 
 
 def p_schedule(kind: str, p: float, L: int, gamma: float = 1.0):

@@ -173,6 +173,19 @@ int32_t zha_route_sched(const zha_cfg* cfg, const float* q, const zha_tree* tree
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * zha_route_topk -- zha_route with a fixed node budget per level instead of top-p
+ * (host array k_levels, entry l-1 for level l, each >= 1): each query head keeps
+ * its k_l best candidates of level l in (score desc, id asc) order, or all of
+ * them when fewer.  With L = 1 this is the flat top-K chunk selection that the
+ * tree is compared against ([ZHA] "어떻게 동작하나": a flat indexer scores every
+ * chunk).
+ */
+int32_t zha_route_topk(const zha_cfg* cfg, const float* q, const zha_tree* tree,
+                       const int64_t* T, const int32_t* k_levels,
+                       int32_t* leaf_ids, uint32_t* leaf_mask, int32_t* leaf_count,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
  * zha_route_level -- one level of zha_route on a given candidate list, for tests
  * and custom schedules.  cand_ids/cand_mask/cand_count use the leaf-list layout
  * with capacity cand_cap ([B][H_kv][cand_cap]; ids ascending, bit g = candidate of

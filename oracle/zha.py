@@ -46,7 +46,7 @@ import numpy as np
 __all__ = [
     "logsumexp", "softmax", "attention", "merge", "rope", "n_nodes",
     "node_ref_query", "leaf_summary", "parent_summary", "build_tree",
-    "plane", "node_score", "topp_cut", "route", "routed_keys", "attend_keys",
+    "plane", "node_score", "topp_cut", "topk_cut", "route", "routed_keys", "attend_keys",
     "TopP", "LevelRoute", "Route", "fp32",
 ]
 
@@ -302,8 +302,24 @@ class Route:
         raise KeyError(l)
 
 
+def topk_cut(ids: Sequence[int], scores: Sequence[float], k: int) -> TopP:
+    """The k best candidates in (fp32 score desc, id asc) order, or all of them:
+    the fixed-budget selection of a flat chunk indexer ([ZHA] "어떻게 동작하나").
+    ``target`` holds the budget used, min(k, n)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    s = fp32(np.asarray(scores, dtype=np.float64))
+    n = ids.size
+    if n == 0:
+        e = np.zeros(0)
+        return TopP(ids, s, np.zeros(0, np.int64), e, 0.0, 0.0, 0, np.zeros(0, np.int64))
+    order = np.array(sorted(range(n), key=lambda i: (-s[i], ids[i])), dtype=np.int64)
+    w = np.exp(s - s[order[0]])
+    m = min(int(k), n)
+    return TopP(ids, s, order, w, float(np.sum(w)), float(m), m, np.sort(ids[order[:m]]))
+
+
 def route(q, tree, T: int, C: int, L: int, p, scale: float,
-          level_override=None) -> Route:
+          level_override=None, topk=None) -> Route:
     """Route one query down a tree ([ZHA] "전제와 한계").
 
     Level L candidates are all level-L nodes.  At each level the candidates are
@@ -313,6 +329,7 @@ def route(q, tree, T: int, C: int, L: int, p, scale: float,
     ``p`` is one top-p for every level, or a sequence of L values (entry l-1 for
     level l): a depth schedule, the open question of scaling p with depth that
     the same section raises.
+    ``topk`` (one count, or L counts) replaces top-p by a fixed budget per level.
     ``level_override`` (optional dict level -> selected ids) replaces the cut of
     that level, so a comparison can continue from another implementation's
     allowed choice.
@@ -324,7 +341,10 @@ def route(q, tree, T: int, C: int, L: int, p, scale: float,
     for level in range(L, 0, -1):
         lv = tree[level - 1]
         scores = np.array([node_score(q, lv["khat"][n], lv["bhat"][n], scale) for n in cand])
-        cut = topp_cut(cand, scores, p[level - 1] if np.ndim(p) else p)
+        if topk is not None:
+            cut = topk_cut(cand, scores, topk[level - 1] if np.ndim(topk) else topk)
+        else:
+            cut = topp_cut(cand, scores, p[level - 1] if np.ndim(p) else p)
         if level_override is not None and level in level_override:
             cut.selected = np.sort(np.asarray(level_override[level], np.int64))
             cut.m = cut.selected.size

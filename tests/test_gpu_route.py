@@ -327,3 +327,50 @@ def test_depth_scheduled_p(case, kind):
         assert zha.ws_status(ws) == 0
     for r in report:
         print("allowed:", case, kind, r)
+
+
+def _check_topk_selection(cut_ids, cut_scores, k, gsel):
+    """The GPU's flat top-k set: min(k, n) entries; every kept entry outranks every
+    dropped one in (score desc, id asc) except near-ties (oracle scores within TIE)."""
+    from tests.route_check import TIE
+    ids = np.asarray(cut_ids, np.int64)
+    s = np.asarray(cut_scores, np.float64)
+    keep = set(int(x) for x in gsel)
+    assert len(keep) == min(k, ids.size)
+    kept = [(s[i], ids[i]) for i in range(ids.size) if ids[i] in keep]
+    dropped = [(s[i], ids[i]) for i in range(ids.size) if ids[i] not in keep]
+    if kept and dropped:
+        worst_kept = min(kept, key=lambda t: (t[0], -t[1]))
+        best_dropped = max(dropped, key=lambda t: (t[0], -t[1]))
+        ok = (worst_kept[0] > best_dropped[0]) or (worst_kept[0] == best_dropped[0] and worst_kept[1] < best_dropped[1])
+        assert ok or abs(worst_kept[0] - best_dropped[0]) < TIE, (worst_kept, best_dropped)
+
+
+@pytest.mark.parametrize("case", ["wide20k", "tiny", "gqa_c16", "deep"])
+@pytest.mark.parametrize("frac", [0.1, 0.5])
+def test_fixed_budget_topk(case, frac):
+    """zha_route_topk against the oracle's fixed-budget route: a budget of
+    frac * n_l nodes per level (at least one)."""
+    wl, T = CASES[case]
+    cfg, K, V, trees = _setup(wl, T)
+    tree = upload(cfg, trees, T)
+    ws = zha.new_workspace(cfg)
+    Tt = torch.full((cfg.B,), T, dtype=torch.int64, device=DEV)
+    ks = [max(1, int(frac * (T // cfg.C ** l))) for l in range(1, cfg.L + 1)]
+    for step in range(2):
+        q = synth.make_query(wl, step, T, "cpu").to(DEV)
+        lst = zha.LeafList(cfg, DEV)
+        zha.route_topk(cfg, q, tree, Tt, ks, lst.ids, lst.mask, lst.count, ws)
+        torch.cuda.synchronize()
+        assert zha.ws_status(ws) == 0
+        full = sets_from_lists(lst.ids, lst.mask, lst.count, cfg.G)
+        qh = f64(q)
+        for b in range(cfg.B):
+            for j in range(cfg.Hq):
+                rt = O.route(qh[b, j], trees[b][j // cfg.G], T, cfg.C, cfg.L, 1.0, cfg.scale,
+                             topk=ks)
+                if cfg.L == 1:
+                    lv = rt.level(1)
+                    _check_topk_selection(lv.cut.ids, lv.cut.scores, ks[0], full[b][j])
+                else:
+                    np.testing.assert_array_equal(full[b][j], rt.leaves)

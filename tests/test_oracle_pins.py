@@ -417,3 +417,38 @@ def test_depth_schedule_indexing_reduces_to_flat_route():
         a = O.route(q, t3, T, C, 3, [0.7, 0.7, 0.7], scale)
         b = O.route(q, t3, T, C, 3, 0.7, scale)
         np.testing.assert_array_equal(a.leaves, b.leaves)
+
+
+def test_topk_cut_definition_and_ties():
+    """Every kept candidate outranks every dropped one in (score desc, id asc);
+    exactly min(k, n) are kept; equal scores keep the lower ids."""
+    rng = np.random.default_rng(9)
+    for n in (1, 5, 12, 40):
+        ids = rng.permutation(100)[:n]
+        sc = np.round(rng.standard_normal(n), 1)          # many ties
+        for k in (1, 3, 12, 50):
+            cut = O.topk_cut(ids, sc, k)
+            assert cut.m == min(k, n) == cut.selected.size
+            keep = set(cut.selected.tolist())
+            s32 = O.fp32(sc)
+            for i in range(n):
+                for j in range(n):
+                    if ids[i] in keep and ids[j] not in keep:
+                        assert (s32[i] > s32[j]) or (s32[i] == s32[j] and ids[i] < ids[j])
+    tie = O.topk_cut(np.array([7, 3, 9, 1]), np.zeros(4), 2)
+    assert tie.selected.tolist() == [1, 3]
+
+
+def test_flat_topk_route_is_the_leaf_topk():
+    rng = np.random.default_rng(10)
+    C, d, R, T = 8, 16, 3, 8 * 60 + 3
+    K = rng.standard_normal((T, d))
+    qref = rng.standard_normal((R, d)) / np.sqrt(d)
+    scale = 1 / np.sqrt(d)
+    t1 = O.build_tree(K, qref, T, C, 1, scale)
+    q = rng.standard_normal(d)
+    n1 = T // C
+    scores = [O.node_score(q, t1[0]["khat"][n], t1[0]["bhat"][n], scale) for n in range(n1)]
+    for k in (1, 7, 60, 100):
+        r = O.route(q, t1, T, C, 1, 0.5, scale, topk=k)
+        np.testing.assert_array_equal(r.leaves, O.topk_cut(np.arange(n1), scores, k).selected)
