@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--schedules", default="",
                     help="depth schedules of p also measured (comma list of uniform,root,power)")
     ap.add_argument("--gamma", type=float, default=1.5, help="exponent of the power schedule")
+    ap.add_argument("--flat", action="store_true",
+                    help="also measure flat (one-level) top-p and top-K routing over all leaves")
     ap.add_argument("--n-sweep", default="17,18,19",
                     help="log2 context lengths also timed routed vs dense (comma list, '' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -126,9 +128,10 @@ class Run:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
-    def routed_steps(self, s0, s1, p, ev=None, counts=None, keep=None):
+    def routed_steps(self, s0, s1, p, ev=None, counts=None, keep=None, router=None):
         """Steps s0..s1-1.  ev: dict collecting (route, attend, append) event pairs;
-        keep: one LeafList per step, to hold each step's routed list."""
+        keep: one LeafList per step, to hold each step's routed list; router:
+        replaces the tree route (called with q, T and the step's leaf list)."""
         zha, dec, C = self.zha, self.dec, self.wl.C
         for s in range(s0, s1):
             T = self.Ts[s]
@@ -146,7 +149,10 @@ class Run:
             if ev is not None:
                 r0 = torch.cuda.Event(enable_timing=True)
                 r0.record()
-            zha.route(self.cfg, q, dec.tree, T, p, lst.ids, lst.mask, lst.count, dec.ws)
+            if router is not None:
+                router(q, T, lst)
+            else:
+                zha.route(self.cfg, q, dec.tree, T, p, lst.ids, lst.mask, lst.count, dec.ws)
             if ev is not None:
                 r1 = torch.cuda.Event(enable_timing=True)
                 r1.record()
@@ -255,6 +261,53 @@ def schedule_report(run, W, K, pl):
         "mass_recall_mean": float(recall.mean()), "mass_recall_min": float(recall.min()),
         "note": "levels listed from 1 (leaves) to L",
     }
+
+
+def flat_report(run, W, K, mode, p, budget):
+    """Flat routing over every leaf (a one-level view of the same leaf summaries):
+    top-p at p, or a fixed budget of leaves per head.  Step time, route time,
+    leaves kept and dense-mass recall over the same steps."""
+    zha, wl = run.zha, run.wl
+    cfg1 = zha.Config(B=wl.B, H_kv=wl.H_kv, G=wl.G, d=wl.d, C=wl.C, L=1, R=wl.R,
+                      T_cap=run.T_cap, kv_dtype=run.cfg.kv_dtype, rope=wl.rope,
+                      rope_base=wl.rope_base)
+    tree1 = zha.Tree.lower_levels(run.dec.tree, cfg1)
+    ws1 = zha.new_workspace(cfg1)
+
+    def router(q, T, lst):
+        if mode == "topk":
+            zha.route_topk(cfg1, q, tree1, T, budget, lst.ids, lst.mask, lst.count, ws1)
+        else:
+            zha.route(cfg1, q, tree1, T, p, lst.ids, lst.mask, lst.count, ws1)
+
+    run.prefill()
+    run.routed_steps(0, W, p, router=router)
+    ms = timed(lambda: run.routed_steps(W, W + K, p, router=router))
+    run.prefill()
+    run.routed_steps(0, W, p, router=router)
+    ev = {"route": [], "attend": [], "append": []}
+    keep = [zha.LeafList(run.cfg) for _ in range(K)]
+    run.routed_steps(W, W + K, p, ev, keep=keep, router=router)
+    torch.cuda.synchronize()
+    if zha.ws_status(ws1) != 0:
+        raise RuntimeError("flat route reported a device error")
+    route_us = 1000 * sum(a.elapsed_time(b) for a, b in ev["route"]) / K
+    leaves = sum(float(lst.count.sum()) for lst in keep) / (K * wl.B * wl.H_kv)
+    recall = []
+    o_r, l_r = torch.empty_like(run.dec.out), torch.empty_like(run.dec.lse)
+    for i, lst in enumerate(keep):
+        s = W + i
+        zha.attend(run.cfg, run.Q[s], run.K, run.V, run.Ts[s], lst.ids, lst.mask, lst.count,
+                   o_r, l_r, run.dec.ws)
+        zha.dense_attend(run.cfg, run.Q[s], run.K, run.V, run.Ts[s], run.dec.out, run.dec.lse,
+                         run.dec.ws)
+        recall.append(torch.exp(l_r - run.dec.lse).flatten())
+    recall = torch.cat(recall).double().cpu()
+    return {"us_per_step": ms * 1000.0 / K, "route_us": route_us,
+            "summary_MB_per_step": wl.B * wl.H_kv * (wl.T0 + W + K // 2) // wl.C * wl.R * (wl.d + 1) * 4 / 1e6,
+            "leaves_per_group": leaves,
+            "mass_recall_mean": float(recall.mean()), "mass_recall_min": float(recall.min()),
+            "budget_leaves_per_head": budget if mode == "topk" else None}
 
 
 def cpu_baseline(run, p, s):
@@ -444,6 +497,17 @@ def main():
                 f"recall {r['mass_recall_mean']:.3f}")
         extra["depth_schedules"] = sched
 
+    # ---- flat routing over every leaf: top-p, and top-K at the tree's leaf budget
+    if args.flat:
+        budget = max(1, int(round(extra.get("kept_per_head_per_level", [64])[0])))
+        flat = {}
+        for mode in ("topp", "topk"):
+            flat[mode] = flat_report(run, W, K, mode, p, budget)
+            r = flat[mode]
+            log(f"[bench] flat {mode}: {r['us_per_step']:.1f} us/step (route {r['route_us']:.1f}), "
+                f"recall {r['mass_recall_mean']:.3f}, leaves/group {r['leaves_per_group']:.0f}")
+        extra["flat_comparator"] = flat
+
     # ---- context-length sweep at the same geometry: routed vs dense
     sweep = {}
     for e in [int(x) for x in args.n_sweep.split(",") if x.strip()]:
@@ -463,6 +527,19 @@ def main():
         sweep[str(wls.T0)] = {"routed_us_per_step": ms_r * 1000.0 / Ks,
                               "dense_us_per_step": ms_d * 1000.0 / Ks,
                               "speedup_vs_dense": ms_d / ms_r}
+        if args.flat:
+            rs.prefill()
+            rs.routed_steps(0, Ws, p)
+            recs_s = []
+            rs.routed_steps(Ws, Ws + Ks, p, counts=recs_s)
+            kept1 = sum(float(r[2][0].sum()) for r in recs_s) / (Ks * wls.B * wls.Hq)
+            budget_s = max(1, int(round(kept1)))
+            sweep[str(wls.T0)]["flat_topp"] = flat_report(rs, Ws, Ks, "topp", p, budget_s)
+            sweep[str(wls.T0)]["flat_topk"] = flat_report(rs, Ws, Ks, "topk", p, budget_s)
+            rs.prefill()
+            rs.routed_steps(0, Ws, 0.75)
+            ms_75 = timed(lambda: rs.routed_steps(Ws, Ws + Ks, 0.75))
+            sweep[str(wls.T0)]["routed_p0.75_us_per_step"] = ms_75 * 1000.0 / Ks
         log(f"[bench] T={wls.T0}: routed {ms_r * 1000 / Ks:.1f} us/step, dense {ms_d * 1000 / Ks:.1f}")
         del rs
         torch.cuda.empty_cache()
@@ -470,6 +547,11 @@ def main():
         sweep[str(wl.T0)] = {"routed_us_per_step": us_step,
                              "dense_us_per_step": dense["us_per_step"] if dense else None,
                              "speedup_vs_dense": (dense["us_per_step"] / us_step) if dense else None}
+        if args.flat:
+            sweep[str(wl.T0)]["flat_topp"] = extra["flat_comparator"]["topp"]
+            sweep[str(wl.T0)]["flat_topk"] = extra["flat_comparator"]["topk"]
+            if "p0.75" in extra:
+                sweep[str(wl.T0)]["routed_p0.75_us_per_step"] = extra["p0.75"]["us_per_step"]
         extra["context_sweep"] = sweep
 
     cpu = None

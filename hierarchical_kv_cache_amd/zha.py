@@ -165,6 +165,19 @@ class Tree:
             self.bhat.append(torch.zeros(cfg.B, cfg.H_kv, n, cfg.R, dtype=torch.float32, device=device))
         self.n_built = torch.zeros(cfg.L, cfg.B, dtype=torch.int64, device=device)
 
+    @classmethod
+    def lower_levels(cls, tree: "Tree", cfg: "Config") -> "Tree":
+        """The lowest cfg.L levels of an existing tree, shared (no copy): for
+        example its leaf level alone, as a one-level tree."""
+        if cfg.L > tree.cfg.L:
+            raise ValueError("the view has more levels than the tree")
+        t = cls.__new__(cls)
+        t.cfg = cfg
+        t.khat = tree.khat[:cfg.L]
+        t.bhat = tree.bhat[:cfg.L]
+        t.n_built = tree.n_built[:cfg.L]
+        return t
+
     def c(self) -> _Tree:
         t = _Tree()
         for i in range(self.cfg.L):
