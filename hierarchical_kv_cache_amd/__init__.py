@@ -6,7 +6,7 @@ first use so that ``python -m hierarchical_kv_cache_amd.buildlib`` can rebuild t
 library; using any of them without a built library raises ImportError.
 """
 _API = ("Config", "Decoder", "LeafList", "Tree", "ZhaError", "append", "attend", "build",
-        "build_level", "dense_attend", "new_workspace", "p_schedule", "route", "route_level", "route_topk",
+        "build_level", "dense_attend", "new_workspace", "p_schedule", "route", "route_level", "route_quality", "route_topk",
         "route_counts", "workspace_bytes", "ws_status")
 
 __all__ = list(_API) + ["zha"]

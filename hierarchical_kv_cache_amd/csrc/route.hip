@@ -1099,6 +1099,150 @@ __global__ void __launch_bounds__(kSmallThreads) cut_upper(UpperParams U) {
   }
 }
 
+// ---------------------------------------------------------------- quality forward
+//
+// [ZHA] "어떻게 쓰나": the reference queries are fit so that the estimated node
+// distribution follows the true one.  Per level and query head this computes
+// KL(p || p_hat) over the level's complete nodes, p = softmax_n F_n(q) with F_n
+// the exact log-mass of the node's keys, p_hat = softmax_n of the routing score.
+// F of the leaves comes from the keys (leaf_logmass), F of a parent is the LSE of
+// its children's F (parent_logmass), the scores from score_nodes over every node.
+
+struct QualityParams {
+  const float* q;              // [BHq][d]
+  const void* K;               // [BH][T_cap][d]
+  const int64_t* T;            // [B]
+  int64_t T_cap;
+  float* F;                    // [BHq][cap] this level's log-mass
+  const float* Fc;             // [BHq][ccap] the level below (parent_logmass)
+  int64_t cap, ccap;
+  int64_t span;                // C^level
+  int32_t B, H_kv, G, C, kv_dtype;
+  float scale;
+};
+
+__device__ inline int64_t clamp_T(const int64_t* Tp, int b, int64_t T_cap) {
+  int64_t T = Tp[b];
+  if (T < 0) T = 0;
+  return T > T_cap ? T_cap : T;
+}
+
+// 256 threads per block of 64 keys: thread t takes key t / 4 of the block and a
+// quarter of its dims; the quarter dots are summed across the four threads, the
+// block's scores staged in LDS, and each (head, leaf) takes the LSE of its C.
+template <int D>
+__global__ void __launch_bounds__(256) leaf_logmass(QualityParams P) {
+  constexpr int DQ = D / 4;
+  __shared__ float qs[ZHA_MAX_G][D];
+  __shared__ float z[ZHA_MAX_G][64];
+  const int gi = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t T = clamp_T(P.T, gi / P.H_kv, P.T_cap);
+  const int64_t n1 = T / P.C;
+  const int64_t nblk = (n1 * P.C + 63) / 64;
+  for (int i = tid; i < P.G * D; i += 256)
+    qs[i / D][i % D] = P.q[((int64_t)gi * P.G + i / D) * D + i % D] * P.scale;
+  __syncthreads();
+  const int kk = tid >> 2, qt = tid & 3;
+  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int64_t key = blk * 64 + kk;
+    const bool ok = key < n1 * P.C;
+    float kv[DQ];
+    const int64_t row = ((int64_t)gi * P.T_cap + (ok ? key : 0)) * D + qt * DQ;
+    if (P.kv_dtype == ZHA_BF16) {
+      const uint16_t* kp = (const uint16_t*)P.K + row;
+#pragma unroll
+      for (int j = 0; j < DQ; ++j) kv[j] = __uint_as_float((uint32_t)kp[j] << 16);
+    } else {
+      const float* kp = (const float*)P.K + row;
+#pragma unroll
+      for (int j = 0; j < DQ; ++j) kv[j] = kp[j];
+    }
+    for (int g = 0; g < P.G; ++g) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < DQ; ++j) acc = fmaf(qs[g][qt * DQ + j], kv[j], acc);
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      if (qt == 0) z[g][kk] = ok ? acc : -INFINITY;
+    }
+    __syncthreads();
+    const int per = 64 / P.C;                      // leaves in the block
+    for (int i = tid; i < per * P.G; i += 256) {
+      const int g = i / per, lf = i % per;
+      const int64_t leaf = blk * per + lf;
+      if (leaf < n1) {
+        float m = -INFINITY;
+        for (int j = 0; j < P.C; ++j) m = fmaxf(m, z[g][lf * P.C + j]);
+        float sum = 0.0f;
+        for (int j = 0; j < P.C; ++j) sum += expf(z[g][lf * P.C + j] - m);
+        P.F[((int64_t)gi * P.G + g) * P.cap + leaf] = m + logf(sum);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(256) parent_logmass(QualityParams P) {
+  const int head = blockIdx.y;
+  const int gi = head / P.G;
+  const int64_t T = clamp_T(P.T, gi / P.H_kv, P.T_cap);
+  const int64_t n = T / P.span;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float* fc = P.Fc + (int64_t)head * P.ccap + i * P.C;
+    float m = -INFINITY;
+    for (int c = 0; c < P.C; ++c) m = fmaxf(m, fc[c]);
+    float sum = 0.0f;
+    for (int c = 0; c < P.C; ++c) sum += expf(fc[c] - m);
+    P.F[(int64_t)head * P.cap + i] = m + logf(sum);
+  }
+}
+
+// KL(softmax F || softmax s) over the level's n nodes, one workgroup per head.
+__global__ void __launch_bounds__(1024) level_kl(QualityParams P, const float* S, float* kl) {
+  constexpr int NW = 1024 / kWave;
+  __shared__ float red[NW];
+  const int head = blockIdx.x;
+  const int gi = head / P.G;
+  const int64_t T = clamp_T(P.T, gi / P.H_kv, P.T_cap);
+  const int64_t n = T / P.span;
+  const float* f = P.F + (int64_t)head * P.cap;
+  const float* s = S + (int64_t)head * P.cap;
+  if (n == 0) {
+    if (threadIdx.x == 0) kl[head] = NAN;
+    return;
+  }
+  float mf = -INFINITY, ms = -INFINITY;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) { mf = fmaxf(mf, f[i]); ms = fmaxf(ms, s[i]); }
+  mf = block_max_f<NW>(mf, red);
+  ms = block_max_f<NW>(ms, red);
+  float zf = 0.0f, zs = 0.0f, e = 0.0f;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) {
+    const float wf = expf(f[i] - mf);
+    zf += wf;
+    zs += expf(s[i] - ms);
+    e += wf * (f[i] - s[i]);
+  }
+  // fixed-order block sums (no atomics): deterministic
+  auto bsum = [&](float v) {
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += red[w];
+    __syncthreads();
+    return t;
+  };
+  zf = bsum(zf);
+  zs = bsum(zs);
+  e = bsum(e);
+  if (threadIdx.x == 0) {
+    const float lse_f = mf + logf(zf), lse_s = ms + logf(zs);
+    kl[head] = e / zf - lse_f + lse_s;
+  }
+}
+
 // ---------------------------------------------------------------- host
 
 static void launch_score(const LevelParams& P, int64_t ucap, hipStream_t s) {
@@ -1365,4 +1509,54 @@ extern "C" int32_t zha_route_counts(const zha_cfg* cfg, const void* ws, int32_t*
       return ZHA_EHIP;
   }
   return ZHA_OK;
+}
+
+extern "C" int32_t zha_route_quality(const zha_cfg* cfg, const float* q, const zha_kv* kv,
+                                     const zha_tree* tree, float* kl, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  using namespace zha;
+  const float one = 1.0f;
+  int32_t rc = check_route_common(cfg, q, tree, &one, 1);
+  if (rc != ZHA_OK) return rc;
+  if (kv == nullptr || kv->K == nullptr || kv->T == nullptr || kl == nullptr) return ZHA_EINVAL;
+  rc = zha_check_ws(cfg, ZHA_OP_ROUTE, ws, ws_bytes);
+  if (rc != ZHA_OK) return rc;
+  const WsLayout w = ws_layout(*cfg);
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  const int BH = cfg->B * cfg->H_kv, BHq = BH * cfg->G, L = cfg->L;
+  QualityParams Q;
+  Q.q = q; Q.K = kv->K; Q.T = kv->T; Q.T_cap = cfg->T_cap;
+  Q.B = cfg->B; Q.H_kv = cfg->H_kv; Q.G = cfg->G; Q.C = cfg->C; Q.kv_dtype = cfg->kv_dtype;
+  Q.scale = cfg->scale;
+  int64_t span = 1;
+  for (int l = 1; l <= L; ++l) {
+    span *= cfg->C;
+    Q.F = (float*)(base + w.logmass[l - 1]);
+    Q.cap = w.cap[l - 1];
+    Q.span = span;
+    if (l == 1) {
+      int64_t gx = ceil_div(cfg->T_cap, 64);
+      if (gx > 1024) gx = 1024;
+      if (gx < 1) gx = 1;
+      if (cfg->d == 128) hipLaunchKernelGGL(leaf_logmass<128>, dim3((unsigned)gx, (unsigned)BH), dim3(256), 0, s, Q);
+      else hipLaunchKernelGGL(leaf_logmass<64>, dim3((unsigned)gx, (unsigned)BH), dim3(256), 0, s, Q);
+    } else {
+      Q.Fc = (const float*)(base + w.logmass[l - 2]);
+      Q.ccap = w.cap[l - 2];
+      int64_t gx = ceil_div(w.cap[l - 1], 256);
+      if (gx < 1) gx = 1;
+      if (gx > 64) gx = 64;
+      hipLaunchKernelGGL(parent_logmass, dim3((unsigned)gx, (unsigned)BHq), dim3(256), 0, s, Q);
+    }
+    // the routing score of every node of the level (an implicit list of them all)
+    LevelParams P = level_params(cfg, q, tree, l, 1.0f, ws, w);
+    P.list.T = kv->T;
+    P.ucap = w.cap[l - 1];
+    P.scores = (float*)(base + w.scores[l - 1]);
+    launch_score(P, P.ucap, s);
+    hipLaunchKernelGGL(level_kl, dim3(BHq), dim3(1024), 0, s, Q, (const float*)P.scores,
+                       kl + (size_t)(l - 1) * BHq);
+  }
+  return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
 }

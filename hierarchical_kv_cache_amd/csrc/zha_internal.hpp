@@ -27,6 +27,7 @@ struct WsLayout {
   size_t kids[ZHA_MAX_L], kmask[ZHA_MAX_L], kcount[ZHA_MAX_L];  // kept list per level
   size_t ucount[ZHA_MAX_L];  // candidate list length per level and group (diagnostics)
   size_t scores[ZHA_MAX_L], sel[ZHA_MAX_L], kept[ZHA_MAX_L];
+  size_t logmass[ZHA_MAX_L];  // per head: true node log-mass (quality forward)
   size_t selbits[ZHA_MAX_L];  // per head: kept bits of the union list, 64 entries a word
   int64_t nwcap[ZHA_MAX_L];
   int64_t cap[ZHA_MAX_L];
@@ -73,6 +74,7 @@ inline WsLayout ws_layout(const zha_cfg& c) {
     w.kcount[l - 1] = off; off = align_up(off + (size_t)BH * 4, 256);
     w.ucount[l - 1] = off; off = align_up(off + (size_t)BH * 4, 256);
     w.scores[l - 1] = off; off = align_up(off + (size_t)BHq * cap * 4, 256);
+    w.logmass[l - 1] = off; off = align_up(off + (size_t)BHq * cap * 4, 256);
     w.sel[l - 1] = off;    off = align_up(off + (size_t)BHq * cap, 256);
     w.kept[l - 1] = off;   off = align_up(off + (size_t)BHq * 4, 256);
     w.nwcap[l - 1] = (cap + 63) / 64;

@@ -24,7 +24,7 @@ F32, BF16 = 0, 1
 OP_BUILD, OP_ROUTE, OP_ATTEND, OP_DENSE, OP_ALL = range(5)
 
 EXPORTS = ["zha_workspace_bytes", "zha_status_str", "zha_build_level", "zha_append",
-           "zha_route", "zha_route_sched", "zha_route_topk", "zha_route_level", "zha_attend", "dense_attend",
+           "zha_route", "zha_route_sched", "zha_route_topk", "zha_route_quality", "zha_route_level", "zha_attend", "dense_attend",
            "zha_route_counts", "zha_ws_status"]
 
 
@@ -66,6 +66,7 @@ def _load() -> ctypes.CDLL:
         "zha_route": (i32, [cfgp, P, treep, P, f32, P, P, P, P, sz, P]),
         "zha_route_sched": (i32, [cfgp, P, treep, P, ctypes.POINTER(f32), P, P, P, P, sz, P]),
         "zha_route_topk": (i32, [cfgp, P, treep, P, ctypes.POINTER(i32), P, P, P, P, sz, P]),
+        "zha_route_quality": (i32, [cfgp, P, kvp, treep, P, P, sz, P]),
         "zha_route_level": (i32, [cfgp, i32, P, treep, f32, P, P, P, i32, P, P, P, sz, P]),
         "zha_attend": (i32, [cfgp, P, kvp, P, P, P, P, P, P, sz, P]),
         "dense_attend": (i32, [cfgp, P, kvp, P, P, P, sz, P]),
@@ -238,6 +239,13 @@ def route_topk(cfg: Config, q, tree: Tree, T, k, leaf_ids, leaf_mask, leaf_count
     _check(_lib.zha_route_topk(ctypes.byref(cfg.c()), _ptr(q), ctypes.byref(tree.c()), _ptr(T),
                                arr, _ptr(leaf_ids), _ptr(leaf_mask), _ptr(leaf_count), _ptr(ws),
                                ws.numel(), _stream(stream)), "zha_route_topk")
+
+
+def route_quality(cfg: Config, q, K, V, T, tree: Tree, kl, ws, stream=None):
+    """Per-level KL(p || p_hat) of the routing estimate: kl is [L][B][Hq] fp32."""
+    _check(_lib.zha_route_quality(ctypes.byref(cfg.c()), _ptr(q), ctypes.byref(_kv(K, V, T)),
+                                  ctypes.byref(tree.c()), _ptr(kl), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "zha_route_quality")
 
 
 def p_schedule(kind: str, p: float, L: int, gamma: float = 1.0):

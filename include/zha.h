@@ -186,6 +186,20 @@ int32_t zha_route_topk(const zha_cfg* cfg, const float* q, const zha_tree* tree,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * zha_route_quality -- routing quality per level ([ZHA] "어떻게 쓰나": the
+ * reference queries are fit so the estimated node distribution follows the true
+ * one).  For each level l and query head j, over the level's complete nodes n:
+ * kl[(l-1)][b][j] = KL(p || p_hat), p = softmax_n F_n(q_j), F_n the exact
+ * log-mass LSE over the node's keys of scale q.k, and p_hat = softmax_n of the
+ * routing score max_r (scale q.k_hat_{r,n} + b_hat_{r,n}).  kl is [L][B][Hq] fp32
+ * (NaN for a level with no complete node).  Reads every key: a diagnostic, not
+ * part of a decode step.  Uses the route workspace.
+ */
+int32_t zha_route_quality(const zha_cfg* cfg, const float* q, const zha_kv* kv,
+                          const zha_tree* tree, float* kl,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
  * zha_route_level -- one level of zha_route on a given candidate list, for tests
  * and custom schedules.  cand_ids/cand_mask/cand_count use the leaf-list layout
  * with capacity cand_cap ([B][H_kv][cand_cap]; ids ascending, bit g = candidate of

@@ -47,7 +47,7 @@ __all__ = [
     "logsumexp", "softmax", "attention", "merge", "rope", "n_nodes",
     "node_ref_query", "leaf_summary", "parent_summary", "build_tree",
     "plane", "node_score", "topp_cut", "topk_cut", "route", "routed_keys", "attend_keys",
-    "TopP", "LevelRoute", "Route", "fp32",
+    "TopP", "LevelRoute", "Route", "fp32", "node_logmass", "level_kl",
 ]
 
 
@@ -372,3 +372,42 @@ def attend_keys(q, K, V, keys, scale: float):
     """Exact softmax attention of q over the listed cache rows."""
     keys = np.asarray(keys, dtype=np.int64)
     return attention(q, np.asarray(K)[keys], np.asarray(V)[keys], scale)
+
+
+def node_logmass(q, K, T: int, C: int, L: int, scale: float):
+    """True log-mass of every complete node for one query, per level (list index
+    level-1): F_n(q) = LSE over the node's keys of scale * q.k ([ZHA] "무엇과 다른가":
+    the chunk log-mass the tangent planes estimate).  A node's keys are the union
+    of its children's, so each level's F is the LSE of its children's F."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    out = []
+    n1 = n_nodes(T, C, 1)
+    z = scale * (K[: n1 * C] @ q)
+    f = np.array([logsumexp(z[n * C:(n + 1) * C]) for n in range(n1)])
+    out.append(f)
+    for level in range(2, L + 1):
+        n = n_nodes(T, C, level)
+        f = np.array([logsumexp(out[-1][c * C:(c + 1) * C]) for c in range(n)])
+        out.append(f)
+    return out
+
+
+def level_kl(q, K, tree, T: int, C: int, L: int, scale: float):
+    """Routing quality per level ([ZHA] "어떻게 쓰나": the reference queries are fit
+    so the estimated node distribution matches the true one): KL(p || p_hat) over
+    the complete nodes of each level, p = softmax_n F_n(q), p_hat = softmax_n of
+    the routing score max_r t_r(q).  Levels with no node give nan."""
+    F = node_logmass(q, K, T, C, L, scale)
+    out = []
+    for level in range(1, L + 1):
+        f = F[level - 1]
+        if f.size == 0:
+            out.append(float("nan"))
+            continue
+        lv = tree[level - 1]
+        s = np.array([node_score(q, lv["khat"][n], lv["bhat"][n], scale) for n in range(f.size)])
+        lp = f - logsumexp(f)
+        lph = s - logsumexp(s)
+        out.append(float(np.sum(np.exp(lp) * (lp - lph))))
+    return out

@@ -374,3 +374,30 @@ def test_fixed_budget_topk(case, frac):
                     _check_topk_selection(lv.cut.ids, lv.cut.scores, ks[0], full[b][j])
                 else:
                     np.testing.assert_array_equal(full[b][j], rt.leaves)
+
+
+@pytest.mark.parametrize("case", ["tiny", "gqa_c16", "deep", "rope"])
+def test_route_quality_kl_per_level(case):
+    """zha_route_quality against the oracle's per-level KL on the oracle's tree."""
+    wl, T = CASES[case]
+    cfg, K, V, trees = _setup(wl, T)
+    tree = upload(cfg, trees, T)
+    ws = zha.new_workspace(cfg)
+    Tt = torch.full((cfg.B,), T, dtype=torch.int64, device=DEV)
+    Kd, Vd = K.to(DEV), V.to(DEV)
+    q = synth.make_query(wl, 0, T, "cpu").to(DEV)
+    kl = torch.full((cfg.L, cfg.B, cfg.Hq), -1.0, device=DEV)
+    zha.route_quality(cfg, q, Kd, Vd, Tt, tree, kl, ws)
+    torch.cuda.synchronize()
+    assert zha.ws_status(ws) == 0
+    klh = kl.cpu().numpy()
+    qh = f64(q)
+    for b in range(cfg.B):
+        for j in range(cfg.Hq):
+            ref = O.level_kl(qh[b, j], f64(K[b, j // cfg.G, :T]), trees[b][j // cfg.G], T, cfg.C,
+                             cfg.L, cfg.scale)
+            for l in range(cfg.L):
+                if np.isnan(ref[l]):
+                    assert np.isnan(klh[l, b, j])
+                else:
+                    assert abs(klh[l, b, j] - ref[l]) <= 5e-4 + 2e-3 * abs(ref[l]), (l, b, j, klh[l, b, j], ref[l])

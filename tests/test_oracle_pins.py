@@ -452,3 +452,49 @@ def test_flat_topk_route_is_the_leaf_topk():
     for k in (1, 7, 60, 100):
         r = O.route(q, t1, T, C, 1, 0.5, scale, topk=k)
         np.testing.assert_array_equal(r.leaves, O.topk_cut(np.arange(n1), scores, k).selected)
+
+
+def test_level_kl_zero_for_constant_chunks_and_positive_otherwise():
+    """Closed form: when every key of a leaf is the same vector k, F_n = scale q.k +
+    log C and every tangent plane of the leaf is exactly that (k_hat = k, b_hat =
+    log C), so the leaf-level KL is 0.  Distinct keys make the estimate a strict
+    lower bound somewhere: KL > 0 at every level."""
+    rng = np.random.default_rng(12)
+    C, d, R, L = 4, 8, 2, 3
+    n1 = 4 ** 2 * 3
+    T = n1 * C
+    base = rng.standard_normal((n1, d))
+    K_const = np.repeat(base, C, axis=0)
+    qref = rng.standard_normal((R, d)) / np.sqrt(d)
+    scale = 1 / np.sqrt(d)
+    tree = O.build_tree(K_const, qref, T, C, L, scale)
+    q = rng.standard_normal(d)
+    kl = O.level_kl(q, K_const, tree, T, C, 1, scale)
+    assert abs(kl[0]) < 1e-12
+    K = K_const + 0.5 * rng.standard_normal(K_const.shape)
+    tree = O.build_tree(K, qref, T, C, L, scale)
+    kl = O.level_kl(q, K, tree, T, C, L, scale)
+    assert all(x > 1e-6 for x in kl)
+
+
+def test_level_kl_matches_brute_force_definition():
+    rng = np.random.default_rng(13)
+    C, d, R, L = 4, 8, 3, 2
+    T = 4 * 4 * 5 + 3
+    K = rng.standard_normal((T, d))
+    qref = rng.standard_normal((R, d)) / np.sqrt(d)
+    scale = 1 / np.sqrt(d)
+    tree = O.build_tree(K, qref, T, C, L, scale)
+    q = rng.standard_normal(d)
+    kl = O.level_kl(q, K, tree, T, C, L, scale)
+    z = scale * (K @ q)
+    for level in (1, 2):
+        span = C ** level
+        n = T // span
+        # true mass of each node straight from the keys, estimated from the planes
+        P = np.array([np.exp(z[i * span:(i + 1) * span]).sum() for i in range(n)])
+        P /= P.sum()
+        lv = tree[level - 1]
+        S = np.array([max(scale * lv["khat"][i][r] @ q + lv["bhat"][i][r] for r in range(R)) for i in range(n)])
+        Ph = np.exp(S) / np.exp(S).sum()
+        assert abs(kl[level - 1] - float(np.sum(P * np.log(P / Ph)))) < 1e-10
