@@ -446,10 +446,22 @@ def main():
             oerr.append((num / run.dec.out.abs().amax(dim=-1).clamp_min(1e-30)).flatten())
         recall = torch.cat(recall).double().cpu()
         oerr = torch.cat(oerr).double().cpu()
+        # per-level KL(p || p_hat) of the routing estimate, on the final tree state
+        # (every step's query against the tree at the last step's length)
+        kl = torch.empty(wl.L, wl.B, wl.Hq, device="cuda")
+        kls = []
+        s_last = W + K - 1
+        for s in range(W, W + K, max(1, K // 8)):
+            zha.route_quality(run.cfg, run.Q[s], run.K, run.V, run.Ts[s_last], run.dec.tree, kl,
+                              run.dec.ws)
+            kls.append(kl.clone())
+        kls = torch.stack(kls).double().cpu()
         extra["quality_vs_dense"] = {
             "mass_recall_mean": float(recall.mean()), "mass_recall_min": float(recall.min()),
             "out_rel_err_mean": float(oerr.mean()), "out_rel_err_max": float(oerr.max()),
-            "note": "per query head and step: recall = dense softmax mass of the routed key set"}
+            "kl_per_level_mean": [float(kls[:, l].mean()) for l in range(wl.L)],
+            "note": "per query head and step: recall = dense softmax mass of the routed key set; "
+                    "kl = KL(true || estimated) node distribution per level (1 .. L)"}
         log(f"[bench] dense-mass recall of the routed sets: mean {float(recall.mean()):.4f}, "
             f"min {float(recall.min()):.4f}")
 
