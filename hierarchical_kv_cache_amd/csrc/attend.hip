@@ -1038,50 +1038,57 @@ attend_partial_f32(AttendParams P) {
 // ---------------------------------------------------------------- merge
 //
 // [ASM] "방법론": lse = log sum_s Z_s, out = sum_s (Z_s / Z) a_s, evaluated in the
-// log domain in two passes: the maximum of the partial maxima, then the rescaled
-// sums.  Wave w of the workgroup takes partials w, w+4, ... (lanes over dims, the
-// loads of successive partials are independent); the four wave sums are added in
-// a fixed order, so the result is deterministic.
-constexpr int kMergeWaves = 16;
+// log domain: the maximum of the partial maxima, then the rescaled sums.  Two
+// levels, so a head's partials are read by many workgroups: attend_merge_seg
+// merges each of kMergeSegs contiguous segments of a head's partials into one
+// state (waves take partials w, w+4, ..., lanes over dims, kMergeInFlight
+// partials' loads in flight per wave, the four wave states added in a fixed
+// order); attend_merge_final merges a head's segment states in segment order and
+// writes out and lse.  Deterministic.
+constexpr int kMergeSegs = kMergeSegments;
+constexpr int kMergeInFlight = 8;
 
 template <int D>
-__global__ void __launch_bounds__(kMergeWaves * 64)
-attend_merge(AttendParams P, float* out, float* lse) {
+__global__ void __launch_bounds__(256) attend_merge_seg(AttendParams P, float* seg) {
   constexpr int DPL = D / kWave;
-  constexpr int U = 8;                       // partials in flight per wave
-  __shared__ float red[kMergeWaves];
-  __shared__ float acc_o[kMergeWaves][D];
-  __shared__ float acc_l[kMergeWaves];
+  constexpr int NW = 4;
+  constexpr int U = kMergeInFlight;
+  __shared__ float red[NW];
+  __shared__ float acc_o[NW][D];
+  __shared__ float acc_l[NW];
   const int head = blockIdx.x;              // b * Hq + j
+  const int k = blockIdx.y;                 // segment
   const int gi = head / P.G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const GroupInfo g = group_info(P, gi);
   const int n = min(g.items, P.split_cap);
+  const int per = (n + kMergeSegs - 1) / kMergeSegs;
+  const int i_lo = k * per, i_hi = min(n, i_lo + per);
   const float* base = P.part + (int64_t)head * P.split_cap * (D + 2);
   float M = -INFINITY;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, base[(int64_t)i * (D + 2)]);
-  M = block_max_f<kMergeWaves>(M, red);
+  for (int i = i_lo + threadIdx.x; i < i_hi; i += blockDim.x) M = fmaxf(M, base[(int64_t)i * (D + 2)]);
+  M = block_max_f<NW>(M, red);
   float l = 0.0f, o[DPL];
 #pragma unroll
   for (int j = 0; j < DPL; ++j) o[j] = 0.0f;
   if (M != -INFINITY) {
-    for (int i0 = wave; i0 < n; i0 += kMergeWaves * U) {
+    for (int i0 = i_lo + wave; i0 < i_hi; i0 += NW * U) {
       float mi[U], li[U], oi[U][DPL];
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int i = i0 + k * kMergeWaves;
-        const float* pi = base + (int64_t)(i < n ? i : 0) * (D + 2);
-        mi[k] = (i < n) ? pi[0] : -INFINITY;
-        li[k] = pi[1];
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NW;
+        const float* pi = base + (int64_t)(i < i_hi ? i : i_lo) * (D + 2);
+        mi[u] = (i < i_hi) ? pi[0] : -INFINITY;
+        li[u] = pi[1];
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) oi[k][j] = pi[2 + lane + j * kWave];
+        for (int j = 0; j < DPL; ++j) oi[u][j] = pi[2 + lane + j * kWave];
       }
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const float w = exp2f(mi[k] - M);      // 0 for an empty or absent partial
-        l += (w != 0.0f) ? li[k] * w : 0.0f;
+      for (int u = 0; u < U; ++u) {
+        const float w = exp2f(mi[u] - M);      // 0 for an empty or absent partial
+        l += (w != 0.0f) ? li[u] * w : 0.0f;
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) o[j] += (w != 0.0f) ? oi[k][j] * w : 0.0f;
+        for (int j = 0; j < DPL; ++j) o[j] += (w != 0.0f) ? oi[u][j] * w : 0.0f;
       }
     }
   }
@@ -1089,13 +1096,49 @@ attend_merge(AttendParams P, float* out, float* lse) {
   for (int j = 0; j < DPL; ++j) acc_o[wave][lane + j * kWave] = o[j];
   if (lane == 0) acc_l[wave] = l;
   __syncthreads();
+  float* dst = seg + ((int64_t)head * kMergeSegs + k) * (D + 2);
   for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    float L = 0.0f, Ov = 0.0f;
+    float Ov = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) { L += acc_l[w]; Ov += acc_o[w][c]; }
-    out[(int64_t)head * D + c] = (L > 0.0f) ? Ov / L : 0.0f;
-    if (c == 0) lse[head] = (L > 0.0f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+    for (int w = 0; w < NW; ++w) Ov += acc_o[w][c];
+    dst[2 + c] = Ov;
   }
+  if (threadIdx.x == 0) {
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) L += acc_l[w];
+    dst[0] = M;
+    dst[1] = L;
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(64) attend_merge_final(const float* seg, float* out, float* lse) {
+  constexpr int DPL = D / kWave;
+  const int head = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* base = seg + (int64_t)head * kMergeSegs * (D + 2);
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMergeSegs; ++k) M = fmaxf(M, base[(int64_t)k * (D + 2)]);
+  float L = 0.0f, o[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) o[j] = 0.0f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int k = 0; k < kMergeSegs; ++k) {
+      const float* pk = base + (int64_t)k * (D + 2);
+      const float w = exp2f(pk[0] - M);
+      if (w != 0.0f) {
+        L += pk[1] * w;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) o[j] += pk[2 + lane + j * kWave] * w;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) out[(int64_t)head * D + lane + j * kWave] = (L > 0.0f) ? o[j] / L : 0.0f;
+  if (lane == 0) lse[head] = (L > 0.0f) ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------- host
@@ -1144,6 +1187,7 @@ static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
   P.leaf_count = dense ? nullptr : leaf_count;
   P.leaf_cap = cfg->leaf_cap;
   P.part = (float*)((char*)ws + w.attend_off);
+  float* seg = (float*)((char*)ws + w.merge_off);
   P.status = (int32_t*)ws;
   P.B = cfg->B; P.H_kv = cfg->H_kv; P.G = cfg->G; P.C = cfg->C;
   P.T_cap = cfg->T_cap;
@@ -1155,10 +1199,12 @@ static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
   const int BHq = cfg->B * cfg->H_kv * cfg->G;
   if (cfg->d == 64) {
     launch_partial_g<64>(P, cfg->kv_dtype, grid, s);
-    hipLaunchKernelGGL((attend_merge<64>), dim3(BHq), dim3(kMergeWaves * 64), 0, s, P, out, lse);
+    hipLaunchKernelGGL((attend_merge_seg<64>), dim3(BHq, kMergeSegs), dim3(256), 0, s, P, seg);
+    hipLaunchKernelGGL((attend_merge_final<64>), dim3(BHq), dim3(64), 0, s, (const float*)seg, out, lse);
   } else {
     launch_partial_g<128>(P, cfg->kv_dtype, grid, s);
-    hipLaunchKernelGGL((attend_merge<128>), dim3(BHq), dim3(kMergeWaves * 64), 0, s, P, out, lse);
+    hipLaunchKernelGGL((attend_merge_seg<128>), dim3(BHq, kMergeSegs), dim3(256), 0, s, P, seg);
+    hipLaunchKernelGGL((attend_merge_final<128>), dim3(BHq), dim3(64), 0, s, (const float*)seg, out, lse);
   }
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
 }
