@@ -36,18 +36,21 @@ struct BuildParams {
   int64_t T_cap, span;        // span = C^level
 };
 
-// Reference queries of node n at `level`, rotated when P.rope, into qh[R][d].
+// Reference queries r0 .. r1-1 of node n at `level`, rotated when P.rope, into
+// qh[r][d] (row stride ld).
 __device__ inline void load_ref_queries(const BuildParams& P, int h, int64_t pos,
-                                        float* qh, int ld) {
+                                        float* qh, int ld, int r0 = 0, int r1 = -1) {
   const int d = P.d, half = d / 2;
+  if (r1 < 0) r1 = P.R;
+  const int nr = r1 - r0;
   const float* qr = P.qref + (int64_t)h * P.R * d;
   if (!P.rope) {
-    for (int idx = threadIdx.x; idx < P.R * d; idx += blockDim.x)
-      qh[(idx / d) * ld + idx % d] = qr[idx];
+    for (int idx = threadIdx.x; idx < nr * d; idx += blockDim.x)
+      qh[(r0 + idx / d) * ld + idx % d] = qr[r0 * d + idx];
     return;
   }
-  for (int idx = threadIdx.x; idx < P.R * half; idx += blockDim.x) {
-    const int r = idx / half, i = idx % half;
+  for (int idx = threadIdx.x; idx < nr * half; idx += blockDim.x) {
+    const int r = r0 + idx / half, i = idx % half;
     const double theta = pow((double)P.rope_base, -2.0 * (double)i / (double)d);
     const double ang = (double)pos * theta;
     double sn, cs;
@@ -148,6 +151,239 @@ __global__ void __launch_bounds__(256) build_leaves(BuildParams P) {
   }
 }
 
+// ---------------------------------------------------------------- leaves on MFMA
+//
+// bf16 keys, C in {16, 32, 64}, R <= 16: both products of a leaf are dense
+// contractions, Z = Q_hat K^T (R x C over d) and k_hat = softmax(Z) K (R x d over
+// C), and run on MFMA 16x16x32 bf16.  The fp32 operand of each (the scaled
+// reference queries, then the softmax weights) is split into three bf16 terms
+// hi + mid + lo, which carry it to ~2^-24; the keys are exact in bf16; products
+// accumulate in fp32.  Rows are the planes (padded to 16).  Z: wave w takes keys
+// 16w..16w+15, its key operand read straight from the cache rows.  k_hat: wave w
+// takes the 16-dim tiles w, w+4, ..., its key operand read from K^T staged in
+// LDS.  Under RoPE the reference queries are rotated per leaf, with one fp64
+// sincos per dimension pair shared by the R planes.
+
+typedef __bf16 bf16x8b_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4b_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4b_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+
+__device__ inline void split3(float x, __bf16& hi, __bf16& mid, __bf16& lo) {
+  const uint16_t h = f32_to_bf16_rne(x);
+  const float r1 = x - __uint_as_float((uint32_t)h << 16);
+  const uint16_t m = f32_to_bf16_rne(r1);
+  const float r2 = r1 - __uint_as_float((uint32_t)m << 16);
+  const uint16_t l = f32_to_bf16_rne(r2);
+  hi = __builtin_bit_cast(__bf16, h);
+  mid = __builtin_bit_cast(__bf16, m);
+  lo = __builtin_bit_cast(__bf16, l);
+}
+
+template <int D, int C>
+__global__ void __launch_bounds__(256) build_leaves_mfma(BuildParams P) {
+  constexpr int KST = D / 32;              // contraction steps of Z
+  constexpr int KP = kMaxC + 8;            // key stride of K^T in LDS (bf16 elements)
+  constexpr int NTZ = C / 16;              // key tiles of Z, one per wave
+  constexpr int KSTEPS = (C + 31) / 32;    // contraction steps of W K
+  __shared__ __attribute__((aligned(16))) uint16_t kt[D][KP];   // K^T (bf16 bits)
+  __shared__ __attribute__((aligned(16))) float wsm[16][kMaxC + 4];   // softmax weights
+  __shared__ float qs[16][D + 4];          // scaled (rotated) reference queries
+  __shared__ float rc[D / 2], rsn[D / 2];  // RoPE cos / sin of the leaf position
+  __shared__ float red[3][4][16];          // per-wave plane max, sum, sum w z
+  const int gi = blockIdx.y;
+  const int b = gi / P.H_kv, h = gi % P.H_kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = P.R;
+  int64_t n0, n1;
+  node_range(P, b, n0, n1);
+  const float* qr = P.qref + (int64_t)h * R * D;
+
+  // keys C..31 of K^T stay zero (the 32-key contraction step pads short leaves)
+  for (int i = tid; i < D * KP; i += 256) (&kt[0][0])[i] = 0;
+  if (C < 32)                              // and so do their weights
+    for (int i = tid; i < 16 * (kMaxC + 4); i += 256) (&wsm[0][0])[i] = 0.0f;
+  auto stage_queries = [&](int64_t pos) {
+    if (!P.rope) {
+      for (int i = tid; i < 16 * D; i += 256) {
+        const int r = i / D, c = i % D;
+        qs[r][c] = (r < R) ? qr[r * D + c] * P.scale : 0.0f;
+      }
+      return;
+    }
+    constexpr int H2 = D / 2;
+    if (tid < H2) {
+      const double theta = pow((double)P.rope_base, -2.0 * (double)tid / (double)D);
+      double sn, cs;
+      sincos((double)pos * theta, &sn, &cs);
+      rc[tid] = (float)cs;
+      rsn[tid] = (float)sn;
+    }
+    __syncthreads();
+    for (int i = tid; i < 16 * H2; i += 256) {
+      const int r = i / H2, c = i % H2;
+      float x1 = 0.0f, x2 = 0.0f;
+      if (r < R) {
+        const double a = qr[r * D + c], bb = qr[r * D + c + H2];
+        const double cs = rc[c], sn = rsn[c];
+        x1 = (float)(a * cs - bb * sn);
+        x2 = (float)(a * sn + bb * cs);
+      }
+      qs[r][c] = x1 * P.scale;
+      qs[r][c + H2] = x2 * P.scale;
+    }
+  };
+  bf16x8b_t qa[3][KST];
+  auto load_qa = [&]() {
+    const int row = lane & 15, kg = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < KST; ++s) {
+      bf16x8b_t a0, a1, a2;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        __bf16 x0, x1, x2;
+        split3(qs[row][s * 32 + kg * 8 + j], x0, x1, x2);
+        a0[j] = x0; a1[j] = x1; a2[j] = x2;
+      }
+      qa[0][s] = a0; qa[1][s] = a1; qa[2][s] = a2;
+    }
+  };
+  if (!P.rope) {
+    stage_queries(0);
+    __syncthreads();
+    load_qa();
+  }
+  // Wave w < C/16 owns keys 16w + (lane % 16); its MFMA B operand of step s is
+  // the 8 dimensions 32s + 8(lane / 16).. of that key.  The same registers fill
+  // K^T in LDS.  Two register sets alternate between leaves, so the keys of the
+  // next two leaves are in flight while one is summarised.
+  const uint16_t* Kb = (const uint16_t*)P.K;
+  const int krow = 16 * wave + (lane & 15), kg0 = lane >> 4;
+  const int64_t g = gridDim.x;
+  auto fetch = [&](int64_t n, u32x4b_t (&v)[KST]) {
+    if (wave >= NTZ || n >= n1) return;
+    const uint16_t* kr = Kb + ((int64_t)gi * P.T_cap + n * C + krow) * D + kg0 * 8;
+#pragma unroll
+    for (int s = 0; s < KST; ++s) v[s] = __builtin_nontemporal_load((const u32x4b_t*)(kr + s * 32));
+  };
+  auto leaf = [&](int64_t n, u32x4b_t (&kv)[KST]) {
+    __syncthreads();                       // the previous leaf's LDS reads are done
+    if (P.rope) stage_queries(n * C);
+    if (wave < NTZ) {
+#pragma unroll
+      for (int s = 0; s < KST; ++s) {
+        const int c0 = 32 * s + 8 * kg0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kt[c0 + 2 * e][krow] = (uint16_t)(kv[s][e] & 0xffffu);
+          kt[c0 + 2 * e + 1][krow] = (uint16_t)(kv[s][e] >> 16);
+        }
+      }
+    }
+    if (P.rope) {
+      __syncthreads();
+      load_qa();
+    }
+    // ---- Z = Q_hat K^T: z[i] is plane 4(lane/16)+i, key 16w + lane%16
+    f32x4b_t z = {0.f, 0.f, 0.f, 0.f};
+    if (wave < NTZ) {
+#pragma unroll
+      for (int s = 0; s < KST; ++s) {
+        const bf16x8b_t kb = __builtin_bit_cast(bf16x8b_t, kv[s]);
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][s], kb, z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][s], kb, z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2][s], kb, z, 0, 0, 0);
+      }
+    }
+    fetch(n + 2 * g, kv);                  // this register set's next leaf
+    if (wave < NTZ) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {        // per-wave max over its 16 keys
+        float m = z[i];
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        m = fmaxf(m, __shfl_xor(m, 4, 64));
+        m = fmaxf(m, __shfl_xor(m, 8, 64));
+        if ((lane & 15) == 0) red[0][wave][4 * (lane >> 4) + i] = m;
+      }
+    }
+    __syncthreads();
+    float e4[4];
+    if (wave < NTZ) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pl = 4 * (lane >> 4) + i;
+        float M = red[0][0][pl];
+#pragma unroll
+        for (int w = 1; w < NTZ; ++w) M = fmaxf(M, red[0][w][pl]);
+        const float e = expf(z[i] - M);
+        e4[i] = e;
+        float sm = e, sz = e * z[i];
+        sm += __shfl_xor(sm, 1, 64); sz += __shfl_xor(sz, 1, 64);
+        sm += __shfl_xor(sm, 2, 64); sz += __shfl_xor(sz, 2, 64);
+        sm += __shfl_xor(sm, 4, 64); sz += __shfl_xor(sz, 4, 64);
+        sm += __shfl_xor(sm, 8, 64); sz += __shfl_xor(sz, 8, 64);
+        if ((lane & 15) == 0) { red[1][wave][pl] = sm; red[2][wave][pl] = sz; }
+      }
+    }
+    __syncthreads();
+    if (wave < NTZ) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pl = 4 * (lane >> 4) + i;
+        float S = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NTZ; ++w) S += red[1][w][pl];
+        wsm[pl][16 * wave + (lane & 15)] = e4[i] / S;
+      }
+    }
+    if (tid < R) {
+      float M = red[0][0][tid], S = 0.0f, SZ = 0.0f;
+#pragma unroll
+      for (int w = 1; w < NTZ; ++w) M = fmaxf(M, red[0][w][tid]);
+#pragma unroll
+      for (int w = 0; w < NTZ; ++w) { S += red[1][w][tid]; SZ += red[2][w][tid]; }
+      // b_hat = F - sum_j w_j z_j, F = M + log S
+      P.bhat[((int64_t)gi * P.ncap + n) * R + tid] = (M + logf(S)) - SZ / S;
+    }
+    __syncthreads();
+    // ---- k_hat = W K: wave w, 16-dim tiles w, w + 4, ...
+    const int row = lane & 15, kg = lane >> 4;
+    float* kh = P.khat + ((int64_t)gi * P.ncap + n) * R * D;
+#pragma unroll
+    for (int t = wave; t < D / 16; t += 4) {
+      f32x4b_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        bf16x8b_t a0, a1, a2;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          __bf16 x0, x1, x2;
+          split3(wsm[row][s * 32 + kg * 8 + j], x0, x1, x2);
+          a0[j] = x0; a1[j] = x1; a2[j] = x2;
+        }
+        const bf16x8b_t kb = __builtin_bit_cast(bf16x8b_t,
+                                                *(const u32x4b_t*)&kt[t * 16 + row][s * 32 + kg * 8]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, kb, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, kb, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, kb, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pl = 4 * kg + i;
+        if (pl < R) kh[(int64_t)pl * D + t * 16 + row] = acc[i];
+      }
+    }
+  };
+  u32x4b_t ka[KST], kb2[KST];
+  const int64_t first = n0 + blockIdx.x;
+  fetch(first, ka);
+  fetch(first + g, kb2);
+  for (int64_t n = first; n < n1; n += 2 * g) {
+    leaf(n, ka);
+    if (n + g < n1) leaf(n + g, kb2);
+  }
+}
+
 __global__ void __launch_bounds__(256) build_parents(BuildParams P) {
   __shared__ BuildSmem sm;
   const int gi = blockIdx.y;
@@ -155,14 +391,37 @@ __global__ void __launch_bounds__(256) build_parents(BuildParams P) {
   int64_t n0, n1;
   node_range(P, b, n0, n1);
   const int d = P.d, C = P.C, R = P.R;
-  for (int64_t n = n0 + blockIdx.x; n < n1; n += gridDim.x) {
-    load_ref_queries(P, h, n * P.span, &sm.qh[0][0], kMaxD + 1);
+  // one (node, plane) pair at a time: planes of a node are independent
+  for (int64_t pr = blockIdx.x; pr < (n1 - n0) * R; pr += gridDim.x) {
+    const int64_t n = n0 + pr / R;
+    const int r = (int)(pr % R);
+    __syncthreads();                      // the previous pair's LDS reads are done
+    load_ref_queries(P, h, n * P.span, &sm.qh[0][0], kMaxD + 1, r, r + 1);
     const int64_t ch0 = n * C;   // first child
-    for (int r = 0; r < R; ++r) {
-      // children's plane r -> LDS
-      for (int idx = threadIdx.x; idx < C * d; idx += blockDim.x) {
-        const int j = idx / d, c = idx % d;
-        sm.k[j][c] = P.khat_ch[(((int64_t)gi * P.ncap_ch + ch0 + j) * R + r) * d + c];
+    {
+      // children's plane r -> LDS: 16-byte loads (d is 64 or 128), all of a
+      // thread's loads (at most 8) in flight before its stores
+      {
+        // 256 is a multiple of d/4, so a thread keeps its column and steps rows
+        constexpr int IT = kMaxC * kMaxD / 4 / 256;
+        const int dq = d / 4, rstep = 256 / dq;
+        const int j0 = threadIdx.x / dq, c = 4 * (threadIdx.x % dq);
+        const float* src = P.khat_ch + (((int64_t)gi * P.ncap_ch + ch0 + j0) * R + r) * d + c;
+        const int64_t step = (int64_t)rstep * R * d;
+        float4 v[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+          if (j0 + it * rstep < C) v[it] = *(const float4*)(src + it * step);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+          const int j = j0 + it * rstep;
+          if (j < C) {
+            sm.k[j][c] = v[it].x;
+            sm.k[j][c + 1] = v[it].y;
+            sm.k[j][c + 2] = v[it].z;
+            sm.k[j][c + 3] = v[it].w;
+          }
+        }
       }
       __syncthreads();
       // s_j = scale q_hat_P . k_hat_{r,j} + b_hat_{r,j}: 4 waves split d, then sum
@@ -259,10 +518,23 @@ static void launch_level(const BuildParams& P, int64_t max_nodes, hipStream_t s)
   int64_t gx = max_nodes < 1 ? 1 : max_nodes;
   if (gx > 65535) gx = 65535;
   const dim3 grid((unsigned)gx, (unsigned)(P.B * P.H_kv));
-  if (P.level == 1)
+  // the MFMA leaf builder loops over leaves with a prefetch: about two
+  // workgroups per compute unit in all (its register budget allows two)
+  const int64_t lx = (512 + P.B * P.H_kv - 1) / (P.B * P.H_kv);
+  const dim3 lgrid((unsigned)(gx < lx ? gx : lx), (unsigned)(P.B * P.H_kv));
+  const bool mfma = P.kv_dtype == ZHA_BF16 && P.R <= 16 && (P.C == 16 || P.C == 32 || P.C == 64);
+  // parents are built one (node, plane) pair per workgroup iteration
+  const dim3 pgrid((unsigned)(gx * P.R > 65535 ? 65535 : gx * P.R), (unsigned)(P.B * P.H_kv));
+  if (P.level == 1 && mfma) {
+    const auto k = P.d == 128 ? (P.C == 64 ? build_leaves_mfma<128, 64>
+                                 : P.C == 32 ? build_leaves_mfma<128, 32> : build_leaves_mfma<128, 16>)
+                              : (P.C == 64 ? build_leaves_mfma<64, 64>
+                                 : P.C == 32 ? build_leaves_mfma<64, 32> : build_leaves_mfma<64, 16>);
+    hipLaunchKernelGGL(k, lgrid, dim3(256), 0, s, P);
+  } else if (P.level == 1)
     hipLaunchKernelGGL(build_leaves, grid, dim3(256), 0, s, P);
   else
-    hipLaunchKernelGGL(build_parents, grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL(build_parents, pgrid, dim3(256), 0, s, P);
 }
 
 }  // namespace zha

@@ -72,6 +72,17 @@ def test_build_bf16_nope_levels(C, L, T, G):
         _compare_tree(cfg, K, qref, tree, T, None, h=h)
 
 
+@pytest.mark.parametrize("C,rope", [(32, False), (16, True), (64, False)])
+def test_build_bf16_d64(C, rope):
+    """Head dimension 64 on the matrix-core leaf builder, with and without RoPE."""
+    wl = _workload("rope_batch" if rope else "gqa128k", B=1, H_kv=2, G=4, d=64, C=C, L=2,
+                   n_clusters=64)
+    T = C * C * 3 + C * 5 + 7
+    cfg, K, V, qref, tree, ws, Tt = _build_gpu(wl, T)
+    for h in range(2):
+        _compare_tree(cfg, K, qref, tree, T, wl.rope_base if rope else None, h=h)
+
+
 def test_build_rope_parent_correction():
     """RoPE: reference queries rotated to each node's first key position; parents
     rescore children at their own rotated query (the correction term)."""
@@ -82,14 +93,16 @@ def test_build_rope_parent_correction():
         _compare_tree(cfg, K, qref, tree, T, wl.rope_base, b=b)
 
 
-def test_append_cascade_equals_prefill_build():
+@pytest.mark.parametrize("C,L", [(8, 3), (16, 2)])
+def test_append_cascade_equals_prefill_build(C, L):
     """Growing T one token at a time with zha_append yields exactly the tree a
-    prefill build of the final length gives (the append cadence)."""
-    wl = _workload("gqa128k", H_kv=2, G=4, C=8, L=3, n_clusters=16)
-    T0, T1 = 8 ** 3 - 37, 8 ** 3 * 2 + 70
-    K, V = synth.make_cache(wl.with_(N=T1, open_len=0, steps=0), DEV, T1 + 8)
+    prefill build of the final length gives (the append cadence); C = 16 takes
+    the matrix-core leaf builder, C = 8 the plain one."""
+    wl = _workload("gqa128k", H_kv=2, G=4, C=C, L=L, n_clusters=16)
+    T0, T1 = C ** L - 37, C ** L * 2 + 70
+    K, V = synth.make_cache(wl.with_(N=T1, open_len=0, steps=0), DEV, T1 + C)
     qref = synth.make_qref(wl, DEV)
-    cfg = zha.Config(B=1, H_kv=2, G=4, d=128, C=8, L=3, R=16, T_cap=T1 + 8)
+    cfg = zha.Config(B=1, H_kv=2, G=4, d=128, C=C, L=L, R=16, T_cap=T1 + C)
     tree = zha.Tree(cfg, DEV)
     ws = zha.new_workspace(cfg)
     T = torch.tensor([T0], dtype=torch.int64, device=DEV)
@@ -106,12 +119,12 @@ def test_append_cascade_equals_prefill_build():
     ref = zha.Tree(cfg, DEV)
     zha.build(cfg, K, V, T, qref, ref, ws)
     torch.cuda.synchronize()
-    for level in range(1, 4):
-        n = T1 // 8 ** level
+    for level in range(1, L + 1):
+        n = T1 // C ** level
         assert torch.equal(tree.khat[level - 1][:, :, :n], ref.khat[level - 1][:, :, :n])
         assert torch.equal(tree.bhat[level - 1][:, :, :n], ref.bhat[level - 1][:, :, :n])
         assert torch.equal(tree2.khat[level - 1][:, :, :n], ref.khat[level - 1][:, :, :n])
-    assert tree.n_built[:, 0].tolist() == [T1 // 8, T1 // 64, T1 // 512]
+    assert tree.n_built[:, 0].tolist() == [T1 // C ** l for l in range(1, L + 1)]
     assert zha.ws_status(ws) == 0
 
 
