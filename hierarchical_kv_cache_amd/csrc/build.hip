@@ -179,62 +179,65 @@ __device__ inline void split3(float x, __bf16& hi, __bf16& mid, __bf16& lo) {
   lo = __builtin_bit_cast(__bf16, l);
 }
 
+// Leaf summaries on the matrix cores, one wave per leaf (bf16 keys).
+//   Z = Q_hat K^T          A = scaled reference queries (3-way bf16 split),
+//                          B = the leaf's keys as loaded (row = key, 8 dims)
+//   softmax over keys per plane in registers, b_hat = F - sum_j w_j z_j
+//   k_hat^T = K^T W^T      A = K^T through LDS, B = W (3-way bf16 split)
+// A wave loops over leaves with the next leaf's keys in flight; no workgroup
+// barriers are needed (a workgroup is one wave).
 template <int D, int C>
-__global__ void __launch_bounds__(256) build_leaves_mfma(BuildParams P) {
-  constexpr int KST = D / 32;              // contraction steps of Z
-  constexpr int KP = kMaxC + 8;            // key stride of K^T in LDS (bf16 elements)
-  constexpr int NTZ = C / 16;              // key tiles of Z, one per wave
-  constexpr int KSTEPS = (C + 31) / 32;    // contraction steps of W K
-  __shared__ __attribute__((aligned(16))) uint16_t kt[D][KP];   // K^T (bf16 bits)
-  __shared__ __attribute__((aligned(16))) float wsm[16][kMaxC + 4];   // softmax weights
-  __shared__ float qs[16][D + 4];          // scaled (rotated) reference queries
-  __shared__ float rc[D / 2], rsn[D / 2];  // RoPE cos / sin of the leaf position
-  __shared__ float red[3][4][16];          // per-wave plane max, sum, sum w z
+__global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
+  constexpr int KST = D / 32;              // dimension steps of Z
+  constexpr int NT = C / 16;               // key tiles of Z
+  constexpr int CK = C < 32 ? 32 : C;      // keys padded to whole contraction steps
+  constexpr int KS2 = CK / 32;             // key steps of k_hat
+  constexpr int KP = CK + 8;               // K^T row stride (bf16 elements)
+  constexpr int WP = CK + 4;               // W row stride (floats)
+  constexpr int H2 = D / 2;
+  constexpr int KT_BYTES = D * KP * 2;
+  static_assert(16 * (D + 4) * 4 <= KT_BYTES, "query staging aliases K^T");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[KT_BYTES + 16 * WP * 4];
+  uint16_t (*kt)[KP] = reinterpret_cast<uint16_t (*)[KP]>(lds);
+  float (*qs)[D + 4] = reinterpret_cast<float (*)[D + 4]>(lds);   // before K^T is written
+  float (*wsm)[WP] = reinterpret_cast<float (*)[WP]>(lds + KT_BYTES);
   const int gi = blockIdx.y;
   const int b = gi / P.H_kv, h = gi % P.H_kv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x, row = lane & 15, kg = lane >> 4;
   const int R = P.R;
   int64_t n0, n1;
   node_range(P, b, n0, n1);
   const float* qr = P.qref + (int64_t)h * R * D;
+  // weights of the padded keys C..CK-1 stay zero
+  for (int i = lane; i < 16 * WP; i += 64) (&wsm[0][0])[i] = 0.0f;
+  // RoPE: lane handles frequency lane % (d/2) for every plane it stages
+  double theta = 0.0;
+  if (P.rope) theta = pow((double)P.rope_base, -2.0 * (double)(lane % H2) / (double)D);
 
-  // keys C..31 of K^T stay zero (the 32-key contraction step pads short leaves)
-  for (int i = tid; i < D * KP; i += 256) (&kt[0][0])[i] = 0;
-  if (C < 32)                              // and so do their weights
-    for (int i = tid; i < 16 * (kMaxC + 4); i += 256) (&wsm[0][0])[i] = 0.0f;
-  auto stage_queries = [&](int64_t pos) {
+  bf16x8b_t qa[3][KST];
+  auto build_qa = [&](int64_t pos) {
+    __syncthreads();                       // the previous leaf's K^T reads are done
     if (!P.rope) {
-      for (int i = tid; i < 16 * D; i += 256) {
+      for (int i = lane; i < 16 * D; i += 64) {
         const int r = i / D, c = i % D;
         qs[r][c] = (r < R) ? qr[r * D + c] * P.scale : 0.0f;
       }
-      return;
-    }
-    constexpr int H2 = D / 2;
-    if (tid < H2) {
-      const double theta = pow((double)P.rope_base, -2.0 * (double)tid / (double)D);
+    } else {
       double sn, cs;
       sincos((double)pos * theta, &sn, &cs);
-      rc[tid] = (float)cs;
-      rsn[tid] = (float)sn;
+      for (int idx = lane; idx < 16 * H2; idx += 64) {
+        const int r = idx / H2, c = idx % H2;   // c == lane % H2
+        float x1 = 0.0f, x2 = 0.0f;
+        if (r < R) {
+          const double a = qr[r * D + c], bb = qr[r * D + c + H2];
+          x1 = (float)(a * cs - bb * sn);
+          x2 = (float)(a * sn + bb * cs);
+        }
+        qs[r][c] = x1 * P.scale;
+        qs[r][c + H2] = x2 * P.scale;
+      }
     }
     __syncthreads();
-    for (int i = tid; i < 16 * H2; i += 256) {
-      const int r = i / H2, c = i % H2;
-      float x1 = 0.0f, x2 = 0.0f;
-      if (r < R) {
-        const double a = qr[r * D + c], bb = qr[r * D + c + H2];
-        const double cs = rc[c], sn = rsn[c];
-        x1 = (float)(a * cs - bb * sn);
-        x2 = (float)(a * sn + bb * cs);
-      }
-      qs[r][c] = x1 * P.scale;
-      qs[r][c + H2] = x2 * P.scale;
-    }
-  };
-  bf16x8b_t qa[3][KST];
-  auto load_qa = [&]() {
-    const int row = lane & 15, kg = lane >> 4;
 #pragma unroll
     for (int s = 0; s < KST; ++s) {
       bf16x8b_t a0, a1, a2;
@@ -246,141 +249,104 @@ __global__ void __launch_bounds__(256) build_leaves_mfma(BuildParams P) {
       }
       qa[0][s] = a0; qa[1][s] = a1; qa[2][s] = a2;
     }
+    __syncthreads();                       // K^T may overwrite the staging now
   };
-  if (!P.rope) {
-    stage_queries(0);
-    __syncthreads();
-    load_qa();
-  }
-  // Wave w < C/16 owns keys 16w + (lane % 16); its MFMA B operand of step s is
-  // the 8 dimensions 32s + 8(lane / 16).. of that key.  The same registers fill
-  // K^T in LDS.  Two register sets alternate between leaves, so the keys of the
-  // next two leaves are in flight while one is summarised.
+  if (!P.rope) build_qa(0);
+
+  // lane's share of a leaf: keys 16t + row, dimensions 32s + 8kg .. +8
   const uint16_t* Kb = (const uint16_t*)P.K;
-  const int krow = 16 * wave + (lane & 15), kg0 = lane >> 4;
-  const int64_t g = gridDim.x;
-  auto fetch = [&](int64_t n, u32x4b_t (&v)[KST]) {
-    if (wave >= NTZ || n >= n1) return;
-    const uint16_t* kr = Kb + ((int64_t)gi * P.T_cap + n * C + krow) * D + kg0 * 8;
+  auto fetch = [&](int64_t n, u32x4b_t (&v)[NT][KST]) {
+    const uint16_t* kr = Kb + ((int64_t)gi * P.T_cap + n * C + row) * D + kg * 8;
 #pragma unroll
-    for (int s = 0; s < KST; ++s) v[s] = __builtin_nontemporal_load((const u32x4b_t*)(kr + s * 32));
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int s = 0; s < KST; ++s)
+        v[t][s] = __builtin_nontemporal_load((const u32x4b_t*)(kr + t * 16 * D + s * 32));
   };
-  auto leaf = [&](int64_t n, u32x4b_t (&kv)[KST]) {
-    __syncthreads();                       // the previous leaf's LDS reads are done
-    if (P.rope) stage_queries(n * C);
-    if (wave < NTZ) {
+  u32x4b_t kv[NT][KST];
+  int64_t n = n0 + blockIdx.x;
+  if (n < n1) fetch(n, kv);
+  for (; n < n1; n += gridDim.x) {
+    if (P.rope) build_qa(n * C);
+    // ---- Z: z[t][i] = logit of plane 4kg + i, key 16t + row
+    f32x4b_t z[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      z[t] = f32x4b_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KST; ++s) {
-        const int c0 = 32 * s + 8 * kg0;
+        const bf16x8b_t kb = __builtin_bit_cast(bf16x8b_t, kv[t][s]);
+        z[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][s], kb, z[t], 0, 0, 0);
+        z[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][s], kb, z[t], 0, 0, 0);
+        z[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2][s], kb, z[t], 0, 0, 0);
+      }
+    }
+    // ---- K^T into LDS (padded keys zero), then the next leaf's keys in flight
+#pragma unroll
+    for (int t = 0; t < CK / 16; ++t)
+#pragma unroll
+      for (int s = 0; s < KST; ++s)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          kt[c0 + 2 * e][krow] = (uint16_t)(kv[s][e] & 0xffffu);
-          kt[c0 + 2 * e + 1][krow] = (uint16_t)(kv[s][e] >> 16);
+          const uint32_t x = t < NT ? kv[t < NT ? t : 0][s][e] : 0u;
+          kt[32 * s + 8 * kg + 2 * e][16 * t + row] = (uint16_t)(x & 0xffffu);
+          kt[32 * s + 8 * kg + 2 * e + 1][16 * t + row] = (uint16_t)(x >> 16);
         }
+    if (n + gridDim.x < n1) fetch(n + gridDim.x, kv);
+    // ---- softmax over the leaf's keys, per plane (16 lanes share a plane)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pl = 4 * kg + i;
+      float M = z[0][i];
+#pragma unroll
+      for (int t = 1; t < NT; ++t) M = fmaxf(M, z[t][i]);
+      M = fmaxf(M, __shfl_xor(M, 1, 64));
+      M = fmaxf(M, __shfl_xor(M, 2, 64));
+      M = fmaxf(M, __shfl_xor(M, 4, 64));
+      M = fmaxf(M, __shfl_xor(M, 8, 64));
+      float e[NT], S = 0.0f, SZ = 0.0f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        e[t] = expf(z[t][i] - M);
+        S += e[t];
+        SZ += e[t] * z[t][i];
       }
-    }
-    if (P.rope) {
-      __syncthreads();
-      load_qa();
-    }
-    // ---- Z = Q_hat K^T: z[i] is plane 4(lane/16)+i, key 16w + lane%16
-    f32x4b_t z = {0.f, 0.f, 0.f, 0.f};
-    if (wave < NTZ) {
-#pragma unroll
-      for (int s = 0; s < KST; ++s) {
-        const bf16x8b_t kb = __builtin_bit_cast(bf16x8b_t, kv[s]);
-        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0][s], kb, z, 0, 0, 0);
-        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1][s], kb, z, 0, 0, 0);
-        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2][s], kb, z, 0, 0, 0);
-      }
-    }
-    fetch(n + 2 * g, kv);                  // this register set's next leaf
-    if (wave < NTZ) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {        // per-wave max over its 16 keys
-        float m = z[i];
-        m = fmaxf(m, __shfl_xor(m, 1, 64));
-        m = fmaxf(m, __shfl_xor(m, 2, 64));
-        m = fmaxf(m, __shfl_xor(m, 4, 64));
-        m = fmaxf(m, __shfl_xor(m, 8, 64));
-        if ((lane & 15) == 0) red[0][wave][4 * (lane >> 4) + i] = m;
-      }
-    }
-    __syncthreads();
-    float e4[4];
-    if (wave < NTZ) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pl = 4 * (lane >> 4) + i;
-        float M = red[0][0][pl];
-#pragma unroll
-        for (int w = 1; w < NTZ; ++w) M = fmaxf(M, red[0][w][pl]);
-        const float e = expf(z[i] - M);
-        e4[i] = e;
-        float sm = e, sz = e * z[i];
-        sm += __shfl_xor(sm, 1, 64); sz += __shfl_xor(sz, 1, 64);
-        sm += __shfl_xor(sm, 2, 64); sz += __shfl_xor(sz, 2, 64);
-        sm += __shfl_xor(sm, 4, 64); sz += __shfl_xor(sz, 4, 64);
-        sm += __shfl_xor(sm, 8, 64); sz += __shfl_xor(sz, 8, 64);
-        if ((lane & 15) == 0) { red[1][wave][pl] = sm; red[2][wave][pl] = sz; }
-      }
-    }
-    __syncthreads();
-    if (wave < NTZ) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pl = 4 * (lane >> 4) + i;
-        float S = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NTZ; ++w) S += red[1][w][pl];
-        wsm[pl][16 * wave + (lane & 15)] = e4[i] / S;
-      }
-    }
-    if (tid < R) {
-      float M = red[0][0][tid], S = 0.0f, SZ = 0.0f;
-#pragma unroll
-      for (int w = 1; w < NTZ; ++w) M = fmaxf(M, red[0][w][tid]);
-#pragma unroll
-      for (int w = 0; w < NTZ; ++w) { S += red[1][w][tid]; SZ += red[2][w][tid]; }
+      S += __shfl_xor(S, 1, 64); SZ += __shfl_xor(SZ, 1, 64);
+      S += __shfl_xor(S, 2, 64); SZ += __shfl_xor(SZ, 2, 64);
+      S += __shfl_xor(S, 4, 64); SZ += __shfl_xor(SZ, 4, 64);
+      S += __shfl_xor(S, 8, 64); SZ += __shfl_xor(SZ, 8, 64);
       // b_hat = F - sum_j w_j z_j, F = M + log S
-      P.bhat[((int64_t)gi * P.ncap + n) * R + tid] = (M + logf(S)) - SZ / S;
+      if (row == 0 && pl < R) P.bhat[((int64_t)gi * P.ncap + n) * R + pl] = (M + logf(S)) - SZ / S;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) wsm[pl][16 * t + row] = e[t] / S;
     }
     __syncthreads();
-    // ---- k_hat = W K: wave w, 16-dim tiles w, w + 4, ...
-    const int row = lane & 15, kg = lane >> 4;
+    // ---- k_hat^T = K^T W^T; acc[i] = k_hat of plane row, dimension 16td + 4kg + i
+    bf16x8b_t wb[3][KS2];
+#pragma unroll
+    for (int s = 0; s < KS2; ++s) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        __bf16 x0, x1, x2;
+        split3(wsm[row][32 * s + 8 * kg + j], x0, x1, x2);
+        wb[0][s][j] = x0; wb[1][s][j] = x1; wb[2][s][j] = x2;
+      }
+    }
     float* kh = P.khat + ((int64_t)gi * P.ncap + n) * R * D;
 #pragma unroll
-    for (int t = wave; t < D / 16; t += 4) {
+    for (int td = 0; td < D / 16; ++td) {
       f32x4b_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        bf16x8b_t a0, a1, a2;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          __bf16 x0, x1, x2;
-          split3(wsm[row][s * 32 + kg * 8 + j], x0, x1, x2);
-          a0[j] = x0; a1[j] = x1; a2[j] = x2;
-        }
-        const bf16x8b_t kb = __builtin_bit_cast(bf16x8b_t,
-                                                *(const u32x4b_t*)&kt[t * 16 + row][s * 32 + kg * 8]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, kb, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, kb, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, kb, acc, 0, 0, 0);
+      for (int s = 0; s < KS2; ++s) {
+        const bf16x8b_t ka = __builtin_bit_cast(bf16x8b_t,
+                                                *(const u32x4b_t*)&kt[16 * td + row][32 * s + 8 * kg]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, wb[0][s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, wb[1][s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, wb[2][s], acc, 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pl = 4 * kg + i;
-        if (pl < R) kh[(int64_t)pl * D + t * 16 + row] = acc[i];
-      }
+      if (row < R) *(float4*)(kh + (int64_t)row * D + 16 * td + 4 * kg) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
-  };
-  u32x4b_t ka[KST], kb2[KST];
-  const int64_t first = n0 + blockIdx.x;
-  fetch(first, ka);
-  fetch(first + g, kb2);
-  for (int64_t n = first; n < n1; n += 2 * g) {
-    leaf(n, ka);
-    if (n + g < n1) leaf(n + g, kb2);
+    __syncthreads();                       // K^T and W are reused by the next leaf
   }
 }
 
@@ -518,9 +484,9 @@ static void launch_level(const BuildParams& P, int64_t max_nodes, hipStream_t s)
   int64_t gx = max_nodes < 1 ? 1 : max_nodes;
   if (gx > 65535) gx = 65535;
   const dim3 grid((unsigned)gx, (unsigned)(P.B * P.H_kv));
-  // the MFMA leaf builder loops over leaves with a prefetch: about two
-  // workgroups per compute unit in all (its register budget allows two)
-  const int64_t lx = (512 + P.B * P.H_kv - 1) / (P.B * P.H_kv);
+  // the MFMA leaf builder is one wave per workgroup looping over leaves: about
+  // seven waves per compute unit in all (its LDS share allows seven)
+  const int64_t lx = (7 * 256 + P.B * P.H_kv - 1) / (P.B * P.H_kv);
   const dim3 lgrid((unsigned)(gx < lx ? gx : lx), (unsigned)(P.B * P.H_kv));
   const bool mfma = P.kv_dtype == ZHA_BF16 && P.R <= 16 && (P.C == 16 || P.C == 32 || P.C == 64);
   // parents are built one (node, plane) pair per workgroup iteration
@@ -530,7 +496,7 @@ static void launch_level(const BuildParams& P, int64_t max_nodes, hipStream_t s)
                                  : P.C == 32 ? build_leaves_mfma<128, 32> : build_leaves_mfma<128, 16>)
                               : (P.C == 64 ? build_leaves_mfma<64, 64>
                                  : P.C == 32 ? build_leaves_mfma<64, 32> : build_leaves_mfma<64, 16>);
-    hipLaunchKernelGGL(k, lgrid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL(k, lgrid, dim3(64), 0, s, P);
   } else if (P.level == 1)
     hipLaunchKernelGGL(build_leaves, grid, dim3(256), 0, s, P);
   else
