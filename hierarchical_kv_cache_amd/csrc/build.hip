@@ -36,21 +36,19 @@ struct BuildParams {
   int64_t T_cap, span;        // span = C^level
 };
 
-// Reference queries r0 .. r1-1 of node n at `level`, rotated when P.rope, into
-// qh[r][d] (row stride ld).
+// The R reference queries of a node whose first key is at position pos, rotated
+// when P.rope, into qh[r][d] (row stride ld).
 __device__ inline void load_ref_queries(const BuildParams& P, int h, int64_t pos,
-                                        float* qh, int ld, int r0 = 0, int r1 = -1) {
-  const int d = P.d, half = d / 2;
-  if (r1 < 0) r1 = P.R;
-  const int nr = r1 - r0;
-  const float* qr = P.qref + (int64_t)h * P.R * d;
+                                        float* qh, int ld) {
+  const int d = P.d, half = d / 2, R = P.R;
+  const float* qr = P.qref + (int64_t)h * R * d;
   if (!P.rope) {
-    for (int idx = threadIdx.x; idx < nr * d; idx += blockDim.x)
-      qh[(r0 + idx / d) * ld + idx % d] = qr[r0 * d + idx];
+    for (int idx = threadIdx.x; idx < R * d; idx += blockDim.x)
+      qh[(idx / d) * ld + idx % d] = qr[idx];
     return;
   }
-  for (int idx = threadIdx.x; idx < nr * half; idx += blockDim.x) {
-    const int r = r0 + idx / half, i = idx % half;
+  for (int idx = threadIdx.x; idx < R * half; idx += blockDim.x) {
+    const int r = idx / half, i = idx % half;
     const double theta = pow((double)P.rope_base, -2.0 * (double)i / (double)d);
     const double ang = (double)pos * theta;
     double sn, cs;
@@ -350,82 +348,117 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
   }
 }
 
+// Parent summaries, one wave per (node, plane) pair: the children's planes r
+// (child 4t + lane/16, dimensions (lane%16)*d/16 ..) stay in registers, and an
+// exact two-pass softmax over the children gives k_hat and b_hat.  No LDS, no
+// workgroup barriers.
+template <int D>
 __global__ void __launch_bounds__(256) build_parents(BuildParams P) {
-  __shared__ BuildSmem sm;
+  constexpr int DPL = D / 16;              // dimensions per lane
+  constexpr int NV = DPL / 4;              // float4 per child per lane
+  constexpr int H2 = D / 2;
+  constexpr int MT = kMaxC / 4;            // child rounds
   const int gi = blockIdx.y;
   const int b = gi / P.H_kv, h = gi % P.H_kv;
+  const int lane = threadIdx.x & 63, cg = lane >> 4, ds = (lane & 15) * DPL;
+  const int C = P.C, R = P.R;
   int64_t n0, n1;
   node_range(P, b, n0, n1);
-  const int d = P.d, C = P.C, R = P.R;
-  // one (node, plane) pair at a time: planes of a node are independent
-  for (int64_t pr = blockIdx.x; pr < (n1 - n0) * R; pr += gridDim.x) {
+  const float* qr = P.qref + (int64_t)h * R * D;
+  // RoPE: lane computes frequency lane % (d/2) and shares it by shuffles
+  double theta = 0.0;
+  if (P.rope) theta = pow((double)P.rope_base, -2.0 * (double)(lane % H2) / (double)D);
+  const int64_t npairs = (n1 - n0) * R;
+  for (int64_t pr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); pr < npairs;
+       pr += (int64_t)gridDim.x * 4) {
     const int64_t n = n0 + pr / R;
     const int r = (int)(pr % R);
-    __syncthreads();                      // the previous pair's LDS reads are done
-    load_ref_queries(P, h, n * P.span, &sm.qh[0][0], kMaxD + 1, r, r + 1);
-    const int64_t ch0 = n * C;   // first child
-    {
-      // children's plane r -> LDS: 16-byte loads (d is 64 or 128), all of a
-      // thread's loads (at most 8) in flight before its stores
-      {
-        // 256 is a multiple of d/4, so a thread keeps its column and steps rows
-        constexpr int IT = kMaxC * kMaxD / 4 / 256;
-        const int dq = d / 4, rstep = 256 / dq;
-        const int j0 = threadIdx.x / dq, c = 4 * (threadIdx.x % dq);
-        const float* src = P.khat_ch + (((int64_t)gi * P.ncap_ch + ch0 + j0) * R + r) * d + c;
-        const int64_t step = (int64_t)rstep * R * d;
-        float4 v[IT];
+    const int64_t ch0 = n * C;
+    float4 v[MT][NV];
+    const float* src = P.khat_ch + (((int64_t)gi * P.ncap_ch + ch0 + cg) * R + r) * D + ds;
+    const int64_t cstep = (int64_t)4 * R * D;
 #pragma unroll
-        for (int it = 0; it < IT; ++it)
-          if (j0 + it * rstep < C) v[it] = *(const float4*)(src + it * step);
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int it = 0; it < IT; ++it) {
-          const int j = j0 + it * rstep;
-          if (j < C) {
-            sm.k[j][c] = v[it].x;
-            sm.k[j][c + 1] = v[it].y;
-            sm.k[j][c + 2] = v[it].z;
-            sm.k[j][c + 3] = v[it].w;
-          }
-        }
+      for (int q = 0; q < NV; ++q)
+        v[t][q] = 4 * t + cg < C ? *(const float4*)(src + t * cstep + 4 * q)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float bl = lane < C ? P.bhat_ch[((int64_t)gi * P.ncap_ch + ch0 + lane) * R + r] : 0.0f;
+    // plane r's reference query at the node's first key position
+    float qv[DPL];
+    if (!P.rope) {
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) qv[k] = qr[r * D + ds + k];
+    } else {
+      double sn, cs;
+      sincos((double)(n * P.span) * theta, &sn, &cs);
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        const int c = ds + k, i = c < H2 ? c : c - H2;
+        const double ci = __shfl(cs, i, 64), si = __shfl(sn, i, 64);
+        const double x1 = qr[r * D + i], x2 = qr[r * D + i + H2];
+        qv[k] = c < H2 ? (float)(x1 * ci - x2 * si) : (float)(x1 * si + x2 * ci);
       }
-      __syncthreads();
-      // s_j = scale q_hat_P . k_hat_{r,j} + b_hat_{r,j}: 4 waves split d, then sum
-      {
-        const int j = threadIdx.x & 63, part = threadIdx.x >> 6;
-        const int cq = d / 4;
-        float acc = 0.0f;
-        if (j < C)
-          for (int c = part * cq; c < (part + 1) * cq; ++c) acc += sm.qh[r][c] * sm.k[j][c];
-        sm.w[part][j] = acc;  // scratch (reused below)
-      }
-      __syncthreads();
-      if (threadIdx.x < 64) {
-        const int j = threadIdx.x;
-        float s = -INFINITY, dot = 0.0f;
-        if (j < C) {
-          dot = (sm.w[0][j] + sm.w[1][j]) + (sm.w[2][j] + sm.w[3][j]);
-          s = dot * P.scale + P.bhat_ch[((int64_t)gi * P.ncap_ch + ch0 + j) * R + r];
-        }
-        const float m = wave_max(s);
-        const float e = j < C ? expf(s - m) : 0.0f;
-        const float sum = wave_sum(e);
-        const float w = e / sum;
-        const float wdot = wave_sum(j < C ? w * dot * P.scale : 0.0f);
-        if (j < C) sm.z[0][j] = w;
-        if (j == 0) { sm.F[0] = m + logf(sum); sm.wz[0] = wdot; }
-      }
-      __syncthreads();
-      float* kh = P.khat + (((int64_t)gi * P.ncap + n) * R + r) * d;
-      for (int c = threadIdx.x; c < d; c += blockDim.x) {
-        float acc = 0.0f;
-        for (int j = 0; j < C; ++j) acc += sm.z[0][j] * sm.k[j][c];
-        kh[c] = acc;
-      }
-      if (threadIdx.x == 0)
-        P.bhat[((int64_t)gi * P.ncap + n) * R + r] = sm.F[0] - sm.wz[0];
-      __syncthreads();
     }
+    // logits s_j = scale q.k_hat_{r,j} + b_hat_{r,j}
+    float sl[MT], dot[MT];
+    float M = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        acc = fmaf(v[t][q].x, qv[4 * q], acc);
+        acc = fmaf(v[t][q].y, qv[4 * q + 1], acc);
+        acc = fmaf(v[t][q].z, qv[4 * q + 2], acc);
+        acc = fmaf(v[t][q].w, qv[4 * q + 3], acc);
+      }
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      acc += __shfl_xor(acc, 4, 64);
+      acc += __shfl_xor(acc, 8, 64);
+      const int j = 4 * t + cg;
+      const float bj = __shfl(bl, j, 64);
+      dot[t] = acc * P.scale;
+      sl[t] = j < C ? dot[t] + bj : -INFINITY;
+      M = fmaxf(M, sl[t]);
+    }
+    M = fmaxf(M, __shfl_xor(M, 16, 64));
+    M = fmaxf(M, __shfl_xor(M, 32, 64));
+    float S = 0.0f, SW = 0.0f, ka[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) ka[k] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const float e = 4 * t + cg < C ? expf(sl[t] - M) : 0.0f;
+      S += e;
+      SW += e * dot[t];
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        ka[4 * q] = fmaf(e, v[t][q].x, ka[4 * q]);
+        ka[4 * q + 1] = fmaf(e, v[t][q].y, ka[4 * q + 1]);
+        ka[4 * q + 2] = fmaf(e, v[t][q].z, ka[4 * q + 2]);
+        ka[4 * q + 3] = fmaf(e, v[t][q].w, ka[4 * q + 3]);
+      }
+    }
+    S += __shfl_xor(S, 16, 64);
+    SW += __shfl_xor(SW, 16, 64);
+    S += __shfl_xor(S, 32, 64);
+    SW += __shfl_xor(SW, 32, 64);
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+      ka[k] += __shfl_xor(ka[k], 16, 64);
+      ka[k] += __shfl_xor(ka[k], 32, 64);
+    }
+    if (cg == 0) {
+      float* kh = P.khat + (((int64_t)gi * P.ncap + n) * R + r) * D + ds;
+#pragma unroll
+      for (int q = 0; q < NV; ++q)
+        *(float4*)(kh + 4 * q) = make_float4(ka[4 * q] / S, ka[4 * q + 1] / S,
+                                             ka[4 * q + 2] / S, ka[4 * q + 3] / S);
+    }
+    // b_hat = F - sum_j w_j z_j with F = M + log S and z_j = scale q.k_hat_{r,j}
+    if (lane == 0) P.bhat[((int64_t)gi * P.ncap + n) * R + r] = (M + logf(S)) - SW / S;
   }
 }
 
@@ -489,8 +522,10 @@ static void launch_level(const BuildParams& P, int64_t max_nodes, hipStream_t s)
   const int64_t lx = (7 * 256 + P.B * P.H_kv - 1) / (P.B * P.H_kv);
   const dim3 lgrid((unsigned)(gx < lx ? gx : lx), (unsigned)(P.B * P.H_kv));
   const bool mfma = P.kv_dtype == ZHA_BF16 && P.R <= 16 && (P.C == 16 || P.C == 32 || P.C == 64);
-  // parents are built one (node, plane) pair per workgroup iteration
-  const dim3 pgrid((unsigned)(gx * P.R > 65535 ? 65535 : gx * P.R), (unsigned)(P.B * P.H_kv));
+  // parents: one wave per (node, plane) pair, four waves per workgroup, about
+  // four workgroups per compute unit in all
+  const int64_t pw = (gx * P.R + 3) / 4, pmax = (1024 + P.B * P.H_kv - 1) / (P.B * P.H_kv);
+  const dim3 pgrid((unsigned)(pw < pmax ? pw : pmax), (unsigned)(P.B * P.H_kv));
   if (P.level == 1 && mfma) {
     const auto k = P.d == 128 ? (P.C == 64 ? build_leaves_mfma<128, 64>
                                  : P.C == 32 ? build_leaves_mfma<128, 32> : build_leaves_mfma<128, 16>)
@@ -500,7 +535,8 @@ static void launch_level(const BuildParams& P, int64_t max_nodes, hipStream_t s)
   } else if (P.level == 1)
     hipLaunchKernelGGL(build_leaves, grid, dim3(256), 0, s, P);
   else
-    hipLaunchKernelGGL(build_parents, pgrid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL(P.d == 128 ? build_parents<128> : build_parents<64>, pgrid, dim3(256), 0,
+                       s, P);
 }
 
 }  // namespace zha
