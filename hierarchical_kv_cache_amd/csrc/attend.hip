@@ -42,6 +42,7 @@ struct AttendParams {
   const int32_t* leaf_count;  // [BH] or null (dense)
   int32_t leaf_cap;
   float* part;                // [BHq][split_cap][d + 2]
+  int32_t* prefix;            // [BH + 1] group item prefix (pipelined kernel)
   int32_t* status;
   int32_t B, H_kv, G, C;
   int64_t T_cap;
@@ -701,8 +702,20 @@ __device__ inline void pipe_chunk_rows(const AttendParams& P, const PipeSmem<D, 
   hm = __builtin_amdgcn_readfirstlane(hm);
 }
 
+// The pipelined kernel gives workgroup w the contiguous items
+// [run_start(w), run_start(w + 1)) of the group-ordered item list (the grid is
+// clamped to the item count, so no range is empty).  Consecutive items of one
+// group fold into one running state, so a group's partials are one per
+// workgroup whose range meets it: slot w - run_owner(first item of the group).
+__device__ inline int run_start(int w, int total, int grid) {
+  return (int)((int64_t)total * w / grid);
+}
+__device__ inline int run_owner(int item, int total, int grid) {
+  return (int)(((int64_t)(item + 1) * grid - 1) / total);
+}
+
 template <int D, int GP>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, GP == 4 ? 2 : 1)
 attend_partial_bf16_pipe(AttendParams P) {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(GP == 4 || GP == 8 || GP == 16, "padded heads");
@@ -745,8 +758,12 @@ attend_partial_bf16_pipe(AttendParams P) {
     if (tid == 0) sm.item_prefix[BH] = total;
     __syncthreads();
   }
-  int item = blockIdx.x;
-  if (item >= total) return;
+  const int gridp = min((int)gridDim.x, total);
+  if ((int)blockIdx.x >= gridp) return;
+  if (blockIdx.x == 0)
+    for (int k = tid; k <= BH; k += blockDim.x) P.prefix[k] = sm.item_prefix[k];
+  int item = run_start(blockIdx.x, total, gridp);
+  const int item_end = run_start(blockIdx.x + 1, total, gridp);
 
   // ---- the first item: staged synchronously
   PipeItem it = pipe_item<D, GP>(P, sm, BH, item, cshift);
@@ -803,10 +820,20 @@ attend_partial_bf16_pipe(AttendParams P) {
     }
   }
 
+  // running state of the current run of same-group items
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.0f; }
+  float o[GP][8];
+#pragma unroll
+  for (int hh = 0; hh < GP; ++hh)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[hh][j] = 0.0f;
+
   for (;;) {
     // ---- prefetch what the next item needs besides K/V
-    const int next = item + gridDim.x;
-    const bool has_next = next < total;
+    const int next = item + 1;
+    const bool has_next = next < item_end;
     PipeItem nx = it;
     if (has_next) nx = pipe_item<D, GP>(P, sm, BH, next, cshift);
     const bool new_q = has_next && nx.gi != it.gi;
@@ -835,14 +862,6 @@ attend_partial_bf16_pipe(AttendParams P) {
     }
 
     // ---- the current item's chunks: chunk c+4's loads in flight while c computes
-    float m_run[4], l_run[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.0f; }
-    float o[GP][8];
-#pragma unroll
-    for (int hh = 0; hh < GP; ++hh)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[hh][j] = 0.0f;
     {
       const int64_t kv_base = (int64_t)it.gi * P.T_cap;
       const uint16_t* klane = (const uint16_t*)P.K + kv_base * D + (lane >> 4) * 8;
@@ -873,43 +892,55 @@ attend_partial_bf16_pipe(AttendParams P) {
                          (const uint16_t*)P.V + kv_base * D + (lane % LPR) * 8, lane, r0, nv, hm, cur);
     }
 
-    // ---- wave totals: l over the 16 key columns, o over the V row groups
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = l_run[i];
-      v += swz_xor<1>(v);
-      v += swz_xor<2>(v);
-      v += swz_xor<4>(v);
-      v += swz_xor<8>(v);
-      l_run[i] = v;
-    }
-#pragma unroll
-    for (int hh = 0; hh < GP; ++hh)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v = o[hh][j];
-        if (LPR <= 8) v += swz_xor<8>(v);
-        v += swz_xor<16>(v);
-        v += shfl_xor32(v);
-        o[hh][j] = v;
-      }
-    if ((lane & 15) == 0 && hrow < GP) {
+    // ---- the run ends at a group change or at the range's end: wave totals
+    // (l over the 16 key columns, o over the V row groups), then the partial
+    if (!has_next || new_q) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sm.state[wave][hrow + i][0] = m_run[i];
-        sm.state[wave][hrow + i][1] = l_run[i];
+        float v = l_run[i];
+        v += swz_xor<1>(v);
+        v += swz_xor<2>(v);
+        v += swz_xor<4>(v);
+        v += swz_xor<8>(v);
+        l_run[i] = v;
       }
-    }
-    if (lane < LPR) {
 #pragma unroll
       for (int hh = 0; hh < GP; ++hh)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sm.state[wave][hh][2 + lane * 8 + j] = o[hh][j];
+        for (int j = 0; j < 8; ++j) {
+          float v = o[hh][j];
+          if (LPR <= 8) v += swz_xor<8>(v);
+          v += swz_xor<16>(v);
+          v += shfl_xor32(v);
+          o[hh][j] = v;
+        }
+      if ((lane & 15) == 0 && hrow < GP) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sm.state[wave][hrow + i][0] = m_run[i];
+          sm.state[wave][hrow + i][1] = l_run[i];
+        }
+      }
+      if (lane < LPR) {
+#pragma unroll
+        for (int hh = 0; hh < GP; ++hh)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sm.state[wave][hh][2 + lane * 8 + j] = o[hh][j];
+      }
+      __syncthreads();
+      write_partial_state<D, GP>(P, sm.state, it.gi,
+                                  blockIdx.x - run_owner(sm.item_prefix[it.gi], total, gridp));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.0f; }
+#pragma unroll
+      for (int hh = 0; hh < GP; ++hh)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[hh][j] = 0.0f;
     }
-    __syncthreads();
-    write_partial_state<D, GP>(P, sm.state, it.gi, it.li);
     if (!has_next) break;
-    // ---- the next item's entries and queries into LDS
+    // ---- the next item's entries and queries into LDS, once every wave is
+    // done with the current item's
+    __syncthreads();
     if (!nx.tail && P.leaf_ids != nullptr && tid < nx.nent) {
       if (pf_id < 0 || pf_id >= sm.g_n1[nx.gi]) { pf_id = 0; pf_m = 0u; }
       sm.lid[tid] = pf_id;
@@ -1141,26 +1172,104 @@ __global__ void __launch_bounds__(64) attend_merge_final(const float* seg, float
   if (lane == 0) lse[head] = (L > 0.0f) ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
+// Merge of the pipelined kernel's partials: one workgroup per query head over
+// the head's runs (one per workgroup range that meets the group), waves taking
+// partials w, w+4, ..., lanes over dims, kMergeInFlight partials in flight per
+// wave, the four wave states added in a fixed order; writes out and lse.
+// Deterministic.
+template <int D>
+__global__ void __launch_bounds__(256) attend_merge_runs(AttendParams P, int grid, float* out,
+                                                         float* lse) {
+  constexpr int DPL = D / kWave;
+  constexpr int NW = 4;
+  constexpr int U = kMergeInFlight;
+  __shared__ float red[NW];
+  __shared__ float acc_o[NW][D];
+  __shared__ float acc_l[NW];
+  const int head = blockIdx.x;              // b * Hq + j
+  const int gi = head / P.G;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int BH = P.B * P.H_kv;
+  const int total = P.prefix[BH];
+  const int gridp = min(grid, total);
+  const int n = run_owner(P.prefix[gi + 1] - 1, total, gridp) -
+                run_owner(P.prefix[gi], total, gridp) + 1;
+  const float* base = P.part + (int64_t)head * P.split_cap * (D + 2);
+  float M = -INFINITY;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, base[(int64_t)i * (D + 2)]);
+  M = block_max_f<NW>(M, red);
+  float l = 0.0f, o[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) o[j] = 0.0f;
+  if (M != -INFINITY) {
+    for (int i0 = wave; i0 < n; i0 += NW * U) {
+      float mi[U], li[U], oi[U][DPL];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NW;
+        const float* pi = base + (int64_t)(i < n ? i : 0) * (D + 2);
+        mi[u] = (i < n) ? pi[0] : -INFINITY;
+        li[u] = pi[1];
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) oi[u][j] = pi[2 + lane + j * kWave];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = exp2f(mi[u] - M);      // 0 for an empty or absent partial
+        l += (w != 0.0f) ? li[u] * w : 0.0f;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) o[j] += (w != 0.0f) ? oi[u][j] * w : 0.0f;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) acc_o[wave][lane + j * kWave] = o[j];
+  if (lane == 0) acc_l[wave] = l;
+  __syncthreads();
+  float L = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) L += acc_l[w];
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float Ov = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Ov += acc_o[w][c];
+    out[(int64_t)head * D + c] = (L > 0.0f) ? Ov / L : 0.0f;
+  }
+  if (threadIdx.x == 0) lse[head] = (L > 0.0f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
 // ---------------------------------------------------------------- host
+
+// The pipelined kernel (bf16, dense or chunks of at least 16 keys) folds its
+// items into runs and is merged by attend_merge_runs; the other kernels write
+// one partial per item and are merged in two levels.
+inline bool pipelined(const AttendParams& P, int kv_dtype) {
+  return kv_dtype == ZHA_BF16 && (P.leaf_ids == nullptr || P.C >= 16);
+}
 
 template <int D, int GP>
 static void launch_partial(const AttendParams& P, int kv_dtype, int grid, hipStream_t s) {
-  const bool contig = (P.leaf_ids == nullptr) || (P.C >= 16);
-  if (kv_dtype == ZHA_BF16) {
-    if (contig)
-      hipLaunchKernelGGL((attend_partial_bf16_pipe<D, GP>), dim3(grid), dim3(256), 0, s, P);
-    else
-      hipLaunchKernelGGL((attend_partial_bf16<D, GP, false>), dim3(grid), dim3(256), 0, s, P);
-  } else {
+  if (pipelined(P, kv_dtype))
+    hipLaunchKernelGGL((attend_partial_bf16_pipe<D, GP>), dim3(grid), dim3(256), 0, s, P);
+  else if (kv_dtype == ZHA_BF16)
+    hipLaunchKernelGGL((attend_partial_bf16<D, GP, false>), dim3(grid), dim3(256), 0, s, P);
+  else
     hipLaunchKernelGGL((attend_partial_f32<D, GP>), dim3(grid), dim3(256), 0, s, P);
-  }
 }
 
 template <int D>
-static void launch_partial_g(const AttendParams& P, int kv_dtype, int grid, hipStream_t s) {
+static void launch_attend(const AttendParams& P, int kv_dtype, int grid, int BHq, float* seg,
+                          float* out, float* lse, hipStream_t s) {
   if (P.G <= 4) launch_partial<D, 4>(P, kv_dtype, grid, s);
   else if (P.G <= 8) launch_partial<D, 8>(P, kv_dtype, grid, s);
   else launch_partial<D, 16>(P, kv_dtype, grid, s);
+  if (pipelined(P, kv_dtype)) {
+    hipLaunchKernelGGL((attend_merge_runs<D>), dim3(BHq), dim3(256), 0, s, P, grid, out, lse);
+  } else {
+    hipLaunchKernelGGL((attend_merge_seg<D>), dim3(BHq, kMergeSegs), dim3(256), 0, s, P, seg);
+    hipLaunchKernelGGL((attend_merge_final<D>), dim3(BHq), dim3(64), 0, s, (const float*)seg,
+                       out, lse);
+  }
 }
 
 static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
@@ -1188,6 +1297,7 @@ static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
   P.leaf_cap = cfg->leaf_cap;
   P.part = (float*)((char*)ws + w.attend_off);
   float* seg = (float*)((char*)ws + w.merge_off);
+  P.prefix = (int32_t*)((char*)ws + w.prefix_off);
   P.status = (int32_t*)ws;
   P.B = cfg->B; P.H_kv = cfg->H_kv; P.G = cfg->G; P.C = cfg->C;
   P.T_cap = cfg->T_cap;
@@ -1197,15 +1307,10 @@ static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
   const int64_t max_items = (int64_t)cfg->B * cfg->H_kv * w.split_cap;
   const int grid = (int)(max_items < kAttendGrid ? max_items : kAttendGrid);
   const int BHq = cfg->B * cfg->H_kv * cfg->G;
-  if (cfg->d == 64) {
-    launch_partial_g<64>(P, cfg->kv_dtype, grid, s);
-    hipLaunchKernelGGL((attend_merge_seg<64>), dim3(BHq, kMergeSegs), dim3(256), 0, s, P, seg);
-    hipLaunchKernelGGL((attend_merge_final<64>), dim3(BHq), dim3(64), 0, s, (const float*)seg, out, lse);
-  } else {
-    launch_partial_g<128>(P, cfg->kv_dtype, grid, s);
-    hipLaunchKernelGGL((attend_merge_seg<128>), dim3(BHq, kMergeSegs), dim3(256), 0, s, P, seg);
-    hipLaunchKernelGGL((attend_merge_final<128>), dim3(BHq), dim3(64), 0, s, (const float*)seg, out, lse);
-  }
+  if (cfg->d == 64)
+    launch_attend<64>(P, cfg->kv_dtype, grid, BHq, seg, out, lse, s);
+  else
+    launch_attend<128>(P, cfg->kv_dtype, grid, BHq, seg, out, lse, s);
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
 }
 

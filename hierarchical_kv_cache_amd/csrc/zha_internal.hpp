@@ -37,6 +37,7 @@ struct WsLayout {
   int64_t stage_cap = 0;
   int32_t split_cap = 0;   // partial slots per query head
   size_t merge_off = 0;    // merged segment states [B*Hq][kMergeSegments][d+2]
+  size_t prefix_off = 0;   // attend items: per-group prefix [B*H_kv + 1] (int32)
 };
 
 constexpr int kTileKeys = 64;       // keys per attend tile
@@ -97,6 +98,8 @@ inline WsLayout ws_layout(const zha_cfg& c) {
   off = align_up(off + (size_t)BHq * w.split_cap * (c.d + kPartPad) * 4, 256);
   w.merge_off = off;
   off = align_up(off + (size_t)BHq * kMergeSegments * (c.d + kPartPad) * 4, 256);
+  w.prefix_off = off;
+  off = align_up(off + (size_t)(BH + 1) * 4, 256);
   w.attend_bytes = off - w.attend_off;
   w.total = off;
   return w;

@@ -173,3 +173,43 @@ def test_zha_attend_matches_oracle_on_key_set(kvd, d, G, H_kv, B, C, frac):
     zha.attend(cfg, q, K, V, T, ids.to(DEV), mask.to(DEV), count.to(DEV), out3, lse3, ws)
     torch.cuda.synchronize()
     assert torch.equal(out, out3) and torch.equal(lse, lse3)
+
+
+def test_attend_folded_runs_across_groups():
+    """More work items than workgroups: each workgroup folds a contiguous run of
+    items into one state, and runs cross group boundaries.  Dense and routed
+    attention at ~1000 items over 6 groups of different lengths, then a short
+    call on the same workspace (the merge must read only this call's runs)."""
+    B, H_kv, G, d, C = 2, 3, 4, 128, 64
+    T_cap = 200_000
+    Tlist = [196_613, 150_001]
+    K, V = _cache(B, H_kv, T_cap, d, torch.bfloat16, seed=41, T_fill=max(Tlist))
+    cfg = zha.Config(B=B, H_kv=H_kv, G=G, d=d, C=C, L=2, R=4, T_cap=T_cap, kv_dtype=zha.BF16)
+    q = torch.randn(B, cfg.Hq, d, generator=torch.Generator().manual_seed(9)).to(DEV)
+    T = torch.tensor(Tlist, dtype=torch.int64, device=DEV)
+    ws = zha.new_workspace(cfg)
+    out = torch.empty(B, cfg.Hq, d, device=DEV)
+    lse = torch.empty(B, cfg.Hq, device=DEV)
+    zha.dense_attend(cfg, q, K, V, T, out, lse, ws)
+    torch.cuda.synchronize()
+    _dense_check(cfg, q, K, V, Tlist, out, lse, TOL["bf16"])
+
+    rng = np.random.default_rng(17)
+    sets = [_random_sets(rng, Tlist[b] // C, cfg.Hq, 0.7) for b in range(B)]
+    ids, mask, count = lists_from_sets(sets, B, H_kv, G, cfg.leaf_cap)
+    zha.attend(cfg, q, K, V, T, ids.to(DEV), mask.to(DEV), count.to(DEV), out, lse, ws)
+    torch.cuda.synchronize()
+    Kh, Vh, qh = f64(K), f64(V), f64(q)
+    for b in range(B):
+        for j in range(cfg.Hq):
+            keys = O.routed_keys(sets[b][j], Tlist[b], C)
+            o_ref, l_ref = O.attend_keys(qh[b, j], Kh[b, j // G], Vh[b, j // G], keys, cfg.scale)
+            assert rel_err(out[b, j].cpu().numpy(), o_ref) <= TOL["bf16"], (b, j)
+            assert abs(lse[b, j].item() - l_ref) <= 1e-4 * max(1.0, abs(l_ref))
+
+    short = [5000, 3]
+    T.copy_(torch.tensor(short, dtype=torch.int64))
+    zha.dense_attend(cfg, q, K, V, T, out, lse, ws)
+    torch.cuda.synchronize()
+    _dense_check(cfg, q, K, V, short, out, lse, TOL["bf16"])
+    assert zha.ws_status(ws) == 0
