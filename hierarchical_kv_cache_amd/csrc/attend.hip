@@ -168,17 +168,16 @@ __device__ inline int find_group(const int32_t* prefix, int BH, int item) {
   return lo;
 }
 
-// WG-level merge of the per-wave states into one partial per query head.
-template <int D, int NH>
-__device__ inline void write_partial_state(const AttendParams& P,
-                                           const float (*state)[NH][D + 2], int gi,
-                                           int item) {
+// WG-level merge of the per-wave states into one partial per query head;
+// st(w, g, c) reads entry c of head g of wave w's state.
+template <int D, typename ST>
+__device__ inline void write_partial_state(const AttendParams& P, ST st, int gi, int item) {
   const int G = P.G;
   for (int idx = threadIdx.x; idx < G * (D + 2); idx += blockDim.x) {
     const int g = idx / (D + 2), c = idx % (D + 2);
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWavesPerWg; ++w) M = fmaxf(M, state[w][g][0]);
+    for (int w = 0; w < kWavesPerWg; ++w) M = fmaxf(M, st(w, g, 0));
     float v;
     if (c == 0) {
       v = M;
@@ -187,8 +186,8 @@ __device__ inline void write_partial_state(const AttendParams& P,
       if (M != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < kWavesPerWg; ++w) {
-          const float mw = state[w][g][0];
-          if (mw != -INFINITY) v += state[w][g][c] * exp2f(mw - M);
+          const float mw = st(w, g, 0);
+          if (mw != -INFINITY) v += st(w, g, c) * exp2f(mw - M);
         }
       }
     }
@@ -200,7 +199,7 @@ __device__ inline void write_partial_state(const AttendParams& P,
 template <int D>
 __device__ inline void write_partial(const AttendParams& P, AttendSmem<D>& sm, int gi,
                                      int item) {
-  write_partial_state<D, 16>(P, sm.state, gi, item);
+  write_partial_state<D>(P, [&](int w, int g, int c) { return sm.state[w][g][c]; }, gi, item);
 }
 
 // Online-softmax state of one wave for the bf16 path.  Scores arrive in MFMA
@@ -234,15 +233,23 @@ struct WaveSoftmax {
 constexpr float kLazy = 8.0f;
 constexpr int kItemKeys = kTilesPerItem * kTileKeys;   // 1024
 
+// A wave's LDS: the current chunk's V rows (bf16, rows padded by 32 bytes so
+// the transposing reads spread over the banks), or, once the wave's chunks are
+// done, its (m, l, o) state for the workgroup merge.  16-byte aligned: the rows
+// are written 16 bytes at a time and read 8 at a time.
+template <int D, int GP>
+union __attribute__((aligned(16))) WaveBuf {
+  uint16_t vt[16][D + 16];
+  float state[GP][D + 2];
+};
+
 template <int D, int GP>
 struct AttendSmemB {
   int32_t item_prefix[kMaxGroups + 1];
   int32_t scan[16];
   int32_t lid[kItemKeys / 2 + 2];               // leaf ids of the item (C >= 2)
   uint32_t lmask[kItemKeys / 2 + 2];
-  float p[kWavesPerWg][16][GP];                 // probabilities per key, head
-  float alpha[kWavesPerWg][16];
-  float state[kWavesPerWg][GP][D + 2];
+  WaveBuf<D, GP> wb[kWavesPerWg];
 };
 
 // Where the keys of one work item come from.
@@ -332,89 +339,99 @@ __device__ inline void load_chunk_rows(const uint16_t* klane, const uint16_t* vl
   buf.kmask = kr < nv ? hm : 0u;
 }
 
-template <int D, int GP, typename SM>
-__device__ inline void compute_chunk(SM& sm, const ChunkBuf<D>& buf,
-                                     const bf16x8_t* a_hi, const bf16x8_t* a_lo,
-                                     int lane, int wave,
-                                     float* m_run, float* l_run, float (*o)[8]) {
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));   // bf16 bits
+
+// One 16-key chunk of a wave.  QK^T runs with K as the A operand, so lane l
+// holds the scores of head l % 16 for keys 4(l/16) + i (i < 4): exactly the A
+// operand layout of P V (16x16x16 MFMA, rows = heads, k = keys).  P enters as
+// two bf16 terms (hi + lo, ~2^-17 relative).  V's B operand comes from the
+// wave's LDS tile by a transposing read: lane m addresses 4 dims of row m / 4,
+// and receives dims 16t + m % 16 of rows 4(m / 16) .. + 3.  o[t][i] is the
+// output of head 4(l/16) + i, dim 16t + l % 16.  m_run, l_run belong to head
+// l % 16 (l_run: this lane's keys only).
+template <int D, int GP>
+__device__ inline void compute_chunk(WaveBuf<D, GP>& wb, const ChunkBuf<D>& buf,
+                                     const bf16x8_t* a_hi, const bf16x8_t* a_lo, int lane,
+                                     float& m_run, float& l_run, f32x4_t (&o)[D / 16]) {
   constexpr int KSTEPS = D / 32, LPR = D / 8, RPI = kWave / LPR, VL = 16 / RPI;
-  const int hrow = (lane >> 4) * 4;
+  const int h = lane & 15, k0 = (lane >> 4) * 4;
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
     const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, buf.k[s]);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[s], kb, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[s], kb, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, a_hi[s], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, a_lo[s], acc, 0, 0, 0);
   }
-  // acc[i]: head hrow+i, key lane%16
-  float cm[4];
-  bool need = false;
+  float cm = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const bool ok = (buf.kmask >> (hrow + i)) & 1u;
-    const float sc = ok ? acc[i] : -INFINITY;
-    acc[i] = sc;
-    float v = sc;
-    v = fmaxf(v, swz_xor<1>(v));
-    v = fmaxf(v, swz_xor<2>(v));
-    v = fmaxf(v, swz_xor<4>(v));
-    v = fmaxf(v, swz_xor<8>(v));
-    cm[i] = v;
-    need = need || (v > m_run[i] + kLazy);
+    const uint32_t km = __shfl(buf.kmask, k0 + i, 64);   // key k0+i's head mask
+    acc[i] = ((km >> h) & 1u) ? acc[i] : -INFINITY;
+    cm = fmaxf(cm, acc[i]);
   }
+  cm = fmaxf(cm, swz_xor<16>(cm));
+  cm = fmaxf(cm, shfl_xor32(cm));
+  const bool need = cm > m_run + kLazy;
   if (__ballot(need) != 0ull) {           // wave-uniform: raise some running maxima
-    float al[4];
+    const float mnew = need ? cm : m_run;
+    const float al = (mnew == -INFINITY) ? 1.0f : exp2f(m_run - mnew);
+    l_run *= al;
+    m_run = mnew;
+    float ar[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float mnew = (cm[i] > m_run[i] + kLazy) ? cm[i] : m_run[i];
-      al[i] = (mnew == -INFINITY) ? 1.0f : exp2f(m_run[i] - mnew);
-      l_run[i] *= al[i];
-      m_run[i] = mnew;
-    }
-    if ((lane & 15) == 0 && hrow < GP) {
-      const f32x4_t av = {al[0], al[1], al[2], al[3]};
-      *(f32x4_t*)&sm.alpha[wave][hrow] = av;
-    }
-    wave_lds_sync();
+    for (int i = 0; i < 4; ++i) ar[i] = __shfl(al, k0 + i, 64);   // heads of o's rows
 #pragma unroll
-    for (int q4 = 0; q4 < GP / 4; ++q4) {
-      const f32x4_t av = *(const f32x4_t*)&sm.alpha[wave][q4 * 4];
+    for (int t = 0; t < D / 16; ++t)
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[q4 * 4 + hh][j] *= av[hh];
-    }
+      for (int i = 0; i < 4; ++i) o[t][i] *= ar[i];
   }
-  f32x4_t pv4;
+  bf16x4_t p_hi, p_lo;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float pv = (acc[i] == -INFINITY) ? 0.0f : exp2f(acc[i] - m_run[i]);
-    pv4[i] = pv;
-    l_run[i] += pv;
+    const float pv = (acc[i] == -INFINITY) ? 0.0f : exp2f(acc[i] - m_run);
+    l_run += pv;
+    const uint16_t hi = f32_to_bf16_rne(pv);
+    p_hi[i] = (short)hi;
+    p_lo[i] = (short)f32_to_bf16_rne(pv - __uint_as_float((uint32_t)hi << 16));
   }
-  if (hrow < GP) *(f32x4_t*)&sm.p[wave][lane & 15][hrow] = pv4;
-  wave_lds_sync();
+  // the chunk's V rows into the tile; rows of keys nobody attends are zero
 #pragma unroll
   for (int i = 0; i < VL; ++i) {
-    const int key = RPI * i + lane / LPR;
-    float vf[8];
-    const bool ok = (buf.vok >> i) & 1u;   // rows of keys nobody attends may hold anything
+    const bool ok = (buf.vok >> i) & 1u;
+    u32x4_t v = buf.v[i];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w = ok ? buf.v[i][j] : 0u;
-      vf[2 * j] = bf16_lo(w);
-      vf[2 * j + 1] = bf16_hi(w);
-    }
-#pragma unroll
-    for (int q4 = 0; q4 < GP / 4; ++q4) {
-      const f32x4_t pp = *(const f32x4_t*)&sm.p[wave][key][q4 * 4];
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[q4 * 4 + hh][j] += pp[hh] * vf[j];
-    }
+    for (int j = 0; j < 4; ++j) v[j] = ok ? v[j] : 0u;
+    *(u32x4_t*)&wb.vt[RPI * i + lane / LPR][(lane % LPR) * 8] = v;
   }
   wave_lds_sync();
+  typedef __attribute__((address_space(3))) __bf16 lds_bf16_t;
+  typedef __bf16 bf16x4v_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
+  typedef __attribute__((address_space(3))) bf16x4v_t lds_bf16x4_t;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    lds_bf16x4_t* src = (lds_bf16x4_t*)(lds_bf16_t*)(&wb.vt[lane >> 2][16 * t + 4 * (lane & 3)]);
+    const bf16x4_t vb = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(src));
+    o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi, vb, o[t], 0, 0, 0);
+    o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo, vb, o[t], 0, 0, 0);
+  }
+  wave_lds_sync();                        // the next chunk's rows overwrite the tile
+}
+
+// A wave's totals into its LDS state: l summed over the four key groups (o is
+// already summed over the keys by the MFMA).
+template <int D, int GP>
+__device__ inline void wave_state_out(WaveBuf<D, GP>& wb, int lane, float m_run, float l_run,
+                                      const f32x4_t (&o)[D / 16]) {
+  float l = l_run;
+  l += swz_xor<16>(l);
+  l += shfl_xor32(l);
+  if (lane < GP) { wb.state[lane][0] = m_run; wb.state[lane][1] = l; }
+  const int h0 = (lane >> 4) * 4, c = lane & 15;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (h0 + i < GP) wb.state[h0 + i][2 + 16 * t + c] = o[t][i];
 }
 
 template <int D, int GP, bool CONTIG>
@@ -431,7 +448,6 @@ attend_partial_bf16(AttendParams P) {
   const int wave = threadIdx.x >> 6;
   const int BH = P.B * P.H_kv;
   const uint32_t full = (P.G >= 32) ? 0xffffffffu : ((1u << P.G) - 1u);
-  const int hrow = (lane >> 4) * 4;
   const int cshift = __ffs(P.C) - 1;
 
   // work items of every group, prefix-summed into LDS
@@ -511,14 +527,10 @@ attend_partial_bf16(AttendParams P) {
     }
     __syncthreads();
 
-    float m_run[4], l_run[4];
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4_t o[D / 16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.0f; }
-    float o[GP][8];
-#pragma unroll
-    for (int hh = 0; hh < GP; ++hh)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[hh][j] = 0.0f;
+    for (int t = 0; t < D / 16; ++t) o[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int64_t kv_base = (int64_t)gi * P.T_cap;
     if constexpr (CONTIG) {
@@ -561,7 +573,7 @@ attend_partial_bf16(AttendParams P) {
           chunk_src(c + kWavesPerWg, r0, nv, hm);
           load_chunk_rows<D>(klane, vlane, lane, r0, nv, hm, nxt);
         }
-        compute_chunk<D, GP>(sm, cur, a_hi, a_lo, lane, wave, m_run, l_run, o);
+        compute_chunk<D, GP>(sm.wb[wave], cur, a_hi, a_lo, lane, m_run, l_run, o);
         if (more) cur = nxt;
       }
     } else {
@@ -569,45 +581,13 @@ attend_partial_bf16(AttendParams P) {
       for (int k = wave; k < nchunks; k += kWavesPerWg) {
         ChunkBuf<D> A;
         load_chunk_any<D>(P, sm, g, it, k, full, kv_base, lane, A);
-        compute_chunk<D, GP>(sm, A, a_hi, a_lo, lane, wave, m_run, l_run, o);
+        compute_chunk<D, GP>(sm.wb[wave], A, a_hi, a_lo, lane, m_run, l_run, o);
       }
     }
 
-    // wave totals: l over the 16 key columns, o over the V row groups
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = l_run[i];
-      v += swz_xor<1>(v);
-      v += swz_xor<2>(v);
-      v += swz_xor<4>(v);
-      v += swz_xor<8>(v);
-      l_run[i] = v;
-    }
-#pragma unroll
-    for (int hh = 0; hh < GP; ++hh)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v = o[hh][j];
-        if (LPR <= 8) v += swz_xor<8>(v);
-        v += swz_xor<16>(v);
-        v += shfl_xor32(v);
-        o[hh][j] = v;
-      }
-    if ((lane & 15) == 0 && hrow < GP) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sm.state[wave][hrow + i][0] = m_run[i];
-        sm.state[wave][hrow + i][1] = l_run[i];
-      }
-    }
-    if (lane < LPR) {
-#pragma unroll
-      for (int hh = 0; hh < GP; ++hh)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sm.state[wave][hh][2 + lane * 8 + j] = o[hh][j];
-    }
+    wave_state_out<D, GP>(sm.wb[wave], lane, m_run, l_run, o);
     __syncthreads();
-    write_partial_state<D, GP>(P, sm.state, gi, li);
+    write_partial_state<D>(P, [&](int w, int g, int c) { return sm.wb[w].state[g][c]; }, gi, li);
     __syncthreads();
   }
 }
@@ -637,9 +617,7 @@ struct PipeSmem {
   int32_t lid[kItemKeys / 16 + 2];   // leaf entries of the current item (C >= 16)
   uint32_t lmask[kItemKeys / 16 + 2];
   float qs[GP * D];                  // the current group's queries, times scale*log2(e)
-  float p[kWavesPerWg][16][GP];
-  float alpha[kWavesPerWg][16];
-  float state[kWavesPerWg][GP][D + 2];
+  WaveBuf<D, GP> wb[kWavesPerWg];
 };
 
 struct PipeItem {
@@ -715,7 +693,7 @@ __device__ inline int run_owner(int item, int total, int grid) {
 }
 
 template <int D, int GP>
-__global__ void __launch_bounds__(256, GP == 4 ? 2 : 1)
+__global__ void __launch_bounds__(256, 2)
 attend_partial_bf16_pipe(AttendParams P) {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(GP == 4 || GP == 8 || GP == 16, "padded heads");
@@ -729,7 +707,6 @@ attend_partial_bf16_pipe(AttendParams P) {
   const int wave = tid >> 6;
   const int BH = P.B * P.H_kv;
   const uint32_t full = (P.G >= 32) ? 0xffffffffu : ((1u << P.G) - 1u);
-  const int hrow = (lane >> 4) * 4;
   const int cshift = __ffs(P.C) - 1;
 
   // ---- per-group geometry and the item prefix, once per workgroup
@@ -821,14 +798,10 @@ attend_partial_bf16_pipe(AttendParams P) {
   }
 
   // running state of the current run of same-group items
-  float m_run[4], l_run[4];
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4_t o[D / 16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.0f; }
-  float o[GP][8];
-#pragma unroll
-  for (int hh = 0; hh < GP; ++hh)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[hh][j] = 0.0f;
+  for (int t = 0; t < D / 16; ++t) o[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (;;) {
     // ---- prefetch what the next item needs besides K/V
@@ -878,7 +851,7 @@ attend_partial_bf16_pipe(AttendParams P) {
           pipe_chunk_rows<D, GP>(P, sm, it, c + kWavesPerWg, cshift, full, eid, em, r0, nv, hm);
           load_chunk_rows<D>(klane, vlane, lane, r0, nv, hm, nxt);
         }
-        compute_chunk<D, GP>(sm, cur, a_hi, a_lo, lane, wave, m_run, l_run, o);
+        compute_chunk<D, GP>(sm.wb[wave], cur, a_hi, a_lo, lane, m_run, l_run, o);
         if (more) cur = nxt;
       }
     }
@@ -892,50 +865,17 @@ attend_partial_bf16_pipe(AttendParams P) {
                          (const uint16_t*)P.V + kv_base * D + (lane % LPR) * 8, lane, r0, nv, hm, cur);
     }
 
-    // ---- the run ends at a group change or at the range's end: wave totals
-    // (l over the 16 key columns, o over the V row groups), then the partial
+    // ---- the run ends at a group change or at the range's end: the wave's
+    // totals, then the workgroup's partial
     if (!has_next || new_q) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = l_run[i];
-        v += swz_xor<1>(v);
-        v += swz_xor<2>(v);
-        v += swz_xor<4>(v);
-        v += swz_xor<8>(v);
-        l_run[i] = v;
-      }
-#pragma unroll
-      for (int hh = 0; hh < GP; ++hh)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float v = o[hh][j];
-          if (LPR <= 8) v += swz_xor<8>(v);
-          v += swz_xor<16>(v);
-          v += shfl_xor32(v);
-          o[hh][j] = v;
-        }
-      if ((lane & 15) == 0 && hrow < GP) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sm.state[wave][hrow + i][0] = m_run[i];
-          sm.state[wave][hrow + i][1] = l_run[i];
-        }
-      }
-      if (lane < LPR) {
-#pragma unroll
-        for (int hh = 0; hh < GP; ++hh)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) sm.state[wave][hh][2 + lane * 8 + j] = o[hh][j];
-      }
+      wave_state_out<D, GP>(sm.wb[wave], lane, m_run, l_run, o);
       __syncthreads();
-      write_partial_state<D, GP>(P, sm.state, it.gi,
-                                  blockIdx.x - run_owner(sm.item_prefix[it.gi], total, gridp));
+      write_partial_state<D>(P, [&](int w, int g, int c) { return sm.wb[w].state[g][c]; }, it.gi,
+                             blockIdx.x - run_owner(sm.item_prefix[it.gi], total, gridp));
+      m_run = -INFINITY;
+      l_run = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.0f; }
-#pragma unroll
-      for (int hh = 0; hh < GP; ++hh)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[hh][j] = 0.0f;
+      for (int t = 0; t < D / 16; ++t) o[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
     if (!has_next) break;
     // ---- the next item's entries and queries into LDS, once every wave is
