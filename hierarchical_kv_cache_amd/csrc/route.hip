@@ -112,6 +112,20 @@ __device__ inline int32_t list_id(const ListRef& L, const ListGeo& g, int gi, in
   return (int32_t)(g.orph0 + (u - (int64_t)g.np * L.C));
 }
 
+// Node id and head mask of entry u, with the kept parents' ids and masks
+// staged in LDS (spid, spm) when given.
+__device__ inline void list_entry_staged(const ListRef& L, const ListGeo& g, int gi, int u,
+                                         const int32_t* spid, const uint32_t* spm,
+                                         int32_t& id, uint32_t& mask) {
+  if (spid == nullptr || L.ids != nullptr || u >= g.np * L.C) {
+    list_entry(L, g, gi, u, id, mask);
+    return;
+  }
+  const int pi = u >> L.cshift;
+  id = spid[pi] * L.C + (u & (L.C - 1));
+  mask = spm[pi];
+}
+
 struct LevelParams {
   const float* q;              // [BHq][d]
   const float* khat;           // [BH][ncap][R][d]
@@ -199,8 +213,11 @@ __device__ inline void load_group_queries(const LevelParams& P, int gi, int lane
 }
 
 // One wave scores list entry u (tree node `node`) of group gi for all G heads.
+// A head outside the entry's mask gets -inf (not its candidate); a candidate's
+// non-finite score is stored as -FLT_MAX, so -inf marks exactly the
+// non-candidates for the cut.
 template <int D, int GP>
-__device__ inline void score_node(const LevelParams& P, int gi, int node, int u,
+__device__ inline void score_node(const LevelParams& P, int gi, int node, uint32_t mask, int u,
                                   const float (&qv)[GP][4], int lane) {
   constexpr int LPR = D / 4;           // lanes per summary row
   constexpr int RPI = kWave / LPR;     // rows per load instruction
@@ -249,7 +266,9 @@ __device__ inline void score_node(const LevelParams& P, int gi, int node, int u,
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int g = lane * J + j;
-      if (g < P.G) P.scores[((int64_t)gi * P.G + g) * P.ucap + u] = sc[j];
+      if (g < P.G)
+        P.scores[((int64_t)gi * P.G + g) * P.ucap + u] =
+            ((mask >> g) & 1u) ? (isfinite(sc[j]) ? sc[j] : -FLT_MAX) : -INFINITY;
     }
   }
 }
@@ -258,6 +277,7 @@ template <int D, int GP>
 __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
   constexpr int kPidLds = 4096;
   __shared__ int32_t s_pid[kPidLds];   // the group's kept parents (implicit lists)
+  __shared__ uint32_t s_pm[kPidLds];   // and their head masks
   const int gi = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (blockIdx.x == 0 && threadIdx.x == 0) stale_check(P, gi);
@@ -265,22 +285,28 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
   const int U = geo.U;
   const bool staged = P.list.ids == nullptr && P.list.pids != nullptr && geo.np <= kPidLds;
   if (staged) {
-    for (int i = threadIdx.x; i < geo.np; i += blockDim.x)
+    for (int i = threadIdx.x; i < geo.np; i += blockDim.x) {
       s_pid[i] = P.list.pids[(int64_t)gi * P.list.pcap + i];
+      s_pm[i] = P.list.pmask[(int64_t)gi * P.list.pcap + i];
+    }
   }
   float qv[GP][4];
   load_group_queries<D, GP>(P, gi, lane, qv);
   __syncthreads();
   const int32_t* spid = staged ? s_pid : nullptr;
+  const uint32_t* spm = staged ? s_pm : nullptr;
   const int nwaves = gridDim.x * (blockDim.x >> 6);
-  // the next node id is fetched one iteration ahead, so a wave's summary loads
+  // the next entry is fetched one iteration ahead, so a wave's summary loads
   // never wait behind the id load that addresses them
   int u = blockIdx.x * (blockDim.x >> 6) + wave;
-  int32_t node_next = (u < U) ? list_id(P.list, geo, gi, u, spid) : 0;
+  int32_t node_next = 0;
+  uint32_t mask_next = 0u;
+  if (u < U) list_entry_staged(P.list, geo, gi, u, spid, spm, node_next, mask_next);
   for (; u < U; u += nwaves) {
     const int node = node_next;
-    if (u + nwaves < U) node_next = list_id(P.list, geo, gi, u + nwaves, spid);
-    score_node<D, GP>(P, gi, node, u, qv, lane);
+    const uint32_t mask = mask_next;
+    if (u + nwaves < U) list_entry_staged(P.list, geo, gi, u + nwaves, spid, spm, node_next, mask_next);
+    score_node<D, GP>(P, gi, node, mask, u, qv, lane);
   }
 }
 
@@ -527,15 +553,10 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
   const int U = geo.U;
   if (g == 0 && tid == 0 && P.ucount_out != nullptr) P.ucount_out[gi] = U;
   const float* sc = P.scores + (int64_t)head * P.ucap;
-  auto cmask = [&](int u) -> uint32_t {
-    int32_t id; uint32_t m;
-    list_entry(P.list, geo, gi, u, id, m);
-    return m;
-  };
+  // the scores mark this head's non-candidates with -inf (candidates are finite)
   uint8_t* out = P.sel ? P.sel + (int64_t)head * P.ucap : nullptr;
   uint64_t* bits = P.selbits ? P.selbits + (int64_t)head * P.nwcap : nullptr;
   const int nrow = (U + 63) >> 6;
-  const uint32_t bit = 1u << g;
   const bool lds = U <= kCutLds;
   uint32_t* skey = lds ? sm.st.key : P.stage + (int64_t)head * P.stage_cap * 2;
   float* sw = lds ? sm.st.w : (float*)(P.stage + (int64_t)head * P.stage_cap * 2 + P.stage_cap);
@@ -551,16 +572,14 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int u = j * kCutThreads + tid;
-      const int uu = u < U ? u : 0;         // in bounds: loads never wait on each other
-      const uint32_t m = cmask(uu);
-      const float sj = sc[uu];
-      sv[j] = (u < U && (m & bit)) ? sanitize(sj) : -INFINITY;
+      const float sj = sc[u < U ? u : 0];   // in bounds: loads never wait on each other
+      sv[j] = u < U ? sj : -INFINITY;
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) mx = fmaxf(mx, sv[j]);
   } else {
     for (int u = tid; u < U; u += kCutThreads)
-      if (cmask(u) & bit) mx = fmaxf(mx, sanitize(sc[u]));
+      mx = fmaxf(mx, sc[u]);
   }
   mx = block_max_f<NW>(mx, sm.redf);     // -inf: the head has no candidates
 
@@ -569,7 +588,7 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
     int kept = 0;
     for (int j0 = 0; j0 < U; j0 += kCutThreads) {
       const int u = j0 + tid;
-      const bool s1 = mx != -INFINITY && u < U && (cmask(u) & bit);
+      const bool s1 = mx != -INFINITY && u < U && sc[u] != -INFINITY;
       const uint64_t b = __ballot(s1);
       if (out && u < U) out[u] = s1 ? 1 : 0;
       const int row = (j0 >> 6) + wave;
@@ -753,8 +772,8 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
     for (int u = tid; u < U; u += kCutThreads) {
       uint32_t k = 0u;
       float w = 0.0f;
-      if (cmask(u) & bit) {
-        const float sc1 = sanitize(sc[u]);
+      if (sc[u] != -INFINITY) {
+        const float sc1 = sc[u];
         k = order_key(sc1);
         w = cut_mass(sc1, mx, P.topk);
         wsum += fixmass(w);
@@ -1011,7 +1030,7 @@ __global__ void __launch_bounds__(256) score_upper(UpperParams U) {
   for (int t = blockIdx.x * NW + wave; t < total; t += gridDim.x * NW) {
     int k = 0, node = t;
     while (node >= (int)upper_nodes(U, k, T)) { node -= (int)upper_nodes(U, k, T); ++k; }
-    score_node<D, GP>(upper_level_params(U, k), gi, node, node, qv, lane);
+    score_node<D, GP>(upper_level_params(U, k), gi, node, 0xffffffffu, node, qv, lane);
   }
 }
 
