@@ -202,6 +202,35 @@ def timed(fn):
     return e0.elapsed_time(e1)
 
 
+def percentile(v, q):
+    """The q-quantile of a non-empty list (nearest rank)."""
+    v = sorted(v)
+    return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+
+
+def step_latency(ev, K):
+    """Median and p90 over steps of route + attend (per-call events), with the
+    appends' total spread over the K steps."""
+    per = [a.elapsed_time(b) + c.elapsed_time(d) for (a, b), (c, d) in zip(ev["route"], ev["attend"])]
+    app = sum(a.elapsed_time(b) for a, b in ev["append"]) / K
+    return {"median_us": 1000 * (percentile(per, 0.5) + app),
+            "p90_us": 1000 * (percentile(per, 0.9) + app)}
+
+
+def copy_bandwidth():
+    """Device-to-device copy rate of a 1 GiB buffer, read + written bytes per second."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    reps = 5
+    ms = timed(lambda: [dst.copy_(src) for _ in range(reps)])
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * reps / (ms * 1e-3) / 1e9
+
+
 def bytes_of_step(wl, rec):
     """Algorithmic bytes of one routed step from its route counts: unique summary
     bytes scored per level, unique K/V bytes of the attended key set, q and out."""
@@ -345,6 +374,21 @@ def cpu_baseline(run, p, s):
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
+    # the same routed step with numpy's thread pools at every core of this process
+    ncores = len(os.sched_getaffinity(0))
+    ctx = threadpool_limits(limits=ncores) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        for g in range(wl.G):
+            rt = O.route(q[g], tree, t, wl.C, wl.L, p, wl.scale)
+            keys = O.routed_keys(rt.leaves, t, wl.C)
+            O.attend_keys(q[g], K, V, keys, wl.scale)
+        step_all_s = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
     groups = wl.B * wl.H_kv
     return {
         "value": step_s * groups * 1e6, "unit": "us/step", "cores": 1, "kind": "oracle",
@@ -352,6 +396,8 @@ def cpu_baseline(run, p, s):
                   f"numpy float64 single-threaded; x{groups} KV-head groups for a full step",
         "dense_us_per_step": dense_s * groups * 1e6,
         "tree_build_s_one_head": build_s,
+        "all_cores": {"value": step_all_s * groups * 1e6, "cores": ncores,
+                      "note": "the same sample with numpy's BLAS/OpenMP pools at every core"},
     }
 
 
@@ -405,6 +451,25 @@ def main():
     route_us = 1000 * sum(route_ms) / K
     log(f"[bench]   route {route_us:.1f} us (per-call events), attend {attend_us:.1f} us "
         f"(replayed), appends {len(append_ms)}")
+    warm = step_latency(ev, K)
+
+    # ---- cold steps: a 512 MB buffer is written before each step (untimed), so a
+    # step starts with nothing of its data in the 256 MB last-level cache
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    run.prefill()
+    run.routed_steps(0, W, p)
+    evc = {"route": [], "attend": [], "append": []}
+    for s in range(W, W + K):
+        flush.fill_(s & 0x7f)
+        run.routed_steps(s, s + 1, p, evc)
+    torch.cuda.synchronize()
+    cold = step_latency(evc, K)
+    del flush
+    torch.cuda.empty_cache()
+    log(f"[bench]   per step (events): warm median {warm['median_us']:.1f} p90 {warm['p90_us']:.1f} us; "
+        f"cold median {cold['median_us']:.1f} p90 {cold['p90_us']:.1f} us")
+    copy_gbps = copy_bandwidth()
+    log(f"[bench]   device copy {copy_gbps:.0f} GB/s")
 
     extra = {}
     # ---- p sweep (same steps, warm)
@@ -587,6 +652,13 @@ def main():
         "append_us_each": (1000 * sum(append_ms) / len(append_ms)) if append_ms else None,
         "appends_in_timed_steps": len(append_ms),
         "prefill_build_ms": build_ms,
+        "step_latency": {"warm": warm, "cold": cold,
+                         "note": "per-step route + attend from per-call events (queue markers add "
+                                 "a little), appends spread over the steps; cold: a 512 MB buffer "
+                                 "written before each step"},
+        "copy_GBps": copy_gbps,
+        "effective_frac_of_copy": (step_gbps / copy_gbps) if step_gbps else None,
+        "attend_frac_of_copy": (att_gbps / copy_gbps) if att_gbps else None,
         "effective_GBps_step": step_gbps,
         "route_GBps": rte_gbps,
         "attend_GBps": att_gbps,
