@@ -1,0 +1,80 @@
+"""The decode loop end to end on the GPU's own tree (gqa128k: 8 KV heads x 4 query
+heads, d = 128, bf16 K/V, 131,104 tokens at the start, C = 64, L = 3, R = 16,
+p = 0.9): each step appends a summary when a chunk completes (at step 32 here),
+routes and attends.  On sampled steps and KV heads the step is checked against
+the oracle run on that step's tree (the GPU's summaries, as fp32 values):
+routing level by level (near-tie allowances only), the route's final leaf sets,
+and the attention outputs over the sets the GPU routed."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.gpu_util import TOL, f64, rel_err, sets_from_lists
+from tests.test_gpu_route import level_sync_compare, upload
+
+pytestmark = pytest.mark.gpu
+zha = pytest.importorskip("hierarchical_kv_cache_amd.zha")
+DEV = "cuda"
+STEPS = 40
+CHECK_STEPS = (0, 31, 32, 33, 39)
+SAMPLED_KV_HEADS = (2, 7)
+
+
+def host_tree(dec, cfg, h, T):
+    """KV head h's built levels (sequence 0) as float64 arrays."""
+    out = []
+    for level in range(1, cfg.L + 1):
+        n = T // cfg.C ** level
+        out.append({"khat": f64(dec.tree.khat[level - 1][0, h, :n]),
+                    "bhat": f64(dec.tree.bhat[level - 1][0, h, :n])})
+    return out
+
+
+def test_decode_loop_append_route_attend():
+    wl = synth.WORKLOADS["gqa128k"]
+    T0, C, p = wl.T0, wl.C, wl.p
+    T_cap = T0 + STEPS + C
+    K, V = synth.make_cache(wl.with_(steps=STEPS), DEV, T_cap)
+    qref = synth.make_qref(wl, DEV)
+    cfg = zha.Config(B=1, H_kv=wl.H_kv, G=wl.G, d=wl.d, C=C, L=wl.L, R=wl.R, T_cap=T_cap)
+    dec = zha.Decoder(cfg, qref, DEV)
+    Tt = torch.tensor([T0], dtype=torch.int64, device=DEV)
+    dec.prefill(K, V, Tt)
+    appends = 0
+    for s in range(STEPS):
+        T = T0 + s
+        Tt.fill_(T)
+        if T % C == 0:
+            dec.append(K, V, Tt, 1)
+            appends += 1
+        q = synth.make_query(wl, s, T, DEV)
+        out, lse = dec.step(q, K, V, Tt, p)
+        torch.cuda.synchronize()
+        assert zha.ws_status(dec.ws) == 0, s
+        if s not in CHECK_STEPS:
+            continue
+        assert dec.tree.n_built[:, 0].tolist() == [T // C ** l for l in range(1, cfg.L + 1)]
+        gpu_sets = sets_from_lists(dec.leaves.ids, dec.leaves.mask, dec.leaves.count, cfg.G)
+        for h in SAMPLED_KV_HEADS:
+            trees = [[host_tree(dec, cfg, h, T)]]
+            cfg1 = zha.Config(B=1, H_kv=1, G=cfg.G, d=cfg.d, C=C, L=cfg.L, R=cfg.R, T_cap=T)
+            tree1 = upload(cfg1, trees, T)
+            ws1 = zha.new_workspace(cfg1)
+            q1 = q[:, h * cfg.G:(h + 1) * cfg.G].contiguous()
+            report = []
+            leaves = level_sync_compare(cfg1, tree1, trees, q1, T, p, ws1, report)
+            for g in range(cfg.G):
+                np.testing.assert_array_equal(gpu_sets[0][h * cfg.G + g], leaves[0][g])
+            for r in report:
+                print("allowed:", s, h, r)
+            Kh, Vh, qh = f64(K[0, h, :T]), f64(V[0, h, :T]), f64(q[0])
+            for g in range(cfg.G):
+                j = h * cfg.G + g
+                keys = O.routed_keys(gpu_sets[0][j], T, C)
+                o_ref, lse_ref = O.attend_keys(qh[j], Kh, Vh, keys, cfg.scale)
+                assert rel_err(f64(out[0, j]), o_ref) <= TOL["bf16"], (s, h, g)
+                assert abs(float(lse[0, j]) - lse_ref) <= 1e-3 * max(1.0, abs(lse_ref)), (s, h, g)
+            del tree1, ws1
+    assert appends == 1
