@@ -441,7 +441,6 @@ attend_partial_bf16(AttendParams P) {
   static_assert(GP == 4 || GP == 8 || GP == 16, "padded heads");
   constexpr int KSTEPS = D / 32;
   constexpr int LPR = D / 8;
-  constexpr int RPI = kWave / LPR;
   __shared__ AttendSmemB<D, GP> sm;
 
   const int lane = threadIdx.x & 63;
@@ -608,44 +607,63 @@ attend_partial_bf16(AttendParams P) {
 
 template <int D, int GP>
 struct PipeSmem {
-  int32_t item_prefix[kMaxGroups + 1];
+  int32_t chunk_prefix[kMaxGroups + 1];   // group-ordered offsets of the groups' chunks
   int32_t g_U[kMaxGroups];           // leaf-list entries (dense: complete leaves)
   int32_t g_n1[kMaxGroups];          // complete leaves
   int32_t g_open[kMaxGroups];        // open-chunk length T - C n1
-  uint32_t g_smask[kMaxGroups];      // heads that take the sink from the tail item
+  uint32_t g_smask[kMaxGroups];      // heads that take the sink from the tail
   int32_t scan[16];
-  int32_t lid[kItemKeys / 16 + 2];   // leaf entries of the current item (C >= 16)
-  uint32_t lmask[kItemKeys / 16 + 2];
+  int32_t lid[2][kItemKeys / 16 + 2];    // leaf entries of the current / next segment (C >= 16)
+  uint32_t lmask[2][kItemKeys / 16 + 2];
   float qs[GP * D];                  // the current group's queries, times scale*log2(e)
   WaveBuf<D, GP> wb[kWavesPerWg];
 };
 
+constexpr int kItemChunks = kItemKeys / 16;   // 16-key chunks of a work item
+
+// One segment of a workgroup's range: chunks of one group inside one work item
+// (1024 list keys), or of the group's tail (the sink chunk, then the open chunk
+// in 16-row pieces).
 struct PipeItem {
-  int gi, li;
-  int tail;          // the sink + open-chunk item
-  int64_t kbase;     // first list key (regular items)
-  int nkeys;         // list keys in the item (regular items)
-  int64_t first;     // first leaf entry of the item
+  int gi;
+  int tail;          // 1: tail chunks
+  int c0;            // tail: first tail chunk (0 is the sink)
+  int64_t kbase;     // first list key (list segments)
+  int nkeys;         // list keys in the segment
+  int64_t first;     // first leaf entry of the segment
   int nent;          // leaf entries touched
   int nchunks;
 };
 
+// Chunks of group gi's leaf list (16 keys each; the last one may be partial).
 template <int D, int GP>
-__device__ inline PipeItem pipe_item(const AttendParams& P, const PipeSmem<D, GP>& sm, int BH,
-                                     int item, int cshift) {
+__device__ inline int list_chunks(const PipeSmem<D, GP>& sm, int gi, int cshift) {
+  return (int)((((int64_t)sm.g_U[gi] << cshift) + 15) / 16);
+}
+
+// The segment starting at global chunk cur, clipped to the range end c_end.
+template <int D, int GP>
+__device__ inline PipeItem pipe_seg(const AttendParams& P, const PipeSmem<D, GP>& sm, int BH,
+                                    int cur, int c_end, int cshift) {
   PipeItem it;
-  it.gi = find_group(sm.item_prefix, BH, item);
-  it.li = item - sm.item_prefix[it.gi];
-  const int items = sm.item_prefix[it.gi + 1] - sm.item_prefix[it.gi];
-  it.tail = (it.li == items - 1) ? 1 : 0;
-  it.kbase = 0; it.nkeys = 0; it.first = 0; it.nent = 0;
-  if (it.tail) {
-    it.nchunks = 1 + (sm.g_open[it.gi] + 15) / 16;
+  it.gi = find_group(sm.chunk_prefix, BH, cur);
+  const int base = sm.chunk_prefix[it.gi];
+  const int local = cur - base;
+  const int lim = min(c_end, sm.chunk_prefix[it.gi + 1]) - base;   // local end in range
+  const int nlist = list_chunks<D, GP>(sm, it.gi, cshift);
+  it.kbase = 0; it.nkeys = 0; it.first = 0; it.nent = 0; it.c0 = 0;
+  if (local >= nlist) {
+    it.tail = 1;
+    it.c0 = local - nlist;
+    it.nchunks = lim - local;
   } else {
-    it.kbase = (int64_t)it.li * kItemKeys;
+    it.tail = 0;
+    const int iend = min((local / kItemChunks + 1) * kItemChunks, nlist);
+    it.nchunks = min(iend, lim) - local;
+    it.kbase = (int64_t)local * 16;
     const int64_t left = ((int64_t)sm.g_U[it.gi] << cshift) - it.kbase;
-    it.nkeys = (int)(left < kItemKeys ? left : kItemKeys);
-    it.nchunks = (it.nkeys + 15) / 16;
+    const int64_t span = (int64_t)it.nchunks * 16;
+    it.nkeys = (int)(left < span ? left : span);
     if (P.leaf_ids != nullptr) {
       it.first = it.kbase >> cshift;
       it.nent = (int)(((it.kbase + it.nkeys - 1) >> cshift) - it.first + 1);
@@ -654,17 +672,18 @@ __device__ inline PipeItem pipe_item(const AttendParams& P, const PipeSmem<D, GP
   return it;
 }
 
-// Rows of chunk c of an item: row0 .. row0+nv-1 of the group under head mask hm.
-// ent_id / ent_mask: the leaf entry covering the chunk (sparse regular items).
+// Rows of chunk c of a segment: row0 .. row0+nv-1 of the group under head mask
+// hm.  ent_id / ent_mask: the leaf entry covering the chunk (sparse list segments).
 template <int D, int GP>
 __device__ inline void pipe_chunk_rows(const AttendParams& P, const PipeSmem<D, GP>& sm,
                                        const PipeItem& it, int c, int cshift, uint32_t full,
                                        int32_t ent_id, uint32_t ent_mask,
                                        int64_t& row0, int& nv, uint32_t& hm) {
   if (it.tail) {
-    if (c == 0) { row0 = 0; nv = 1; hm = sm.g_smask[it.gi]; }
+    const int tc = it.c0 + c;
+    if (tc == 0) { row0 = 0; nv = 1; hm = sm.g_smask[it.gi]; }
     else {
-      const int off = 16 * (c - 1);
+      const int off = 16 * (tc - 1);
       row0 = ((int64_t)sm.g_n1[it.gi] << cshift) + off;
       nv = min(16, sm.g_open[it.gi] - off);
       hm = full;
@@ -680,16 +699,25 @@ __device__ inline void pipe_chunk_rows(const AttendParams& P, const PipeSmem<D, 
   hm = __builtin_amdgcn_readfirstlane(hm);
 }
 
-// The pipelined kernel gives workgroup w the contiguous items
-// [run_start(w), run_start(w + 1)) of the group-ordered item list (the grid is
-// clamped to the item count, so no range is empty).  Consecutive items of one
-// group fold into one running state, so a group's partials are one per
-// workgroup whose range meets it: slot w - run_owner(first item of the group).
+// The pipelined kernel gives workgroup w the contiguous chunks
+// [run_start(w), run_start(w + 1)) of the group-ordered chunk list (16 keys of a
+// group's leaf list, or a piece of its tail; the grid is clamped to the chunk
+// count, so no range is empty): the ranges differ by at most one chunk.
+// Consecutive segments of one group fold into one running state, so a group's
+// partials are one per workgroup whose range meets it: slot
+// w - run_owner(first chunk of the group).
 __device__ inline int run_start(int w, int total, int grid) {
   return (int)((int64_t)total * w / grid);
 }
-__device__ inline int run_owner(int item, int total, int grid) {
-  return (int)(((int64_t)(item + 1) * grid - 1) / total);
+__device__ inline int run_owner(int chunk, int total, int grid) {
+  return (int)(((int64_t)(chunk + 1) * grid - 1) / total);
+}
+// Workgroups that take a range: at most the launched ones, and few enough that
+// every range holds at least kMinRunChunks chunks (which bounds a group's
+// partials by the slots the workspace holds per head).
+__device__ inline int run_grid(int launched, int total) {
+  const int g = total / kMinRunChunks;
+  return max(1, min(launched, g));
 }
 
 template <int D, int GP>
@@ -709,7 +737,7 @@ attend_partial_bf16_pipe(AttendParams P) {
   const uint32_t full = (P.G >= 32) ? 0xffffffffu : ((1u << P.G) - 1u);
   const int cshift = __ffs(P.C) - 1;
 
-  // ---- per-group geometry and the item prefix, once per workgroup
+  // ---- per-group geometry and the chunk prefix, once per workgroup
   int total;
   {
     const int per = (BH + blockDim.x - 1) / blockDim.x;
@@ -719,38 +747,39 @@ attend_partial_bf16_pipe(AttendParams P) {
       const int gi = g0 + k;
       if (gi < BH) {
         const GroupInfo g = group_info(P, gi);
-        mine += g.items;
         sm.g_U[gi] = g.U;
         sm.g_n1[gi] = g.n1;
         sm.g_open[gi] = (int)(g.T - (int64_t)g.n1 * P.C);
         sm.g_smask[gi] = sink_mask(P, gi, g, full);
+        mine += list_chunks<D, GP>(sm, gi, cshift) + 1 + (sm.g_open[gi] + 15) / 16;
       }
     }
     int acc = block_exclusive_scan<int>(mine, sm.scan, &total);
     for (int k = 0; k < per; ++k)
       if (g0 + k < BH) {
-        sm.item_prefix[g0 + k] = acc;
-        acc += sm.g_U[g0 + k] >= 0 ? (int)((((int64_t)sm.g_U[g0 + k] << cshift) + kTileKeys - 1) / kTileKeys + kTilesPerItem - 1) / kTilesPerItem + 1 : 1;
+        sm.chunk_prefix[g0 + k] = acc;
+        acc += list_chunks<D, GP>(sm, g0 + k, cshift) + 1 + (sm.g_open[g0 + k] + 15) / 16;
       }
-    if (tid == 0) sm.item_prefix[BH] = total;
+    if (tid == 0) sm.chunk_prefix[BH] = total;
     __syncthreads();
   }
-  const int gridp = min((int)gridDim.x, total);
+  const int gridp = run_grid((int)gridDim.x, total);
   if ((int)blockIdx.x >= gridp) return;
   if (blockIdx.x == 0)
-    for (int k = tid; k <= BH; k += blockDim.x) P.prefix[k] = sm.item_prefix[k];
-  int item = run_start(blockIdx.x, total, gridp);
-  const int item_end = run_start(blockIdx.x + 1, total, gridp);
+    for (int k = tid; k <= BH; k += blockDim.x) P.prefix[k] = sm.chunk_prefix[k];
+  int cur_c = run_start(blockIdx.x, total, gridp);
+  const int c_end = run_start(blockIdx.x + 1, total, gridp);
 
-  // ---- the first item: staged synchronously
-  PipeItem it = pipe_item<D, GP>(P, sm, BH, item, cshift);
+  // ---- the first segment: staged synchronously
+  PipeItem it = pipe_seg<D, GP>(P, sm, BH, cur_c, c_end, cshift);
+  int pb = 0;   // leaf-entry buffer of the current segment
   if (!it.tail && P.leaf_ids != nullptr && tid < it.nent) {
     const int64_t off = (int64_t)it.gi * P.leaf_cap + it.first + tid;
     int32_t leaf = P.leaf_ids[off];
     uint32_t m = P.leaf_mask[off] & full;
     if (leaf < 0 || leaf >= sm.g_n1[it.gi]) { leaf = 0; m = 0u; }
-    sm.lid[tid] = leaf;
-    sm.lmask[tid] = m;
+    sm.lid[pb][tid] = leaf;
+    sm.lmask[pb][tid] = m;
   }
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
@@ -788,7 +817,7 @@ attend_partial_bf16_pipe(AttendParams P) {
       int32_t eid = 0; uint32_t em = 0u;
       if (!it.tail && P.leaf_ids != nullptr) {
         const int loc = (int)(((it.kbase + 16 * wave) >> cshift) - it.first);
-        eid = sm.lid[loc]; em = sm.lmask[loc];
+        eid = sm.lid[pb][loc]; em = sm.lmask[pb][loc];
       }
       pipe_chunk_rows<D, GP>(P, sm, it, wave, cshift, full, eid, em, r0, nv, hm);
       const int64_t kv_base = (int64_t)it.gi * P.T_cap;
@@ -797,18 +826,18 @@ attend_partial_bf16_pipe(AttendParams P) {
     }
   }
 
-  // running state of the current run of same-group items
+  // running state of the current run of same-group segments
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4_t o[D / 16];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) o[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (;;) {
-    // ---- prefetch what the next item needs besides K/V
-    const int next = item + 1;
-    const bool has_next = next < item_end;
+    // ---- prefetch what the next segment needs besides K/V
+    const int next_c = cur_c + it.nchunks;
+    const bool has_next = next_c < c_end;
     PipeItem nx = it;
-    if (has_next) nx = pipe_item<D, GP>(P, sm, BH, next, cshift);
+    if (has_next) nx = pipe_seg<D, GP>(P, sm, BH, next_c, c_end, cshift);
     const bool new_q = has_next && nx.gi != it.gi;
     int32_t pf_id = 0;
     uint32_t pf_m = 0u;
@@ -823,7 +852,7 @@ attend_partial_bf16_pipe(AttendParams P) {
       const int idx = tid + 256 * k;
       pf_q[k] = (new_q && idx < P.G * D) ? P.q[(int64_t)nx.gi * P.G * D + idx] : 0.0f;
     }
-    // this wave's first chunk of the next item: its leaf entry
+    // this wave's first chunk of the next segment: its leaf entry
     int32_t nf_id = 0;
     uint32_t nf_m = 0u;
     if (has_next && !nx.tail && P.leaf_ids != nullptr && wave < nx.nchunks) {
@@ -834,7 +863,7 @@ attend_partial_bf16_pipe(AttendParams P) {
       if (nf_id < 0 || nf_id >= sm.g_n1[nx.gi]) { nf_id = 0; nf_m = 0u; }
     }
 
-    // ---- the current item's chunks: chunk c+4's loads in flight while c computes
+    // ---- the current segment's chunks: chunk c+4's loads in flight while c computes
     {
       const int64_t kv_base = (int64_t)it.gi * P.T_cap;
       const uint16_t* klane = (const uint16_t*)P.K + kv_base * D + (lane >> 4) * 8;
@@ -845,7 +874,7 @@ attend_partial_bf16_pipe(AttendParams P) {
           int32_t eid = 0; uint32_t em = 0u;
           if (!it.tail && P.leaf_ids != nullptr) {
             const int loc = (int)(((it.kbase + 16 * (c + kWavesPerWg)) >> cshift) - it.first);
-            eid = sm.lid[loc]; em = sm.lmask[loc];
+            eid = sm.lid[pb][loc]; em = sm.lmask[pb][loc];
           }
           int64_t r0; int nv; uint32_t hm;
           pipe_chunk_rows<D, GP>(P, sm, it, c + kWavesPerWg, cshift, full, eid, em, r0, nv, hm);
@@ -856,7 +885,7 @@ attend_partial_bf16_pipe(AttendParams P) {
       }
     }
 
-    // ---- issue the next item's first chunk before merging this one
+    // ---- issue the next segment's first chunk before merging this one
     if (has_next && wave < nx.nchunks) {
       int64_t r0; int nv; uint32_t hm;
       pipe_chunk_rows<D, GP>(P, sm, nx, wave, cshift, full, nf_id, nf_m, r0, nv, hm);
@@ -864,39 +893,47 @@ attend_partial_bf16_pipe(AttendParams P) {
       load_chunk_rows<D>((const uint16_t*)P.K + kv_base * D + (lane >> 4) * 8,
                          (const uint16_t*)P.V + kv_base * D + (lane % LPR) * 8, lane, r0, nv, hm, cur);
     }
+    // ---- the next segment's entries into the other buffer: nobody reads it
+    // (its last readers, two segments back, passed the previous barrier)
+    if (has_next && !nx.tail && P.leaf_ids != nullptr && tid < nx.nent) {
+      if (pf_id < 0 || pf_id >= sm.g_n1[nx.gi]) { pf_id = 0; pf_m = 0u; }
+      sm.lid[pb ^ 1][tid] = pf_id;
+      sm.lmask[pb ^ 1][tid] = pf_m & full;
+    }
 
     // ---- the run ends at a group change or at the range's end: the wave's
     // totals, then the workgroup's partial
     if (!has_next || new_q) {
       wave_state_out<D, GP>(sm.wb[wave], lane, m_run, l_run, o);
       __syncthreads();
-      write_partial_state<D>(P, [&](int w, int g, int c) { return sm.wb[w].state[g][c]; }, it.gi,
-                             blockIdx.x - run_owner(sm.item_prefix[it.gi], total, gridp));
+      const int slot = blockIdx.x - run_owner(sm.chunk_prefix[it.gi], total, gridp);
+      if (slot < P.split_cap)
+        write_partial_state<D>(P, [&](int w, int g, int c) { return sm.wb[w].state[g][c]; },
+                               it.gi, slot);
+      else if (tid == 0)
+        set_status(P.status, ZHA_ECAPACITY);
       m_run = -INFINITY;
       l_run = 0.0f;
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) o[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
     if (!has_next) break;
-    // ---- the next item's entries and queries into LDS, once every wave is
-    // done with the current item's
+    // every wave is done with this segment (its LDS tiles, states and leaf
+    // entries); the next segment's entries are visible after this barrier
     __syncthreads();
-    if (!nx.tail && P.leaf_ids != nullptr && tid < nx.nent) {
-      if (pf_id < 0 || pf_id >= sm.g_n1[nx.gi]) { pf_id = 0; pf_m = 0u; }
-      sm.lid[tid] = pf_id;
-      sm.lmask[tid] = pf_m & full;
-    }
     if (new_q) {
+      // a new group's queries: every wave is past the previous staging's reads
 #pragma unroll
       for (int k = 0; k < QPT; ++k) {
         const int idx = tid + 256 * k;
         if (idx < GP * D) sm.qs[idx] = pf_q[k] * P.qscale;
       }
+      __syncthreads();
+      convert_q();
     }
-    __syncthreads();
-    if (new_q) convert_q();
-    item = next;
+    cur_c = next_c;
     it = nx;
+    pb ^= 1;
   }
 }
 
@@ -1131,9 +1168,9 @@ __global__ void __launch_bounds__(256) attend_merge_runs(AttendParams P, int gri
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int BH = P.B * P.H_kv;
   const int total = P.prefix[BH];
-  const int gridp = min(grid, total);
-  const int n = run_owner(P.prefix[gi + 1] - 1, total, gridp) -
-                run_owner(P.prefix[gi], total, gridp) + 1;
+  const int gridp = run_grid(grid, total);
+  const int n = min(run_owner(P.prefix[gi + 1] - 1, total, gridp) -
+                    run_owner(P.prefix[gi], total, gridp) + 1, P.split_cap);
   const float* base = P.part + (int64_t)head * P.split_cap * (D + 2);
   float M = -INFINITY;
   for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, base[(int64_t)i * (D + 2)]);
@@ -1244,7 +1281,7 @@ static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
   P.split_cap = w.split_cap;
   P.qscale = cfg->scale * kLog2e;
   hipStream_t s = (hipStream_t)stream;
-  const int64_t max_items = (int64_t)cfg->B * cfg->H_kv * w.split_cap;
+  const int64_t max_items = (int64_t)cfg->B * cfg->H_kv * split_capacity(*cfg);
   const int grid = (int)(max_items < kAttendGrid ? max_items : kAttendGrid);
   const int BHq = cfg->B * cfg->H_kv * cfg->G;
   if (cfg->d == 64)

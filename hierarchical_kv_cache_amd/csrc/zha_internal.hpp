@@ -66,6 +66,13 @@ inline int32_t split_capacity(const zha_cfg& c) {
   return (int32_t)(ceil_div(tiles, kTilesPerItem) + 1);
 }
 
+// Partial slots per query head.  The pipelined attend folds each workgroup's
+// range of at least kMinRunChunks chunks (16 keys) into one partial per group it
+// meets: a group of items work items meets at most 2 * items such ranges.  The
+// other attend kernels write one partial per item.
+constexpr int kMinRunChunks = 32;
+inline int32_t run_capacity(const zha_cfg& c) { return 2 * split_capacity(c); }
+
 inline WsLayout ws_layout(const zha_cfg& c) {
   WsLayout w;
   const int64_t BH = (int64_t)c.B * c.H_kv, BHq = BH * c.G;
@@ -94,7 +101,7 @@ inline WsLayout ws_layout(const zha_cfg& c) {
   w.stage = off; off = align_up(off + (size_t)BHq * scap * 8, 256);
   w.route_bytes = off - w.route_off;
   w.attend_off = off;
-  w.split_cap = split_capacity(c);
+  w.split_cap = run_capacity(c);
   off = align_up(off + (size_t)BHq * w.split_cap * (c.d + kPartPad) * 4, 256);
   w.merge_off = off;
   off = align_up(off + (size_t)BHq * kMergeSegments * (c.d + kPartPad) * 4, 256);
