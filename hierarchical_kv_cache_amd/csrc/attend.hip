@@ -7,13 +7,16 @@
 // and Flash-Decoding (split the cache along its length, merge the splits).
 // [ASM] "방법론": two attention states merge as a = (Z_A a_A + Z_B a_B)/(Z_A + Z_B).
 //
-// Work decomposition (one GPU): a "group" is one (sequence, KV head); its leaf
-// list is cut into tiles of 64 keys and tiles into work items of 16 tiles; one
-// extra item per group holds the sink and the open chunk.  A persistent grid
-// walks all items of all groups; the 4 waves of a workgroup take alternate
-// tiles of an item and merge their states before writing one partial per query
-// head.  A group's K/V tile is read once for all G query heads of the group;
-// heads that did not select a leaf see its keys masked to -inf.
+// Work decomposition (one GPU): a "group" is one (sequence, KV head).  Its leaf
+// list is read in 16-key chunks, grouped into work items of 1024 keys; the sink
+// and the open chunk form the group's tail.  The pipelined kernel (bf16, dense
+// or leaves of C >= 16 keys) gives each workgroup of a persistent grid a
+// contiguous range of the group-ordered chunks and writes one partial per
+// query head for each group its range meets; the other kernels walk whole items
+// round-robin and write one partial per item.  The 4 waves of a workgroup take
+// alternate chunks and merge their states before a partial is written.  A
+// group's K/V chunk is read once for all G query heads of the group; heads that
+// did not select a leaf see its keys masked to -inf.
 //
 // Scores are kept in log2 units: q is pre-multiplied by scale * log2(e).  K/V
 // rows are read once per step and carry the non-temporal hint.
@@ -24,7 +27,6 @@ namespace zha {
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4_t __attribute__((__vector_size__(4 * sizeof(uint32_t))));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWavesPerWg = 4;
 constexpr int kMaxGroups = 2048;
@@ -42,7 +44,7 @@ struct AttendParams {
   const int32_t* leaf_count;  // [BH] or null (dense)
   int32_t leaf_cap;
   float* part;                // [BHq][split_cap][d + 2]
-  int32_t* prefix;            // [BH + 1] group item prefix (pipelined kernel)
+  int32_t* prefix;            // [BH + 1] group chunk prefix (pipelined kernel)
   int32_t* status;
   int32_t B, H_kv, G, C;
   int64_t T_cap;
@@ -202,23 +204,17 @@ __device__ inline void write_partial(const AttendParams& P, AttendSmem<D>& sm, i
   write_partial_state<D>(P, [&](int w, int g, int c) { return sm.state[w][g][c]; }, gi, item);
 }
 
-// Online-softmax state of one wave for the bf16 path.  Scores arrive in MFMA
-// output layout: lane holds heads 4*(lane/16)+i (i < 4) for slot lane%16 of each
-// 16-slot column block.
-struct WaveSoftmax {
-  float m[4], l[4];
-};
-
 // ---------------------------------------------------------------- bf16 path
 //
-// QK^T on MFMA 16x16x32 bf16: rows = the group's query heads (padded to 16),
-// columns = 16 keys, contraction over d in steps of 32.  The fp32 query (times
+// QK^T on MFMA 16x16x32 bf16: rows = 16 keys, columns = the group's query heads
+// (padded to 16), contraction over d in steps of 32.  The fp32 query (times
 // scale*log2e) is split into two bf16 parts hi + lo, whose sum carries it to
 // ~2^-17 relative (score error ~1e-4 at d = 128, far inside what bf16 keys
 // allow); both products accumulate in fp32.  Lane l supplies row/column l%16
 // and the 8 consecutive dims s*32 + (l/16)*8 of step s for both operands, so
-// each lane's K load is 16 contiguous bytes.  P V runs on VALU: lane owns 8
-// consecutive dims of a few key rows; V rows load 16 bytes per lane, coalesced.
+// each lane's K load is 16 contiguous bytes.  P V on MFMA 16x16x16 bf16 (see
+// compute_chunk); V rows load 16 bytes per lane, coalesced, and pass through
+// the wave's LDS tile.
 //
 // Each wave walks 16-key chunks of an item (chunks w, w+4, ...).  When every
 // chunk is 16 consecutive cache rows under one head mask (dense, or leaves of
@@ -591,19 +587,18 @@ attend_partial_bf16(AttendParams P) {
   }
 }
 
-// ------------------------------------------------ bf16 path, pipelined over items
+// ---------------------------------------------- bf16 path, pipelined over segments
 //
-// The contiguous-chunk kernel (dense, or leaves of C >= 16 keys).  Everything an
-// item needs besides its K/V rows is fetched while the previous item is being
-// computed, so a workgroup always has K/V loads in flight:
+// The contiguous-chunk kernel (dense, or leaves of C >= 16 keys).  Everything a
+// segment needs besides its K/V rows is fetched while the previous segment is
+// being computed, so a workgroup always has K/V loads in flight:
 //   * per-group geometry (list length, leaf count, open-chunk length, sink mask)
-//     is read once per workgroup into LDS;
-//   * the next item's leaf entries and, when its group changes, its queries are
-//     loaded into registers during the current item's chunk loop and moved to
-//     LDS after it;
-//   * each wave issues the K/V loads of its first chunk of the next item before
-//     the current item's per-wave states are merged and written.
-// Items are assigned round-robin (item = blockIdx.x + k * gridDim.x).
+//     and the chunk prefix are computed once per workgroup into LDS;
+//   * the next segment's leaf entries and, when its group changes, its queries
+//     are loaded into registers during the current segment's chunk loop and
+//     moved to LDS after it (leaf entries into the other of two buffers);
+//   * each wave issues the K/V loads of its first chunk of the next segment
+//     before the current run's per-wave states are merged and written.
 
 template <int D, int GP>
 struct PipeSmem {

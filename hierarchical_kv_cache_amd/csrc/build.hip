@@ -14,8 +14,10 @@
 // Reference queries are rotated (rotate-half pairs (i, i+d/2), angle
 // pos * base^(-2i/d), fp64 angles) to the node's first key position n * C^level.
 //
-// One workgroup builds one node (all R planes) at a time, staging the node's
-// keys (or its children's compressed keys) in LDS as fp32.  b_hat is formed as
+// Three kernels: build_leaves_mfma (bf16 keys, C in {16, 32, 64}): one wave per
+// leaf on the matrix cores; build_leaves (other geometries): one workgroup per
+// leaf, keys staged in LDS as fp32; build_parents: one wave per (node, plane)
+// pair, the children's planes in registers.  b_hat is formed as
 // F - sum_j w_j z_j, which equals F - scale q_hat.k_hat since k_hat = sum_j w_j k_j.
 #include "zha_internal.hpp"
 
@@ -61,8 +63,9 @@ __device__ inline void load_ref_queries(const BuildParams& P, int h, int64_t pos
 
 constexpr int kMaxD = 128, kMaxC = 64, kMaxR = 16;
 
+// LDS of build_leaves (one workgroup per leaf).
 struct BuildSmem {
-  float k[kMaxC][kMaxD + 1];     // node keys (leaf) or one plane of child keys
+  float k[kMaxC][kMaxD + 1];     // the leaf's keys (fp32)
   float qh[kMaxR][kMaxD + 1];    // reference queries of the node
   float z[kMaxR][kMaxC];         // logits
   float w[kMaxR][kMaxC];         // softmax weights

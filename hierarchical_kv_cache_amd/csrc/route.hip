@@ -18,7 +18,7 @@
 // Everything stays on the device between levels.
 //
 // The top-p cut needs only the threshold, not a full sort.  Candidates are
-// histogrammed (count and mass) over 2048 buckets of relative score
+// histogrammed by mass over 2048 buckets of relative score
 // floor((max s - s) * 64), which is monotone in the score, so every bucket holds
 // a contiguous stretch of the descending order; a block scan finds the bucket
 // where the running mass first reaches p * W, and only that bucket is sorted

@@ -37,7 +37,7 @@ struct WsLayout {
   int64_t stage_cap = 0;
   int32_t split_cap = 0;   // partial slots per query head
   size_t merge_off = 0;    // merged segment states [B*Hq][kMergeSegments][d+2]
-  size_t prefix_off = 0;   // attend items: per-group prefix [B*H_kv + 1] (int32)
+  size_t prefix_off = 0;   // pipelined attend: per-group chunk prefix [B*H_kv + 1] (int32)
 };
 
 constexpr int kTileKeys = 64;       // keys per attend tile
