@@ -213,3 +213,38 @@ def test_attend_folded_runs_across_groups():
     torch.cuda.synchronize()
     _dense_check(cfg, q, K, V, short, out, lse, TOL["bf16"])
     assert zha.ws_status(ws) == 0
+
+
+@pytest.mark.parametrize("Tlist", [[37, 0, 65, 1, 129, 64, 3, 200], [700, 5, 1300, 64, 2, 999, 64, 31]])
+def test_attend_many_small_groups(Tlist):
+    """8 sequences x 8 KV heads of short, unequal lengths (0, 1, exactly C, ...):
+    workgroup ranges span many groups' tails, the range floor leaves few
+    workgroups busy, and every group's partials are merged.  Dense and routed."""
+    B, H_kv, G, d, C = 8, 8, 4, 128, 64
+    T_cap = 1408
+    K, V = _cache(B, H_kv, T_cap, d, torch.bfloat16, seed=5, T_fill=max(Tlist))
+    cfg = zha.Config(B=B, H_kv=H_kv, G=G, d=d, C=C, L=2, R=4, T_cap=T_cap, kv_dtype=zha.BF16)
+    q = torch.randn(B, cfg.Hq, d, generator=torch.Generator().manual_seed(21)).to(DEV)
+    T = torch.tensor(Tlist, dtype=torch.int64, device=DEV)
+    ws = zha.new_workspace(cfg)
+    out = torch.empty(B, cfg.Hq, d, device=DEV)
+    lse = torch.empty(B, cfg.Hq, device=DEV)
+    zha.dense_attend(cfg, q, K, V, T, out, lse, ws)
+    torch.cuda.synchronize()
+    _dense_check(cfg, q, K, V, Tlist, out, lse, TOL["bf16"])
+    rng = np.random.default_rng(3)
+    sets = [_random_sets(rng, Tlist[b] // C, cfg.Hq, 0.6) for b in range(B)]
+    ids, mask, count = lists_from_sets(sets, B, H_kv, G, cfg.leaf_cap)
+    zha.attend(cfg, q, K, V, T, ids.to(DEV), mask.to(DEV), count.to(DEV), out, lse, ws)
+    torch.cuda.synchronize()
+    Kh, Vh, qh = f64(K), f64(V), f64(q)
+    for b in range(B):
+        for j in range(cfg.Hq):
+            keys = O.routed_keys(sets[b][j], Tlist[b], C)
+            if len(keys) == 0:
+                assert np.all(out[b, j].cpu().numpy() == 0) and lse[b, j].item() == -math.inf
+                continue
+            o_ref, l_ref = O.attend_keys(qh[b, j], Kh[b, j // G], Vh[b, j // G], keys, cfg.scale)
+            assert rel_err(out[b, j].cpu().numpy(), o_ref) <= TOL["bf16"], (b, j)
+            assert abs(lse[b, j].item() - l_ref) <= 1e-4 * max(1.0, abs(l_ref))
+    assert zha.ws_status(ws) == 0
