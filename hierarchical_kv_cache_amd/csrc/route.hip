@@ -412,18 +412,22 @@ __device__ inline void wave_sort_desc(uint64_t (&v)[NR], int lane) {
   bitonic_merge_all<NR, 2>(v, lane);
 }
 
-constexpr int kRelBuckets = 2048;
-constexpr float kRelScale = 64.0f;     // buckets per unit of score
+constexpr int kRelBuckets = 4096;
+constexpr float kRelScale = 128.0f;    // buckets per unit of score (32 units in all)
 constexpr int kSortMax = 1024;         // largest crossing bucket sorted exactly
 static_assert(kSortMax == kCutThreads, "the crossing-bucket buffer is cleared one entry per thread");
+static_assert(kRelBuckets == 4 * kCutThreads, "each thread scans four buckets");
 
 // ---------------------------------------------------------------- compaction (A5)
 //
-// One workgroup per group, after the cut.  An entry of the level's union list is
-// kept when any head kept it, its mask being the OR of the heads' bits, read from the heads'
-// bitmaps (one 64-bit word per 64 entries); kept entries are written in list
+// After the cut.  An entry of the level's union list is kept when any head kept
+// it, its mask being the OR of the heads' bits, read from the heads' bitmaps
+// (one 64-bit word per row of 64 entries); kept entries are written in list
 // order (ascending ids) as the level's kept list -- the leaf list at level 1,
-// otherwise the parents of the next level's implicit list.
+// otherwise the parents of the next level's implicit list.  Workgroup x of a
+// group places rows [x R, x R + R), R = kCompactRows; it finds its first output
+// position by counting the kept entries of the rows before it itself, so the
+// workgroups never wait for one another.
 
 struct CompactParams {
   ListRef list;                  // this level's union list
@@ -435,92 +439,34 @@ struct CompactParams {
   int32_t* status;
 };
 
-constexpr int kCompactThreads = 1024;
-constexpr int kCompactWords = 8192;   // bitmap words staged in LDS per pass
-constexpr int kCompactPids = 4096;    // kept parents staged in LDS (implicit lists)
+constexpr int kCompactThreads = 256;
+constexpr int kCompactRows = 16;     // rows of 64 entries placed per workgroup
 
-// Compacts group gi's union list (blockDim.x == kCompactThreads); the LDS
-// scratch is kCompactWords words, kCompactThreads row offsets, kCompactPids
-// parent ids and NW scan slots.
-__device__ inline void compact_group(const CompactParams& P, int gi, uint64_t* words,
-                                     int32_t* rowoff, int32_t* s_pid, int32_t* scan) {
-  constexpr int NW = kCompactThreads / kWave;
-  constexpr int kPidLds = kCompactPids;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const ListGeo geo = list_geo(P.list, gi, P.ucap);
-  const int U = geo.U;
-  const int nrow = (U + 63) >> 6;
-  int32_t* ids = P.kids + (int64_t)gi * P.kcap;
-  uint32_t* msk = P.kmask + (int64_t)gi * P.kcap;
-  const uint64_t* hb = P.selbits + (int64_t)gi * P.G * P.nwcap;
-  const bool staged = P.list.ids == nullptr && P.list.pids != nullptr && geo.np <= kPidLds;
-  if (staged)
-    for (int i = tid; i < geo.np; i += kCompactThreads) s_pid[i] = P.list.pids[(int64_t)gi * P.list.pcap + i];
-  const int32_t* spid = staged ? s_pid : nullptr;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes below this one
-
-  // Rows of 64 entries, up to RP a pass.  Thread t loads row t's word of every
-  // head (into LDS) and counts the row's kept entries; a block scan gives each
-  // row's first output position; then wave w places the entries of rows w,
-  // w + 16, ..., lane l taking entry l, its mask the OR of the heads' bits.
-  const int RP = min(kCompactThreads, kCompactWords / P.G);
-  int base = 0;   // kept entries placed by earlier passes
-  for (int c0 = 0; c0 < nrow; c0 += RP) {
-    const int nr = min(RP, nrow - c0);
-    int cnt = 0;
-    if (tid < nr) {
-      const int r = c0 + tid;
-      const int valid = min(64, U - r * 64);
-      const uint64_t vmask = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
-      uint64_t any = 0ull;
-      for (int g = 0; g < P.G; ++g) {
-        const uint64_t w = hb[(int64_t)g * P.nwcap + r] & vmask;
-        words[g * RP + tid] = w;
-        any |= w;
-      }
-      cnt = __popcll(any);
-    }
-    int tot;
-    const int off = block_excl_scan<NW, int>(cnt, scan, &tot);
-    rowoff[tid] = base + off;
-    __syncthreads();
-    for (int i0 = wave; i0 < nr; i0 += 4 * NW) {
-      uint32_t m[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = i0 + k * NW;
-        uint32_t mk = 0u;
-        if (i < nr)
-          for (int g = 0; g < P.G; ++g) mk |= (uint32_t)((words[g * RP + i] >> lane) & 1ull) << g;
-        m[k] = mk;
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = i0 + k * NW;
-        const uint64_t bal = __ballot(m[k] != 0u);   // m[k] == 0 past the pass's rows
-        if (m[k] != 0u) {
-          const int p = rowoff[i] + __popcll(bal & lt);
-          if (p < P.kcap) { ids[p] = list_id(P.list, geo, gi, (c0 + i) * 64 + lane, spid); msk[p] = m[k]; }
-        }
-      }
-    }
-    base += tot;
-    __syncthreads();   // words and rowoff are reused by the next pass
-  }
-  if (tid == 0) {
-    if (base > P.kcap) set_status(P.status, ZHA_ECAPACITY);
-    P.kcount[gi] = base > P.kcap ? (int32_t)P.kcap : base;
-  }
+// Entries of row r kept by at least one head (bit l: entry 64 r + l; U entries).
+__device__ inline uint64_t kept_row(const uint64_t* hb, int64_t nwcap, int G, int r, int U) {
+  const int valid = U - r * 64;
+  const uint64_t vmask = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
+  uint64_t any = 0ull;
+  for (int g = 0; g < G; ++g) any |= hb[(int64_t)g * nwcap + r];
+  return any & vmask;
 }
 
 struct CutSmem {
-  struct { uint32_t key[kCutLds]; float w[kCutLds]; } st;   // general-path staging
   union {
-    unsigned long long relmass[kRelBuckets];
-    struct { uint32_t cnt[256]; unsigned long long mass[256]; } rad;
-    unsigned long long sortbuf[kSortMax];
+    struct {                                      // staged path
+      float sc[kCutReg * kCutThreads];            // the head's scores (-inf past U)
+      unsigned long long relmass[kRelBuckets];    // mass per relative-score bucket
+      unsigned long long ent[kSortMax];           // crossing bucket: key << 32 | ~u, 0 past it
+    } h;
+    struct {                                      // general path
+      uint32_t key[kCutLds];
+      float w[kCutLds];
+      uint32_t cnt[256];
+      unsigned long long mass[256];
+    } g;
   } u;
   float redf[16];
+  unsigned long long scan[16];
   unsigned long long redu[16];
   int32_t redi[16];
   uint32_t bucket;
@@ -541,47 +487,91 @@ __device__ inline int rel_bucket(float s, float mx) {
   return r >= (float)(kRelBuckets - 1) ? kRelBuckets - 1 : (int)r;
 }
 
+// One wave places the cut inside the crossing bucket: its entries (key << 32 |
+// ~u, zero past the last), 64 NR of them, are sorted by score descending then id
+// ascending; their masses are run in that order from `above`, the mass of every
+// bucket before it; the first entry whose running mass reaches target is the
+// cut.  Sets sm.ic (its position) and sm.cut_entry.
+template <int NR>
+__device__ inline void cut_in_bucket(CutSmem& sm, int cstar, float mx, int topk,
+                                     unsigned long long above, double target, int lane) {
+  uint64_t v[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) v[r] = (uint64_t)sm.u.h.ent[r * 64 + lane];
+  wave_sort_desc<NR>(v, lane);
+  int ic = -1;
+  unsigned long long carry = 0ull;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const uint64_t e = v[r];
+    unsigned long long mi = 0ull;
+    if ((uint32_t)(e >> 32) != 0u) mi = fixmass(cut_mass(key_score((uint32_t)(e >> 32)), mx, topk));
+    const unsigned long long inc = wave_incl_scan<unsigned long long>(mi) + carry;
+    const uint64_t reach = __ballot(mi != 0ull && (double)(above + inc) >= target);
+    if (ic < 0 && reach != 0ull) ic = r * 64 + __ffsll((long long)reach) - 1;
+    carry = rl64(inc, 63);
+  }
+  if (ic < 0 || ic > cstar - 1) ic = cstar - 1;
+  const int r_ic = ic >> 6, l_ic = ic & 63;
+  uint64_t ce = 0ull;
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+    if (r == r_ic) ce = rl64(v[r], l_ic);
+  if (lane == 0) { sm.ic = ic; sm.cut_entry = ce; }
+}
+
 // One workgroup cuts one query head.  The head's kept entries are written as a
 // bitmap (bit u % 64 of word u / 64; a wave's 64 consecutive entries are one
 // ballot) and, when sel is given, as bytes.
+//
+// The kernel runs once per level right after the scoring pass has streamed the
+// summaries through the caches, so its instructions are fetched cold: every
+// phase after the loads is a rolled loop over the scores staged in LDS, which
+// keeps the code that runs small.
 __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
   constexpr int NW = kCutThreads / kWave;
+  constexpr int PER = kCutReg;
   const int head = blockIdx.x;
   const int gi = head / P.G, g = head % P.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* sc = P.scores + (int64_t)head * P.ucap;
+  // The scores are loaded up to the list's capacity before its length is known,
+  // so these loads do not wait on the length's; entries past it are dropped.
+  // The scores mark this head's non-candidates with -inf (candidates are finite).
+  const int ucap = (int)(P.ucap < (int64_t)PER * kCutThreads ? P.ucap : (int64_t)PER * kCutThreads);
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    v[j] = -INFINITY;
+    if (j * kCutThreads < ucap) v[j] = sc[min(j * kCutThreads + tid, ucap - 1)];
+  }
   const ListGeo geo = list_geo(P.list, gi, P.ucap);
   const int U = geo.U;
   if (g == 0 && tid == 0 && P.ucount_out != nullptr) P.ucount_out[gi] = U;
-  const float* sc = P.scores + (int64_t)head * P.ucap;
-  // the scores mark this head's non-candidates with -inf (candidates are finite)
   uint8_t* out = P.sel ? P.sel + (int64_t)head * P.ucap : nullptr;
   uint64_t* bits = P.selbits ? P.selbits + (int64_t)head * P.nwcap : nullptr;
   const int nrow = (U + 63) >> 6;
-  const bool lds = U <= kCutLds;
-  uint32_t* skey = lds ? sm.st.key : P.stage + (int64_t)head * P.stage_cap * 2;
-  float* sw = lds ? sm.st.w : (float*)(P.stage + (int64_t)head * P.stage_cap * 2 + P.stage_cap);
-  if (tid == 0) { sm.nabove = 0; sm.count = 0; sm.first = kRelBuckets; }
-
-  // Lists that fit keep this thread's scores (entries j*1024 + tid) in registers
-  // across every pass; all loads are issued before any is used.
-  constexpr int PER = kCutReg;
-  const bool reg = U <= PER * kCutThreads;
-  float sv[PER];
+  const bool staged = U <= PER * kCutThreads;
+  const int nj = (U + kCutThreads - 1) / kCutThreads;   // rows of kCutThreads entries
+  if (tid == 0) { sm.nabove = 0; sm.count = 0; sm.first = kRelBuckets; sm.ic = kSortMax; sm.cut_entry = 0ull; }
   float mx = -INFINITY;
-  if (reg) {
+  if (staged) {
+    for (int i = tid; i < kRelBuckets; i += kCutThreads) sm.u.h.relmass[i] = 0ull;
+    sm.u.h.ent[tid] = 0ull;   // kSortMax == kCutThreads
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int u = j * kCutThreads + tid;
-      const float sj = sc[u < U ? u : 0];   // in bounds: loads never wait on each other
-      sv[j] = u < U ? sj : -INFINITY;
+      const float x = u < U ? v[j] : -INFINITY;
+      sm.u.h.sc[u] = x;
+      mx = fmaxf(mx, x);
     }
-#pragma unroll
-    for (int j = 0; j < PER; ++j) mx = fmaxf(mx, sv[j]);
   } else {
-    for (int u = tid; u < U; u += kCutThreads)
-      mx = fmaxf(mx, sc[u]);
+    for (int u = tid; u < U; u += kCutThreads) mx = fmaxf(mx, sc[u]);
   }
-  mx = block_max_f<NW>(mx, sm.redf);     // -inf: the head has no candidates
+  mx = wave_max_fast(mx);
+  if (lane == 0) sm.redf[wave] = mx;
+  __syncthreads();
+  for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm.redf[w]);   // -inf: the head has no candidates
 
   if (mx == -INFINITY || (P.topk == 0 && P.p >= 1.0f)) {
     // p >= 1 keeps every candidate; no candidates keeps nothing
@@ -601,53 +591,62 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
     return;
   }
 
-  if (reg) {
-    // ---- histogram of mass over relative-score buckets; W is its total
-    for (int i = tid; i < kRelBuckets; i += kCutThreads) sm.u.relmass[i] = 0ull;
+  if (staged) {
+    const float* ss = sm.u.h.sc;
+    // ---- mass per bucket of relative score floor((max - s) * kRelScale)
+#pragma unroll 4
+    for (int j = 0; j < nj; ++j) {
+      const float x = ss[j * kCutThreads + tid];
+      if (x != -INFINITY)
+        atomicAdd(&sm.u.h.relmass[rel_bucket(x, mx)], (unsigned long long)fixmass(cut_mass(x, mx, P.topk)));
+    }
     __syncthreads();
-    unsigned long long wsum = 0ull;
+    // ---- running mass in increasing bucket order (bucket b holds the scores
+    // just below those of buckets < b); thread t owns buckets 4t .. 4t+3.  The
+    // total is W, the sum of every candidate's mass.
+    unsigned long long m[4];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if (sv[j] != -INFINITY) {
-        const uint64_t fx = fixmass(cut_mass(sv[j], mx, P.topk));
-        wsum += fx;
-        atomicAdd(&sm.u.relmass[rel_bucket(sv[j], mx)], (unsigned long long)fx);
-      }
+    for (int i = 0; i < 4; ++i) m[i] = sm.u.h.relmass[4 * tid + i];
+    const unsigned long long own = (m[0] + m[1]) + (m[2] + m[3]);
+    const unsigned long long inc = wave_incl_scan<unsigned long long>(own);
+    if (lane == 63) sm.scan[wave] = inc;
+    __syncthreads();
+    unsigned long long run = inc - own, W = 0ull;
+    for (int w = 0; w < NW; ++w) {
+      const unsigned long long t = sm.scan[w];
+      run += (w < wave) ? t : 0ull;
+      W += t;
     }
-    const unsigned long long W = block_sum<NW, unsigned long long>(wsum, sm.redu);
     const double target = cut_target(P.p, P.topk, W);
-    // bucket b holds the scores just below those of buckets < b: running mass in
-    // increasing b; thread t owns buckets 2t and 2t+1
-    {
-      const unsigned long long m0 = sm.u.relmass[2 * tid], m1 = sm.u.relmass[2 * tid + 1];
-      unsigned long long tot;
-      const unsigned long long pre = block_excl_scan<NW, unsigned long long>(m0 + m1, sm.redu, &tot);
-      // exactly one bucket has its running mass cross p * W
-      const bool c0 = (double)pre < target && (double)(pre + m0) >= target;
-      const bool c1 = (double)(pre + m0) < target && (double)(pre + m0 + m1) >= target;
-      if (c0) { sm.first = 2 * tid; sm.above = pre; }
-      if (c1) { sm.first = 2 * tid + 1; sm.above = pre + m0; }
-      __syncthreads();
+    // exactly one bucket has its running mass cross p W
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if ((double)run < target && (double)(run + m[i]) >= target) { sm.first = 4 * tid + i; sm.above = run; }
+      run += m[i];
     }
+    __syncthreads();
     const int bstar = sm.first;
     const unsigned long long above_b = sm.above;
-    // ---- gather the crossing bucket as (key << 32 | ~u), sorted below by score
-    // descending then id ascending; count the candidates above it
-    sm.u.sortbuf[tid] = 0ull;               // kSortMax == kCutThreads
-    __syncthreads();
+    // ---- gather the crossing bucket; count the candidates above it
+    // (one slot reservation per wave and row: the lanes in the bucket take
+    // consecutive slots in lane order)
     int nab = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if (sv[j] != -INFINITY) {
-        const int b = rel_bucket(sv[j], mx);
-        if (b < bstar) {
-          ++nab;
-        } else if (b == bstar) {
-          const int u = j * kCutThreads + tid;
-          const int slot = atomicAdd(&sm.count, 1);
-          if (slot < kSortMax)
-            sm.u.sortbuf[slot] = ((unsigned long long)order_key(sv[j]) << 32) | (uint32_t)(~(uint32_t)u);
-        }
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes below this one
+#pragma unroll 4
+    for (int j = 0; j < nj; ++j) {
+      const int u = j * kCutThreads + tid;
+      const float x = ss[u];
+      const int b = x != -INFINITY ? rel_bucket(x, mx) : kRelBuckets;
+      nab += b < bstar ? 1 : 0;
+      const uint64_t inb = __ballot(b == bstar);
+      if (inb != 0ull) {                                  // uniform over the wave
+        const int leader = __ffsll((long long)inb) - 1;
+        int base = 0;
+        if (lane == leader) base = atomicAdd(&sm.count, __popcll(inb));
+        base = __shfl(base, leader, 64);
+        const int slot = base + __popcll(inb & lt);
+        if (b == bstar && slot < kSortMax)
+          sm.u.h.ent[slot] = ((unsigned long long)order_key(x) << 32) | (uint32_t)(~(uint32_t)u);
       }
     }
     nab = (int)wave_sum_u32((uint32_t)nab);
@@ -655,91 +654,25 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
     __syncthreads();
     const int cstar = (bstar < kRelBuckets) ? sm.count : kSortMax + 1;
     if (cstar <= kSortMax) {
-      int n2 = 1;
-      while (n2 < cstar) n2 <<= 1;
-      if (n2 <= 4 * kWave) {
-        // one wave sorts in registers and scans; the others wait at the next barrier
-        if (tid < kWave) {
-          auto finish = [&](auto& v, auto nr_tag) {
-            constexpr int NR = decltype(nr_tag)::value;
-            wave_sort_desc<NR>(v, lane);
-            int ic = -1;
-            unsigned long long carry = 0ull;
-#pragma unroll
-            for (int r = 0; r < NR; ++r) {
-              const uint64_t e = v[r];
-              unsigned long long mi = 0ull;
-              if ((uint32_t)(e >> 32) != 0u) mi = fixmass(cut_mass(key_score((uint32_t)(e >> 32)), mx, P.topk));
-              const unsigned long long inc = wave_incl_scan<unsigned long long>(mi) + carry;
-              const uint64_t reach = __ballot(mi != 0ull && (double)(above_b + inc) >= target);
-              if (ic < 0 && reach != 0ull) ic = r * 64 + __ffsll((long long)reach) - 1;
-              carry = rl64(inc, 63);
-            }
-            if (ic < 0 || ic > cstar - 1) ic = cstar - 1;
-            const int r_ic = ic >> 6, l_ic = ic & 63;
-            uint64_t ce = 0ull;
-#pragma unroll
-            for (int r = 0; r < NR; ++r)
-              if (r == r_ic) ce = rl64(v[r], l_ic);
-            if (lane == 0) { sm.ic = ic; sm.cut_entry = ce; }
-          };
-          if (n2 <= kWave) {
-            uint64_t v[1] = {(uint64_t)sm.u.sortbuf[lane]};
-            finish(v, std::integral_constant<int, 1>());
-          } else if (n2 <= 2 * kWave) {
-            uint64_t v[2];
-#pragma unroll
-            for (int r = 0; r < 2; ++r) v[r] = (uint64_t)sm.u.sortbuf[r * 64 + lane];
-            finish(v, std::integral_constant<int, 2>());
-          } else {
-            uint64_t v[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = (uint64_t)sm.u.sortbuf[r * 64 + lane];
-            finish(v, std::integral_constant<int, 4>());
-          }
-        }
-      } else {
-        for (int k2 = 2; k2 <= n2; k2 <<= 1) {
-          for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
-            for (int i = tid; i < n2; i += kCutThreads) {
-              const int ij = i ^ jj;
-              if (ij > i) {
-                const unsigned long long a = sm.u.sortbuf[i], b = sm.u.sortbuf[ij];
-                const bool desc = (i & k2) == 0;
-                if (desc ? (a < b) : (a > b)) { sm.u.sortbuf[i] = b; sm.u.sortbuf[ij] = a; }
-              }
-            }
-            __syncthreads();
-          }
-        }
-        // running mass in sorted order; the cut is the first element reaching p * W
-        unsigned long long mi = 0ull;
-        if (tid < n2) {
-          const unsigned long long e = sm.u.sortbuf[tid];
-          const uint32_t k = (uint32_t)(e >> 32);
-          if (k != 0u) mi = fixmass(cut_mass(key_score(k), mx, P.topk));
-        }
-        unsigned long long tot2;
-        const unsigned long long pre2 = block_excl_scan<NW, unsigned long long>(mi, sm.redu, &tot2);
-        if (tid == 0) sm.ic = kSortMax;
-        __syncthreads();
-        if (tid < n2 && mi != 0ull && (double)(above_b + pre2 + mi) >= target) atomicMin(&sm.ic, tid);
-        __syncthreads();
-        if (tid == 0) {
-          if (sm.ic > cstar - 1) sm.ic = cstar - 1;
-          sm.cut_entry = sm.u.sortbuf[sm.ic];
-        }
+      // one wave sorts the bucket in registers; the others wait at the barrier
+      if (tid < kWave) {
+        if (cstar <= kWave) cut_in_bucket<1>(sm, cstar, mx, P.topk, above_b, target, lane);
+        else if (cstar <= 2 * kWave) cut_in_bucket<2>(sm, cstar, mx, P.topk, above_b, target, lane);
+        else if (cstar <= 4 * kWave) cut_in_bucket<4>(sm, cstar, mx, P.topk, above_b, target, lane);
+        else if (cstar <= 8 * kWave) cut_in_bucket<8>(sm, cstar, mx, P.topk, above_b, target, lane);
+        else cut_in_bucket<16>(sm, cstar, mx, P.topk, above_b, target, lane);
       }
       __syncthreads();
       const unsigned long long ce = sm.cut_entry;
       const uint32_t kap = (uint32_t)(ce >> 32);
       const int ukap = (int)(~(uint32_t)ce);
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
+#pragma unroll 4
+      for (int j = 0; j < nj; ++j) {
         const int u = j * kCutThreads + tid;
+        const float x = ss[u];
         bool s1 = false;
-        if (sv[j] != -INFINITY) {
-          const uint32_t k = order_key(sv[j]);
+        if (x != -INFINITY) {
+          const uint32_t k = order_key(x);
           s1 = k > kap || (k == kap && u <= ukap);
         }
         if (out && u < U) out[u] = s1 ? 1 : 0;
@@ -750,37 +683,25 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
       if (tid == 0) P.kept[head] = sm.nabove + sm.ic + 1;
       return;
     }
-    __syncthreads();
+    __syncthreads();   // the general path's staging overlays the staged scores
   }
 
   // ---- general path: stage (key, w); non-candidates get key 0 and w 0
+  const bool lds = U <= kCutLds;
+  uint32_t* skey = lds ? sm.u.g.key : P.stage + (int64_t)head * P.stage_cap * 2;
+  float* sw = lds ? sm.u.g.w : (float*)(P.stage + (int64_t)head * P.stage_cap * 2 + P.stage_cap);
   unsigned long long wsum = 0;
-  if (reg) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int u = j * kCutThreads + tid;
-      uint32_t k = 0u;
-      float w = 0.0f;
-      if (sv[j] != -INFINITY) {
-        k = order_key(sv[j]);
-        w = cut_mass(sv[j], mx, P.topk);
-        wsum += fixmass(w);
-      }
-      if (u < U) { skey[u] = k; sw[u] = w; }
+  for (int u = tid; u < U; u += kCutThreads) {
+    uint32_t k = 0u;
+    float w = 0.0f;
+    const float sc1 = sc[u];
+    if (sc1 != -INFINITY) {
+      k = order_key(sc1);
+      w = cut_mass(sc1, mx, P.topk);
+      wsum += fixmass(w);
     }
-  } else {
-    for (int u = tid; u < U; u += kCutThreads) {
-      uint32_t k = 0u;
-      float w = 0.0f;
-      if (sc[u] != -INFINITY) {
-        const float sc1 = sc[u];
-        k = order_key(sc1);
-        w = cut_mass(sc1, mx, P.topk);
-        wsum += fixmass(w);
-      }
-      skey[u] = k;
-      sw[u] = w;
-    }
+    skey[u] = k;
+    sw[u] = w;
   }
   if (bits)
     for (int r = tid; r < nrow; r += kCutThreads) bits[r] = 0ull;
@@ -793,7 +714,7 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
   uint32_t tie_count = 0u;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kCutThreads) { sm.u.rad.cnt[i] = 0u; sm.u.rad.mass[i] = 0ull; }
+    for (int i = tid; i < 256; i += kCutThreads) { sm.u.g.cnt[i] = 0u; sm.u.g.mass[i] = 0ull; }
     __syncthreads();
     // Scores cluster, so most lanes of a wave often hit one bucket: such waves
     // add one aggregated (count, mass) instead of 64 conflicting LDS atomics.
@@ -812,12 +733,12 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
         if (lane == leader) {
-          atomicAdd(&sm.u.rad.cnt[lb], (uint32_t)__popcll(act));
-          atomicAdd(&sm.u.rad.mass[lb], tot);
+          atomicAdd(&sm.u.g.cnt[lb], (uint32_t)__popcll(act));
+          atomicAdd(&sm.u.g.mass[lb], tot);
         }
       } else if (in) {
-        atomicAdd(&sm.u.rad.cnt[bkt], 1u);
-        atomicAdd(&sm.u.rad.mass[bkt], ms);
+        atomicAdd(&sm.u.g.cnt[bkt], 1u);
+        atomicAdd(&sm.u.g.mass[bkt], ms);
       }
     }
     __syncthreads();
@@ -825,7 +746,7 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
       // lane owns buckets 4*lane .. 4*lane+3; suffix sums from the top bucket down
       unsigned long long own = 0ull;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) own += sm.u.rad.mass[4 * tid + i];
+      for (int i = 0; i < 4; ++i) own += sm.u.g.mass[4 * tid + i];
       unsigned long long suf = own;   // sum over lanes >= tid
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -839,8 +760,8 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
         unsigned long long run = above + (suf - own);  // mass of buckets above this lane's
         int bk = 4 * tid + 3;
         for (; bk > 4 * tid; --bk) {
-          if ((double)(run + sm.u.rad.mass[bk]) >= target) break;
-          run += sm.u.rad.mass[bk];
+          if ((double)(run + sm.u.g.mass[bk]) >= target) break;
+          run += sm.u.g.mass[bk];
         }
         sm.bucket = (uint32_t)bk;
         sm.above = run;
@@ -851,7 +772,7 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
     above = sm.above;
     prefix |= bk << shift;
     pmask |= 255u << shift;
-    tie_count = sm.u.rad.cnt[bk];
+    tie_count = sm.u.g.cnt[bk];
     __syncthreads();
   }
   // ties at the threshold key: all share one mass; take the first k by position
@@ -896,14 +817,72 @@ __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
   cut_head(P, sm);
 }
 
-// One workgroup per group.
+// grid (ceil(nwcap / kCompactRows), groups).
 __global__ void __launch_bounds__(kCompactThreads) compact_level(CompactParams P) {
   constexpr int NW = kCompactThreads / kWave;
-  __shared__ uint64_t words[kCompactWords];
-  __shared__ int32_t rowoff[kCompactThreads];
-  __shared__ int32_t pid[kCompactPids];
-  __shared__ int32_t scan[NW];
-  compact_group(P, blockIdx.x, words, rowoff, pid, scan);
+  constexpr int RW = kCompactRows;
+  __shared__ uint64_t s_words[ZHA_MAX_G][RW];   // this workgroup's rows, per head
+  __shared__ int32_t s_cnt[RW];                  // kept entries per row
+  __shared__ int32_t s_red[2][NW];
+  const int gi = blockIdx.y, x = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const ListGeo geo = list_geo(P.list, gi, P.ucap);
+  const int U = geo.U, nrow = (U + 63) >> 6;
+  const int r0 = x * RW;
+  if (x > 0 && r0 >= nrow) return;              // no rows here (uniform over the block)
+  const int nr = min(RW, nrow - r0);            // < 1 only for workgroup 0 of an empty list
+  const uint64_t* hb = P.selbits + (int64_t)gi * P.G * P.nwcap;
+  // kept entries in rows [0, r0); workgroup 0 counts every row for the total
+  const int rlim = (x == 0) ? nrow : r0;
+  uint32_t before = 0u, all = 0u;
+  for (int r = tid; r < rlim; r += kCompactThreads) {
+    const uint32_t c = (uint32_t)__popcll(kept_row(hb, P.nwcap, P.G, r, U));
+    all += c;
+    before += (r < r0) ? c : 0u;
+  }
+  if (tid < RW) {
+    int c = 0;
+    if (tid < nr) {
+      const int r = r0 + tid;
+      const int valid = U - r * 64;
+      const uint64_t vmask = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
+      uint64_t any = 0ull;
+      for (int g = 0; g < P.G; ++g) {
+        const uint64_t w = hb[(int64_t)g * P.nwcap + r] & vmask;
+        s_words[g][tid] = w;
+        any |= w;
+      }
+      c = __popcll(any);
+    }
+    s_cnt[tid] = c;
+  }
+  before = wave_sum_u32(before);
+  all = wave_sum_u32(all);
+  if (lane == 0) { s_red[0][wave] = (int32_t)before; s_red[1][wave] = (int32_t)all; }
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) { base += s_red[0][w]; tot += s_red[1][w]; }
+  if (x == 0 && tid == 0) {
+    if (tot > P.kcap) set_status(P.status, ZHA_ECAPACITY);
+    P.kcount[gi] = tot > P.kcap ? (int32_t)P.kcap : tot;
+  }
+  // first output position of row i: lane i of the exclusive scan of the counts
+  const int ci = lane < RW ? s_cnt[lane] : 0;
+  const int rowoff = base + wave_incl_scan<int>(ci) - ci;
+  int32_t* ids = P.kids + (int64_t)gi * P.kcap;
+  uint32_t* msk = P.kmask + (int64_t)gi * P.kcap;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes below this one
+  for (int i = wave; i < nr; i += NW) {
+    uint32_t m = 0u;
+    for (int g = 0; g < P.G; ++g) m |= (uint32_t)((s_words[g][i] >> lane) & 1ull) << g;
+    const uint64_t bal = __ballot(m != 0u);
+    const int p = __shfl(rowoff, i) + __popcll(bal & lt);
+    if (m != 0u && p < P.kcap) {
+      ids[p] = list_id(P.list, geo, gi, (r0 + i) * 64 + lane, nullptr);
+      msk[p] = m;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- small levels
@@ -1443,7 +1422,9 @@ static int32_t route_impl(const zha_cfg* cfg, const float* q, const zha_tree* tr
     launch_score(P, P.ucap, s);
     P.check_stale = 0;
     hipLaunchKernelGGL(cut_topp, dim3(BHq), dim3(kCutThreads), 0, s, P);
-    hipLaunchKernelGGL(compact_level, dim3(BH), dim3(kCompactThreads), 0, s, X);
+    const int64_t cx = ceil_div(X.nwcap, kCompactRows);
+    hipLaunchKernelGGL(compact_level, dim3((unsigned)(cx < 1 ? 1 : cx), (unsigned)BH),
+                       dim3(kCompactThreads), 0, s, X);
   }
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
 }
