@@ -1243,13 +1243,17 @@ __global__ void __launch_bounds__(1024) level_kl(QualityParams P, const float* S
 
 // ---------------------------------------------------------------- host
 
-// Scoring grid: one wave per node up to about 8192 workgroups in all (more than
-// stay resident; they are dispatched group by group).  Measured against 1024,
-// 2048 and 4096: the same on long1m, 3% faster on rope_batch's 64 groups.
+// Scoring grid: one wave per node, at most 128 workgroups per group and about
+// 8192 in all (more than stay resident; they are dispatched group by group).
+// Measured caps per group of 32, 64, 128, 256 and 512, and none: 128 is best or
+// level with the best on every workload (deep 270 -> 195 us per route, gqa128k
+// 60 -> 53 us, long1m and rope_batch unchanged); with more, a wave scores too
+// few nodes to repay its workgroup's start.
 static void launch_score(const LevelParams& P, int64_t ucap, hipStream_t s) {
   const int BH = P.B * P.H_kv;
   int64_t gx = ceil_div(ucap, 4);
   int64_t lim = 8192 / BH;
+  if (lim > 128) lim = 128;
   if (lim < 1) lim = 1;
   if (gx > lim) gx = lim;
   if (gx < 1) gx = 1;
