@@ -296,9 +296,16 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
   const int32_t* spid = staged ? s_pid : nullptr;
   const uint32_t* spm = staged ? s_pm : nullptr;
   const int nwaves = gridDim.x * (blockDim.x >> 6);
+  // Workgroups are dispatched to the 8 XCDs in turn by linear id (x fastest).
+  // Logical workgroup xl takes entries 4 xl + wave, + nwaves, ...; the logical
+  // ids are laid out so that 8 consecutive ones -- the writers of one 128-byte
+  // line of a head's scores -- run on one XCD.  A line written in part by
+  // several XCDs' L2s goes back to HBM as several partial writes.
+  const int xl = (gridDim.x % 8 == 0) ? (int)(blockIdx.x % 8) * (int)(gridDim.x / 8) + (int)(blockIdx.x / 8)
+                                      : (int)blockIdx.x;
   // the next entry is fetched one iteration ahead, so a wave's summary loads
   // never wait behind the id load that addresses them
-  int u = blockIdx.x * (blockDim.x >> 6) + wave;
+  int u = xl * (blockDim.x >> 6) + wave;
   int32_t node_next = 0;
   uint32_t mask_next = 0u;
   if (u < U) list_entry_staged(P.list, geo, gi, u, spid, spm, node_next, mask_next);
