@@ -265,7 +265,8 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
         v[t][s] = __builtin_nontemporal_load((const u32x4b_t*)(kr + t * 16 * D + s * 32));
   };
   u32x4b_t kv[NT][KST];
-  int64_t n = n0 + blockIdx.x;
+  // leaves n and n+1 share a line of b-hat: their workgroups share an XCD
+  int64_t n = n0 + xcd_grouped_x();
   if (n < n1) fetch(n, kv);
   for (; n < n1; n += gridDim.x) {
     if (P.rope) build_qa(n * C);
@@ -372,7 +373,8 @@ __global__ void __launch_bounds__(256) build_parents(BuildParams P) {
   double theta = 0.0;
   if (P.rope) theta = pow((double)P.rope_base, -2.0 * (double)(lane % H2) / (double)D);
   const int64_t npairs = (n1 - n0) * R;
-  for (int64_t pr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); pr < npairs;
+  // the 32 pairs of one line of b-hat run in 8 workgroups on one XCD
+  for (int64_t pr = (int64_t)xcd_grouped_x() * 4 + (threadIdx.x >> 6); pr < npairs;
        pr += (int64_t)gridDim.x * 4) {
     const int64_t n = n0 + pr / R;
     const int r = (int)(pr % R);
@@ -522,12 +524,14 @@ static void launch_level(const BuildParams& P, int64_t max_nodes, hipStream_t s)
   const dim3 grid((unsigned)gx, (unsigned)(P.B * P.H_kv));
   // the MFMA leaf builder is one wave per workgroup looping over leaves: about
   // seven waves per compute unit in all (its LDS share allows seven)
-  const int64_t lx = (7 * 256 + P.B * P.H_kv - 1) / (P.B * P.H_kv);
+  int64_t lx = (7 * 256 + P.B * P.H_kv - 1) / (P.B * P.H_kv);
+  lx = (lx + 7) / 8 * 8;   // whole rounds of the XCDs
   const dim3 lgrid((unsigned)(gx < lx ? gx : lx), (unsigned)(P.B * P.H_kv));
   const bool mfma = P.kv_dtype == ZHA_BF16 && P.R <= 16 && (P.C == 16 || P.C == 32 || P.C == 64);
   // parents: one wave per (node, plane) pair, four waves per workgroup, about
   // four workgroups per compute unit in all
-  const int64_t pw = (gx * P.R + 3) / 4, pmax = (1024 + P.B * P.H_kv - 1) / (P.B * P.H_kv);
+  const int64_t pw = (gx * P.R + 3) / 4;
+  const int64_t pmax = ((1024 + P.B * P.H_kv - 1) / (P.B * P.H_kv) + 7) / 8 * 8;
   const dim3 pgrid((unsigned)(pw < pmax ? pw : pmax), (unsigned)(P.B * P.H_kv));
   if (P.level == 1 && mfma) {
     const auto k = P.d == 128 ? (P.C == 64 ? build_leaves_mfma<128, 64>

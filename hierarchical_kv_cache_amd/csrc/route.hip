@@ -296,13 +296,9 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
   const int32_t* spid = staged ? s_pid : nullptr;
   const uint32_t* spm = staged ? s_pm : nullptr;
   const int nwaves = gridDim.x * (blockDim.x >> 6);
-  // Workgroups are dispatched to the 8 XCDs in turn by linear id (x fastest).
-  // Logical workgroup xl takes entries 4 xl + wave, + nwaves, ...; the logical
-  // ids are laid out so that 8 consecutive ones -- the writers of one 128-byte
-  // line of a head's scores -- run on one XCD.  A line written in part by
-  // several XCDs' L2s goes back to HBM as several partial writes.
-  const int xl = (gridDim.x % 8 == 0) ? (int)(blockIdx.x % 8) * (int)(gridDim.x / 8) + (int)(blockIdx.x / 8)
-                                      : (int)blockIdx.x;
+  // Logical workgroup xl takes entries 4 xl + wave, + nwaves, ...: the 8
+  // writers of one 128-byte line of a head's scores share an XCD (its L2).
+  const int xl = xcd_grouped_x();
   // the next entry is fetched one iteration ahead, so a wave's summary loads
   // never wait behind the id load that addresses them
   int u = xl * (blockDim.x >> 6) + wave;
@@ -1261,6 +1257,7 @@ static void launch_score(const LevelParams& P, int64_t ucap, hipStream_t s) {
   int64_t gx = ceil_div(ucap, 4);
   int64_t lim = 8192 / BH;
   if (lim > 128) lim = 128;
+  if (lim >= 8) lim = lim / 8 * 8;   // whole rounds of the XCDs
   if (lim < 1) lim = 1;
   if (gx > lim) gx = lim;
   if (gx < 1) gx = 1;

@@ -342,6 +342,17 @@ __device__ inline T block_excl_scan(T v, T* scratch, T* total) {
   return before + inc - v;
 }
 
+// Workgroups are dispatched to the 8 XCDs in turn by linear id (x fastest), and
+// each XCD has its own L2.  For a grid width that is a multiple of 8 this maps
+// blockIdx.x to a logical index such that XCD j runs the logical indices
+// [j w/8, (j+1) w/8): neighbouring logical workgroups share an L2, so output
+// lines they write together go back to HBM whole rather than as partial lines
+// from several L2s.  Other widths keep blockIdx.x.
+__device__ inline int xcd_grouped_x() {
+  const int w = (int)gridDim.x, x = (int)blockIdx.x;
+  return (w % 8 == 0) ? (x % 8) * (w / 8) + x / 8 : x;
+}
+
 // Order LDS traffic of one wave against itself (no cross-wave synchronisation).
 __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
