@@ -14,10 +14,11 @@
 // Reference queries are rotated (rotate-half pairs (i, i+d/2), angle
 // pos * base^(-2i/d), fp64 angles) to the node's first key position n * C^level.
 //
-// Three kernels: build_leaves_mfma (bf16 keys, C in {16, 32, 64}): one wave per
-// leaf on the matrix cores; build_leaves (other geometries): one workgroup per
-// leaf, keys staged in LDS as fp32; build_parents: one wave per (node, plane)
-// pair, the children's planes in registers.  b_hat is formed as
+// Four kernels: build_leaves_mfma (bf16 keys, C in {16, 32, 64}): one wave per
+// leaf on the matrix cores; build_leaves_small (bf16 keys, C in {2, 4, 8}): one
+// wave per leaf, lanes over dimensions; build_leaves (other geometries): one
+// workgroup per leaf, keys staged in LDS as fp32; build_parents: one wave per
+// (node, plane) pair, the children's planes in registers.  b_hat is formed as
 // F - sum_j w_j z_j, which equals F - scale q_hat.k_hat since k_hat = sum_j w_j k_j.
 #include "zha_internal.hpp"
 
@@ -352,16 +353,172 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
   }
 }
 
+// ---------------------------------------------------------------- leaves, small C
+//
+// bf16 keys, C in {2, 4, 8}, R <= 16: a leaf is too small for the matrix cores.
+// One wave per leaf; lane l holds dimensions DPL l .. DPL l + DPL - 1 of the 16
+// scaled reference queries (registers) and of the leaf's keys.  The planes go in
+// passes of PP = 32 / CP (CP = max(C, 4) keys, the padding masked): a pass's 32
+// partial dot products are summed over the 64 lanes by a halving butterfly
+// (five rounds, then one plain exchange), which leaves lanes 2e and 2e+1 with
+// entry e = plane * CP + key of the pass; the softmax of a plane runs over the
+// lanes holding its keys; the weights pass through the wave's LDS to every lane,
+// which forms its dimensions of k_hat for every plane.  The scaled queries sit
+// in the wave's LDS (the passes index them at run time).  Same formulas as the
+// MFMA kernel: queries rotated in fp64 then scaled, b_hat = F - sum_j w_j z_j.
+
+// Lane l's N values: the lanes with bit DELTA set keep the upper half, the others
+// the lower half, each adding its partner's copy of the half it keeps.
+template <int N, int DELTA>
+__device__ inline void halve_round(float* a, int lane) {
+  const bool upper = (lane & DELTA) != 0;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float keep = upper ? a[i + N / 2] : a[i];
+    const float send = upper ? a[i] : a[i + N / 2];
+    a[i] = keep + __shfl_xor(send, DELTA, 64);
+  }
+}
+
+template <int D, int CP>
+__global__ void __launch_bounds__(256) build_leaves_small(BuildParams P) {
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(CP == 4 || CP == 8, "padded keys");
+  constexpr int DPL = D / 64;             // dimensions per lane
+  constexpr int PP = 32 / CP;             // planes per pass
+  constexpr int H2 = D / 2;
+  __shared__ float wsh[4][16][CP];        // per wave: the leaf's softmax weights
+  __shared__ __attribute__((aligned(16))) float qsh[4][16][D];   // per wave: scaled queries
+  const int gi = blockIdx.y;
+  const int b = gi / P.H_kv, h = gi % P.H_kv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int C = P.C, R = P.R;
+  int64_t n0, n1;
+  node_range(P, b, n0, n1);
+  const float* qr = P.qref + (int64_t)h * R * D;
+  const int d0 = DPL * lane;
+  // the 16 scaled reference queries at this lane's dimensions, into the wave's LDS
+  float (*qv)[D] = qsh[wave];
+  auto set_q = [&](int64_t pos) {
+    if (!P.rope) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) qv[r][d0 + k] = (r < R) ? qr[r * D + d0 + k] * P.scale : 0.0f;
+      wave_lds_sync();
+      return;
+    }
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+      const int c = d0 + k, i = c < H2 ? c : c - H2;   // rotate-half pair (i, i + d/2)
+      const double theta = pow((double)P.rope_base, -2.0 * (double)i / (double)D);
+      double sn, cs;
+      sincos((double)pos * theta, &sn, &cs);
+#pragma unroll 2
+      for (int r = 0; r < 16; ++r) {
+        float x = 0.0f;
+        if (r < R) {
+          const double a = qr[r * D + i], bb = qr[r * D + i + H2];
+          x = c < H2 ? (float)(a * cs - bb * sn) : (float)(a * sn + bb * cs);
+        }
+        qv[r][d0 + k] = x * P.scale;
+      }
+    }
+    wave_lds_sync();
+  };
+  if (!P.rope) set_q(0);
+  const uint16_t* Kb = (const uint16_t*)P.K;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  // after a pass's butterfly: entry e = lane / 2, plane PP pass + e / CP, key e % CP
+  const int e = lane >> 1, jl = e % CP, rl = e / CP;
+  for (int64_t n = n0 + (int64_t)xcd_grouped_x() * 4 + wave; n < n1; n += nw) {
+    if (P.rope) set_q(n * C);              // (after the previous leaf's closing sync)
+    // this lane's dimensions of the leaf's keys (padding keys zero)
+    float kv[CP][DPL];
+    const uint16_t* kr = Kb + ((int64_t)gi * P.T_cap + n * C) * D + d0;
+#pragma unroll
+    for (int j = 0; j < CP; ++j) {
+      if constexpr (DPL == 2) {
+        const uint32_t pr = j < C ? *(const uint32_t*)(kr + (int64_t)j * D) : 0u;
+        kv[j][0] = bf16_lo(pr);
+        kv[j][1] = bf16_hi(pr);
+      } else {
+        kv[j][0] = j < C ? __uint_as_float((uint32_t)kr[(int64_t)j * D] << 16) : 0.0f;
+      }
+    }
+#pragma unroll 1
+    for (int pass = 0; pass < 16 / PP; ++pass) {
+      float a[32];
+#pragma unroll
+      for (int r = 0; r < PP; ++r) {
+        float q[DPL];
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) q[k] = qv[PP * pass + r][d0 + k];
+#pragma unroll
+        for (int j = 0; j < CP; ++j) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < DPL; ++k) acc = fmaf(q[k], kv[j][k], acc);
+          a[r * CP + j] = acc;
+        }
+      }
+      halve_round<32, 32>(a, lane);
+      halve_round<16, 16>(a, lane);
+      halve_round<8, 8>(a, lane);
+      halve_round<4, 4>(a, lane);
+      halve_round<2, 2>(a, lane);
+      const float zs = a[0] + __shfl_xor(a[0], 1, 64);
+      // softmax of plane PP pass + rl over the lanes holding its keys (lane bits 1 .. log2 CP)
+      const float z = jl < C ? zs : -INFINITY;
+      float M = z;
+#pragma unroll
+      for (int m = 2; m < 2 * CP; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+      const float ex = jl < C ? expf(z - M) : 0.0f;
+      float S = ex, SZ = jl < C ? ex * z : 0.0f;
+#pragma unroll
+      for (int m = 2; m < 2 * CP; m <<= 1) {
+        S += __shfl_xor(S, m, 64);
+        SZ += __shfl_xor(SZ, m, 64);
+      }
+      const int r = PP * pass + rl;
+      // b_hat = F - sum_j w_j z_j, F = M + log S
+      if ((lane & (2 * CP - 1)) == 0 && r < R)
+        P.bhat[((int64_t)gi * P.ncap + n) * R + r] = (M + logf(S)) - SZ / S;
+      if ((lane & 1) == 0) wsh[wave][r][jl] = ex / S;
+    }
+    wave_lds_sync();
+    // k_hat of every plane at this lane's dimensions
+    float* kh = P.khat + ((int64_t)gi * P.ncap + n) * R * D + d0;
+#pragma unroll 2
+    for (int rr = 0; rr < 16; ++rr) {
+      if (rr < R) {
+        float acc[DPL];
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) acc[k] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CP; ++j) {
+          const float w = wsh[wave][rr][j];      // the same address in every lane
+#pragma unroll
+          for (int k = 0; k < DPL; ++k) acc[k] = fmaf(w, kv[j][k], acc[k]);
+        }
+        if constexpr (DPL == 2) *(float2*)(kh + (int64_t)rr * D) = make_float2(acc[0], acc[1]);
+        else kh[(int64_t)rr * D] = acc[0];
+      }
+    }
+    wave_lds_sync();                       // the weights are rewritten by the next leaf
+  }
+}
+
 // Parent summaries, one wave per (node, plane) pair: the children's planes r
 // (child 4t + lane/16, dimensions (lane%16)*d/16 ..) stay in registers, and an
 // exact two-pass softmax over the children gives k_hat and b_hat.  No LDS, no
 // workgroup barriers.
-template <int D>
+template <int D, int MT>
 __global__ void __launch_bounds__(256) build_parents(BuildParams P) {
+  static_assert(MT >= 1 && 4 * MT <= kMaxC, "child rounds");
   constexpr int DPL = D / 16;              // dimensions per lane
   constexpr int NV = DPL / 4;              // float4 per child per lane
-  constexpr int H2 = D / 2;
-  constexpr int MT = kMaxC / 4;            // child rounds
+  constexpr int H2 = D / 2;                // MT: child rounds, ceil(C / 4)
   const int gi = blockIdx.y;
   const int b = gi / P.H_kv, h = gi % P.H_kv;
   const int lane = threadIdx.x & 63, cg = lane >> 4, ds = (lane & 15) * DPL;
@@ -528,6 +685,13 @@ static void launch_level(const BuildParams& P, int64_t max_nodes, hipStream_t s)
   lx = (lx + 7) / 8 * 8;   // whole rounds of the XCDs
   const dim3 lgrid((unsigned)(gx < lx ? gx : lx), (unsigned)(P.B * P.H_kv));
   const bool mfma = P.kv_dtype == ZHA_BF16 && P.R <= 16 && (P.C == 16 || P.C == 32 || P.C == 64);
+  const bool small = P.kv_dtype == ZHA_BF16 && P.R <= 16 && (P.C == 2 || P.C == 4 || P.C == 8);
+  // small-C leaves: one wave per leaf, four per workgroup, about eight
+  // workgroups per compute unit in all
+  int64_t sx = (2048 + P.B * P.H_kv - 1) / (P.B * P.H_kv);
+  sx = (sx + 7) / 8 * 8;
+  const int64_t sw = (gx + 3) / 4;
+  const dim3 sgrid((unsigned)(sw < sx ? sw : sx), (unsigned)(P.B * P.H_kv));
   // parents: one wave per (node, plane) pair, four waves per workgroup, about
   // four workgroups per compute unit in all
   const int64_t pw = (gx * P.R + 3) / 4;
@@ -539,11 +703,22 @@ static void launch_level(const BuildParams& P, int64_t max_nodes, hipStream_t s)
                               : (P.C == 64 ? build_leaves_mfma<64, 64>
                                  : P.C == 32 ? build_leaves_mfma<64, 32> : build_leaves_mfma<64, 16>);
     hipLaunchKernelGGL(k, lgrid, dim3(64), 0, s, P);
-  } else if (P.level == 1)
+  } else if (P.level == 1 && small) {
+    const auto k = P.d == 128 ? (P.C == 8 ? build_leaves_small<128, 8> : build_leaves_small<128, 4>)
+                              : (P.C == 8 ? build_leaves_small<64, 8> : build_leaves_small<64, 4>);
+    hipLaunchKernelGGL(k, sgrid, dim3(256), 0, s, P);
+  } else if (P.level == 1) {
     hipLaunchKernelGGL(build_leaves, grid, dim3(256), 0, s, P);
-  else
-    hipLaunchKernelGGL(P.d == 128 ? build_parents<128> : build_parents<64>, pgrid, dim3(256), 0,
-                       s, P);
+  } else {
+    // child rounds ceil(C / 4): the parents' registers and work follow C
+    const int mt = (P.C + 3) / 4;
+    const auto k = P.d == 128
+        ? (mt <= 1 ? build_parents<128, 1> : mt <= 2 ? build_parents<128, 2> : mt <= 4 ? build_parents<128, 4>
+           : mt <= 8 ? build_parents<128, 8> : build_parents<128, 16>)
+        : (mt <= 1 ? build_parents<64, 1> : mt <= 2 ? build_parents<64, 2> : mt <= 4 ? build_parents<64, 4>
+           : mt <= 8 ? build_parents<64, 8> : build_parents<64, 16>);
+    hipLaunchKernelGGL(k, pgrid, dim3(256), 0, s, P);
+  }
 }
 
 }  // namespace zha
