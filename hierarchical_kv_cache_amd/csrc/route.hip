@@ -1009,7 +1009,8 @@ __global__ void __launch_bounds__(256) score_upper(UpperParams U) {
   for (int k = 0; k < U.nlev; ++k) total += (int)upper_nodes(U, k, T);
   float qv[GP][4];
   load_group_queries<D, GP>(U.base, gi, lane, qv);
-  for (int t = blockIdx.x * NW + wave; t < total; t += gridDim.x * NW) {
+  // node t's score lines are shared by 8 neighbouring workgroups: one XCD runs them
+  for (int t = xcd_grouped_x() * NW + wave; t < total; t += gridDim.x * NW) {
     int k = 0, node = t;
     while (node >= (int)upper_nodes(U, k, T)) { node -= (int)upper_nodes(U, k, T); ++k; }
     score_node<D, GP>(upper_level_params(U, k), gi, node, 0xffffffffu, node, qv, lane);
@@ -1279,6 +1280,7 @@ static void launch_upper(const UpperParams& U, hipStream_t s) {
   int64_t nodes = 0;
   for (int k = 0; k < U.nlev; ++k) nodes += U.lv[k].cap;
   int64_t gx = ceil_div(nodes, 4);   // one node per wave
+  gx = (gx + 7) / 8 * 8;              // whole rounds of the XCDs
   if (gx < 1) gx = 1;
   const dim3 grid((unsigned)gx, (unsigned)BH);
   const int GP = U.base.G <= 4 ? 4 : (U.base.G <= 8 ? 8 : 16);
