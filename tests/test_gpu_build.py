@@ -83,6 +83,20 @@ def test_build_bf16_d64(C, rope):
         _compare_tree(cfg, K, qref, tree, T, wl.rope_base if rope else None, h=h)
 
 
+@pytest.mark.parametrize("C,d,rope,R", [(2, 128, False, 16), (4, 128, True, 16), (8, 128, False, 12),
+                                         (8, 64, True, 16), (4, 64, False, 12)])
+def test_build_bf16_small_chunks(C, d, rope, R):
+    """C in {2, 4, 8}: the one-wave-per-leaf builder (lanes over dimensions) and
+    parents of one or two child rounds, with and without RoPE, d = 64 and 128,
+    and R < 16 (padded planes)."""
+    wl = _workload("rope_batch" if rope else "gqa128k", B=1, H_kv=2, G=4, d=d, C=C, L=3, R=R,
+                   n_clusters=64)
+    T = C ** 3 * 5 + C * 3 + 1
+    cfg, K, V, qref, tree, ws, Tt = _build_gpu(wl, T)
+    for h in range(2):
+        _compare_tree(cfg, K, qref, tree, T, wl.rope_base if rope else None, h=h)
+
+
 def test_build_rope_parent_correction():
     """RoPE: reference queries rotated to each node's first key position; parents
     rescore children at their own rotated query (the correction term)."""
@@ -97,7 +111,7 @@ def test_build_rope_parent_correction():
 def test_append_cascade_equals_prefill_build(C, L):
     """Growing T one token at a time with zha_append yields exactly the tree a
     prefill build of the final length gives (the append cadence); C = 16 takes
-    the matrix-core leaf builder, C = 8 the plain one."""
+    the matrix-core leaf builder, C = 8 the one-wave-per-leaf one."""
     wl = _workload("gqa128k", H_kv=2, G=4, C=C, L=L, n_clusters=16)
     T0, T1 = C ** L - 37, C ** L * 2 + 70
     K, V = synth.make_cache(wl.with_(N=T1, open_len=0, steps=0), DEV, T1 + C)
