@@ -120,9 +120,12 @@ CASES = {
     "deep": (synth.WORKLOADS["deep"].with_(H_kv=1, C=4, L=5, N=4 ** 5 * 3 + 50), 4 ** 5 * 3 + 50),
     "rope": (synth.WORKLOADS["rope_batch"].with_(B=2, H_kv=1, G=4, C=16, L=3, n_clusters=64),
              16 ** 3 * 2 + 40),
+    # sixteen query heads per KV head: the widest head masks (scoring, cut and
+    # compaction with G = 16)
+    "g16": (synth.WORKLOADS["gqa128k"].with_(H_kv=1, G=16, C=16, L=3, n_clusters=128), 12000 + 3),
     # one level of 20000 / 30000 leaves: candidate pools beyond 16384 entries (the
-    # cut's LDS staging) and beyond 24576 (its register capacity), and final
-    # expansions longer than one register batch per wave
+    # cut's LDS staging of the general path) and beyond 24576 (the staged path's
+    # capacity), and final expansions longer than one register batch per wave
     "wide20k": (synth.WORKLOADS["tiny"].with_(G=2, C=2, L=1, R=2, n_clusters=64), 40000),
     "wide30k": (synth.WORKLOADS["tiny"].with_(G=2, C=2, L=1, R=2, n_clusters=64), 60000 + 1),
 }
@@ -248,25 +251,30 @@ def test_all_equal_scores_take_lowest_ids(p):
     assert lst.ids[0, 0, :m].cpu().tolist() == list(range(m))
 
 
-@pytest.mark.parametrize("n_band", [40, 120, 200, 600])
+@pytest.mark.parametrize("n_band", [40, 120, 200, 400, 600, 1000, 1500])
 @pytest.mark.parametrize("p", [0.5, 0.9])
 def test_cut_crossing_bucket_sizes(n_band, p):
     """Scores set exactly through the summaries (k_hat = 0, so a node's score is
-    its best b_hat): n_band nodes are spread over one 1/64-wide score interval
-    around the mass cut, so the bucket the cut falls in holds about n_band
-    entries (one wave sorts up to 256 of them in registers, more take the block
-    sort).  The rest sit far above (kept) or below (dropped)."""
+    its best b_hat): n_band nodes sit inside one bucket of the cut's relative-score
+    histogram (1/128 of a score unit below the maximum per bucket), around the
+    mass cut, so the bucket the cut falls in holds exactly n_band entries.  One
+    wave sorts up to 1024 of them in registers (64, 128, 256, 512 or 1024 at a
+    time); 1500 take the radix select.  The rest sit far above (kept) or below
+    (dropped)."""
     rng = np.random.default_rng(7 + n_band)
     n_hi, n_lo = 5, 3000
     n = n_hi + n_band + n_lo
     C, d, R = 16, 64, 2
     T = n * C
     s = np.empty(n)
-    s[:n_hi] = 3.0 + rng.uniform(0, 1, n_hi)
+    s[:n_hi] = np.float32(3.0 + rng.uniform(0, 1, n_hi))
+    mx = float(np.max(s[:n_hi]))
     # the band holds three times the mass of the nodes above it, so the cut
-    # (1/3 of the way in at p = 0.5, 87% at p = 0.9) falls inside it
+    # (1/3 of the way in at p = 0.5, 87% at p = 0.9) falls inside it; its scores
+    # are placed 0.25 .. 0.75 of the way through bucket k, clear of its edges
     b0 = math.log(3.0 * np.exp(s[:n_hi]).sum() / n_band)
-    s[n_hi:n_hi + n_band] = b0 + rng.uniform(0, 1.0 / 64, n_band)
+    k = math.floor((mx - b0) * 128.0)
+    s[n_hi:n_hi + n_band] = mx - (k + 0.25 + 0.5 * rng.uniform(0, 1, n_band)) / 128.0
     s[n_hi + n_band:] = b0 - 14.0 + rng.uniform(0, 1, n_lo)
     s = np.float32(s)
     perm = rng.permutation(n)
