@@ -18,13 +18,14 @@
 // Everything stays on the device between levels.
 //
 // The top-p cut needs only the threshold, not a full sort.  Candidates are
-// histogrammed by mass over 2048 buckets of relative score
-// floor((max s - s) * 64), which is monotone in the score, so every bucket holds
-// a contiguous stretch of the descending order; a block scan finds the bucket
-// where the running mass first reaches p * W, and only that bucket is sorted
-// exactly by (score desc, id asc) to place the cut.  A bucket too large to sort
-// (near-equal scores) falls back to an MSD radix select over the order-preserving
-// 32-bit image of the scores, four 8-bit digits, ties taken by ascending id.
+// histogrammed by mass over 4096 buckets of relative score
+// floor((max s - s) * 128), which is monotone in the score, so every bucket
+// holds a contiguous stretch of the descending order; a block scan finds the
+// bucket where the running mass first reaches p * W, and only that bucket (up to
+// 1024 entries) is sorted exactly by (score desc, id asc), by one wave, to place
+// the cut.  A larger bucket (near-equal scores) falls back to an MSD radix
+// select over the order-preserving 32-bit image of the scores, four 8-bit
+// digits, ties taken by ascending id.
 // Masses are w = exp(s - max s) in fp32, accumulated as 64-bit fixed point
 // (w * 2^40) with integer atomics, so the cut is deterministic.
 #include "zha_internal.hpp"
