@@ -201,16 +201,23 @@ __device__ inline void tr_round(float* a, int lane) {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// The group's G queries at this lane's dims (t = lane % (D/4)), zero-padded to GP.
+// The group's G queries, zero-padded to GP: at this lane's dims (t = lane %
+// (D/4)) in registers when GP == 4, else into the workgroup's LDS copy qlds
+// ([GP][D]; the caller synchronises the workgroup before it is read).
 template <int D, int GP>
 __device__ inline void load_group_queries(const LevelParams& P, int gi, int lane,
-                                          float (&qv)[GP][4]) {
-  const int t = lane % (D / 4);
+                                          float (&qv)[GP][4], float* qlds) {
+  if constexpr (GP > 4) {
+    for (int i = threadIdx.x; i < GP * D; i += blockDim.x)
+      qlds[i] = (i / D < P.G) ? P.q[(int64_t)gi * P.G * D + i] : 0.0f;
+  } else {
+    const int t = lane % (D / 4);
 #pragma unroll
-  for (int g = 0; g < GP; ++g)
+    for (int g = 0; g < GP; ++g)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      qv[g][j] = (g < P.G) ? P.q[((int64_t)gi * P.G + g) * D + t * 4 + j] : 0.0f;
+      for (int j = 0; j < 4; ++j)
+        qv[g][j] = (g < P.G) ? P.q[((int64_t)gi * P.G + g) * D + t * 4 + j] : 0.0f;
+  }
 }
 
 // One wave scores list entry u (tree node `node`) of group gi for all G heads.
@@ -219,13 +226,12 @@ __device__ inline void load_group_queries(const LevelParams& P, int gi, int lane
 // non-candidates for the cut.
 template <int D, int GP>
 __device__ inline void score_node(const LevelParams& P, int gi, int node, uint32_t mask, int u,
-                                  const float (&qv)[GP][4], int lane) {
+                                  const float (&qv)[GP][4], const float* qlds, int lane) {
   constexpr int LPR = D / 4;           // lanes per summary row
   constexpr int RPI = kWave / LPR;     // rows per load instruction
   constexpr int NS = 16 / RPI;         // load instructions per node (R padded to 16)
-  constexpr int V0 = NS * GP;          // partial dots per lane
-  constexpr int J = GP / 4;            // full dots per lane after the butterfly
-  static_assert(V0 / LPR == J, "butterfly shape");
+  constexpr int V0 = NS * 4;           // partial dots per lane and quad of heads
+  static_assert(V0 / LPR == 1, "butterfly shape");
   const int t = lane % LPR;
   if (node < 0 || node >= P.ncap) {   // not a node of this tree: never selected
     if (lane < P.G) P.scores[((int64_t)gi * P.G + lane) * P.ucap + u] = -INFINITY;
@@ -236,41 +242,54 @@ __device__ inline void score_node(const LevelParams& P, int gi, int node, uint32
   // after the butterfly this lane holds row r = RPI*(t/4) + lane/LPR
   const int r_out = RPI * (t / 4) + lane / LPR;
   const float bh = (r_out < P.R) ? P.bhat[((int64_t)gi * P.ncap + node) * P.R + r_out] : 0.0f;
-  float a[V0];
+  f32x4_t k4[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int r = RPI * s + lane / LPR;
-    f32x4_t k4 = {0.f, 0.f, 0.f, 0.f};
-    if (r < P.R) k4 = __builtin_nontemporal_load((const f32x4_t*)(base + r * D + t * 4));
-#pragma unroll
-    for (int g = 0; g < GP; ++g)
-      a[s * GP + g] = qv[g][0] * k4[0] + qv[g][1] * k4[1] + qv[g][2] * k4[2] + qv[g][3] * k4[3];
+    k4[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (r < P.R) k4[s] = __builtin_nontemporal_load((const f32x4_t*)(base + r * D + t * 4));
   }
-  // butterfly over the LPR lanes of a row: deltas LPR/2 .. 1
-  if constexpr (LPR == 32) tr_round<V0, 16>(a, lane);
-  if constexpr (LPR >= 16) tr_round<V0 * 16 / LPR, 8>(a, lane);
-  tr_round<V0 * 8 / LPR, 4>(a, lane);
-  tr_round<V0 * 4 / LPR, 2>(a, lane);
-  tr_round<V0 * 2 / LPR, 1>(a, lane);
-  // lane now holds dot(s = t/4, g = (t%4)*J + j) for row r_out
-  float sc[J];
+  // The heads go four at a time over the summary held in registers; the
+  // scheduling barrier keeps one quad's partial dots live at a time.  With more
+  // than four heads the queries come from the workgroup's LDS copy (qlds,
+  // [GP][D]), which keeps the kernel at four waves per SIMD.
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    float v = (r_out < P.R) ? fmaf(a[j], P.scale, bh) : -INFINITY;
+  for (int hq = 0; hq < GP / 4; ++hq) {
+    if (hq > 0) __builtin_amdgcn_sched_barrier(0);
+    float q[4][4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if constexpr (GP > 4) {
+        const f32x4_t x = *(const f32x4_t*)(qlds + (4 * hq + g) * D + t * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[g][j] = x[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[g][j] = qv[4 * hq + g][j];
+      }
+    }
+    float a[V0];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        a[s * 4 + g] = q[g][0] * k4[s][0] + q[g][1] * k4[s][1] + q[g][2] * k4[s][2] + q[g][3] * k4[s][3];
+    // butterfly over the LPR lanes of a row: deltas LPR/2 .. 1
+    if constexpr (LPR == 32) tr_round<V0, 16>(a, lane);
+    if constexpr (LPR >= 16) tr_round<V0 * 16 / LPR, 8>(a, lane);
+    tr_round<V0 * 8 / LPR, 4>(a, lane);
+    tr_round<V0 * 4 / LPR, 2>(a, lane);
+    tr_round<V0 * 2 / LPR, 1>(a, lane);
+    // lane now holds dot(s = t/4, head 4 hq + t%4) for row r_out
+    float v = (r_out < P.R) ? fmaf(a[0], P.scale, bh) : -INFINITY;
     v = fmaxf(v, xor_lane<4>(v));
     v = fmaxf(v, xor_lane<8>(v));
     v = fmaxf(v, xor_lane<16>(v));
     v = fmaxf(v, xor_lane<32>(v));
-    sc[j] = v;
-  }
-  if (lane < 4) {
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int g = lane * J + j;
-      if (g < P.G)
-        P.scores[((int64_t)gi * P.G + g) * P.ucap + u] =
-            ((mask >> g) & 1u) ? (isfinite(sc[j]) ? sc[j] : -FLT_MAX) : -INFINITY;
-    }
+    const int g = 4 * hq + lane;
+    if (lane < 4 && g < P.G)
+      P.scores[((int64_t)gi * P.G + g) * P.ucap + u] =
+          ((mask >> g) & 1u) ? (isfinite(v) ? v : -FLT_MAX) : -INFINITY;
   }
 }
 
@@ -291,8 +310,9 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
       s_pm[i] = P.list.pmask[(int64_t)gi * P.list.pcap + i];
     }
   }
+  __shared__ __attribute__((aligned(16))) float s_q[GP > 4 ? GP * D : 4];
   float qv[GP][4];
-  load_group_queries<D, GP>(P, gi, lane, qv);
+  load_group_queries<D, GP>(P, gi, lane, qv, s_q);
   __syncthreads();
   const int32_t* spid = staged ? s_pid : nullptr;
   const uint32_t* spm = staged ? s_pm : nullptr;
@@ -310,7 +330,7 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
     const int node = node_next;
     const uint32_t mask = mask_next;
     if (u + nwaves < U) list_entry_staged(P.list, geo, gi, u + nwaves, spid, spm, node_next, mask_next);
-    score_node<D, GP>(P, gi, node, mask, u, qv, lane);
+    score_node<D, GP>(P, gi, node, mask, u, qv, s_q, lane);
   }
 }
 
@@ -1008,13 +1028,15 @@ __global__ void __launch_bounds__(256) score_upper(UpperParams U) {
   if (T > U.base.list.T_cap) T = U.base.list.T_cap;
   int total = 0;
   for (int k = 0; k < U.nlev; ++k) total += (int)upper_nodes(U, k, T);
+  __shared__ __attribute__((aligned(16))) float s_q[GP > 4 ? GP * D : 4];
   float qv[GP][4];
-  load_group_queries<D, GP>(U.base, gi, lane, qv);
+  load_group_queries<D, GP>(U.base, gi, lane, qv, s_q);
+  __syncthreads();
   // node t's score lines are shared by 8 neighbouring workgroups: one XCD runs them
   for (int t = xcd_grouped_x() * NW + wave; t < total; t += gridDim.x * NW) {
     int k = 0, node = t;
     while (node >= (int)upper_nodes(U, k, T)) { node -= (int)upper_nodes(U, k, T); ++k; }
-    score_node<D, GP>(upper_level_params(U, k), gi, node, 0xffffffffu, node, qv, lane);
+    score_node<D, GP>(upper_level_params(U, k), gi, node, 0xffffffffu, node, qv, s_q, lane);
   }
 }
 
