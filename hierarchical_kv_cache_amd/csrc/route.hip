@@ -337,8 +337,8 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
 // ---------------------------------------------------------------- top-p cut (A4)
 
 constexpr int kCutThreads = 1024;
-constexpr int kCutLds = 16384;         // entries staged in LDS; longer lists use the workspace
-constexpr int kCutReg = 24;            // entries per thread held in registers (24576 per list)
+constexpr int kCutLds = 16384;         // general path: entries staged in LDS; longer lists use the workspace
+constexpr int kCutStage = 24;          // entries per thread staged in LDS by the main path (24576 per list)
 
 // w * 2^40 truncated to an integer, for 0 <= w <= 1, from the fp32 bits: the
 // 24-bit mantissa shifted by (exponent + 17).  Equal to (uint64)((double)w * 2^40).
@@ -478,7 +478,7 @@ __device__ inline uint64_t kept_row(const uint64_t* hb, int64_t nwcap, int G, in
 struct CutSmem {
   union {
     struct {                                      // staged path
-      float sc[kCutReg * kCutThreads];            // the head's scores (-inf past U)
+      float sc[kCutStage * kCutThreads];            // the head's scores (-inf past U)
       unsigned long long relmass[kRelBuckets];    // mass per relative-score bucket
       unsigned long long ent[kSortMax];           // crossing bucket: key << 32 | ~u, 0 past it
     } h;
@@ -554,7 +554,7 @@ __device__ inline void cut_in_bucket(CutSmem& sm, int cstar, float mx, int topk,
 // keeps the code that runs small.
 __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
   constexpr int NW = kCutThreads / kWave;
-  constexpr int PER = kCutReg;
+  constexpr int PER = kCutStage;
   const int head = blockIdx.x;
   const int gi = head / P.G, g = head % P.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
