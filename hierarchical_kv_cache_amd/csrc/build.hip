@@ -163,8 +163,9 @@ __global__ void __launch_bounds__(256) build_leaves(BuildParams P) {
 // accumulate in fp32.  Rows are the planes (padded to 16).  Z: wave w takes keys
 // 16w..16w+15, its key operand read straight from the cache rows.  k_hat: wave w
 // takes the 16-dim tiles w, w+4, ..., its key operand read from K^T staged in
-// LDS.  Under RoPE the reference queries are rotated per leaf, with one fp64
-// sincos per dimension pair shared by the R planes.
+// LDS.  Under RoPE the reference queries are rotated per leaf; the fp64 angle of
+// each dimension pair, shared by the R planes, advances by one fixed rotation
+// from leaf to leaf (a sincos only at a wave's first leaf).
 
 typedef __bf16 bf16x8b_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x4b_t __attribute__((__vector_size__(4 * sizeof(float))));
@@ -217,7 +218,8 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
   if (P.rope) theta = pow((double)P.rope_base, -2.0 * (double)(lane % H2) / (double)D);
 
   bf16x8b_t qa[3][KST];
-  auto build_qa = [&](int64_t pos) {
+  // (cs, sn): cos and sin of this lane's RoPE angle at the current leaf
+  auto build_qa = [&](double cs, double sn) {
     __syncthreads();                       // the previous leaf's K^T reads are done
     if (!P.rope) {
       for (int i = lane; i < 16 * D; i += 64) {
@@ -225,8 +227,6 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
         qs[r][c] = (r < R) ? qr[r * D + c] * P.scale : 0.0f;
       }
     } else {
-      double sn, cs;
-      sincos((double)pos * theta, &sn, &cs);
       for (int idx = lane; idx < 16 * H2; idx += 64) {
         const int r = idx / H2, c = idx % H2;   // c == lane % H2
         float x1 = 0.0f, x2 = 0.0f;
@@ -253,7 +253,7 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
     }
     __syncthreads();                       // K^T may overwrite the staging now
   };
-  if (!P.rope) build_qa(0);
+  if (!P.rope) build_qa(1.0, 0.0);
 
   // lane's share of a leaf: keys 16t + row, dimensions 32s + 8kg .. +8
   const uint16_t* Kb = (const uint16_t*)P.K;
@@ -269,8 +269,21 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
   // leaves n and n+1 share a line of b-hat: their workgroups share an XCD
   int64_t n = n0 + xcd_grouped_x();
   if (n < n1) fetch(n, kv);
+  // RoPE angle of this lane's frequency at leaf n, advanced by the fixed step of
+  // gridDim.x leaves per iteration with one fp64 rotation (the angle pos * theta,
+  // pos = n C, to ~1e-14 over a few hundred steps) instead of a sincos per leaf
+  double rc = 1.0, rs = 0.0, dc = 1.0, ds = 0.0;
+  if (P.rope) {
+    sincos((double)(n * C) * theta, &rs, &rc);
+    sincos((double)((int64_t)gridDim.x * C) * theta, &ds, &dc);
+  }
   for (; n < n1; n += gridDim.x) {
-    if (P.rope) build_qa(n * C);
+    if (P.rope) {
+      build_qa(rc, rs);
+      const double c2 = rc * dc - rs * ds, s2 = rs * dc + rc * ds;
+      rc = c2;
+      rs = s2;
+    }
     // ---- Z: z[t][i] = logit of plane 4kg + i, key 16t + row
     f32x4b_t z[NT];
 #pragma unroll
