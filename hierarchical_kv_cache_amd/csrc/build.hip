@@ -227,13 +227,16 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
         qs[r][c] = (r < R) ? qr[r * D + c] * P.scale : 0.0f;
       }
     } else {
+      // the angle is fp64; the rotations run in fp32 (within an ulp or two of the
+      // fp64-rounded result, far inside the builder's accuracy)
+      const float cf = (float)cs, sf = (float)sn;
       for (int idx = lane; idx < 16 * H2; idx += 64) {
         const int r = idx / H2, c = idx % H2;   // c == lane % H2
         float x1 = 0.0f, x2 = 0.0f;
         if (r < R) {
-          const double a = qr[r * D + c], bb = qr[r * D + c + H2];
-          x1 = (float)(a * cs - bb * sn);
-          x2 = (float)(a * sn + bb * cs);
+          const float a = qr[r * D + c], bb = qr[r * D + c + H2];
+          x1 = fmaf(a, cf, -bb * sf);
+          x2 = fmaf(a, sf, bb * cf);
         }
         qs[r][c] = x1 * P.scale;
         qs[r][c + H2] = x2 * P.scale;
