@@ -381,7 +381,8 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
 // lanes holding its keys; the weights pass through the wave's LDS to every lane,
 // which forms its dimensions of k_hat for every plane.  The scaled queries sit
 // in the wave's LDS (the passes index them at run time).  Same formulas as the
-// MFMA kernel: queries rotated in fp64 then scaled, b_hat = F - sum_j w_j z_j.
+// MFMA kernel (b_hat = F - sum_j w_j z_j); the queries are rotated in fp64 here
+// (one leaf per wave leaves no per-leaf staging to save) and then scaled.
 
 // Lane l's N values: the lanes with bit DELTA set keep the upper half, the others
 // the lower half, each adding its partner's copy of the half it keeps.
