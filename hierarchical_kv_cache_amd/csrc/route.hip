@@ -656,7 +656,6 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
     // consecutive slots in lane order)
     int nab = 0;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));   // lanes below this one
-#pragma unroll 4
     for (int j = 0; j < nj; ++j) {
       const int u = j * kCutThreads + tid;
       const float x = ss[u];
@@ -690,7 +689,6 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
       const unsigned long long ce = sm.cut_entry;
       const uint32_t kap = (uint32_t)(ce >> 32);
       const int ukap = (int)(~(uint32_t)ce);
-#pragma unroll 4
       for (int j = 0; j < nj; ++j) {
         const int u = j * kCutThreads + tid;
         const float x = ss[u];
