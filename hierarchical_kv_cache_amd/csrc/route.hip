@@ -395,45 +395,51 @@ __device__ inline uint64_t xor_partner64(uint64_t v, int lane) {
          xor_partner32<J>((uint32_t)v, lane);
 }
 
+// Bitonic network, descending, over the 64 NR values of a wave held blocked:
+// entry i = NR lane + r is v[r] of lane `lane`.  Exchanges between entries fewer
+// than NR apart stay in a lane's registers; the others pair lanes J/NR apart.
 template <int NR, int K2, int J>
 __device__ inline void bitonic_stage(uint64_t (&v)[NR], int lane) {
-  if constexpr (J >= 64) {
-    constexpr int jr = J >> 6;
+  if constexpr (J < NR) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      if ((r & jr) == 0) {
-        const int r2 = r | jr;
-        const bool desc = ((r * 64) & K2) == 0;
+      if ((r & J) == 0) {
+        const int r2 = r | J;
+        const bool desc = ((NR * lane + r) & K2) == 0;
         const uint64_t a = v[r], b = v[r2];
-        const bool sw = desc ? (a < b) : (a > b);
+        const bool sw = (a < b) == desc;   // a descending pair puts the larger first
         v[r] = sw ? b : a;
         v[r2] = sw ? a : b;
       }
     }
   } else {
+    constexpr int JL = J / NR;
+    const bool lower = (lane & JL) == 0;
+    const bool desc = ((NR * lane) & K2) == 0;   // K2 > J >= NR: r stays below bit K2
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const uint64_t a = v[r];
-      const uint64_t b = xor_partner64<J>(a, lane);
-      const bool lower = (lane & J) == 0;
-      const bool desc = ((r * 64 + lane) & K2) == 0;
-      const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-      v[r] = (lower == desc) ? hi : lo;   // the lower entry of a descending pair keeps the larger
+      const uint64_t b = xor_partner64<JL>(a, lane);
+      // the lower entry of a descending pair keeps the larger, and so on
+      v[r] = ((b > a) == (lower == desc)) ? b : a;
     }
   }
   if constexpr (J > 1) bitonic_stage<NR, K2, J / 2>(v, lane);
 }
 
-template <int NR, int K2>
+template <int NR, int K2, int KMAX>
 __device__ inline void bitonic_merge_all(uint64_t (&v)[NR], int lane) {
   bitonic_stage<NR, K2, K2 / 2>(v, lane);
-  if constexpr (K2 < 64 * NR) bitonic_merge_all<NR, K2 * 2>(v, lane);
+  if constexpr (K2 < KMAX) bitonic_merge_all<NR, K2 * 2, KMAX>(v, lane);
 }
 
-// Bitonic sort, descending, of the 64*NR values v[r] of lane l (entry r*64 + l).
-template <int NR>
+// Sorts the blocked entries descending.  With KMAX < 64 NR only the networks of
+// KMAX entries run: the first KMAX entries come out sorted when every later one
+// is zero (a shorter list padded with zeros).
+template <int NR, int KMAX = 64 * NR>
 __device__ inline void wave_sort_desc(uint64_t (&v)[NR], int lane) {
-  bitonic_merge_all<NR, 2>(v, lane);
+  static_assert(KMAX >= 2 && KMAX <= 64 * NR && (KMAX & (KMAX - 1)) == 0, "power-of-two network");
+  bitonic_merge_all<NR, 2, KMAX>(v, lane);
 }
 
 constexpr int kRelBuckets = 4096;
@@ -512,31 +518,41 @@ __device__ inline int rel_bucket(float s, float mx) {
 }
 
 // One wave places the cut inside the crossing bucket: its entries (key << 32 |
-// ~u, zero past the last), 64 NR of them, are sorted by score descending then id
-// ascending; their masses are run in that order from `above`, the mass of every
-// bucket before it; the first entry whose running mass reaches target is the
-// cut.  Sets sm.ic (its position) and sm.cut_entry.
-template <int NR>
+// ~u, zero past the last), at most KMAX of them, are sorted by score descending
+// then id ascending; their masses are run in that order from `above`, the mass
+// of every bucket before it; the first entry whose running mass reaches target
+// is the cut.  Sets sm.ic (its position) and sm.cut_entry.
+template <int NR, int KMAX = 64 * NR>
 __device__ inline void cut_in_bucket(CutSmem& sm, int cstar, float mx, int topk,
                                      unsigned long long above, double target, int lane) {
   uint64_t v[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) v[r] = (uint64_t)sm.u.h.ent[r * 64 + lane];
-  wave_sort_desc<NR>(v, lane);
-  int ic = -1;
-  unsigned long long carry = 0ull;
+  for (int r = 0; r < NR; ++r) v[r] = (uint64_t)sm.u.h.ent[NR * lane + r];
+  wave_sort_desc<NR, KMAX>(v, lane);
+  // running mass in sorted order: this lane's entries follow those of lower lanes
+  unsigned long long mi[NR], own = 0ull;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const uint64_t e = v[r];
-    unsigned long long mi = 0ull;
-    if ((uint32_t)(e >> 32) != 0u) mi = fixmass(cut_mass(key_score((uint32_t)(e >> 32)), mx, topk));
-    const unsigned long long inc = wave_incl_scan<unsigned long long>(mi) + carry;
-    const uint64_t reach = __ballot(mi != 0ull && (double)(above + inc) >= target);
-    if (ic < 0 && reach != 0ull) ic = r * 64 + __ffsll((long long)reach) - 1;
-    carry = rl64(inc, 63);
+    mi[r] = 0ull;
+    if ((uint32_t)(e >> 32) != 0u) mi[r] = fixmass(cut_mass(key_score((uint32_t)(e >> 32)), mx, topk));
+    own += mi[r];
+  }
+  unsigned long long run = above + wave_incl_scan<unsigned long long>(own) - own;
+  int rf = NR;   // this lane's first entry whose running mass reaches target
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    run += mi[r];
+    if (rf == NR && mi[r] != 0ull && (double)run >= target) rf = r;
+  }
+  const uint64_t reach = __ballot(rf < NR);
+  int ic = -1;
+  if (reach != 0ull) {
+    const int l = __ffsll((long long)reach) - 1;
+    ic = NR * l + (int)rl32((uint32_t)rf, l);
   }
   if (ic < 0 || ic > cstar - 1) ic = cstar - 1;
-  const int r_ic = ic >> 6, l_ic = ic & 63;
+  const int l_ic = ic / NR, r_ic = ic % NR;
   uint64_t ce = 0ull;
 #pragma unroll
   for (int r = 0; r < NR; ++r)
@@ -679,7 +695,8 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
     if (cstar <= kSortMax) {
       // one wave sorts the bucket in registers; the others wait at the barrier
       if (tid < kWave) {
-        if (cstar <= kWave) cut_in_bucket<1>(sm, cstar, mx, P.topk, above_b, target, lane);
+        if (cstar <= 16) cut_in_bucket<1, 16>(sm, cstar, mx, P.topk, above_b, target, lane);
+        else if (cstar <= kWave) cut_in_bucket<1>(sm, cstar, mx, P.topk, above_b, target, lane);
         else if (cstar <= 2 * kWave) cut_in_bucket<2>(sm, cstar, mx, P.topk, above_b, target, lane);
         else if (cstar <= 4 * kWave) cut_in_bucket<4>(sm, cstar, mx, P.topk, above_b, target, lane);
         else if (cstar <= 8 * kWave) cut_in_bucket<8>(sm, cstar, mx, P.topk, above_b, target, lane);
@@ -920,53 +937,59 @@ __global__ void __launch_bounds__(kCompactThreads) compact_level(CompactParams P
 constexpr int kSmallCap = 256;
 constexpr int kSmallThreads = 256;
 
-// Top-p cut of one head over a list of U <= 64*NR entries, by one wave; ORs the
+// Top-p cut of one head over a list of U <= KMAX entries, by one wave; ORs the
 // head's bit into or_bits[u] of every kept entry and returns the kept count.
-template <int NR>
+template <int NR, int KMAX = 64 * NR>
 __device__ inline int cut_head_wave(const float* sc, const uint32_t* cand_mask, uint32_t bit,
                                     int U, float p, int topk, uint32_t* or_bits, int lane) {
   uint64_t v[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    const int u = r * 64 + lane;
+    const int u = NR * lane + r;
     uint64_t e = 0ull;
     if (u < U && (cand_mask[u] & bit))
       e = ((uint64_t)order_key(sanitize(sc[u])) << 32) | (uint32_t)(~(uint32_t)u);
     v[r] = e;
   }
-  wave_sort_desc<NR>(v, lane);
+  wave_sort_desc<NR, KMAX>(v, lane);
   const uint64_t first = rl64(v[0], 0);
   if (first == 0ull) return 0;                       // no candidates
   const float mx = key_score((uint32_t)(first >> 32));
   uint64_t ms[NR];
   uint32_t nc = 0;
-  uint64_t part = 0ull;
+  uint64_t own = 0ull;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     ms[r] = (v[r] != 0ull) ? fixmass(cut_mass(key_score((uint32_t)(v[r] >> 32)), mx, topk)) : 0ull;
-    part += ms[r];
+    own += ms[r];
     nc += __popcll(__ballot(v[r] != 0ull));
   }
   int ic;
   if (topk == 0 && p >= 1.0f) {
     ic = (int)nc - 1;
   } else {
-    const uint64_t W = wave_sum_u64(part);
+    // running mass in sorted order: this lane's entries follow those of lower lanes
+    const uint64_t inc = wave_incl_scan<uint64_t>(own);
+    const uint64_t W = rl64(inc, 63);
     const double target = cut_target(p, topk, W);
-    ic = -1;
-    uint64_t carry = 0ull;
+    uint64_t run = inc - own;
+    int rf = NR;   // this lane's first entry whose running mass reaches target
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      const uint64_t inc = wave_incl_scan<uint64_t>(ms[r]) + carry;
-      const uint64_t reach = __ballot(ms[r] != 0ull && (double)inc >= target);
-      if (ic < 0 && reach != 0ull) ic = r * 64 + __ffsll((long long)reach) - 1;
-      carry = rl64(inc, 63);
+      run += ms[r];
+      if (rf == NR && ms[r] != 0ull && (double)run >= target) rf = r;
+    }
+    const uint64_t reach = __ballot(rf < NR);
+    ic = -1;
+    if (reach != 0ull) {
+      const int l = __ffsll((long long)reach) - 1;
+      ic = NR * l + (int)rl32((uint32_t)rf, l);
     }
     if (ic < 0 || ic > (int)nc - 1) ic = (int)nc - 1;
   }
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    if (v[r] != 0ull && r * 64 + lane <= ic) atomicOr(&or_bits[~(uint32_t)v[r]], bit);
+    if (v[r] != 0ull && NR * lane + r <= ic) atomicOr(&or_bits[~(uint32_t)v[r]], bit);
   }
   return ic + 1;
 }
@@ -1087,7 +1110,8 @@ __global__ void __launch_bounds__(kSmallThreads) cut_upper(UpperParams U) {
     __syncthreads();
     for (int g = wave; g < B.G; g += NW) {
       int kept;
-      if (cnt <= 64) kept = cut_head_wave<1>(s_sc[g], s_cm, 1u << g, cnt, lv.p, lv.topk, s_or, lane);
+      if (cnt <= 16) kept = cut_head_wave<1, 16>(s_sc[g], s_cm, 1u << g, cnt, lv.p, lv.topk, s_or, lane);
+      else if (cnt <= 64) kept = cut_head_wave<1>(s_sc[g], s_cm, 1u << g, cnt, lv.p, lv.topk, s_or, lane);
       else if (cnt <= 128) kept = cut_head_wave<2>(s_sc[g], s_cm, 1u << g, cnt, lv.p, lv.topk, s_or, lane);
       else kept = cut_head_wave<4>(s_sc[g], s_cm, 1u << g, cnt, lv.p, lv.topk, s_or, lane);
       if (lane == 0) lv.kept[(int64_t)gi * B.G + g] = kept;
