@@ -935,7 +935,10 @@ __global__ void __launch_bounds__(kCompactThreads) compact_level(CompactParams P
 // LDS and the kept entries compacted in list order.
 
 constexpr int kSmallCap = 256;
-constexpr int kSmallThreads = 256;
+// cut_upper runs one wave per query head of the group, and at least one thread
+// per list entry.
+template <int GP>
+constexpr int small_threads() { return 64 * GP > kSmallCap ? 64 * GP : kSmallCap; }
 
 // Top-p cut of one head over a list of U <= KMAX entries, by one wave; ORs the
 // head's bit into or_bits[u] of every kept entry and returns the kept count.
@@ -1062,8 +1065,9 @@ __global__ void __launch_bounds__(256) score_upper(UpperParams U) {
 }
 
 template <int GP>
-__global__ void __launch_bounds__(kSmallThreads) cut_upper(UpperParams U) {
-  constexpr int NW = kSmallThreads / kWave;
+__global__ void __launch_bounds__(small_threads<GP>()) cut_upper(UpperParams U) {
+  constexpr int NT = small_threads<GP>();
+  constexpr int NW = NT / kWave;
   __shared__ int32_t s_id[kSmallCap];     // this level's list: node ids
   __shared__ uint32_t s_cm[kSmallCap];    //   head masks
   __shared__ float s_sc[GP][kSmallCap];   //   scores per head
@@ -1094,7 +1098,7 @@ __global__ void __launch_bounds__(kSmallThreads) cut_upper(UpperParams U) {
       cnt = np * C + (int)(orph > 0 ? orph : 0);
     }
     if (cnt > kSmallCap) cnt = kSmallCap;
-    for (int u = tid; u < kSmallCap; u += kSmallThreads) {
+    for (int u = tid; u < kSmallCap; u += NT) {
       s_or[u] = 0u;
       if (u < cnt) {
         int32_t id;
@@ -1136,7 +1140,7 @@ __global__ void __launch_bounds__(kSmallThreads) cut_upper(UpperParams U) {
     __syncthreads();
   }
   const int nout = np < U.kcap ? np : (int)U.kcap;
-  for (int i = tid; i < nout; i += kSmallThreads) {
+  for (int i = tid; i < nout; i += NT) {
     U.kids[(int64_t)gi * U.kcap + i] = s_kid[i];
     U.kmask[(int64_t)gi * U.kcap + i] = s_km[i];
   }
@@ -1338,9 +1342,9 @@ static void launch_upper(const UpperParams& U, hipStream_t s) {
     else if (GP == 8) hipLaunchKernelGGL((score_upper<64, 8>), grid, dim3(256), 0, s, U);
     else hipLaunchKernelGGL((score_upper<64, 16>), grid, dim3(256), 0, s, U);
   }
-  if (GP == 4) hipLaunchKernelGGL((cut_upper<4>), dim3(BH), dim3(kSmallThreads), 0, s, U);
-  else if (GP == 8) hipLaunchKernelGGL((cut_upper<8>), dim3(BH), dim3(kSmallThreads), 0, s, U);
-  else hipLaunchKernelGGL((cut_upper<16>), dim3(BH), dim3(kSmallThreads), 0, s, U);
+  if (GP == 4) hipLaunchKernelGGL((cut_upper<4>), dim3(BH), dim3(small_threads<4>()), 0, s, U);
+  else if (GP == 8) hipLaunchKernelGGL((cut_upper<8>), dim3(BH), dim3(small_threads<8>()), 0, s, U);
+  else hipLaunchKernelGGL((cut_upper<16>), dim3(BH), dim3(small_threads<16>()), 0, s, U);
 }
 
 static int32_t check_route_common(const zha_cfg* cfg, const float* q, const zha_tree* tree,
