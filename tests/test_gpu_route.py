@@ -22,14 +22,20 @@ DEV = "cuda"
 SCORE_TOL = 2e-5  # |s_gpu - s_ref| / max(1, |s_ref|): fp32 dot of d terms + fp32 plane
 
 
+def t_of(T, b):
+    """Cache length of sequence b: T is one length for the batch or one per sequence."""
+    return int(T[b]) if isinstance(T, (list, tuple)) else int(T)
+
+
 def oracle_tree32(wl, T, K):
     """Oracle trees of every (b, h), rounded to fp32: list[b][h] of levels."""
     qref = f64(synth.make_qref(wl, "cpu"))
     trees = []
     for b in range(wl.B):
         row = []
+        Tb = t_of(T, b)
         for h in range(wl.H_kv):
-            t = O.build_tree(f64(K[b, h, :T]), qref[h], T, wl.C, wl.L, wl.scale,
+            t = O.build_tree(f64(K[b, h, :Tb]), qref[h], Tb, wl.C, wl.L, wl.scale,
                              wl.rope_base if wl.rope else None)
             row.append([{"khat": O.fp32(lv["khat"]), "bhat": O.fp32(lv["bhat"])} for lv in t])
         trees.append(row)
@@ -39,14 +45,15 @@ def oracle_tree32(wl, T, K):
 def upload(cfg, trees, T):
     tree = zha.Tree(cfg, DEV)
     for b in range(cfg.B):
+        Tb = t_of(T, b)
         for h in range(cfg.H_kv):
             for level in range(1, cfg.L + 1):
-                n = T // cfg.C ** level
+                n = Tb // cfg.C ** level
                 if n:
                     tree.khat[level - 1][b, h, :n] = torch.tensor(trees[b][h][level - 1]["khat"], dtype=torch.float32)
                     tree.bhat[level - 1][b, h, :n] = torch.tensor(trees[b][h][level - 1]["bhat"], dtype=torch.float32)
-    for level in range(1, cfg.L + 1):
-        tree.n_built[level - 1, :] = T // cfg.C ** level
+        for level in range(1, cfg.L + 1):
+            tree.n_built[level - 1, b] = Tb // cfg.C ** level
     return tree
 
 
@@ -62,7 +69,7 @@ def level_sync_compare(cfg, tree_gpu, trees_host, q, T, p, ws, report):
         for b in range(cfg.B):
             cb, kb = [], []
             for j in range(cfg.Hq):
-                rt = O.route(qh[b, j], trees_host[b][j // G], T, C, L, p, cfg.scale,
+                rt = O.route(qh[b, j], trees_host[b][j // G], t_of(T, b), C, L, p, cfg.scale,
                              level_override=over[b][j])
                 lr = rt.level(level)
                 cb.append(lr.cut)
