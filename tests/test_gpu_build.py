@@ -142,6 +142,41 @@ def test_append_cascade_equals_prefill_build(C, L):
     assert zha.ws_status(ws) == 0
 
 
+@pytest.mark.parametrize("C,L", [(8, 3), (16, 2)])
+def test_append_ragged_batch_equals_prefill_build(C, L):
+    """Batched decode over sequences of different lengths: every sequence grows by
+    one token per step, so each completes its chunks (and parents) at its own
+    steps; one append per step must leave the tree a prefill build of the final
+    lengths gives.  One sequence starts with two tokens (no nodes yet)."""
+    wl = _workload("gqa128k", B=3, H_kv=2, G=4, C=C, L=L, n_clusters=16)
+    T0 = [C ** L - 5, 5 * C - 1, 2]
+    steps = 2 * C + 3
+    T_cap = max(T0) + steps
+    K, V = synth.make_cache(wl.with_(N=T_cap, open_len=0, steps=0), DEV, T_cap)
+    qref = synth.make_qref(wl, DEV)
+    cfg = zha.Config(B=3, H_kv=2, G=4, d=128, C=C, L=L, R=16, T_cap=T_cap)
+    tree = zha.Tree(cfg, DEV)
+    ws = zha.new_workspace(cfg)
+    T = torch.tensor(T0, dtype=torch.int64, device=DEV)
+    zha.build(cfg, K, V, T, qref, tree, ws)
+    for _ in range(steps):
+        T += 1
+        zha.append(cfg, K, V, T, qref, tree, ws, max_new_tokens=1)
+    ref = zha.Tree(cfg, DEV)
+    zha.build(cfg, K, V, T, qref, ref, ws)
+    torch.cuda.synchronize()
+    T1 = [t + steps for t in T0]
+    for b in range(3):
+        assert tree.n_built[:, b].tolist() == [T1[b] // C ** l for l in range(1, L + 1)]
+        for level in range(1, L + 1):
+            n = T1[b] // C ** level
+            assert torch.equal(tree.khat[level - 1][b, :, :n], ref.khat[level - 1][b, :, :n]), (b, level)
+            assert torch.equal(tree.bhat[level - 1][b, :, :n], ref.bhat[level - 1][b, :, :n]), (b, level)
+    for b in range(3):
+        _compare_tree(cfg, K, qref, tree, T1[b], None, b=b, h=1)
+    assert zha.ws_status(ws) == 0
+
+
 def test_build_is_deterministic():
     wl = _workload("gqa128k", H_kv=1, G=4, C=64, L=2, n_clusters=8)
     cfg, K, V, qref, tree, ws, Tt = _build_gpu(wl, 8192)
