@@ -404,8 +404,8 @@ def cpu_baseline(run, p, s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
-              "sharding of this path is a design note, not part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the path is not "
+              "sharded over several GPUs", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -15,3 +15,12 @@ def test_graft_build_entry_compiles_and_imports():
                        timeout=900)
     assert r.returncode == 0, r.stderr[-2000:]
     assert "imports" in r.stdout
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The measurement runs on one GPU; asking for more exits with a message before
+    any device work."""
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
