@@ -8,7 +8,7 @@ down the tree (zha_route) and attend over the routed keys (zha_attend).  Inputs
 are synthetic and resident in HBM before timing starts.  The same steps are then
 timed with the dense split-K baseline (dense_attend) over every key.
 
-Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
+Prints one JSON line.  ``--gpus`` above 1 is refused: the path runs on one GPU.
 """
 from __future__ import annotations
 
