@@ -139,7 +139,7 @@ CASES = {
 
 
 @pytest.mark.parametrize("case", list(CASES))
-@pytest.mark.parametrize("p", [0.5, 0.9])
+@pytest.mark.parametrize("p", [0.05, 0.5, 0.9, 0.99])
 def test_route_level_parity_and_zha_route_composition(case, p):
     wl, T = CASES[case]
     cfg, K, V, trees = _setup(wl, T)
