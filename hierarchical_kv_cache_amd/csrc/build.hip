@@ -13,6 +13,10 @@
 //
 // Reference queries are rotated (rotate-half pairs (i, i+d/2), angle
 // pos * base^(-2i/d), fp64 angles) to the node's first key position n * C^level.
+// build_leaves_mfma takes the fp64 cosine and sine of each pair's angle,
+// advanced from leaf to leaf by one fixed fp64 rotation, and applies the
+// rotation in fp32; the other kernels compute the sine and cosine per node and
+// rotate in fp64.
 //
 // Four kernels: build_leaves_mfma (bf16 keys, C in {16, 32, 64}): one wave per
 // leaf on the matrix cores; build_leaves_small (bf16 keys, C in {2, 4, 8}): one
