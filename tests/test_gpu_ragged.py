@@ -1,17 +1,20 @@
 """A batch whose sequences hold different numbers of tokens, through the whole path.
 
-Three sequences of 20,007, 9,000 and 15 tokens share one cache of capacity
+Four sequences of 20,007, 9,000, 15 and 0 tokens share one cache of capacity
 20,007: 2 KV heads x 4 query heads, d = 128, bf16 K/V, C = 16, L = 3, R = 16.
 The third is shorter than one chunk, so it has no nodes at any level and its key
-set is the sink plus the open chunk, all of its keys.  Every level's node count
-follows each sequence's own length ([ZHA] "무엇과 다른가": one tree per KV head,
-its nodes completed as the cache grows).
+set is the sink plus the open chunk, all of its keys.  The fourth is empty: no
+keys, a zero output and lse = -inf.  Every level's node count follows each
+sequence's own length ([ZHA] "무엇과 다른가": one tree per KV head, its nodes
+completed as the cache grows).
 
 Checked against the oracle: the tree the GPU builds for every (sequence, KV
 head); the router level by level and end to end on the oracle's fp32 trees,
 each sequence at its own length; and attention over the sets the GPU routes on
 its own tree.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -25,12 +28,12 @@ from tests.test_gpu_route import level_sync_compare, oracle_tree32, upload
 pytestmark = pytest.mark.gpu
 zha = pytest.importorskip("hierarchical_kv_cache_amd.zha")
 DEV = "cuda"
-TLIST = [20007, 9000, 15]
+TLIST = [20007, 9000, 15, 0]
 
 
 @pytest.mark.parametrize("p", [0.5, 0.9])
 def test_ragged_batch_build_route_attend(p):
-    wl = synth.WORKLOADS["gqa128k"].with_(B=3, H_kv=2, G=4, C=16, L=3, n_clusters=128)
+    wl = synth.WORKLOADS["gqa128k"].with_(B=len(TLIST), H_kv=2, G=4, C=16, L=3, n_clusters=128)
     T_cap = max(TLIST)
     K, V = synth.make_cache(wl.with_(N=T_cap, open_len=0, steps=0), "cpu", T_cap)
     qref = synth.make_qref(wl, "cpu")
@@ -62,7 +65,8 @@ def test_ragged_batch_build_route_attend(p):
         for b in range(cfg.B):
             for j in range(cfg.Hq):
                 np.testing.assert_array_equal(full[b][j], leaves[b][j])
-        assert all(len(full[2][j]) == 0 for j in range(cfg.Hq))   # no leaves below one chunk
+        for b in (2, 3):   # no leaves below one chunk
+            assert all(len(full[b][j]) == 0 for j in range(cfg.Hq))
         assert zha.ws_status(ws) == 0
     for r in report:
         print("allowed:", p, r)
@@ -79,6 +83,9 @@ def test_ragged_batch_build_route_attend(p):
             Kh, Vh = f64(K[b, h, :Tb]), f64(V[b, h, :Tb])
             for g in range(cfg.G):
                 j = h * cfg.G + g
+                if Tb == 0:
+                    assert torch.all(out[b, j] == 0) and float(lse[b, j]) == -math.inf, (p, b, j)
+                    continue
                 keys = O.routed_keys(sets[b][j], Tb, cfg.C)
                 if Tb < cfg.C:
                     assert list(keys) == list(range(Tb))
