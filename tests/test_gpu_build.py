@@ -64,7 +64,8 @@ def test_build_tiny_fp32_nope():
     _compare_tree(cfg, K, qref, tree, 4096, None)
 
 
-@pytest.mark.parametrize("C,L,T,G", [(16, 3, 10000, 4), (64, 2, 9000 + 17, 4), (4, 4, 1500, 8)])
+@pytest.mark.parametrize("C,L,T,G", [(16, 3, 10000, 4), (64, 2, 9000 + 17, 4), (4, 4, 1500, 8),
+                                     (2, 8, 2 ** 8 * 3 + 37, 4)])
 def test_build_bf16_nope_levels(C, L, T, G):
     wl = _workload("gqa128k", H_kv=2, G=G, C=C, L=L, n_clusters=64)
     cfg, K, V, qref, tree, ws, Tt = _build_gpu(wl, T)

@@ -130,6 +130,8 @@ CASES = {
     # sixteen query heads per KV head: the widest head masks (scoring, cut and
     # compaction with G = 16)
     "g16": (synth.WORKLOADS["gqa128k"].with_(H_kv=1, G=16, C=16, L=3, n_clusters=128), 12000 + 3),
+    # the deepest tree (L = 8, C = 2): seven small levels in the walk, then the leaves
+    "deep8": (synth.WORKLOADS["gqa128k"].with_(H_kv=1, G=4, C=2, L=8, n_clusters=32), 2 ** 8 * 3 + 37),
     # one level of 20000 / 30000 leaves: candidate pools beyond 16384 entries (the
     # cut's LDS staging of the general path) and beyond 24576 (the staged path's
     # capacity), and final expansions longer than one register batch per wave
