@@ -131,6 +131,10 @@ def _random_sets(rng, n1, Hq, frac):
     ("bf16", 128, 8, 1, 1, 32, 0.5),
     ("bf16", 64, 4, 2, 1, 4, 0.1),
     ("bf16", 128, 4, 1, 1, 64, 1.0),
+    # group sizes that are not a power of two (padded heads must stay silent)
+    ("bf16", 128, 3, 2, 1, 64, 0.4),
+    ("bf16", 128, 6, 1, 2, 32, 0.4),
+    ("bf16", 64, 12, 1, 1, 16, 0.3),
 ])
 def test_zha_attend_matches_oracle_on_key_set(kvd, d, G, H_kv, B, C, frac):
     """out_j = attention over {0} U keys(leaves with bit j) U [C n_1, T)."""

@@ -130,6 +130,10 @@ CASES = {
     # sixteen query heads per KV head: the widest head masks (scoring, cut and
     # compaction with G = 16)
     "g16": (synth.WORKLOADS["gqa128k"].with_(H_kv=1, G=16, C=16, L=3, n_clusters=128), 12000 + 3),
+    # group sizes that are not a power of two: kernels pad the group to 4, 8 or 16
+    # heads, and the padding heads must neither score, cut nor set mask bits
+    "g3": (synth.WORKLOADS["gqa128k"].with_(H_kv=2, G=3, C=16, L=3, n_clusters=128), 9000 + 5),
+    "g6": (synth.WORKLOADS["gqa128k"].with_(H_kv=1, G=6, C=8, L=3, n_clusters=64), 4000 + 3),
     # the deepest tree (L = 8, C = 2): seven small levels in the walk, then the leaves
     "deep8": (synth.WORKLOADS["gqa128k"].with_(H_kv=1, G=4, C=2, L=8, n_clusters=32), 2 ** 8 * 3 + 37),
     # one level of 20000 / 30000 leaves: candidate pools beyond 16384 entries (the
