@@ -134,6 +134,9 @@ CASES = {
     # heads, and the padding heads must neither score, cut nor set mask bits
     "g3": (synth.WORKLOADS["gqa128k"].with_(H_kv=2, G=3, C=16, L=3, n_clusters=128), 9000 + 5),
     "g6": (synth.WORKLOADS["gqa128k"].with_(H_kv=1, G=6, C=8, L=3, n_clusters=64), 4000 + 3),
+    # the largest chunks: C = 64 and 32 with more than 256 leaves (the full cut path)
+    "c64": (synth.WORKLOADS["gqa128k"].with_(H_kv=1, G=4, C=64, L=2, n_clusters=64), 64 * 64 * 5 + 33),
+    "c32": (synth.WORKLOADS["gqa128k"].with_(H_kv=1, G=8, C=32, L=3, n_clusters=64), 32 ** 3 + 777),
     # the deepest tree (L = 8, C = 2): seven small levels in the walk, then the leaves
     "deep8": (synth.WORKLOADS["gqa128k"].with_(H_kv=1, G=4, C=2, L=8, n_clusters=32), 2 ** 8 * 3 + 37),
     # one level of 20000 / 30000 leaves: candidate pools beyond 16384 entries (the
