@@ -22,9 +22,13 @@
  *  * All pointers are DEVICE pointers unless marked (host).  Every buffer is
  *    allocated and freed by the caller; the library allocates nothing, keeps no
  *    pointer after a call returns and holds no global state.  Calls are
- *    asynchronous on ``stream`` (a hipStream_t; NULL = the null stream) and never
- *    synchronise the host.  Calls on different streams with disjoint outputs and
- *    workspaces may run concurrently.
+ *    asynchronous on ``stream`` (a hipStream_t; NULL = the null stream) and,
+ *    except zha_ws_status, never synchronise the host.  Calls on different
+ *    streams with disjoint outputs and workspaces may run concurrently.
+ *  * Stream capture: every entry point except zha_ws_status (a host
+ *    synchronisation) and zha_route_counts (device copies) only launches kernels
+ *    on ``stream``, so it can be recorded into a graph and replayed; its scalar
+ *    arguments (p, level, topk, new lengths on the host) are fixed at capture.
  *  * Layouts are row-major and dense:
  *      K, V   [B][H_kv][T_cap][d]   fp32 or bf16 (cfg.kv_dtype), keys post-RoPE
  *      T      [B] int64             current length of each sequence (device)
