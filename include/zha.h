@@ -28,7 +28,7 @@
  *  * Stream capture: every entry point except zha_ws_status (a host
  *    synchronisation) and zha_route_counts (device copies) only launches kernels
  *    on ``stream``, so it can be recorded into a graph and replayed; its scalar
- *    arguments (p, level, topk, new lengths on the host) are fixed at capture.
+ *    arguments (p, level, topk, max_new_tokens) are fixed at capture.
  *  * Layouts are row-major and dense:
  *      K, V   [B][H_kv][T_cap][d]   fp32 or bf16 (cfg.kv_dtype), keys post-RoPE
  *      T      [B] int64             current length of each sequence (device)
