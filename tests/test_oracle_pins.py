@@ -498,3 +498,97 @@ def test_level_kl_matches_brute_force_definition():
         S = np.array([max(scale * lv["khat"][i][r] @ q + lv["bhat"][i][r] for r in range(R)) for i in range(n)])
         Ph = np.exp(S) / np.exp(S).sum()
         assert abs(kl[level - 1] - float(np.sum(P * np.log(P / Ph)))) < 1e-10
+
+
+# ---------------------------------------------------------------- node positions and scores
+
+def _periodic_rope_keys(C, T, d, base, seed):
+    """Keys whose unrotated content repeats every C tokens: k_t = RoPE(u_{t mod C}, t)."""
+    rng = np.random.default_rng(seed)
+    u = rng.normal(size=(C, d)) * 1.5
+    return np.stack([O.rope(u[t % C], t, base) for t in range(T)])
+
+
+def test_rope_node_reference_query_is_at_first_key():
+    """[ZHA] '무엇과 다른가' (RoPE: a node rescores at its rotated reference query):
+    the reference query of node n at level l sits at the node's first key, n C^l.
+
+    (a) Equivariance.  When every leaf holds the same unrotated keys, the keys of
+        node n are those of node 0 rotated by n C^l (rotations compose by adding
+        angles), so node n's summary must be node 0's with k_hat rotated by n C^l and
+        b_hat unchanged; a position of n C^(l-1), or one that ignores n, breaks it.
+    (b) Anchor.  Position 0 is the identity rotation, so leaf 0 is the plain leaf
+        formula at the unrotated reference queries; the last key as the position
+        (an offset shared by every node, which (a) cannot see) breaks it.
+    (c) Tangency at the stated point, computed here with rope() and not with the
+        oracle's own position helper: every plane r of node n touches its target at
+        q* = RoPE(q_ref[r], n C^l) -- the exact log-mass of the leaf's keys, or the
+        LSE of the children's planes r for a parent -- and stays below it elsewhere.
+    """
+    base, C, L, R, d = 40.0, 4, 3, 3, 8
+    rng = np.random.default_rng(21)
+    qref = rng.normal(size=(R, d)) / math.sqrt(d)
+    scale = 1 / math.sqrt(d)
+    T = C ** L * 2 + C + 1
+    K = _periodic_rope_keys(C, T, d, base, seed=22)
+    tree = O.build_tree(K, qref, T, C, L, scale, base)
+    for level in range(1, L + 1):
+        lv = tree[level - 1]
+        for n in range(1, lv["khat"].shape[0]):
+            for r in range(R):
+                np.testing.assert_allclose(lv["khat"][n, r], O.rope(lv["khat"][0, r], n * C ** level, base),
+                                           rtol=0, atol=1e-10)
+                assert abs(lv["bhat"][n, r] - lv["bhat"][0, r]) < 1e-10
+    for r in range(R):
+        kh, bh = O.leaf_summary(qref[r], K[0:C], scale)
+        np.testing.assert_allclose(tree[0]["khat"][0, r], kh, rtol=0, atol=1e-13)
+        assert abs(tree[0]["bhat"][0, r] - bh) < 1e-13
+
+    # (c) on keys with no period
+    K, V, qref, tree, T, C, L, scale = _small_tree(rope_base=base, seed=23)
+    probes = [rng.normal(size=K.shape[1]) * s for s in (0.5, 2.0)]
+    for level in range(1, L + 1):
+        lv = tree[level - 1]
+        for n in range(lv["khat"].shape[0]):
+            for r in range(qref.shape[0]):
+                qs = O.rope(qref[r], n * C ** level, base)
+                if level == 1:
+                    def target(q):
+                        return _subtree_lse(q, K, n, 1, C, scale)
+                else:
+                    ch = tree[level - 2]
+                    kids = range(n * C, (n + 1) * C)
+
+                    def target(q):
+                        return O.logsumexp([O.plane(q, ch["khat"][c, r], ch["bhat"][c, r], scale)
+                                            for c in kids])
+                t_at = O.plane(qs, lv["khat"][n, r], lv["bhat"][n, r], scale)
+                assert abs(t_at - target(qs)) < 1e-11 * max(1.0, abs(t_at)), (level, n, r)
+                for q in probes:
+                    assert O.plane(q, lv["khat"][n, r], lv["bhat"][n, r], scale) <= target(q) + 1e-9
+
+
+def test_node_score_is_the_best_plane():
+    """[ZHA] '무엇과 다른가': a node's estimated log-mass is the maximum of its R
+    tangent planes.  Every plane is below the convex log-mass F, so the score is too
+    (a sum of planes is not); at a leaf's tangent point q_hat_r plane r equals F and
+    the others are below it, so the score equals F there (a minimum or a mean of
+    the planes does not)."""
+    K, V, qref, tree, T, C, L, scale = _small_tree(None, R=4, seed=24)
+    R = qref.shape[0]
+    rng = np.random.default_rng(25)
+    lv = tree[0]
+    strict = 0
+    for n in range(lv["khat"].shape[0]):
+        for _ in range(3):
+            q = rng.normal(size=K.shape[1]) * 2
+            F = _subtree_lse(q, K, n, 1, C, scale)
+            assert O.node_score(q, lv["khat"][n], lv["bhat"][n], scale) <= F + 1e-12 * max(1, abs(F))
+        for r in range(R):
+            F = _subtree_lse(qref[r], K, n, 1, C, scale)
+            s = O.node_score(qref[r], lv["khat"][n], lv["bhat"][n], scale)
+            assert abs(s - F) < 1e-11 * max(1.0, abs(F))
+            others = [O.plane(qref[r], lv["khat"][n, x], lv["bhat"][n, x], scale) for x in range(R) if x != r]
+            strict += int(max(others) < F - 1e-6)
+    # the test has teeth: the other planes are strictly below F at most tangent points
+    assert strict > lv["khat"].shape[0]
