@@ -1347,12 +1347,19 @@ static void launch_upper(const UpperParams& U, hipStream_t s) {
   else hipLaunchKernelGGL((cut_upper<16>), dim3(BH), dim3(small_threads<16>()), 0, s, U);
 }
 
+// Top-p masses are summed as w 2^40 (w <= 1) in 64 bits, so a cut pool of n
+// entries sums to at most n 2^40, which fits while n < 2^24.  The largest pool
+// a route cuts is level 1's union list, at most T_cap / C entries; an explicit
+// list of zha_route_level holds at most cand_cap.
+constexpr int64_t kMaxCutPool = (int64_t(1) << 24) - 1;
+
 static int32_t check_route_common(const zha_cfg* cfg, const float* q, const zha_tree* tree,
                                   const float* p, int np) {
   int32_t rc = zha_check_cfg(cfg);
   if (rc != ZHA_OK) return rc;
   if (cfg->G > 16) return ZHA_EUNSUPPORTED;
   if ((int64_t)cfg->B * cfg->H_kv > 65535) return ZHA_EUNSUPPORTED;
+  if (level_cap(*cfg, 1) > kMaxCutPool) return ZHA_EUNSUPPORTED;
   if (q == nullptr || tree == nullptr || p == nullptr) return ZHA_EINVAL;
   for (int i = 0; i < np; ++i)
     if (!(p[i] > 0.0f) || !(p[i] <= 1.0f)) return ZHA_EINVAL;
@@ -1541,6 +1548,7 @@ extern "C" int32_t zha_route_level(const zha_cfg* cfg, int32_t level, const floa
   if (rc != ZHA_OK) return rc;
   const WsLayout w = ws_layout(*cfg);
   if ((int64_t)cand_cap > w.stage_cap) return ZHA_EINVAL;
+  if ((int64_t)cand_cap > kMaxCutPool) return ZHA_EUNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   LevelParams P = level_params(cfg, q, tree, level, p, ws, w);
   P.list.ids = cand_ids; P.list.mask = cand_mask; P.list.count = cand_count;

@@ -64,7 +64,8 @@ extern "C" {
 enum zha_status {
   ZHA_OK = 0,
   ZHA_EINVAL = 1,        /* null pointer, bad shape, p not in (0,1], bad level */
-  ZHA_EUNSUPPORTED = 2,  /* d not in {64,128}, C not a power of two in [2,64], dtype */
+  ZHA_EUNSUPPORTED = 2,  /* d not in {64,128}, C not a power of two in [2,64], dtype;
+                            routing: a cut pool above 2^24 - 1 entries (T_cap / C) */
   ZHA_EWORKSPACE = 3,    /* ws_bytes smaller than zha_workspace_bytes() */
   ZHA_ECAPACITY = 4,     /* a list would exceed its capacity (device-detected) */
   ZHA_EHIP = 5,          /* a HIP launch or runtime call failed */
@@ -158,7 +159,11 @@ int32_t zha_append(const zha_cfg* cfg, const zha_kv* kv, const float* qref,
  * leaves of all G heads of a group are written as one leaf list (ascending ids,
  * head masks).  The sink token and the open chunk are not in the list; zha_attend
  * adds them.  Requires a current tree (n_built == T / C^l, else ZHA_ESTALE in the
- * workspace status) and cfg.leaf_cap >= T_cap / C.
+ * workspace status) and cfg.leaf_cap >= T_cap / C.  The cut sums masses exactly
+ * as 64-bit fixed point (w 2^40, w <= 1), so every routing call (zha_route,
+ * _sched, _topk, _quality, _level) returns ZHA_EUNSUPPORTED when a pool could
+ * exceed 2^24 - 1 entries: T_cap / C (level 1, the largest), or cand_cap for
+ * zha_route_level.
  */
 int32_t zha_route(const zha_cfg* cfg, const float* q, const zha_tree* tree,
                   const int64_t* T, float p,

@@ -117,3 +117,30 @@ def test_p_schedules_multiply_to_p():
         assert zha.p_schedule("uniform", 0.8, L) == [0.8] * L
     pw = zha.p_schedule("power", 0.8, 4, gamma=1.0)
     assert pw == sorted(pw)   # the leaf level cuts hardest
+
+
+def test_cut_pool_beyond_fixed_point_range_is_rejected():
+    """The cut sums masses as w 2^40 in 64 bits: a level-1 pool of 2^24 or more
+    entries could wrap, so such a geometry is refused before any launch, while
+    the largest pool that fits is accepted."""
+    C = 2
+    ok = zha.Config(B=1, H_kv=1, G=4, d=64, C=C, L=2, R=4, T_cap=((1 << 24) - 1) * C)
+    big = zha.Config(B=1, H_kv=1, G=4, d=64, C=C, L=2, R=4, T_cap=(1 << 24) * C)
+    huge_ws = 1 << 40   # sizes are checked, never touched: nothing is launched
+    assert _route(big, ws_bytes=huge_ws) == zha.EUNSUPPORTED
+    rc = _route(ok, ws_bytes=huge_ws, q=0)   # passes the pool check, fails on the null q
+    assert rc == zha.EINVAL
+    # zha_route_level: an explicit list longer than the limit
+    cfg = zha.Config(B=1, H_kv=1, G=4, d=64, C=C, L=2, R=4, T_cap=(1 << 24) * C + 8,
+                     leaf_cap=1 << 25)
+    fake = ctypes.c_void_p(0x1000)
+    tree = zha._Tree()
+    for i in range(cfg.L):
+        tree.khat[i] = 0x2000
+        tree.bhat[i] = 0x3000
+        tree.n_cap[i] = cfg.level_cap(i + 1)
+    tree.n_built = 0x4000
+    rc = zha._lib.zha_route_level(ctypes.byref(cfg.c()), 1, fake, ctypes.byref(tree), ctypes.c_float(0.9),
+                                  fake, fake, fake, 1 << 24, fake, fake, ctypes.c_void_p(0x100000),
+                                  huge_ws, None)
+    assert rc == zha.EUNSUPPORTED
