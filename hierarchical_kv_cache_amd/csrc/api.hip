@@ -7,7 +7,7 @@ extern "C" size_t zha_workspace_bytes(const zha_cfg* cfg, int32_t op) {
   if (cfg == nullptr || zha_check_cfg(cfg) != ZHA_OK) return 0;
   zha::WsLayout w = zha::ws_layout(*cfg);
   switch (op) {
-    case ZHA_OP_BUILD: return 256;
+    case ZHA_OP_BUILD: return w.build_off + w.build_bytes;
     case ZHA_OP_ROUTE: return w.route_off + w.route_bytes;
     case ZHA_OP_ATTEND:
     case ZHA_OP_DENSE:

@@ -103,58 +103,65 @@ __device__ inline void plane_softmax(BuildSmem& sm, int R, int C) {
   }
 }
 
-__global__ void __launch_bounds__(256) build_leaves(BuildParams P) {
+// One leaf of sequence-head gi (head h) summarised by a whole workgroup of
+// kGenericThreads threads: keys and reference queries staged in LDS as fp32.
+constexpr int kGenericThreads = 256;
+
+__device__ inline void generic_leaf(const BuildParams& P, BuildSmem& sm, int gi, int h, int64_t n) {
+  constexpr int NW = kGenericThreads / kWave;
+  const int d = P.d, C = P.C, R = P.R;
+  // keys of the leaf -> LDS fp32
+  const int64_t row0 = (int64_t)gi * P.T_cap + n * C;
+  if (P.kv_dtype == ZHA_BF16) {
+    const uint16_t* Kb = (const uint16_t*)P.K + row0 * d;
+    for (int idx = threadIdx.x; idx < C * d / 2; idx += kGenericThreads) {
+      const uint32_t pr = ((const uint32_t*)Kb)[idx];
+      const int e = idx * 2;
+      sm.k[e / d][e % d] = bf16_lo(pr);
+      sm.k[e / d][e % d + 1] = bf16_hi(pr);
+    }
+  } else {
+    const float* Kf = (const float*)P.K + row0 * d;
+    for (int idx = threadIdx.x; idx < C * d; idx += kGenericThreads)
+      sm.k[idx / d][idx % d] = Kf[idx];
+  }
+  load_ref_queries(P, h, n * C, &sm.qh[0][0], kMaxD + 1);
+  __syncthreads();
+  // logits z[r][j] = scale * q_hat_r . k_j; thread: key j = t % 64, planes t/64 + NW i
+  {
+    const int j = threadIdx.x & 63;
+    const int r0 = threadIdx.x >> 6;
+    if (j < C) {
+      for (int r = r0; r < R; r += NW) {
+        float acc = 0.0f;
+        for (int c = 0; c < d; ++c) acc += sm.qh[r][c] * sm.k[j][c];
+        sm.z[r][j] = acc * P.scale;
+      }
+    }
+  }
+  __syncthreads();
+  plane_softmax(sm, R, C);
+  __syncthreads();
+  // k_hat[r][c] = sum_j w[r][j] k[j][c]
+  float* kh = P.khat + (((int64_t)gi * P.ncap + n) * R) * d;
+  for (int idx = threadIdx.x; idx < R * d; idx += kGenericThreads) {
+    const int r = idx / d, c = idx % d;
+    float acc = 0.0f;
+    for (int j = 0; j < C; ++j) acc += sm.w[r][j] * sm.k[j][c];
+    kh[idx] = acc;
+  }
+  if (threadIdx.x < R)
+    P.bhat[((int64_t)gi * P.ncap + n) * R + threadIdx.x] = sm.F[threadIdx.x] - sm.wz[threadIdx.x];
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(kGenericThreads) build_leaves(BuildParams P) {
   __shared__ BuildSmem sm;
   const int gi = blockIdx.y;
   const int b = gi / P.H_kv, h = gi % P.H_kv;
   int64_t n0, n1;
   node_range(P, b, n0, n1);
-  const int d = P.d, C = P.C, R = P.R;
-  for (int64_t n = n0 + blockIdx.x; n < n1; n += gridDim.x) {
-    // keys of the leaf -> LDS fp32
-    const int64_t row0 = (int64_t)gi * P.T_cap + n * C;
-    if (P.kv_dtype == ZHA_BF16) {
-      const uint16_t* Kb = (const uint16_t*)P.K + row0 * d;
-      for (int idx = threadIdx.x; idx < C * d / 2; idx += blockDim.x) {
-        const uint32_t pr = ((const uint32_t*)Kb)[idx];
-        const int e = idx * 2;
-        sm.k[e / d][e % d] = bf16_lo(pr);
-        sm.k[e / d][e % d + 1] = bf16_hi(pr);
-      }
-    } else {
-      const float* Kf = (const float*)P.K + row0 * d;
-      for (int idx = threadIdx.x; idx < C * d; idx += blockDim.x)
-        sm.k[idx / d][idx % d] = Kf[idx];
-    }
-    load_ref_queries(P, h, n * C, &sm.qh[0][0], kMaxD + 1);
-    __syncthreads();
-    // logits z[r][j] = scale * q_hat_r . k_j; thread: key j = t % 64, planes t/64 + 4i
-    {
-      const int j = threadIdx.x & 63;
-      const int r0 = threadIdx.x >> 6;
-      if (j < C) {
-        for (int r = r0; r < R; r += 4) {
-          float acc = 0.0f;
-          for (int c = 0; c < d; ++c) acc += sm.qh[r][c] * sm.k[j][c];
-          sm.z[r][j] = acc * P.scale;
-        }
-      }
-    }
-    __syncthreads();
-    plane_softmax(sm, R, C);
-    __syncthreads();
-    // k_hat[r][c] = sum_j w[r][j] k[j][c]
-    float* kh = P.khat + (((int64_t)gi * P.ncap + n) * R) * d;
-    for (int idx = threadIdx.x; idx < R * d; idx += blockDim.x) {
-      const int r = idx / d, c = idx % d;
-      float acc = 0.0f;
-      for (int j = 0; j < C; ++j) acc += sm.w[r][j] * sm.k[j][c];
-      kh[idx] = acc;
-    }
-    if (threadIdx.x < R)
-      P.bhat[((int64_t)gi * P.ncap + n) * R + threadIdx.x] = sm.F[threadIdx.x] - sm.wz[threadIdx.x];
-    __syncthreads();
-  }
+  for (int64_t n = n0 + blockIdx.x; n < n1; n += gridDim.x) generic_leaf(P, sm, gi, h, n);
 }
 
 // ---------------------------------------------------------------- leaves on MFMA
@@ -191,40 +198,39 @@ __device__ inline void split3(float x, __bf16& hi, __bf16& mid, __bf16& lo) {
 //                          B = the leaf's keys as loaded (row = key, 8 dims)
 //   softmax over keys per plane in registers, b_hat = F - sum_j w_j z_j
 //   k_hat^T = K^T W^T      A = K^T through LDS, B = W (3-way bf16 split)
-// A wave loops over leaves with the next leaf's keys in flight; no workgroup
-// barriers are needed (a workgroup is one wave).
+// The wave's LDS (kLds bytes) holds K^T and W; the query staging aliases K^T.
+// Only the wave's own lanes touch it, so wave-level LDS syncs order it.
 template <int D, int C>
-__global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
-  constexpr int KST = D / 32;              // dimension steps of Z
-  constexpr int NT = C / 16;               // key tiles of Z
-  constexpr int CK = C < 32 ? 32 : C;      // keys padded to whole contraction steps
-  constexpr int KS2 = CK / 32;             // key steps of k_hat
-  constexpr int KP = CK + 8;               // K^T row stride (bf16 elements)
-  constexpr int WP = CK + 4;               // W row stride (floats)
-  constexpr int H2 = D / 2;
-  constexpr int KT_BYTES = D * KP * 2;
+struct MfmaLeaf {
+  static constexpr int KST = D / 32;              // dimension steps of Z
+  static constexpr int NT = C / 16;               // key tiles of Z
+  static constexpr int CK = C < 32 ? 32 : C;      // keys padded to whole contraction steps
+  static constexpr int KS2 = CK / 32;             // key steps of k_hat
+  static constexpr int KP = CK + 8;               // K^T row stride (bf16 elements)
+  static constexpr int WP = CK + 4;               // W row stride (floats)
+  static constexpr int H2 = D / 2;
+  static constexpr int KT_BYTES = D * KP * 2;
+  static constexpr int kLds = KT_BYTES + 16 * WP * 4;
   static_assert(16 * (D + 4) * 4 <= KT_BYTES, "query staging aliases K^T");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[KT_BYTES + 16 * WP * 4];
-  uint16_t (*kt)[KP] = reinterpret_cast<uint16_t (*)[KP]>(lds);
-  float (*qs)[D + 4] = reinterpret_cast<float (*)[D + 4]>(lds);   // before K^T is written
-  float (*wsm)[WP] = reinterpret_cast<float (*)[WP]>(lds + KT_BYTES);
-  const int gi = blockIdx.y;
-  const int b = gi / P.H_kv, h = gi % P.H_kv;
-  const int lane = threadIdx.x, row = lane & 15, kg = lane >> 4;
-  const int R = P.R;
-  int64_t n0, n1;
-  node_range(P, b, n0, n1);
-  const float* qr = P.qref + (int64_t)h * R * D;
-  // weights of the padded keys C..CK-1 stay zero
-  for (int i = lane; i < 16 * WP; i += 64) (&wsm[0][0])[i] = 0.0f;
-  // RoPE: lane handles frequency lane % (d/2) for every plane it stages
-  double theta = 0.0;
-  if (P.rope) theta = pow((double)P.rope_base, -2.0 * (double)(lane % H2) / (double)D);
+  typedef u32x4b_t Keys[NT][KST];
+  typedef bf16x8b_t QOps[3][KST];
 
-  bf16x8b_t qa[3][KST];
-  // (cs, sn): cos and sin of this lane's RoPE angle at the current leaf
-  auto build_qa = [&](double cs, double sn) {
-    __syncthreads();                       // the previous leaf's K^T reads are done
+  // The weights of the padded keys C..CK-1 stay zero.
+  __device__ static void init(unsigned char* lds, int lane) {
+    float* wsm = reinterpret_cast<float*>(lds + KT_BYTES);
+    for (int i = lane; i < 16 * WP; i += 64) wsm[i] = 0.0f;
+  }
+
+  // The scaled reference queries of head h as split MFMA A operands; under RoPE
+  // rotated by the angle whose cosine and sine (of this lane's frequency,
+  // lane % (d/2)) are cs and sn.
+  __device__ static void build_qa(const BuildParams& P, int h, double cs, double sn,
+                                  unsigned char* lds, QOps& qa, int lane) {
+    float (*qs)[D + 4] = reinterpret_cast<float (*)[D + 4]>(lds);
+    const int row = lane & 15, kg = lane >> 4;
+    const int R = P.R;
+    const float* qr = P.qref + (int64_t)h * R * D;
+    wave_lds_sync();                       // the previous leaf's K^T reads are done
     if (!P.rope) {
       for (int i = lane; i < 16 * D; i += 64) {
         const int r = i / D, c = i % D;
@@ -246,7 +252,7 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
         qs[r][c + H2] = x2 * P.scale;
       }
     }
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int s = 0; s < KST; ++s) {
       bf16x8b_t a0, a1, a2;
@@ -258,39 +264,29 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
       }
       qa[0][s] = a0; qa[1][s] = a1; qa[2][s] = a2;
     }
-    __syncthreads();                       // K^T may overwrite the staging now
-  };
-  if (!P.rope) build_qa(1.0, 0.0);
+    wave_lds_sync();                       // K^T may overwrite the staging now
+  }
 
-  // lane's share of a leaf: keys 16t + row, dimensions 32s + 8kg .. +8
-  const uint16_t* Kb = (const uint16_t*)P.K;
-  auto fetch = [&](int64_t n, u32x4b_t (&v)[NT][KST]) {
-    const uint16_t* kr = Kb + ((int64_t)gi * P.T_cap + n * C + row) * D + kg * 8;
+  // This lane's share of leaf n's keys: keys 16t + row, dimensions 32s + 8kg .. +8.
+  __device__ static void fetch(const BuildParams& P, int gi, int64_t n, Keys& v, int lane) {
+    const int row = lane & 15, kg = lane >> 4;
+    const uint16_t* kr = (const uint16_t*)P.K + ((int64_t)gi * P.T_cap + n * C + row) * D + kg * 8;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int s = 0; s < KST; ++s)
         v[t][s] = __builtin_nontemporal_load((const u32x4b_t*)(kr + t * 16 * D + s * 32));
-  };
-  u32x4b_t kv[NT][KST];
-  // leaves n and n+1 share a line of b-hat: their workgroups share an XCD
-  int64_t n = n0 + xcd_grouped_x();
-  if (n < n1) fetch(n, kv);
-  // RoPE angle of this lane's frequency at leaf n, advanced by the fixed step of
-  // gridDim.x leaves per iteration with one fp64 rotation (the angle pos * theta,
-  // pos = n C, to ~1e-14 over a few hundred steps) instead of a sincos per leaf
-  double rc = 1.0, rs = 0.0, dc = 1.0, ds = 0.0;
-  if (P.rope) {
-    sincos((double)(n * C) * theta, &rs, &rc);
-    sincos((double)((int64_t)gridDim.x * C) * theta, &ds, &dc);
   }
-  for (; n < n1; n += gridDim.x) {
-    if (P.rope) {
-      build_qa(rc, rs);
-      const double c2 = rc * dc - rs * ds, s2 = rs * dc + rc * ds;
-      rc = c2;
-      rs = s2;
-    }
+
+  // Leaf n of sequence-head gi from its keys kv.  `next` is called once K^T is
+  // in LDS and kv is free, to put the following leaf's keys in flight.
+  template <class Next>
+  __device__ static void leaf(const BuildParams& P, int gi, int64_t n, Keys& kv, const QOps& qa,
+                              unsigned char* lds, int lane, Next&& next) {
+    uint16_t (*kt)[KP] = reinterpret_cast<uint16_t (*)[KP]>(lds);
+    float (*wsm)[WP] = reinterpret_cast<float (*)[WP]>(lds + KT_BYTES);
+    const int row = lane & 15, kg = lane >> 4;
+    const int R = P.R;
     // ---- Z: z[t][i] = logit of plane 4kg + i, key 16t + row
     f32x4b_t z[NT];
 #pragma unroll
@@ -315,7 +311,7 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
           kt[32 * s + 8 * kg + 2 * e][16 * t + row] = (uint16_t)(x & 0xffffu);
           kt[32 * s + 8 * kg + 2 * e + 1][16 * t + row] = (uint16_t)(x >> 16);
         }
-    if (n + gridDim.x < n1) fetch(n + gridDim.x, kv);
+    next();
     // ---- softmax over the leaf's keys, per plane (16 lanes share a plane)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -343,7 +339,7 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) wsm[pl][16 * t + row] = e[t] / S;
     }
-    __syncthreads();
+    wave_lds_sync();
     // ---- k_hat^T = K^T W^T; acc[i] = k_hat of plane row, dimension 16td + 4kg + i
     bf16x8b_t wb[3][KS2];
 #pragma unroll
@@ -369,7 +365,50 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
       }
       if (row < R) *(float4*)(kh + (int64_t)row * D + 16 * td + 4 * kg) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
-    __syncthreads();                       // K^T and W are reused by the next leaf
+    wave_lds_sync();                       // K^T and W are reused by the next leaf
+  }
+};
+
+// Prefill: one wave per workgroup loops over leaves with the next leaf's keys in
+// flight.  Under RoPE the reference queries are rotated per leaf; the fp64 angle
+// of each dimension pair, shared by the R planes, advances by one fixed rotation
+// from leaf to leaf (a sincos only at a wave's first leaf).
+template <int D, int C>
+__global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
+  using M = MfmaLeaf<D, C>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[M::kLds];
+  const int gi = blockIdx.y;
+  const int b = gi / P.H_kv, h = gi % P.H_kv;
+  const int lane = threadIdx.x;
+  int64_t n0, n1;
+  node_range(P, b, n0, n1);
+  M::init(lds, lane);
+  // RoPE: lane handles frequency lane % (d/2) for every plane it stages
+  double theta = 0.0;
+  if (P.rope) theta = pow((double)P.rope_base, -2.0 * (double)(lane % M::H2) / (double)D);
+  typename M::QOps qa;
+  if (!P.rope) M::build_qa(P, h, 1.0, 0.0, lds, qa, lane);
+  typename M::Keys kv;
+  // leaves n and n+1 share a line of b-hat: their workgroups share an XCD
+  int64_t n = n0 + xcd_grouped_x();
+  if (n < n1) M::fetch(P, gi, n, kv, lane);
+  // RoPE angle of this lane's frequency at leaf n, advanced by the fixed step of
+  // gridDim.x leaves per iteration with one fp64 rotation (the angle pos * theta,
+  // pos = n C, to ~1e-14 over a few hundred steps) instead of a sincos per leaf
+  double rc = 1.0, rs = 0.0, dc = 1.0, ds = 0.0;
+  if (P.rope) {
+    sincos((double)(n * C) * theta, &rs, &rc);
+    sincos((double)((int64_t)gridDim.x * C) * theta, &ds, &dc);
+  }
+  for (; n < n1; n += gridDim.x) {
+    if (P.rope) {
+      M::build_qa(P, h, rc, rs, lds, qa, lane);
+      const double c2 = rc * dc - rs * ds, s2 = rs * dc + rc * ds;
+      rc = c2;
+      rs = s2;
+    }
+    const int64_t nn = n + gridDim.x;
+    M::leaf(P, gi, n, kv, qa, lds, lane, [&] { if (nn < n1) M::fetch(P, gi, nn, kv, lane); });
   }
 }
 
@@ -401,26 +440,21 @@ __device__ inline void halve_round(float* a, int lane) {
   }
 }
 
+// One leaf per wave; the wave's LDS holds the 16 scaled reference queries (qv,
+// [16][D]) and the leaf's softmax weights (w, [16][CP]).
 template <int D, int CP>
-__global__ void __launch_bounds__(256) build_leaves_small(BuildParams P) {
+struct SmallLeaf {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(CP == 4 || CP == 8, "padded keys");
-  constexpr int DPL = D / 64;             // dimensions per lane
-  constexpr int PP = 32 / CP;             // planes per pass
-  constexpr int H2 = D / 2;
-  __shared__ float wsh[4][16][CP];        // per wave: the leaf's softmax weights
-  __shared__ __attribute__((aligned(16))) float qsh[4][16][D];   // per wave: scaled queries
-  const int gi = blockIdx.y;
-  const int b = gi / P.H_kv, h = gi % P.H_kv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int C = P.C, R = P.R;
-  int64_t n0, n1;
-  node_range(P, b, n0, n1);
-  const float* qr = P.qref + (int64_t)h * R * D;
-  const int d0 = DPL * lane;
-  // the 16 scaled reference queries at this lane's dimensions, into the wave's LDS
-  float (*qv)[D] = qsh[wave];
-  auto set_q = [&](int64_t pos) {
+  static constexpr int DPL = D / 64;             // dimensions per lane
+  static constexpr int PP = 32 / CP;             // planes per pass
+  static constexpr int H2 = D / 2;
+
+  // The reference queries of head h at this lane's dimensions, rotated to
+  // position pos under RoPE, scaled, into the wave's LDS.
+  __device__ static void set_q(const BuildParams& P, int h, int64_t pos, float (*qv)[D], int lane) {
+    const int R = P.R, d0 = DPL * lane;
+    const float* qr = P.qref + (int64_t)h * R * D;
     if (!P.rope) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -446,17 +480,17 @@ __global__ void __launch_bounds__(256) build_leaves_small(BuildParams P) {
       }
     }
     wave_lds_sync();
-  };
-  if (!P.rope) set_q(0);
-  const uint16_t* Kb = (const uint16_t*)P.K;
-  const int64_t nw = (int64_t)gridDim.x * 4;
-  // after a pass's butterfly: entry e = lane / 2, plane PP pass + e / CP, key e % CP
-  const int e = lane >> 1, jl = e % CP, rl = e / CP;
-  for (int64_t n = n0 + (int64_t)xcd_grouped_x() * 4 + wave; n < n1; n += nw) {
-    if (P.rope) set_q(n * C);              // (after the previous leaf's closing sync)
+  }
+
+  // Leaf n of sequence-head gi, with the queries already in qv.
+  __device__ static void leaf(const BuildParams& P, int gi, int64_t n, const float (*qv)[D],
+                              float (*wsh)[CP], int lane) {
+    const int C = P.C, R = P.R, d0 = DPL * lane;
+    // after a pass's butterfly: entry e = lane / 2, plane PP pass + e / CP, key e % CP
+    const int e = lane >> 1, jl = e % CP, rl = e / CP;
     // this lane's dimensions of the leaf's keys (padding keys zero)
     float kv[CP][DPL];
-    const uint16_t* kr = Kb + ((int64_t)gi * P.T_cap + n * C) * D + d0;
+    const uint16_t* kr = (const uint16_t*)P.K + ((int64_t)gi * P.T_cap + n * C) * D + d0;
 #pragma unroll
     for (int j = 0; j < CP; ++j) {
       if constexpr (DPL == 2) {
@@ -505,7 +539,7 @@ __global__ void __launch_bounds__(256) build_leaves_small(BuildParams P) {
       // b_hat = F - sum_j w_j z_j, F = M + log S
       if ((lane & (2 * CP - 1)) == 0 && r < R)
         P.bhat[((int64_t)gi * P.ncap + n) * R + r] = (M + logf(S)) - SZ / S;
-      if ((lane & 1) == 0) wsh[wave][r][jl] = ex / S;
+      if ((lane & 1) == 0) wsh[r][jl] = ex / S;
     }
     wave_lds_sync();
     // k_hat of every plane at this lane's dimensions
@@ -518,7 +552,7 @@ __global__ void __launch_bounds__(256) build_leaves_small(BuildParams P) {
         for (int k = 0; k < DPL; ++k) acc[k] = 0.0f;
 #pragma unroll
         for (int j = 0; j < CP; ++j) {
-          const float w = wsh[wave][rr][j];      // the same address in every lane
+          const float w = wsh[rr][j];            // the same address in every lane
 #pragma unroll
           for (int k = 0; k < DPL; ++k) acc[k] = fmaf(w, kv[j][k], acc[k]);
         }
@@ -528,120 +562,255 @@ __global__ void __launch_bounds__(256) build_leaves_small(BuildParams P) {
     }
     wave_lds_sync();                       // the weights are rewritten by the next leaf
   }
+};
+
+template <int D, int CP>
+__global__ void __launch_bounds__(256) build_leaves_small(BuildParams P) {
+  using S = SmallLeaf<D, CP>;
+  __shared__ float wsh[4][16][CP];        // per wave: the leaf's softmax weights
+  __shared__ __attribute__((aligned(16))) float qsh[4][16][D];   // per wave: scaled queries
+  const int gi = blockIdx.y;
+  const int b = gi / P.H_kv, h = gi % P.H_kv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t n0, n1;
+  node_range(P, b, n0, n1);
+  if (!P.rope) S::set_q(P, h, 0, qsh[wave], lane);
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  for (int64_t n = n0 + (int64_t)xcd_grouped_x() * 4 + wave; n < n1; n += nw) {
+    if (P.rope) S::set_q(P, h, n * P.C, qsh[wave], lane);   // (after the previous leaf's closing sync)
+    S::leaf(P, gi, n, qsh[wave], wsh[wave], lane);
+  }
 }
 
 // Parent summaries, one wave per (node, plane) pair: the children's planes r
 // (child 4t + lane/16, dimensions (lane%16)*d/16 ..) stay in registers, and an
 // exact two-pass softmax over the children gives k_hat and b_hat.  No LDS, no
-// workgroup barriers.
+// workgroup barriers.  MT: child rounds, ceil(C / 4).
+
+// RoPE frequency of this lane, lane % (d/2) (shared with the others by shuffles).
+template <int D>
+__device__ inline double parent_theta(const BuildParams& P, int lane) {
+  return P.rope ? pow((double)P.rope_base, -2.0 * (double)(lane % (D / 2)) / (double)D) : 0.0;
+}
+
 template <int D, int MT>
-__global__ void __launch_bounds__(256) build_parents(BuildParams P) {
+__device__ inline void parent_pair(const BuildParams& P, int gi, int h, int64_t n, int r,
+                                   double theta, int lane) {
   static_assert(MT >= 1 && 4 * MT <= kMaxC, "child rounds");
   constexpr int DPL = D / 16;              // dimensions per lane
   constexpr int NV = DPL / 4;              // float4 per child per lane
-  constexpr int H2 = D / 2;                // MT: child rounds, ceil(C / 4)
+  constexpr int H2 = D / 2;
+  const int cg = lane >> 4, ds = (lane & 15) * DPL;
+  const int C = P.C, R = P.R;
+  const float* qr = P.qref + (int64_t)h * R * D;
+  const int64_t ch0 = n * C;
+  float4 v[MT][NV];
+  const float* src = P.khat_ch + (((int64_t)gi * P.ncap_ch + ch0 + cg) * R + r) * D + ds;
+  const int64_t cstep = (int64_t)4 * R * D;
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+      v[t][q] = 4 * t + cg < C ? *(const float4*)(src + t * cstep + 4 * q)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float bl = lane < C ? P.bhat_ch[((int64_t)gi * P.ncap_ch + ch0 + lane) * R + r] : 0.0f;
+  // plane r's reference query at the node's first key position
+  float qv[DPL];
+  if (!P.rope) {
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) qv[k] = qr[r * D + ds + k];
+  } else {
+    double sn, cs;
+    sincos((double)(n * P.span) * theta, &sn, &cs);
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+      const int c = ds + k, i = c < H2 ? c : c - H2;
+      const double ci = __shfl(cs, i, 64), si = __shfl(sn, i, 64);
+      const double x1 = qr[r * D + i], x2 = qr[r * D + i + H2];
+      qv[k] = c < H2 ? (float)(x1 * ci - x2 * si) : (float)(x1 * si + x2 * ci);
+    }
+  }
+  // logits s_j = scale q.k_hat_{r,j} + b_hat_{r,j}
+  float sl[MT], dot[MT];
+  float M = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      acc = fmaf(v[t][q].x, qv[4 * q], acc);
+      acc = fmaf(v[t][q].y, qv[4 * q + 1], acc);
+      acc = fmaf(v[t][q].z, qv[4 * q + 2], acc);
+      acc = fmaf(v[t][q].w, qv[4 * q + 3], acc);
+    }
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    acc += __shfl_xor(acc, 4, 64);
+    acc += __shfl_xor(acc, 8, 64);
+    const int j = 4 * t + cg;
+    const float bj = __shfl(bl, j, 64);
+    dot[t] = acc * P.scale;
+    sl[t] = j < C ? dot[t] + bj : -INFINITY;
+    M = fmaxf(M, sl[t]);
+  }
+  M = fmaxf(M, __shfl_xor(M, 16, 64));
+  M = fmaxf(M, __shfl_xor(M, 32, 64));
+  float S = 0.0f, SW = 0.0f, ka[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) ka[k] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const float e = 4 * t + cg < C ? expf(sl[t] - M) : 0.0f;
+    S += e;
+    SW += e * dot[t];
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      ka[4 * q] = fmaf(e, v[t][q].x, ka[4 * q]);
+      ka[4 * q + 1] = fmaf(e, v[t][q].y, ka[4 * q + 1]);
+      ka[4 * q + 2] = fmaf(e, v[t][q].z, ka[4 * q + 2]);
+      ka[4 * q + 3] = fmaf(e, v[t][q].w, ka[4 * q + 3]);
+    }
+  }
+  S += __shfl_xor(S, 16, 64);
+  SW += __shfl_xor(SW, 16, 64);
+  S += __shfl_xor(S, 32, 64);
+  SW += __shfl_xor(SW, 32, 64);
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) {
+    ka[k] += __shfl_xor(ka[k], 16, 64);
+    ka[k] += __shfl_xor(ka[k], 32, 64);
+  }
+  if (cg == 0) {
+    float* kh = P.khat + (((int64_t)gi * P.ncap + n) * R + r) * D + ds;
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+      *(float4*)(kh + 4 * q) = make_float4(ka[4 * q] / S, ka[4 * q + 1] / S,
+                                           ka[4 * q + 2] / S, ka[4 * q + 3] / S);
+  }
+  // b_hat = F - sum_j w_j z_j with F = M + log S and z_j = scale q.k_hat_{r,j}
+  if (lane == 0) P.bhat[((int64_t)gi * P.ncap + n) * R + r] = (M + logf(S)) - SW / S;
+}
+
+template <int D, int MT>
+__global__ void __launch_bounds__(256) build_parents(BuildParams P) {
   const int gi = blockIdx.y;
   const int b = gi / P.H_kv, h = gi % P.H_kv;
-  const int lane = threadIdx.x & 63, cg = lane >> 4, ds = (lane & 15) * DPL;
-  const int C = P.C, R = P.R;
+  const int lane = threadIdx.x & 63;
+  const int R = P.R;
   int64_t n0, n1;
   node_range(P, b, n0, n1);
-  const float* qr = P.qref + (int64_t)h * R * D;
-  // RoPE: lane computes frequency lane % (d/2) and shares it by shuffles
-  double theta = 0.0;
-  if (P.rope) theta = pow((double)P.rope_base, -2.0 * (double)(lane % H2) / (double)D);
+  const double theta = parent_theta<D>(P, lane);
   const int64_t npairs = (n1 - n0) * R;
   // the 32 pairs of one line of b-hat run in 8 workgroups on one XCD
   for (int64_t pr = (int64_t)xcd_grouped_x() * 4 + (threadIdx.x >> 6); pr < npairs;
-       pr += (int64_t)gridDim.x * 4) {
-    const int64_t n = n0 + pr / R;
-    const int r = (int)(pr % R);
-    const int64_t ch0 = n * C;
-    float4 v[MT][NV];
-    const float* src = P.khat_ch + (((int64_t)gi * P.ncap_ch + ch0 + cg) * R + r) * D + ds;
-    const int64_t cstep = (int64_t)4 * R * D;
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int q = 0; q < NV; ++q)
-        v[t][q] = 4 * t + cg < C ? *(const float4*)(src + t * cstep + 4 * q)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float bl = lane < C ? P.bhat_ch[((int64_t)gi * P.ncap_ch + ch0 + lane) * R + r] : 0.0f;
-    // plane r's reference query at the node's first key position
-    float qv[DPL];
-    if (!P.rope) {
-#pragma unroll
-      for (int k = 0; k < DPL; ++k) qv[k] = qr[r * D + ds + k];
+       pr += (int64_t)gridDim.x * 4)
+    parent_pair<D, MT>(P, gi, h, n0 + pr / R, (int)(pr % R), theta, lane);
+}
+
+// ---------------------------------------------------------------- one-launch append
+//
+// A decode step completes at most one chunk, so one append builds at most one
+// node per level and tree: a leaf every C steps, a level-2 node every C^2, and
+// so on ([ZHA] "무엇과 다른가", append cadence).  This kernel does the cascade of
+// one (sequence, KV head) tree in one workgroup: its new leaves (one wave each,
+// by the same device code as the prefill kernels, so the summaries are bit for
+// bit the prefill's), then level by level the new parents' (node, plane) pairs
+// over all waves, with a workgroup barrier between levels (a parent reads
+// children this workgroup has just written).  The sequence's node counts are
+// shared by its H_kv trees, and every workgroup reads them first: the last of
+// the sequence's workgroups to arrive (a counter in the workspace, returned to
+// zero by that workgroup) writes them.  It loops over however many nodes are
+// missing, so any growth is built, only slower.
+
+struct AppendParams {
+  BuildParams lv[ZHA_MAX_L];   // level l at index l-1 (append mode)
+  int32_t L;
+  int32_t* arrive;             // [B] arrival counters, zero between calls
+};
+
+constexpr int kLeafGeneric = 0, kLeafMfma = 1, kLeafSmall = 2;
+
+// Global writes of every wave of the workgroup visible to every wave.
+__device__ inline void workgroup_sync_global() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+template <int D, int KIND, int CL, int MT, int NT>
+__global__ void __launch_bounds__(NT) append_chunk(AppendParams A) {
+  constexpr int NW = NT / kWave;
+  static_assert(KIND != kLeafGeneric || NT == kGenericThreads, "generic leaves: one workgroup");
+  const int gi = blockIdx.x;
+  const BuildParams& P1 = A.lv[0];
+  const int H = P1.H_kv, R = P1.R;
+  const int b = gi / H, h = gi % H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // ---- level 1: the tree's new leaves, one wave each (generic: the workgroup)
+  {
+    int64_t n0, n1;
+    node_range(P1, b, n0, n1);
+    if constexpr (KIND == kLeafGeneric) {
+      __shared__ BuildSmem sm;
+      for (int64_t n = n0; n < n1; ++n) generic_leaf(P1, sm, gi, h, n);
+    } else if constexpr (KIND == kLeafMfma) {
+      using M = MfmaLeaf<D, CL>;
+      __shared__ __attribute__((aligned(16))) unsigned char lds[M::kLds];
+      if (wave == 0 && n0 < n1) {
+        M::init(lds, lane);
+        const double theta = P1.rope ? pow((double)P1.rope_base, -2.0 * (double)(lane % M::H2) / (double)D) : 0.0;
+        typename M::QOps qa;
+        if (!P1.rope) M::build_qa(P1, h, 1.0, 0.0, lds, qa, lane);
+        for (int64_t n = n0; n < n1; ++n) {
+          if (P1.rope) {
+            double cs, sn;
+            sincos((double)(n * CL) * theta, &sn, &cs);
+            M::build_qa(P1, h, cs, sn, lds, qa, lane);
+          }
+          typename M::Keys kv;
+          M::fetch(P1, gi, n, kv, lane);
+          M::leaf(P1, gi, n, kv, qa, lds, lane, [] {});
+        }
+      }
     } else {
-      double sn, cs;
-      sincos((double)(n * P.span) * theta, &sn, &cs);
-#pragma unroll
-      for (int k = 0; k < DPL; ++k) {
-        const int c = ds + k, i = c < H2 ? c : c - H2;
-        const double ci = __shfl(cs, i, 64), si = __shfl(sn, i, 64);
-        const double x1 = qr[r * D + i], x2 = qr[r * D + i + H2];
-        qv[k] = c < H2 ? (float)(x1 * ci - x2 * si) : (float)(x1 * si + x2 * ci);
+      using S = SmallLeaf<D, CL>;
+      constexpr int LW = 4;   // waves with a leaf staging area
+      __shared__ float wsh[LW][16][CL];
+      __shared__ __attribute__((aligned(16))) float qsh[LW][16][D];
+      if (wave < LW) {
+        for (int64_t n = n0 + wave; n < n1; n += LW) {
+          S::set_q(P1, h, n * P1.C, qsh[wave], lane);
+          S::leaf(P1, gi, n, qsh[wave], wsh[wave], lane);
+        }
       }
     }
-    // logits s_j = scale q.k_hat_{r,j} + b_hat_{r,j}
-    float sl[MT], dot[MT];
-    float M = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int q = 0; q < NV; ++q) {
-        acc = fmaf(v[t][q].x, qv[4 * q], acc);
-        acc = fmaf(v[t][q].y, qv[4 * q + 1], acc);
-        acc = fmaf(v[t][q].z, qv[4 * q + 2], acc);
-        acc = fmaf(v[t][q].w, qv[4 * q + 3], acc);
+  }
+  workgroup_sync_global();
+  // ---- levels 2..L: (node, plane) pairs of the new parents over all waves
+  const double theta = parent_theta<D>(P1, lane);
+  for (int l = 2; l <= A.L; ++l) {
+    const BuildParams& P = A.lv[l - 1];
+    int64_t n0, n1;
+    node_range(P, b, n0, n1);
+    const int64_t items = (n1 - n0) * R;
+    for (int64_t i = wave; i < items; i += NW)
+      parent_pair<D, MT>(P, gi, h, n0 + i / R, (int)(i % R), theta, lane);
+    workgroup_sync_global();
+  }
+  // ---- the sequence's node counts, once all its trees have read the old ones
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(&A.arrive[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == H - 1) {
+      int64_t T = P1.T[b];
+      if (T < 0) T = 0;
+      if (T > P1.T_cap) T = P1.T_cap;
+      int64_t span = 1;
+      for (int l = 1; l <= A.L; ++l) {
+        span *= P1.C;
+        P1.n_built[(int64_t)(l - 1) * P1.B + b] = T / span;
       }
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      acc += __shfl_xor(acc, 4, 64);
-      acc += __shfl_xor(acc, 8, 64);
-      const int j = 4 * t + cg;
-      const float bj = __shfl(bl, j, 64);
-      dot[t] = acc * P.scale;
-      sl[t] = j < C ? dot[t] + bj : -INFINITY;
-      M = fmaxf(M, sl[t]);
+      __hip_atomic_store(&A.arrive[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    M = fmaxf(M, __shfl_xor(M, 16, 64));
-    M = fmaxf(M, __shfl_xor(M, 32, 64));
-    float S = 0.0f, SW = 0.0f, ka[DPL];
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) ka[k] = 0.0f;
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const float e = 4 * t + cg < C ? expf(sl[t] - M) : 0.0f;
-      S += e;
-      SW += e * dot[t];
-#pragma unroll
-      for (int q = 0; q < NV; ++q) {
-        ka[4 * q] = fmaf(e, v[t][q].x, ka[4 * q]);
-        ka[4 * q + 1] = fmaf(e, v[t][q].y, ka[4 * q + 1]);
-        ka[4 * q + 2] = fmaf(e, v[t][q].z, ka[4 * q + 2]);
-        ka[4 * q + 3] = fmaf(e, v[t][q].w, ka[4 * q + 3]);
-      }
-    }
-    S += __shfl_xor(S, 16, 64);
-    SW += __shfl_xor(SW, 16, 64);
-    S += __shfl_xor(S, 32, 64);
-    SW += __shfl_xor(SW, 32, 64);
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) {
-      ka[k] += __shfl_xor(ka[k], 16, 64);
-      ka[k] += __shfl_xor(ka[k], 32, 64);
-    }
-    if (cg == 0) {
-      float* kh = P.khat + (((int64_t)gi * P.ncap + n) * R + r) * D + ds;
-#pragma unroll
-      for (int q = 0; q < NV; ++q)
-        *(float4*)(kh + 4 * q) = make_float4(ka[4 * q] / S, ka[4 * q + 1] / S,
-                                             ka[4 * q + 2] / S, ka[4 * q + 3] / S);
-    }
-    // b_hat = F - sum_j w_j z_j with F = M + log S and z_j = scale q.k_hat_{r,j}
-    if (lane == 0) P.bhat[((int64_t)gi * P.ncap + n) * R + r] = (M + logf(S)) - SW / S;
   }
 }
 
@@ -742,6 +911,31 @@ static void launch_level(const BuildParams& P, int64_t max_nodes, hipStream_t s)
   }
 }
 
+// The one-launch append: one workgroup per (sequence, KV head).  Leaves take the
+// prefill's kernel family for the geometry; parents take ceil(C / 4) child
+// rounds (the workgroup size follows their registers).
+template <int D>
+static void launch_append_d(const AppendParams& A, hipStream_t s) {
+  const BuildParams& P = A.lv[0];
+  const dim3 grid((unsigned)(P.B * P.H_kv));
+  const bool bf = P.kv_dtype == ZHA_BF16 && P.R <= 16;
+  if (bf && P.C == 64) hipLaunchKernelGGL((append_chunk<D, kLeafMfma, 64, 16, 512>), grid, dim3(512), 0, s, A);
+  else if (bf && P.C == 32) hipLaunchKernelGGL((append_chunk<D, kLeafMfma, 32, 8, 512>), grid, dim3(512), 0, s, A);
+  else if (bf && P.C == 16) hipLaunchKernelGGL((append_chunk<D, kLeafMfma, 16, 4, 512>), grid, dim3(512), 0, s, A);
+  else if (bf && P.C == 8) hipLaunchKernelGGL((append_chunk<D, kLeafSmall, 8, 2, 1024>), grid, dim3(1024), 0, s, A);
+  else if (bf) hipLaunchKernelGGL((append_chunk<D, kLeafSmall, 4, 1, 1024>), grid, dim3(1024), 0, s, A);
+  else if (P.C <= 4) hipLaunchKernelGGL((append_chunk<D, kLeafGeneric, 0, 1, kGenericThreads>), grid, dim3(kGenericThreads), 0, s, A);
+  else if (P.C == 8) hipLaunchKernelGGL((append_chunk<D, kLeafGeneric, 0, 2, kGenericThreads>), grid, dim3(kGenericThreads), 0, s, A);
+  else if (P.C == 16) hipLaunchKernelGGL((append_chunk<D, kLeafGeneric, 0, 4, kGenericThreads>), grid, dim3(kGenericThreads), 0, s, A);
+  else if (P.C == 32) hipLaunchKernelGGL((append_chunk<D, kLeafGeneric, 0, 8, kGenericThreads>), grid, dim3(kGenericThreads), 0, s, A);
+  else hipLaunchKernelGGL((append_chunk<D, kLeafGeneric, 0, 16, kGenericThreads>), grid, dim3(kGenericThreads), 0, s, A);
+}
+
+static void launch_append_chunk(const AppendParams& A, hipStream_t s) {
+  if (A.lv[0].d == 128) launch_append_d<128>(A, s);
+  else launch_append_d<64>(A, s);
+}
+
 }  // namespace zha
 
 extern "C" int32_t zha_build_level(const zha_cfg* cfg, int32_t level, const zha_kv* kv,
@@ -765,8 +959,19 @@ extern "C" int32_t zha_append(const zha_cfg* cfg, const zha_kv* kv, const float*
   int32_t rc = zha::check_build(cfg, kv, qref, tree);
   if (rc != ZHA_OK) return rc;
   if (max_new_tokens < 0) return ZHA_EINVAL;
-  (void)ws; (void)ws_bytes;
+  rc = zha_check_ws(cfg, ZHA_OP_BUILD, ws, ws_bytes);
+  if (rc != ZHA_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
+  if (max_new_tokens <= cfg->C) {
+    // at most one new node per level and tree: the one-launch cascade
+    zha::AppendParams A;
+    for (int level = 1; level <= cfg->L; ++level)
+      A.lv[level - 1] = zha::make_params(cfg, kv, qref, tree, level, 1);
+    A.L = cfg->L;
+    A.arrive = (int32_t*)((char*)ws + zha::ws_layout(*cfg).build_off);
+    zha::launch_append_chunk(A, s);
+    return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
+  }
   int64_t span = 1;
   for (int level = 1; level <= cfg->L; ++level) {
     span *= cfg->C;

@@ -16,12 +16,15 @@ constexpr int kWave = 64;
 // One workspace serves every operation; regions are disjoint so a route and the
 // attend that consumes its leaf list may share one buffer.
 //   [0, 256)            header: int32 status word (sticky first error)
+//   build region        per sequence: int32 arrival counter of the one-launch
+//                       append (zero between calls)
 //   route region        per level l (1..L): kept list (ids, masks, count), list
 //                       length, scores, true log-mass (quality), per-head kept
 //                       counts and kept bitmaps; plus cut staging
 //   attend region       split partials [B*Hq][split_cap][d+2] fp32, then the
 //                       merged segment states [B*Hq][kMergeSegments][d+2]
 struct WsLayout {
+  size_t build_off = 0, build_bytes = 0;
   size_t route_off = 0, route_bytes = 0;
   size_t attend_off = 0, attend_bytes = 0;
   size_t total = 0;
@@ -77,6 +80,9 @@ inline WsLayout ws_layout(const zha_cfg& c) {
   WsLayout w;
   const int64_t BH = (int64_t)c.B * c.H_kv, BHq = BH * c.G;
   size_t off = 256;
+  w.build_off = off;
+  off = align_up(off + (size_t)c.B * 4, 256);
+  w.build_bytes = off - w.build_off;
   w.route_off = off;
   for (int l = 1; l <= c.L; ++l) {
     int64_t cap = level_cap(c, l);

@@ -110,8 +110,9 @@ typedef struct zha_tree {
 
 /*
  * Bytes of workspace the given operation needs for this geometry.  A workspace
- * must be zero-filled before its first use (it holds the status word).  Calls
- * that share a workspace must not overlap (use one stream per workspace).
+ * must be zero-filled before its first use (it holds the status word and the
+ * append's arrival counters).  Calls that share a workspace must not overlap
+ * (use one stream per workspace).  A ZHA_OP_ALL workspace serves every call.
  */
 size_t zha_workspace_bytes(const zha_cfg* cfg, int32_t op);
 
@@ -140,8 +141,15 @@ int32_t zha_build_level(const zha_cfg* cfg, int32_t level, const zha_kv* kv,
  * zha_append -- [ZHA] "무엇과 다른가": incremental growth.  A level-1 summary is
  * added every C decode steps and a level-2 one every C^2 steps; this builds, level
  * by level, every node in [n_built[l-1][b], T[b] / C^l) and advances n_built.
- * max_new_tokens (host) bounds the growth of T since the tree was last current and
- * only sizes the launch grid; any growth is handled.
+ * max_new_tokens (host) bounds the growth of T since the tree was last current;
+ * any growth is handled.  With max_new_tokens <= C (a decode step: at most one
+ * new node per level and tree) the whole cascade runs as one launch, one
+ * workgroup per (b, h_kv) tree, and the summaries are bit for bit those of
+ * zha_build_level (with RoPE and C >= 16, equal to rounding: the prefill advances
+ * its rotation angle from leaf to leaf).  Larger growth runs one launch per level.
+ * ws: at least zha_workspace_bytes(cfg, ZHA_OP_BUILD) bytes, zero-filled before
+ * its first use; the one-launch cascade keeps a per-sequence arrival counter
+ * there and returns it to zero.
  */
 int32_t zha_append(const zha_cfg* cfg, const zha_kv* kv, const float* qref,
                    const zha_tree* tree, int64_t max_new_tokens,

@@ -144,3 +144,25 @@ def test_cut_pool_beyond_fixed_point_range_is_rejected():
                                   fake, fake, fake, 1 << 24, fake, fake, ctypes.c_void_p(0x100000),
                                   huge_ws, None)
     assert rc == zha.EUNSUPPORTED
+
+
+def test_append_needs_its_workspace():
+    """The one-launch append keeps per-sequence arrival counters in the workspace:
+    a missing or short workspace is refused before any launch."""
+    cfg = zha.Config(B=2, H_kv=2, G=4, d=128, C=16, L=2, R=16, T_cap=4096)
+    fake = ctypes.c_void_p(0x1000)
+    kv = zha._KV(0x1000, 0x2000, 0x3000)
+    tree = zha._Tree()
+    for i in range(cfg.L):
+        tree.khat[i] = 0x2000
+        tree.bhat[i] = 0x3000
+        tree.n_cap[i] = cfg.level_cap(i + 1)
+    tree.n_built = 0x4000
+    need = zha.workspace_bytes(cfg, zha.OP_BUILD)
+    assert need > 256
+    rc = zha._lib.zha_append(ctypes.byref(cfg.c()), ctypes.byref(kv), fake, ctypes.byref(tree), 1,
+                             None, 0, None)
+    assert rc == zha.EWORKSPACE
+    rc = zha._lib.zha_append(ctypes.byref(cfg.c()), ctypes.byref(kv), fake, ctypes.byref(tree), 1,
+                             ctypes.c_void_p(0x100000), need - 1, None)
+    assert rc == zha.EWORKSPACE
