@@ -83,9 +83,10 @@ def attend_source_hash():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload, p):
-    """HBM bytes per zha_attend call from committed counter runs, if they were
-    taken on the current attend kernel source; otherwise None."""
+def stored_traffic_ratio(workload, p):
+    """HBM bytes over algorithmic bytes of zha_attend, from committed counter runs
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), if they were taken on
+    the current attend kernel source; otherwise None."""
     path = os.path.join(ROOT, "profiles", f"attend_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -93,7 +94,7 @@ def stored_traffic(workload, p):
         rec = json.load(f)
     if rec.get("source_hash") != attend_source_hash() or abs(rec.get("p", -1) - p) > 1e-9:
         return None
-    return rec.get("hbm_bytes_per_call")
+    return rec["hbm_bytes_per_call"] / rec["algorithmic_bytes_per_call"]
 
 
 class Run:
@@ -128,24 +129,27 @@ class Run:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
-    def routed_steps(self, s0, s1, p, ev=None, counts=None, keep=None, router=None):
+    def routed_steps(self, s0, s1, p, ev=None, counts=None, keep=None, router=None, aev=None):
         """Steps s0..s1-1.  ev: dict collecting (route, attend, append) event pairs;
-        keep: one LeafList per step, to hold each step's routed list; router:
-        replaces the tree route (called with q, T and the step's leaf list)."""
+        aev: list collecting event pairs around the appends only (the other calls
+        stay back to back); keep: one LeafList per step, to hold each step's
+        routed list; router: replaces the tree route (called with q, T and the
+        step's leaf list)."""
         zha, dec, C = self.zha, self.dec, self.wl.C
         for s in range(s0, s1):
             T = self.Ts[s]
             q = self.Q[s]
             lst = keep[s - s0] if keep is not None else dec.leaves
             if (self.wl.T0 + s) % C == 0:
-                if ev is not None:
+                marks = ev["append"] if ev is not None else aev
+                if marks is not None:
                     a0 = torch.cuda.Event(enable_timing=True)
                     a0.record()
                 dec.append(self.K, self.V, T, 1)
-                if ev is not None:
+                if marks is not None:
                     a1 = torch.cuda.Event(enable_timing=True)
                     a1.record()
-                    ev["append"].append((a0, a1))
+                    marks.append((a0, a1))
             if ev is not None:
                 r0 = torch.cuda.Event(enable_timing=True)
                 r0.record()
@@ -192,6 +196,99 @@ class Run:
                 ev.append((d0, d1))
 
 
+def append_cadence(run, reps=5):
+    """zha_append as a decode loop meets it: one call when a chunk completes, every
+    C steps ([ZHA] page, append cadence).  An append that completes exactly the
+    levels 1..k (the token count is a multiple of C^k and, below the top level,
+    not of C^(k+1)) happens for a fraction 1/C^(k-1) - 1/C^k of the chunks
+    (1/C^(L-1) for k = L).  Each kind is timed on its own, cache resident in
+    HBM: the tree is rebuilt at T_b - 1 (untimed), then the append to T_b is
+    timed with events; median of ``reps``.  The amortised cost per decode step
+    is sum_k freq_k t_k / C."""
+    zha, wl, dec = run.zha, run.wl, run.dec
+    C, L = wl.C, wl.L
+    Tt = torch.empty(wl.B, dtype=torch.int64, device="cuda")
+    kinds = {}
+    amort = 0.0
+    for k in range(1, L + 1):
+        span = C ** k
+        Tb = (wl.T0 // span) * span
+        if k < L and Tb % (span * C) == 0:
+            Tb -= span
+        freq = (1.0 / C ** (k - 1) - 1.0 / C ** k) if k < L else 1.0 / C ** (L - 1)
+        if Tb < span:
+            kinds[str(k)] = {"us": None, "freq": freq, "T": None}
+            continue
+        times = []
+        for _ in range(reps + 1):
+            Tt.fill_(Tb - 1)
+            dec.tree.n_built.zero_()
+            dec.prefill(run.K, run.V, Tt)
+            Tt.fill_(Tb)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dec.append(run.K, run.V, Tt, 1)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(1000.0 * e0.elapsed_time(e1))
+        if zha.ws_status(dec.ws) != 0:
+            raise RuntimeError("append reported a device error")
+        us = percentile(times[1:], 0.5)      # the first call also loads the kernel
+        kinds[str(k)] = {"us": us, "freq": freq, "T": Tb}
+        amort += freq * us
+    return {"by_levels_completed": kinds,
+            "us_per_append": amort,
+            "us_per_step": amort / C}
+
+
+def graph_window(run, p, W, K):
+    """The same K steps with route + attend captured once in a HIP graph and
+    replayed: each step copies its query and length into the captured buffers,
+    runs zha_append eagerly when a chunk completes, then replays.  Returns the
+    route + attend time per step (appends bracketed by events and left out)."""
+    zha, dec, wl = run.zha, run.dec, run.wl
+    q_st, T_st = run.Q[W].clone(), run.Ts[W].clone()
+    lst = dec.leaves
+    run.prefill()
+    run.routed_steps(0, W, p)
+
+    def step():
+        zha.route(run.cfg, q_st, dec.tree, T_st, p, lst.ids, lst.mask, lst.count, dec.ws)
+        zha.attend(run.cfg, q_st, run.K, run.V, T_st, lst.ids, lst.mask, lst.count, dec.out,
+                   dec.lse, dec.ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    aev = []
+
+    def steps():
+        for s in range(W, W + K):
+            if (wl.T0 + s) % wl.C == 0:
+                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record()
+                dec.append(run.K, run.V, run.Ts[s], 1)
+                a1.record()
+                aev.append((a0, a1))
+            q_st.copy_(run.Q[s])
+            T_st.copy_(run.Ts[s])
+            g.replay()
+
+    ms = timed(steps)
+    if zha.ws_status(dec.ws) != 0:
+        raise RuntimeError("graph replay reported a device error")
+    ms -= sum(a.elapsed_time(b) for a, b in aev)
+    del g
+    return ms * 1000.0 / K
+
+
 def timed(fn):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -208,13 +305,12 @@ def percentile(v, q):
     return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
 
 
-def step_latency(ev, K):
-    """Median and p90 over steps of route + attend (per-call events), with the
-    appends' total spread over the K steps."""
+def step_latency(ev, append_us_per_step):
+    """Median and p90 over steps of route + attend (per-call events), plus the
+    append cost amortised at its cadence."""
     per = [a.elapsed_time(b) + c.elapsed_time(d) for (a, b), (c, d) in zip(ev["route"], ev["attend"])]
-    app = sum(a.elapsed_time(b) for a, b in ev["append"]) / K
-    return {"median_us": 1000 * (percentile(per, 0.5) + app),
-            "p90_us": 1000 * (percentile(per, 0.9) + app)}
+    return {"median_us": 1000 * percentile(per, 0.5) + append_us_per_step,
+            "p90_us": 1000 * percentile(per, 0.9) + append_us_per_step}
 
 
 def copy_bandwidth():
@@ -424,13 +520,22 @@ def main():
     log(f"[bench] prefill tree build: {build_ms:.2f} ms")
 
     # ---- routed: warmup, then exactly K timed steps, nothing else in the queue
+    # (events bracket only the appends that fall in the window)
     run.routed_steps(0, W, p)
-    total_ms = timed(lambda: run.routed_steps(W, W + K, p))
+    aev = []
+    total_ms = timed(lambda: run.routed_steps(W, W + K, p, aev=aev))
     st = zha.ws_status(run.dec.ws)
     if st != 0:
         raise RuntimeError(f"device status {zha.status_str(st)}")
-    us_step = total_ms * 1000.0 / K
-    log(f"[bench] routed p={p}: {us_step:.1f} us/step")
+    window_append_ms = sum(a.elapsed_time(b) for a, b in aev)
+    ra_us = (total_ms - window_append_ms) * 1000.0 / K
+    # the append at its cadence (one per C steps, with the parents it completes),
+    # timed on its own: the window holds too few steps to sample it
+    cad = append_cadence(run)
+    us_step = ra_us + cad["us_per_step"]
+    log(f"[bench] routed p={p}: {us_step:.1f} us/step (route + attend {ra_us:.1f}, append "
+        f"{cad['us_per_append']:.1f} us per chunk = {cad['us_per_step']:.2f} us/step; "
+        f"raw window {total_ms * 1000.0 / K:.1f} with {len(aev)} appends)")
 
     # ---- the same steps again, for the breakdown: events around each call (each
     # event is a queue marker, so route_us + attend_us slightly exceed a step),
@@ -451,7 +556,7 @@ def main():
     route_us = 1000 * sum(route_ms) / K
     log(f"[bench]   route {route_us:.1f} us (per-call events), attend {attend_us:.1f} us "
         f"(replayed), appends {len(append_ms)}")
-    warm = step_latency(ev, K)
+    warm = step_latency(ev, cad["us_per_step"])
 
     # ---- cold steps: a 512 MB buffer is written before each step (untimed), so a
     # step starts with nothing of its data in the 256 MB last-level cache
@@ -463,11 +568,14 @@ def main():
         flush.fill_(s & 0x7f)
         run.routed_steps(s, s + 1, p, evc)
     torch.cuda.synchronize()
-    cold = step_latency(evc, K)
+    cold = step_latency(evc, cad["us_per_step"])
     del flush
     torch.cuda.empty_cache()
     log(f"[bench]   per step (events): warm median {warm['median_us']:.1f} p90 {warm['p90_us']:.1f} us; "
         f"cold median {cold['median_us']:.1f} p90 {cold['p90_us']:.1f} us")
+    graph_ra_us = graph_window(run, p, W, K)
+    log(f"[bench]   graph-replayed route + attend: {graph_ra_us:.1f} us/step "
+        f"(eager {ra_us:.1f})")
     copy_gbps = copy_bandwidth()
     log(f"[bench]   device copy {copy_gbps:.0f} GB/s")
 
@@ -478,9 +586,11 @@ def main():
             continue
         run.prefill()
         run.routed_steps(0, W, ps)
-        ms = timed(lambda: run.routed_steps(W, W + K, ps))
-        extra[f"p{ps}"] = {"us_per_step": ms * 1000.0 / K}
-        log(f"[bench] routed p={ps}: {ms * 1000.0 / K:.1f} us/step")
+        aev_s = []
+        ms = timed(lambda: run.routed_steps(W, W + K, ps, aev=aev_s))
+        ms -= sum(a.elapsed_time(b) for a, b in aev_s)
+        extra[f"p{ps}"] = {"us_per_step": ms * 1000.0 / K + cad["us_per_step"]}
+        log(f"[bench] routed p={ps}: {extra[f'p{ps}']['us_per_step']:.1f} us/step")
 
     # ---- dense baseline over the same steps
     dense = None
@@ -552,14 +662,19 @@ def main():
     step_gbps = (attend_bytes + route_bytes) / (total_ms * 1e-3) / 1e9 if attend_bytes else None
     dominant = "attend" if attend_us >= route_us else "route"
     ach = att_gbps if dominant == "attend" else rte_gbps
+    alg = (attend_bytes if dominant == "attend" else route_bytes) / K
+    ratio = stored_traffic_ratio(wl.name, p) if dominant == "attend" else None
     roofline = {
         "bound": "hbm",
         "kernel": "zha_attend (split-K partial + merge)" if dominant == "attend" else "zha_route (all levels)",
         "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": (ach / HBM_PEAK_GBPS) if ach else None,
-        "traffic": stored_traffic(wl.name, p) if dominant == "attend" else None,
+        "traffic": (ratio * alg) if (ratio is not None and alg) else None,
+        "traffic_source": (f"counter HBM bytes / algorithmic bytes = {ratio:.4f} from "
+                           f"profiles/attend_{wl.name}_traffic.json (same attend source), times "
+                           f"this run's algorithmic bytes") if ratio is not None else None,
         "avg_launch_us": attend_us if dominant == "attend" else route_us,
-        "algorithmic_bytes_per_launch": (attend_bytes if dominant == "attend" else route_bytes) / K,
+        "algorithmic_bytes_per_launch": alg,
     }
 
     # ---- depth schedules of p (same product p = the headline p for root/power)
@@ -641,7 +756,11 @@ def main():
     out = {
         "metric": METRIC, "value": us_step, "unit": "us/step", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": total_ms / K, "higher_is_better": False,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.kv_dtype, "data": "synthetic",
+        "precision": ("K/V bf16; q.k and p.v on bf16 MFMA with q and p each split into a hi + lo "
+                      "bf16 pair (~2^-17 relative), fp32 accumulation; scores, softmax, summaries, "
+                      "routing, out and lse in fp32") if wl.kv_dtype == "bf16" else
+                     "fp32 throughout (K/V, scores, softmax, summaries, out, lse)",
         "config": {"workload": wl.name, "B": wl.B, "H_kv": wl.H_kv, "G": wl.G, "d": wl.d,
                    "T0": wl.T0, "C": wl.C, "L": wl.L, "R": wl.R, "p": p, "kv_dtype": wl.kv_dtype,
                    "clusters": wl.n_clusters, "cluster_law": wl.freq},
@@ -649,8 +768,19 @@ def main():
         "cpu_baseline": cpu,
         "route_us": route_us,
         "attend_us": attend_us,
-        "append_us_each": (1000 * sum(append_ms) / len(append_ms)) if append_ms else None,
-        "appends_in_timed_steps": len(append_ms),
+        "route_attend_us": ra_us,
+        "graph": {"route_attend_us": graph_ra_us, "us_per_step": graph_ra_us + cad["us_per_step"],
+                  "note": "route + attend captured once in a HIP graph and replayed per step "
+                          "(query and length copied into the captured buffers each step, appends "
+                          "eager); value is the eager loop"},
+        "append": {**cad, "frac_of_step": cad["us_per_step"] / us_step,
+                   "within_1pct": cad["us_per_step"] <= 0.01 * us_step,
+                   "note": "zha_append per completed chunk (one call every C steps), by the levels "
+                           "it completes, weighted by their cadence; us_per_step = us_per_append / C, "
+                           "included in value"},
+        "append_us_each": cad["us_per_append"],
+        "window_us_per_step_raw": total_ms * 1000.0 / K,
+        "appends_in_timed_steps": len(aev),
         "prefill_build_ms": build_ms,
         "step_latency": {"warm": warm, "cold": cold,
                          "note": "per-step route + attend from per-call events (queue markers add "
