@@ -487,6 +487,7 @@ struct CutSmem {
       float sc[kCutStage * kCutThreads];            // the head's scores (-inf past U)
       unsigned long long relmass[kRelBuckets];    // mass per relative-score bucket
       unsigned long long ent[kSortMax];           // crossing bucket: key << 32 | ~u, 0 past it
+      unsigned long long kbits[kCutStage * kCutThreads / 64];   // kept bits, 64 entries a word
     } h;
     struct {                                      // general path
       uint32_t key[kCutLds];
@@ -505,7 +506,6 @@ struct CutSmem {
   int32_t nabove;      // candidates in buckets above the crossing one
   int32_t ic;          // sorted position of the cut entry within the crossing bucket
   unsigned long long above;
-  unsigned long long cut_entry;
 };
 
 __device__ inline float key_score(uint32_t k) {
@@ -521,7 +521,8 @@ __device__ inline int rel_bucket(float s, float mx) {
 // ~u, zero past the last), at most KMAX of them, are sorted by score descending
 // then id ascending; their masses are run in that order from `above`, the mass
 // of every bucket before it; the first entry whose running mass reaches target
-// is the cut.  Sets sm.ic (its position) and sm.cut_entry.
+// is the cut.  Sets sm.ic (its position) and sets the kept entries' bits in
+// sm.u.h.kbits.
 template <int NR, int KMAX = 64 * NR>
 __device__ inline void cut_in_bucket(CutSmem& sm, int cstar, float mx, int topk,
                                      unsigned long long above, double target, int lane) {
@@ -552,12 +553,86 @@ __device__ inline void cut_in_bucket(CutSmem& sm, int cstar, float mx, int topk,
     ic = NR * l + (int)rl32((uint32_t)rf, l);
   }
   if (ic < 0 || ic > cstar - 1) ic = cstar - 1;
-  const int l_ic = ic / NR, r_ic = ic % NR;
-  uint64_t ce = 0ull;
+  // the bucket's entries up to the cut are kept
 #pragma unroll
-  for (int r = 0; r < NR; ++r)
-    if (r == r_ic) ce = rl64(v[r], l_ic);
-  if (lane == 0) { sm.ic = ic; sm.cut_entry = ce; }
+  for (int r = 0; r < NR; ++r) {
+    if (v[r] != 0ull && NR * lane + r <= ic) {
+      const uint32_t u = ~(uint32_t)v[r];
+      atomicOr(&sm.u.h.kbits[u >> 6], 1ull << (u & 63));
+    }
+  }
+  if (lane == 0) sm.ic = ic;
+}
+
+// A list of at most kSortMax entries: one wave sorts the head's candidates whole
+// in registers (key << 32 | ~u, blocked NR per lane) and runs their masses in
+// that order; the first entry whose running mass reaches the target is the cut.
+// The same integers and comparisons as the bucketed path, without its passes.
+// The kept bits go through the wave's LDS words (wbits, NR of them) to the
+// head's bitmap rows.
+template <int NR, int KMAX = 64 * NR>
+__device__ inline void cut_list_wave(const LevelParams& P, const float* sc, int U, int head,
+                                     uint8_t* out, uint64_t* bits, uint64_t* wbits, int lane) {
+  uint64_t v[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int u = NR * lane + r;
+    uint64_t e = 0ull;
+    if (u < U) {
+      const float x = sc[u];
+      if (x != -INFINITY) e = ((uint64_t)order_key(x) << 32) | (uint32_t)(~(uint32_t)u);
+    }
+    v[r] = e;
+  }
+  wave_sort_desc<NR, KMAX>(v, lane);
+  const uint64_t first = rl64(v[0], 0);
+  int ic = -1;   // sorted position of the last kept entry; -1: no candidates
+  if (first != 0ull) {
+    const float mx = key_score((uint32_t)(first >> 32));
+    uint64_t ms[NR];
+    uint32_t nc = 0;
+    uint64_t own = 0ull;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      ms[r] = (v[r] != 0ull) ? fixmass(cut_mass(key_score((uint32_t)(v[r] >> 32)), mx, P.topk)) : 0ull;
+      own += ms[r];
+      nc += __popcll(__ballot(v[r] != 0ull));
+    }
+    if (P.topk == 0 && P.p >= 1.0f) {
+      ic = (int)nc - 1;
+    } else {
+      const uint64_t inc = wave_incl_scan<uint64_t>(own);
+      const double target = cut_target(P.p, P.topk, rl64(inc, 63));
+      uint64_t run = inc - own;
+      int rf = NR;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        run += ms[r];
+        if (rf == NR && ms[r] != 0ull && (double)run >= target) rf = r;
+      }
+      const uint64_t reach = __ballot(rf < NR);
+      if (reach != 0ull) {
+        const int l = __ffsll((long long)reach) - 1;
+        ic = NR * l + (int)rl32((uint32_t)rf, l);
+      }
+      if (ic < 0 || ic > (int)nc - 1) ic = (int)nc - 1;
+    }
+  }
+  const int nrow = (U + 63) >> 6;
+  if (lane < NR) wbits[lane] = 0ull;
+  wave_lds_sync();
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    if (v[r] != 0ull && NR * lane + r <= ic) {
+      const uint32_t u = ~(uint32_t)v[r];
+      atomicOr((unsigned long long*)&wbits[u >> 6], 1ull << (u & 63));
+    }
+  }
+  wave_lds_sync();
+  if (bits && lane < nrow) bits[lane] = wbits[lane];
+  if (out)
+    for (int u = lane; u < U; u += kWave) out[u] = (uint8_t)((wbits[u >> 6] >> (u & 63)) & 1ull);
+  if (lane == 0) P.kept[head] = ic + 1;
 }
 
 // One workgroup cuts one query head.  The head's kept entries are written as a
@@ -590,10 +665,23 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
   if (g == 0 && tid == 0 && P.ucount_out != nullptr) P.ucount_out[gi] = U;
   uint8_t* out = P.sel ? P.sel + (int64_t)head * P.ucap : nullptr;
   uint64_t* bits = P.selbits ? P.selbits + (int64_t)head * P.nwcap : nullptr;
+  if (U <= kSortMax) {
+    // short list: one wave, no histogram; the other waves leave
+    if (wave == 0) {
+      uint64_t* wbits = (uint64_t*)sm.u.h.relmass;
+      if (U <= 16) cut_list_wave<1, 16>(P, sc, U, head, out, bits, wbits, lane);
+      else if (U <= kWave) cut_list_wave<1>(P, sc, U, head, out, bits, wbits, lane);
+      else if (U <= 2 * kWave) cut_list_wave<2>(P, sc, U, head, out, bits, wbits, lane);
+      else if (U <= 4 * kWave) cut_list_wave<4>(P, sc, U, head, out, bits, wbits, lane);
+      else if (U <= 8 * kWave) cut_list_wave<8>(P, sc, U, head, out, bits, wbits, lane);
+      else cut_list_wave<16>(P, sc, U, head, out, bits, wbits, lane);
+    }
+    return;
+  }
   const int nrow = (U + 63) >> 6;
   const bool staged = U <= PER * kCutThreads;
   const int nj = (U + kCutThreads - 1) / kCutThreads;   // rows of kCutThreads entries
-  if (tid == 0) { sm.nabove = 0; sm.count = 0; sm.first = kRelBuckets; sm.ic = kSortMax; sm.cut_entry = 0ull; }
+  if (tid == 0) { sm.nabove = 0; sm.count = 0; sm.first = kRelBuckets; sm.ic = kSortMax; }
   float mx = -INFINITY;
   if (staged) {
     for (int i = tid; i < kRelBuckets; i += kCutThreads) sm.u.h.relmass[i] = 0ull;
@@ -677,6 +765,9 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
       const float x = ss[u];
       const int b = x != -INFINITY ? rel_bucket(x, mx) : kRelBuckets;
       nab += b < bstar ? 1 : 0;
+      // row u / 64 = j NW + wave: every entry of a bucket above the crossing one is kept
+      const uint64_t above_row = __ballot(b < bstar);
+      if (lane == 0) sm.u.h.kbits[j * NW + wave] = above_row;
       const uint64_t inb = __ballot(b == bstar);
       if (inb != 0ull) {                                  // uniform over the wave
         const int leader = __ffsll((long long)inb) - 1;
@@ -703,22 +794,12 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
         else cut_in_bucket<16>(sm, cstar, mx, P.topk, above_b, target, lane);
       }
       __syncthreads();
-      const unsigned long long ce = sm.cut_entry;
-      const uint32_t kap = (uint32_t)(ce >> 32);
-      const int ukap = (int)(~(uint32_t)ce);
-      for (int j = 0; j < nj; ++j) {
-        const int u = j * kCutThreads + tid;
-        const float x = ss[u];
-        bool s1 = false;
-        if (x != -INFINITY) {
-          const uint32_t k = order_key(x);
-          s1 = k > kap || (k == kap && u <= ukap);
-        }
-        if (out && u < U) out[u] = s1 ? 1 : 0;
-        const uint64_t b = __ballot(s1);
-        const int row = j * NW + wave;
-        if (bits && lane == 0 && row < nrow) bits[row] = b;
-      }
+      // the kept bits: rows above the crossing bucket from the gather, the
+      // bucket's kept entries from the sort
+      if (bits)
+        for (int r = tid; r < nrow; r += kCutThreads) bits[r] = sm.u.h.kbits[r];
+      if (out)
+        for (int u = tid; u < U; u += kCutThreads) out[u] = (uint8_t)((sm.u.h.kbits[u >> 6] >> (u & 63)) & 1ull);
       if (tid == 0) P.kept[head] = sm.nabove + sm.ic + 1;
       return;
     }
