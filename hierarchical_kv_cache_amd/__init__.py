@@ -5,7 +5,7 @@ The compute path is libzha.so (HIP kernels behind a C ABI, include/zha.h);
 first use so that ``python -m hierarchical_kv_cache_amd.buildlib`` can rebuild the
 library; using any of them without a built library raises ImportError.
 """
-_API = ("Config", "Decoder", "LeafList", "Tree", "ZhaError", "append", "attend", "build",
+_API = ("Config", "Decoder", "LeafList", "Tree", "ZhaError", "append", "attend", "attend_static", "build",
         "build_level", "dense_attend", "new_workspace", "p_schedule", "route", "route_level", "route_quality", "route_topk",
         "route_counts", "workspace_bytes", "ws_status")
 

@@ -22,6 +22,8 @@
 // rows are read once per step and carry the non-temporal hint.
 #include "zha_internal.hpp"
 
+#include <mutex>
+
 namespace zha {
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -1244,10 +1246,11 @@ static void launch_attend(const AttendParams& P, int kv_dtype, int grid, int BHq
   }
 }
 
-static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
-                          const int32_t* leaf_ids, const uint32_t* leaf_mask,
-                          const int32_t* leaf_count, float* out, float* lse,
-                          void* ws, size_t ws_bytes, void* stream, bool dense) {
+// Checks of the arguments every attend call shares.
+static int32_t check_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
+                            const int32_t* leaf_ids, const uint32_t* leaf_mask,
+                            const int32_t* leaf_count, const float* out, const float* lse,
+                            bool dense) {
   int32_t rc = zha_check_cfg(cfg);
   if (rc != ZHA_OK) return rc;
   if (cfg->G > 16) return ZHA_EUNSUPPORTED;
@@ -1258,32 +1261,116 @@ static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
   if (!dense && (leaf_ids == nullptr || leaf_mask == nullptr || leaf_count == nullptr ||
                  cfg->leaf_cap < 1))
     return ZHA_EINVAL;
-  rc = zha_check_ws(cfg, dense ? ZHA_OP_DENSE : ZHA_OP_ATTEND, ws, ws_bytes);
-  if (rc != ZHA_OK) return rc;
-  const WsLayout w = ws_layout(*cfg);
+  return ZHA_OK;
+}
+
+// The attend's scratch: split partials, merged segment states and the group
+// chunk prefix, at the given addresses (256-byte aligned), with split_cap
+// partial slots per query head; device-detected errors go to *status.
+struct AttendScratch {
+  float* part;
+  float* seg;
+  int32_t* prefix;
+  int32_t* status;
+  int32_t split_cap;
+};
+
+static int32_t launch_attend_call(const zha_cfg* cfg, const float* q, const zha_kv* kv,
+                                  const int32_t* leaf_ids, const uint32_t* leaf_mask,
+                                  const int32_t* leaf_count, float* out, float* lse,
+                                  const AttendScratch& S, void* stream, bool dense) {
   AttendParams P;
   P.q = q; P.K = kv->K; P.V = kv->V; P.T = kv->T;
   P.leaf_ids = dense ? nullptr : leaf_ids;
   P.leaf_mask = dense ? nullptr : leaf_mask;
   P.leaf_count = dense ? nullptr : leaf_count;
   P.leaf_cap = cfg->leaf_cap;
-  P.part = (float*)((char*)ws + w.attend_off);
-  float* seg = (float*)((char*)ws + w.merge_off);
-  P.prefix = (int32_t*)((char*)ws + w.prefix_off);
-  P.status = (int32_t*)ws;
+  P.part = S.part;
+  P.prefix = S.prefix;
+  P.status = S.status;
   P.B = cfg->B; P.H_kv = cfg->H_kv; P.G = cfg->G; P.C = cfg->C;
   P.T_cap = cfg->T_cap;
-  P.split_cap = w.split_cap;
+  P.split_cap = S.split_cap;
   P.qscale = cfg->scale * kLog2e;
   hipStream_t s = (hipStream_t)stream;
   const int64_t max_items = (int64_t)cfg->B * cfg->H_kv * split_capacity(*cfg);
   const int grid = (int)(max_items < kAttendGrid ? max_items : kAttendGrid);
   const int BHq = cfg->B * cfg->H_kv * cfg->G;
   if (cfg->d == 64)
-    launch_attend<64>(P, cfg->kv_dtype, grid, BHq, seg, out, lse, s);
+    launch_attend<64>(P, cfg->kv_dtype, grid, BHq, S.seg, out, lse, s);
   else
-    launch_attend<128>(P, cfg->kv_dtype, grid, BHq, seg, out, lse, s);
+    launch_attend<128>(P, cfg->kv_dtype, grid, BHq, S.seg, out, lse, s);
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
+}
+
+static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
+                          const int32_t* leaf_ids, const uint32_t* leaf_mask,
+                          const int32_t* leaf_count, float* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream, bool dense) {
+  int32_t rc = check_attend(cfg, q, kv, leaf_ids, leaf_mask, leaf_count, out, lse, dense);
+  if (rc != ZHA_OK) return rc;
+  rc = zha_check_ws(cfg, dense ? ZHA_OP_DENSE : ZHA_OP_ATTEND, ws, ws_bytes);
+  if (rc != ZHA_OK) return rc;
+  const WsLayout w = ws_layout(*cfg);
+  AttendScratch S;
+  S.part = (float*)((char*)ws + w.attend_off);
+  S.seg = (float*)((char*)ws + w.merge_off);
+  S.prefix = (int32_t*)((char*)ws + w.prefix_off);
+  S.status = (int32_t*)ws;
+  S.split_cap = w.split_cap;
+  return launch_attend_call(cfg, q, kv, leaf_ids, leaf_mask, leaf_count, out, lse, S, stream,
+                            dense);
+}
+
+// ---------------------------------------------------------------- no-allocation attend
+//
+// zha_attend_static keeps the attend's scratch in `scratch`, a buffer of
+// kStaticScratchBytes that the library holds on every device it runs on.  In
+// host code `scratch` names a host-side stand-in, never the device memory: the
+// device address is looked up once per device (hipGetSymbolAddress, with that
+// device current) at the first call there, kept in static_scratch_ptr, and only
+// that address is handed to kernels.  Calls on one device share the buffer.
+
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr int kStaticMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+static void* static_scratch_ptr[kStaticMaxDevices];
+static std::mutex static_scratch_mu;
+
+// Device address of this device's scratch, looked up at the first call.
+static int32_t static_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kStaticMaxDevices) return ZHA_EHIP;
+  std::lock_guard<std::mutex> lock(static_scratch_mu);
+  if (static_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ZHA_EHIP;
+    static_scratch_ptr[dev] = p;
+  }
+  *ptr = static_scratch_ptr[dev];
+  return ZHA_OK;
+}
+
+// Layout of the attend's scratch alone: [0, 256) a status sink, then partials,
+// merged segment states and the chunk prefix.  Returns the bytes needed.
+static size_t static_layout(const zha_cfg& c, char* base, AttendScratch* S) {
+  const size_t BH = (size_t)c.B * c.H_kv, BHq = BH * c.G;
+  const int32_t cap = run_capacity(c);
+  size_t off = 256;
+  const size_t part = off;
+  off = align_up(off + BHq * (size_t)cap * (c.d + kPartPad) * 4, 256);
+  const size_t seg = off;
+  off = align_up(off + BHq * (size_t)kMergeSegments * (c.d + kPartPad) * 4, 256);
+  const size_t prefix = off;
+  off = align_up(off + (BH + 1) * 4, 256);
+  if (S != nullptr) {
+    S->part = (float*)(base + part);
+    S->seg = (float*)(base + seg);
+    S->prefix = (int32_t*)(base + prefix);
+    S->status = (int32_t*)base;
+    S->split_cap = cap;
+  }
+  return off;
 }
 
 }  // namespace zha
@@ -1301,4 +1388,22 @@ extern "C" int32_t dense_attend(const zha_cfg* cfg, const float* q, const zha_kv
                                 void* stream) {
   return zha::run_attend(cfg, q, kv, nullptr, nullptr, nullptr, out, lse, ws, ws_bytes,
                          stream, true);
+}
+
+extern "C" int32_t zha_attend_static(const zha_cfg* cfg, const float* q, const zha_kv* kv,
+                                     const int32_t* leaf_ids, const uint32_t* leaf_mask,
+                                     const int32_t* leaf_count, float* out, float* lse,
+                                     int32_t* status, void* stream) {
+  using namespace zha;
+  int32_t rc = check_attend(cfg, q, kv, leaf_ids, leaf_mask, leaf_count, out, lse, false);
+  if (rc != ZHA_OK) return rc;
+  if (static_layout(*cfg, nullptr, nullptr) > kStaticScratchBytes) return ZHA_EWORKSPACE;
+  void* base = nullptr;
+  rc = static_scratch(&base);
+  if (rc != ZHA_OK) return rc;
+  AttendScratch S;
+  static_layout(*cfg, (char*)base, &S);
+  if (status != nullptr) S.status = status;
+  return launch_attend_call(cfg, q, kv, leaf_ids, leaf_mask, leaf_count, out, lse, S, stream,
+                            false);
 }

@@ -24,8 +24,8 @@ F32, BF16 = 0, 1
 OP_BUILD, OP_ROUTE, OP_ATTEND, OP_DENSE, OP_ALL = range(5)
 
 EXPORTS = ["zha_workspace_bytes", "zha_status_str", "zha_build_level", "zha_append",
-           "zha_route", "zha_route_sched", "zha_route_topk", "zha_route_quality", "zha_route_level", "zha_attend", "dense_attend",
-           "zha_route_counts", "zha_ws_status"]
+           "zha_route", "zha_route_sched", "zha_route_topk", "zha_route_quality", "zha_route_level", "zha_attend",
+           "zha_attend_static", "dense_attend", "zha_route_counts", "zha_ws_status"]
 
 
 class ZhaError(RuntimeError):
@@ -69,6 +69,7 @@ def _load() -> ctypes.CDLL:
         "zha_route_quality": (i32, [cfgp, P, kvp, treep, P, P, sz, P]),
         "zha_route_level": (i32, [cfgp, i32, P, treep, f32, P, P, P, i32, P, P, P, sz, P]),
         "zha_attend": (i32, [cfgp, P, kvp, P, P, P, P, P, P, sz, P]),
+        "zha_attend_static": (i32, [cfgp, P, kvp, P, P, P, P, P, P, P]),
         "dense_attend": (i32, [cfgp, P, kvp, P, P, P, sz, P]),
         "zha_route_counts": (i32, [cfgp, P, P, P, P]),
         "zha_ws_status": (i32, [P, P, ctypes.POINTER(i32)]),
@@ -280,6 +281,15 @@ def attend(cfg: Config, q, K, V, T, leaf_ids, leaf_mask, leaf_count, out, lse, w
     _check(_lib.zha_attend(ctypes.byref(cfg.c()), _ptr(q), ctypes.byref(_kv(K, V, T)),
                            _ptr(leaf_ids), _ptr(leaf_mask), _ptr(leaf_count), _ptr(out),
                            _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)), "zha_attend")
+
+
+def attend_static(cfg: Config, q, K, V, T, leaf_ids, leaf_mask, leaf_count, out, lse,
+                  status=None, stream=None):
+    """zha_attend with the library's own per-device scratch (no workspace; nothing
+    allocated).  status: optional int32 device tensor for device-detected errors."""
+    _check(_lib.zha_attend_static(ctypes.byref(cfg.c()), _ptr(q), ctypes.byref(_kv(K, V, T)),
+                                  _ptr(leaf_ids), _ptr(leaf_mask), _ptr(leaf_count), _ptr(out),
+                                  _ptr(lse), _ptr(status), _stream(stream)), "zha_attend_static")
 
 
 def dense_attend(cfg: Config, q, K, V, T, out, lse, ws, stream=None):

@@ -146,6 +146,21 @@ def test_cut_pool_beyond_fixed_point_range_is_rejected():
     assert rc == zha.EUNSUPPORTED
 
 
+def test_static_attend_refuses_geometry_beyond_its_scratch():
+    """zha_attend_static keeps its scratch in a fixed 64 MiB buffer per device; a
+    geometry needing more is refused on the host, before anything is launched
+    (16 sequences x 32 query heads at 1M tokens need ~0.5 GB of split partials)."""
+    big = zha.Config(B=16, H_kv=8, G=4, d=128, C=64, L=3, R=16, T_cap=1 << 20)
+    fake = ctypes.c_void_p(0x1000)
+    kv = zha._KV(0x1000, 0x2000, 0x3000)
+    rc = zha._lib.zha_attend_static(ctypes.byref(big.c()), fake, ctypes.byref(kv), fake, fake, fake,
+                                    fake, fake, None, None)
+    assert rc == zha.EWORKSPACE
+    rc = zha._lib.zha_attend_static(ctypes.byref(big.c()), None, ctypes.byref(kv), fake, fake, fake,
+                                    fake, fake, None, None)
+    assert rc == zha.EINVAL
+
+
 def test_append_needs_its_workspace():
     """The one-launch append keeps per-sequence arrival counters in the workspace:
     a missing or short workspace is refused before any launch."""
