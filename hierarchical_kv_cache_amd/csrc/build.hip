@@ -446,6 +446,7 @@ template <int D, int CP>
 struct SmallLeaf {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(CP == 4 || CP == 8, "padded keys");
+  static constexpr int kCP = CP;                 // padded keys per leaf
   static constexpr int DPL = D / 64;             // dimensions per lane
   static constexpr int PP = 32 / CP;             // planes per pass
   static constexpr int H2 = D / 2;
@@ -483,13 +484,11 @@ struct SmallLeaf {
   }
 
   // Leaf n of sequence-head gi, with the queries already in qv.
-  __device__ static void leaf(const BuildParams& P, int gi, int64_t n, const float (*qv)[D],
-                              float (*wsh)[CP], int lane) {
-    const int C = P.C, R = P.R, d0 = DPL * lane;
-    // after a pass's butterfly: entry e = lane / 2, plane PP pass + e / CP, key e % CP
-    const int e = lane >> 1, jl = e % CP, rl = e / CP;
-    // this lane's dimensions of the leaf's keys (padding keys zero)
-    float kv[CP][DPL];
+  typedef float Keys[CP][DPL];
+
+  // This lane's dimensions of leaf n's keys (padding keys zero).
+  __device__ static void load_keys(const BuildParams& P, int gi, int64_t n, Keys& kv, int lane) {
+    const int C = P.C, d0 = DPL * lane;
     const uint16_t* kr = (const uint16_t*)P.K + ((int64_t)gi * P.T_cap + n * C) * D + d0;
 #pragma unroll
     for (int j = 0; j < CP; ++j) {
@@ -501,6 +500,22 @@ struct SmallLeaf {
         kv[j][0] = j < C ? __uint_as_float((uint32_t)kr[(int64_t)j * D] << 16) : 0.0f;
       }
     }
+  }
+
+  // Leaf n of sequence-head gi, with the queries already in qv.
+  __device__ static void leaf(const BuildParams& P, int gi, int64_t n, const float (*qv)[D],
+                              float (*wsh)[CP], int lane) {
+    Keys kv;
+    load_keys(P, gi, n, kv, lane);
+    leaf_from(P, gi, n, kv, qv, wsh, lane);
+  }
+
+  // Leaf n of sequence-head gi from its keys kv.
+  __device__ static void leaf_from(const BuildParams& P, int gi, int64_t n, const Keys& kv,
+                                   const float (*qv)[D], float (*wsh)[CP], int lane) {
+    const int C = P.C, R = P.R, d0 = DPL * lane;
+    // after a pass's butterfly: entry e = lane / 2, plane PP pass + e / CP, key e % CP
+    const int e = lane >> 1, jl = e % CP, rl = e / CP;
 #pragma unroll 1
     for (int pass = 0; pass < 16 / PP; ++pass) {
       float a[32];
@@ -717,10 +732,10 @@ __global__ void __launch_bounds__(256) build_parents(BuildParams P) {
 // bit the prefill's), then level by level the new parents' (node, plane) pairs
 // over all waves, with a workgroup barrier between levels (a parent reads
 // children this workgroup has just written).  The sequence's node counts are
-// shared by its H_kv trees, and every workgroup reads them first: the last of
-// the sequence's workgroups to arrive (a counter in the workspace, returned to
-// zero by that workgroup) writes them.  It loops over however many nodes are
-// missing, so any growth is built, only slower.
+// shared by its H_kv trees: every workgroup reads them first thing, then
+// arrives at a counter in the workspace, and the last to arrive (which returns
+// the counter to zero) writes the new counts.  It loops over however many nodes
+// are missing, so any growth is built, only slower.
 
 struct AppendParams {
   BuildParams lv[ZHA_MAX_L];   // level l at index l-1 (append mode)
@@ -740,78 +755,110 @@ __device__ inline void workgroup_sync_global() {
 template <int D, int KIND, int CL, int MT, int NT>
 __global__ void __launch_bounds__(NT) append_chunk(AppendParams A) {
   constexpr int NW = NT / kWave;
+  constexpr int LW = 4;   // waves with a leaf staging area (small chunks)
   static_assert(KIND != kLeafGeneric || NT == kGenericThreads, "generic leaves: one workgroup");
+  static_assert(NW > LW || KIND == kLeafGeneric, "a wave besides the leaf waves");
   const int gi = blockIdx.x;
   const BuildParams& P1 = A.lv[0];
-  const int H = P1.H_kv, R = P1.R;
+  const int H = P1.H_kv, R = P1.R, L = A.L;
   const int b = gi / H, h = gi % H;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // ---- level 1: the tree's new leaves, one wave each (generic: the workgroup)
-  {
-    int64_t n0, n1;
-    node_range(P1, b, n0, n1);
-    if constexpr (KIND == kLeafGeneric) {
-      __shared__ BuildSmem sm;
-      for (int64_t n = n0; n < n1; ++n) generic_leaf(P1, sm, gi, h, n);
-    } else if constexpr (KIND == kLeafMfma) {
-      using M = MfmaLeaf<D, CL>;
-      __shared__ __attribute__((aligned(16))) unsigned char lds[M::kLds];
-      if (wave == 0 && n0 < n1) {
-        M::init(lds, lane);
-        const double theta = P1.rope ? pow((double)P1.rope_base, -2.0 * (double)(lane % M::H2) / (double)D) : 0.0;
-        typename M::QOps qa;
-        if (!P1.rope) M::build_qa(P1, h, 1.0, 0.0, lds, qa, lane);
-        for (int64_t n = n0; n < n1; ++n) {
-          if (P1.rope) {
-            double cs, sn;
-            sincos((double)(n * CL) * theta, &sn, &cs);
-            M::build_qa(P1, h, cs, sn, lds, qa, lane);
-          }
-          typename M::Keys kv;
-          M::fetch(P1, gi, n, kv, lane);
-          M::leaf(P1, gi, n, kv, qa, lds, lane, [] {});
-        }
-      }
-    } else {
-      using S = SmallLeaf<D, CL>;
-      constexpr int LW = 4;   // waves with a leaf staging area
-      __shared__ float wsh[LW][16][CL];
-      __shared__ __attribute__((aligned(16))) float qsh[LW][16][D];
-      if (wave < LW) {
-        for (int64_t n = n0 + wave; n < n1; n += LW) {
-          S::set_q(P1, h, n * P1.C, qsh[wave], lane);
-          S::leaf(P1, gi, n, qsh[wave], wsh[wave], lane);
-        }
-      }
+  const int last = NW - 1;   // reads the old counts and arrives; builds no leaf
+  // ---- the old node counts of every level and the length, in one round trip
+  // by the last wave, while the leaf waves stage the reference queries (without
+  // RoPE they do not depend on the node)
+  __shared__ int64_t s_old[ZHA_MAX_L + 1];
+  if (wave == last) {
+    if (lane < L) s_old[lane] = P1.n_built[(int64_t)lane * P1.B + b];
+    else if (lane == kWave - 1) s_old[ZHA_MAX_L] = P1.T[b];
+  }
+  using M = MfmaLeaf<D, KIND == kLeafMfma ? CL : 16>;
+  using S = SmallLeaf<D, KIND == kLeafSmall ? CL : 4>;
+  __shared__ __attribute__((aligned(16))) unsigned char
+      leaf_lds[KIND == kLeafMfma ? M::kLds : KIND == kLeafSmall ? LW * 16 * (CL + D) * 4 : 16];
+  float (*wsh)[16][S::kCP] = reinterpret_cast<float (*)[16][S::kCP]>(leaf_lds);
+  float (*qsh)[16][D] = reinterpret_cast<float (*)[16][D]>(leaf_lds + LW * 16 * S::kCP * 4);
+  typename M::QOps qa;
+  if constexpr (KIND == kLeafMfma) {
+    if (wave == 0) {
+      M::init(leaf_lds, lane);
+      if (!P1.rope) M::build_qa(P1, h, 1.0, 0.0, leaf_lds, qa, lane);
     }
+  } else if constexpr (KIND == kLeafSmall) {
+    if (wave < LW && !P1.rope) S::set_q(P1, h, 0, qsh[wave], lane);
   }
-  workgroup_sync_global();
-  // ---- levels 2..L: (node, plane) pairs of the new parents over all waves
-  const double theta = parent_theta<D>(P1, lane);
-  for (int l = 2; l <= A.L; ++l) {
+  __syncthreads();
+  int64_t T = s_old[ZHA_MAX_L];
+  if (T < 0) T = 0;
+  if (T > P1.T_cap) T = P1.T_cap;
+  // Nodes [n0, n1) of level l are missing.
+  auto range = [&](int l, int64_t& n0, int64_t& n1) {
     const BuildParams& P = A.lv[l - 1];
-    int64_t n0, n1;
-    node_range(P, b, n0, n1);
-    const int64_t items = (n1 - n0) * R;
-    for (int64_t i = wave; i < items; i += NW)
-      parent_pair<D, MT>(P, gi, h, n0 + i / R, (int)(i % R), theta, lane);
-    workgroup_sync_global();
-  }
-  // ---- the sequence's node counts, once all its trees have read the old ones
-  if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(&A.arrive[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    n1 = T / P.span;
+    if (n1 > P.ncap) n1 = P.ncap;
+    n0 = s_old[l - 1];
+    if (n0 < 0) n0 = 0;
+    if (n0 > n1) n0 = n1;
+  };
+  // The sequence's node counts: every tree of it has read the old ones before
+  // it arrives, so the last to arrive may write the new ones.
+  auto arrive = [&] {
+    const int prev = __hip_atomic_fetch_add(&A.arrive[b], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == H - 1) {
-      int64_t T = P1.T[b];
-      if (T < 0) T = 0;
-      if (T > P1.T_cap) T = P1.T_cap;
       int64_t span = 1;
-      for (int l = 1; l <= A.L; ++l) {
+      for (int l = 1; l <= L; ++l) {
         span *= P1.C;
         P1.n_built[(int64_t)(l - 1) * P1.B + b] = T / span;
       }
       __hip_atomic_store(&A.arrive[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  };
+  if (KIND != kLeafGeneric && threadIdx.x == last * kWave) arrive();
+  // ---- level 1: the tree's new leaves, one wave each (generic: the workgroup)
+  int64_t n0, n1;
+  range(1, n0, n1);
+  bool dirty = n1 > n0;   // nodes written since the last barrier
+  if constexpr (KIND == kLeafGeneric) {
+    __shared__ BuildSmem sm;
+    for (int64_t n = n0; n < n1; ++n) generic_leaf(P1, sm, gi, h, n);
+  } else if constexpr (KIND == kLeafMfma) {
+    if (wave == 0 && n0 < n1) {
+      const double theta = P1.rope ? pow((double)P1.rope_base, -2.0 * (double)(lane % M::H2) / (double)D) : 0.0;
+      for (int64_t n = n0; n < n1; ++n) {
+        typename M::Keys kv;
+        M::fetch(P1, gi, n, kv, lane);        // in flight while the queries are staged
+        if (P1.rope) {
+          double cs, sn;
+          sincos((double)(n * CL) * theta, &sn, &cs);
+          M::build_qa(P1, h, cs, sn, leaf_lds, qa, lane);
+        }
+        M::leaf(P1, gi, n, kv, qa, leaf_lds, lane, [] {});
+      }
+    }
+  } else {
+    if (wave < LW) {
+      for (int64_t n = n0 + wave; n < n1; n += LW) {
+        typename S::Keys kv;
+        S::load_keys(P1, gi, n, kv, lane);    // in flight while the queries are staged
+        if (P1.rope) S::set_q(P1, h, n * P1.C, qsh[wave], lane);
+        S::leaf_from(P1, gi, n, kv, qsh[wave], wsh[wave], lane);
+      }
+    }
   }
+  // ---- levels 2..L: (node, plane) pairs of the new parents over all waves; a
+  // barrier orders a level's reads after the writes of the levels below
+  const double theta = parent_theta<D>(P1, lane);
+  for (int l = 2; l <= L; ++l) {
+    range(l, n0, n1);
+    if (n1 <= n0) continue;
+    if (dirty) workgroup_sync_global();
+    const BuildParams& P = A.lv[l - 1];
+    const int64_t items = (n1 - n0) * R;
+    for (int64_t i = wave; i < items; i += NW)
+      parent_pair<D, MT>(P, gi, h, n0 + i / R, (int)(i % R), theta, lane);
+    dirty = true;
+  }
+  if (KIND == kLeafGeneric && threadIdx.x == 0) arrive();
 }
 
 // Record the built node counts once every build launch of the call is done.
