@@ -1330,6 +1330,9 @@ static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
 // device address is looked up once per device (hipGetSymbolAddress, with that
 // device current) at the first call there, kept in static_scratch_ptr, and only
 // that address is handed to kernels.  Calls on one device share the buffer.
+// No part of it needs to start at zero: every partial and segment state is
+// written before it is read, and without a caller's status word the header
+// word is a sink that nothing reads.
 
 constexpr size_t kStaticScratchBytes = size_t(64) << 20;
 constexpr int kStaticMaxDevices = 64;

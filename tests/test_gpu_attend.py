@@ -82,6 +82,8 @@ def test_pin1_worked_example_through_dense_attend():
     ("bf16", 64, 4, 3, 1, 4),
     ("bf16", 128, 16, 1, 1, 64),
     ("bf16", 64, 3, 2, 2, 16),
+    ("f32", 128, 8, 1, 2, 4),
+    ("f32", 64, 12, 2, 1, 64),
 ])
 def test_dense_attend_matches_oracle(kvd, d, G, H_kv, B, C):
     dt = torch.float32 if kvd == "f32" else torch.bfloat16
@@ -135,6 +137,12 @@ def _random_sets(rng, n1, Hq, frac):
     ("bf16", 128, 3, 2, 1, 64, 0.4),
     ("bf16", 128, 6, 1, 2, 32, 0.4),
     ("bf16", 64, 12, 1, 1, 16, 0.3),
+    # fp32 keys with eight and twelve query heads (the 8- and 16-head kernels),
+    # at the smallest and largest chunks
+    ("f32", 128, 8, 1, 1, 4, 0.2),
+    ("f32", 128, 8, 2, 1, 64, 0.4),
+    ("f32", 64, 12, 1, 2, 4, 0.3),
+    ("f32", 128, 12, 1, 1, 64, 1.0),
 ])
 def test_zha_attend_matches_oracle_on_key_set(kvd, d, G, H_kv, B, C, frac):
     """out_j = attention over {0} U keys(leaves with bit j) U [C n_1, T)."""
