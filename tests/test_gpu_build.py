@@ -13,10 +13,17 @@ pytestmark = pytest.mark.gpu
 zha = pytest.importorskip("hierarchical_kv_cache_amd.zha")
 DEV = "cuda"
 
-# fp32 accumulation bounds of the builder relative to the data scale; each level
-# adds one weighted mean of the level below
-KHAT_TOL = {l: 1e-5 * 2 ** (l - 1) * 1.5 for l in range(1, 9)}
-BHAT_TOL = {l: 2e-5 * 2 ** (l - 1) * 1.25 for l in range(1, 9)}
+# Bounds of the builder's fp32 rounding: |k_hat - ref| / max |ref| over a level,
+# and |b_hat - ref| / max(1, |ref|).  A node's k_hat is a softmax-weighted mean
+# (a convex combination) of its keys or of its children's k_hat, so the error it
+# inherits from the level below does not grow, and each level adds one more
+# rounding of a C-term weighted sum (about sqrt(C) 2^-24 typically, C 2^-24 at
+# worst) plus the weights' rounding.  Measured worst errors over C = 2..64,
+# L up to 8, fp32 and bf16 keys, with and without RoPE: k_hat 4.3e-7, b_hat
+# 2.6e-7, with no growth from level 1 to level 8.  The bounds allow about five
+# times that, and a slow linear growth with the level.
+KHAT_TOL = {l: 2e-6 + 2e-7 * (l - 1) for l in range(1, 9)}
+BHAT_TOL = {l: 1e-6 + 2e-7 * (l - 1) for l in range(1, 9)}
 
 
 def _workload(name, **kw):
