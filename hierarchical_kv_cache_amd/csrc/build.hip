@@ -232,9 +232,18 @@ struct MfmaLeaf {
     const float* qr = P.qref + (int64_t)h * R * D;
     wave_lds_sync();                       // the previous leaf's K^T reads are done
     if (!P.rope) {
-      for (int i = lane; i < 16 * D; i += 64) {
-        const int r = i / D, c = i % D;
-        qs[r][c] = (r < R) ? qr[r * D + c] * P.scale : 0.0f;
+      // float4 pieces, lane l taking pieces l + 64 i: every piece is loaded (a
+      // padding row reads the last real row and is scaled by zero), so all the
+      // loads are in flight at once instead of each waiting behind a branch on R
+      constexpr int Q4 = 16 * D / 4, RQ = D / 4;
+#pragma unroll
+      for (int i = lane; i < Q4; i += 64) {
+        const int r = i / RQ, c = (i % RQ) * 4;
+        const bool real = r < R;
+        const float f = real ? P.scale : 0.0f;   // padding rows are scaled to zero
+        float4 x = *(const float4*)(qr + (real ? r : R - 1) * D + c);
+        x.x *= f; x.y *= f; x.z *= f; x.w *= f;
+        *(float4*)&qs[r][c] = x;
       }
     } else {
       // the angle is fp64; the rotations run in fp32 (within an ulp or two of the
@@ -242,9 +251,10 @@ struct MfmaLeaf {
       const float cf = (float)cs, sf = (float)sn;
       for (int idx = lane; idx < 16 * H2; idx += 64) {
         const int r = idx / H2, c = idx % H2;   // c == lane % H2
+        const int rr = r < R ? r : R - 1;
+        const float a = qr[rr * D + c], bb = qr[rr * D + c + H2];
         float x1 = 0.0f, x2 = 0.0f;
         if (r < R) {
-          const float a = qr[r * D + c], bb = qr[r * D + c + H2];
           x1 = fmaf(a, cf, -bb * sf);
           x2 = fmaf(a, sf, bb * cf);
         }
@@ -457,10 +467,19 @@ struct SmallLeaf {
     const int R = P.R, d0 = DPL * lane;
     const float* qr = P.qref + (int64_t)h * R * D;
     if (!P.rope) {
+      // float4 pieces, lane l taking pieces l + 64 i: every piece is loaded (a
+      // padding row reads the last real row and is scaled by zero), so all the
+      // loads are in flight at once instead of each waiting behind a branch on R
+      constexpr int Q4 = 16 * D / 4, RQ = D / 4;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) qv[r][d0 + k] = (r < R) ? qr[r * D + d0 + k] * P.scale : 0.0f;
+      for (int i = lane; i < Q4; i += kWave) {
+        const int r = i / RQ, c = (i % RQ) * 4;
+        const bool real = r < R;
+        const float f = real ? P.scale : 0.0f;   // padding rows are scaled to zero
+        float4 x = *(const float4*)(qr + (real ? r : R - 1) * D + c);
+        x.x *= f; x.y *= f; x.z *= f; x.w *= f;
+        *(float4*)&qv[r][c] = x;
+      }
       wave_lds_sync();
       return;
     }
@@ -472,11 +491,10 @@ struct SmallLeaf {
       sincos((double)pos * theta, &sn, &cs);
 #pragma unroll 2
       for (int r = 0; r < 16; ++r) {
+        const int rr = r < R ? r : R - 1;
+        const double a = qr[rr * D + i], bb = qr[rr * D + i + H2];
         float x = 0.0f;
-        if (r < R) {
-          const double a = qr[r * D + i], bb = qr[r * D + i + H2];
-          x = c < H2 ? (float)(a * cs - bb * sn) : (float)(a * sn + bb * cs);
-        }
+        if (r < R) x = c < H2 ? (float)(a * cs - bb * sn) : (float)(a * sn + bb * cs);
         qv[r][d0 + k] = x * P.scale;
       }
     }
@@ -768,9 +786,10 @@ __global__ void __launch_bounds__(NT) append_chunk(AppendParams A) {
   // by the last wave, while the leaf waves stage the reference queries (without
   // RoPE they do not depend on the node)
   __shared__ int64_t s_old[ZHA_MAX_L + 1];
-  if (wave == last) {
-    if (lane < L) s_old[lane] = P1.n_built[(int64_t)lane * P1.B + b];
-    else if (lane == kWave - 1) s_old[ZHA_MAX_L] = P1.T[b];
+  if (wave == last && (lane < L || lane == kWave - 1)) {
+    // one load instruction: lanes below L read a level's count, the top lane T
+    const int64_t* src = lane < L ? P1.n_built + (int64_t)lane * P1.B + b : P1.T + b;
+    s_old[lane < L ? lane : ZHA_MAX_L] = *src;
   }
   using M = MfmaLeaf<D, KIND == kLeafMfma ? CL : 16>;
   using S = SmallLeaf<D, KIND == kLeafSmall ? CL : 4>;
@@ -791,10 +810,11 @@ __global__ void __launch_bounds__(NT) append_chunk(AppendParams A) {
   int64_t T = s_old[ZHA_MAX_L];
   if (T < 0) T = 0;
   if (T > P1.T_cap) T = P1.T_cap;
+  const int cshift = __builtin_ctz((unsigned)P1.C);   // C is a power of two: T / C^l by shifts
   // Nodes [n0, n1) of level l are missing.
   auto range = [&](int l, int64_t& n0, int64_t& n1) {
     const BuildParams& P = A.lv[l - 1];
-    n1 = T / P.span;
+    n1 = T >> (l * cshift);
     if (n1 > P.ncap) n1 = P.ncap;
     n0 = s_old[l - 1];
     if (n0 < 0) n0 = 0;
@@ -805,11 +825,7 @@ __global__ void __launch_bounds__(NT) append_chunk(AppendParams A) {
   auto arrive = [&] {
     const int prev = __hip_atomic_fetch_add(&A.arrive[b], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == H - 1) {
-      int64_t span = 1;
-      for (int l = 1; l <= L; ++l) {
-        span *= P1.C;
-        P1.n_built[(int64_t)(l - 1) * P1.B + b] = T / span;
-      }
+      for (int l = 1; l <= L; ++l) P1.n_built[(int64_t)(l - 1) * P1.B + b] = T >> (l * cshift);
       __hip_atomic_store(&A.arrive[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
