@@ -49,9 +49,30 @@ struct ListRef {
   const int64_t* T;            // [B]
   int64_t T_cap;
   int64_t span;                // C^level: tokens per node of this level
+  int32_t level_shift;         // log2 span (C is a power of two)
   int32_t C, cshift, H_kv;
   uint32_t full;               // every head's bit
+  const int64_t* dummy;        // 8 readable bytes: stands in for an absent T or count
 };
+
+// The list's length inputs: the sequence length T and the count (explicit
+// list, or kept parents of an implicit one).  Both loads are issued before
+// either value is used (a missing one reads the dummy), so they cost one round
+// trip; the geometry below is computed from them.
+struct ListFetch {
+  int64_t T;
+  int32_t count;
+};
+
+__device__ inline ListFetch list_fetch(const ListRef& L, int gi) {
+  const int64_t* tp = L.T != nullptr ? L.T + gi / L.H_kv : L.dummy;
+  const int32_t* cp = L.ids != nullptr ? L.count + gi
+                    : (L.pids != nullptr ? L.pcount + gi : (const int32_t*)L.dummy);
+  ListFetch f;
+  f.T = *tp;
+  f.count = *cp;
+  return f;
+}
 
 struct ListGeo {
   int U;          // entries
@@ -59,22 +80,22 @@ struct ListGeo {
   int64_t orph0;  // implicit: id of the first parentless node
 };
 
-__device__ inline ListGeo list_geo(const ListRef& L, int gi, int64_t ucap) {
+__device__ inline ListGeo list_geo_from(const ListRef& L, const ListFetch& f, int64_t ucap) {
   ListGeo g{0, 0, 0};
   if (L.ids != nullptr) {
-    int32_t u = L.count[gi];
+    const int32_t u = f.count;
     g.U = u < 0 ? 0 : (u > L.cap ? (int)L.cap : u);
   } else {
-    int64_t T = L.T[gi / L.H_kv];
+    int64_t T = f.T;
     if (T < 0) T = 0;
     if (T > L.T_cap) T = L.T_cap;
-    const int64_t n_here = T / L.span;
+    const int64_t n_here = T >> L.level_shift;
     int64_t U;
     if (L.pids != nullptr) {
-      int32_t np = L.pcount[gi];
+      int32_t np = f.count;
       np = np < 0 ? 0 : (np > L.pcap ? (int)L.pcap : np);
       g.np = np;
-      g.orph0 = (T / (L.span * L.C)) * L.C;
+      g.orph0 = (T >> (L.level_shift + L.cshift)) << L.cshift;
       const int64_t orph = n_here - g.orph0;
       U = (int64_t)np * L.C + (orph > 0 ? orph : 0);
     } else {
@@ -83,6 +104,10 @@ __device__ inline ListGeo list_geo(const ListRef& L, int gi, int64_t ucap) {
     g.U = (int)(U < ucap ? U : ucap);
   }
   return g;
+}
+
+__device__ inline ListGeo list_geo(const ListRef& L, int gi, int64_t ucap) {
+  return list_geo_from(L, list_fetch(L, gi), ucap);
 }
 
 // Node id and head mask of entry u (< U) of group gi's list.
@@ -151,17 +176,17 @@ struct LevelParams {
 };
 
 // The first launch of a route checks that every level was built for the current T.
-__device__ inline void stale_check(const LevelParams& P, int gi) {
-  if (!P.check_stale || (gi % P.H_kv) != 0) return;
-  const int b = gi / P.H_kv;
-  int64_t T = P.list.T[b];
+// The first launch of a route checks that every level was built for the current
+// T: one wave, lane l holding level l + 1's built count (loaded by
+// stale_count, issued with the prologue's other loads), compared once T is in.
+__device__ inline int64_t stale_count(const LevelParams& P, int gi, int lane, bool chk) {
+  return (chk && lane < P.L) ? P.n_built[(int64_t)lane * P.B + gi / P.H_kv] : 0;
+}
+__device__ inline void stale_check(const LevelParams& P, int64_t T, int64_t nb, int lane, bool chk) {
   if (T < 0) T = 0;
   if (T > P.list.T_cap) T = P.list.T_cap;
-  int64_t span = 1;
-  for (int l = 1; l <= P.L; ++l) {
-    span *= P.list.C;
-    if (P.n_built[(int64_t)(l - 1) * P.B + b] != T / span) set_status(P.status, ZHA_ESTALE);
-  }
+  const bool bad = chk && lane < P.L && nb != (T >> ((lane + 1) * P.list.cshift));
+  if (__ballot(bad) != 0ull && lane == 0) set_status(P.status, ZHA_ESTALE);
 }
 
 __device__ inline int clamp_count(int32_t u, int64_t cap) {
@@ -296,23 +321,49 @@ __device__ inline void score_node(const LevelParams& P, int gi, int node, uint32
 template <int D, int GP>
 __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
   constexpr int kPidLds = 4096;
+  constexpr int kPre = 4;              // parents per thread loaded with the prologue
   __shared__ int32_t s_pid[kPidLds];   // the group's kept parents (implicit lists)
   __shared__ uint32_t s_pm[kPidLds];   // and their head masks
   const int gi = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (blockIdx.x == 0 && threadIdx.x == 0) stale_check(P, gi);
-  const ListGeo geo = list_geo(P.list, gi, P.ucap);
+  // ---- prologue: every load that does not wait on another is issued first --
+  // the queries, the list's length inputs, the stale check's counts and the
+  // first kPre * 256 kept parents (the list's capacity bounds their number) --
+  // so they cost one round trip; only longer parent lists need a second.
+  __shared__ __attribute__((aligned(16))) float s_q[GP > 4 ? GP * D : 4];
+  float qv[GP][4];
+  load_group_queries<D, GP>(P, gi, lane, qv, s_q);
+  const bool chk = P.check_stale && blockIdx.x == 0 && wave == 0 && (gi % P.H_kv) == 0;
+  const int64_t nb = stale_count(P, gi, lane, chk);
+  const ListFetch lf = list_fetch(P.list, gi);
+  const bool implicit = P.list.ids == nullptr && P.list.pids != nullptr;
+  int32_t pre_id[kPre];
+  uint32_t pre_m[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    pre_id[k] = 0;
+    pre_m[k] = 0u;
+    if (implicit && i < P.list.pcap) {
+      pre_id[k] = P.list.pids[(int64_t)gi * P.list.pcap + i];
+      pre_m[k] = P.list.pmask[(int64_t)gi * P.list.pcap + i];
+    }
+  }
+  const ListGeo geo = list_geo_from(P.list, lf, P.ucap);
+  stale_check(P, lf.T, nb, lane, chk);
   const int U = geo.U;
-  const bool staged = P.list.ids == nullptr && P.list.pids != nullptr && geo.np <= kPidLds;
+  const bool staged = implicit && geo.np <= kPidLds;
   if (staged) {
-    for (int i = threadIdx.x; i < geo.np; i += blockDim.x) {
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const int i = threadIdx.x + 256 * k;
+      if (i < geo.np) { s_pid[i] = pre_id[k]; s_pm[i] = pre_m[k]; }
+    }
+    for (int i = threadIdx.x + 256 * kPre; i < geo.np; i += blockDim.x) {
       s_pid[i] = P.list.pids[(int64_t)gi * P.list.pcap + i];
       s_pm[i] = P.list.pmask[(int64_t)gi * P.list.pcap + i];
     }
   }
-  __shared__ __attribute__((aligned(16))) float s_q[GP > 4 ? GP * D : 4];
-  float qv[GP][4];
-  load_group_queries<D, GP>(P, gi, lane, qv, s_q);
   __syncthreads();
   const int32_t* spid = staged ? s_pid : nullptr;
   const uint32_t* spm = staged ? s_pm : nullptr;
@@ -1095,6 +1146,7 @@ struct UpperLevel {
   float* scores;               // [BHq][cap], by node id
   int64_t cap;
   int64_t span;                // C^level
+  int32_t shift;               // log2 span
   int32_t* kept;               // [BHq] kept per head (diagnostics)
   int32_t* ucount;             // [BH] candidates per group (diagnostics)
   float p;                     // this level's top-p
@@ -1119,7 +1171,7 @@ __device__ inline LevelParams upper_level_params(const UpperParams& U, int k) {
 }
 
 __device__ inline int64_t upper_nodes(const UpperParams& U, int k, int64_t T) {
-  const int64_t n = T / U.lv[k].span;
+  const int64_t n = T >> U.lv[k].shift;
   return n < U.lv[k].cap ? n : U.lv[k].cap;
 }
 
@@ -1128,14 +1180,15 @@ __global__ void __launch_bounds__(256) score_upper(UpperParams U) {
   constexpr int NW = 256 / kWave;
   const int gi = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the queries and the length are loaded together (one round trip)
+  __shared__ __attribute__((aligned(16))) float s_q[GP > 4 ? GP * D : 4];
+  float qv[GP][4];
+  load_group_queries<D, GP>(U.base, gi, lane, qv, s_q);
   int64_t T = U.base.list.T[gi / U.base.H_kv];
   if (T < 0) T = 0;
   if (T > U.base.list.T_cap) T = U.base.list.T_cap;
   int total = 0;
   for (int k = 0; k < U.nlev; ++k) total += (int)upper_nodes(U, k, T);
-  __shared__ __attribute__((aligned(16))) float s_q[GP > 4 ? GP * D : 4];
-  float qv[GP][4];
-  load_group_queries<D, GP>(U.base, gi, lane, qv, s_q);
   __syncthreads();
   // node t's score lines are shared by 8 neighbouring workgroups: one XCD runs them
   for (int t = xcd_grouped_x() * NW + wave; t < total; t += gridDim.x * NW) {
@@ -1159,8 +1212,10 @@ __global__ void __launch_bounds__(small_threads<GP>()) cut_upper(UpperParams U) 
   const LevelParams& B = U.base;
   const int gi = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) stale_check(B, gi);
+  const bool chk = B.check_stale && wave == 0 && (gi % B.H_kv) == 0;
+  const int64_t nb = stale_count(B, gi, lane, chk);   // with the length: one round trip
   int64_t T = B.list.T[gi / B.H_kv];
+  stale_check(B, T, nb, lane, chk);
   if (T < 0) T = 0;
   if (T > B.list.T_cap) T = B.list.T_cap;
   const int C = B.list.C, cshift = B.list.cshift;
@@ -1174,7 +1229,7 @@ __global__ void __launch_bounds__(small_threads<GP>()) cut_upper(UpperParams U) 
     if (k == 0) {
       cnt = (int)n_here;
     } else {
-      orph0 = (T / (lv.span * C)) * C;
+      orph0 = (T >> (lv.shift + cshift)) << cshift;
       const int64_t orph = n_here - orph0;
       cnt = np * C + (int)(orph > 0 ? orph : 0);
     }
@@ -1482,6 +1537,8 @@ static LevelParams level_params(const zha_cfg* cfg, const float* q, const zha_tr
   L.span = span;
   L.C = cfg->C;
   L.cshift = __builtin_ctz((unsigned)cfg->C);
+  L.level_shift = level * L.cshift;
+  L.dummy = (const int64_t*)((const char*)ws + 8);   // inside the 256-byte header
   L.H_kv = cfg->H_kv;
   L.full = (cfg->G >= 32) ? 0xffffffffu : ((1u << cfg->G) - 1u);
   return P;
@@ -1537,6 +1594,7 @@ static int32_t route_impl(const zha_cfg* cfg, const float* q, const zha_tree* tr
       int64_t span = 1;
       for (int i = 0; i < l; ++i) span *= cfg->C;
       v.span = span;
+      v.shift = l * __builtin_ctz((unsigned)cfg->C);
       v.kept = (int32_t*)(base + w.kept[l - 1]);
       v.ucount = (int32_t*)(base + w.ucount[l - 1]);
       v.p = pl[l - 1];
