@@ -173,7 +173,20 @@ struct LevelParams {
   int32_t topk;                // > 0: keep this many nodes per head instead of top-p
   const int64_t* n_built;      // [L][B]: checked against T by the first launch of a route
   int32_t check_stale, L;
+  // Compaction of the parent level (the level whose kept nodes' children this
+  // list holds), done by this level's scoring instead of a launch of its own:
+  // every workgroup compacts it into LDS, workgroup 0 also writes it out.
+  int32_t fused;
+  const uint64_t* fbits;       // parent level's kept bits [BHq][fnwcap]
+  int64_t fnwcap;
+  ListRef flist;               // parent level's candidate list
+  int64_t fucap;
+  int32_t* fkids; uint32_t* fkmask; int32_t* fkcount; int64_t fkcap;   // its kept list out
 };
+
+// Parent levels of at most this many nodes are compacted by the next level's
+// scoring (their kept list fits the scoring kernel's LDS staging).
+constexpr int64_t kFuseCap = 4096;
 
 // The first launch of a route checks that every level was built for the current T.
 // The first launch of a route checks that every level was built for the current
@@ -318,7 +331,7 @@ __device__ inline void score_node(const LevelParams& P, int gi, int node, uint32
   }
 }
 
-template <int D, int GP>
+template <int D, int GP, bool FUSED>
 __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
   constexpr int kPidLds = 4096;
   constexpr int kPre = 4;              // parents per thread loaded with the prologue
@@ -335,7 +348,18 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
   load_group_queries<D, GP>(P, gi, lane, qv, s_q);
   const bool chk = P.check_stale && blockIdx.x == 0 && wave == 0 && (gi % P.H_kv) == 0;
   const int64_t nb = stale_count(P, gi, lane, chk);
-  const ListFetch lf = list_fetch(P.list, gi);
+  // fused: the length and the grandparents' count (the parent level's list),
+  // and the parent level's bitmap rows (every row the capacity allows)
+  const ListFetch lf = list_fetch(FUSED ? P.flist : P.list, gi);
+  uint64_t fw[FUSED ? ZHA_MAX_G : 1];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int g = 0; g < ZHA_MAX_G; ++g) {
+      fw[g] = 0ull;
+      if (wave == 0 && g < P.G && lane < P.fnwcap)
+        fw[g] = P.fbits[((int64_t)gi * P.G + g) * P.fnwcap + lane];
+    }
+  }
   const bool implicit = P.list.ids == nullptr && P.list.pids != nullptr;
   int32_t pre_id[kPre];
   uint32_t pre_m[kPre];
@@ -344,16 +368,79 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
     const int i = threadIdx.x + 256 * k;
     pre_id[k] = 0;
     pre_m[k] = 0u;
-    if (implicit && i < P.list.pcap) {
+    if (implicit && !FUSED && i < P.list.pcap) {
       pre_id[k] = P.list.pids[(int64_t)gi * P.list.pcap + i];
       pre_m[k] = P.list.pmask[(int64_t)gi * P.list.pcap + i];
     }
   }
-  const ListGeo geo = list_geo_from(P.list, lf, P.ucap);
+  ListGeo geo;
+  bool staged;
+  if constexpr (FUSED) {
+    // the parent level's kept list, compacted here from its heads' bitmaps: rows
+    // of 64 list entries, the kept entries (any head's bit) in list order
+    __shared__ uint64_t s_w[ZHA_MAX_G][kFuseCap / 64];   // heads' words per row
+    __shared__ uint64_t s_any[kFuseCap / 64];
+    __shared__ int32_t s_off[kFuseCap / 64];
+    __shared__ int32_t s_np;
+    const ListGeo pg = list_geo_from(P.flist, lf, P.fucap);
+    const int prow = (pg.U + 63) >> 6;                      // <= kFuseCap / 64
+    if (wave == 0) {
+      uint64_t any = 0ull;
+      if (lane < prow) {
+        const int valid = pg.U - lane * 64;
+        const uint64_t vmask = valid >= 64 ? ~0ull : ((1ull << valid) - 1ull);
+#pragma unroll
+        for (int g = 0; g < ZHA_MAX_G; ++g) {
+          const uint64_t wd = fw[g] & vmask;
+          if (g < P.G) s_w[g][lane] = wd;
+          any |= wd;
+        }
+        s_any[lane] = any;
+      }
+      const int c = __popcll(any);
+      const int inc = wave_incl_scan<int>(c);
+      if (lane < prow) s_off[lane] = inc - c;
+      if (lane == kWave - 1) s_np = inc;
+    }
+    __syncthreads();
+    const int np_all = s_np;
+    const int np = np_all < P.fkcap ? np_all : (int)P.fkcap;
+    for (int u = threadIdx.x; u < prow * 64; u += blockDim.x) {
+      const int r = u >> 6, bpos = u & 63;
+      const uint64_t any = s_any[r];
+      if ((any >> bpos) & 1ull) {
+        const int pos = s_off[r] + __popcll(any & ((1ull << bpos) - 1ull));
+        uint32_t m = 0u;
+        for (int g = 0; g < P.G; ++g) m |= (uint32_t)((s_w[g][r] >> bpos) & 1ull) << g;
+        if (pos < np) {
+          s_pid[pos] = list_id(P.flist, pg, gi, u, nullptr);
+          s_pm[pos] = m;
+        }
+      }
+    }
+    ListFetch own;
+    own.T = lf.T;
+    own.count = np;
+    geo = list_geo_from(P.list, own, P.ucap);
+    staged = true;
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int i = threadIdx.x; i < np; i += blockDim.x) {
+        P.fkids[(int64_t)gi * P.fkcap + i] = s_pid[i];
+        P.fkmask[(int64_t)gi * P.fkcap + i] = s_pm[i];
+      }
+      if (threadIdx.x == 0) {
+        if (np_all > P.fkcap) set_status(P.status, ZHA_ECAPACITY);
+        P.fkcount[gi] = np;
+      }
+    }
+  } else {
+    geo = list_geo_from(P.list, lf, P.ucap);
+    staged = implicit && geo.np <= kPidLds;
+  }
   stale_check(P, lf.T, nb, lane, chk);
   const int U = geo.U;
-  const bool staged = implicit && geo.np <= kPidLds;
-  if (staged) {
+  if (staged && !FUSED) {
 #pragma unroll
     for (int k = 0; k < kPre; ++k) {
       const int i = threadIdx.x + 256 * k;
@@ -1449,14 +1536,26 @@ static void launch_score(const LevelParams& P, int64_t ucap, hipStream_t s) {
   if (gx < 1) gx = 1;
   const dim3 grid((unsigned)gx, (unsigned)BH);
   const int GP = P.G <= 4 ? 4 : (P.G <= 8 ? 8 : 16);
+  if (P.fused) {
+    if (P.d == 128) {
+      if (GP == 4) hipLaunchKernelGGL((score_nodes<128, 4, true>), grid, dim3(256), 0, s, P);
+      else if (GP == 8) hipLaunchKernelGGL((score_nodes<128, 8, true>), grid, dim3(256), 0, s, P);
+      else hipLaunchKernelGGL((score_nodes<128, 16, true>), grid, dim3(256), 0, s, P);
+    } else {
+      if (GP == 4) hipLaunchKernelGGL((score_nodes<64, 4, true>), grid, dim3(256), 0, s, P);
+      else if (GP == 8) hipLaunchKernelGGL((score_nodes<64, 8, true>), grid, dim3(256), 0, s, P);
+      else hipLaunchKernelGGL((score_nodes<64, 16, true>), grid, dim3(256), 0, s, P);
+    }
+    return;
+  }
   if (P.d == 128) {
-    if (GP == 4) hipLaunchKernelGGL((score_nodes<128, 4>), grid, dim3(256), 0, s, P);
-    else if (GP == 8) hipLaunchKernelGGL((score_nodes<128, 8>), grid, dim3(256), 0, s, P);
-    else hipLaunchKernelGGL((score_nodes<128, 16>), grid, dim3(256), 0, s, P);
+    if (GP == 4) hipLaunchKernelGGL((score_nodes<128, 4, false>), grid, dim3(256), 0, s, P);
+    else if (GP == 8) hipLaunchKernelGGL((score_nodes<128, 8, false>), grid, dim3(256), 0, s, P);
+    else hipLaunchKernelGGL((score_nodes<128, 16, false>), grid, dim3(256), 0, s, P);
   } else {
-    if (GP == 4) hipLaunchKernelGGL((score_nodes<64, 4>), grid, dim3(256), 0, s, P);
-    else if (GP == 8) hipLaunchKernelGGL((score_nodes<64, 8>), grid, dim3(256), 0, s, P);
-    else hipLaunchKernelGGL((score_nodes<64, 16>), grid, dim3(256), 0, s, P);
+    if (GP == 4) hipLaunchKernelGGL((score_nodes<64, 4, false>), grid, dim3(256), 0, s, P);
+    else if (GP == 8) hipLaunchKernelGGL((score_nodes<64, 8, false>), grid, dim3(256), 0, s, P);
+    else hipLaunchKernelGGL((score_nodes<64, 16, false>), grid, dim3(256), 0, s, P);
   }
 }
 
@@ -1528,6 +1627,9 @@ static LevelParams level_params(const zha_cfg* cfg, const float* q, const zha_tr
   P.n_built = tree->n_built;
   P.check_stale = 0;
   P.L = cfg->L;
+  P.fused = 0;
+  P.fbits = nullptr; P.fnwcap = 0; P.fucap = 0;
+  P.fkids = nullptr; P.fkmask = nullptr; P.fkcount = nullptr; P.fkcap = 0;
   ListRef& L = P.list;
   L.ids = nullptr; L.mask = nullptr; L.count = nullptr; L.cap = 0;
   L.pids = nullptr; L.pmask = nullptr; L.pcount = nullptr; L.pcap = 0;
@@ -1603,10 +1705,25 @@ static int32_t route_impl(const zha_cfg* cfg, const float* q, const zha_tree* tr
     kept_list(lo, U.kids, U.kmask, U.kcount, U.kcap);
     launch_upper(U, s);
   }
+  // A level of at most kFuseCap nodes (other than the leaves) is compacted by
+  // the next level's scoring: one launch fewer per such level.
+  bool pend = false;           // the level above awaits its compaction
+  ListRef pend_list;
   for (int l = lo - 1; l >= 1; --l) {
     LevelParams P = level_params(cfg, q, tree, l, pl[l - 1], ws, w);
     P.topk = kl ? kl[l - 1] : 0;
     P.list.T = T;
+    if (pend) {
+      P.fused = 1;
+      P.fbits = (const uint64_t*)(base + w.selbits[l]);
+      P.fnwcap = w.nwcap[l];
+      P.flist = pend_list;
+      P.fucap = w.cap[l];
+      P.fkids = (int32_t*)(base + w.kids[l]);
+      P.fkmask = (uint32_t*)(base + w.kmask[l]);
+      P.fkcount = (int32_t*)(base + w.kcount[l]);
+      P.fkcap = w.cap[l];
+    }
     if (l < L) {   // children of the kept nodes of level l+1, then the parentless nodes
       P.list.pids = (const int32_t*)(base + w.kids[l]);
       P.list.pmask = (const uint32_t*)(base + w.kmask[l]);
@@ -1626,10 +1743,16 @@ static int32_t route_impl(const zha_cfg* cfg, const float* q, const zha_tree* tr
     X.status = (int32_t*)ws;
     launch_score(P, P.ucap, s);
     P.check_stale = 0;
+    P.fused = 0;
     hipLaunchKernelGGL(cut_topp, dim3(BHq), dim3(kCutThreads), 0, s, P);
-    const int64_t cx = ceil_div(X.nwcap, kCompactRows);
-    hipLaunchKernelGGL(compact_level, dim3((unsigned)(cx < 1 ? 1 : cx), (unsigned)BH),
-                       dim3(kCompactThreads), 0, s, X);
+    pend = l >= 2 && w.cap[l - 1] <= kFuseCap;
+    if (pend) {
+      pend_list = P.list;
+    } else {
+      const int64_t cx = ceil_div(X.nwcap, kCompactRows);
+      hipLaunchKernelGGL(compact_level, dim3((unsigned)(cx < 1 ? 1 : cx), (unsigned)BH),
+                         dim3(kCompactThreads), 0, s, X);
+    }
   }
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
 }

@@ -139,6 +139,9 @@ CASES = {
     "c32": (synth.WORKLOADS["gqa128k"].with_(H_kv=1, G=8, C=32, L=3, n_clusters=64), 32 ** 3 + 777),
     # the deepest tree (L = 8, C = 2): seven small levels in the walk, then the leaves
     "deep8": (synth.WORKLOADS["gqa128k"].with_(H_kv=1, G=4, C=2, L=8, n_clusters=32), 2 ** 8 * 3 + 37),
+    # three levels below the walk (512, 2048 and 8193 nodes): the first two are
+    # compacted by the next level's scoring, the leaves by their own launch
+    "fused": (synth.WORKLOADS["gqa128k"].with_(H_kv=2, G=4, C=4, L=7, n_clusters=64), 4 ** 7 * 2 + 5),
     # one level of 20000 / 30000 leaves: candidate pools beyond 16384 entries (the
     # cut's LDS staging of the general path) and beyond 24576 (the staged path's
     # capacity), and final expansions longer than one register batch per wave
