@@ -1043,47 +1043,46 @@ attend_partial_f32(AttendParams P) {
 // ---------------------------------------------------------------- merge
 //
 // [ASM] "방법론": lse = log sum_s Z_s, out = sum_s (Z_s / Z) a_s, evaluated in the
-// log domain: the maximum of the partial maxima, then the rescaled sums.  Two
-// levels, so a head's partials are read by many workgroups: attend_merge_seg
-// merges each of kMergeSegs contiguous segments of a head's partials into one
-// state (waves take partials w, w+4, ..., lanes over dims, kMergeInFlight
-// partials' loads in flight per wave, the four wave states added in a fixed
-// order); attend_merge_final merges a head's segment states in segment order and
-// writes out and lse.  Deterministic.
-constexpr int kMergeSegs = kMergeSegments;
+// log domain: the maximum of the partial maxima, then the rescaled sums.
 constexpr int kMergeInFlight = 8;
 
+// Merge of the other kernels' partials (one per work item): one workgroup of
+// kMergeItemWaves waves per query head over the head's items, waves taking
+// partials w, w+NW, ..., lanes over dims, kMergeInFlight partials in flight per
+// wave, the wave states added in a fixed order; writes out and lse.  One launch
+// (a step's launches each cost a few microseconds whatever their work; a head
+// has at most a few hundred items).  Deterministic.
+constexpr int kMergeItemWaves = 16;
+
 template <int D>
-__global__ void __launch_bounds__(256) attend_merge_seg(AttendParams P, float* seg) {
+__global__ void __launch_bounds__(64 * kMergeItemWaves) attend_merge_items(AttendParams P, float* out,
+                                                                           float* lse) {
   constexpr int DPL = D / kWave;
-  constexpr int NW = 4;
+  constexpr int NW = kMergeItemWaves;
   constexpr int U = kMergeInFlight;
   __shared__ float red[NW];
   __shared__ float acc_o[NW][D];
   __shared__ float acc_l[NW];
   const int head = blockIdx.x;              // b * Hq + j
-  const int k = blockIdx.y;                 // segment
   const int gi = head / P.G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const GroupInfo g = group_info(P, gi);
   const int n = min(g.items, P.split_cap);
-  const int per = (n + kMergeSegs - 1) / kMergeSegs;
-  const int i_lo = k * per, i_hi = min(n, i_lo + per);
   const float* base = P.part + (int64_t)head * P.split_cap * (D + 2);
   float M = -INFINITY;
-  for (int i = i_lo + threadIdx.x; i < i_hi; i += blockDim.x) M = fmaxf(M, base[(int64_t)i * (D + 2)]);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, base[(int64_t)i * (D + 2)]);
   M = block_max_f<NW>(M, red);
   float l = 0.0f, o[DPL];
 #pragma unroll
   for (int j = 0; j < DPL; ++j) o[j] = 0.0f;
   if (M != -INFINITY) {
-    for (int i0 = i_lo + wave; i0 < i_hi; i0 += NW * U) {
+    for (int i0 = wave; i0 < n; i0 += NW * U) {
       float mi[U], li[U], oi[U][DPL];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = i0 + u * NW;
-        const float* pi = base + (int64_t)(i < i_hi ? i : i_lo) * (D + 2);
-        mi[u] = (i < i_hi) ? pi[0] : -INFINITY;
+        const float* pi = base + (int64_t)(i < n ? i : 0) * (D + 2);
+        mi[u] = (i < n) ? pi[0] : -INFINITY;
         li[u] = pi[1];
 #pragma unroll
         for (int j = 0; j < DPL; ++j) oi[u][j] = pi[2 + lane + j * kWave];
@@ -1101,49 +1100,16 @@ __global__ void __launch_bounds__(256) attend_merge_seg(AttendParams P, float* s
   for (int j = 0; j < DPL; ++j) acc_o[wave][lane + j * kWave] = o[j];
   if (lane == 0) acc_l[wave] = l;
   __syncthreads();
-  float* dst = seg + ((int64_t)head * kMergeSegs + k) * (D + 2);
+  float L = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) L += acc_l[w];
   for (int c = threadIdx.x; c < D; c += blockDim.x) {
     float Ov = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) Ov += acc_o[w][c];
-    dst[2 + c] = Ov;
+    out[(int64_t)head * D + c] = (L > 0.0f) ? Ov / L : 0.0f;
   }
-  if (threadIdx.x == 0) {
-    float L = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) L += acc_l[w];
-    dst[0] = M;
-    dst[1] = L;
-  }
-}
-
-template <int D>
-__global__ void __launch_bounds__(64) attend_merge_final(const float* seg, float* out, float* lse) {
-  constexpr int DPL = D / kWave;
-  const int head = blockIdx.x;
-  const int lane = threadIdx.x;
-  const float* base = seg + (int64_t)head * kMergeSegs * (D + 2);
-  float M = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < kMergeSegs; ++k) M = fmaxf(M, base[(int64_t)k * (D + 2)]);
-  float L = 0.0f, o[DPL];
-#pragma unroll
-  for (int j = 0; j < DPL; ++j) o[j] = 0.0f;
-  if (M != -INFINITY) {
-#pragma unroll
-    for (int k = 0; k < kMergeSegs; ++k) {
-      const float* pk = base + (int64_t)k * (D + 2);
-      const float w = exp2f(pk[0] - M);
-      if (w != 0.0f) {
-        L += pk[1] * w;
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) o[j] += pk[2 + lane + j * kWave] * w;
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < DPL; ++j) out[(int64_t)head * D + lane + j * kWave] = (L > 0.0f) ? o[j] / L : 0.0f;
-  if (lane == 0) lse[head] = (L > 0.0f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+  if (threadIdx.x == 0) lse[head] = (L > 0.0f) ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // Merge of the pipelined kernel's partials: one workgroup per query head over
@@ -1216,7 +1182,7 @@ __global__ void __launch_bounds__(256) attend_merge_runs(AttendParams P, int gri
 
 // The pipelined kernel (bf16, dense or chunks of at least 16 keys) folds its
 // items into runs and is merged by attend_merge_runs; the other kernels write
-// one partial per item and are merged in two levels.
+// one partial per item, merged by attend_merge_items.
 inline bool pipelined(const AttendParams& P, int kv_dtype) {
   return kv_dtype == ZHA_BF16 && (P.leaf_ids == nullptr || P.C >= 16);
 }
@@ -1232,18 +1198,16 @@ static void launch_partial(const AttendParams& P, int kv_dtype, int grid, hipStr
 }
 
 template <int D>
-static void launch_attend(const AttendParams& P, int kv_dtype, int grid, int BHq, float* seg,
-                          float* out, float* lse, hipStream_t s) {
+static void launch_attend(const AttendParams& P, int kv_dtype, int grid, int BHq, float* out,
+                          float* lse, hipStream_t s) {
   if (P.G <= 4) launch_partial<D, 4>(P, kv_dtype, grid, s);
   else if (P.G <= 8) launch_partial<D, 8>(P, kv_dtype, grid, s);
   else launch_partial<D, 16>(P, kv_dtype, grid, s);
-  if (pipelined(P, kv_dtype)) {
+  if (pipelined(P, kv_dtype))
     hipLaunchKernelGGL((attend_merge_runs<D>), dim3(BHq), dim3(256), 0, s, P, grid, out, lse);
-  } else {
-    hipLaunchKernelGGL((attend_merge_seg<D>), dim3(BHq, kMergeSegs), dim3(256), 0, s, P, seg);
-    hipLaunchKernelGGL((attend_merge_final<D>), dim3(BHq), dim3(64), 0, s, (const float*)seg,
+  else
+    hipLaunchKernelGGL((attend_merge_items<D>), dim3(BHq), dim3(64 * kMergeItemWaves), 0, s, P,
                        out, lse);
-  }
 }
 
 // Checks of the arguments every attend call shares.
@@ -1264,7 +1228,7 @@ static int32_t check_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv
   return ZHA_OK;
 }
 
-// The attend's scratch: split partials, merged segment states and the group
+// The attend's scratch: split partials and the group
 // chunk prefix, at the given addresses (256-byte aligned), with split_cap
 // partial slots per query head; device-detected errors go to *status.
 struct AttendScratch {
@@ -1297,9 +1261,9 @@ static int32_t launch_attend_call(const zha_cfg* cfg, const float* q, const zha_
   const int grid = (int)(max_items < kAttendGrid ? max_items : kAttendGrid);
   const int BHq = cfg->B * cfg->H_kv * cfg->G;
   if (cfg->d == 64)
-    launch_attend<64>(P, cfg->kv_dtype, grid, BHq, S.seg, out, lse, s);
+    launch_attend<64>(P, cfg->kv_dtype, grid, BHq, out, lse, s);
   else
-    launch_attend<128>(P, cfg->kv_dtype, grid, BHq, S.seg, out, lse, s);
+    launch_attend<128>(P, cfg->kv_dtype, grid, BHq, out, lse, s);
   return hipGetLastError() == hipSuccess ? ZHA_OK : ZHA_EHIP;
 }
 
@@ -1314,7 +1278,6 @@ static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
   const WsLayout w = ws_layout(*cfg);
   AttendScratch S;
   S.part = (float*)((char*)ws + w.attend_off);
-  S.seg = (float*)((char*)ws + w.merge_off);
   S.prefix = (int32_t*)((char*)ws + w.prefix_off);
   S.status = (int32_t*)ws;
   S.split_cap = w.split_cap;
@@ -1330,8 +1293,8 @@ static int32_t run_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
 // device address is looked up once per device (hipGetSymbolAddress, with that
 // device current) at the first call there, kept in static_scratch_ptr, and only
 // that address is handed to kernels.  Calls on one device share the buffer.
-// No part of it needs to start at zero: every partial and segment state is
-// written before it is read, and without a caller's status word the header
+// No part of it needs to start at zero: every partial is written before it is
+// read, and without a caller's status word the header
 // word is a sink that nothing reads.
 
 constexpr size_t kStaticScratchBytes = size_t(64) << 20;
@@ -1354,21 +1317,18 @@ static int32_t static_scratch(void** ptr) {
   return ZHA_OK;
 }
 
-// Layout of the attend's scratch alone: [0, 256) a status sink, then partials,
-// merged segment states and the chunk prefix.  Returns the bytes needed.
+// Layout of the attend's scratch alone: [0, 256) a status sink, then partials
+// and the chunk prefix.  Returns the bytes needed.
 static size_t static_layout(const zha_cfg& c, char* base, AttendScratch* S) {
   const size_t BH = (size_t)c.B * c.H_kv, BHq = BH * c.G;
   const int32_t cap = run_capacity(c);
   size_t off = 256;
   const size_t part = off;
   off = align_up(off + BHq * (size_t)cap * (c.d + kPartPad) * 4, 256);
-  const size_t seg = off;
-  off = align_up(off + BHq * (size_t)kMergeSegments * (c.d + kPartPad) * 4, 256);
   const size_t prefix = off;
   off = align_up(off + (BH + 1) * 4, 256);
   if (S != nullptr) {
     S->part = (float*)(base + part);
-    S->seg = (float*)(base + seg);
     S->prefix = (int32_t*)(base + prefix);
     S->status = (int32_t*)base;
     S->split_cap = cap;

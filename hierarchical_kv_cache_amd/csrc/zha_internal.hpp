@@ -22,7 +22,7 @@ constexpr int kWave = 64;
 //                       length, scores, true log-mass (quality), per-head kept
 //                       counts and kept bitmaps; plus cut staging
 //   attend region       split partials [B*Hq][split_cap][d+2] fp32, then the
-//                       merged segment states [B*Hq][kMergeSegments][d+2]
+//                       pipelined attend's group chunk prefix
 struct WsLayout {
   size_t build_off = 0, build_bytes = 0;
   size_t route_off = 0, route_bytes = 0;
@@ -39,14 +39,12 @@ struct WsLayout {
   size_t stage = 0;        // cut staging: [B*Hq][stage_cap] (u32 key, f32 w)
   int64_t stage_cap = 0;
   int32_t split_cap = 0;   // partial slots per query head
-  size_t merge_off = 0;    // merged segment states [B*Hq][kMergeSegments][d+2]
   size_t prefix_off = 0;   // pipelined attend: per-group chunk prefix [B*H_kv + 1] (int32)
 };
 
 constexpr int kTileKeys = 64;       // keys per attend tile
 constexpr int kTilesPerItem = 16;   // tiles per split (work item)
 constexpr int kPartPad = 2;         // (m, l) ahead of the d outputs
-constexpr int kMergeSegments = 16;  // first-level merge segments per query head
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -109,8 +107,6 @@ inline WsLayout ws_layout(const zha_cfg& c) {
   w.attend_off = off;
   w.split_cap = run_capacity(c);
   off = align_up(off + (size_t)BHq * w.split_cap * (c.d + kPartPad) * 4, 256);
-  w.merge_off = off;
-  off = align_up(off + (size_t)BHq * kMergeSegments * (c.d + kPartPad) * 4, 256);
   w.prefix_off = off;
   off = align_up(off + (size_t)(BH + 1) * 4, 256);
   w.attend_bytes = off - w.attend_off;

@@ -248,12 +248,12 @@ int32_t zha_attend(const zha_cfg* cfg, const float* q, const zha_kv* kv,
  * zha_attend_static -- zha_attend for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation.  The same kernels and results as zha_attend, with no workspace
- * argument: their scratch (split partials, merged segment states, the chunk
+ * argument: their scratch (split partials and the chunk
  * prefix) lives in a buffer of 64 MiB that the library holds on every device it
  * runs on, from the first call there until the process ends (the call looks up
  * that device's address on its first use; the current device must be the
  * stream's).  Nothing is allocated or freed.  Returns ZHA_EWORKSPACE when the
- * geometry needs more than 64 MiB of scratch (B Hq (2 s + 16) (d + 2) 4 bytes
+ * geometry needs more than 64 MiB of scratch (B Hq 2 s (d + 2) 4 bytes
  * and a little more, s the split slots per query head, about T_cap / 512).
  * status: device int32, or NULL; device-detected errors (ZHA_ECAPACITY) are
  * recorded there with the sticky first-error rule of the workspace status word.
