@@ -63,10 +63,33 @@ struct GroupInfo {
   int32_t items;   // work items incl. the tail item
 };
 
-__device__ inline GroupInfo group_info(const AttendParams& P, int gi) {
+// A group's raw inputs: the sequence length, the leaf count and the first
+// leaf entry (for the sink).  The four loads are issued together, so they cost
+// one round trip; a missing array (dense attention) reads the length instead.
+struct GroupRaw {
+  int64_t T;
+  int32_t count;
+  int32_t id0;
+  uint32_t m0;
+};
+
+__device__ inline GroupRaw group_raw(const AttendParams& P, int gi) {
+  const int64_t* tp = P.T + gi / P.H_kv;
+  const int32_t* cp = P.leaf_count != nullptr ? P.leaf_count + gi : (const int32_t*)tp;
+  const int64_t e0 = (int64_t)gi * P.leaf_cap;
+  const int32_t* ip = P.leaf_ids != nullptr ? P.leaf_ids + e0 : (const int32_t*)tp;
+  const uint32_t* mp = P.leaf_mask != nullptr ? P.leaf_mask + e0 : (const uint32_t*)tp;
+  GroupRaw r;
+  r.T = *tp;
+  r.count = *cp;
+  r.id0 = *ip;
+  r.m0 = *mp;
+  return r;
+}
+
+__device__ inline GroupInfo group_info_from(const AttendParams& P, const GroupRaw& r) {
   GroupInfo g;
-  const int b = gi / P.H_kv;
-  int64_t T = P.T[b];
+  int64_t T = r.T;
   if (T < 0) T = 0;
   if (T > P.T_cap) T = P.T_cap;
   g.T = T;
@@ -74,7 +97,7 @@ __device__ inline GroupInfo group_info(const AttendParams& P, int gi) {
   if (P.leaf_ids == nullptr) {
     g.U = g.n1;
   } else {
-    int32_t u = P.leaf_count[gi];
+    int32_t u = r.count;
     if (u < 0) u = 0;
     if (u > P.leaf_cap) u = P.leaf_cap;
     g.U = u;
@@ -82,6 +105,10 @@ __device__ inline GroupInfo group_info(const AttendParams& P, int gi) {
   g.tiles = (int32_t)(((int64_t)g.U * P.C + kTileKeys - 1) / kTileKeys);
   g.items = (g.tiles + kTilesPerItem - 1) / kTilesPerItem + 1;
   return g;
+}
+
+__device__ inline GroupInfo group_info(const AttendParams& P, int gi) {
+  return group_info_from(P, group_raw(P, gi));
 }
 
 // Token and head mask of key slot `slot` (0..63) of tile `tile` of a group;
@@ -122,13 +149,15 @@ __device__ inline Slot slot_of(const AttendParams& P, int gi, const GroupInfo& g
 
 // Sink mask of a group: heads that did not select leaf 0 take token 0 from the
 // tail tile.  Dense attention and T < C never need it.
+__device__ inline uint32_t sink_mask_from(const AttendParams& P, const GroupInfo& g,
+                                          const GroupRaw& r, uint32_t full) {
+  if (P.leaf_ids == nullptr || g.n1 == 0) return 0u;
+  const uint32_t m0 = (g.U > 0 && r.id0 == 0) ? r.m0 : 0u;
+  return full & ~m0;
+}
 __device__ inline uint32_t sink_mask(const AttendParams& P, int gi, const GroupInfo& g,
                                      uint32_t full) {
-  if (P.leaf_ids == nullptr || g.n1 == 0) return 0u;
-  uint32_t m0 = 0u;
-  if (g.U > 0 && P.leaf_ids[(int64_t)gi * P.leaf_cap] == 0)
-    m0 = P.leaf_mask[(int64_t)gi * P.leaf_cap];
-  return full & ~m0;
+  return sink_mask_from(P, g, group_raw(P, gi), full);
 }
 
 // LDS of the partial kernels.
@@ -471,7 +500,8 @@ attend_partial_bf16(AttendParams P) {
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int gi = find_group(sm.item_prefix, BH, item);
     const int li = item - sm.item_prefix[gi];
-    const GroupInfo g = group_info(P, gi);
+    const GroupRaw graw = group_raw(P, gi);
+    const GroupInfo g = group_info_from(P, graw);
 
     if (gi != cur_group) {
       cur_group = gi;
@@ -503,7 +533,7 @@ attend_partial_bf16(AttendParams P) {
     if (it.tail) {
       it.kbase = 0;
       it.nkeys = kTileKeys;
-      it.smask = sink_mask(P, gi, g, full);
+      it.smask = sink_mask_from(P, g, graw, full);
     } else {
       it.kbase = (int64_t)li * kItemKeys;
       const int64_t left = (int64_t)g.U * P.C - it.kbase;
@@ -743,11 +773,12 @@ attend_partial_bf16_pipe(AttendParams P) {
     for (int k = 0; k < per; ++k) {
       const int gi = g0 + k;
       if (gi < BH) {
-        const GroupInfo g = group_info(P, gi);
+        const GroupRaw r = group_raw(P, gi);
+        const GroupInfo g = group_info_from(P, r);
         sm.g_U[gi] = g.U;
         sm.g_n1[gi] = g.n1;
         sm.g_open[gi] = (int)(g.T - (int64_t)g.n1 * P.C);
-        sm.g_smask[gi] = sink_mask(P, gi, g, full);
+        sm.g_smask[gi] = sink_mask_from(P, g, r, full);
         mine += list_chunks<D, GP>(sm, gi, cshift) + 1 + (sm.g_open[gi] + 15) / 16;
       }
     }
@@ -955,7 +986,8 @@ attend_partial_f32(AttendParams P) {
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int gi = find_group(sm.item_prefix, BH, item);
     const int li = item - sm.item_prefix[gi];
-    const GroupInfo g = group_info(P, gi);
+    const GroupRaw graw = group_raw(P, gi);
+    const GroupInfo g = group_info_from(P, graw);
     for (int idx = threadIdx.x; idx < 16 * D; idx += blockDim.x) {
       const int hh = idx / D, c = idx % D;
       sm.qf[hh][c] = (hh < P.G) ? P.q[((int64_t)gi * P.G + hh) * D + c] * P.qscale : 0.0f;
@@ -963,7 +995,7 @@ attend_partial_f32(AttendParams P) {
     __syncthreads();
 
     const bool tail = (li == g.items - 1);
-    const uint32_t smask = tail ? sink_mask(P, gi, g, full) : 0u;
+    const uint32_t smask = tail ? sink_mask_from(P, g, graw, full) : 0u;
     int tile, t_end, t_step;
     if (tail) { tile = (wave == 0) ? -1 : 0; t_end = 0; t_step = 1; }
     else {
