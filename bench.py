@@ -129,10 +129,9 @@ class Run:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
-    def routed_steps(self, s0, s1, p, ev=None, counts=None, keep=None, router=None, aev=None):
+    def routed_steps(self, s0, s1, p, ev=None, counts=None, keep=None, router=None):
         """Steps s0..s1-1.  ev: dict collecting (route, attend, append) event pairs;
-        aev: list collecting event pairs around the appends only (the other calls
-        stay back to back); keep: one LeafList per step, to hold each step's
+        keep: one LeafList per step, to hold each step's
         routed list; router: replaces the tree route (called with q, T and the
         step's leaf list)."""
         zha, dec, C = self.zha, self.dec, self.wl.C
@@ -141,7 +140,7 @@ class Run:
             q = self.Q[s]
             lst = keep[s - s0] if keep is not None else dec.leaves
             if (self.wl.T0 + s) % C == 0:
-                marks = ev["append"] if ev is not None else aev
+                marks = ev["append"] if ev is not None else None
                 if marks is not None:
                     a0 = torch.cuda.Event(enable_timing=True)
                     a0.record()
@@ -196,18 +195,38 @@ class Run:
                 ev.append((d0, d1))
 
 
-def append_cadence(run, reps=5):
+def append_kind(wl, T):
+    """The levels an append at length T completes (0: no chunk completes)."""
+    if T <= 0 or T % wl.C:
+        return 0
+    k = 1
+    while k < wl.L and T % wl.C ** (k + 1) == 0:
+        k += 1
+    return k
+
+
+def append_cadence(run, p, reps=3, iters=16):
     """zha_append as a decode loop meets it: one call when a chunk completes, every
     C steps ([ZHA] page, append cadence).  An append that completes exactly the
     levels 1..k (the token count is a multiple of C^k and, below the top level,
     not of C^(k+1)) happens for a fraction 1/C^(k-1) - 1/C^k of the chunks
-    (1/C^(L-1) for k = L).  Each kind is timed on its own, cache resident in
-    HBM: the tree is rebuilt at T_b - 1 (untimed), then the append to T_b is
-    timed with events; median of ``reps``.  The amortised cost per decode step
-    is sum_k freq_k t_k / C."""
+    (1/C^(L-1) for k = L).
+
+    Each kind is measured inside the loop, by difference: at a length T_b of
+    that kind, with the tree built, ``iters`` back-to-back iterations of (reset
+    the built counts to those of T_b - 1, append, route, attend) against the
+    same iterations with the counts reset to their own values and no append.
+    The reset is the same small copy in both, and the append rebuilds the same
+    nodes with the same values each time, so the difference is what the append
+    adds to a step where it falls: its kernel queued between the attend and the
+    next route, nothing bracketed by events.  Median over ``reps`` pairs.  The
+    same append alone between two events, queued behind a prefill, is reported
+    as ``isolated_us`` (the events' own overhead included).  The amortised cost per step is sum_k freq_k t_k / C."""
     zha, wl, dec = run.zha, run.wl, run.dec
     C, L = wl.C, wl.L
     Tt = torch.empty(wl.B, dtype=torch.int64, device="cuda")
+    q = run.Q[0]
+    lst = dec.leaves
     kinds = {}
     amort = 0.0
     for k in range(1, L + 1):
@@ -217,10 +236,37 @@ def append_cadence(run, reps=5):
             Tb -= span
         freq = (1.0 / C ** (k - 1) - 1.0 / C ** k) if k < L else 1.0 / C ** (L - 1)
         if Tb < span:
-            kinds[str(k)] = {"us": None, "freq": freq, "T": None}
+            kinds[str(k)] = {"us": None, "isolated_us": None, "freq": freq, "T": None}
             continue
-        times = []
-        for _ in range(reps + 1):
+        assert append_kind(wl, Tb) == k
+        Tt.fill_(Tb)
+        dec.tree.n_built.zero_()
+        dec.prefill(run.K, run.V, Tt)
+        after = dec.tree.n_built.clone()
+        before = torch.tensor([[(Tb - 1) // C ** l] * wl.B for l in range(1, L + 1)],
+                              dtype=after.dtype, device="cuda")
+
+        def loop(with_append):
+            for _ in range(iters):
+                dec.tree.n_built.copy_(before if with_append else after)
+                if with_append:
+                    dec.append(run.K, run.V, Tt, 1)
+                zha.route(run.cfg, q, dec.tree, Tt, p, lst.ids, lst.mask, lst.count, dec.ws)
+                zha.attend(run.cfg, q, run.K, run.V, Tt, lst.ids, lst.mask, lst.count,
+                           dec.out, dec.lse, dec.ws)
+
+        loop(True)
+        loop(False)
+        diffs = []
+        for _ in range(reps):
+            a = timed(lambda: loop(True))
+            b = timed(lambda: loop(False))
+            diffs.append(1000.0 * (a - b) / iters)
+        if zha.ws_status(dec.ws) != 0:
+            raise RuntimeError("append reported a device error")
+        iso = []
+        for _ in range(4):
+            # queued behind a prefill to T_b - 1, so the GPU is busy when the first event is set
             Tt.fill_(Tb - 1)
             dec.tree.n_built.zero_()
             dec.prefill(run.K, run.V, Tt)
@@ -230,22 +276,33 @@ def append_cadence(run, reps=5):
             dec.append(run.K, run.V, Tt, 1)
             e1.record()
             torch.cuda.synchronize()
-            times.append(1000.0 * e0.elapsed_time(e1))
-        if zha.ws_status(dec.ws) != 0:
-            raise RuntimeError("append reported a device error")
-        us = percentile(times[1:], 0.5)      # the first call also loads the kernel
-        kinds[str(k)] = {"us": us, "freq": freq, "T": Tb}
+            iso.append(1000.0 * e0.elapsed_time(e1))
+        us = max(percentile(diffs, 0.5), 0.0)
+        kinds[str(k)] = {"us": us, "isolated_us": percentile(iso[1:], 0.5), "freq": freq, "T": Tb}
         amort += freq * us
     return {"by_levels_completed": kinds,
             "us_per_append": amort,
             "us_per_step": amort / C}
 
 
-def graph_window(run, p, W, K):
+def window_append_us(run, cad, s0, s1):
+    """The in-loop cost of the appends that fall in steps s0..s1-1, by kind."""
+    tot, n = 0.0, 0
+    for s in range(s0, s1):
+        k = append_kind(run.wl, run.wl.T0 + s)
+        if k:
+            us = cad["by_levels_completed"][str(k)]["us"]
+            tot += us if us is not None else 0.0
+            n += 1
+    return tot, n
+
+
+def graph_window(run, p, W, K, cad):
     """The same K steps with route + attend captured once in a HIP graph and
     replayed: each step copies its query and length into the captured buffers,
     runs zha_append eagerly when a chunk completes, then replays.  Returns the
-    route + attend time per step (appends bracketed by events and left out)."""
+    route + attend time per step (the window's appends taken out at their in-loop
+    cost)."""
     zha, dec, wl = run.zha, run.dec, run.wl
     q_st, T_st = run.Q[W].clone(), run.Ts[W].clone()
     lst = dec.leaves
@@ -267,16 +324,11 @@ def graph_window(run, p, W, K):
     with torch.cuda.graph(g):
         step()
     torch.cuda.synchronize()
-    aev = []
 
     def steps():
         for s in range(W, W + K):
             if (wl.T0 + s) % wl.C == 0:
-                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a0.record()
                 dec.append(run.K, run.V, run.Ts[s], 1)
-                a1.record()
-                aev.append((a0, a1))
             q_st.copy_(run.Q[s])
             T_st.copy_(run.Ts[s])
             g.replay()
@@ -284,9 +336,8 @@ def graph_window(run, p, W, K):
     ms = timed(steps)
     if zha.ws_status(dec.ws) != 0:
         raise RuntimeError("graph replay reported a device error")
-    ms -= sum(a.elapsed_time(b) for a, b in aev)
     del g
-    return ms * 1000.0 / K
+    return (ms * 1000.0 - window_append_us(run, cad, W, W + K)[0]) / K
 
 
 def timed(fn):
@@ -519,23 +570,23 @@ def main():
     build_ms = run.prefill()
     log(f"[bench] prefill tree build: {build_ms:.2f} ms")
 
-    # ---- routed: warmup, then exactly K timed steps, nothing else in the queue
-    # (events bracket only the appends that fall in the window)
+    # ---- routed: warmup, then exactly K timed steps back to back, nothing else in
+    # the queue (the appends that fall in the window included, no events inside)
     run.routed_steps(0, W, p)
-    aev = []
-    total_ms = timed(lambda: run.routed_steps(W, W + K, p, aev=aev))
+    total_ms = timed(lambda: run.routed_steps(W, W + K, p))
     st = zha.ws_status(run.dec.ws)
     if st != 0:
         raise RuntimeError(f"device status {zha.status_str(st)}")
-    window_append_ms = sum(a.elapsed_time(b) for a, b in aev)
-    ra_us = (total_ms - window_append_ms) * 1000.0 / K
     # the append at its cadence (one per C steps, with the parents it completes),
-    # timed on its own: the window holds too few steps to sample it
-    cad = append_cadence(run)
+    # measured in the loop kind by kind: a K-step window holds too few chunks to
+    # sample the mixture, so the window's own appends are replaced by it
+    cad = append_cadence(run, p)
+    win_app_us, n_app = window_append_us(run, cad, W, W + K)
+    ra_us = (total_ms * 1000.0 - win_app_us) / K
     us_step = ra_us + cad["us_per_step"]
     log(f"[bench] routed p={p}: {us_step:.1f} us/step (route + attend {ra_us:.1f}, append "
         f"{cad['us_per_append']:.1f} us per chunk = {cad['us_per_step']:.2f} us/step; "
-        f"raw window {total_ms * 1000.0 / K:.1f} with {len(aev)} appends)")
+        f"raw window {total_ms * 1000.0 / K:.1f} with {n_app} appends)")
 
     # ---- the same steps again, for the breakdown: events around each call (each
     # event is a queue marker, so route_us + attend_us slightly exceed a step),
@@ -573,7 +624,7 @@ def main():
     torch.cuda.empty_cache()
     log(f"[bench]   per step (events): warm median {warm['median_us']:.1f} p90 {warm['p90_us']:.1f} us; "
         f"cold median {cold['median_us']:.1f} p90 {cold['p90_us']:.1f} us")
-    graph_ra_us = graph_window(run, p, W, K)
+    graph_ra_us = graph_window(run, p, W, K, cad)
     log(f"[bench]   graph-replayed route + attend: {graph_ra_us:.1f} us/step "
         f"(eager {ra_us:.1f})")
     copy_gbps = copy_bandwidth()
@@ -586,10 +637,8 @@ def main():
             continue
         run.prefill()
         run.routed_steps(0, W, ps)
-        aev_s = []
-        ms = timed(lambda: run.routed_steps(W, W + K, ps, aev=aev_s))
-        ms -= sum(a.elapsed_time(b) for a, b in aev_s)
-        extra[f"p{ps}"] = {"us_per_step": ms * 1000.0 / K + cad["us_per_step"]}
+        ms = timed(lambda: run.routed_steps(W, W + K, ps))
+        extra[f"p{ps}"] = {"us_per_step": (ms * 1000.0 - win_app_us) / K + cad["us_per_step"]}
         log(f"[bench] routed p={ps}: {extra[f'p{ps}']['us_per_step']:.1f} us/step")
 
     # ---- dense baseline over the same steps
@@ -776,11 +825,14 @@ def main():
         "append": {**cad, "frac_of_step": cad["us_per_step"] / us_step,
                    "within_1pct": cad["us_per_step"] <= 0.01 * us_step,
                    "note": "zha_append per completed chunk (one call every C steps), by the levels "
-                           "it completes, weighted by their cadence; us_per_step = us_per_append / C, "
-                           "included in value"},
+                           "it completes, measured inside the decode loop (difference of back-to-back "
+                           "iterations with and without the append; isolated_us: the call alone "
+                           "between two events), weighted by their cadence; us_per_step = "
+                           "us_per_append / C, included in value in place of the window's own "
+                           "appends"},
         "append_us_each": cad["us_per_append"],
         "window_us_per_step_raw": total_ms * 1000.0 / K,
-        "appends_in_timed_steps": len(aev),
+        "appends_in_timed_steps": n_app,
         "prefill_build_ms": build_ms,
         "step_latency": {"warm": warm, "cold": cold,
                          "note": "per-step route + attend from per-call events (queue markers add "

@@ -450,6 +450,27 @@ __device__ inline void halve_round(float* a, int lane) {
   }
 }
 
+// Reference queries under RoPE for the small-C leaves, in two steps shared by
+// the one-wave leaf and the plane-per-wave append, so the two round alike: the
+// fp64 angle of dimension c at position pos (rotate-half pairs (i, i + d/2)),
+// then dimension c of a row rotated by it and scaled.
+template <int D>
+__device__ inline void small_rope_angle(int c, int64_t pos, double rope_base, double& cs,
+                                        double& sn) {
+  const int i = c < D / 2 ? c : c - D / 2;
+  const double theta = pow(rope_base, -2.0 * (double)i / (double)D);
+  sincos((double)pos * theta, &sn, &cs);
+}
+template <int D>
+__device__ inline float small_rope_q(const float* row, int c, double cs, double sn, float scale) {
+#pragma clang fp contract(off)
+  constexpr int H2 = D / 2;
+  const int i = c < H2 ? c : c - H2;
+  const double a = row[i], bb = row[i + H2];
+  const float x = c < H2 ? (float)(a * cs - bb * sn) : (float)(a * sn + bb * cs);
+  return x * scale;
+}
+
 // One leaf per wave; the wave's LDS holds the 16 scaled reference queries (qv,
 // [16][D]) and the leaf's softmax weights (w, [16][CP]).
 template <int D, int CP>
@@ -485,17 +506,14 @@ struct SmallLeaf {
     }
 #pragma unroll
     for (int k = 0; k < DPL; ++k) {
-      const int c = d0 + k, i = c < H2 ? c : c - H2;   // rotate-half pair (i, i + d/2)
-      const double theta = pow((double)P.rope_base, -2.0 * (double)i / (double)D);
-      double sn, cs;
-      sincos((double)pos * theta, &sn, &cs);
+      const int c = d0 + k;
+      double cs, sn;
+      small_rope_angle<D>(c, pos, (double)P.rope_base, cs, sn);
 #pragma unroll 2
       for (int r = 0; r < 16; ++r) {
         const int rr = r < R ? r : R - 1;
-        const double a = qr[rr * D + i], bb = qr[rr * D + i + H2];
-        float x = 0.0f;
-        if (r < R) x = c < H2 ? (float)(a * cs - bb * sn) : (float)(a * sn + bb * cs);
-        qv[r][d0 + k] = x * P.scale;
+        const float x = small_rope_q<D>(qr + rr * D, c, cs, sn, P.scale);
+        qv[r][d0 + k] = r < R ? x : 0.0f;
       }
     }
     wave_lds_sync();
@@ -504,18 +522,21 @@ struct SmallLeaf {
   // Leaf n of sequence-head gi, with the queries already in qv.
   typedef float Keys[CP][DPL];
 
-  // This lane's dimensions of leaf n's keys (padding keys zero).
+  // This lane's dimensions of leaf n's keys.  A padding key (j >= C) repeats
+  // the last real key: its softmax weight is zero, so any finite value serves,
+  // and every load goes out at once instead of one per branch on C.
   __device__ static void load_keys(const BuildParams& P, int gi, int64_t n, Keys& kv, int lane) {
     const int C = P.C, d0 = DPL * lane;
     const uint16_t* kr = (const uint16_t*)P.K + ((int64_t)gi * P.T_cap + n * C) * D + d0;
 #pragma unroll
     for (int j = 0; j < CP; ++j) {
+      const int64_t row = j < C ? j : C - 1;
       if constexpr (DPL == 2) {
-        const uint32_t pr = j < C ? *(const uint32_t*)(kr + (int64_t)j * D) : 0u;
+        const uint32_t pr = *(const uint32_t*)(kr + row * D);
         kv[j][0] = bf16_lo(pr);
         kv[j][1] = bf16_hi(pr);
       } else {
-        kv[j][0] = j < C ? __uint_as_float((uint32_t)kr[(int64_t)j * D] << 16) : 0.0f;
+        kv[j][0] = __uint_as_float((uint32_t)kr[row * D] << 16);
       }
     }
   }
@@ -595,6 +616,79 @@ struct SmallLeaf {
     }
     wave_lds_sync();                       // the weights are rewritten by the next leaf
   }
+
+  // Plane r of leaf n alone, in one wave, from its keys kv: the append's leaf,
+  // with its R planes on R waves.  The arithmetic is leaf_from's, step for step
+  // and in the same order (this lane's partial dots, lane sums over xor
+  // distances 32 .. 1, the keys' softmax terms summed pairwise by key index
+  // bits 0, 1, 2, the weights applied to the keys in key order), so the plane
+  // equals the one-wave leaf's bit for bit.  Needs no LDS.
+  template <bool ROPE>
+  __device__ static void plane(const BuildParams& P, int gi, int h, int64_t n, int r,
+                               const Keys& kv, int lane) {
+    const int C = P.C, R = P.R, d0 = DPL * lane;
+    const float* row = P.qref + ((int64_t)h * R + r) * D;
+    float q[DPL];
+    if constexpr (!ROPE) {
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) q[k] = row[d0 + k] * P.scale;
+    } else {
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        double cs, sn;
+        small_rope_angle<D>(d0 + k, n * C, (double)P.rope_base, cs, sn);
+        q[k] = small_rope_q<D>(row, d0 + k, cs, sn, P.scale);
+      }
+    }
+    float z[CP];
+#pragma unroll
+    for (int j = 0; j < CP; ++j) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) acc = fmaf(q[k], kv[j][k], acc);
+      z[j] = acc;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+#pragma unroll
+      for (int j = 0; j < CP; ++j) z[j] += __shfl_xor(z[j], m, 64);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < CP; ++j) {
+      if (j >= C) z[j] = -INFINITY;
+      M = fmaxf(M, z[j]);
+    }
+    float ex[CP], s[CP], sz[CP];
+#pragma unroll
+    for (int j = 0; j < CP; ++j) {
+      ex[j] = j < C ? expf(z[j] - M) : 0.0f;
+      s[j] = ex[j];
+      sz[j] = j < C ? ex[j] * z[j] : 0.0f;
+    }
+#pragma unroll
+    for (int w = 1; w < CP; w <<= 1) {
+#pragma unroll
+      for (int j = 0; j < CP; j += 2 * w) {
+        s[j] = s[j] + s[j + w];
+        sz[j] = sz[j] + sz[j + w];
+      }
+    }
+    const float S = s[0];
+    if (lane == 0) P.bhat[((int64_t)gi * P.ncap + n) * R + r] = (M + logf(S)) - sz[0] / S;
+    float acc[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[k] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CP; ++j) {
+      const float w = ex[j] / S;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(w, kv[j][k], acc[k]);
+    }
+    float* kh = P.khat + (((int64_t)gi * P.ncap + n) * R + r) * D + d0;
+    if constexpr (DPL == 2) *(float2*)kh = make_float2(acc[0], acc[1]);
+    else kh[0] = acc[0];
+  }
 };
 
 template <int D, int CP>
@@ -626,7 +720,17 @@ __device__ inline double parent_theta(const BuildParams& P, int lane) {
   return P.rope ? pow((double)P.rope_base, -2.0 * (double)(lane % (D / 2)) / (double)D) : 0.0;
 }
 
-template <int D, int MT>
+// The same frequency where the caller has already branched on RoPE.  The fp64
+// pow is straight-line code, so the optimiser would otherwise compute it ahead
+// of the branch (and out of loops) on every path; the empty asm statement on
+// its input keeps it where it is written.
+template <int D>
+__device__ inline double rope_theta_here(float rope_base, int i) {
+  asm volatile("" : "+v"(rope_base));
+  return pow((double)rope_base, -2.0 * (double)i / (double)D);
+}
+
+template <int D, int MT, int RP = -1>   // RP: RoPE off (0), on (1), or P.rope (-1)
 __device__ inline void parent_pair(const BuildParams& P, int gi, int h, int64_t n, int r,
                                    double theta, int lane) {
   static_assert(MT >= 1 && 4 * MT <= kMaxC, "child rounds");
@@ -649,7 +753,7 @@ __device__ inline void parent_pair(const BuildParams& P, int gi, int h, int64_t 
   const float bl = lane < C ? P.bhat_ch[((int64_t)gi * P.ncap_ch + ch0 + lane) * R + r] : 0.0f;
   // plane r's reference query at the node's first key position
   float qv[DPL];
-  if (!P.rope) {
+  if (RP == 0 || (RP < 0 && !P.rope)) {
 #pragma unroll
     for (int k = 0; k < DPL; ++k) qv[k] = qr[r * D + ds + k];
   } else {
@@ -756,9 +860,9 @@ __global__ void __launch_bounds__(256) build_parents(BuildParams P) {
 // are missing, so any growth is built, only slower.
 
 struct AppendParams {
-  BuildParams lv[ZHA_MAX_L];   // level l at index l-1 (append mode)
-  int32_t L;
+  int32_t L;                   // first, so the prologue's arguments share few cache lines
   int32_t* arrive;             // [B] arrival counters, zero between calls
+  BuildParams lv[ZHA_MAX_L];   // level l at index l-1 (append mode)
 };
 
 constexpr int kLeafGeneric = 0, kLeafMfma = 1, kLeafSmall = 2;
@@ -770,76 +874,127 @@ __device__ inline void workgroup_sync_global() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Nodes [n0, n1) of level l are missing: from the count before the call (old)
+// to the count the length T completes, within the level's capacity.
+__device__ inline void missing_nodes(const BuildParams& P, int l, int64_t old, int64_t T,
+                                     int cshift, int64_t& n0, int64_t& n1) {
+  n1 = T >> (l * cshift);
+  if (n1 > P.ncap) n1 = P.ncap;
+  n0 = old < 0 ? 0 : old;
+  if (n0 > n1) n0 = n1;
+}
+
+// The append's parents, levels 2..L with new nodes (bit l of work): their
+// (node, plane) pairs over all waves, a barrier before each level that reads
+// nodes written in this launch.  RP as for parent_pair: a compile-time RoPE
+// choice leaves the non-RoPE cascade without the fp64 angle code (used where
+// the registers allow both copies).
+template <int D, int MT, int NW, int RP>
+__device__ inline void append_parents(const AppendParams& A, const int64_t* s_old, int64_t T,
+                                      int cshift, uint32_t work, bool dirty, int gi, int h,
+                                      int wave, int lane) {
+  const int R = A.lv[0].R;
+  double theta = 0.0;
+  if (RP == 1 || (RP < 0 && A.lv[0].rope))
+    theta = rope_theta_here<D>(A.lv[0].rope_base, lane % (D / 2));
+  for (int l = 2; l <= A.L; ++l) {
+    if (!((work >> l) & 1u)) continue;
+    const BuildParams& P = A.lv[l - 1];
+    int64_t n0, n1;
+    missing_nodes(P, l, s_old[l - 1], T, cshift, n0, n1);
+    if (dirty) workgroup_sync_global();
+    const int64_t items = (n1 - n0) * R;
+    for (int64_t i = wave; i < items; i += NW)
+      parent_pair<D, MT, RP>(P, gi, h, n0 + i / R, (int)(i % R), theta, lane);
+    dirty = true;
+  }
+}
+
+// Plane r of every new small-C leaf of the tree on wave r (R <= 16 <= waves).
+template <int D, int CL, int NW, bool ROPE>
+__device__ inline void append_small_leaves(const BuildParams& P, int gi, int h, int64_t n0,
+                                           int64_t n1, int wave, int lane) {
+  using S = SmallLeaf<D, CL>;
+  for (int64_t n = n0; n < n1; ++n)
+    for (int r = wave; r < P.R; r += NW) {
+      typename S::Keys kv;
+      S::load_keys(P, gi, n, kv, lane);
+      S::template plane<ROPE>(P, gi, h, n, r, kv, lane);
+    }
+}
+
 template <int D, int KIND, int CL, int MT, int NT>
 __global__ void __launch_bounds__(NT) append_chunk(AppendParams A) {
   constexpr int NW = NT / kWave;
-  constexpr int LW = 4;   // waves with a leaf staging area (small chunks)
   static_assert(KIND != kLeafGeneric || NT == kGenericThreads, "generic leaves: one workgroup");
-  static_assert(NW > LW || KIND == kLeafGeneric, "a wave besides the leaf waves");
+  static_assert(KIND != kLeafSmall || NW >= 16, "small leaves: a wave per plane");
   const int gi = blockIdx.x;
   const BuildParams& P1 = A.lv[0];
-  const int H = P1.H_kv, R = P1.R, L = A.L;
+  // The arguments the prologue needs, loaded together: a kernel argument first
+  // read inside a branch costs a round trip of its own, and they add up.
+  const int H = P1.H_kv, L = A.L, Bn = P1.B, C1 = P1.C;
+  const int64_t* const Tp = P1.T;
+  int64_t* const nb = P1.n_built;
+  const int64_t Tcap = P1.T_cap;
+  asm volatile("" ::"s"(H), "s"(L), "s"(Bn), "s"(C1), "s"(Tp), "s"(nb), "s"(Tcap));
   const int b = gi / H, h = gi % H;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int last = NW - 1;   // reads the old counts and arrives; builds no leaf
+  const int last = NW - 1;   // reads the old counts and arrives
   // ---- the old node counts of every level and the length, in one round trip
-  // by the last wave, while the leaf waves stage the reference queries (without
-  // RoPE they do not depend on the node)
+  // by the last wave, while the matrix-core leaf wave stages the reference
+  // queries (without RoPE they do not depend on the node)
   __shared__ int64_t s_old[ZHA_MAX_L + 1];
   if (wave == last && (lane < L || lane == kWave - 1)) {
     // one load instruction: lanes below L read a level's count, the top lane T
-    const int64_t* src = lane < L ? P1.n_built + (int64_t)lane * P1.B + b : P1.T + b;
+    const int64_t* src = lane < L ? nb + (int64_t)lane * Bn + b : Tp + b;
     s_old[lane < L ? lane : ZHA_MAX_L] = *src;
   }
   using M = MfmaLeaf<D, KIND == kLeafMfma ? CL : 16>;
-  using S = SmallLeaf<D, KIND == kLeafSmall ? CL : 4>;
-  __shared__ __attribute__((aligned(16))) unsigned char
-      leaf_lds[KIND == kLeafMfma ? M::kLds : KIND == kLeafSmall ? LW * 16 * (CL + D) * 4 : 16];
-  float (*wsh)[16][S::kCP] = reinterpret_cast<float (*)[16][S::kCP]>(leaf_lds);
-  float (*qsh)[16][D] = reinterpret_cast<float (*)[16][D]>(leaf_lds + LW * 16 * S::kCP * 4);
+  __shared__ __attribute__((aligned(16))) unsigned char leaf_lds[KIND == kLeafMfma ? M::kLds : 16];
   typename M::QOps qa;
   if constexpr (KIND == kLeafMfma) {
     if (wave == 0) {
       M::init(leaf_lds, lane);
       if (!P1.rope) M::build_qa(P1, h, 1.0, 0.0, leaf_lds, qa, lane);
     }
-  } else if constexpr (KIND == kLeafSmall) {
-    if (wave < LW && !P1.rope) S::set_q(P1, h, 0, qsh[wave], lane);
   }
   __syncthreads();
   int64_t T = s_old[ZHA_MAX_L];
   if (T < 0) T = 0;
-  if (T > P1.T_cap) T = P1.T_cap;
-  const int cshift = __builtin_ctz((unsigned)P1.C);   // C is a power of two: T / C^l by shifts
-  // Nodes [n0, n1) of level l are missing.
-  auto range = [&](int l, int64_t& n0, int64_t& n1) {
-    const BuildParams& P = A.lv[l - 1];
-    n1 = T >> (l * cshift);
-    if (n1 > P.ncap) n1 = P.ncap;
-    n0 = s_old[l - 1];
-    if (n0 < 0) n0 = 0;
-    if (n0 > n1) n0 = n1;
-  };
+  if (T > Tcap) T = Tcap;
+  const int cshift = __builtin_ctz((unsigned)C1);   // C is a power of two: T / C^l by shifts
+  // Which levels above the leaves have new nodes (bit l), from the length and
+  // the old counts alone: a level's capacity is at least T_cap / C^l (checked
+  // on the host), so it cannot cut the range here.  A leaf-only append then
+  // runs no parent code and reads no parent level's arguments.
+  uint32_t work = 0;
+#pragma unroll
+  for (int l = 2; l <= ZHA_MAX_L; ++l) {
+    const int64_t old = s_old[l - 1];   // (every entry is read: no branch per level)
+    work |= (uint32_t)((l <= L) & ((T >> (l * cshift)) > (old < 0 ? 0 : old))) << l;
+  }
   // The sequence's node counts: every tree of it has read the old ones before
   // it arrives, so the last to arrive may write the new ones.
   auto arrive = [&] {
     const int prev = __hip_atomic_fetch_add(&A.arrive[b], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == H - 1) {
-      for (int l = 1; l <= L; ++l) P1.n_built[(int64_t)(l - 1) * P1.B + b] = T >> (l * cshift);
+      for (int l = 1; l <= L; ++l) nb[(int64_t)(l - 1) * Bn + b] = T >> (l * cshift);
       __hip_atomic_store(&A.arrive[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
   if (KIND != kLeafGeneric && threadIdx.x == last * kWave) arrive();
-  // ---- level 1: the tree's new leaves, one wave each (generic: the workgroup)
+  // ---- level 1: the tree's new leaves: one wave each (matrix cores), one wave
+  // per plane (small C), or the workgroup (generic)
   int64_t n0, n1;
-  range(1, n0, n1);
-  bool dirty = n1 > n0;   // nodes written since the last barrier
+  missing_nodes(P1, 1, s_old[0], T, cshift, n0, n1);
+  const bool dirty = n1 > n0;   // nodes written since the last barrier
   if constexpr (KIND == kLeafGeneric) {
     __shared__ BuildSmem sm;
     for (int64_t n = n0; n < n1; ++n) generic_leaf(P1, sm, gi, h, n);
   } else if constexpr (KIND == kLeafMfma) {
     if (wave == 0 && n0 < n1) {
-      const double theta = P1.rope ? pow((double)P1.rope_base, -2.0 * (double)(lane % M::H2) / (double)D) : 0.0;
+      double theta = 0.0;
+      if (P1.rope) theta = rope_theta_here<D>(P1.rope_base, lane % M::H2);
       for (int64_t n = n0; n < n1; ++n) {
         typename M::Keys kv;
         M::fetch(P1, gi, n, kv, lane);        // in flight while the queries are staged
@@ -852,27 +1007,17 @@ __global__ void __launch_bounds__(NT) append_chunk(AppendParams A) {
       }
     }
   } else {
-    if (wave < LW) {
-      for (int64_t n = n0 + wave; n < n1; n += LW) {
-        typename S::Keys kv;
-        S::load_keys(P1, gi, n, kv, lane);    // in flight while the queries are staged
-        if (P1.rope) S::set_q(P1, h, n * P1.C, qsh[wave], lane);
-        S::leaf_from(P1, gi, n, kv, qsh[wave], wsh[wave], lane);
-      }
-    }
+    if (P1.rope) append_small_leaves<D, CL, NW, true>(P1, gi, h, n0, n1, wave, lane);
+    else append_small_leaves<D, CL, NW, false>(P1, gi, h, n0, n1, wave, lane);
   }
-  // ---- levels 2..L: (node, plane) pairs of the new parents over all waves; a
-  // barrier orders a level's reads after the writes of the levels below
-  const double theta = parent_theta<D>(P1, lane);
-  for (int l = 2; l <= L; ++l) {
-    range(l, n0, n1);
-    if (n1 <= n0) continue;
-    if (dirty) workgroup_sync_global();
-    const BuildParams& P = A.lv[l - 1];
-    const int64_t items = (n1 - n0) * R;
-    for (int64_t i = wave; i < items; i += NW)
-      parent_pair<D, MT>(P, gi, h, n0 + i / R, (int)(i % R), theta, lane);
-    dirty = true;
+  // ---- levels 2..L with new nodes
+  if (work != 0) {
+    if constexpr (KIND == kLeafSmall) {
+      if (P1.rope) append_parents<D, MT, NW, 1>(A, s_old, T, cshift, work, dirty, gi, h, wave, lane);
+      else append_parents<D, MT, NW, 0>(A, s_old, T, cshift, work, dirty, gi, h, wave, lane);
+    } else {
+      append_parents<D, MT, NW, -1>(A, s_old, T, cshift, work, dirty, gi, h, wave, lane);
+    }
   }
   if (KIND == kLeafGeneric && threadIdx.x == 0) arrive();
 }

@@ -115,27 +115,30 @@ def test_build_rope_parent_correction():
         _compare_tree(cfg, K, qref, tree, T, wl.rope_base, b=b)
 
 
-@pytest.mark.parametrize("C,L,kv,rope", [(8, 3, "bf16", False), (16, 2, "bf16", False),
-                                         (4, 4, "bf16", False), (64, 2, "bf16", False),
-                                         (16, 2, "f32", False), (4, 3, "f32", False),
-                                         (4, 3, "bf16", True), (32, 2, "bf16", True)])
-def test_append_cascade_equals_prefill_build(C, L, kv, rope):
+@pytest.mark.parametrize("C,L,kv,rope,R", [(8, 3, "bf16", False, 16), (16, 2, "bf16", False, 16),
+                                           (4, 4, "bf16", False, 16), (64, 2, "bf16", False, 16),
+                                           (16, 2, "f32", False, 16), (4, 3, "f32", False, 16),
+                                           (4, 3, "bf16", True, 16), (32, 2, "bf16", True, 16),
+                                           (2, 5, "bf16", False, 16), (8, 2, "bf16", False, 12),
+                                           (2, 3, "bf16", True, 5)])
+def test_append_cascade_equals_prefill_build(C, L, kv, rope, R):
     """Growing T one token at a time with zha_append yields exactly the tree a
     prefill build of the final length gives (the append cadence).  One token at a
     time takes the one-launch cascade (one workgroup per sequence); a jump of more
     than C tokens takes the per-level launches.  C = 16..64 bf16 leaves use the
-    matrix-core builder, C <= 8 the one-wave-per-leaf one, fp32 keys the
-    workgroup-per-leaf one.  Under RoPE the matrix-core prefill advances each
+    matrix-core builder; at C <= 8 the prefill builds a leaf per wave and the
+    one-launch append a plane per wave (R < 16 included), which must agree bit
+    for bit; fp32 keys use the workgroup-per-leaf builder.  Under RoPE the matrix-core prefill advances each
     wave's rotation angle from leaf to leaf while an append rotates from the
     leaf's own position, so there the two agree to the builder's accuracy, not
     bit for bit."""
-    wl = _workload("rope_batch" if rope else "gqa128k", B=1, H_kv=2, G=4, C=C, L=L, n_clusters=16,
-                   kv_dtype=kv)
+    wl = _workload("rope_batch" if rope else "gqa128k", B=1, H_kv=2, G=4, C=C, L=L, R=R,
+                   n_clusters=16, kv_dtype=kv)
     T0, T1 = C ** L - 37 if C ** L > 40 else C ** L - 3, C ** L * 2 + 70
     T_cap = T1 + C
     K, V = synth.make_cache(wl.with_(N=T1, open_len=0, steps=0), DEV, T_cap)
     qref = synth.make_qref(wl, DEV)
-    cfg = zha.Config(B=1, H_kv=2, G=4, d=128, C=C, L=L, R=16, T_cap=T_cap,
+    cfg = zha.Config(B=1, H_kv=2, G=4, d=128, C=C, L=L, R=R, T_cap=T_cap,
                      kv_dtype=zha.F32 if kv == "f32" else zha.BF16, rope=rope, rope_base=wl.rope_base)
     tree = zha.Tree(cfg, DEV)
     ws = zha.new_workspace(cfg)
