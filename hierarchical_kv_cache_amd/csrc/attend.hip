@@ -464,6 +464,7 @@ __device__ inline void wave_state_out(WaveBuf<D, GP>& wb, int lane, float m_run,
 template <int D, int GP, bool CONTIG>
 __global__ void __launch_bounds__(256)
 attend_partial_bf16(AttendParams P) {
+  touch_args(P);
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(GP == 4 || GP == 8 || GP == 16, "padded heads");
   constexpr int KSTEPS = D / 32;
@@ -750,6 +751,7 @@ __device__ inline int run_grid(int launched, int total) {
 template <int D, int GP>
 __global__ void __launch_bounds__(256, 2)
 attend_partial_bf16_pipe(AttendParams P) {
+  touch_args(P);
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(GP == 4 || GP == 8 || GP == 16, "padded heads");
   constexpr int KSTEPS = D / 32;
@@ -973,6 +975,7 @@ attend_partial_bf16_pipe(AttendParams P) {
 template <int D, int GP>
 __global__ void __launch_bounds__(256)
 attend_partial_f32(AttendParams P) {
+  touch_args(P);
   constexpr int DPL = D / kWave;            // dims per lane in P V
   __shared__ AttendSmem<D> sm;
   const int lane = threadIdx.x & 63;
@@ -1089,6 +1092,7 @@ constexpr int kMergeItemWaves = 16;
 template <int D>
 __global__ void __launch_bounds__(64 * kMergeItemWaves) attend_merge_items(AttendParams P, float* out,
                                                                            float* lse) {
+  touch_args(P);
   constexpr int DPL = D / kWave;
   constexpr int NW = kMergeItemWaves;
   constexpr int U = kMergeInFlight;
@@ -1152,6 +1156,7 @@ __global__ void __launch_bounds__(64 * kMergeItemWaves) attend_merge_items(Atten
 template <int D>
 __global__ void __launch_bounds__(256) attend_merge_runs(AttendParams P, int grid, float* out,
                                                          float* lse) {
+  touch_args(P);
   constexpr int DPL = D / kWave;
   constexpr int NW = 4;
   constexpr int U = kMergeInFlight;

@@ -333,6 +333,7 @@ __device__ inline void score_node(const LevelParams& P, int gi, int node, uint32
 
 template <int D, int GP, bool FUSED>
 __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
+  touch_args(P);
   constexpr int kPidLds = 4096;
   constexpr int kPre = 4;              // parents per thread loaded with the prologue
   __shared__ int32_t s_pid[kPidLds];   // the group's kept parents (implicit lists)
@@ -1071,12 +1072,14 @@ __device__ inline void cut_head(const LevelParams& P, CutSmem& sm) {
 }
 
 __global__ void __launch_bounds__(kCutThreads) cut_topp(LevelParams P) {
+  touch_args(P);
   __shared__ CutSmem sm;
   cut_head(P, sm);
 }
 
 // grid (ceil(nwcap / kCompactRows), groups).
 __global__ void __launch_bounds__(kCompactThreads) compact_level(CompactParams P) {
+  touch_args(P);
   constexpr int NW = kCompactThreads / kWave;
   constexpr int RW = kCompactRows;
   __shared__ uint64_t s_words[ZHA_MAX_G][RW];   // this workgroup's rows, per head
@@ -1264,6 +1267,7 @@ __device__ inline int64_t upper_nodes(const UpperParams& U, int k, int64_t T) {
 
 template <int D, int GP>
 __global__ void __launch_bounds__(256) score_upper(UpperParams U) {
+  touch_args(U);
   constexpr int NW = 256 / kWave;
   const int gi = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1287,6 +1291,7 @@ __global__ void __launch_bounds__(256) score_upper(UpperParams U) {
 
 template <int GP>
 __global__ void __launch_bounds__(small_threads<GP>()) cut_upper(UpperParams U) {
+  touch_args(U);
   constexpr int NT = small_threads<GP>();
   constexpr int NW = NT / kWave;
   __shared__ int32_t s_id[kSmallCap];     // this level's list: node ids

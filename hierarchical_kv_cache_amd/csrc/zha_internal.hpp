@@ -116,6 +116,26 @@ inline WsLayout ws_layout(const zha_cfg& c) {
 
 // ---------------------------------------------------------------- device helpers
 
+// Every 64-byte line of a kernel's argument block read at once, first thing: an
+// argument first read later, inside a branch, costs a memory round trip of its
+// own (~0.5 us), and the short latency-bound kernels read many such lines one
+// after another.  One scalar word per line goes into an empty asm statement,
+// which makes all the lines' loads issue together and complete before any
+// branch; the later reads of the arguments then hit the scalar cache.
+template <class T>
+__device__ inline void touch_args(const T& args) {
+  constexpr int kLines = (int)((sizeof(T) + 63) / 64);
+  static_assert(kLines <= 24, "argument block too large to touch at once");
+  const int* w = reinterpret_cast<const int*>(&args);
+  int v[24];
+#pragma unroll
+  for (int i = 0; i < 24; ++i) v[i] = i < kLines ? w[16 * i] : 0;
+  asm volatile("" ::"s"(v[0]), "s"(v[1]), "s"(v[2]), "s"(v[3]), "s"(v[4]), "s"(v[5]),
+               "s"(v[6]), "s"(v[7]), "s"(v[8]), "s"(v[9]), "s"(v[10]), "s"(v[11]));
+  asm volatile("" ::"s"(v[12]), "s"(v[13]), "s"(v[14]), "s"(v[15]), "s"(v[16]), "s"(v[17]),
+               "s"(v[18]), "s"(v[19]), "s"(v[20]), "s"(v[21]), "s"(v[22]), "s"(v[23]));
+}
+
 __device__ inline void set_status(int32_t* status, int32_t code) {
   atomicCAS(status, 0, code);
 }
