@@ -51,6 +51,7 @@ struct AttendParams {
   int32_t B, H_kv, G, C;
   int64_t T_cap;
   int32_t split_cap;
+  int32_t item_tiles;         // tiles per work item of the per-item kernels
   float qscale;               // scale * log2(e)
 };
 
@@ -103,7 +104,7 @@ __device__ inline GroupInfo group_info_from(const AttendParams& P, const GroupRa
     g.U = u;
   }
   g.tiles = (int32_t)(((int64_t)g.U * P.C + kTileKeys - 1) / kTileKeys);
-  g.items = (g.tiles + kTilesPerItem - 1) / kTilesPerItem + 1;
+  g.items = (g.tiles + P.item_tiles - 1) / P.item_tiles + 1;
   return g;
 }
 
@@ -462,7 +463,7 @@ __device__ inline void wave_state_out(WaveBuf<D, GP>& wb, int lane, float m_run,
 }
 
 template <int D, int GP, bool CONTIG>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 attend_partial_bf16(AttendParams P) {
   touch_args(P);
   static_assert(D == 64 || D == 128, "head dim");
@@ -536,9 +537,10 @@ attend_partial_bf16(AttendParams P) {
       it.nkeys = kTileKeys;
       it.smask = sink_mask_from(P, g, graw, full);
     } else {
-      it.kbase = (int64_t)li * kItemKeys;
+      const int item_keys = P.item_tiles * kTileKeys;   // <= kItemKeys
+      it.kbase = (int64_t)li * item_keys;
       const int64_t left = (int64_t)g.U * P.C - it.kbase;
-      it.nkeys = (int)(left < kItemKeys ? left : kItemKeys);
+      it.nkeys = (int)(left < item_keys ? left : item_keys);
       if (P.leaf_ids != nullptr) {
         it.first = it.kbase >> cshift;
         const int64_t last = (it.kbase + it.nkeys - 1) >> cshift;
@@ -605,11 +607,17 @@ attend_partial_bf16(AttendParams P) {
         if (more) cur = nxt;
       }
     } else {
+      // gathered rows (leaves of C < 16 keys); the same rotating buffer: chunk
+      // k+4's rows are in flight while chunk k computes
       const int nchunks = (it.nkeys + 15) / 16;
-      for (int k = wave; k < nchunks; k += kWavesPerWg) {
-        ChunkBuf<D> A;
-        load_chunk_any<D>(P, sm, g, it, k, full, kv_base, lane, A);
-        compute_chunk<D, GP>(sm.wb[wave], A, a_hi, a_lo, lane, m_run, l_run, o);
+      ChunkBuf<D> cur, nxt;
+      int k = wave;
+      if (k < nchunks) load_chunk_any<D>(P, sm, g, it, k, full, kv_base, lane, cur);
+      for (; k < nchunks; k += kWavesPerWg) {
+        const bool more = k + kWavesPerWg < nchunks;
+        if (more) load_chunk_any<D>(P, sm, g, it, k + kWavesPerWg, full, kv_base, lane, nxt);
+        compute_chunk<D, GP>(sm.wb[wave], cur, a_hi, a_lo, lane, m_run, l_run, o);
+        if (more) cur = nxt;
       }
     }
 
@@ -1002,8 +1010,8 @@ attend_partial_f32(AttendParams P) {
     int tile, t_end, t_step;
     if (tail) { tile = (wave == 0) ? -1 : 0; t_end = 0; t_step = 1; }
     else {
-      tile = li * kTilesPerItem + wave;
-      t_end = min(g.tiles, (li + 1) * kTilesPerItem);
+      tile = li * P.item_tiles + wave;
+      t_end = min(g.tiles, (li + 1) * P.item_tiles);
       t_step = kWavesPerWg;
     }
     float m[GP], l[GP], o[GP][DPL];
@@ -1292,6 +1300,7 @@ static int32_t launch_attend_call(const zha_cfg* cfg, const float* q, const zha_
   P.B = cfg->B; P.H_kv = cfg->H_kv; P.G = cfg->G; P.C = cfg->C;
   P.T_cap = cfg->T_cap;
   P.split_cap = S.split_cap;
+  P.item_tiles = item_tiles(*cfg);
   P.qscale = cfg->scale * kLog2e;
   hipStream_t s = (hipStream_t)stream;
   const int64_t max_items = (int64_t)cfg->B * cfg->H_kv * split_capacity(*cfg);

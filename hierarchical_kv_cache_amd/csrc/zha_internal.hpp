@@ -43,7 +43,8 @@ struct WsLayout {
 };
 
 constexpr int kTileKeys = 64;       // keys per attend tile
-constexpr int kTilesPerItem = 16;   // tiles per split (work item)
+constexpr int kTilesPerItem = 16;   // tiles per split (work item): 1024 keys
+constexpr int kGatherItemTiles = 4; // gathered bf16 leaves of C < 16 keys: 256-key items
 constexpr int kPartPad = 2;         // (m, l) ahead of the d outputs
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -57,6 +58,13 @@ inline int64_t level_cap(const zha_cfg& c, int l) {
   return n < 1 ? 1 : n;
 }
 
+// Tiles per work item of the per-item attend kernels.  The kernel that gathers
+// the rows of small leaves (bf16, C < 16) waits on every chunk's scattered
+// loads, so it takes shorter items: four times the workgroups in flight.
+inline int32_t item_tiles(const zha_cfg& c) {
+  return (c.kv_dtype == ZHA_BF16 && c.C < 16) ? kGatherItemTiles : kTilesPerItem;
+}
+
 // Work items (splits) per query head: tiles of the largest leaf list, plus the
 // tail item holding the open chunk and the sink.
 inline int32_t split_capacity(const zha_cfg& c) {
@@ -64,7 +72,7 @@ inline int32_t split_capacity(const zha_cfg& c) {
   int64_t dense_leaves = c.T_cap / c.C;
   if (dense_leaves > leaves) leaves = dense_leaves;
   int64_t tiles = ceil_div(leaves * c.C, kTileKeys);
-  return (int32_t)(ceil_div(tiles, kTilesPerItem) + 1);
+  return (int32_t)(ceil_div(tiles, item_tiles(c)) + 1);
 }
 
 // Partial slots per query head.  The pipelined attend folds each workgroup's
