@@ -52,6 +52,10 @@ def parse():
                     help="also measure flat (one-level) top-p and top-K routing over all leaves")
     ap.add_argument("--n-sweep", default="17,18,19",
                     help="log2 context lengths also timed routed vs dense (comma list, '' for none)")
+    ap.add_argument("--no-append-cadence", action="store_true",
+                    help="skip the in-loop append measurement (profiler runs: its extra route and "
+                         "attend calls would dilute the per-dispatch figures); the window's own "
+                         "appends then stay in value as they fell")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (known bytes) for counter calibration")
     return ap.parse_args()
@@ -286,7 +290,10 @@ def append_cadence(run, p, reps=3, iters=16):
 
 
 def window_append_us(run, cad, s0, s1):
-    """The in-loop cost of the appends that fall in steps s0..s1-1, by kind."""
+    """The in-loop cost of the appends that fall in steps s0..s1-1, by kind (none
+    taken out when the measurement was skipped)."""
+    if cad.get("skipped"):
+        return 0.0, 0
     tot, n = 0.0, 0
     for s in range(s0, s1):
         k = append_kind(run.wl, run.wl.T0 + s)
@@ -580,8 +587,13 @@ def main():
     # the append at its cadence (one per C steps, with the parents it completes),
     # measured in the loop kind by kind: a K-step window holds too few chunks to
     # sample the mixture, so the window's own appends are replaced by it
-    cad = append_cadence(run, p)
-    win_app_us, n_app = window_append_us(run, cad, W, W + K)
+    if args.no_append_cadence:
+        cad = {"by_levels_completed": {}, "us_per_append": 0.0, "us_per_step": 0.0,
+               "skipped": True}
+        win_app_us, n_app = 0.0, sum(1 for s_ in range(W, W + K) if append_kind(wl, wl.T0 + s_))
+    else:
+        cad = append_cadence(run, p)
+        win_app_us, n_app = window_append_us(run, cad, W, W + K)
     ra_us = (total_ms * 1000.0 - win_app_us) / K
     us_step = ra_us + cad["us_per_step"]
     log(f"[bench] routed p={p}: {us_step:.1f} us/step (route + attend {ra_us:.1f}, append "
@@ -822,8 +834,8 @@ def main():
                   "note": "route + attend captured once in a HIP graph and replayed per step "
                           "(query and length copied into the captured buffers each step, appends "
                           "eager); value is the eager loop"},
-        "append": {**cad, "frac_of_step": cad["us_per_step"] / us_step,
-                   "within_1pct": cad["us_per_step"] <= 0.01 * us_step,
+        "append": {**cad, "frac_of_step": None if cad.get("skipped") else cad["us_per_step"] / us_step,
+                   "within_1pct": None if cad.get("skipped") else cad["us_per_step"] <= 0.01 * us_step,
                    "note": "zha_append per completed chunk (one call every C steps), by the levels "
                            "it completes, measured inside the decode loop (difference of back-to-back "
                            "iterations with and without the append; isolated_us: the call alone "
