@@ -331,8 +331,8 @@ __device__ inline void score_node(const LevelParams& P, int gi, int node, uint32
   }
 }
 
-template <int D, int GP, bool FUSED>
-__global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
+template <int D, int GP, bool FUSED, int NT>
+__global__ void __launch_bounds__(NT) score_nodes(LevelParams P) {
   touch_args(P);
   constexpr int kPidLds = 4096;
   constexpr int kPre = 4;              // parents per thread loaded with the prologue
@@ -342,7 +342,7 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // ---- prologue: every load that does not wait on another is issued first --
   // the queries, the list's length inputs, the stale check's counts and the
-  // first kPre * 256 kept parents (the list's capacity bounds their number) --
+  // first kPre * blockDim.x kept parents (the list's capacity bounds their number) --
   // so they cost one round trip; only longer parent lists need a second.
   __shared__ __attribute__((aligned(16))) float s_q[GP > 4 ? GP * D : 4];
   float qv[GP][4];
@@ -366,7 +366,7 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
   uint32_t pre_m[kPre];
 #pragma unroll
   for (int k = 0; k < kPre; ++k) {
-    const int i = threadIdx.x + 256 * k;
+    const int i = threadIdx.x + blockDim.x * k;
     pre_id[k] = 0;
     pre_m[k] = 0u;
     if (implicit && !FUSED && i < P.list.pcap) {
@@ -444,10 +444,10 @@ __global__ void __launch_bounds__(256) score_nodes(LevelParams P) {
   if (staged && !FUSED) {
 #pragma unroll
     for (int k = 0; k < kPre; ++k) {
-      const int i = threadIdx.x + 256 * k;
+      const int i = threadIdx.x + blockDim.x * k;
       if (i < geo.np) { s_pid[i] = pre_id[k]; s_pm[i] = pre_m[k]; }
     }
-    for (int i = threadIdx.x + 256 * kPre; i < geo.np; i += blockDim.x) {
+    for (int i = threadIdx.x + blockDim.x * kPre; i < geo.np; i += blockDim.x) {
       s_pid[i] = P.list.pids[(int64_t)gi * P.list.pcap + i];
       s_pm[i] = P.list.pmask[(int64_t)gi * P.list.pcap + i];
     }
@@ -1530,6 +1530,33 @@ __global__ void __launch_bounds__(1024) level_kl(QualityParams P, const float* S
 // level with the best on every workload (deep 270 -> 195 us per route, gqa128k
 // 60 -> 53 us, long1m and rope_batch unchanged); with more, a wave scores too
 // few nodes to repay its workgroup's start.
+template <int NT>
+static void launch_score_nt(const LevelParams& P, dim3 grid, hipStream_t s) {
+  const int GP = P.G <= 4 ? 4 : (P.G <= 8 ? 8 : 16);
+  const dim3 block(NT);
+  if (P.fused) {
+    if (P.d == 128) {
+      if (GP == 4) hipLaunchKernelGGL((score_nodes<128, 4, true, NT>), grid, block, 0, s, P);
+      else if (GP == 8) hipLaunchKernelGGL((score_nodes<128, 8, true, NT>), grid, block, 0, s, P);
+      else hipLaunchKernelGGL((score_nodes<128, 16, true, NT>), grid, block, 0, s, P);
+    } else {
+      if (GP == 4) hipLaunchKernelGGL((score_nodes<64, 4, true, NT>), grid, block, 0, s, P);
+      else if (GP == 8) hipLaunchKernelGGL((score_nodes<64, 8, true, NT>), grid, block, 0, s, P);
+      else hipLaunchKernelGGL((score_nodes<64, 16, true, NT>), grid, block, 0, s, P);
+    }
+    return;
+  }
+  if (P.d == 128) {
+    if (GP == 4) hipLaunchKernelGGL((score_nodes<128, 4, false, NT>), grid, block, 0, s, P);
+    else if (GP == 8) hipLaunchKernelGGL((score_nodes<128, 8, false, NT>), grid, block, 0, s, P);
+    else hipLaunchKernelGGL((score_nodes<128, 16, false, NT>), grid, block, 0, s, P);
+  } else {
+    if (GP == 4) hipLaunchKernelGGL((score_nodes<64, 4, false, NT>), grid, block, 0, s, P);
+    else if (GP == 8) hipLaunchKernelGGL((score_nodes<64, 8, false, NT>), grid, block, 0, s, P);
+    else hipLaunchKernelGGL((score_nodes<64, 16, false, NT>), grid, block, 0, s, P);
+  }
+}
+
 static void launch_score(const LevelParams& P, int64_t ucap, hipStream_t s) {
   const int BH = P.B * P.H_kv;
   int64_t gx = ceil_div(ucap, 4);
@@ -1540,28 +1567,10 @@ static void launch_score(const LevelParams& P, int64_t ucap, hipStream_t s) {
   if (gx > lim) gx = lim;
   if (gx < 1) gx = 1;
   const dim3 grid((unsigned)gx, (unsigned)BH);
-  const int GP = P.G <= 4 ? 4 : (P.G <= 8 ? 8 : 16);
-  if (P.fused) {
-    if (P.d == 128) {
-      if (GP == 4) hipLaunchKernelGGL((score_nodes<128, 4, true>), grid, dim3(256), 0, s, P);
-      else if (GP == 8) hipLaunchKernelGGL((score_nodes<128, 8, true>), grid, dim3(256), 0, s, P);
-      else hipLaunchKernelGGL((score_nodes<128, 16, true>), grid, dim3(256), 0, s, P);
-    } else {
-      if (GP == 4) hipLaunchKernelGGL((score_nodes<64, 4, true>), grid, dim3(256), 0, s, P);
-      else if (GP == 8) hipLaunchKernelGGL((score_nodes<64, 8, true>), grid, dim3(256), 0, s, P);
-      else hipLaunchKernelGGL((score_nodes<64, 16, true>), grid, dim3(256), 0, s, P);
-    }
-    return;
-  }
-  if (P.d == 128) {
-    if (GP == 4) hipLaunchKernelGGL((score_nodes<128, 4, false>), grid, dim3(256), 0, s, P);
-    else if (GP == 8) hipLaunchKernelGGL((score_nodes<128, 8, false>), grid, dim3(256), 0, s, P);
-    else hipLaunchKernelGGL((score_nodes<128, 16, false>), grid, dim3(256), 0, s, P);
-  } else {
-    if (GP == 4) hipLaunchKernelGGL((score_nodes<64, 4, false>), grid, dim3(256), 0, s, P);
-    else if (GP == 8) hipLaunchKernelGGL((score_nodes<64, 8, false>), grid, dim3(256), 0, s, P);
-    else hipLaunchKernelGGL((score_nodes<64, 16, false>), grid, dim3(256), 0, s, P);
-  }
+  // few groups (the per-group cap leaves under 1024 workgroups): eight waves
+  // per workgroup instead of four, so the GPU holds as many waves in flight
+  if (gx * BH < 1024) launch_score_nt<512>(P, grid, s);
+  else launch_score_nt<256>(P, grid, s);
 }
 
 static void launch_upper(const UpperParams& U, hipStream_t s) {
