@@ -496,27 +496,43 @@ attend_partial_bf16(AttendParams P) {
     __syncthreads();
   }
 
-  int cur_group = -1;
   bf16x8_t a_hi[KSTEPS], a_lo[KSTEPS];
+  const int item_keys = P.item_tiles * kTileKeys;   // <= kItemKeys
+  const int span_max = (item_keys >> cshift) + 1;   // leaf entries an item can touch
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int gi = find_group(sm.item_prefix, BH, item);
     const int li = item - sm.item_prefix[gi];
+    // Every load of the item's prologue goes out before any is waited on: the
+    // group's geometry, the leaf entries the item could span (clamped to the
+    // row; the ones past the list are dropped below) and the group's queries.
     const GroupRaw graw = group_raw(P, gi);
+    const int64_t first0 = ((int64_t)li * item_keys) >> cshift;
+    const bool one_pass = span_max <= (int)blockDim.x;
+    int32_t e_id = 0;
+    uint32_t e_m = 0u;
+    if (P.leaf_ids != nullptr && one_pass && P.leaf_cap > 0) {
+      const int64_t e = min(first0 + (int64_t)threadIdx.x, (int64_t)P.leaf_cap - 1);
+      e_id = P.leaf_ids[(int64_t)gi * P.leaf_cap + e];
+      e_m = P.leaf_mask[(int64_t)gi * P.leaf_cap + e];
+    }
+    const int row = lane & 15;
+    const int kg = lane >> 4;
+    const float* qrow = P.q + ((int64_t)gi * P.G + (row < P.G ? row : P.G - 1)) * D + kg * 8;
+    float qx[KSTEPS][8];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qx[s][j] = qrow[s * 32 + j];
     const GroupInfo g = group_info_from(P, graw);
-
-    if (gi != cur_group) {
-      cur_group = gi;
-      const int row = lane & 15;
-      const int kg = lane >> 4;
+    {
+      const float f = row < P.G ? P.qscale : 0.0f;   // padding rows are zero
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         bf16x8_t hi, lo;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          float x = 0.0f;
-          if (row < P.G)
-            x = P.q[((int64_t)gi * P.G + row) * D + s * 32 + kg * 8 + j] * P.qscale;
+          const float x = qx[s][j] * f;
           const uint16_t h16 = f32_to_bf16_rne(x);
           const float r1 = x - __uint_as_float((uint32_t)h16 << 16);
           const uint16_t l16 = f32_to_bf16_rne(r1);
@@ -537,21 +553,30 @@ attend_partial_bf16(AttendParams P) {
       it.nkeys = kTileKeys;
       it.smask = sink_mask_from(P, g, graw, full);
     } else {
-      const int item_keys = P.item_tiles * kTileKeys;   // <= kItemKeys
       it.kbase = (int64_t)li * item_keys;
       const int64_t left = (int64_t)g.U * P.C - it.kbase;
       it.nkeys = (int)(left < item_keys ? left : item_keys);
       if (P.leaf_ids != nullptr) {
-        it.first = it.kbase >> cshift;
+        it.first = first0;
         const int64_t last = (it.kbase + it.nkeys - 1) >> cshift;
         const int cnt = (int)(last - it.first + 1);
-        for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
-          const int64_t off = (int64_t)gi * P.leaf_cap + it.first + i;
-          int32_t leaf = P.leaf_ids[off];
-          uint32_t m = P.leaf_mask[off] & full;
-          if (leaf < 0 || leaf >= g.n1) { leaf = 0; m = 0u; }
-          sm.lid[i] = leaf;
-          sm.lmask[i] = m;
+        if (one_pass) {
+          if ((int)threadIdx.x < cnt) {
+            int32_t leaf = e_id;
+            uint32_t m = e_m & full;
+            if (leaf < 0 || leaf >= g.n1) { leaf = 0; m = 0u; }
+            sm.lid[threadIdx.x] = leaf;
+            sm.lmask[threadIdx.x] = m;
+          }
+        } else {
+          for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
+            const int64_t off = (int64_t)gi * P.leaf_cap + it.first + i;
+            int32_t leaf = P.leaf_ids[off];
+            uint32_t m = P.leaf_mask[off] & full;
+            if (leaf < 0 || leaf >= g.n1) { leaf = 0; m = 0u; }
+            sm.lid[i] = leaf;
+            sm.lmask[i] = m;
+          }
         }
       }
     }

@@ -1567,9 +1567,11 @@ static void launch_score(const LevelParams& P, int64_t ucap, hipStream_t s) {
   if (gx > lim) gx = lim;
   if (gx < 1) gx = 1;
   const dim3 grid((unsigned)gx, (unsigned)BH);
-  // few groups (the per-group cap leaves under 1024 workgroups): eight waves
-  // per workgroup instead of four, so the GPU holds as many waves in flight
-  if (gx * BH < 1024) launch_score_nt<512>(P, grid, s);
+  // few groups (the per-group cap leaves under 1024 workgroups) and lists long
+  // enough to keep them busy: eight waves per workgroup instead of four, so the
+  // GPU holds as many waves in flight (deep's levels 3 to 1: 62 -> 48 us at
+  // level 1; its 1024-node level 4 was 1.2 us slower with them)
+  if (gx * BH < 1024 && ucap >= 2048) launch_score_nt<512>(P, grid, s);
   else launch_score_nt<256>(P, grid, s);
 }
 
