@@ -1304,9 +1304,37 @@ __global__ void __launch_bounds__(small_threads<GP>()) cut_upper(UpperParams U) 
   const LevelParams& B = U.base;
   const int gi = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The first two levels' scores of every node and head (scored whole, by
+  // node id), loaded with the length: their addresses need neither the length
+  // nor the level above's cut, so the walk reads them from LDS.
+  constexpr int kPreLv = 2;
+  constexpr int kPerT = GP * kSmallCap / NT;
+  __shared__ float s_pre[kPreLv][GP][kSmallCap];
+  float pre[kPreLv][kPerT];
+#pragma unroll
+  for (int k = 0; k < kPreLv; ++k) {
+    const bool have = k < U.nlev;   // otherwise level 0's (valid) scores are read and unused
+    const float* sb = have ? U.lv[k].scores : U.lv[0].scores;
+    const int64_t capk = have ? U.lv[k].cap : U.lv[0].cap;
+#pragma unroll
+    for (int i = 0; i < kPerT; ++i) {
+      const int idx = tid + i * NT, g = idx / kSmallCap, u = idx % kSmallCap;
+      const int gg = g < B.G ? g : B.G - 1;
+      const int64_t uu = u < capk ? u : capk - 1;
+      pre[k][i] = sb[((int64_t)gi * B.G + gg) * capk + uu];
+    }
+  }
   const bool chk = B.check_stale && wave == 0 && (gi % B.H_kv) == 0;
   const int64_t nb = stale_count(B, gi, lane, chk);   // with the length: one round trip
   int64_t T = B.list.T[gi / B.H_kv];
+#pragma unroll
+  for (int k = 0; k < kPreLv; ++k)
+#pragma unroll
+    for (int i = 0; i < kPerT; ++i) {
+      const int idx = tid + i * NT;
+      s_pre[k][idx / kSmallCap][idx % kSmallCap] = pre[k][i];
+    }
+  __syncthreads();
   stale_check(B, T, nb, lane, chk);
   if (T < 0) T = 0;
   if (T > B.list.T_cap) T = B.list.T_cap;
@@ -1336,7 +1364,10 @@ __global__ void __launch_bounds__(small_threads<GP>()) cut_upper(UpperParams U) 
         else { id = (int32_t)(orph0 + (u - np * C)); m = full; }
         s_id[u] = id;
         s_cm[u] = m;
-        for (int g = 0; g < B.G; ++g) s_sc[g][u] = lv.scores[((int64_t)gi * B.G + g) * lv.cap + id];
+        if (k < kPreLv)
+          for (int g = 0; g < B.G; ++g) s_sc[g][u] = s_pre[k][g][id];
+        else
+          for (int g = 0; g < B.G; ++g) s_sc[g][u] = lv.scores[((int64_t)gi * B.G + g) * lv.cap + id];
       }
     }
     __syncthreads();
