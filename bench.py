@@ -209,7 +209,7 @@ def append_kind(wl, T):
     return k
 
 
-def append_cadence(run, p, reps=3, iters=16):
+def append_cadence(run, p, reps=5, iters=32):
     """zha_append as a decode loop meets it: one call when a chunk completes, every
     C steps ([ZHA] page, append cadence).  An append that completes exactly the
     levels 1..k (the token count is a multiple of C^k and, below the top level,

@@ -1114,54 +1114,72 @@ attend_partial_f32(AttendParams P) {
 // log domain: the maximum of the partial maxima, then the rescaled sums.
 constexpr int kMergeInFlight = 8;
 
-// Merge of the other kernels' partials (one per work item): one workgroup of
-// kMergeItemWaves waves per query head over the head's items, waves taking
+// One query head's merge over its n partials at base, by NW waves: wave w takes
 // partials w, w+NW, ..., lanes over dims, kMergeInFlight partials in flight per
-// wave, the wave states added in a fixed order; writes out and lse.  One launch
-// (a step's launches each cost a few microseconds whatever their work; a head
-// has at most a few hundred items).  Deterministic.
-constexpr int kMergeItemWaves = 16;
-
-template <int D>
-__global__ void __launch_bounds__(64 * kMergeItemWaves) attend_merge_items(AttendParams P, float* out,
-                                                                           float* lse) {
-  touch_args(P);
+// wave, the wave states added in a fixed order; writes out and lse.
+// Deterministic.  When every partial fits one round of loads (n <= NW *
+// kMergeInFlight, the usual case) they are loaded before the maximum is known
+// and the maximum is taken over the loaded values, so the merge costs one memory
+// round trip; otherwise a first pass finds the maximum.  Either way each
+// partial is weighted by exp2(m - M) with the same M.
+template <int D, int NW>
+__device__ inline void merge_head(const float* base, int n, int head, float* out, float* lse) {
   constexpr int DPL = D / kWave;
-  constexpr int NW = kMergeItemWaves;
   constexpr int U = kMergeInFlight;
   __shared__ float red[NW];
   __shared__ float acc_o[NW][D];
   __shared__ float acc_l[NW];
-  const int head = blockIdx.x;              // b * Hq + j
-  const int gi = head / P.G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const GroupInfo g = group_info(P, gi);
-  const int n = min(g.items, P.split_cap);
-  const float* base = P.part + (int64_t)head * P.split_cap * (D + 2);
-  float M = -INFINITY;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, base[(int64_t)i * (D + 2)]);
-  M = block_max_f<NW>(M, red);
   float l = 0.0f, o[DPL];
 #pragma unroll
   for (int j = 0; j < DPL; ++j) o[j] = 0.0f;
-  if (M != -INFINITY) {
-    for (int i0 = wave; i0 < n; i0 += NW * U) {
-      float mi[U], li[U], oi[U][DPL];
+  float M;
+  if (n <= NW * U) {
+    float mi[U], li[U], oi[U][DPL];
+    float mloc = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * NW;
-        const float* pi = base + (int64_t)(i < n ? i : 0) * (D + 2);
-        mi[u] = (i < n) ? pi[0] : -INFINITY;
-        li[u] = pi[1];
+    for (int u = 0; u < U; ++u) {
+      const int i = wave + u * NW;
+      const float* pi = base + (int64_t)(i < n ? i : 0) * (D + 2);
+      mi[u] = (i < n) ? pi[0] : -INFINITY;
+      li[u] = pi[1];
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) oi[u][j] = pi[2 + lane + j * kWave];
-      }
+      for (int j = 0; j < DPL; ++j) oi[u][j] = pi[2 + lane + j * kWave];
+      mloc = fmaxf(mloc, mi[u]);
+    }
+    M = block_max_f<NW>(mloc, red);
+    if (M != -INFINITY) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const float w = exp2f(mi[u] - M);      // 0 for an empty or absent partial
         l += (w != 0.0f) ? li[u] * w : 0.0f;
 #pragma unroll
         for (int j = 0; j < DPL; ++j) o[j] += (w != 0.0f) ? oi[u][j] * w : 0.0f;
+      }
+    }
+  } else {
+    M = -INFINITY;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, base[(int64_t)i * (D + 2)]);
+    M = block_max_f<NW>(M, red);
+    if (M != -INFINITY) {
+      for (int i0 = wave; i0 < n; i0 += NW * U) {
+        float mi[U], li[U], oi[U][DPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * NW;
+          const float* pi = base + (int64_t)(i < n ? i : 0) * (D + 2);
+          mi[u] = (i < n) ? pi[0] : -INFINITY;
+          li[u] = pi[1];
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) oi[u][j] = pi[2 + lane + j * kWave];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float w = exp2f(mi[u] - M);
+          l += (w != 0.0f) ? li[u] * w : 0.0f;
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) o[j] += (w != 0.0f) ? oi[u][j] * w : 0.0f;
+        }
       }
     }
   }
@@ -1181,71 +1199,36 @@ __global__ void __launch_bounds__(64 * kMergeItemWaves) attend_merge_items(Atten
   if (threadIdx.x == 0) lse[head] = (L > 0.0f) ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
-// Merge of the pipelined kernel's partials: one workgroup per query head over
-// the head's runs (one per workgroup range that meets the group), waves taking
-// partials w, w+4, ..., lanes over dims, kMergeInFlight partials in flight per
-// wave, the four wave states added in a fixed order; writes out and lse.
-// Deterministic.
+// Merge of the per-item kernels' partials (one per work item), one workgroup
+// per query head.  One launch: a step's launches each cost a few microseconds
+// whatever their work, and a head has at most a few hundred items.
+constexpr int kMergeWaves = 16;
+
 template <int D>
-__global__ void __launch_bounds__(256) attend_merge_runs(AttendParams P, int grid, float* out,
-                                                         float* lse) {
+__global__ void __launch_bounds__(64 * kMergeWaves) attend_merge_items(AttendParams P, float* out,
+                                                                       float* lse) {
   touch_args(P);
-  constexpr int DPL = D / kWave;
-  constexpr int NW = 4;
-  constexpr int U = kMergeInFlight;
-  __shared__ float red[NW];
-  __shared__ float acc_o[NW][D];
-  __shared__ float acc_l[NW];
+  const int head = blockIdx.x;              // b * Hq + j
+  const GroupInfo g = group_info(P, head / P.G);
+  const int n = min(g.items, P.split_cap);
+  merge_head<D, kMergeWaves>(P.part + (int64_t)head * P.split_cap * (D + 2), n, head, out, lse);
+}
+
+// Merge after the pipelined kernel: one workgroup per query head over the
+// partials of the runs (workgroup ranges) that met the head's group, in run
+// order.
+template <int D>
+__global__ void __launch_bounds__(64 * kMergeWaves) attend_merge_runs(AttendParams P, int grid,
+                                                                      float* out, float* lse) {
+  touch_args(P);
   const int head = blockIdx.x;              // b * Hq + j
   const int gi = head / P.G;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int BH = P.B * P.H_kv;
   const int total = P.prefix[BH];
   const int gridp = run_grid(grid, total);
   const int n = min(run_owner(P.prefix[gi + 1] - 1, total, gridp) -
                     run_owner(P.prefix[gi], total, gridp) + 1, P.split_cap);
-  const float* base = P.part + (int64_t)head * P.split_cap * (D + 2);
-  float M = -INFINITY;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) M = fmaxf(M, base[(int64_t)i * (D + 2)]);
-  M = block_max_f<NW>(M, red);
-  float l = 0.0f, o[DPL];
-#pragma unroll
-  for (int j = 0; j < DPL; ++j) o[j] = 0.0f;
-  if (M != -INFINITY) {
-    for (int i0 = wave; i0 < n; i0 += NW * U) {
-      float mi[U], li[U], oi[U][DPL];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * NW;
-        const float* pi = base + (int64_t)(i < n ? i : 0) * (D + 2);
-        mi[u] = (i < n) ? pi[0] : -INFINITY;
-        li[u] = pi[1];
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) oi[u][j] = pi[2 + lane + j * kWave];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float w = exp2f(mi[u] - M);      // 0 for an empty or absent partial
-        l += (w != 0.0f) ? li[u] * w : 0.0f;
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) o[j] += (w != 0.0f) ? oi[u][j] * w : 0.0f;
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < DPL; ++j) acc_o[wave][lane + j * kWave] = o[j];
-  if (lane == 0) acc_l[wave] = l;
-  __syncthreads();
-  float L = 0.0f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) L += acc_l[w];
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    float Ov = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) Ov += acc_o[w][c];
-    out[(int64_t)head * D + c] = (L > 0.0f) ? Ov / L : 0.0f;
-  }
-  if (threadIdx.x == 0) lse[head] = (L > 0.0f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+  merge_head<D, kMergeWaves>(P.part + (int64_t)head * P.split_cap * (D + 2), n, head, out, lse);
 }
 
 // ---------------------------------------------------------------- host
@@ -1274,9 +1257,10 @@ static void launch_attend(const AttendParams& P, int kv_dtype, int grid, int BHq
   else if (P.G <= 8) launch_partial<D, 8>(P, kv_dtype, grid, s);
   else launch_partial<D, 16>(P, kv_dtype, grid, s);
   if (pipelined(P, kv_dtype))
-    hipLaunchKernelGGL((attend_merge_runs<D>), dim3(BHq), dim3(256), 0, s, P, grid, out, lse);
+    hipLaunchKernelGGL((attend_merge_runs<D>), dim3(BHq), dim3(64 * kMergeWaves), 0, s, P, grid,
+                       out, lse);
   else
-    hipLaunchKernelGGL((attend_merge_items<D>), dim3(BHq), dim3(64 * kMergeItemWaves), 0, s, P,
+    hipLaunchKernelGGL((attend_merge_items<D>), dim3(BHq), dim3(64 * kMergeWaves), 0, s, P,
                        out, lse);
 }
 
