@@ -425,15 +425,17 @@ __global__ void __launch_bounds__(64) build_leaves_mfma(BuildParams P) {
 // ---------------------------------------------------------------- leaves, small C
 //
 // bf16 keys, C in {2, 4, 8}, R <= 16: a leaf is too small for the matrix cores.
-// One wave per leaf; lane l holds dimensions DPL l .. DPL l + DPL - 1 of the 16
-// scaled reference queries (registers) and of the leaf's keys.  The planes go in
-// passes of PP = 32 / CP (CP = max(C, 4) keys, the padding masked): a pass's 32
+// One wave per leaf; lane l holds dimensions DPL l .. DPL l + DPL - 1 of the
+// leaf's keys (registers) and reads the same dimensions of the 16 scaled
+// reference queries from the wave's LDS.  The planes go in passes of
+// PP = 32 / CP (CP = max(C, 4) keys; a padding key repeats the last real one and
+// gets weight zero): a pass's 32
 // partial dot products are summed over the 64 lanes by a halving butterfly
 // (five rounds, then one plain exchange), which leaves lanes 2e and 2e+1 with
 // entry e = plane * CP + key of the pass; the softmax of a plane runs over the
 // lanes holding its keys; the weights pass through the wave's LDS to every lane,
-// which forms its dimensions of k_hat for every plane.  The scaled queries sit
-// in the wave's LDS (the passes index them at run time).  Same formulas as the
+// which forms its dimensions of k_hat for every plane (the passes index the
+// queries at run time, hence LDS rather than registers).  Same formulas as the
 // MFMA kernel (b_hat = F - sum_j w_j z_j); the queries are rotated in fp64 here
 // (one leaf per wave leaves no per-leaf staging to save) and then scaled.
 
@@ -849,11 +851,12 @@ __global__ void __launch_bounds__(256) build_parents(BuildParams P) {
 // A decode step completes at most one chunk, so one append builds at most one
 // node per level and tree: a leaf every C steps, a level-2 node every C^2, and
 // so on ([ZHA] "무엇과 다른가", append cadence).  This kernel does the cascade of
-// one (sequence, KV head) tree in one workgroup: its new leaves (one wave each,
-// by the same device code as the prefill kernels, so the summaries are bit for
-// bit the prefill's), then level by level the new parents' (node, plane) pairs
-// over all waves, with a workgroup barrier between levels (a parent reads
-// children this workgroup has just written).  The sequence's node counts are
+// one (sequence, KV head) tree in one workgroup: its new leaves (one wave per
+// leaf with the prefill's matrix-core code for C >= 16; for C <= 8 one wave per
+// plane, with the prefill's arithmetic in the prefill's order; either way the
+// summaries are bit for bit the prefill's), then level by level the new
+// parents' (node, plane) pairs over all waves, with a workgroup barrier between
+// levels (a parent reads children this workgroup has just written).  The sequence's node counts are
 // shared by its H_kv trees: every workgroup reads them first thing, then
 // arrives at a counter in the workspace, and the last to arrive (which returns
 // the counter to zero) writes the new counts.  It loops over however many nodes
