@@ -8,7 +8,8 @@
 // [ASM] "방법론": two attention states merge as a = (Z_A a_A + Z_B a_B)/(Z_A + Z_B).
 //
 // Work decomposition (one GPU): a "group" is one (sequence, KV head).  Its leaf
-// list is read in 16-key chunks, grouped into work items of 1024 keys; the sink
+// list is read in 16-key chunks, grouped into work items (1024 keys; 256 for
+// the kernel that gathers the rows of leaves shorter than 16 keys); the sink
 // and the open chunk form the group's tail.  The pipelined kernel (bf16, dense
 // or leaves of C >= 16 keys) gives each workgroup of a persistent grid a
 // contiguous range of the group-ordered chunks and writes one partial per
