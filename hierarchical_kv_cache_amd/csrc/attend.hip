@@ -1202,25 +1202,28 @@ __device__ inline void merge_head(const float* base, int n, int head, float* out
 
 // Merge of the per-item kernels' partials (one per work item), one workgroup
 // per query head.  One launch: a step's launches each cost a few microseconds
-// whatever their work, and a head has at most a few hundred items.
-constexpr int kMergeWaves = 16;
+// whatever their work, and a head has at most a few hundred items.  Sixteen
+// waves per head when the heads are few (the partials of a head then load in
+// one round), four when they are many (rope_batch's 512 heads: 1024-thread
+// workgroups made the launch 3 us slower).
+constexpr int kMergeHeadsMany = 256;
 
-template <int D>
-__global__ void __launch_bounds__(64 * kMergeWaves) attend_merge_items(AttendParams P, float* out,
-                                                                       float* lse) {
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW) attend_merge_items(AttendParams P, float* out,
+                                                              float* lse) {
   touch_args(P);
   const int head = blockIdx.x;              // b * Hq + j
   const GroupInfo g = group_info(P, head / P.G);
   const int n = min(g.items, P.split_cap);
-  merge_head<D, kMergeWaves>(P.part + (int64_t)head * P.split_cap * (D + 2), n, head, out, lse);
+  merge_head<D, NW>(P.part + (int64_t)head * P.split_cap * (D + 2), n, head, out, lse);
 }
 
 // Merge after the pipelined kernel: one workgroup per query head over the
 // partials of the runs (workgroup ranges) that met the head's group, in run
 // order.
-template <int D>
-__global__ void __launch_bounds__(64 * kMergeWaves) attend_merge_runs(AttendParams P, int grid,
-                                                                      float* out, float* lse) {
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW) attend_merge_runs(AttendParams P, int grid, float* out,
+                                                             float* lse) {
   touch_args(P);
   const int head = blockIdx.x;              // b * Hq + j
   const int gi = head / P.G;
@@ -1229,7 +1232,7 @@ __global__ void __launch_bounds__(64 * kMergeWaves) attend_merge_runs(AttendPara
   const int gridp = run_grid(grid, total);
   const int n = min(run_owner(P.prefix[gi + 1] - 1, total, gridp) -
                     run_owner(P.prefix[gi], total, gridp) + 1, P.split_cap);
-  merge_head<D, kMergeWaves>(P.part + (int64_t)head * P.split_cap * (D + 2), n, head, out, lse);
+  merge_head<D, NW>(P.part + (int64_t)head * P.split_cap * (D + 2), n, head, out, lse);
 }
 
 // ---------------------------------------------------------------- host
@@ -1257,12 +1260,18 @@ static void launch_attend(const AttendParams& P, int kv_dtype, int grid, int BHq
   if (P.G <= 4) launch_partial<D, 4>(P, kv_dtype, grid, s);
   else if (P.G <= 8) launch_partial<D, 8>(P, kv_dtype, grid, s);
   else launch_partial<D, 16>(P, kv_dtype, grid, s);
-  if (pipelined(P, kv_dtype))
-    hipLaunchKernelGGL((attend_merge_runs<D>), dim3(BHq), dim3(64 * kMergeWaves), 0, s, P, grid,
-                       out, lse);
-  else
-    hipLaunchKernelGGL((attend_merge_items<D>), dim3(BHq), dim3(64 * kMergeWaves), 0, s, P,
-                       out, lse);
+  const bool few = BHq < kMergeHeadsMany;
+  if (pipelined(P, kv_dtype)) {
+    if (few)
+      hipLaunchKernelGGL((attend_merge_runs<D, 16>), dim3(BHq), dim3(64 * 16), 0, s, P, grid, out, lse);
+    else
+      hipLaunchKernelGGL((attend_merge_runs<D, 4>), dim3(BHq), dim3(64 * 4), 0, s, P, grid, out, lse);
+  } else {
+    if (few)
+      hipLaunchKernelGGL((attend_merge_items<D, 16>), dim3(BHq), dim3(64 * 16), 0, s, P, out, lse);
+    else
+      hipLaunchKernelGGL((attend_merge_items<D, 4>), dim3(BHq), dim3(64 * 4), 0, s, P, out, lse);
+  }
 }
 
 // Checks of the arguments every attend call shares.

@@ -227,34 +227,35 @@ def test_attend_folded_runs_across_groups():
     assert zha.ws_status(ws) == 0
 
 
-@pytest.mark.parametrize("kvd,C,T,routed", [
-    ("bf16", 64, 300_000, False),   # dense: 512 workgroup runs in one group
-    ("bf16", 4, 40_000, True),      # gathered 4-key leaves: 157 items of 256 keys
-    ("f32", 16, 140_000, True),     # fp32 per-item kernel: 137 items of 1024 keys
+@pytest.mark.parametrize("kvd,C,T,routed,B", [
+    ("bf16", 64, 300_000, False, 1),   # dense: 512 workgroup runs in one group
+    ("bf16", 4, 40_000, True, 1),      # gathered 4-key leaves: 157 items of 256 keys
+    ("f32", 16, 140_000, True, 1),     # fp32 per-item kernel: 137 items of 1024 keys
+    ("bf16", 4, 9_000, True, 64),      # 256 heads (the four-wave merge): 36 items each
 ])
-def test_merge_of_many_partials_per_head(kvd, C, T, routed):
-    """One group holding more partials than the merge loads in one round (16
-    waves x 8): the merge first finds their maximum, then weights them.  Checked
-    against the oracle's attention over every key (the full leaf list when
-    routed)."""
+def test_merge_of_many_partials_per_head(kvd, C, T, routed, B):
+    """Heads holding more partials than the merge loads in one round (16 waves x
+    8, or 4 waves x 8 when there are 256 heads or more): the merge first finds
+    their maximum, then weights them.  Checked against the oracle's attention over
+    every key (the full leaf list when routed)."""
     dt = torch.float32 if kvd == "f32" else torch.bfloat16
     d, G = 128, 4
-    K, V = _cache(1, 1, T, d, dt, seed=C + 3, T_fill=T)
-    cfg = zha.Config(B=1, H_kv=1, G=G, d=d, C=C, L=2, R=4, T_cap=T,
+    K, V = _cache(B, 1, T, d, dt, seed=C + 3, T_fill=T)
+    cfg = zha.Config(B=B, H_kv=1, G=G, d=d, C=C, L=2, R=4, T_cap=T,
                      kv_dtype=zha.F32 if kvd == "f32" else zha.BF16)
-    q = torch.randn(1, G, d, generator=torch.Generator().manual_seed(13)).to(DEV)
-    Tt = torch.tensor([T], dtype=torch.int64, device=DEV)
+    q = torch.randn(B, G, d, generator=torch.Generator().manual_seed(13)).to(DEV)
+    Tt = torch.full((B,), T, dtype=torch.int64, device=DEV)
     ws = zha.new_workspace(cfg)
-    out = torch.empty(1, G, d, device=DEV)
-    lse = torch.empty(1, G, device=DEV)
+    out = torch.empty(B, G, d, device=DEV)
+    lse = torch.empty(B, G, device=DEV)
     if routed:
-        sets = [[np.arange(T // C)] * G]
-        ids, mask, count = lists_from_sets(sets, 1, 1, G, cfg.leaf_cap)
+        sets = [[np.arange(T // C)] * G for _ in range(B)]
+        ids, mask, count = lists_from_sets(sets, B, 1, G, cfg.leaf_cap)
         zha.attend(cfg, q, K, V, Tt, ids.to(DEV), mask.to(DEV), count.to(DEV), out, lse, ws)
     else:
         zha.dense_attend(cfg, q, K, V, Tt, out, lse, ws)
     torch.cuda.synchronize()
-    _dense_check(cfg, q, K, V, [T], out, lse, TOL[kvd])
+    _dense_check(cfg, q, K, V, [T] * B, out, lse, TOL[kvd])
     assert zha.ws_status(ws) == 0
 
 
