@@ -357,6 +357,11 @@ def timed(fn):
     return e0.elapsed_time(e1)
 
 
+def finite_or_none(x):
+    """x, or None where it is not finite (a level with no nodes): the line stays JSON."""
+    return x if math.isfinite(x) else None
+
+
 def percentile(v, q):
     """The q-quantile of a non-empty list (nearest rank)."""
     v = sorted(v)
@@ -696,7 +701,7 @@ def main():
         extra["quality_vs_dense"] = {
             "mass_recall_mean": float(recall.mean()), "mass_recall_min": float(recall.min()),
             "out_rel_err_mean": float(oerr.mean()), "out_rel_err_max": float(oerr.max()),
-            "kl_per_level_mean": [float(kls[:, l].mean()) for l in range(wl.L)],
+            "kl_per_level_mean": [finite_or_none(float(kls[:, l].mean())) for l in range(wl.L)],
             "note": "per query head and step: recall = dense softmax mass of the routed key set; "
                     "kl = KL(true || estimated) node distribution per level (1 .. L)"}
         log(f"[bench] dense-mass recall of the routed sets: mean {float(recall.mean()):.4f}, "
