@@ -67,3 +67,29 @@ extern "C" int32_t zha_ws_status(void* ws, void* stream, int32_t* status) {
   *status = host;
   return ZHA_OK;
 }
+
+// Per-level top-p of a depth schedule, computed in double and rounded once to
+// float.  The weights of the power schedule are l^-gamma normalised to sum to
+// one, so the product of the levels' p is p itself.
+extern "C" int32_t zha_p_schedule(int32_t kind, float p, int32_t L, float gamma, float* p_levels) {
+  if (p_levels == nullptr || L < 1 || L > ZHA_MAX_L) return ZHA_EINVAL;
+  if (!(p > 0.0f) || !(p <= 1.0f)) return ZHA_EINVAL;
+  const double lp = log((double)p);
+  switch (kind) {
+    case ZHA_SCHED_UNIFORM:
+      for (int l = 0; l < L; ++l) p_levels[l] = p;
+      return ZHA_OK;
+    case ZHA_SCHED_ROOT:
+      for (int l = 0; l < L; ++l) p_levels[l] = (float)exp(lp / (double)L);
+      return ZHA_OK;
+    case ZHA_SCHED_POWER: {
+      if (!isfinite(gamma)) return ZHA_EINVAL;
+      double tot = 0.0;
+      for (int l = 1; l <= L; ++l) tot += pow((double)l, -(double)gamma);
+      for (int l = 1; l <= L; ++l) p_levels[l - 1] = (float)exp(lp * pow((double)l, -(double)gamma) / tot);
+      return ZHA_OK;
+    }
+    default:
+      return ZHA_EINVAL;
+  }
+}

@@ -22,10 +22,12 @@ MAX_L = 8
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ECAPACITY, EHIP, ESTALE = range(7)
 F32, BF16 = 0, 1
 OP_BUILD, OP_ROUTE, OP_ATTEND, OP_DENSE, OP_ALL = range(5)
+SCHED = {"uniform": 0, "root": 1, "power": 2}
 
 EXPORTS = ["zha_workspace_bytes", "zha_status_str", "zha_build_level", "zha_append",
            "zha_route", "zha_route_sched", "zha_route_topk", "zha_route_quality", "zha_route_level", "zha_attend",
-           "zha_attend_static", "dense_attend", "zha_route_counts", "zha_ws_status"]
+           "zha_attend_static", "dense_attend", "zha_route_counts", "zha_ws_status",
+           "zha_p_schedule"]
 
 
 class ZhaError(RuntimeError):
@@ -73,6 +75,7 @@ def _load() -> ctypes.CDLL:
         "dense_attend": (i32, [cfgp, P, kvp, P, P, P, sz, P]),
         "zha_route_counts": (i32, [cfgp, P, P, P, P]),
         "zha_ws_status": (i32, [P, P, ctypes.POINTER(i32)]),
+        "zha_p_schedule": (i32, [i32, f32, i32, f32, ctypes.POINTER(f32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -249,23 +252,15 @@ def route_quality(cfg: Config, q, K, V, T, tree: Tree, kl, ws, stream=None):
                                   _stream(stream)), "zha_route_quality")
 
 
-def p_schedule(kind: str, p: float, L: int, gamma: float = 1.0):
-    """Per-level top-p whose product is p (entry l-1 for level l).
-
-    "uniform": p at every level (the product is then p^L).
-    "root": p^(1/L) at every level.
-    "power": p^(w_l) with w_l proportional to l^-gamma and summing to one, so the
-    lowest levels, which hold the most candidates, cut hardest.
-    """
-    if kind == "uniform":
-        return [float(p)] * L
-    if kind == "root":
-        return [float(p) ** (1.0 / L)] * L
-    if kind == "power":
-        w = [float(l) ** (-gamma) for l in range(1, L + 1)]
-        tot = sum(w)
-        return [float(p) ** (x / tot) for x in w]
-    raise ValueError(f"unknown schedule {kind!r}")
+def p_schedule(kind: str, p: float, L: int, gamma: float = 1.0) -> List[float]:
+    """Per-level top-p of a depth schedule (zha_p_schedule; entry l-1 for level
+    l): "uniform" (p at every level), "root" (p^(1/L)) or "power" (p^(w_l),
+    w_l proportional to l^-gamma and summing to one)."""
+    if kind not in SCHED:
+        raise ValueError(f"unknown schedule {kind!r}")
+    arr = (ctypes.c_float * max(1, int(L)))()
+    _check(_lib.zha_p_schedule(SCHED[kind], float(p), int(L), float(gamma), arr), "zha_p_schedule")
+    return [float(x) for x in arr[:L]]
 
 
 def route_level(cfg: Config, level: int, q, tree: Tree, p: float, cand_ids, cand_mask,

@@ -74,6 +74,10 @@ enum zha_status {
 
 enum zha_dtype { ZHA_F32 = 0, ZHA_BF16 = 1 };
 
+enum zha_sched {          /* depth schedules, see zha_p_schedule */
+  ZHA_SCHED_UNIFORM = 0, ZHA_SCHED_ROOT = 1, ZHA_SCHED_POWER = 2
+};
+
 enum zha_op {             /* workspace sizing, see zha_workspace_bytes */
   ZHA_OP_BUILD = 0, ZHA_OP_ROUTE = 1, ZHA_OP_ATTEND = 2, ZHA_OP_DENSE = 3,
   ZHA_OP_ALL = 4
@@ -188,6 +192,22 @@ int32_t zha_route_sched(const zha_cfg* cfg, const float* q, const zha_tree* tree
                         const int64_t* T, const float* p_levels,
                         int32_t* leaf_ids, uint32_t* leaf_mask, int32_t* leaf_count,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * zha_p_schedule -- the per-level top-p of a depth schedule whose levels
+ * together keep p ([ZHA] "전제와 한계" leaves open how p should scale with
+ * depth; these are the plainest candidates).  Host function: no device work.
+ *   ZHA_SCHED_UNIFORM: p at every level (the levels together keep p^L);
+ *   ZHA_SCHED_ROOT:    p^(1/L) at every level;
+ *   ZHA_SCHED_POWER:   p^(w_l) at level l, w_l = l^-gamma / sum_k k^-gamma, so the
+ *                      leaf level (l = 1, the most candidates) cuts hardest when
+ *                      gamma > 0.
+ * Writes p_levels[l-1] for level l = 1..L (caller-owned host array of L floats),
+ * each computed in double and rounded to float.  Returns ZHA_EINVAL for a null
+ * p_levels, L outside [1, ZHA_MAX_L], p outside (0, 1], an unknown kind, or a
+ * non-finite gamma (power only).
+ */
+int32_t zha_p_schedule(int32_t kind, float p, int32_t L, float gamma, float* p_levels);
 
 /*
  * zha_route_topk -- zha_route with a fixed node budget per level instead of top-p

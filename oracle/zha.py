@@ -47,7 +47,7 @@ __all__ = [
     "logsumexp", "softmax", "attention", "merge", "rope", "n_nodes",
     "node_ref_query", "leaf_summary", "parent_summary", "build_tree",
     "plane", "node_score", "topp_cut", "topk_cut", "route", "routed_keys", "attend_keys",
-    "TopP", "LevelRoute", "Route", "fp32", "node_logmass", "level_kl",
+    "TopP", "LevelRoute", "Route", "fp32", "node_logmass", "level_kl", "p_schedule",
 ]
 
 
@@ -316,6 +316,29 @@ def topk_cut(ids: Sequence[int], scores: Sequence[float], k: int) -> TopP:
     w = np.exp(s - s[order[0]])
     m = min(int(k), n)
     return TopP(ids, s, order, w, float(np.sum(w)), float(m), m, np.sort(ids[order[:m]]))
+
+
+def p_schedule(kind: str, p: float, L: int, gamma: float = 1.0):
+    """Per-level top-p for levels 1..L (entry l-1 for level l), in float64.
+
+    [ZHA] "전제와 한계" leaves open how the cut should scale with depth; a route
+    keeps at most the product of its levels' p of the estimated mass.  The
+    schedules are the plain candidates for that product:
+      uniform  p at every level (product p**L);
+      root     p**(1/L) at every level (product p);
+      power    p**w_l with w_l = l**-gamma / sum_k k**-gamma (product p), so with
+               gamma > 0 the leaf level, which holds the most candidates, keeps
+               the smallest share.
+    """
+    p = float(p)
+    if kind == "uniform":
+        return [p] * L
+    if kind == "root":
+        return [p ** (1.0 / L)] * L
+    if kind == "power":
+        w = np.array([float(l) ** (-float(gamma)) for l in range(1, L + 1)])
+        return [p ** float(x) for x in w / w.sum()]
+    raise ValueError(f"unknown schedule {kind!r}")
 
 
 def route(q, tree, T: int, C: int, L: int, p, scale: float,

@@ -8,7 +8,10 @@ import shutil
 import subprocess
 import sys
 
+import numpy as np
 import pytest
+
+import oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "zha.h")
@@ -113,10 +116,36 @@ def test_p_schedules_multiply_to_p():
         for kind in ("root", "power"):
             pl = zha.p_schedule(kind, 0.8, L, gamma=1.5)
             assert len(pl) == L and all(0 < x <= 1 for x in pl)
-            assert abs(math.prod(pl) - 0.8) < 1e-12
-        assert zha.p_schedule("uniform", 0.8, L) == [0.8] * L
+            assert abs(math.prod(pl) - 0.8) < 1e-6   # each level rounded to float
+        assert zha.p_schedule("uniform", 0.8, L) == [float(np.float32(0.8))] * L
     pw = zha.p_schedule("power", 0.8, 4, gamma=1.0)
     assert pw == sorted(pw)   # the leaf level cuts hardest
+
+
+@pytest.mark.parametrize("kind", ["uniform", "root", "power"])
+def test_p_schedule_matches_the_oracle(kind):
+    """zha_p_schedule (host code of the library) against the oracle's float64
+    schedule, each level within one float32 step of it."""
+    for p in (0.5, 0.75, 0.8, 0.9, 0.99, 1.0):
+        pf = float(np.float32(p))
+        for L in range(1, zha.MAX_L + 1):
+            for gamma in (0.0, 0.5, 1.5, 3.0):
+                got = np.array(zha.p_schedule(kind, pf, L, gamma=gamma))
+                ref = np.array(O.p_schedule(kind, pf, L, gamma))
+                ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
+                assert np.all(np.abs(got - ref) <= ulp), (kind, p, L, gamma, got, ref)
+
+
+def test_p_schedule_rejects_bad_arguments():
+    lib = zha._lib
+    out = (ctypes.c_float * 8)()
+    for kind, p, L, gamma in [(0, 0.9, 0, 1.0), (0, 0.9, zha.MAX_L + 1, 1.0), (1, 0.0, 3, 1.0),
+                              (1, 1.5, 3, 1.0), (1, float("nan"), 3, 1.0), (7, 0.9, 3, 1.0),
+                              (2, 0.9, 3, float("inf")), (2, 0.9, 3, float("nan"))]:
+        assert lib.zha_p_schedule(kind, p, L, gamma, out) == zha.EINVAL, (kind, p, L, gamma)
+    assert lib.zha_p_schedule(0, 0.9, 3, 1.0, None) == zha.EINVAL
+    with pytest.raises(ValueError):
+        zha.p_schedule("cubic", 0.9, 3)
 
 
 def test_cut_pool_beyond_fixed_point_range_is_rejected():

@@ -592,3 +592,29 @@ def test_node_score_is_the_best_plane():
             strict += int(max(others) < F - 1e-6)
     # the test has teeth: the other planes are strictly below F at most tangent points
     assert strict > lv["khat"].shape[0]
+
+
+# ---------------------------------------------------------------- depth schedules
+
+def test_p_schedule_closed_forms():
+    """[ZHA] "전제와 한계": a route keeps at most the product of its levels' p.
+    root and power keep p in all (their weights sum to one); power's level l
+    takes the share l^-gamma of the first level's log p (a flipped exponent, an
+    unnormalised weight or a level taken in reverse fails); gamma = 0 reduces
+    power to root; a one-level tree is the flat cut at p."""
+    for p in (0.5, 0.8, 0.9):
+        for L in (1, 2, 3, 6, 8):
+            assert O.p_schedule("uniform", p, L) == [p] * L
+            root = O.p_schedule("root", p, L)
+            assert abs(np.prod(root) - p) < 1e-14 and np.allclose(root, root[0], rtol=0, atol=0)
+            for gamma in (0.5, 1.0, 1.5, 3.0):
+                pw = O.p_schedule("power", p, L, gamma)
+                assert abs(np.prod(pw) - p) < 1e-14
+                ratio = np.log(pw) / np.log(pw[0])
+                np.testing.assert_allclose(ratio, np.arange(1, L + 1) ** -gamma, rtol=1e-12)
+                assert pw == sorted(pw)   # the leaf level (l = 1) keeps the least
+            np.testing.assert_allclose(O.p_schedule("power", p, L, 0.0), root, rtol=1e-15)
+            if L == 1:
+                assert O.p_schedule("power", p, 1, 1.5) == [p] and root == [p]
+    with pytest.raises(ValueError):
+        O.p_schedule("cubic", 0.9, 3)
