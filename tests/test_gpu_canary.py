@@ -1,0 +1,141 @@
+"""Every output buffer the library writes sits between canary margins, and no
+call writes past its buffer's bounds.
+
+The tree levels, node counts, leaf lists, outputs, KL array and the workspace
+are views into larger device buffers whose margins hold a fixed bit pattern
+(a NaN payload for 32-bit words, 0xA5 for workspace bytes).  Each call of the
+decode path -- prefill build, the append that completes C new tokens, route
+(one p, a depth schedule, a node budget), the routing-quality forward, the
+sparse attend with a workspace and with the static scratch, and the dense
+attend -- runs on ragged batches over several geometries, and every margin must
+still hold its pattern afterwards.
+"""
+import math
+
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+zha = pytest.importorskip("hierarchical_kv_cache_amd.zha")
+DEV = "cuda"
+PAD = 4096                       # canary words on each side of a buffer
+WORD = 0x7FBADBAD                # a NaN payload no kernel produces
+BYTE = 0xA5
+
+
+class Guarded:
+    """Padded device buffers handed out as contiguous views; check() verifies
+    that every margin still holds its pattern."""
+
+    def __init__(self):
+        self.bufs = []
+
+    def tensor(self, shape, dtype):
+        n = math.prod(shape)
+        if dtype in (torch.float32, torch.int32):
+            raw = torch.full((PAD + n + PAD,), WORD, dtype=torch.int32, device=DEV)
+            mid = raw[PAD:PAD + n]
+            view = mid.view(dtype) if dtype == torch.float32 else mid
+        elif dtype == torch.int64:
+            raw = torch.full((PAD + n + PAD,), (WORD << 32) | WORD, dtype=torch.int64, device=DEV)
+            view = raw[PAD:PAD + n]
+        else:
+            raise TypeError(dtype)
+        self.bufs.append((raw, n, f"{tuple(shape)} {dtype}"))
+        return view.view(shape)
+
+    def workspace(self, nbytes):
+        front = 256 * 16                                 # keeps the 256-byte alignment
+        raw = torch.full((front + nbytes + front,), BYTE, dtype=torch.uint8, device=DEV)
+        ws = raw[front:front + nbytes]
+        ws.zero_()
+        assert ws.data_ptr() % 256 == 0
+        self.bufs.append((raw, None, f"workspace {nbytes} B"))
+        self.ws_front = front
+        return ws
+
+    def check(self, where):
+        torch.cuda.synchronize()
+        for raw, n, name in self.bufs:
+            if n is None:
+                nb = raw.numel() - 2 * self.ws_front
+                margins = torch.cat([raw[:self.ws_front], raw[self.ws_front + nb:]])
+                bad = int((margins != BYTE).sum())
+            else:
+                margins = torch.cat([raw[:PAD], raw[PAD + n:]])
+                pat = WORD if raw.dtype == torch.int32 else (WORD << 32) | WORD
+                bad = int((margins != pat).sum())
+            assert bad == 0, f"{where}: {bad} margin words of {name} overwritten"
+
+
+CASES = {
+    # name: (workload, overrides, T per sequence before the append)
+    "bf16_c16": ("gqa128k", dict(B=3, H_kv=2, G=4, C=16, L=3, n_clusters=64), [5003, 2000, 9]),
+    "bf16_c64": ("gqa128k", dict(B=2, H_kv=2, G=4, C=64, L=2, n_clusters=64), [9000, 130]),
+    "bf16_c4_d64": ("deep", dict(B=2, H_kv=2, G=8, d=64, C=4, L=4), [3001, 700]),
+    "f32_g3": ("tiny", dict(B=2, H_kv=2, G=3, C=16, L=2, R=4), [4100, 37]),
+    "rope_c32": ("rope_batch", dict(B=2, H_kv=2, G=8, C=32, L=2, n_clusters=64), [6000, 1100]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_no_write_outside_any_output(case):
+    name, over, T0 = CASES[case]
+    wl = synth.WORKLOADS[name].with_(**over)
+    C = wl.C
+    T1 = [t + C for t in T0]                     # after the append: C more tokens each
+    T_cap = max(T1) + C
+    K, V = synth.make_cache(wl.with_(N=T_cap, open_len=0, steps=0), DEV, T_cap)
+    qref = synth.make_qref(wl, DEV)
+    cfg = zha.Config(B=wl.B, H_kv=wl.H_kv, G=wl.G, d=wl.d, C=C, L=wl.L, R=wl.R, T_cap=T_cap,
+                     kv_dtype=zha.F32 if wl.kv_dtype == "f32" else zha.BF16,
+                     rope=wl.rope, rope_base=wl.rope_base)
+    g = Guarded()
+    tree = zha.Tree.__new__(zha.Tree)
+    tree.cfg = cfg
+    tree.khat = [g.tensor((cfg.B, cfg.H_kv, cfg.level_cap(l), cfg.R, cfg.d), torch.float32)
+                 for l in range(1, cfg.L + 1)]
+    tree.bhat = [g.tensor((cfg.B, cfg.H_kv, cfg.level_cap(l), cfg.R), torch.float32)
+                 for l in range(1, cfg.L + 1)]
+    tree.n_built = g.tensor((cfg.L, cfg.B), torch.int64)
+    tree.n_built.zero_()
+    ws = g.workspace(zha.workspace_bytes(cfg))
+    ids = g.tensor((cfg.B, cfg.H_kv, cfg.leaf_cap), torch.int32)
+    mask = g.tensor((cfg.B, cfg.H_kv, cfg.leaf_cap), torch.int32)
+    count = g.tensor((cfg.B, cfg.H_kv), torch.int32)
+    out = g.tensor((cfg.B, cfg.Hq, cfg.d), torch.float32)
+    lse = g.tensor((cfg.B, cfg.Hq), torch.float32)
+    out_s = g.tensor((cfg.B, cfg.Hq, cfg.d), torch.float32)
+    lse_s = g.tensor((cfg.B, cfg.Hq), torch.float32)
+    status = g.tensor((1,), torch.int32)
+    status.zero_()
+    kl = g.tensor((cfg.L, cfg.B, cfg.Hq), torch.float32)
+
+    T = torch.tensor(T0, dtype=torch.int64, device=DEV)
+    zha.build(cfg, K, V, T, qref, tree, ws)
+    g.check("build")
+    T.copy_(torch.tensor(T1, dtype=torch.int64))
+    zha.append(cfg, K, V, T, qref, tree, ws, max_new_tokens=C)
+    g.check("append")
+    assert tree.n_built[0].tolist() == [t // C for t in T1]
+    q = synth.make_query(wl, 0, max(T1), DEV)
+    for p in (0.9, 1.0):
+        zha.route(cfg, q, tree, T, p, ids, mask, count, ws)
+        g.check(f"route p={p}")
+        zha.attend(cfg, q, K, V, T, ids, mask, count, out, lse, ws)
+        g.check(f"attend p={p}")
+        zha.attend_static(cfg, q, K, V, T, ids, mask, count, out_s, lse_s, status=status)
+        g.check(f"attend_static p={p}")
+        assert torch.equal(out, out_s) and torch.equal(lse, lse_s)
+    zha.route(cfg, q, tree, T, zha.p_schedule("power", 0.9, cfg.L, gamma=1.5), ids, mask, count, ws)
+    g.check("route_sched")
+    zha.route_topk(cfg, q, tree, T, 3, ids, mask, count, ws)
+    g.check("route_topk")
+    zha.route_quality(cfg, q, K, V, T, tree, kl, ws)
+    g.check("route_quality")
+    zha.dense_attend(cfg, q, K, V, T, out, lse, ws)
+    g.check("dense_attend")
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    assert zha.ws_status(ws) == 0 and int(status[0]) == 0
