@@ -56,6 +56,8 @@ def parse():
                     help="skip the in-loop append measurement (profiler runs: its extra route and "
                          "attend calls would dilute the per-dispatch figures); the window's own "
                          "appends then stay in value as they fell")
+    ap.add_argument("--no-bf16-copy", action="store_true",
+                    help="skip the measurement of routing from bf16 copies of the summaries")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (known bytes) for counter calibration")
     return ap.parse_args()
@@ -451,6 +453,51 @@ def schedule_report(run, W, K, pl):
     }
 
 
+def bf16_copy_report(run, W, K, p):
+    """The same steps with the route scoring from a bf16 copy of every level's
+    k_hat (zha_tree.khat16, written by the builder beside the fp32 tree): step
+    time (raw window, its appends included), route time, summary bytes the route
+    reads, and the dense-mass recall of the routed sets.  The tree goes back to
+    fp32 routing afterwards."""
+    zha, wl, tree = run.zha, run.wl, run.dec.tree
+    tree.khat16 = [torch.zeros(k.shape, dtype=torch.bfloat16, device=k.device) for k in tree.khat]
+    try:
+        run.prefill()
+        run.routed_steps(0, W, p)
+        ms = timed(lambda: run.routed_steps(W, W + K, p))
+        run.prefill()
+        run.routed_steps(0, W, p)
+        ev = {"route": [], "attend": [], "append": []}
+        recs, keep = [], [zha.LeafList(run.cfg) for _ in range(K)]
+        run.routed_steps(W, W + K, p, ev, counts=recs, keep=keep)
+        torch.cuda.synchronize()
+        route_us = 1000.0 * sum(a.elapsed_time(b) for a, b in ev["route"]) / K
+        node_bytes = wl.R * wl.d * 2 + wl.R * 4          # bf16 k_hat rows + fp32 b_hat
+        scored = sum(float(rec[1].to(torch.float64).sum()) for rec in recs) / K
+        recall = []
+        o_r, l_r = torch.empty_like(run.dec.out), torch.empty_like(run.dec.lse)
+        for i, lst in enumerate(keep):
+            s = W + i
+            zha.attend(run.cfg, run.Q[s], run.K, run.V, run.Ts[s], lst.ids, lst.mask, lst.count,
+                       o_r, l_r, run.dec.ws)
+            zha.dense_attend(run.cfg, run.Q[s], run.K, run.V, run.Ts[s], run.dec.out, run.dec.lse,
+                             run.dec.ws)
+            recall.append(torch.exp(l_r - run.dec.lse).flatten())
+        recall = torch.cat(recall).double().cpu()
+    finally:
+        tree.khat16 = [None] * wl.L
+        torch.cuda.empty_cache()
+    return {
+        "us_per_step": ms * 1000.0 / K, "route_us": route_us,
+        "route_summary_GB_per_step": scored * node_bytes / 1e9,
+        "route_GBps": scored * node_bytes / (route_us * 1e-6) / 1e9,
+        "mass_recall_mean": float(recall.mean()), "mass_recall_min": float(recall.min()),
+        "note": "route scoring from bf16 copies of k_hat (b_hat and all arithmetic fp32); raw "
+                "window over the same steps, its appends included; the headline value uses the "
+                "fp32 summaries",
+    }
+
+
 def flat_report(run, W, K, mode, p, budget):
     """Flat routing over every leaf (a one-level view of the same leaf summaries):
     top-p at p, or a fixed budget of leaves per head.  Step time, route time,
@@ -742,6 +789,14 @@ def main():
         "avg_launch_us": attend_us if dominant == "attend" else route_us,
         "algorithmic_bytes_per_launch": alg,
     }
+
+    # ---- the route scoring from bf16 copies of k_hat (same steps, same p)
+    if not args.no_bf16_copy:
+        r16 = bf16_copy_report(run, W, K, p)
+        extra["route_bf16_copy"] = r16
+        log(f"[bench] route from bf16 k_hat copies: {r16['us_per_step']:.1f} us/step "
+            f"(route {r16['route_us']:.1f} us, {r16['route_summary_GB_per_step']:.3f} GB), "
+            f"recall {r16['mass_recall_mean']:.4f}")
 
     # ---- depth schedules of p (same product p = the headline p for root/power)
     kinds = [x.strip() for x in args.schedules.split(",") if x.strip()]

@@ -34,6 +34,7 @@ struct BuildParams {
   const float* qref;          // [H_kv][R][d]
   float* khat;                // level l:   [BH][ncap][R][d]
   float* bhat;                //            [BH][ncap][R]
+  uint16_t* khat16;           //            bf16 copy of khat, or null
   const float* khat_ch;       // level l-1: [BH][ncap_ch][R][d]
   const float* bhat_ch;
   int64_t ncap, ncap_ch;
@@ -42,6 +43,22 @@ struct BuildParams {
   float scale, rope_base;
   int64_t T_cap, span;        // span = C^level
 };
+
+// The bf16 copy of k_hat that routing may read (zha_tree.khat16): each value
+// rounded to nearest even (the summaries are finite).
+__device__ inline uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ inline void store_bf16x4(uint16_t* p, float a, float b, float c, float d) {
+  uint2 v;
+  v.x = bf16_bits(a) | (bf16_bits(b) << 16);
+  v.y = bf16_bits(c) | (bf16_bits(d) << 16);
+  *(uint2*)p = v;
+}
+__device__ inline void store_bf16x2(uint16_t* p, float a, float b) {
+  *(uint32_t*)p = bf16_bits(a) | (bf16_bits(b) << 16);
+}
 
 // The R reference queries of a node whose first key is at position pos, rotated
 // when P.rope, into qh[r][d] (row stride ld).
@@ -144,11 +161,13 @@ __device__ inline void generic_leaf(const BuildParams& P, BuildSmem& sm, int gi,
   __syncthreads();
   // k_hat[r][c] = sum_j w[r][j] k[j][c]
   float* kh = P.khat + (((int64_t)gi * P.ncap + n) * R) * d;
+  uint16_t* kh16 = P.khat16 ? P.khat16 + (((int64_t)gi * P.ncap + n) * R) * d : nullptr;
   for (int idx = threadIdx.x; idx < R * d; idx += kGenericThreads) {
     const int r = idx / d, c = idx % d;
     float acc = 0.0f;
     for (int j = 0; j < C; ++j) acc += sm.w[r][j] * sm.k[j][c];
     kh[idx] = acc;
+    if (kh16) kh16[idx] = (uint16_t)bf16_bits(acc);
   }
   if (threadIdx.x < R)
     P.bhat[((int64_t)gi * P.ncap + n) * R + threadIdx.x] = sm.F[threadIdx.x] - sm.wz[threadIdx.x];
@@ -373,7 +392,12 @@ struct MfmaLeaf {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, wb[1][s], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, wb[2][s], acc, 0, 0, 0);
       }
-      if (row < R) *(float4*)(kh + (int64_t)row * D + 16 * td + 4 * kg) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      if (row < R) {
+        *(float4*)(kh + (int64_t)row * D + 16 * td + 4 * kg) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        if (P.khat16)
+          store_bf16x4(P.khat16 + ((int64_t)gi * P.ncap + n) * R * D + (int64_t)row * D + 16 * td + 4 * kg,
+                       acc[0], acc[1], acc[2], acc[3]);
+      }
     }
     wave_lds_sync();                       // K^T and W are reused by the next leaf
   }
@@ -614,6 +638,11 @@ struct SmallLeaf {
         }
         if constexpr (DPL == 2) *(float2*)(kh + (int64_t)rr * D) = make_float2(acc[0], acc[1]);
         else kh[(int64_t)rr * D] = acc[0];
+        if (P.khat16) {
+          uint16_t* kh16 = P.khat16 + ((int64_t)gi * P.ncap + n) * R * D + d0 + (int64_t)rr * D;
+          if constexpr (DPL == 2) store_bf16x2(kh16, acc[0], acc[1]);
+          else kh16[0] = (uint16_t)bf16_bits(acc[0]);
+        }
       }
     }
     wave_lds_sync();                       // the weights are rewritten by the next leaf
@@ -690,6 +719,11 @@ struct SmallLeaf {
     float* kh = P.khat + (((int64_t)gi * P.ncap + n) * R + r) * D + d0;
     if constexpr (DPL == 2) *(float2*)kh = make_float2(acc[0], acc[1]);
     else kh[0] = acc[0];
+    if (P.khat16) {
+      uint16_t* kh16 = P.khat16 + (((int64_t)gi * P.ncap + n) * R + r) * D + d0;
+      if constexpr (DPL == 2) store_bf16x2(kh16, acc[0], acc[1]);
+      else kh16[0] = (uint16_t)bf16_bits(acc[0]);
+    }
   }
 };
 
@@ -822,9 +856,12 @@ __device__ inline void parent_pair(const BuildParams& P, int gi, int h, int64_t 
   if (cg == 0) {
     float* kh = P.khat + (((int64_t)gi * P.ncap + n) * R + r) * D + ds;
 #pragma unroll
-    for (int q = 0; q < NV; ++q)
-      *(float4*)(kh + 4 * q) = make_float4(ka[4 * q] / S, ka[4 * q + 1] / S,
-                                           ka[4 * q + 2] / S, ka[4 * q + 3] / S);
+    for (int q = 0; q < NV; ++q) {
+      const float4 v = make_float4(ka[4 * q] / S, ka[4 * q + 1] / S, ka[4 * q + 2] / S, ka[4 * q + 3] / S);
+      *(float4*)(kh + 4 * q) = v;
+      if (P.khat16)
+        store_bf16x4(P.khat16 + (((int64_t)gi * P.ncap + n) * R + r) * D + ds + 4 * q, v.x, v.y, v.z, v.w);
+    }
   }
   // b_hat = F - sum_j w_j z_j with F = M + log S and z_j = scale q.k_hat_{r,j}
   if (lane == 0) P.bhat[((int64_t)gi * P.ncap + n) * R + r] = (M + logf(S)) - SW / S;
@@ -1061,6 +1098,7 @@ static BuildParams make_params(const zha_cfg* cfg, const zha_kv* kv, const float
   BuildParams P;
   P.K = kv->K; P.T = kv->T; P.qref = qref;
   P.khat = tree->khat[level - 1]; P.bhat = tree->bhat[level - 1];
+  P.khat16 = tree->khat16[level - 1];
   P.ncap = tree->n_cap[level - 1];
   P.khat_ch = level > 1 ? tree->khat[level - 2] : nullptr;
   P.bhat_ch = level > 1 ? tree->bhat[level - 2] : nullptr;

@@ -156,6 +156,7 @@ struct LevelParams {
   const float* q;              // [BHq][d]
   const float* khat;           // [BH][ncap][R][d]
   const float* bhat;           // [BH][ncap][R]
+  const uint16_t* khat16;      // [BH][ncap][R][d] bf16 copy of khat, read instead when set
   int64_t ncap;
   ListRef list;                // this level's candidate union list
   int32_t* ucount_out;         // [BH] list length (diagnostics), or null
@@ -210,14 +211,16 @@ __device__ inline int clamp_count(int32_t u, int64_t cap) {
 
 // ---------------------------------------------------------------- scoring (A3)
 //
-// One wave scores one node: the node's R x d summary (8 KiB at R=16, d=128) is
-// read as 1 KiB contiguous rows per load instruction, with the non-temporal hint
-// (summaries are streamed once per step; keeping them out of the caches measured
-// ~10% faster).  Lane l holds rows
-// r = RPI*s + l/LPR (s < NS) at dims (l%LPR)*4..+4 and the group's G query heads
-// at the same dims.  The NS x GP partial dots are summed over the LPR lanes of a
-// row by a transposing butterfly (each round halves the values a lane keeps),
-// leaving GP/4 full dots per lane; the max over planes is a second butterfly.
+// One wave scores one node: the node's R x d summary (8 KiB at R=16, d=128 in
+// fp32; half that from a bf16 copy) is read as 1 KiB contiguous rows per load
+// instruction (16 bytes per lane), with the non-temporal hint (summaries are
+// streamed once per step; keeping them out of the caches measured ~10% faster).
+// A lane holds EPL values of a row (4 fp32, or 8 bf16 widened to fp32): lane l
+// holds rows r = RPI*s + l/LPR (s < NS) at dims (l%LPR)*EPL..+EPL and the
+// group's G query heads at the same dims.  The NS x GP partial dots are summed
+// over the LPR lanes of a row by a transposing butterfly (each round halves the
+// values a lane keeps), leaving GP/4 full dots per lane; the max over planes is
+// a second butterfly.
 
 template <int DELTA>
 __device__ inline float xor_lane(float v) {
@@ -238,54 +241,74 @@ __device__ inline void tr_round(float* a, int lane) {
 }
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4s_t __attribute__((ext_vector_type(4)));
 
-// The group's G queries, zero-padded to GP: at this lane's dims (t = lane %
-// (D/4)) in registers when GP == 4, else into the workgroup's LDS copy qlds
-// ([GP][D]; the caller synchronises the workgroup before it is read).
-template <int D, int GP>
+// k_hat values per lane and load: 16 bytes of fp32 or of the bf16 copy.
+template <bool H16>
+constexpr int epl() { return H16 ? 8 : 4; }
+
+// The group's G queries, zero-padded to GP: at this lane's EPL dims (t = lane %
+// (D/EPL)) in registers when the scorer keeps them there, else into the
+// workgroup's LDS copy qlds ([GP][D]; the caller synchronises the workgroup
+// before it is read).
+template <int D, int GP, int EPL, bool QLDS>
 __device__ inline void load_group_queries(const LevelParams& P, int gi, int lane,
-                                          float (&qv)[GP][4], float* qlds) {
-  if constexpr (GP > 4) {
+                                          float (&qv)[GP][EPL], float* qlds) {
+  if constexpr (QLDS) {
     for (int i = threadIdx.x; i < GP * D; i += blockDim.x)
       qlds[i] = (i / D < P.G) ? P.q[(int64_t)gi * P.G * D + i] : 0.0f;
   } else {
-    const int t = lane % (D / 4);
+    const int t = lane % (D / EPL);
 #pragma unroll
     for (int g = 0; g < GP; ++g)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        qv[g][j] = (g < P.G) ? P.q[((int64_t)gi * P.G + g) * D + t * 4 + j] : 0.0f;
+      for (int j = 0; j < EPL; ++j)
+        qv[g][j] = (g < P.G) ? P.q[((int64_t)gi * P.G + g) * D + t * EPL + j] : 0.0f;
   }
 }
 
-// One wave scores list entry u (tree node `node`) of group gi for all G heads.
-// A head outside the entry's mask gets -inf (not its candidate); a candidate's
-// non-finite score is stored as -FLT_MAX, so -inf marks exactly the
-// non-candidates for the cut.
-template <int D, int GP>
+// One wave scores list entry u (tree node `node`) of group gi for all G heads,
+// from the fp32 k_hat or (H16) its bf16 copy.  A head outside the entry's mask
+// gets -inf (not its candidate); a candidate's non-finite score is stored as
+// -FLT_MAX, so -inf marks exactly the non-candidates for the cut.  QLDS: the
+// queries come from the workgroup's LDS copy instead of registers.
+template <int D, int GP, bool H16, bool QLDS>
 __device__ inline void score_node(const LevelParams& P, int gi, int node, uint32_t mask, int u,
-                                  const float (&qv)[GP][4], const float* qlds, int lane) {
-  constexpr int LPR = D / 4;           // lanes per summary row
+                                  const float (&qv)[GP][epl<H16>()], const float* qlds, int lane) {
+  constexpr int EPL = epl<H16>();
+  constexpr int LPR = D / EPL;         // lanes per summary row
   constexpr int RPI = kWave / LPR;     // rows per load instruction
   constexpr int NS = 16 / RPI;         // load instructions per node (R padded to 16)
   constexpr int V0 = NS * 4;           // partial dots per lane and quad of heads
-  static_assert(V0 / LPR == 1, "butterfly shape");
+  static_assert(V0 == LPR, "butterfly shape");
   const int t = lane % LPR;
   if (node < 0 || node >= P.ncap) {   // not a node of this tree: never selected
     if (lane < P.G) P.scores[((int64_t)gi * P.G + lane) * P.ucap + u] = -INFINITY;
     if (lane == 0) set_status(P.status, ZHA_EINVAL);
     return;
   }
-  const float* base = P.khat + ((int64_t)gi * P.ncap + node) * P.R * D;
+  const int64_t row0 = ((int64_t)gi * P.ncap + node) * P.R;
   // after the butterfly this lane holds row r = RPI*(t/4) + lane/LPR
   const int r_out = RPI * (t / 4) + lane / LPR;
-  const float bh = (r_out < P.R) ? P.bhat[((int64_t)gi * P.ncap + node) * P.R + r_out] : 0.0f;
-  f32x4_t k4[NS];
+  const float bh = (r_out < P.R) ? P.bhat[row0 + r_out] : 0.0f;
+  float k[NS][EPL];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int r = RPI * s + lane / LPR;
-    k4[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (r < P.R) k4[s] = __builtin_nontemporal_load((const f32x4_t*)(base + r * D + t * 4));
+    if constexpr (H16) {
+      u32x4s_t v = u32x4s_t{0u, 0u, 0u, 0u};
+      if (r < P.R) v = __builtin_nontemporal_load((const u32x4s_t*)(P.khat16 + (row0 + r) * D + t * EPL));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {       // bf16 -> fp32 is exact: the bits move up
+        k[s][2 * j] = __uint_as_float(v[j] << 16);
+        k[s][2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+      }
+    } else {
+      f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (r < P.R) v = __builtin_nontemporal_load((const f32x4_t*)(P.khat + (row0 + r) * D + t * EPL));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) k[s][j] = v[j];
+    }
   }
   // The heads go four at a time over the summary held in registers; the
   // scheduling barrier keeps one quad's partial dots live at a time.  With more
@@ -294,24 +317,31 @@ __device__ inline void score_node(const LevelParams& P, int gi, int node, uint32
 #pragma unroll
   for (int hq = 0; hq < GP / 4; ++hq) {
     if (hq > 0) __builtin_amdgcn_sched_barrier(0);
-    float q[4][4];
+    float q[4][EPL];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      if constexpr (GP > 4) {
-        const f32x4_t x = *(const f32x4_t*)(qlds + (4 * hq + g) * D + t * 4);
+      if constexpr (QLDS) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) q[g][j] = x[j];
+        for (int j4 = 0; j4 < EPL / 4; ++j4) {
+          const f32x4_t x = *(const f32x4_t*)(qlds + (4 * hq + g) * D + t * EPL + 4 * j4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) q[g][4 * j4 + j] = x[j];
+        }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) q[g][j] = qv[4 * hq + g][j];
+        for (int j = 0; j < EPL; ++j) q[g][j] = qv[4 * hq + g][j];
       }
     }
     float a[V0];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        a[s * 4 + g] = q[g][0] * k4[s][0] + q[g][1] * k4[s][1] + q[g][2] * k4[s][2] + q[g][3] * k4[s][3];
+      for (int g = 0; g < 4; ++g) {
+        float acc = q[g][0] * k[s][0];
+#pragma unroll
+        for (int j = 1; j < EPL; ++j) acc = fmaf(q[g][j], k[s][j], acc);
+        a[s * 4 + g] = acc;
+      }
     // butterfly over the LPR lanes of a row: deltas LPR/2 .. 1
     if constexpr (LPR == 32) tr_round<V0, 16>(a, lane);
     if constexpr (LPR >= 16) tr_round<V0 * 16 / LPR, 8>(a, lane);
@@ -331,7 +361,7 @@ __device__ inline void score_node(const LevelParams& P, int gi, int node, uint32
   }
 }
 
-template <int D, int GP, bool FUSED, int NT>
+template <int D, int GP, bool FUSED, int NT, bool H16>
 __global__ void __launch_bounds__(NT) score_nodes(LevelParams P) {
   touch_args(P);
   constexpr int kPidLds = 4096;
@@ -345,8 +375,8 @@ __global__ void __launch_bounds__(NT) score_nodes(LevelParams P) {
   // first kPre * blockDim.x kept parents (the list's capacity bounds their number) --
   // so they cost one round trip; only longer parent lists need a second.
   __shared__ __attribute__((aligned(16))) float s_q[GP > 4 ? GP * D : 4];
-  float qv[GP][4];
-  load_group_queries<D, GP>(P, gi, lane, qv, s_q);
+  float qv[GP][epl<H16>()];
+  load_group_queries<D, GP, epl<H16>(), (GP > 4)>(P, gi, lane, qv, s_q);
   const bool chk = P.check_stale && blockIdx.x == 0 && wave == 0 && (gi % P.H_kv) == 0;
   const int64_t nb = stale_count(P, gi, lane, chk);
   // fused: the length and the grandparents' count (the parent level's list),
@@ -469,7 +499,7 @@ __global__ void __launch_bounds__(NT) score_nodes(LevelParams P) {
     const int node = node_next;
     const uint32_t mask = mask_next;
     if (u + nwaves < U) list_entry_staged(P.list, geo, gi, u + nwaves, spid, spm, node_next, mask_next);
-    score_node<D, GP>(P, gi, node, mask, u, qv, s_q, lane);
+    score_node<D, GP, H16, (GP > 4)>(P, gi, node, mask, u, qv, s_q, lane);
   }
 }
 
@@ -1232,6 +1262,7 @@ __device__ inline int cut_head_wave(const float* sc, const uint32_t* cand_mask, 
 struct UpperLevel {
   const float* khat;           // [BH][ncap][R][d]
   const float* bhat;           // [BH][ncap][R]
+  const uint16_t* khat16;      // bf16 copy of khat, read instead when set
   int64_t ncap;
   float* scores;               // [BHq][cap], by node id
   int64_t cap;
@@ -1254,6 +1285,7 @@ __device__ inline LevelParams upper_level_params(const UpperParams& U, int k) {
   LevelParams P = U.base;
   P.khat = U.lv[k].khat;
   P.bhat = U.lv[k].bhat;
+  P.khat16 = U.lv[k].khat16;
   P.ncap = U.lv[k].ncap;
   P.scores = U.lv[k].scores;
   P.ucap = U.lv[k].cap;
@@ -1271,10 +1303,12 @@ __global__ void __launch_bounds__(256) score_upper(UpperParams U) {
   constexpr int NW = 256 / kWave;
   const int gi = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // the queries and the length are loaded together (one round trip)
-  __shared__ __attribute__((aligned(16))) float s_q[GP > 4 ? GP * D : 4];
-  float qv[GP][4];
-  load_group_queries<D, GP>(U.base, gi, lane, qv, s_q);
+  // the queries and the length are loaded together (one round trip); the
+  // queries go to LDS for every group size, since the levels of the run may
+  // score from fp32 k_hat or from its bf16 copy, whose lanes hold different dims
+  __shared__ __attribute__((aligned(16))) float s_q[GP * D];
+  float qv[GP][4], qv16[GP][8];
+  load_group_queries<D, GP, 4, true>(U.base, gi, lane, qv, s_q);
   int64_t T = U.base.list.T[gi / U.base.H_kv];
   if (T < 0) T = 0;
   if (T > U.base.list.T_cap) T = U.base.list.T_cap;
@@ -1285,7 +1319,9 @@ __global__ void __launch_bounds__(256) score_upper(UpperParams U) {
   for (int t = xcd_grouped_x() * NW + wave; t < total; t += gridDim.x * NW) {
     int k = 0, node = t;
     while (node >= (int)upper_nodes(U, k, T)) { node -= (int)upper_nodes(U, k, T); ++k; }
-    score_node<D, GP>(upper_level_params(U, k), gi, node, 0xffffffffu, node, qv, s_q, lane);
+    const LevelParams P = upper_level_params(U, k);
+    if (P.khat16 != nullptr) score_node<D, GP, true, true>(P, gi, node, 0xffffffffu, node, qv16, s_q, lane);
+    else score_node<D, GP, false, true>(P, gi, node, 0xffffffffu, node, qv, s_q, lane);
   }
 }
 
@@ -1561,30 +1597,30 @@ __global__ void __launch_bounds__(1024) level_kl(QualityParams P, const float* S
 // level with the best on every workload (deep 270 -> 195 us per route, gqa128k
 // 60 -> 53 us, long1m and rope_batch unchanged); with more, a wave scores too
 // few nodes to repay its workgroup's start.
+template <int D, int GP, int NT>
+static void launch_score_g(const LevelParams& P, dim3 grid, hipStream_t s) {
+  const dim3 block(NT);
+  const bool h16 = P.khat16 != nullptr;
+  if (P.fused) {
+    if (h16) hipLaunchKernelGGL((score_nodes<D, GP, true, NT, true>), grid, block, 0, s, P);
+    else hipLaunchKernelGGL((score_nodes<D, GP, true, NT, false>), grid, block, 0, s, P);
+  } else {
+    if (h16) hipLaunchKernelGGL((score_nodes<D, GP, false, NT, true>), grid, block, 0, s, P);
+    else hipLaunchKernelGGL((score_nodes<D, GP, false, NT, false>), grid, block, 0, s, P);
+  }
+}
+
 template <int NT>
 static void launch_score_nt(const LevelParams& P, dim3 grid, hipStream_t s) {
   const int GP = P.G <= 4 ? 4 : (P.G <= 8 ? 8 : 16);
-  const dim3 block(NT);
-  if (P.fused) {
-    if (P.d == 128) {
-      if (GP == 4) hipLaunchKernelGGL((score_nodes<128, 4, true, NT>), grid, block, 0, s, P);
-      else if (GP == 8) hipLaunchKernelGGL((score_nodes<128, 8, true, NT>), grid, block, 0, s, P);
-      else hipLaunchKernelGGL((score_nodes<128, 16, true, NT>), grid, block, 0, s, P);
-    } else {
-      if (GP == 4) hipLaunchKernelGGL((score_nodes<64, 4, true, NT>), grid, block, 0, s, P);
-      else if (GP == 8) hipLaunchKernelGGL((score_nodes<64, 8, true, NT>), grid, block, 0, s, P);
-      else hipLaunchKernelGGL((score_nodes<64, 16, true, NT>), grid, block, 0, s, P);
-    }
-    return;
-  }
   if (P.d == 128) {
-    if (GP == 4) hipLaunchKernelGGL((score_nodes<128, 4, false, NT>), grid, block, 0, s, P);
-    else if (GP == 8) hipLaunchKernelGGL((score_nodes<128, 8, false, NT>), grid, block, 0, s, P);
-    else hipLaunchKernelGGL((score_nodes<128, 16, false, NT>), grid, block, 0, s, P);
+    if (GP == 4) launch_score_g<128, 4, NT>(P, grid, s);
+    else if (GP == 8) launch_score_g<128, 8, NT>(P, grid, s);
+    else launch_score_g<128, 16, NT>(P, grid, s);
   } else {
-    if (GP == 4) hipLaunchKernelGGL((score_nodes<64, 4, false, NT>), grid, block, 0, s, P);
-    else if (GP == 8) hipLaunchKernelGGL((score_nodes<64, 8, false, NT>), grid, block, 0, s, P);
-    else hipLaunchKernelGGL((score_nodes<64, 16, false, NT>), grid, block, 0, s, P);
+    if (GP == 4) launch_score_g<64, 4, NT>(P, grid, s);
+    else if (GP == 8) launch_score_g<64, 8, NT>(P, grid, s);
+    else launch_score_g<64, 16, NT>(P, grid, s);
   }
 }
 
@@ -1660,6 +1696,7 @@ static LevelParams level_params(const zha_cfg* cfg, const float* q, const zha_tr
   P.q = q;
   P.khat = tree->khat[level - 1];
   P.bhat = tree->bhat[level - 1];
+  P.khat16 = tree->khat16[level - 1];
   P.ncap = tree->n_cap[level - 1];
   P.stage = (uint32_t*)((char*)ws + w.stage);
   P.stage_cap = w.stage_cap;
@@ -1737,6 +1774,7 @@ static int32_t route_impl(const zha_cfg* cfg, const float* q, const zha_tree* tr
       UpperLevel& v = U.lv[k];
       v.khat = tree->khat[l - 1];
       v.bhat = tree->bhat[l - 1];
+      v.khat16 = tree->khat16[l - 1];
       v.ncap = tree->n_cap[l - 1];
       v.scores = (float*)(base + w.scores[l - 1]);
       v.cap = w.cap[l - 1];

@@ -50,7 +50,8 @@ class _KV(ctypes.Structure):
 
 class _Tree(ctypes.Structure):
     _fields_ = [("khat", ctypes.c_void_p * MAX_L), ("bhat", ctypes.c_void_p * MAX_L),
-                ("n_cap", ctypes.c_int64 * MAX_L), ("n_built", ctypes.c_void_p)]
+                ("n_cap", ctypes.c_int64 * MAX_L), ("n_built", ctypes.c_void_p),
+                ("khat16", ctypes.c_void_p * MAX_L)]
 
 
 def _load() -> ctypes.CDLL:
@@ -158,9 +159,12 @@ def new_workspace(cfg: Config, op: int = OP_ALL, device="cuda") -> torch.Tensor:
 
 
 class Tree:
-    """Device storage of one tree per (sequence, KV head), all levels."""
+    """Device storage of one tree per (sequence, KV head), all levels.
 
-    def __init__(self, cfg: Config, device="cuda"):
+    bf16_copy: also keep a bf16 copy of every level's k_hat (zha_tree.khat16),
+    written by the builder and read by the route instead of the fp32 k_hat."""
+
+    def __init__(self, cfg: Config, device="cuda", bf16_copy: bool = False):
         self.cfg = cfg
         self.khat: List[torch.Tensor] = []
         self.bhat: List[torch.Tensor] = []
@@ -169,6 +173,9 @@ class Tree:
             self.khat.append(torch.zeros(cfg.B, cfg.H_kv, n, cfg.R, cfg.d, dtype=torch.float32, device=device))
             self.bhat.append(torch.zeros(cfg.B, cfg.H_kv, n, cfg.R, dtype=torch.float32, device=device))
         self.n_built = torch.zeros(cfg.L, cfg.B, dtype=torch.int64, device=device)
+        self.khat16: List[Optional[torch.Tensor]] = [None] * cfg.L
+        if bf16_copy:
+            self.khat16 = [torch.zeros(k.shape, dtype=torch.bfloat16, device=device) for k in self.khat]
 
     @classmethod
     def lower_levels(cls, tree: "Tree", cfg: "Config") -> "Tree":
@@ -181,6 +188,7 @@ class Tree:
         t.khat = tree.khat[:cfg.L]
         t.bhat = tree.bhat[:cfg.L]
         t.n_built = tree.n_built[:cfg.L]
+        t.khat16 = list(getattr(tree, "khat16", [None] * tree.cfg.L))[:cfg.L]
         return t
 
     def c(self) -> _Tree:
@@ -189,6 +197,12 @@ class Tree:
             t.khat[i] = self.khat[i].data_ptr()
             t.bhat[i] = self.bhat[i].data_ptr()
             t.n_cap[i] = self.khat[i].shape[2]
+            k16 = getattr(self, "khat16", None)
+            if k16 is not None and k16[i] is not None:
+                if k16[i].shape != self.khat[i].shape or k16[i].dtype != torch.bfloat16 \
+                        or not k16[i].is_contiguous():
+                    raise ValueError("khat16 must be a contiguous bf16 tensor shaped like khat")
+                t.khat16[i] = k16[i].data_ptr()
         t.n_built = self.n_built.data_ptr()
         return t
 
@@ -322,10 +336,10 @@ class Decoder:
     writes each new token's key/value before the step, as a KV cache does.
     """
 
-    def __init__(self, cfg: Config, qref: torch.Tensor, device="cuda"):
+    def __init__(self, cfg: Config, qref: torch.Tensor, device="cuda", bf16_copy: bool = False):
         self.cfg = cfg
         self.qref = qref
-        self.tree = Tree(cfg, device)
+        self.tree = Tree(cfg, device, bf16_copy)
         self.ws = new_workspace(cfg, OP_ALL, device)
         self.leaves = LeafList(cfg, device)
         self.out = torch.zeros(cfg.B, cfg.Hq, cfg.d, dtype=torch.float32, device=device)

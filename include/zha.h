@@ -110,6 +110,13 @@ typedef struct zha_tree {
   float* bhat[ZHA_MAX_L];     /* [B][H_kv][n_cap[l-1]][R] */
   int64_t n_cap[ZHA_MAX_L];   /* node capacity per level, >= T_cap / C^l */
   int64_t* n_built;           /* [L][B] int64 nodes built per level and sequence */
+  /* Optional bf16 copy of a level's k_hat (same layout as khat, each value
+   * rounded to nearest even), or NULL.  When set, zha_build_level and zha_append
+   * write it beside khat, and every routing call scores that level from it
+   * instead of khat: half the bytes per node, each k_hat value to 2^-9 relative,
+   * b_hat and all arithmetic still fp32.  A level's copy must be set when the
+   * level is built and appended, or the route reads stale values. */
+  uint16_t* khat16[ZHA_MAX_L];
 } zha_tree;
 
 /*

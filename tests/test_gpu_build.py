@@ -220,3 +220,43 @@ def test_build_is_deterministic():
     torch.cuda.synchronize()
     for a, b in zip(tree.khat + tree.bhat, tree2.khat + tree2.bhat):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("C,L,kv,rope", [(64, 2, "bf16", False), (32, 2, "bf16", True), (16, 3, "bf16", False),
+                                         (8, 3, "bf16", False), (4, 3, "bf16", True), (2, 4, "bf16", False),
+                                         (16, 2, "f32", False), (4, 3, "f32", False)])
+def test_bf16_copy_is_the_rounded_khat(C, L, kv, rope):
+    """zha_tree.khat16: every builder kernel (matrix-core, small-C and generic
+    leaves, parents), the one-launch append cascade and the per-level append
+    write, beside each k_hat value, that value rounded to bf16 (nearest even):
+    the copy equals torch's rounding of the fp32 tree bit for bit."""
+    wl = _workload("rope_batch" if rope else "gqa128k", B=2, H_kv=2, G=4, C=C, L=L, R=16,
+                   n_clusters=16, kv_dtype=kv)
+    T0 = C ** L + 3
+    T1 = T0 + 2 * C + 5
+    T_cap = T1 + 2 * C
+    K, V = synth.make_cache(wl.with_(N=T_cap, open_len=0, steps=0), DEV, T_cap)
+    qref = synth.make_qref(wl, DEV)
+    cfg = zha.Config(B=2, H_kv=2, G=4, d=128, C=C, L=L, R=16, T_cap=T_cap,
+                     kv_dtype=zha.F32 if kv == "f32" else zha.BF16, rope=rope, rope_base=wl.rope_base)
+    ws = zha.new_workspace(cfg)
+
+    def same(tree, where):
+        torch.cuda.synchronize()
+        for level in range(1, L + 1):
+            assert torch.equal(tree.khat16[level - 1].view(torch.int16),
+                               tree.khat[level - 1].to(torch.bfloat16).view(torch.int16)), (where, level)
+        assert bool(torch.isfinite(tree.khat[0][:, :, :T1 // C]).all())
+
+    tree = zha.Tree(cfg, DEV, bf16_copy=True)
+    T = torch.tensor([T0, T0 - C + 1], dtype=torch.int64, device=DEV)
+    zha.build(cfg, K, V, T, qref, tree, ws)
+    same(tree, "prefill")
+    for _ in range(T1 - T0):                     # one token per step: one-launch cascade
+        T += 1
+        zha.append(cfg, K, V, T, qref, tree, ws, max_new_tokens=1)
+    same(tree, "append")
+    T += C + 1                                   # more than C at once: per-level launches
+    zha.append(cfg, K, V, T, qref, tree, ws, max_new_tokens=C + 1)
+    same(tree, "append per level")
+    assert zha.ws_status(ws) == 0

@@ -1,7 +1,8 @@
 """Every output buffer the library writes sits between canary margins, and no
 call writes past its buffer's bounds.
 
-The tree levels, node counts, leaf lists, outputs, KL array and the workspace
+The tree levels (and their bf16 copies of k_hat), node counts, leaf lists,
+outputs, KL array and the workspace
 are views into larger device buffers whose margins hold a fixed bit pattern
 (a NaN payload for 32-bit words, 0xA5 for workspace bytes).  Each call of the
 decode path -- prefill build, the append that completes C new tokens, route
@@ -41,6 +42,11 @@ class Guarded:
         elif dtype == torch.int64:
             raw = torch.full((PAD + n + PAD,), (WORD << 32) | WORD, dtype=torch.int64, device=DEV)
             view = raw[PAD:PAD + n]
+        elif dtype == torch.bfloat16:            # two per 32-bit word
+            n32 = (n + 1) // 2
+            raw = torch.full((PAD + n32 + PAD,), WORD, dtype=torch.int32, device=DEV)
+            view = raw[PAD:PAD + n32].view(torch.bfloat16)[:n]
+            n = n32
         else:
             raise TypeError(dtype)
         self.bufs.append((raw, n, f"{tuple(shape)} {dtype}"))
@@ -80,8 +86,9 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("bf16_copy", [False, True])
 @pytest.mark.parametrize("case", sorted(CASES))
-def test_no_write_outside_any_output(case):
+def test_no_write_outside_any_output(case, bf16_copy):
     name, over, T0 = CASES[case]
     wl = synth.WORKLOADS[name].with_(**over)
     C = wl.C
@@ -99,6 +106,7 @@ def test_no_write_outside_any_output(case):
                  for l in range(1, cfg.L + 1)]
     tree.bhat = [g.tensor((cfg.B, cfg.H_kv, cfg.level_cap(l), cfg.R), torch.float32)
                  for l in range(1, cfg.L + 1)]
+    tree.khat16 = [g.tensor(k.shape, torch.bfloat16) if bf16_copy else None for k in tree.khat]
     tree.n_built = g.tensor((cfg.L, cfg.B), torch.int64)
     tree.n_built.zero_()
     ws = g.workspace(zha.workspace_bytes(cfg))
@@ -120,6 +128,12 @@ def test_no_write_outside_any_output(case):
     zha.append(cfg, K, V, T, qref, tree, ws, max_new_tokens=C)
     g.check("append")
     assert tree.n_built[0].tolist() == [t // C for t in T1]
+    if bf16_copy:   # built nodes only: the others still hold the canary pattern
+        for level, (k, k16) in enumerate(zip(tree.khat, tree.khat16), start=1):
+            for b, t in enumerate(T1):
+                n = t // C ** level
+                assert torch.equal(k16[b, :, :n].view(torch.int16),
+                                   k[b, :, :n].to(torch.bfloat16).view(torch.int16)), (level, b)
     q = synth.make_query(wl, 0, max(T1), DEV)
     for p in (0.9, 1.0):
         zha.route(cfg, q, tree, T, p, ids, mask, count, ws)

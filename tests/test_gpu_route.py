@@ -428,3 +428,53 @@ def test_route_quality_kl_per_level(case):
                     assert np.isnan(klh[l, b, j])
                 else:
                     assert abs(klh[l, b, j] - ref[l]) <= 5e-4 + 2e-3 * abs(ref[l]), (l, b, j, klh[l, b, j], ref[l])
+
+
+# ---------------------------------------------------------------- bf16 copy of k_hat
+
+def bf16_trees(trees):
+    """The oracle trees with every k_hat rounded to bf16 (nearest even) and
+    upcast exactly: the values a zha_tree.khat16 copy holds; b_hat stays fp32."""
+    out = []
+    for row in trees:
+        out.append([[{"khat": f64(torch.tensor(lv["khat"], dtype=torch.float32).to(torch.bfloat16)),
+                       "bhat": lv["bhat"]} for lv in levels] for levels in row])
+    return out
+
+
+def upload_bf16(cfg, trees16, T):
+    """A tree whose khat16 copies hold the rounded k_hat (khat holds it too)."""
+    tree = upload(cfg, trees16, T)
+    tree.khat16 = [k.to(torch.bfloat16) for k in tree.khat]
+    return tree
+
+
+@pytest.mark.parametrize("case", ["tiny", "gqa_c16", "deep", "rope", "g16", "g3", "c64", "fused", "wide20k"])
+@pytest.mark.parametrize("p", [0.5, 0.9])
+def test_route_scores_from_the_bf16_copy(case, p):
+    """With zha_tree.khat16 set, every routing call scores from the bf16 copy:
+    level by level the same as the oracle routing on the rounded summaries, and
+    zha_route's sets equal to that composition.  The fp32 khat of the uploaded
+    tree is poisoned, so a level scored from it would fail."""
+    wl, T = CASES[case]
+    cfg, K, V, trees = _setup(wl, T)
+    trees16 = bf16_trees(trees)
+    tree = upload_bf16(cfg, trees16, T)
+    for k in tree.khat:
+        k.fill_(float("nan"))
+    ws = zha.new_workspace(cfg)
+    Tt = torch.full((cfg.B,), T, dtype=torch.int64, device=DEV)
+    report = []
+    for step in range(2):
+        q = synth.make_query(wl, step, T, "cpu").to(DEV)
+        leaves = level_sync_compare(cfg, tree, trees16, q, T, p, ws, report)
+        lst = zha.LeafList(cfg, DEV)
+        zha.route(cfg, q, tree, Tt, p, lst.ids, lst.mask, lst.count, ws)
+        torch.cuda.synchronize()
+        full = sets_from_lists(lst.ids, lst.mask, lst.count, cfg.G)
+        for b in range(cfg.B):
+            for j in range(cfg.Hq):
+                np.testing.assert_array_equal(full[b][j], leaves[b][j])
+        assert zha.ws_status(ws) == 0
+    for r in report:
+        print("allowed:", case, p, r)
