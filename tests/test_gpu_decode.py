@@ -4,7 +4,10 @@ p = 0.9): each step appends a summary when a chunk completes (at step 32 here),
 routes and attends.  On sampled steps and KV heads the step is checked against
 the oracle run on that step's tree (the GPU's summaries, as fp32 values):
 routing level by level (near-tie allowances only), the route's final leaf sets,
-and the attention outputs over the sets the GPU routed."""
+and the attention outputs over the sets the GPU routed.  The same loop runs
+with the tree's bf16 copy of k_hat (zha_tree.khat16): the copy must stay the
+rounded fp32 tree through the append, and routing is checked on the copy's
+values."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +15,7 @@ import torch
 import oracle as O
 import synth
 from tests.gpu_util import TOL, f64, rel_err, sets_from_lists
-from tests.test_gpu_route import level_sync_compare, upload
+from tests.test_gpu_route import level_sync_compare, upload, upload_bf16
 
 pytestmark = pytest.mark.gpu
 zha = pytest.importorskip("hierarchical_kv_cache_amd.zha")
@@ -22,24 +25,26 @@ CHECK_STEPS = (0, 31, 32, 33, 39)
 SAMPLED_KV_HEADS = (2, 7)
 
 
-def host_tree(dec, cfg, h, T):
-    """KV head h's built levels (sequence 0) as float64 arrays."""
+def host_tree(dec, cfg, h, T, bf16_copy=False):
+    """KV head h's built levels (sequence 0) as float64 arrays: the k_hat the
+    route reads (the fp32 tree, or its bf16 copy) and b_hat."""
     out = []
     for level in range(1, cfg.L + 1):
         n = T // cfg.C ** level
-        out.append({"khat": f64(dec.tree.khat[level - 1][0, h, :n]),
-                    "bhat": f64(dec.tree.bhat[level - 1][0, h, :n])})
+        kh = dec.tree.khat16[level - 1] if bf16_copy else dec.tree.khat[level - 1]
+        out.append({"khat": f64(kh[0, h, :n]), "bhat": f64(dec.tree.bhat[level - 1][0, h, :n])})
     return out
 
 
-def test_decode_loop_append_route_attend():
+@pytest.mark.parametrize("bf16_copy", [False, True])
+def test_decode_loop_append_route_attend(bf16_copy):
     wl = synth.WORKLOADS["gqa128k"]
     T0, C, p = wl.T0, wl.C, wl.p
     T_cap = T0 + STEPS + C
     K, V = synth.make_cache(wl.with_(steps=STEPS), DEV, T_cap)
     qref = synth.make_qref(wl, DEV)
     cfg = zha.Config(B=1, H_kv=wl.H_kv, G=wl.G, d=wl.d, C=C, L=wl.L, R=wl.R, T_cap=T_cap)
-    dec = zha.Decoder(cfg, qref, DEV)
+    dec = zha.Decoder(cfg, qref, DEV, bf16_copy=bf16_copy)
     Tt = torch.tensor([T0], dtype=torch.int64, device=DEV)
     dec.prefill(K, V, Tt)
     appends = 0
@@ -56,11 +61,14 @@ def test_decode_loop_append_route_attend():
         if s not in CHECK_STEPS:
             continue
         assert dec.tree.n_built[:, 0].tolist() == [T // C ** l for l in range(1, cfg.L + 1)]
+        if bf16_copy:
+            for k, k16 in zip(dec.tree.khat, dec.tree.khat16):
+                assert torch.equal(k16.view(torch.int16), k.to(torch.bfloat16).view(torch.int16)), s
         gpu_sets = sets_from_lists(dec.leaves.ids, dec.leaves.mask, dec.leaves.count, cfg.G)
         for h in SAMPLED_KV_HEADS:
-            trees = [[host_tree(dec, cfg, h, T)]]
+            trees = [[host_tree(dec, cfg, h, T, bf16_copy)]]
             cfg1 = zha.Config(B=1, H_kv=1, G=cfg.G, d=cfg.d, C=C, L=cfg.L, R=cfg.R, T_cap=T)
-            tree1 = upload(cfg1, trees, T)
+            tree1 = upload_bf16(cfg1, trees, T) if bf16_copy else upload(cfg1, trees, T)
             ws1 = zha.new_workspace(cfg1)
             q1 = q[:, h * cfg.G:(h + 1) * cfg.G].contiguous()
             report = []
