@@ -334,6 +334,8 @@ class Decoder:
 
     Holds the tree, the workspace and the leaf list; the caller owns K, V, T and
     writes each new token's key/value before the step, as a KV cache does.
+    bf16_copy: the tree also keeps a bf16 copy of every level's k_hat, which the
+    builder writes and the route scores from (half the summary bytes per step).
     """
 
     def __init__(self, cfg: Config, qref: torch.Tensor, device="cuda", bf16_copy: bool = False):
