@@ -104,7 +104,8 @@ typedef struct zha_kv {
   const int64_t* T;      /* [B] current lengths, 0 <= T <= T_cap */
 } zha_kv;
 
-/* Tree storage (host struct holding device pointers); entry l-1 is level l. */
+/* Tree storage (host struct holding device pointers); entry l-1 is level l.
+ * Zero-initialise it (zha_tree t = {0};) so the optional pointers are NULL. */
 typedef struct zha_tree {
   float* khat[ZHA_MAX_L];     /* [B][H_kv][n_cap[l-1]][R][d] */
   float* bhat[ZHA_MAX_L];     /* [B][H_kv][n_cap[l-1]][R] */
