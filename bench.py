@@ -841,6 +841,9 @@ def main():
         sweep[str(wls.T0)] = {"routed_us_per_step": ms_r * 1000.0 / Ks,
                               "dense_us_per_step": ms_d * 1000.0 / Ks,
                               "speedup_vs_dense": ms_d / ms_r}
+        if not args.no_bf16_copy:
+            r16 = bf16_copy_report(rs, Ws, Ks, p)
+            sweep[str(wls.T0)]["routed_bf16_copy_us_per_step"] = r16["us_per_step"]
         if args.flat:
             rs.prefill()
             rs.routed_steps(0, Ws, p)
@@ -854,13 +857,17 @@ def main():
             rs.routed_steps(0, Ws, 0.75)
             ms_75 = timed(lambda: rs.routed_steps(Ws, Ws + Ks, 0.75))
             sweep[str(wls.T0)]["routed_p0.75_us_per_step"] = ms_75 * 1000.0 / Ks
-        log(f"[bench] T={wls.T0}: routed {ms_r * 1000 / Ks:.1f} us/step, dense {ms_d * 1000 / Ks:.1f}")
+        log(f"[bench] T={wls.T0}: routed {ms_r * 1000 / Ks:.1f} us/step, dense {ms_d * 1000 / Ks:.1f}"
+            + (f", routed from the bf16 copy {sweep[str(wls.T0)]['routed_bf16_copy_us_per_step']:.1f}"
+               if "routed_bf16_copy_us_per_step" in sweep[str(wls.T0)] else ""))
         del rs
         torch.cuda.empty_cache()
     if sweep:
         sweep[str(wl.T0)] = {"routed_us_per_step": us_step,
                              "dense_us_per_step": dense["us_per_step"] if dense else None,
                              "speedup_vs_dense": (dense["us_per_step"] / us_step) if dense else None}
+        if "route_bf16_copy" in extra:
+            sweep[str(wl.T0)]["routed_bf16_copy_us_per_step"] = extra["route_bf16_copy"]["us_per_step"]
         if args.flat:
             sweep[str(wl.T0)]["flat_topp"] = extra["flat_comparator"]["topp"]
             sweep[str(wl.T0)]["flat_topk"] = extra["flat_comparator"]["topk"]
