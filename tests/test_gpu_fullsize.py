@@ -112,3 +112,61 @@ def test_full_size_build_route_attend_on_sampled_heads(name, p):
 def tree_slice(level_tensor, b, h, idx):
     """Rows idx of KV head h of sequence b of one tree level."""
     return level_tensor[b, h].index_select(0, idx)
+
+
+@pytest.mark.parametrize("name", ["long1m", "rope_batch"])
+def test_full_size_bf16_copy(name):
+    """The tree's bf16 copy of k_hat at full size: after the prefill every level's
+    copy is the fp32 tree rounded to bf16 (nearest even) bit for bit; the router
+    scoring from a copy of the oracle's tree matches the oracle routing on the
+    same rounded values, level by level and end to end, on sampled heads; and the
+    decode step routed from the GPU's own copy attends within tolerance of the
+    oracle over the sets it routed."""
+    from tests.test_gpu_route import bf16_trees, upload_bf16
+    wl = synth.WORKLOADS[name]
+    T, p = wl.T0, wl.p
+    K, V = synth.make_cache(wl.with_(steps=0), DEV, T)
+    qref = synth.make_qref(wl, DEV)
+    cfg = zha.Config(B=wl.B, H_kv=wl.H_kv, G=wl.G, d=wl.d, C=wl.C, L=wl.L, R=wl.R, T_cap=T,
+                     rope=wl.rope, rope_base=wl.rope_base)
+    dec = zha.Decoder(cfg, qref, DEV, bf16_copy=True)
+    Tt = torch.full((wl.B,), T, dtype=torch.int64, device=DEV)
+    dec.prefill(K, V, Tt)
+    torch.cuda.synchronize()
+    for level in range(cfg.L):
+        assert torch.equal(dec.tree.khat16[level].view(torch.int16),
+                           dec.tree.khat[level].to(torch.bfloat16).view(torch.int16)), level
+    q = synth.make_query(wl, 1, T, DEV)
+    out, lse = dec.step(q, K, V, Tt, p)
+    torch.cuda.synchronize()
+    assert zha.ws_status(dec.ws) == 0
+    gpu_sets = sets_from_lists(dec.leaves.ids, dec.leaves.mask, dec.leaves.count, cfg.G)
+    rope_base = wl.rope_base if wl.rope else None
+    b, h = SAMPLED[name][0]
+    Kh, Vh, qh = f64(K[b, h, :T]), f64(V[b, h, :T]), f64(q[b])
+    ref = O.build_tree(Kh, f64(qref[h]), T, cfg.C, cfg.L, cfg.scale, rope_base)
+    cfg1 = zha.Config(B=1, H_kv=1, G=cfg.G, d=cfg.d, C=cfg.C, L=cfg.L, R=cfg.R, T_cap=T)
+    trees16 = bf16_trees([[[{"khat": O.fp32(lv["khat"]), "bhat": O.fp32(lv["bhat"])} for lv in ref]]])
+    tree1 = upload_bf16(cfg1, trees16, T)
+    for k in tree1.khat:
+        k.fill_(float("nan"))          # only the copy may be read
+    ws1 = zha.new_workspace(cfg1)
+    q1 = q[b:b + 1, h * cfg.G:(h + 1) * cfg.G].contiguous()
+    report = []
+    leaves = level_sync_compare(cfg1, tree1, trees16, q1, T, p, ws1, report)
+    lst = zha.LeafList(cfg1, DEV)
+    zha.route(cfg1, q1, tree1, torch.tensor([T], dtype=torch.int64, device=DEV), p,
+              lst.ids, lst.mask, lst.count, ws1)
+    torch.cuda.synchronize()
+    full = sets_from_lists(lst.ids, lst.mask, lst.count, cfg1.G)
+    for g in range(cfg.G):
+        np.testing.assert_array_equal(full[0][g], leaves[0][g])
+    assert zha.ws_status(ws1) == 0
+    for r in report:
+        print("allowed:", name, b, h, r)
+    for g in range(cfg.G):
+        j = h * cfg.G + g
+        keys = O.routed_keys(gpu_sets[b][j], T, cfg.C)
+        o_ref, lse_ref = O.attend_keys(qh[j], Kh, Vh, keys, cfg.scale)
+        assert rel_err(f64(out[b, j]), o_ref) <= TOL["bf16"], (name, g)
+        assert abs(float(lse[b, j]) - lse_ref) <= 1e-3 * max(1.0, abs(lse_ref)), (name, g)
