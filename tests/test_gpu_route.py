@@ -326,14 +326,21 @@ def test_cut_crossing_bucket_sizes(n_band, p):
     assert zha.ws_status(ws) == 0
 
 
+@pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("case", ["gqa_c16", "deep", "tiny"])
 @pytest.mark.parametrize("kind", ["root", "power", "mixed"])
-def test_depth_scheduled_p(case, kind):
+def test_depth_scheduled_p(case, kind, bf16):
     """zha_route_sched: one top-p per level, level by level against the oracle,
-    and end to end equal to the level-by-level composition."""
+    and end to end equal to the level-by-level composition; also scoring from
+    the bf16 copy of k_hat, against the oracle on the rounded summaries."""
     wl, T = CASES[case]
     cfg, K, V, trees = _setup(wl, T)
     tree = upload(cfg, trees, T)
+    if bf16:
+        trees = bf16_trees(trees)
+        tree = upload_bf16(cfg, trees, T)
+        for k in tree.khat:
+            k.fill_(float("nan"))
     ws = zha.new_workspace(cfg)
     Tt = torch.full((cfg.B,), T, dtype=torch.int64, device=DEV)
     if kind == "mixed":
@@ -373,14 +380,21 @@ def _check_topk_selection(cut_ids, cut_scores, k, gsel):
         assert ok or abs(worst_kept[0] - best_dropped[0]) < TIE, (worst_kept, best_dropped)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("case", ["wide20k", "tiny", "gqa_c16", "deep"])
 @pytest.mark.parametrize("frac", [0.1, 0.5])
-def test_fixed_budget_topk(case, frac):
+def test_fixed_budget_topk(case, frac, bf16):
     """zha_route_topk against the oracle's fixed-budget route: a budget of
-    frac * n_l nodes per level (at least one)."""
+    frac * n_l nodes per level (at least one); also scoring from the bf16 copy
+    of k_hat, against the oracle on the rounded summaries."""
     wl, T = CASES[case]
     cfg, K, V, trees = _setup(wl, T)
     tree = upload(cfg, trees, T)
+    if bf16:
+        trees = bf16_trees(trees)
+        tree = upload_bf16(cfg, trees, T)
+        for k in tree.khat:
+            k.fill_(float("nan"))
     ws = zha.new_workspace(cfg)
     Tt = torch.full((cfg.B,), T, dtype=torch.int64, device=DEV)
     ks = [max(1, int(frac * (T // cfg.C ** l))) for l in range(1, cfg.L + 1)]
@@ -403,12 +417,20 @@ def test_fixed_budget_topk(case, frac):
                     np.testing.assert_array_equal(full[b][j], rt.leaves)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("case", ["tiny", "gqa_c16", "deep", "rope"])
-def test_route_quality_kl_per_level(case):
-    """zha_route_quality against the oracle's per-level KL on the oracle's tree."""
+def test_route_quality_kl_per_level(case, bf16):
+    """zha_route_quality against the oracle's per-level KL on the oracle's tree
+    (its estimate scored from the bf16 copy of k_hat too, against the oracle on
+    the rounded summaries)."""
     wl, T = CASES[case]
     cfg, K, V, trees = _setup(wl, T)
     tree = upload(cfg, trees, T)
+    if bf16:
+        trees = bf16_trees(trees)
+        tree = upload_bf16(cfg, trees, T)
+        for k in tree.khat:
+            k.fill_(float("nan"))
     ws = zha.new_workspace(cfg)
     Tt = torch.full((cfg.B,), T, dtype=torch.int64, device=DEV)
     Kd, Vd = K.to(DEV), V.to(DEV)
