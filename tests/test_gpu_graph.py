@@ -5,7 +5,8 @@ synchronisation and no memory-set or copy nodes, so a caller can capture a
 step.  The graph is replayed for several queries, with eager work and
 synchronisations between the replays, and every replay must give the eager
 step's outputs bit for bit: the same kernels on the same inputs, with fixed
-reduction orders.
+reduction orders.  The same holds with the route scoring from the tree's bf16
+copy of k_hat.
 """
 import pytest
 import torch
@@ -17,13 +18,14 @@ zha = pytest.importorskip("hierarchical_kv_cache_amd.zha")
 DEV = "cuda"
 
 
-def test_decode_step_in_a_graph_matches_eager():
+@pytest.mark.parametrize("bf16_copy", [False, True])
+def test_decode_step_in_a_graph_matches_eager(bf16_copy):
     wl = synth.WORKLOADS["gqa128k"].with_(H_kv=2, G=4, C=16, L=3, n_clusters=128)
     T = 20000 + 7
     K, V = synth.make_cache(wl.with_(N=T, open_len=0, steps=0), DEV, T)
     qref = synth.make_qref(wl, DEV)
     cfg = zha.Config(B=1, H_kv=2, G=4, d=128, C=16, L=3, R=16, T_cap=T)
-    dec = zha.Decoder(cfg, qref, DEV)
+    dec = zha.Decoder(cfg, qref, DEV, bf16_copy=bf16_copy)
     Tt = torch.tensor([T], dtype=torch.int64, device=DEV)
     dec.prefill(K, V, Tt)
     q_static = synth.make_query(wl, 0, T, DEV).clone()
