@@ -216,25 +216,26 @@ __device__ inline void split3(float x, __bf16& hi, __bf16& mid, __bf16& lo) {
 //   Z = Q_hat K^T          A = scaled reference queries (3-way bf16 split),
 //                          B = the leaf's keys as loaded (row = key, 8 dims)
 //   softmax over keys per plane in registers, b_hat = F - sum_j w_j z_j
-//   k_hat^T = K^T W^T      A = K^T through LDS, B = W (3-way bf16 split)
-// The wave's LDS (kLds bytes) holds K^T and W; the query staging aliases K^T.
-// Only the wave's own lanes touch it, so wave-level LDS syncs order it.
+//   k_hat^T = K^T W^T      MFMA 16x16x16: A = 16 dims x 16 keys of K^T, read
+//                          from the keys as stored in LDS (row = key) by the
+//                          transposing LDS read; B = W^T (3-way bf16 split)
+// The wave's LDS (kLds bytes) holds the keys and W; the query staging aliases
+// the keys.  Only the wave's own lanes touch it, so wave-level LDS syncs order it.
 template <int D, int C>
 struct MfmaLeaf {
   static constexpr int KST = D / 32;              // dimension steps of Z
-  static constexpr int NT = C / 16;               // key tiles of Z
-  static constexpr int CK = C < 32 ? 32 : C;      // keys padded to whole contraction steps
-  static constexpr int KS2 = CK / 32;             // key steps of k_hat
-  static constexpr int KP = CK + 8;               // K^T row stride (bf16 elements)
-  static constexpr int WP = CK + 4;               // W row stride (floats)
+  static constexpr int NT = C / 16;               // key tiles of Z, key blocks of k_hat
+  static constexpr int KRP = D + 16;              // key row stride in LDS (bf16 elements)
+  static constexpr int WP = C + 4;                // W row stride (floats)
   static constexpr int H2 = D / 2;
-  static constexpr int KT_BYTES = D * KP * 2;
+  static constexpr int KR_BYTES = C * KRP * 2;
+  static constexpr int QS_BYTES = 16 * (D + 4) * 4;
+  static constexpr int KT_BYTES = KR_BYTES > QS_BYTES ? KR_BYTES : QS_BYTES;
   static constexpr int kLds = KT_BYTES + 16 * WP * 4;
-  static_assert(16 * (D + 4) * 4 <= KT_BYTES, "query staging aliases K^T");
   typedef u32x4b_t Keys[NT][KST];
   typedef bf16x8b_t QOps[3][KST];
+  typedef short bf16x4s_t __attribute__((ext_vector_type(4)));   // bf16 bits
 
-  // The weights of the padded keys C..CK-1 stay zero.
   __device__ static void init(unsigned char* lds, int lane) {
     float* wsm = reinterpret_cast<float*>(lds + KT_BYTES);
     for (int i = lane; i < 16 * WP; i += 64) wsm[i] = 0.0f;
@@ -312,7 +313,7 @@ struct MfmaLeaf {
   template <class Next>
   __device__ static void leaf(const BuildParams& P, int gi, int64_t n, Keys& kv, const QOps& qa,
                               unsigned char* lds, int lane, Next&& next) {
-    uint16_t (*kt)[KP] = reinterpret_cast<uint16_t (*)[KP]>(lds);
+    uint16_t (*kr)[KRP] = reinterpret_cast<uint16_t (*)[KRP]>(lds);
     float (*wsm)[WP] = reinterpret_cast<float (*)[WP]>(lds + KT_BYTES);
     const int row = lane & 15, kg = lane >> 4;
     const int R = P.R;
@@ -329,17 +330,13 @@ struct MfmaLeaf {
         z[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[2][s], kb, z[t], 0, 0, 0);
       }
     }
-    // ---- K^T into LDS (padded keys zero), then the next leaf's keys in flight
+    // ---- the keys into LDS as loaded (a key's 8 dims per 16-byte store), then
+    // the next leaf's keys in flight
 #pragma unroll
-    for (int t = 0; t < CK / 16; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int s = 0; s < KST; ++s)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t x = t < NT ? kv[t < NT ? t : 0][s][e] : 0u;
-          kt[32 * s + 8 * kg + 2 * e][16 * t + row] = (uint16_t)(x & 0xffffu);
-          kt[32 * s + 8 * kg + 2 * e + 1][16 * t + row] = (uint16_t)(x >> 16);
-        }
+        *(u32x4b_t*)&kr[16 * t + row][32 * s + 8 * kg] = kv[t][s];
     next();
     // ---- softmax over the leaf's keys, per plane (16 lanes share a plane)
 #pragma unroll
@@ -369,28 +366,37 @@ struct MfmaLeaf {
       for (int t = 0; t < NT; ++t) wsm[pl][16 * t + row] = e[t] / S;
     }
     wave_lds_sync();
-    // ---- k_hat^T = K^T W^T; acc[i] = k_hat of plane row, dimension 16td + 4kg + i
-    bf16x8b_t wb[3][KS2];
+    // ---- k_hat^T = K^T W^T; acc[i] = k_hat of plane row, dimension 16td + 4kg + i.
+    // B: this lane's plane (row) at keys 16kb + 4kg .. +3, split three ways
+    bf16x4s_t wb[3][NT];
 #pragma unroll
-    for (int s = 0; s < KS2; ++s) {
+    for (int kb = 0; kb < NT; ++kb) {
+      const float4 w4 = *(const float4*)&wsm[row][16 * kb + 4 * kg];
+      const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         __bf16 x0, x1, x2;
-        split3(wsm[row][32 * s + 8 * kg + j], x0, x1, x2);
-        wb[0][s][j] = x0; wb[1][s][j] = x1; wb[2][s][j] = x2;
+        split3(wv[j], x0, x1, x2);
+        wb[0][kb][j] = __builtin_bit_cast(short, x0);
+        wb[1][kb][j] = __builtin_bit_cast(short, x1);
+        wb[2][kb][j] = __builtin_bit_cast(short, x2);
       }
     }
+    typedef __attribute__((address_space(3))) __bf16 lds_bf16_t;
+    typedef __bf16 bf16x4v_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
+    typedef __attribute__((address_space(3))) bf16x4v_t lds_bf16x4_t;
     float* kh = P.khat + ((int64_t)gi * P.ncap + n) * R * D;
 #pragma unroll
     for (int td = 0; td < D / 16; ++td) {
       f32x4b_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS2; ++s) {
-        const bf16x8b_t ka = __builtin_bit_cast(bf16x8b_t,
-                                                *(const u32x4b_t*)&kt[16 * td + row][32 * s + 8 * kg]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, wb[0][s], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, wb[1][s], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, wb[2][s], acc, 0, 0, 0);
+      for (int kb = 0; kb < NT; ++kb) {
+        // A: dims 16td + row, keys 16kb + 4kg .. +3 of the stored keys, transposed
+        lds_bf16x4_t* src = (lds_bf16x4_t*)(lds_bf16_t*)(&kr[16 * kb + (lane >> 2)][16 * td + 4 * (lane & 3)]);
+        const bf16x4s_t ka = __builtin_bit_cast(bf16x4s_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(src));
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, wb[0][kb], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, wb[1][kb], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, wb[2][kb], acc, 0, 0, 0);
       }
       if (row < R) {
         *(float4*)(kh + (int64_t)row * D + 16 * td + 4 * kg) = make_float4(acc[0], acc[1], acc[2], acc[3]);
