@@ -189,7 +189,6 @@ struct LevelParams {
 // scoring (their kept list fits the scoring kernel's LDS staging).
 constexpr int64_t kFuseCap = 4096;
 
-// The first launch of a route checks that every level was built for the current T.
 // The first launch of a route checks that every level was built for the current
 // T: one wave, lane l holding level l + 1's built count (loaded by
 // stale_count, issued with the prologue's other loads), compared once T is in.
